@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark of the Medusa tree-verify step on one MI355X.
+
+A step is one full pass of the hot path from device-resident decode state:
+Medusa heads + top-s + tree fill, embedding, L decoder layers over the tree
+(ancestor-masked tree attention, positions n + depth), final norm + LM head,
+acceptance with next-root selection, KV compaction.  The timed region replays
+the captured step graph `--steps` times with the inputs resident in HBM.
+
+Prints ONE JSON line (rank 0) with steps/s as `value`, tree tokens/s, the
+algorithmic HBM bytes per step and the end-to-end fraction of the 8 TB/s
+peak, the roofline of the dominant kernel (gate/up GEMM, timed per launch
+with HIP events on the library's stream), and the CPU oracle timed on a
+bounded sample of the same step on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "tree-verify steps/s + tree tokens/s, 7B-shape 64-node tree, bs1; % HBM peak"
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def bytes_model(D, B, T, depth, n_mean, acc_mean):
+    """Algorithmic HBM bytes of one step: every weight once (backbone, LM
+    head, heads 1..depth), the prefix K/V read once for all T queries, the
+    tree's K/V written, the fp32 logits written and read by acceptance, and
+    the compaction's row copies."""
+    w = 2 * (D.L * (4 * D.d * D.d + 3 * D.d * D.F) + D.V * D.d + depth * (D.d * D.d + D.V * D.d))
+    kv = B * D.L * 2 * n_mean * D.d * 2
+    tree_kv = B * D.L * 2 * T * D.d * 2
+    logits = B * T * D.V * 4 * 2
+    compact = B * D.L * 2 * 2 * (1 + acc_mean) * D.d * 2
+    return w + kv + tree_kv + logits + compact
+
+
+def gate_up_bytes(D, M):
+    """Algorithmic bytes of one gate/up GEMM launch (one layer): gate and up
+    weights, the normalised activations in, the SwiGLU output out."""
+    return 2 * D.F * D.d * 2 + M * D.d * 2 + M * D.F * 2
+
+
+def cpu_baseline(w, n0, sample_layers=2):
+    """The oracle (float64 NumPy, as it stands) on a bounded sample of one
+    step of workload `w`: all Medusa heads with top-s and tree fill,
+    `sample_layers` of the L decoder layers over the whole tree against an
+    n0-token prefix cache, final norm + LM head, greedy acceptance.  The step
+    time is scaled to all L layers."""
+    import numpy as np
+    from oracle import accept as oa
+    from oracle import heads as oh
+    from oracle import model as om
+    from oracle import tree as otree
+    from workloads import synth
+
+    D = w.dims
+    Wt = synth.Weights(w)
+    paths = synth.tree_paths(w, 0)
+    t = otree.compile_tree(paths)
+    s = synth.tree_topk(w)
+    rng = np.random.default_rng(0)
+    cap = n0 + t.T
+    kv = om.KVCache(sample_layers, D.H, D.hd, cap)
+    for l in range(sample_layers):
+        kv.K[l][:, :n0] = rng.standard_normal((D.H, n0, D.hd))
+        kv.V[l][:, :n0] = rng.standard_normal((D.H, n0, D.hd))
+    h = rng.standard_normal(D.d)
+    # generate the sampled weights up front (input generation is not timed)
+    for k in range(1, t.max_depth + 1):
+        Wt.get(f"head{k}.w1"), Wt.get(f"head{k}.w2")
+    for l in range(sample_layers):
+        Wt.layer(l)
+    Wt.get("embed"), Wt.get("lm_head"), Wt.get("final_norm")
+    t0 = time.perf_counter()
+    z = oh.medusa_heads(Wt.get, h, t.max_depth)
+    top = oh.head_topk(z, s)
+    tok = otree.fill_tokens(t, 0, top)
+    x = om.f64(Wt.get("embed"))[tok]
+    t1 = time.perf_counter()
+    pos, slots, vis = om.tree_positions(t, n0), n0 + np.arange(t.T), om.tree_visibility(t, n0, cap)
+    for l in range(sample_layers):
+        x = om.decoder_layer(x, Wt.layer(l), kv.K[l], kv.V[l], pos, slots, vis, D.H)
+    t2 = time.perf_counter()
+    hn = om.rmsnorm(x, Wt.get("final_norm"))
+    logits = hn @ om.f64(Wt.get("lm_head")).T
+    oa.greedy_accept(t, tok, logits)
+    t3 = time.perf_counter()
+    per_layer = (t2 - t1) / sample_layers
+    step = (t1 - t0) + D.L * per_layer + (t3 - t2)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    return {"value": 1.0 / step, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"one step with {sample_layers} of {D.L} decoder layers timed "
+                       f"({per_layer:.2f} s/layer) plus heads, LM head and acceptance, "
+                       f"scaled to {D.L} layers; float64 NumPy; T={t.T}, n={n0}"),
+            "tree_tokens_per_s": t.T / step, "seconds_per_step": step}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=32)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--profile-steps", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the tree-verify "
+              "step of one sequence batch is a single-GPU workload here", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import tree_verify_step_amd as tv
+    from tree_verify_step_amd import runtime as rt
+    from workloads import configs, synth
+
+    tv.lib()
+    w = configs.get(args.workload) if args.workload else configs.HEADLINE
+    D = w.dims
+    B = w.batch
+    K, W = args.steps, args.warmup
+    P = args.profile_steps if args.profile_steps is not None else K
+    s = synth.tree_topk(w)
+    paths = [synth.tree_paths(w, b) for b in range(B)]
+    ids = synth.prefix_ids(w)
+    n0 = [len(x) for x in ids]
+    trees = rt.DeviceTrees(paths, s)
+    T, depth = trees.T, trees.depth
+    cap = ((max(n0) + T + (K + W + P + 4) * (depth + 1) + 63) // 64) * 64
+    log(f"[bench] workload {w.name}: L={D.L} d={D.d} F={D.F} V={D.V} T={T} depth={depth} "
+        f"B={B} n0={n0} cap={cap}")
+    t_setup = time.perf_counter()
+    dw = rt.DeviceWeights(D, None, seed=w.seed_weights, std=w.init_std)
+    acc = tv.AcceptParams(mode=tv.ACCEPT_GREEDY if w.accept == "greedy" else tv.ACCEPT_TYPICAL,
+                          root_mode=tv.ROOT_ARGMAX if w.root == "argmax" else tv.ROOT_SAMPLE,
+                          temperature=w.temperature, eps=w.eps, delta=w.delta)
+    u = synth.uniform_draws(w, K + W + P + 4)
+    sess = rt.Session(D, B, T, s, cap, dw, trees, acc, u_draws=u)
+    sess.prefill(ids)
+    torch.cuda.synchronize()
+    log(f"[bench] setup + prefill {time.perf_counter() - t_setup:.1f} s")
+
+    for _ in range(W):
+        sess.step(graph=True)
+    torch.cuda.synchronize()
+    n_start = sess.n_prefix.cpu().numpy().astype(np.int64)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        sess.step(graph=True)
+    ev1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    n_end = sess.n_prefix.cpu().numpy().astype(np.int64)
+    wall = t1 - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    log(f"[bench] timed {K} steps: wall {wall * 1e3:.2f} ms, events {gpu_ms:.2f} ms")
+    steps_per_s = K / wall
+    ms_per_step = wall * 1e3 / K
+    acc_mean = float(np.mean((n_end - n_start) / K - 1))
+    n_mean = float(np.mean((n_start + n_end) / 2))
+    bstep = bytes_model(D, B, T, depth, n_mean, acc_mean)
+    hbm_gbs = bstep * steps_per_s / 1e9
+
+    # per-kind kernel timing: eager steps with HIP events around each launch group
+    prof = {}
+    for _ in range(P):
+        for k, (ms, cnt) in sess.ctx.step_profile().items():
+            a = prof.setdefault(k, [0.0, 0])
+            a[0] += ms
+            a[1] += cnt
+    torch.cuda.synchronize()
+    kernels = {k: {"ms_per_step": v[0] / P, "avg_launch_us": 1e3 * v[0] / max(v[1], 1),
+                   "launches_per_step": v[1] / P} for k, v in prof.items()}
+    for k, v in kernels.items():
+        log(f"[bench]   {k:14s} {v['ms_per_step']:8.3f} ms/step  {v['avg_launch_us']:8.2f} us/launch"
+            f"  x{v['launches_per_step']:.0f}")
+    gu = kernels["gemm_gate_up"]
+    gu_bytes = gate_up_bytes(D, B * T)
+    achieved = gu_bytes / (gu["avg_launch_us"] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "gemm_kernel<4,4,1,EPI_SWIGLU> (gate/up + SwiGLU, one layer)",
+                "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu["avg_launch_us"], 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(w, n0[0])
+        log(f"[bench] oracle: {cpu['seconds_per_step']:.1f} s/step on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC,
+        "value": round(steps_per_s, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded random-init bf16 weights N(0,0.02), uniform random prefix ids, "
+                "seeded sparse tree",
+        "config": {"workload": w.name, "batch": B, "tree_nodes": T, "tree_depth": depth,
+                   "prefix": n0[0] if B == 1 else n0, "acceptance": w.accept,
+                   "layers": D.L, "width": D.d, "ffn": D.F, "vocab": D.V, "medusa_heads": D.K},
+        "tree_tokens_per_s": round(steps_per_s * B * T, 1),
+        "accepted_tokens_per_step": round(1 + acc_mean, 3),
+        "hbm_bytes_per_step": int(bstep),
+        "hbm_gbs_end_to_end": round(hbm_gbs, 1),
+        "hbm_frac_end_to_end": round(hbm_gbs / HBM_PEAK_GBS, 4),
+        "graph_event_ms_per_step": round(gpu_ms / K, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in kernels.items()},
+    }
+    sess.close()
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,338 @@
+/*
+ * medusa_verify.h -- C ABI of the gfx950 (MI355X) Medusa tree-verify step.
+ *
+ * One Medusa decoding step (Medusa paper digest, "Algorithm: Medusa decoding
+ * step", steps 1-6; Method items 1-5):
+ *   1. root token t0 from the LM-head logits at the last accepted position;
+ *      each Medusa head k takes its top-s_k tokens           -> mv_medusa_heads
+ *   2. the tree's nodes get their tokens (root: t0)           -> mv_medusa_heads
+ *   3. all tree nodes go through one backbone forward with the
+ *      ancestor-only mask, position id = prefix length + depth -> mv_embed,
+ *                                   mv_decoder_layer x L (uses mv_tree_attention),
+ *                                   mv_lm_head
+ *   4-5. greedy or typical acceptance, longest accepted prefix -> mv_accept
+ *   6. the accepted path's KV moved into contiguous slots       -> mv_kv_compact
+ * mv_step runs the whole step from device-resident state (one hipGraph).
+ *
+ * Conventions (all entry points):
+ *  - Every pointer argument marked "device" is device memory owned by the
+ *    caller; the library never allocates or frees caller memory and keeps no
+ *    pointer beyond the call (except inside an mv_ctx, see mv_ctx_create).
+ *  - bf16 tensors are raw 16-bit bf16 patterns; fp32 is IEEE float.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls only enqueue work on it and never synchronise; device faults
+ *    surface at the caller's next synchronisation.
+ *  - Every call validates its scalar arguments (and, where stated, host-side
+ *    tree arrays) before enqueuing anything.  On failure it returns a
+ *    negative mv_status, enqueues nothing and leaves every output untouched;
+ *    mv_last_error() then describes the failure (thread-local string).
+ *  - Device pointers must be 16-byte aligned.
+ *
+ * Data layouts:
+ *  - Rows of the verify pass: m = b * T + v for sequence b and tree node v.
+ *  - Fragment-packed bf16 matrix [R][C] (R % 16 == 0, C % 32 == 0): blocks of
+ *    16 rows x 32 columns in row-block-major order, each block 64 pieces of 8
+ *    consecutive columns, piece l = row (l % 16), columns 8 * (l / 16) ..;
+ *    element (r, c) sits at
+ *      ((((r/16) * (C/32) + c/32) * 64 + (r%16) + 16*((c%32)/8)) * 8 + c%8.
+ *    Weights of the backbone GEMMs are passed packed (see mv_pack_weight).
+ *  - KV cache (one buffer for K, one for V, all layers):
+ *      K: bf16 [L][B][H][cap][hd]             (slot-major rows)
+ *      V: bf16 [L][B][H][cap/4][hd][4]        (4 consecutive slots interleaved
+ *                                              per dim)
+ *    element (l, b, h, slot, i) of V sits at
+ *      ((((l*B + b)*H + h)*(cap/4) + slot/4)*hd + i)*4 + slot%4.
+ *    cap % 64 == 0.  Slots >= n + T may hold anything.
+ *  - Tree (per sequence, T nodes, root = node 0, parents before children):
+ *    parent[T] (root: -1), depth_of[T] (root: 0), rank[T] (rank of the node's
+ *    token within its head's top-s list; root: 0), and the ancestor bitmask
+ *    anc[T][mask_words] (bit a of node v's words set iff a == v or a is an
+ *    ancestor of v).  Node v's K/V sit at slot n + v, its position id is
+ *    n + depth_of[v] (Medusa paper digest, Method 3 and Pitfalls).
+ */
+#ifndef MEDUSA_VERIFY_H
+#define MEDUSA_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MV_API __attribute__((visibility("default")))
+
+typedef enum {
+  MV_OK = 0,
+  MV_EINVAL = -1,        /* bad scalar argument or null required pointer */
+  MV_EUNSUPPORTED = -2,  /* shape outside what the kernels implement */
+  MV_ECAPACITY = -3,     /* n + T would exceed the cache capacity */
+  MV_EWORKSPACE = -4,    /* workspace smaller than mv_workspace_size() */
+  MV_EHIP = -5,          /* a HIP runtime call failed (detail in mv_last_error) */
+  MV_ETREE = -6          /* invalid tree (not prefix-closed, too deep, ...) */
+} mv_status;
+
+#define MV_MAX_T 256        /* tree nodes per sequence, root included */
+#define MV_MAX_DEPTH 16     /* tree depth (<= number of Medusa heads used) */
+#define MV_MAX_TOPK 16      /* candidates per head */
+#define MV_MAX_BATCH 4      /* sequences per call (Medusa head GEMV) */
+
+#define MV_ACCEPT_GREEDY 0
+#define MV_ACCEPT_TYPICAL 1
+#define MV_ROOT_ARGMAX 0
+#define MV_ROOT_SAMPLE 1
+
+#define MV_PACK_PLAIN 0
+#define MV_PACK_QKV 1
+
+/* Backbone and head shapes.  Multi-head attention: H * hd == d.
+ * Supported: d % 64 == 0, F % 32 == 0, V % 64 == 0, hd in {16,32,64,128},
+ * 1 <= K <= MV_MAX_DEPTH. */
+typedef struct {
+  int32_t L, d, H, hd, F, V, K;
+} mv_dims;
+
+/* Device-side trees of a batch: every sequence has T nodes; arrays are
+ * [B][T] (anc: [B][T][mask_words]); depth = max depth over the batch;
+ * mask_words = ceil(T / 64). */
+typedef struct {
+  int32_t T, depth, mask_words;
+  const int32_t* parent;
+  const int32_t* depth_of;
+  const int32_t* rank;
+  const uint64_t* anc;
+} mv_tree;
+
+/* The whole KV cache (layouts above). */
+typedef struct {
+  void* k;
+  void* v;
+  int32_t L, B, H, hd, cap;
+} mv_kv;
+
+/* One decoder layer's weights (device): RMSNorm gains bf16 [d]; the
+ * projections fragment-packed bf16: wqkv [3d][d] packed with MV_PACK_QKV
+ * (rows: q then k then v, each (out, in)), wo [d][d], wgate [F][d],
+ * wup [F][d], wdown [d][F] packed with MV_PACK_PLAIN. */
+typedef struct {
+  const void* attn_norm;
+  const void* wqkv;
+  const void* wo;
+  const void* ffn_norm;
+  const void* wgate;
+  const void* wup;
+  const void* wdown;
+} mv_layer_weights;
+
+/* Acceptance rule (Medusa paper digest, Method 5 and "Paper vs code"):
+ * GREEDY: candidate accepted iff it equals the argmax of its parent's row;
+ * TYPICAL: iff q(x) > min(eps, delta * exp(-H(q))) with q = softmax(z /
+ * temperature) of the parent's row and H(q) = -sum q log(q + 1e-5).
+ * root_mode ARGMAX: next root = argmax of the best node's row; SAMPLE: the
+ * smallest id whose cumulative softmax(z / temperature) mass (id order)
+ * exceeds the step's uniform draw.  temperature > 0 for TYPICAL / SAMPLE. */
+typedef struct {
+  int32_t mode;
+  int32_t root_mode;
+  float temperature;
+  float eps;
+  float delta;
+} mv_accept_params;
+
+/* ---- errors -------------------------------------------------------------- */
+MV_API const char* mv_strerror(int status);          /* static string */
+MV_API const char* mv_last_error(void);              /* thread-local detail */
+
+/* ---- host helpers -------------------------------------------------------- */
+
+/* Flatten a candidate tree given as its paths of 0-based head ranks (Medusa
+ * paper digest, Method 2-4; the released sparse trees are such path lists).
+ * paths: host int32 [n_paths][max_len] row-major, path p = paths[p][0 ..
+ * path_len[p]-1] (ranks i_1..i_k: head j's i_j-th candidate).  The list must
+ * be prefix-closed, duplicate-free, with 1 <= len <= MV_MAX_DEPTH and
+ * 0 <= rank < topk.  Node order: root, then by (depth, lexicographic path).
+ * Outputs (host): parent, depth_of, rank [T], anc [T][mask_words], *T_out =
+ * n_paths + 1; capacity `cap_nodes` >= n_paths + 1 and mask_words >=
+ * ceil(T/64).  Errors: MV_ETREE (with the offending path in mv_last_error),
+ * MV_EINVAL. */
+MV_API int mv_tree_compile(const int32_t* paths, const int32_t* path_len, int32_t n_paths,
+                           int32_t max_len, int32_t topk, int32_t cap_nodes,
+                           int32_t mask_words, int32_t* parent, int32_t* depth_of,
+                           int32_t* rank, uint64_t* anc, int32_t* T_out);
+
+/* Reorder a row-major bf16 weight [rows][cols] (out, in) into the
+ * fragment-packed layout the backbone GEMMs read.  layout MV_PACK_QKV: the
+ * matrix is the fused [3d][d] q|k|v projection with head size hd; q and k
+ * rows are additionally permuted so that each 64-row tile holds RoPE pairs
+ * (dims i and i + hd/2 of a head).  src and dst are device buffers of
+ * rows*cols bf16 and must not overlap.  rows % 16 == 0, cols % 32 == 0. */
+MV_API int mv_pack_weight(const void* src, void* dst, int32_t rows, int32_t cols,
+                          int32_t layout, int32_t hd, void* stream);
+
+/* Bytes of device workspace needed by the calls below for this shape
+ * (the largest of the per-call needs; one workspace serves them all). */
+MV_API int mv_workspace_size(const mv_dims* dims, int32_t B, int32_t T, int32_t cap,
+                             size_t* bytes);
+
+/* ---- the step's operations ----------------------------------------------- */
+
+/* Medusa heads (Medusa paper digest, Method 1-2, Algorithm steps 1-2):
+ *   u_k = h + SiLU(W1_k h),  z_k = W2_k u_k,  k = 1..D (D <= dims.K),
+ *   top_ids[b][k-1][0..s) = the s largest z_k (larger value first, lower id
+ *   first on ties), top_vals the matching logits;
+ *   tree_tok[b][v] = root_tok[b] for the root, top_ids[b][depth(v)-1][rank(v)]
+ *   otherwise (skipped when tree == NULL).
+ * h: device bf16 [B][d] (final-normed hidden state at the last accepted
+ * position); w1: device bf16 [K][d][d], w2: device bf16 [K][V][d], both
+ * row-major (out, in); head_logits: device fp32 [B][D][V] or NULL (then the
+ * workspace holds them).  B <= MV_MAX_BATCH, s <= MV_MAX_TOPK, s <= V. */
+MV_API int mv_medusa_heads(const mv_dims* dims, int32_t B, int32_t D, int32_t s, const void* h,
+                           const void* w1, const void* w2, const mv_tree* tree,
+                           const int32_t* root_tok, int32_t* top_ids, float* top_vals,
+                           int32_t* tree_tok, float* head_logits, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* Tree attention of one layer (Medusa paper digest, Method 3; wq-win lecture
+ * note, 二.2): for every node v of sequence b and head h,
+ *   out[b][v][h] = sum_s softmax_s(q . K_s / sqrt(hd)) V_s
+ * over the slots s in [0, n[b]) and s = n[b] + a for each ancestor a of v
+ * (v included).  q: device bf16 [B][T][H][hd], RoPE already applied at
+ * position n + depth; the tree's K/V must already sit at slots n .. n+T-1 of
+ * layer `layer`; n_prefix: device int32 [B]; out: device bf16 [B][T][H][hd].
+ * Requires n[b] + T <= cap (not checked on the device: the caller owns n). */
+MV_API int mv_tree_attention(const mv_dims* dims, int32_t B, const mv_tree* tree,
+                             const int32_t* n_prefix, const void* q, const mv_kv* kv,
+                             int32_t layer, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* One pre-norm Llama decoder layer over all B*T tree rows (the verify
+ * forward of Algorithm step 3):
+ *   r = RMSNorm(x) (eps 1e-5);  q,k,v = r Wq^T, r Wk^T, r Wv^T;
+ *   RoPE (base 10000, pairs (i, i + hd/2)) at position n[b] + depth(v);
+ *   K/V rows -> cache slots n[b] + v;  o = tree attention;
+ *   x += o Wo^T;  r' = RMSNorm(x);  x += (SiLU(r' Wg^T) * (r' Wu^T)) Wd^T.
+ * x: device fp32 [B*T][d], the residual stream, updated in place. */
+MV_API int mv_decoder_layer(const mv_dims* dims, int32_t B, const mv_tree* tree,
+                            const int32_t* n_prefix, const mv_layer_weights* w, const mv_kv* kv,
+                            int32_t layer, float* x, void* ws, size_t ws_bytes, void* stream);
+
+/* x[m] = embed[tokens[m]] widened to fp32.  tokens: device int32 [M] (values
+ * clamped to [0, V)); embed: device bf16 [V][d] row-major; x: fp32 [M][d]. */
+MV_API int mv_embed(const mv_dims* dims, int32_t M, const int32_t* tokens, const void* embed,
+                    float* x, void* stream);
+
+/* Final RMSNorm and LM head ("head 0"): hn = RMSNorm(x) * final_norm (bf16),
+ * logits = hn W_lm^T in fp32.  lm_head: fragment-packed bf16 [V][d];
+ * logits: device fp32 [M][V]; hn_rows: device bf16 [M][d] row-major or NULL. */
+MV_API int mv_lm_head(const mv_dims* dims, int32_t M, const float* x, const void* final_norm,
+                      const void* lm_head, float* logits, void* hn_rows, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* Acceptance (Algorithm steps 4-5): decisions per edge, accepted prefix,
+ * best node v* = deepest accepted node (TYPICAL: then larger summed
+ * log-probability of the accepted candidates; then lower index).
+ * logits: device fp32 [B][T][V]; tree_tok: device int32 [B][T];
+ * u: device double [B] uniform draws in [0,1) (SAMPLE only, else NULL).
+ * Outputs (device): accept_len [B] (= depth of v*), path [B][depth+1] (node
+ * indices root..v*, then -1), best [B], next_root [B]; optional: emitted
+ * [B][depth+1] (tokens of the path, then -1), margin double [B][T+1]
+ * ((q - thr)/thr per edge for TYPICAL, [T]: |cdf - u| of the sampled root),
+ * hn bf16 [B*T][d] with h_last bf16 [B][d] (h_last[b] = hn[b*T + v*]). */
+MV_API int mv_accept(int32_t B, int32_t T, int32_t V, int32_t d, const float* logits,
+                     const mv_tree* tree, const int32_t* tree_tok, const mv_accept_params* p,
+                     const double* u, int32_t* accept_len, int32_t* path, int32_t* best,
+                     int32_t* next_root, int32_t* emitted, double* margin, const void* hn,
+                     void* h_last, void* ws, size_t ws_bytes, void* stream);
+
+/* KV compaction (Algorithm step 6; Medusa paper digest, Pitfalls): for every
+ * layer, sequence b and m = 0..accept_len[b]: slot n[b] + m <- slot n[b] +
+ * path[b][m] (K and V; all sources read before any destination is written),
+ * then n[b] += 1 + accept_len[b].  path: device int32 [B][path_stride];
+ * accept_len, n_prefix: device int32 [B] (n_prefix updated in place). */
+MV_API int mv_kv_compact(const mv_kv* kv, const int32_t* path, int32_t path_stride,
+                         const int32_t* accept_len, int32_t* n_prefix, void* stream);
+
+/* ---- whole step ---------------------------------------------------------- */
+
+/* Everything one decode step reads and writes (all device, caller-owned).
+ * State carried between steps: n_prefix [B], root_tok [B], h_last bf16
+ * [B][d], the KV cache, and (SAMPLE roots) the draw counter u_index (int32,
+ * device) into u_draws double [n_draws][B]. */
+typedef struct {
+  mv_dims dims;
+  int32_t B, T, s;                 /* s: candidates per head (topk) */
+  const mv_layer_weights* layers;  /* host array [L] of device pointers */
+  const void* embed;               /* bf16 [V][d] */
+  const void* final_norm;          /* bf16 [d] */
+  const void* lm_head;             /* packed bf16 [V][d] */
+  const void* w1;                  /* bf16 [K][d][d] */
+  const void* w2;                  /* bf16 [K][V][d] */
+  mv_kv kv;
+  mv_tree tree;
+  mv_accept_params accept;
+  int32_t* n_prefix;
+  int32_t* root_tok;
+  void* h_last;
+  const double* u_draws;           /* SAMPLE only */
+  int32_t* u_index;                /* SAMPLE only */
+  int32_t n_draws;
+  /* per-step outputs */
+  int32_t* tree_tok;               /* [B][T] */
+  float* logits;                   /* [B][T][V] */
+  int32_t* accept_len;             /* [B] */
+  int32_t* path;                   /* [B][depth+1] */
+  int32_t* emitted;                /* [B][depth+1] */
+  int32_t* best;                   /* [B] */
+  /* optional per-step outputs (NULL: kept in the workspace) */
+  float* head_logits;              /* [B][depth][V] Medusa head logits */
+  int32_t* top_ids;                /* [B][depth][s] per-head candidates */
+  void* ws;
+  size_t ws_bytes;
+} mv_step_desc;
+
+typedef struct mv_ctx mv_ctx;
+
+/* Validate the description and bind it.  The context keeps the pointers in
+ * `desc` (and copies the host layer array); it owns only a captured hipGraph
+ * and a few small device arrays for prefill chain trees. */
+MV_API int mv_ctx_create(mv_ctx** out, const mv_step_desc* desc);
+MV_API void mv_ctx_destroy(mv_ctx* ctx);
+
+/* Prefill: run the prompts through the backbone in chunks of up to T tokens
+ * as chain trees (parent = previous token, so the tree mask is the causal
+ * mask), filling KV slots [0, n), then set h_last, root_tok (ARGMAX or SAMPLE
+ * with draw u_draws[u_index]) and n_prefix = n.  ids: device int32 [B][ld];
+ * n_ids: host int32 [B] (1 <= n <= cap - T); counter u_index is set to 1. */
+MV_API int mv_prefill(mv_ctx* ctx, const int32_t* ids, int32_t ld, const int32_t* n_ids,
+                      void* stream);
+
+/* One tree-verify step from the device-resident state.  graph != 0: the
+ * step is captured into a hipGraph on the first call and replayed after;
+ * graph == 0: the kernels are enqueued directly. */
+MV_API int mv_step(mv_ctx* ctx, int32_t graph, void* stream);
+
+/* Launch-group kinds reported by mv_step_profile. */
+#define MV_K_HEADS 0     /* Medusa heads: W1 block, vocab projection, top-s, tree fill */
+#define MV_K_EMBED 1     /* embedding gather and RoPE table */
+#define MV_K_NORM 2      /* RMSNorm into the packed GEMM operand (2 per layer) */
+#define MV_K_QKV 3       /* fused QKV GEMM with RoPE and KV-cache write */
+#define MV_K_ATTN 4      /* tree attention and range combine */
+#define MV_K_O 5         /* output projection GEMM + residual */
+#define MV_K_GATE_UP 6   /* gate/up GEMM with SwiGLU */
+#define MV_K_DOWN 7      /* down projection GEMM + residual */
+#define MV_K_LM_HEAD 8   /* final RMSNorm and LM-head GEMM */
+#define MV_K_ACCEPT 9    /* acceptance and next root */
+#define MV_K_COUNT 11
+#define MV_K_COMPACT 10  /* KV compaction and n update */
+
+/* One step enqueued directly (no graph) with a pair of HIP events on
+ * `stream` around every launch group; waits for the step, then reports per
+ * kind the summed milliseconds ms[MV_K_COUNT] and launch-group counts
+ * count[MV_K_COUNT] (host arrays).  Same kernels and launch shapes as
+ * mv_step. */
+MV_API int mv_step_profile(mv_ctx* ctx, float* ms, int32_t* count, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MEDUSA_VERIFY_H */

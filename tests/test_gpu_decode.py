@@ -1,0 +1,156 @@
+"""End-to-end GPU decode against the oracle (run on an MI355X).
+
+* Teacher-forced: every step's head logits, tree logits and KV rows agree with
+  the oracle within 2e-2, and every index decision (candidates, tree tokens,
+  acceptance, path, next root, emitted tokens, n) is bit-exact given the
+  GPU's own logits; the oracle then follows the GPU's decisions, so all steps
+  are compared.
+* Free-running: the GPU's token stream equals the oracle's own decode up to
+  the first near-tie (a decision whose deciding logit gap is within the
+  measured error), and equals plain greedy decoding (lossless acceptance).
+"""
+import numpy as np
+import pytest
+import torch
+
+import tree_verify_step_amd as tv
+from tree_verify_step_amd import runtime as rt
+from oracle import accept as oa
+from oracle import decode as od
+from oracle import heads as oh
+from oracle import model as om
+from oracle import tree as otree
+from workloads import configs, synth
+
+from gpu_helpers import TOL
+
+pytestmark = pytest.mark.gpu
+
+
+def _session(w, cap, debug=True, u=None):
+    D = w.dims
+    Wt = synth.Weights(w)
+    s = synth.tree_topk(w)
+    paths = [synth.tree_paths(w, b) for b in range(w.batch)]
+    trees = rt.DeviceTrees(paths, s)
+    dw = rt.DeviceWeights(D, Wt.get)
+    p = tv.AcceptParams(mode=tv.ACCEPT_GREEDY if w.accept == "greedy" else tv.ACCEPT_TYPICAL,
+                        root_mode=tv.ROOT_ARGMAX if w.root == "argmax" else tv.ROOT_SAMPLE,
+                        temperature=w.temperature, eps=w.eps, delta=w.delta)
+    sess = rt.Session(D, w.batch, trees.T, s, cap, dw, trees, p, u_draws=u, debug=debug)
+    return Wt, paths, sess
+
+
+def _params(w):
+    return od.StepParams(mode=w.accept, root=w.root, temperature=w.temperature, eps=w.eps,
+                         delta=w.delta, topk=synth.tree_topk(w))
+
+
+@pytest.mark.parametrize("graph", [False, True])
+@pytest.mark.parametrize("variant", ["greedy", "typical_sample"])
+def test_tiny_decode_teacher_forced(graph, variant):
+    w = configs.TINY.with_(weight_dtype="bf16")
+    if variant == "typical_sample":
+        w = w.with_(accept="typical", root="sample", temperature=0.7, eps=0.09, delta=0.3)
+    print(f"tiny decode teacher-forced graph={graph} {variant}", flush=True)
+    D = w.dims
+    cap = 256
+    u = synth.uniform_draws(w, w.steps + 1)
+    Wt, paths, sess = _session(w, cap, u=u)
+    ids = synth.prefix_ids(w)[0]
+    sess.prefill([ids])
+    torch.cuda.synchronize()
+    p = _params(w)
+    st = od.prefill(Wt.get, D.L, D.H, ids, cap, D.hd, p, u=u[0, 0])
+    t = otree.compile_tree(paths[0])
+    assert int(sess.n_prefix[0]) == len(ids)
+    np.testing.assert_allclose(sess.h_last[0].float().cpu().numpy(), st.h_last, atol=TOL)
+    # the prefill's last chunk leaves its logits in place: the first root is
+    # chosen from the row of the last prompt token
+    last = sess.logits[0, (len(ids) - 1) % sess.T].cpu().numpy().astype(np.float64)
+    if w.root == "argmax":
+        assert int(sess.root_tok[0]) == oa.argmax_lowest(last)
+    else:
+        want, margin = oa.sample_root(last, w.temperature, u[0, 0])
+        if margin > 1e-6:
+            assert int(sess.root_tok[0]) == want
+    st.t0 = int(sess.root_tok[0])            # follow the GPU's root (checked below per step)
+    for step in range(w.steps):
+        sess.step(graph=graph)
+        torch.cuda.synchronize()
+        # heads
+        hz = sess.head_logits[0].cpu().numpy()
+        want_z = oh.medusa_heads(Wt.get, st.h_last, t.max_depth)
+        assert np.abs(hz - want_z).max() <= TOL, step
+        top = sess.top_ids[0].cpu().numpy()
+        np.testing.assert_array_equal(top, oh.head_topk(hz, p.topk))
+        tok = otree.fill_tokens(t, st.t0, top)
+        np.testing.assert_array_equal(sess.tree_tok[0].cpu().numpy(), tok)
+        # verify forward
+        n0 = st.n
+        hn, logits = om.tree_forward(Wt.get, D.L, D.H, t, tok, n0, st.kv)
+        gl = sess.logits[0].cpu().numpy().astype(np.float64)
+        assert np.abs(gl - logits).max() <= TOL, step
+        # acceptance on the GPU's logits is bit-exact
+        if w.accept == "greedy":
+            res = oa.greedy_accept(t, tok, gl)
+        else:
+            res = oa.typical_accept(t, tok, gl, w.temperature, w.eps, w.delta)
+        assert int(sess.accept_len[0]) == res.accept_len, step
+        np.testing.assert_array_equal(sess.path[0].cpu().numpy()[:res.accept_len + 1], res.path)
+        np.testing.assert_array_equal(sess.emitted[0].cpu().numpy()[:res.accept_len + 1],
+                                      tok[res.path])
+        if w.root == "argmax":
+            assert int(sess.root_tok[0]) == oa.argmax_lowest(gl[res.best])
+        else:
+            want, margin = oa.sample_root(gl[res.best], w.temperature, u[step + 1, 0])
+            if margin > 1e-6:
+                assert int(sess.root_tok[0]) == want
+        # follow the GPU: compact, carry state
+        od.compact_kv(st.kv, n0, res.path)
+        st.n = n0 + len(res.path)
+        st.t0 = int(sess.root_tok[0])
+        st.h_last = hn[res.best]
+        assert int(sess.n_prefix[0]) == st.n
+        kg = sess.kv.k[:, 0].float().cpu().numpy()
+        for l in range(D.L):
+            assert np.abs(kg[l][:, :st.n] - st.kv.K[l][:, :st.n]).max() <= TOL
+
+
+def test_tiny_decode_free_running_is_lossless():
+    """The GPU's greedy Medusa stream equals plain greedy decoding (oracle) up
+    to the first decision that the rounding difference could flip."""
+    w = configs.TINY.with_(weight_dtype="bf16")
+    print("tiny decode free-running", flush=True)
+    D = w.dims
+    cap = 256
+    Wt, paths, sess = _session(w, cap, debug=False)
+    ids = synth.prefix_ids(w)[0]
+    sess.prefill([ids])
+    emitted = []
+    for _ in range(w.steps):
+        sess.step(graph=True)
+        torch.cuda.synchronize()
+        L = int(sess.accept_len[0])
+        emitted += [int(x) for x in sess.emitted[0].cpu().numpy()[:L + 1]]
+    p = _params(w)
+    st = od.prefill(Wt.get, D.L, D.H, ids, cap, D.hd, p)
+    # plain greedy decode with the oracle, tracking each decision's logit gap
+    t = st.t0
+    n = st.n
+    ref, gaps = [], []
+    for _ in range(len(emitted)):
+        ref.append(int(t))
+        _, lg = om.causal_forward(Wt.get, D.L, D.H, np.array([t]), n, st.kv)
+        n += 1
+        z = np.sort(lg[-1])
+        gaps.append(z[-1] - z[-2])
+        t = oa.argmax_lowest(lg[-1])
+    # compare up to the first near-tie (gap below a margin over the observed error)
+    k = len(ref)
+    for i, g in enumerate(gaps):
+        if g <= 5e-3:
+            k = i + 1
+            break
+    assert emitted[:k] == ref[:k]
+    assert k >= 8, f"only {k} tokens compared before a near-tie"

@@ -1,0 +1,369 @@
+"""GPU parity of each library entry point against the oracle (run on an MI355X).
+
+Floating-point outputs (logits, attention outputs, layer outputs) must agree
+with the float64 oracle within 2e-2 absolute; index outputs (top-s ids, tree
+tokens, accept decisions, paths, compacted rows) must agree bit-exactly when
+the oracle is given the GPU's own logits.  Inputs are seeded and synthetic.
+"""
+import numpy as np
+import pytest
+import torch
+
+import tree_verify_step_amd as tv
+from tree_verify_step_amd import runtime as rt
+from oracle import accept as oa
+from oracle import heads as oh
+from oracle import model as om
+from oracle import tree as otree
+from workloads import configs, synth
+
+from gpu_helpers import (DEV, TOL, bf16_values, device_tree, dims_struct, fill_prefix_kv, i32,
+                         random_trees, workload_with, workspace)
+
+pytestmark = pytest.mark.gpu
+
+
+def _flush(msg):
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------- packing + GEMM (LM head)
+
+@pytest.mark.parametrize("M,d,V", [(15, 64, 512), (64, 256, 1024), (100, 128, 640), (256, 128, 512)])
+def test_lm_head_matches_oracle(M, d, V):
+    _flush(f"lm_head M={M} d={d} V={V}")
+    rng = np.random.default_rng(M + d)
+    D = configs.Dims(L=1, d=d, H=d // 64, hd=64, F=64, V=V, K=1)
+    x = rng.standard_normal((M, d)).astype(np.float32)
+    g = bf16_values(1 + 0.1 * rng.standard_normal(d))
+    W = bf16_values(0.05 * rng.standard_normal((V, d)))
+    xt = torch.from_numpy(x).to(DEV)
+    gt = torch.from_numpy(g.astype(np.float32)).to(DEV).to(torch.bfloat16)
+    Wp = rt.pack(torch.from_numpy(W.astype(np.float32)).to(DEV).to(torch.bfloat16))
+    logits = torch.zeros(M, V, device=DEV)
+    hn = torch.zeros(M, d, device=DEV, dtype=torch.bfloat16)
+    ws = workspace(D, (M + 255) // 256, (M + (M + 255) // 256 - 1) // ((M + 255) // 256), 64)
+    tv.lm_head(dims_struct(D), M, xt, gt, Wp, logits, hn, ws)
+    torch.cuda.synchronize()
+    hn_ref = om.rmsnorm(x.astype(np.float64), g)
+    want = hn_ref @ W.T
+    got = logits.cpu().numpy()
+    assert np.abs(got - want).max() <= TOL
+    assert np.abs(hn.float().cpu().numpy() - hn_ref).max() <= 2e-2
+
+
+# ---------------------------------------------------------------- tree attention
+
+def _attention_case(D, B, T, ns, depth, topk, seed, cap=None):
+    rng = np.random.default_rng(seed)
+    paths = random_trees(rng, B, T - 1, depth, topk)
+    trees = [otree.compile_tree(p) for p in paths]
+    cap = cap or ((max(ns) + T + 63) // 64) * 64
+    ocaches, kv = fill_prefix_kv(rng, D, B, ns, cap)
+    # tree K/V at slots n..n+T-1 (random bf16 values) and RoPE'd q
+    q = bf16_values(rng.standard_normal((B, T, D.H, D.hd)))
+    kt = bf16_values(rng.standard_normal((B, D.H, T, D.hd)))
+    vt = bf16_values(rng.standard_normal((B, D.H, T, D.hd)))
+    krow = kv.k.float().cpu()
+    vrow = kv.v_rows().float().cpu()
+    for b, n in enumerate(ns):
+        ocaches[b].K[0][:, n:n + T] = kt[b]
+        ocaches[b].V[0][:, n:n + T] = vt[b]
+        krow[0, b, :, n:n + T] = torch.from_numpy(kt[b].astype(np.float32))
+        vrow[0, b, :, n:n + T] = torch.from_numpy(vt[b].astype(np.float32))
+    kv.k.copy_(krow.to(DEV).to(torch.bfloat16))
+    kv.v.copy_(rt.KVCache.interleave_v(vrow).to(DEV).to(torch.bfloat16))
+    return rng, paths, trees, ocaches, kv, q, cap
+
+
+@pytest.mark.parametrize("hd,H,B,T,ns", [
+    (16, 4, 1, 15, [32]),            # tiny shape
+    (128, 2, 1, 64, [512]),          # 7B head dim, one mask word
+    (128, 2, 1, 64, [37]),           # ragged prefix, not a multiple of 4 or 64
+    (128, 2, 4, 64, [1030, 64, 7, 2047]),  # batch with ragged prefixes
+    (64, 2, 1, 256, [300]),          # four mask words
+    (128, 1, 1, 1, [100]),           # root only: a vanilla decode step
+    (32, 2, 2, 17, [0, 5]),          # empty prefix for one sequence
+])
+def test_tree_attention_matches_oracle(hd, H, B, T, ns):
+    _flush(f"tree_attention hd={hd} H={H} B={B} T={T} ns={ns}")
+    D = configs.Dims(L=1, d=H * hd, H=H, hd=hd, F=64, V=64, K=4)
+    rng, paths, trees, ocaches, kv, q, cap = _attention_case(D, B, T, ns, 4, 5, hd + T + B)
+    dt = device_tree(paths, 5)
+    out = torch.zeros(B, T, H, hd, device=DEV, dtype=torch.bfloat16)
+    ws = workspace(D, B, T, cap)
+    tv.tree_attention(dims_struct(D), B, dt.struct(), i32(ns), torch.from_numpy(
+        q.astype(np.float32)).to(DEV).to(torch.bfloat16), kv.struct(), 0, out, ws)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    for b, n in enumerate(ns):
+        vis = om.tree_visibility(trees[b], n, cap)
+        want = om.attend(q[b], ocaches[b].K[0], ocaches[b].V[0], vis)
+        err = np.abs(got[b] - want).max()
+        assert err <= TOL, (b, err)
+
+
+def test_tree_attention_ignores_non_ancestors_bit_exact():
+    """Changing the K/V of every non-ancestor tree slot of node v leaves v's
+    output bit-for-bit unchanged (masked keys are skipped, not weighted 0)."""
+    D = configs.Dims(L=1, d=256, H=2, hd=128, F=64, V=64, K=4)
+    B, T, ns = 1, 64, [200]
+    rng, paths, trees, ocaches, kv, q, cap = _attention_case(D, B, T, ns, 4, 10, 77)
+    dt = device_tree(paths, 10)
+    qt = torch.from_numpy(q.astype(np.float32)).to(DEV).to(torch.bfloat16)
+    ws = workspace(D, B, T, cap)
+    out1 = torch.zeros(B, T, D.H, D.hd, device=DEV, dtype=torch.bfloat16)
+    tv.tree_attention(dims_struct(D), B, dt.struct(), i32(ns), qt, kv.struct(), 0, out1, ws)
+    v = T - 1
+    others = [a for a in range(T) if not trees[0].anc[v, a]]
+    slots = [ns[0] + a for a in others]
+    kv.k[0, 0, :, slots] = (kv.k[0, 0, :, slots].float() * -3.0 + 1.0).to(torch.bfloat16)
+    vr = kv.v_rows()
+    vr[0, 0, :, slots] = vr[0, 0, :, slots] * 5.0 - 2.0
+    kv.v.copy_(rt.KVCache.interleave_v(vr))
+    out2 = torch.zeros_like(out1)
+    tv.tree_attention(dims_struct(D), B, dt.struct(), i32(ns), qt, kv.struct(), 0, out2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out1[0, v], out2[0, v])
+
+
+def test_tree_attention_chain_equals_causal():
+    D = configs.Dims(L=1, d=128, H=1, hd=128, F=64, V=64, K=4)
+    rng = np.random.default_rng(5)
+    T, n = 64, 130
+    chain = [(0,) * k for k in range(1, T)]
+    t = otree.compile_tree(chain)
+    cap = 256
+    ocaches, kv = fill_prefix_kv(rng, D, 1, [n + T], cap)      # prefix + chain rows all random
+    q = bf16_values(rng.standard_normal((1, T, 1, 128)))
+    dt = device_tree([chain], 1)
+    out = torch.zeros(1, T, 1, 128, device=DEV, dtype=torch.bfloat16)
+    ws = workspace(D, 1, T, cap)
+    tv.tree_attention(dims_struct(D), 1, dt.struct(), i32([n]),
+                      torch.from_numpy(q.astype(np.float32)).to(DEV).to(torch.bfloat16),
+                      kv.struct(), 0, out, ws)
+    torch.cuda.synchronize()
+    causal = np.arange(cap)[None, :] <= (n + np.arange(T))[:, None]
+    want = om.attend(q[0], ocaches[0].K[0], ocaches[0].V[0], causal)
+    assert np.abs(out[0].float().cpu().numpy() - want).max() <= TOL
+
+
+# ---------------------------------------------------------------- decoder layer
+
+def _layer_case(D, B, ns, paths_per_seq, topk, seed, gain_std=0.1):
+    w = workload_with(D, norm_gain_std=gain_std, seed_weights=seed)
+    Wt = synth.Weights(w)
+    rng = np.random.default_rng(seed)
+    trees = [otree.compile_tree(p) for p in paths_per_seq]
+    T = trees[0].T
+    cap = ((max(ns) + T + 63) // 64) * 64
+    ocaches, kv = fill_prefix_kv(rng, D, B, ns, cap, scale=1.5)
+    x = rng.standard_normal((B * T, D.d)).astype(np.float32)
+    return Wt, trees, ocaches, kv, x, cap
+
+
+@pytest.mark.parametrize("name,B,ns", [
+    ("tiny", 1, [32]),
+    ("mid", 1, [77]),          # hd = 128 with a 64-wide tile: RoPE-paired packing
+    ("mid", 2, [64, 301]),
+])
+def test_decoder_layer_matches_oracle(name, B, ns):
+    _flush(f"decoder_layer {name} B={B} ns={ns}")
+    D = {"tiny": configs.TINY.dims,
+         "mid": configs.Dims(L=1, d=256, H=2, hd=128, F=512, V=512, K=3)}[name]
+    D = configs.Dims(L=1, d=D.d, H=D.H, hd=D.hd, F=D.F, V=D.V, K=D.K)
+    rng = np.random.default_rng(11)
+    paths = [synth.cartesian_paths((2, 2, 2))] * B if name == "tiny" else \
+        random_trees(rng, B, 63, 4, 6)
+    Wt, trees, ocaches, kv, x, cap = _layer_case(D, B, ns, paths, 6, 2024 + B)
+    dw = rt.DeviceWeights(D, Wt.get, heads=False)
+    dt = device_tree(paths, 6)
+    T = dt.T
+    xt = torch.from_numpy(x).to(DEV)
+    ws = workspace(D, B, T, cap)
+    tv.decoder_layer(dims_struct(D), B, dt.struct(), i32(ns), dw.layer_structs[0], kv.struct(), 0,
+                     xt, ws)
+    torch.cuda.synchronize()
+    got = xt.cpu().numpy()
+    kgot = kv.k.float().cpu().numpy()
+    vgot = kv.v_rows().float().cpu().numpy()
+    Wl = Wt.layer(0)
+    for b, n in enumerate(ns):
+        t = trees[b]
+        xb = x[b * T:(b + 1) * T].astype(np.float64)
+        want = om.decoder_layer(xb, Wl, ocaches[b].K[0], ocaches[b].V[0], n + t.depth,
+                                n + np.arange(T), om.tree_visibility(t, n, cap), D.H)
+        err = np.abs(got[b * T:(b + 1) * T] - want).max()
+        assert err <= TOL, (b, err)
+        # the tree's K/V rows written at slots n .. n+T-1
+        kerr = np.abs(kgot[0, b, :, n:n + T] - ocaches[b].K[0][:, n:n + T]).max()
+        verr = np.abs(vgot[0, b, :, n:n + T] - ocaches[b].V[0][:, n:n + T]).max()
+        assert kerr <= TOL and verr <= TOL, (kerr, verr)
+
+
+# ---------------------------------------------------------------- heads
+
+@pytest.mark.parametrize("B,d,V,K,s", [(1, 64, 512, 3, 2), (1, 256, 1024, 4, 10), (4, 128, 640, 4, 10)])
+def test_medusa_heads_match_oracle(B, d, V, K, s):
+    _flush(f"medusa_heads B={B} d={d} V={V} K={K} s={s}")
+    D = configs.Dims(L=1, d=d, H=d // 64, hd=64, F=64, V=V, K=K)
+    w = workload_with(D)
+    Wt = synth.Weights(w)
+    rng = np.random.default_rng(d + V)
+    h = bf16_values(rng.standard_normal((B, d)))
+    paths = [synth.sparse_tree_paths(7 + b, 20, K, s) for b in range(B)]
+    dt = device_tree(paths, s)
+    w1 = torch.stack([rt.upload_bf16(Wt[f"head{k}.w1"]) for k in range(1, K + 1)])
+    w2 = torch.stack([rt.upload_bf16(Wt[f"head{k}.w2"]) for k in range(1, K + 1)])
+    Dn = dt.depth
+    top_ids = torch.zeros(B, Dn, s, device=DEV, dtype=torch.int32)
+    top_vals = torch.zeros(B, Dn, s, device=DEV)
+    tree_tok = torch.zeros(B, dt.T, device=DEV, dtype=torch.int32)
+    z = torch.zeros(B, Dn, V, device=DEV)
+    root = i32(rng.integers(0, V, B))
+    ws = workspace(D, B, dt.T, 64)
+    tv.medusa_heads(dims_struct(D), B, Dn, s, torch.from_numpy(h.astype(np.float32)).to(DEV).to(
+        torch.bfloat16), w1, w2, dt.struct(), root, top_ids, top_vals, tree_tok, z, ws)
+    torch.cuda.synchronize()
+    zg = z.cpu().numpy()
+    ids = top_ids.cpu().numpy()
+    toks = tree_tok.cpu().numpy()
+    for b in range(B):
+        want = oh.medusa_heads(Wt.get, h[b], Dn)
+        assert np.abs(zg[b] - want).max() <= TOL
+        # given the GPU's own logits, the selection is bit-exact
+        np.testing.assert_array_equal(ids[b], oh.head_topk(zg[b], s))
+        np.testing.assert_array_equal(top_vals[b].cpu().numpy(),
+                                      np.take_along_axis(zg[b], ids[b].astype(np.int64), 1))
+        t = otree.compile_tree(paths[b])
+        np.testing.assert_array_equal(toks[b], otree.fill_tokens(t, int(root[b]), ids[b]))
+
+
+def test_zero_w1_heads_reproduce_lm_head_on_gpu():
+    D = configs.Dims(L=1, d=128, H=2, hd=64, F=64, V=512, K=2)
+    Wt = synth.Weights(workload_with(D), zero_w1=True)
+    h = bf16_values(np.random.default_rng(3).standard_normal((1, 128)))
+    w1 = torch.stack([rt.upload_bf16(Wt[f"head{k}.w1"]) for k in (1, 2)])
+    w2 = torch.stack([rt.upload_bf16(Wt[f"head{k}.w2"]) for k in (1, 2)])
+    z = torch.zeros(1, 2, 512, device=DEV)
+    ids = torch.zeros(1, 2, 4, device=DEV, dtype=torch.int32)
+    vals = torch.zeros(1, 2, 4, device=DEV)
+    ws = workspace(D, 1, 1, 64)
+    tv.medusa_heads(dims_struct(D), 1, 2, 4, torch.from_numpy(h.astype(np.float32)).to(DEV).to(
+        torch.bfloat16), w1, w2, None, None, ids, vals, None, z, ws)
+    torch.cuda.synchronize()
+    lm = h[0] @ Wt["lm_head"].astype(np.float64).T
+    zg = z.cpu().numpy()
+    assert np.array_equal(zg[0, 0], zg[0, 1])
+    assert np.abs(zg[0, 0] - lm).max() <= TOL
+
+
+# ---------------------------------------------------------------- accept
+
+def _accept_case(rng, B, T, V, depth, topk, bias):
+    paths = random_trees(rng, B, T - 1, depth, topk)
+    trees = [otree.compile_tree(p) for p in paths]
+    toks = []
+    logits = rng.standard_normal((B, T, V)).astype(np.float32) * 2
+    for b, t in enumerate(trees):
+        top = np.stack([rng.permutation(V)[:topk] for _ in range(depth)])
+        tok = otree.fill_tokens(t, int(rng.integers(V)), top)
+        toks.append(tok)
+        for v in range(T):      # make some children the argmax of their parent
+            if t.children[v] and rng.random() < bias:
+                c = t.children[v][rng.integers(len(t.children[v]))]
+                logits[b, v, tok[c]] = logits[b, v].max() + rng.random() + 0.1
+    return paths, trees, np.stack(toks), logits
+
+
+@pytest.mark.parametrize("mode,root", [("greedy", "argmax"), ("typical", "argmax"),
+                                       ("typical", "sample"), ("greedy", "sample")])
+@pytest.mark.parametrize("B,T", [(1, 64), (4, 64), (1, 256), (2, 15)])
+def test_accept_matches_oracle_given_gpu_logits(mode, root, B, T):
+    _flush(f"accept {mode}/{root} B={B} T={T}")
+    rng = np.random.default_rng(T * 7 + B + len(mode) + len(root))
+    V, depth, topk, d = 1024, 5, 6, 64
+    paths, trees, toks, logits = _accept_case(rng, B, T, V, depth, topk, 0.7)
+    dt = device_tree(paths, topk)
+    temp, eps, delta = 0.7, 0.09, 0.3
+    p = tv.AcceptParams(mode=tv.ACCEPT_GREEDY if mode == "greedy" else tv.ACCEPT_TYPICAL,
+                        root_mode=tv.ROOT_ARGMAX if root == "argmax" else tv.ROOT_SAMPLE,
+                        temperature=temp, eps=eps, delta=delta)
+    u = rng.random(B)
+    hn = torch.from_numpy(rng.standard_normal((B * T, d)).astype(np.float32)).to(DEV).to(torch.bfloat16)
+    P = dt.depth + 1
+    outs = dict(accept_len=torch.zeros(B, device=DEV, dtype=torch.int32),
+                path=torch.zeros(B, P, device=DEV, dtype=torch.int32),
+                best=torch.zeros(B, device=DEV, dtype=torch.int32),
+                next_root=torch.zeros(B, device=DEV, dtype=torch.int32),
+                emitted=torch.zeros(B, P, device=DEV, dtype=torch.int32),
+                margin=torch.zeros(B, T + 1, device=DEV, dtype=torch.float64),
+                h_last=torch.zeros(B, d, device=DEV, dtype=torch.bfloat16))
+    ws = torch.zeros(1 << 20, device=DEV, dtype=torch.uint8)
+    tv.accept(B, T, V, d, torch.from_numpy(logits).to(DEV), dt.struct(), i32(toks), p,
+              torch.from_numpy(u).to(DEV) if root == "sample" else None, outs["accept_len"],
+              outs["path"], outs["best"], outs["next_root"], outs["emitted"], outs["margin"], hn,
+              outs["h_last"], ws)
+    torch.cuda.synchronize()
+    o = {k: v.cpu().numpy() for k, v in outs.items()}
+    near = 0
+    for b in range(B):
+        t, tok = trees[b], toks[b]
+        if mode == "greedy":
+            res = oa.greedy_accept(t, tok, logits[b])
+        else:
+            res = oa.typical_accept(t, tok, logits[b], temp, eps, delta)
+            m = res.margin[1:]
+            if np.any(np.abs(m[np.isfinite(m)]) <= 1e-5):
+                near += 1
+                continue
+            np.testing.assert_allclose(o["margin"][b, 1:T], res.margin[1:], rtol=1e-9, atol=1e-12)
+        assert o["accept_len"][b] == res.accept_len
+        assert o["best"][b] == res.best
+        np.testing.assert_array_equal(o["path"][b, :res.accept_len + 1], res.path)
+        assert np.all(o["path"][b, res.accept_len + 1:] == -1)
+        np.testing.assert_array_equal(o["emitted"][b, :res.accept_len + 1], tok[res.path])
+        if root == "argmax":
+            assert o["next_root"][b] == oa.argmax_lowest(logits[b, res.best])
+        else:
+            want, margin = oa.sample_root(logits[b, res.best], temp, u[b])
+            if margin > 1e-6:
+                assert o["next_root"][b] == want
+        np.testing.assert_array_equal(outs["h_last"][b].cpu().numpy(),
+                                      hn[b * T + res.best].cpu().numpy())
+    assert near <= max(1, B // 4)
+
+
+# ---------------------------------------------------------------- compaction
+
+@pytest.mark.parametrize("B", [1, 4])
+def test_kv_compact_bit_exact(B):
+    rng = np.random.default_rng(B)
+    D = configs.Dims(L=3, d=256, H=2, hd=128, F=64, V=64, K=4)
+    cap = 320
+    ns = [int(x) for x in rng.integers(1, 200, B)]
+    _, kv = fill_prefix_kv(rng, D, B, [cap] * B, cap)
+    k0 = kv.k.clone()
+    v0 = kv.v_rows().clone()
+    P = 5
+    paths = np.full((B, P), -1, np.int32)
+    lens = rng.integers(0, P, B).astype(np.int32)
+    for b in range(B):
+        nodes = np.sort(rng.choice(np.arange(1, 64), size=lens[b], replace=False))
+        paths[b, 0] = 0
+        paths[b, 1:lens[b] + 1] = nodes
+    n_dev = i32(ns)
+    tv.kv_compact(kv.struct(), i32(paths), P, i32(lens), n_dev)
+    torch.cuda.synchronize()
+    k1, v1 = kv.k.cpu(), kv.v_rows().cpu()
+    k0, v0 = k0.cpu(), v0.cpu()
+    for b in range(B):
+        n = ns[b]
+        ek, ev = k0.clone(), v0.clone()
+        src = [n + int(p) for p in paths[b, :lens[b] + 1]]
+        dst = [n + m for m in range(lens[b] + 1)]
+        ek[:, b, :, dst] = k0[:, b, :, src]
+        ev[:, b, :, dst] = v0[:, b, :, src]
+        assert torch.equal(k1[:, b], ek[:, b])
+        assert torch.equal(v1[:, b], ev[:, b])
+    np.testing.assert_array_equal(n_dev.cpu().numpy(), np.array(ns) + 1 + lens)

@@ -1,0 +1,12 @@
+"""MI355X (gfx950) Medusa tree-verify step: HIP kernels behind a C ABI.
+
+The compute lives in libmedusa_verify.so (csrc/, declared in
+include/medusa_verify.h); `_lib` is a ctypes binding with the same entry
+point names, and `runtime` allocates device buffers with PyTorch and wires
+them to the library.  Nothing here computes the method in Python.
+"""
+from . import _lib  # noqa: F401
+from ._lib import (ACCEPT_GREEDY, ACCEPT_TYPICAL, PACK_PLAIN, PACK_QKV, ROOT_ARGMAX,  # noqa: F401
+                   ROOT_SAMPLE, AcceptParams, Ctx, Dims, KV, LayerWeights, MVError, StepDesc,
+                   Tree, accept, decoder_layer, embed, kv_compact, lib, lm_head, medusa_heads,
+                   pack_weight, tree_attention, tree_compile, workspace_size)

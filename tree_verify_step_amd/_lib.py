@@ -1,0 +1,275 @@
+"""ctypes binding of libmedusa_verify.so (argument marshalling only).
+
+Every function here forwards to the C entry point of the same name (without
+the `mv_` prefix); tensors are passed as raw device pointers and the current
+torch stream as the HIP stream.  No computation happens in Python.  Loading
+fails loudly when the library has not been built: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmedusa_verify.so")
+
+MV_OK = 0
+MV_MAX_T = 256
+MV_MAX_DEPTH = 16
+MV_MAX_TOPK = 16
+MV_MAX_BATCH = 4
+ACCEPT_GREEDY, ACCEPT_TYPICAL = 0, 1
+ROOT_ARGMAX, ROOT_SAMPLE = 0, 1
+PACK_PLAIN, PACK_QKV = 0, 1
+
+EXPORTS = ("mv_strerror", "mv_last_error", "mv_tree_compile", "mv_pack_weight",
+           "mv_workspace_size", "mv_medusa_heads", "mv_tree_attention", "mv_decoder_layer",
+           "mv_embed", "mv_lm_head", "mv_accept", "mv_kv_compact", "mv_ctx_create",
+           "mv_ctx_destroy", "mv_prefill", "mv_step", "mv_step_profile")
+
+# launch-group kinds of mv_step_profile
+KINDS = ("heads", "embed_rope", "norm", "gemm_qkv", "attention", "gemm_o", "gemm_gate_up",
+         "gemm_down", "lm_head", "accept", "compact")
+
+
+class MVError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status}: {detail}")
+        self.status = status
+
+
+class Dims(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("L", "d", "H", "hd", "F", "V", "K")]
+
+
+class Tree(C.Structure):
+    _fields_ = [("T", C.c_int32), ("depth", C.c_int32), ("mask_words", C.c_int32),
+                ("parent", C.c_void_p), ("depth_of", C.c_void_p), ("rank", C.c_void_p),
+                ("anc", C.c_void_p)]
+
+
+class KV(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("L", C.c_int32), ("B", C.c_int32),
+                ("H", C.c_int32), ("hd", C.c_int32), ("cap", C.c_int32)]
+
+
+class LayerWeights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("attn_norm", "wqkv", "wo", "ffn_norm", "wgate", "wup",
+                                          "wdown")]
+
+
+class AcceptParams(C.Structure):
+    _fields_ = [("mode", C.c_int32), ("root_mode", C.c_int32), ("temperature", C.c_float),
+                ("eps", C.c_float), ("delta", C.c_float)]
+
+
+class StepDesc(C.Structure):
+    _fields_ = [("dims", Dims), ("B", C.c_int32), ("T", C.c_int32), ("s", C.c_int32),
+                ("layers", C.c_void_p), ("embed", C.c_void_p), ("final_norm", C.c_void_p),
+                ("lm_head", C.c_void_p), ("w1", C.c_void_p), ("w2", C.c_void_p),
+                ("kv", KV), ("tree", Tree), ("accept", AcceptParams),
+                ("n_prefix", C.c_void_p), ("root_tok", C.c_void_p), ("h_last", C.c_void_p),
+                ("u_draws", C.c_void_p), ("u_index", C.c_void_p), ("n_draws", C.c_int32),
+                ("tree_tok", C.c_void_p), ("logits", C.c_void_p), ("accept_len", C.c_void_p),
+                ("path", C.c_void_p), ("emitted", C.c_void_p), ("best", C.c_void_p),
+                ("head_logits", C.c_void_p), ("top_ids", C.c_void_p),
+                ("ws", C.c_void_p), ("ws_bytes", C.c_size_t)]
+
+
+_lib: Optional[C.CDLL] = None
+
+
+def lib() -> C.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -c 'import __graft_entry__ as g; g.build()'`")
+    L = C.CDLL(LIB_PATH)
+    vp, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
+    sig = {
+        "mv_strerror": (C.c_char_p, [C.c_int]),
+        "mv_last_error": (C.c_char_p, []),
+        "mv_tree_compile": (C.c_int, [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]),
+        "mv_pack_weight": (C.c_int, [vp, vp, i32, i32, i32, i32, vp]),
+        "mv_workspace_size": (C.c_int, [C.POINTER(Dims), i32, i32, i32, C.POINTER(C.c_size_t)]),
+        "mv_medusa_heads": (C.c_int, [C.POINTER(Dims), i32, i32, i32, vp, vp, vp, C.POINTER(Tree),
+                                      vp, vp, vp, vp, vp, vp, sz, vp]),
+        "mv_tree_attention": (C.c_int, [C.POINTER(Dims), i32, C.POINTER(Tree), vp, vp,
+                                        C.POINTER(KV), i32, vp, vp, sz, vp]),
+        "mv_decoder_layer": (C.c_int, [C.POINTER(Dims), i32, C.POINTER(Tree), vp,
+                                       C.POINTER(LayerWeights), C.POINTER(KV), i32, vp, vp, sz,
+                                       vp]),
+        "mv_embed": (C.c_int, [C.POINTER(Dims), i32, vp, vp, vp, vp]),
+        "mv_lm_head": (C.c_int, [C.POINTER(Dims), i32, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "mv_accept": (C.c_int, [i32, i32, i32, i32, vp, C.POINTER(Tree), vp,
+                                C.POINTER(AcceptParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                sz, vp]),
+        "mv_kv_compact": (C.c_int, [C.POINTER(KV), vp, i32, vp, vp, vp]),
+        "mv_ctx_create": (C.c_int, [C.POINTER(vp), C.POINTER(StepDesc)]),
+        "mv_ctx_destroy": (None, [vp]),
+        "mv_prefill": (C.c_int, [vp, vp, i32, vp, vp]),
+        "mv_step": (C.c_int, [vp, i32, vp]),
+        "mv_step_profile": (C.c_int, [vp, vp, vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def check(status: int, where: str) -> None:
+    if status != MV_OK:
+        L = lib()
+        raise MVError(status, where, f"{L.mv_strerror(status).decode()}: "
+                                     f"{L.mv_last_error().decode()}")
+
+
+def ptr(t) -> Optional[int]:
+    """Device (or host) address of a tensor / ndarray, None for None."""
+    if t is None:
+        return None
+    if hasattr(t, "data_ptr"):
+        return t.data_ptr()
+    return t.ctypes.data
+
+
+def stream_ptr(stream=None) -> Optional[int]:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+# ---------------------------------------------------------------------------
+# thin wrappers (same names as the C entry points, without mv_)
+# ---------------------------------------------------------------------------
+
+def tree_compile(paths: Sequence[Sequence[int]], topk: int, mask_words: Optional[int] = None):
+    """Host flattening; returns numpy (parent, depth_of, rank, anc[T][mask_words])."""
+    import numpy as np
+    n = len(paths)
+    T = n + 1
+    maxlen = max([len(p) for p in paths] + [1])
+    mw = mask_words if mask_words is not None else (T + 63) // 64
+    flat = np.zeros((max(n, 1), maxlen), dtype=np.int32)
+    lens = np.zeros(max(n, 1), dtype=np.int32)
+    for i, p in enumerate(paths):
+        flat[i, :len(p)] = p
+        lens[i] = len(p)
+    parent = np.zeros(T, np.int32)
+    depth = np.zeros(T, np.int32)
+    rank = np.zeros(T, np.int32)
+    anc = np.zeros((T, mw), np.uint64)
+    Tout = C.c_int32(0)
+    check(lib().mv_tree_compile(ptr(flat), ptr(lens), n, maxlen, topk, T, mw, ptr(parent),
+                                ptr(depth), ptr(rank), ptr(anc), C.byref(Tout)), "tree_compile")
+    assert Tout.value == T
+    return parent, depth, rank, anc
+
+
+def pack_weight(src, dst, layout: int = PACK_PLAIN, hd: int = 0, stream=None) -> None:
+    rows, cols = src.shape
+    check(lib().mv_pack_weight(ptr(src), ptr(dst), rows, cols, layout, hd, stream_ptr(stream)),
+          "pack_weight")
+
+
+def workspace_size(dims: Dims, B: int, T: int, cap: int) -> int:
+    out = C.c_size_t(0)
+    check(lib().mv_workspace_size(C.byref(dims), B, T, cap, C.byref(out)), "workspace_size")
+    return out.value
+
+
+def medusa_heads(dims: Dims, B: int, D: int, s: int, h, w1, w2, tree: Optional[Tree], root_tok,
+                 top_ids, top_vals, tree_tok, head_logits, ws, stream=None) -> None:
+    check(lib().mv_medusa_heads(C.byref(dims), B, D, s, ptr(h), ptr(w1), ptr(w2),
+                                C.byref(tree) if tree is not None else None, ptr(root_tok),
+                                ptr(top_ids), ptr(top_vals), ptr(tree_tok), ptr(head_logits),
+                                ptr(ws), ws.numel() * ws.element_size(), stream_ptr(stream)),
+          "medusa_heads")
+
+
+def tree_attention(dims: Dims, B: int, tree: Tree, n_prefix, q, kv: KV, layer: int, out, ws,
+                   stream=None) -> None:
+    check(lib().mv_tree_attention(C.byref(dims), B, C.byref(tree), ptr(n_prefix), ptr(q),
+                                  C.byref(kv), layer, ptr(out), ptr(ws),
+                                  ws.numel() * ws.element_size(), stream_ptr(stream)),
+          "tree_attention")
+
+
+def decoder_layer(dims: Dims, B: int, tree: Tree, n_prefix, w: LayerWeights, kv: KV, layer: int,
+                  x, ws, stream=None) -> None:
+    check(lib().mv_decoder_layer(C.byref(dims), B, C.byref(tree), ptr(n_prefix), C.byref(w),
+                                 C.byref(kv), layer, ptr(x), ptr(ws),
+                                 ws.numel() * ws.element_size(), stream_ptr(stream)),
+          "decoder_layer")
+
+
+def embed(dims: Dims, M: int, tokens, table, x, stream=None) -> None:
+    check(lib().mv_embed(C.byref(dims), M, ptr(tokens), ptr(table), ptr(x), stream_ptr(stream)),
+          "embed")
+
+
+def lm_head(dims: Dims, M: int, x, final_norm, lm, logits, hn_rows, ws, stream=None) -> None:
+    check(lib().mv_lm_head(C.byref(dims), M, ptr(x), ptr(final_norm), ptr(lm), ptr(logits),
+                           ptr(hn_rows), ptr(ws), ws.numel() * ws.element_size(),
+                           stream_ptr(stream)), "lm_head")
+
+
+def accept(B: int, T: int, V: int, d: int, logits, tree: Tree, tree_tok, p: AcceptParams, u,
+           accept_len, path, best, next_root, emitted=None, margin=None, hn=None, h_last=None,
+           ws=None, stream=None) -> None:
+    check(lib().mv_accept(B, T, V, d, ptr(logits), C.byref(tree), ptr(tree_tok), C.byref(p),
+                          ptr(u), ptr(accept_len), ptr(path), ptr(best), ptr(next_root),
+                          ptr(emitted), ptr(margin), ptr(hn), ptr(h_last), ptr(ws),
+                          ws.numel() * ws.element_size(), stream_ptr(stream)), "accept")
+
+
+def kv_compact(kv: KV, path, path_stride: int, accept_len, n_prefix, stream=None) -> None:
+    check(lib().mv_kv_compact(C.byref(kv), ptr(path), path_stride, ptr(accept_len),
+                              ptr(n_prefix), stream_ptr(stream)), "kv_compact")
+
+
+class Ctx:
+    """Owning handle of an mv_ctx (whole-step driver)."""
+
+    def __init__(self, desc: StepDesc, layers_array):
+        self._layers = layers_array        # keep the host array alive for the call
+        self.desc = desc
+        h = C.c_void_p()
+        check(lib().mv_ctx_create(C.byref(h), C.byref(desc)), "ctx_create")
+        self.h = h
+
+    def prefill(self, ids, n_ids, stream=None) -> None:
+        import numpy as np
+        n = np.ascontiguousarray(n_ids, dtype=np.int32)
+        check(lib().mv_prefill(self.h, ptr(ids), ids.shape[1], ptr(n), stream_ptr(stream)),
+              "prefill")
+
+    def step(self, graph: bool = True, stream=None) -> None:
+        check(lib().mv_step(self.h, 1 if graph else 0, stream_ptr(stream)), "step")
+
+    def step_profile(self, stream=None):
+        """One eager step timed per launch-group kind with HIP events on the
+        library's stream; returns {kind: (milliseconds, launch groups)}."""
+        import numpy as np
+        ms = np.zeros(len(KINDS), np.float32)
+        cnt = np.zeros(len(KINDS), np.int32)
+        check(lib().mv_step_profile(self.h, ptr(ms), ptr(cnt), stream_ptr(stream)),
+              "step_profile")
+        return {k: (float(ms[i]), int(cnt[i])) for i, k in enumerate(KINDS)}
+
+    def close(self) -> None:
+        if self.h:
+            lib().mv_ctx_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,148 @@
+// Shared device/host helpers of the gfx950 Medusa tree-verify library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "medusa_verify.h"
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16;
+
+#define MV_WAVE 64
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32.  bf16 is kept as raw 16-bit patterns in memory.  Widening is
+// exact (append 16 zero bits); narrowing rounds to nearest, ties to even
+// (the hardware v_cvt_pk_bf16_f32 conversion on gfx950).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(u16 b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+__device__ __forceinline__ u16 f32_to_bf16(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(u16, h);
+}
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// ---------------------------------------------------------------------------
+// Fragment-packed bf16 matrices.
+//
+// A matrix [R][C] (R % 16 == 0, C % 32 == 0) is stored as R/16 x C/32 blocks
+// of 16 rows x 32 columns, blocks ordered row-block-major; inside a block,
+// lane l (0..63) owns row (l % 16) and columns 8*(l/16) .. 8*(l/16)+7, and
+// the 64 lanes' 16-byte pieces are consecutive.  This is the operand layout of
+// v_mfma_f32_16x16x32_bf16 for both A (rows = M) and B (rows = N), so one
+// wave reads one 1 KiB block with one fully coalesced 16-byte load per lane.
+// ---------------------------------------------------------------------------
+__host__ __device__ __forceinline__ size_t packed_index(int r, int c, int C) {
+  const int rb = r >> 4, cb = c >> 5;
+  const int lane = (r & 15) + 16 * ((c & 31) >> 3);
+  return ((((size_t)rb * (C >> 5) + cb) * 64 + lane) << 3) + (c & 7);
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float warp_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ double warp_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float warp_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+
+// ---------------------------------------------------------------------------
+// Internal launchers (defined in the .hip files; called by api.cpp).
+// All return hipError_t of the launch.
+// ---------------------------------------------------------------------------
+namespace mvk {
+
+enum GemmEpi {
+  EPI_STORE = 0,     // out_f32[m][n] = y
+  EPI_ADD = 1,       // out_f32[m][n] += y          (residual stream)
+  EPI_SWIGLU = 2,    // tile = [gate cols | up cols]; out_bf16 packed h = SiLU(g) * u
+  EPI_QKV = 3,       // RoPE on q,k; q -> bf16 [M][d]; k,v -> KV cache slots
+  EPI_PARTIAL = 4,   // ws_f32[split][M][N] = y (reduced by gemm_reduce)
+};
+
+struct QkvArgs {
+  u16* q;                 // bf16 [M][d] row-major, RoPE'd
+  u16* kcache;            // bf16 [B][H][cap][hd] of this layer
+  u16* vcache;            // bf16 [B][H][cap/4][hd][4] of this layer
+  const int32_t* n_prefix;   // device [B]
+  const int32_t* depth_of;   // device [B][T]
+  const float2* rope;     // (cos, sin) [B*T][hd/2] at each row's position
+  int B, T, H, hd, cap, d;
+};
+
+struct GemmArgs {
+  const u16* A;      // packed activations [Mp][K]
+  const u16* W;      // packed weights [N][K] (for SWIGLU: gate weights)
+  const u16* W2;     // SWIGLU: packed up weights [N][K]; else unused
+  int M, Mp, N, K;   // Mp = M rounded up to 16; for SWIGLU N = F (output cols)
+  int splits;        // K splits across workgroups (EPI_PARTIAL when > 1)
+  int epi;
+  float* out_f32;    // STORE / ADD target [M][N]
+  u16* out_bf16;     // SWIGLU target (packed [Mp][N])
+  float* partial;    // PARTIAL target [splits][M][Ncols]
+  QkvArgs qkv;
+};
+
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
+hipError_t launch_gemm_reduce(const GemmArgs& g, hipStream_t s);
+hipError_t launch_pack(const u16* src, u16* dst, int R, int C, int rope_hd, int rope_rows,
+                       hipStream_t s);
+hipError_t launch_embed(const int32_t* tok, const u16* E, float* x, int M, int d,
+                        int V, hipStream_t s);
+hipError_t launch_rmsnorm_pack(const float* x, const u16* g, u16* out_packed, u16* out_rows,
+                               int M, int Mp, int d, hipStream_t s);
+hipError_t launch_rope_table(const int32_t* n_prefix, const int32_t* depth_of, float2* rope,
+                             int B, int T, int hd, hipStream_t s);
+hipError_t launch_attention(const u16* q, const u16* kc, const u16* vc, const int32_t* n_prefix,
+                            const uint64_t* anc, int B, int T, int H, int hd, int cap, int mw,
+                            int nsplit, float* part_o, float* part_ml, hipStream_t s);
+hipError_t launch_attn_combine(const float* part_o, const float* part_ml, u16* out, int packed,
+                               int B, int T, int H, int hd, int nsplit, int Mp, hipStream_t s);
+hipError_t launch_heads_w1(const u16* h, const u16* w1, float* u, int B, int D, int d,
+                           hipStream_t s);
+hipError_t launch_heads_w2(const float* u, const u16* w2, float* z, int B, int D, int d, int V,
+                           hipStream_t s);
+hipError_t launch_topk(const float* z, int rows, int V, int s_top, int32_t* ids, float* vals,
+                       hipStream_t s);
+hipError_t launch_tree_fill(const int32_t* top_ids, const int32_t* root, const int32_t* depth_of,
+                            const int32_t* rank, int32_t* tok, int B, int T, int D, int s_top,
+                            hipStream_t s);
+hipError_t launch_row_stats(const float* logits, int rows, int V, int mode, float temperature,
+                            int32_t* argmax, double* stats, hipStream_t s);
+hipError_t launch_accept_finish(const float* logits, const int32_t* argmax, const double* stats,
+                                const int32_t* parent, const int32_t* depth_of,
+                                const int32_t* tok, int B, int T, int V, int depth, int mode,
+                                int root_mode, float temperature, float eps, float delta,
+                                const double* u, const int32_t* u_index, int u_stride,
+                                int32_t* accept_len, int32_t* path, int32_t* best,
+                                int32_t* next_root, int32_t* emitted, double* margin,
+                                const u16* hn, u16* h_last, int d, hipStream_t s);
+hipError_t launch_compact(u16* kc, u16* vc, int L, int B, int H, int hd, int cap,
+                          const int32_t* path, int path_stride, const int32_t* accept_len,
+                          const int32_t* n_prefix, hipStream_t s);
+hipError_t launch_advance(int32_t* n_prefix, const int32_t* accept_len, int B,
+                          int32_t* counter, hipStream_t s);
+hipError_t launch_copy_rows_bf16(const u16* src_packed, u16* dst, const int32_t* row_of_b,
+                                 int B, int d, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
+
+}  // namespace mvk
