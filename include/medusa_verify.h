@@ -30,12 +30,16 @@
  *
  * Data layouts:
  *  - Rows of the verify pass: m = b * T + v for sequence b and tree node v.
- *  - Fragment-packed bf16 matrix [R][C] (R % 16 == 0, C % 32 == 0): blocks of
- *    16 rows x 32 columns in row-block-major order, each block 64 pieces of 8
- *    consecutive columns, piece l = row (l % 16), columns 8 * (l / 16) ..;
- *    element (r, c) sits at
- *      ((((r/16) * (C/32) + c/32) * 64 + (r%16) + 16*((c%32)/8)) * 8 + c%8.
+ *  - Fragment-packed bf16 weight [R][C] (R % 16 == 0, C % 32 == 0): blocks of
+ *    16 rows x 32 columns in k-block-major order (all row blocks of column
+ *    block 0 first), each block 64 pieces of 8 consecutive columns, piece
+ *    l = row (l % 16), columns 8 * (l / 16) ..; element (r, c) sits at
+ *      ((((c/32) * (R/16) + r/16) * 64 + (r%16) + 16*((c%32)/8)) * 8 + c%8.
  *    Weights of the backbone GEMMs are passed packed (see mv_pack_weight).
+ *  - Workspace: caller-owned device memory of mv_workspace_size() bytes,
+ *    zero-filled before its first use; the library keeps its internal
+ *    arrival counters at zero between calls.  Calls sharing a workspace must
+ *    be ordered on one stream.
  *  - KV cache (one buffer for K, one for V, all layers):
  *      K: bf16 [L][B][H][cap][hd]             (slot-major rows)
  *      V: bf16 [L][B][H][cap/4][hd][4]        (4 consecutive slots interleaved
@@ -134,9 +138,9 @@ typedef struct {
 typedef struct {
   int32_t mode;
   int32_t root_mode;
-  float temperature;
-  float eps;
-  float delta;
+  double temperature;
+  double eps;
+  double delta;
 } mv_accept_params;
 
 /* ---- errors -------------------------------------------------------------- */
@@ -149,7 +153,9 @@ MV_API const char* mv_last_error(void);              /* thread-local detail */
  * paper digest, Method 2-4; the released sparse trees are such path lists).
  * paths: host int32 [n_paths][max_len] row-major, path p = paths[p][0 ..
  * path_len[p]-1] (ranks i_1..i_k: head j's i_j-th candidate).  The list must
- * be prefix-closed, duplicate-free, with 1 <= len <= MV_MAX_DEPTH and
+ * be prefix-closed, duplicate-free, with 1 <= len < MV_MAX_T (trees deeper
+ * than MV_MAX_DEPTH, e.g. chains, are accepted by mv_tree_attention and
+ * mv_decoder_layer only) and
  * 0 <= rank < topk.  Node order: root, then by (depth, lexicographic path).
  * Outputs (host): parent, depth_of, rank [T], anc [T][mask_words], *T_out =
  * n_paths + 1; capacity `cap_nodes` >= n_paths + 1 and mask_words >=
@@ -221,11 +227,11 @@ MV_API int mv_embed(const mv_dims* dims, int32_t M, const int32_t* tokens, const
                     float* x, void* stream);
 
 /* Final RMSNorm and LM head ("head 0"): hn = RMSNorm(x) * final_norm (bf16),
- * logits = hn W_lm^T in fp32.  lm_head: fragment-packed bf16 [V][d];
- * logits: device fp32 [M][V]; hn_rows: device bf16 [M][d] row-major or NULL. */
+ * logits = hn W_lm^T in fp32.  x: device fp32 [M][d]; lm_head:
+ * fragment-packed bf16 [V][d]; logits: device fp32 [M][V]. */
 MV_API int mv_lm_head(const mv_dims* dims, int32_t M, const float* x, const void* final_norm,
-                      const void* lm_head, float* logits, void* hn_rows, void* ws,
-                      size_t ws_bytes, void* stream);
+                      const void* lm_head, float* logits, void* ws, size_t ws_bytes,
+                      void* stream);
 
 /* Acceptance (Algorithm steps 4-5): decisions per edge, accepted prefix,
  * best node v* = deepest accepted node (TYPICAL: then larger summed
@@ -236,12 +242,15 @@ MV_API int mv_lm_head(const mv_dims* dims, int32_t M, const float* x, const void
  * indices root..v*, then -1), best [B], next_root [B]; optional: emitted
  * [B][depth+1] (tokens of the path, then -1), margin double [B][T+1]
  * ((q - thr)/thr per edge for TYPICAL, [T]: |cdf - u| of the sampled root),
- * hn bf16 [B*T][d] with h_last bf16 [B][d] (h_last[b] = hn[b*T + v*]). */
+ * and, given the verify pass's fp32 residual rows x [B*T][d] and the final
+ * RMSNorm gain (bf16 [d]), the carried hidden state h_last bf16 [B][d] =
+ * RMSNorm(x[b*T + v*]) * final_norm (the input of the next step's heads). */
 MV_API int mv_accept(int32_t B, int32_t T, int32_t V, int32_t d, const float* logits,
                      const mv_tree* tree, const int32_t* tree_tok, const mv_accept_params* p,
                      const double* u, int32_t* accept_len, int32_t* path, int32_t* best,
-                     int32_t* next_root, int32_t* emitted, double* margin, const void* hn,
-                     void* h_last, void* ws, size_t ws_bytes, void* stream);
+                     int32_t* next_root, int32_t* emitted, double* margin, const float* x,
+                     const void* final_norm, void* h_last, void* ws, size_t ws_bytes,
+                     void* stream);
 
 /* KV compaction (Algorithm step 6; Medusa paper digest, Pitfalls): for every
  * layer, sequence b and m = 0..accept_len[b]: slot n[b] + m <- slot n[b] +

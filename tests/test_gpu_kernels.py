@@ -41,15 +41,13 @@ def test_lm_head_matches_oracle(M, d, V):
     gt = torch.from_numpy(g.astype(np.float32)).to(DEV).to(torch.bfloat16)
     Wp = rt.pack(torch.from_numpy(W.astype(np.float32)).to(DEV).to(torch.bfloat16))
     logits = torch.zeros(M, V, device=DEV)
-    hn = torch.zeros(M, d, device=DEV, dtype=torch.bfloat16)
     ws = workspace(D, (M + 255) // 256, (M + (M + 255) // 256 - 1) // ((M + 255) // 256), 64)
-    tv.lm_head(dims_struct(D), M, xt, gt, Wp, logits, hn, ws)
+    tv.lm_head(dims_struct(D), M, xt, gt, Wp, logits, ws)
     torch.cuda.synchronize()
     hn_ref = om.rmsnorm(x.astype(np.float64), g)
     want = hn_ref @ W.T
     got = logits.cpu().numpy()
     assert np.abs(got - want).max() <= TOL
-    assert np.abs(hn.float().cpu().numpy() - hn_ref).max() <= 2e-2
 
 
 # ---------------------------------------------------------------- tree attention
@@ -211,7 +209,8 @@ def test_medusa_heads_match_oracle(B, d, V, K, s):
     Wt = synth.Weights(w)
     rng = np.random.default_rng(d + V)
     h = bf16_values(rng.standard_normal((B, d)))
-    paths = [synth.sparse_tree_paths(7 + b, 20, K, s) for b in range(B)]
+    n_nodes = min(20, sum(s ** k for k in range(1, K + 1)))
+    paths = [synth.sparse_tree_paths(7 + b, n_nodes, K, s) for b in range(B)]
     dt = device_tree(paths, s)
     w1 = torch.stack([rt.upload_bf16(Wt[f"head{k}.w1"]) for k in range(1, K + 1)])
     w2 = torch.stack([rt.upload_bf16(Wt[f"head{k}.w2"]) for k in range(1, K + 1)])
@@ -290,7 +289,8 @@ def test_accept_matches_oracle_given_gpu_logits(mode, root, B, T):
                         root_mode=tv.ROOT_ARGMAX if root == "argmax" else tv.ROOT_SAMPLE,
                         temperature=temp, eps=eps, delta=delta)
     u = rng.random(B)
-    hn = torch.from_numpy(rng.standard_normal((B * T, d)).astype(np.float32)).to(DEV).to(torch.bfloat16)
+    xres = rng.standard_normal((B * T, d)).astype(np.float32) * 3
+    gain = bf16_values(1 + 0.1 * rng.standard_normal(d))
     P = dt.depth + 1
     outs = dict(accept_len=torch.zeros(B, device=DEV, dtype=torch.int32),
                 path=torch.zeros(B, P, device=DEV, dtype=torch.int32),
@@ -302,10 +302,12 @@ def test_accept_matches_oracle_given_gpu_logits(mode, root, B, T):
     ws = torch.zeros(1 << 20, device=DEV, dtype=torch.uint8)
     tv.accept(B, T, V, d, torch.from_numpy(logits).to(DEV), dt.struct(), i32(toks), p,
               torch.from_numpy(u).to(DEV) if root == "sample" else None, outs["accept_len"],
-              outs["path"], outs["best"], outs["next_root"], outs["emitted"], outs["margin"], hn,
+              outs["path"], outs["best"], outs["next_root"], outs["emitted"], outs["margin"],
+              torch.from_numpy(xres).to(DEV),
+              torch.from_numpy(gain.astype(np.float32)).to(DEV).to(torch.bfloat16),
               outs["h_last"], ws)
     torch.cuda.synchronize()
-    o = {k: v.cpu().numpy() for k, v in outs.items()}
+    o = {k: v.cpu().numpy() for k, v in outs.items() if k != "h_last"}
     near = 0
     for b in range(B):
         t, tok = trees[b], toks[b]
@@ -329,8 +331,10 @@ def test_accept_matches_oracle_given_gpu_logits(mode, root, B, T):
             want, margin = oa.sample_root(logits[b, res.best], temp, u[b])
             if margin > 1e-6:
                 assert o["next_root"][b] == want
-        np.testing.assert_array_equal(outs["h_last"][b].cpu().numpy(),
-                                      hn[b * T + res.best].cpu().numpy())
+        # carried hidden state: final RMSNorm of the best node's residual row
+        want_h = om.rmsnorm(xres[b * T + res.best].astype(np.float64), gain)
+        got_h = outs["h_last"][b].float().cpu().numpy()
+        np.testing.assert_allclose(got_h, want_h, rtol=8e-3, atol=1e-6)
     assert near <= max(1, B // 4)
 
 

@@ -114,7 +114,7 @@ def test_calls_reject_bad_arguments_before_touching_the_gpu():
     p = tv.AcceptParams(mode=1, root_mode=0, temperature=0.0, eps=0.09, delta=0.3)
     tree3 = tv.Tree(T=15, depth=3, mask_words=1, parent=1, depth_of=1, rank=1, anc=1)
     rc = L.mv_accept(1, 15, 512, 64, 1, C.byref(tree3), 1, C.byref(p), None, 1, 1, 1, 1, None,
-                     None, None, None, 1, 1 << 20, None)
+                     None, None, None, None, 1, 1 << 20, None)
     assert rc == -1
     # compaction with an absurd path stride
     kv = tv.KV(k=1, v=1, L=2, B=1, H=4, hd=16, cap=128)

@@ -60,8 +60,8 @@ class LayerWeights(C.Structure):
 
 
 class AcceptParams(C.Structure):
-    _fields_ = [("mode", C.c_int32), ("root_mode", C.c_int32), ("temperature", C.c_float),
-                ("eps", C.c_float), ("delta", C.c_float)]
+    _fields_ = [("mode", C.c_int32), ("root_mode", C.c_int32), ("temperature", C.c_double),
+                ("eps", C.c_double), ("delta", C.c_double)]
 
 
 class StepDesc(C.Structure):
@@ -104,10 +104,10 @@ def lib() -> C.CDLL:
                                        C.POINTER(LayerWeights), C.POINTER(KV), i32, vp, vp, sz,
                                        vp]),
         "mv_embed": (C.c_int, [C.POINTER(Dims), i32, vp, vp, vp, vp]),
-        "mv_lm_head": (C.c_int, [C.POINTER(Dims), i32, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "mv_lm_head": (C.c_int, [C.POINTER(Dims), i32, vp, vp, vp, vp, vp, sz, vp]),
         "mv_accept": (C.c_int, [i32, i32, i32, i32, vp, C.POINTER(Tree), vp,
                                 C.POINTER(AcceptParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                sz, vp]),
+                                vp, sz, vp]),
         "mv_kv_compact": (C.c_int, [C.POINTER(KV), vp, i32, vp, vp, vp]),
         "mv_ctx_create": (C.c_int, [C.POINTER(vp), C.POINTER(StepDesc)]),
         "mv_ctx_destroy": (None, [vp]),
@@ -214,19 +214,19 @@ def embed(dims: Dims, M: int, tokens, table, x, stream=None) -> None:
           "embed")
 
 
-def lm_head(dims: Dims, M: int, x, final_norm, lm, logits, hn_rows, ws, stream=None) -> None:
+def lm_head(dims: Dims, M: int, x, final_norm, lm, logits, ws, stream=None) -> None:
     check(lib().mv_lm_head(C.byref(dims), M, ptr(x), ptr(final_norm), ptr(lm), ptr(logits),
-                           ptr(hn_rows), ptr(ws), ws.numel() * ws.element_size(),
-                           stream_ptr(stream)), "lm_head")
+                           ptr(ws), ws.numel() * ws.element_size(), stream_ptr(stream)),
+          "lm_head")
 
 
 def accept(B: int, T: int, V: int, d: int, logits, tree: Tree, tree_tok, p: AcceptParams, u,
-           accept_len, path, best, next_root, emitted=None, margin=None, hn=None, h_last=None,
-           ws=None, stream=None) -> None:
+           accept_len, path, best, next_root, emitted=None, margin=None, x=None,
+           final_norm=None, h_last=None, ws=None, stream=None) -> None:
     check(lib().mv_accept(B, T, V, d, ptr(logits), C.byref(tree), ptr(tree_tok), C.byref(p),
                           ptr(u), ptr(accept_len), ptr(path), ptr(best), ptr(next_root),
-                          ptr(emitted), ptr(margin), ptr(hn), ptr(h_last), ptr(ws),
-                          ws.numel() * ws.element_size(), stream_ptr(stream)), "accept")
+                          ptr(emitted), ptr(margin), ptr(x), ptr(final_norm), ptr(h_last),
+                          ptr(ws), ws.numel() * ws.element_size(), stream_ptr(stream)), "accept")
 
 
 def kv_compact(kv: KV, path, path_stride: int, accept_len, n_prefix, stream=None) -> None:

@@ -13,6 +13,7 @@
 // emitted tokens, the next root (argmax of the best row, or inverse-CDF
 // sampling of its tempered softmax with the step's uniform draw) and the
 // carried hidden state (that row of the final-normed hidden states).
+// All decision arithmetic (thresholds, probabilities, sums) is double.
 #include "common.hpp"
 
 namespace mvk {
@@ -21,25 +22,11 @@ __device__ __forceinline__ bool better_iv(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
-__global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict__ logits, int V,
-                                                        int mode, float temperature,
-                                                        int32_t* __restrict__ amax,
-                                                        double* __restrict__ stats) {
+// Block-wide (256 threads) argmax with lowest-index ties; result in all threads.
+__device__ __forceinline__ void block_argmax(float& bv, int& bi) {
   __shared__ float rv[4];
   __shared__ int ri[4];
-  __shared__ double rd[4];
-  const int row = blockIdx.x;
-  const float* z = logits + (size_t)row * V;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  float bv = -INFINITY;
-  int bi = 0x7fffffff;
-  for (int i = threadIdx.x; i < V; i += 256) {
-    const float v = z[i];
-    if (better_iv(v, i, bv, bi)) {
-      bv = v;
-      bi = i;
-    }
-  }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     const float ov = __shfl_xor(bv, o, 64);
@@ -54,42 +41,121 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict_
     ri[wave] = bi;
   }
   __syncthreads();
-  float mx = rv[0];
-  int mi = ri[0];
+  bv = rv[0];
+  bi = ri[0];
   for (int w = 1; w < 4; ++w)
-    if (better_iv(rv[w], ri[w], mx, mi)) {
-      mx = rv[w];
-      mi = ri[w];
+    if (better_iv(rv[w], ri[w], bv, bi)) {
+      bv = rv[w];
+      bi = ri[w];
     }
-  if (threadIdx.x == 0) amax[row] = mi;
+  __syncthreads();
+}
+
+__device__ __forceinline__ double block_sum_d(double v) {
+  __shared__ double rd[4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  v = warp_sum_d(v);
+  if (lane == 0) rd[wave] = v;
+  __syncthreads();
+  v = rd[0] + rd[1] + rd[2] + rd[3];
+  __syncthreads();
+  return v;
+}
+
+// h[c] = bf16(x[c] * rsqrt(mean(x^2) + 1e-5) * g[c]) for one row of width d
+// (the final RMSNorm of the carried hidden state).  Whole workgroup calls it.
+__device__ void block_norm_row(const float* __restrict__ xr, const u16* __restrict__ g,
+                               u16* __restrict__ h, int d) {
+  __shared__ float rf[4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float sq = 0.f;
+  for (int c = threadIdx.x * 4; c < d; c += 1024) {
+    const float4 v = *reinterpret_cast<const float4*>(xr + c);
+    sq += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  sq = warp_sum(sq);
+  if (lane == 0) rf[wave] = sq;
+  __syncthreads();
+  sq = rf[0] + rf[1] + rf[2] + rf[3];
+  __syncthreads();
+  const float rs = 1.0f / sqrtf(sq / (float)d + 1e-5f);
+  for (int c = threadIdx.x; c < d; c += 256) h[c] = f32_to_bf16(xr[c] * rs * bf16_to_f32(g[c]));
+}
+
+// Rows are read as float4 (V % 4 == 0), 4 independent loads in flight per
+// thread per iteration.
+__global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict__ logits, int V,
+                                                        int mode, double temperature,
+                                                        int32_t* __restrict__ amax,
+                                                        double* __restrict__ stats) {
+  const int row = blockIdx.x;
+  const float4* z4 = reinterpret_cast<const float4*>(logits + (size_t)row * V);
+  const int V4 = V >> 2;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i0 = threadIdx.x; i0 < V4; i0 += 1024) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * 256;
+      v[u] = i < V4 ? z4[i] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int id = (i0 + u * 256) * 4;
+      if (better_iv(v[u].x, id, bv, bi)) { bv = v[u].x; bi = id; }
+      if (better_iv(v[u].y, id + 1, bv, bi)) { bv = v[u].y; bi = id + 1; }
+      if (better_iv(v[u].z, id + 2, bv, bi)) { bv = v[u].z; bi = id + 2; }
+      if (better_iv(v[u].w, id + 3, bv, bi)) { bv = v[u].w; bi = id + 3; }
+    }
+  }
+  block_argmax(bv, bi);
+  if (threadIdx.x == 0) amax[row] = bi;
   if (mode != MV_ACCEPT_TYPICAL) return;
 
-  const double inv_t = 1.0 / (double)temperature;
-  const double m = (double)mx;
+  const double inv_t = 1.0 / temperature;
+  const double m = (double)bv;
   double S = 0.0;
-  for (int i = threadIdx.x; i < V; i += 256) S += exp(((double)z[i] - m) * inv_t);
-  S = warp_sum_d(S);
-  __syncthreads();
-  if (lane == 0) rd[wave] = S;
-  __syncthreads();
-  S = rd[0] + rd[1] + rd[2] + rd[3];
-  double Hs = 0.0;
-  for (int i = threadIdx.x; i < V; i += 256) {
-    const double q = exp(((double)z[i] - m) * inv_t) / S;
-    Hs += q * log(q + 1e-5);
+  for (int i0 = threadIdx.x; i0 < V4; i0 += 1024) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * 256;
+      v[u] = i < V4 ? z4[i] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      S += exp(((double)v[u].x - m) * inv_t) + exp(((double)v[u].y - m) * inv_t) +
+           exp(((double)v[u].z - m) * inv_t) + exp(((double)v[u].w - m) * inv_t);
   }
-  Hs = warp_sum_d(Hs);
-  __syncthreads();
-  if (lane == 0) rd[wave] = Hs;
-  __syncthreads();
+  S = block_sum_d(S);
+  double Hs = 0.0;
+  for (int i0 = threadIdx.x; i0 < V4; i0 += 1024) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * 256;
+      v[u] = i < V4 ? z4[i] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const double q = exp(((double)e[j] - m) * inv_t) / S;
+        Hs += q * log(q + 1e-5);
+      }
+    }
+  }
+  Hs = block_sum_d(Hs);
   if (threadIdx.x == 0) {
     stats[(size_t)row * 3 + 0] = m;
     stats[(size_t)row * 3 + 1] = S;
-    stats[(size_t)row * 3 + 2] = -(rd[0] + rd[1] + rd[2] + rd[3]);
+    stats[(size_t)row * 3 + 2] = -Hs;
   }
 }
 
-hipError_t launch_row_stats(const float* logits, int rows, int V, int mode, float temperature,
+hipError_t launch_row_stats(const float* logits, int rows, int V, int mode, double temperature,
                             int32_t* argmax, double* stats, hipStream_t s) {
   hipLaunchKernelGGL(row_stats_kernel, dim3(rows), dim3(256), 0, s, logits, V, mode, temperature,
                      argmax, stats);
@@ -101,18 +167,23 @@ hipError_t launch_row_stats(const float* logits, int rows, int V, int mode, floa
 // Inverse-CDF sample of softmax(z * inv_t) over ids in increasing order:
 // the smallest id whose cumulative mass exceeds u (if rounding leaves none,
 // the largest id of nonzero mass).  Whole workgroup (256 threads) calls it;
-// each thread sums a contiguous chunk of ids, an exclusive prefix over the
-// chunk sums locates the crossing.  Writes *out (and |cdf - u| to *margin).
+// each thread sums a contiguous chunk of ids (multiple of 4), an exclusive
+// prefix over the chunk sums locates the crossing.  Writes *out (and
+// |cdf - u| to *margin).
 __device__ void block_sample(const float* __restrict__ z, int V, int amax_id, double inv_t,
                              double u, int32_t* out, double* margin) {
   __shared__ double csum[256];
   __shared__ double s_total;
   __shared__ int s_found;
   const double m = (double)z[amax_id];
-  const int chunk = (V + 255) / 256;
-  const int c0 = threadIdx.x * chunk, c1 = min(V, c0 + chunk);
+  const int chunk = (((V + 255) / 256) + 3) & ~3;
+  const int c0 = min(V, (int)threadIdx.x * chunk), c1 = min(V, c0 + chunk);
   double part = 0.0;
-  for (int i = c0; i < c1; ++i) part += exp(((double)z[i] - m) * inv_t);
+  for (int i = c0; i < c1; i += 4) {
+    const float4 v = *reinterpret_cast<const float4*>(z + i);
+    part += exp(((double)v.x - m) * inv_t) + exp(((double)v.y - m) * inv_t) +
+            exp(((double)v.z - m) * inv_t) + exp(((double)v.w - m) * inv_t);
+  }
   csum[threadIdx.x] = part;
   if (threadIdx.x == 0) s_found = 0x7fffffff;
   __syncthreads();
@@ -130,7 +201,7 @@ __device__ void block_sample(const float* __restrict__ z, int V, int amax_id, do
   double cum = csum[threadIdx.x];
   int found = -1;
   double mg = INFINITY;
-  if (cum / S <= u) {
+  if (c0 < c1 && cum / S <= u) {
     for (int i = c0; i < c1; ++i) {
       const double prev = cum / S;
       cum += exp(((double)z[i] - m) * inv_t);
@@ -156,16 +227,16 @@ __device__ void block_sample(const float* __restrict__ z, int V, int amax_id, do
   __syncthreads();
 }
 
-
 __global__ __launch_bounds__(256) void accept_finish_kernel(
     const float* __restrict__ logits, const int32_t* __restrict__ amax,
     const double* __restrict__ stats, const int32_t* __restrict__ parent,
     const int32_t* __restrict__ depth_of, const int32_t* __restrict__ tok, int T, int V, int depth,
-    int mode, int root_mode, float temperature, float eps, float delta, const double* __restrict__ u,
-    const int32_t* __restrict__ u_index, int u_stride, int32_t* __restrict__ accept_len,
-    int32_t* __restrict__ path, int32_t* __restrict__ best_out, int32_t* __restrict__ next_root,
-    int32_t* __restrict__ emitted, double* __restrict__ margin, const u16* __restrict__ hn,
-    u16* __restrict__ h_last, int d) {
+    int mode, int root_mode, double temperature, double eps, double delta,
+    const double* __restrict__ u, const int32_t* __restrict__ u_index, int u_stride,
+    int32_t* __restrict__ accept_len, int32_t* __restrict__ path, int32_t* __restrict__ best_out,
+    int32_t* __restrict__ next_root, int32_t* __restrict__ emitted, double* __restrict__ margin,
+    const float* __restrict__ x, const u16* __restrict__ final_norm, u16* __restrict__ h_last,
+    int d) {
   __shared__ unsigned char pass[MV_MAXT], ok[MV_MAXT];
   __shared__ double lq[MV_MAXT], score[MV_MAXT];
   __shared__ int s_best;
@@ -174,9 +245,9 @@ __global__ __launch_bounds__(256) void accept_finish_kernel(
   const int32_t* dep = depth_of + (size_t)b * T;
   const int32_t* tk = tok + (size_t)b * T;
   const int row0 = b * T;
-  const double inv_t = 1.0 / (double)temperature;
+  const double inv_t = 1.0 / temperature;
 
-  // per-edge decisions
+  // per-edge decisions, one node per thread
   for (int v = threadIdx.x; v < T; v += 256) {
     if (v == 0) {
       pass[0] = 1;
@@ -193,7 +264,7 @@ __global__ __launch_bounds__(256) void accept_finish_kernel(
       const double zt = (double)logits[(size_t)(row0 + p) * V + tk[v]];
       const double lqv = (zt - st[0]) * inv_t - log(st[1]);
       const double q = exp(lqv);
-      const double thr = fmin((double)eps, (double)delta * exp(-st[2]));
+      const double thr = fmin(eps, delta * exp(-st[2]));
       pass[v] = q > thr;
       lq[v] = lqv;
       if (margin) margin[(size_t)b * (T + 1) + v] = thr != 0.0 ? (q - thr) / thr : INFINITY;
@@ -214,7 +285,6 @@ __global__ __launch_bounds__(256) void accept_finish_kernel(
           best = v;
       }
     }
-    // root path
     int nodes[MV_MAX_DEPTH + 1];
     int cnt = 0;
     for (int v = best; v >= 0 && cnt <= MV_MAX_DEPTH; v = (v == 0 ? -1 : par[v])) nodes[cnt++] = v;
@@ -232,12 +302,7 @@ __global__ __launch_bounds__(256) void accept_finish_kernel(
   const int best = s_best;
   const int brow = row0 + best;
 
-  // carried hidden state
-  if (hn && h_last) {
-    for (int c = threadIdx.x; c < d; c += 256) h_last[(size_t)b * d + c] = hn[(size_t)brow * d + c];
-  }
-
-  // next root
+  if (x && h_last) block_norm_row(x + (size_t)brow * d, final_norm, h_last + (size_t)b * d, d);
   if (root_mode == MV_ROOT_ARGMAX) {
     if (threadIdx.x == 0) next_root[b] = amax[brow];
     return;
@@ -247,49 +312,52 @@ __global__ __launch_bounds__(256) void accept_finish_kernel(
                margin ? margin + (size_t)b * (T + 1) + T : nullptr);
 }
 
+hipError_t launch_accept_finish(const float* logits, const int32_t* argmax, const double* stats,
+                                const int32_t* parent, const int32_t* depth_of,
+                                const int32_t* tok, int B, int T, int V, int depth, int mode,
+                                int root_mode, double temperature, double eps, double delta,
+                                const double* u, const int32_t* u_index, int u_stride,
+                                int32_t* accept_len, int32_t* path, int32_t* best,
+                                int32_t* next_root, int32_t* emitted, double* margin,
+                                const float* x, const u16* final_norm, u16* h_last, int d,
+                                hipStream_t s) {
+  hipLaunchKernelGGL(accept_finish_kernel, dim3(B), dim3(256), 0, s, logits, argmax, stats,
+                     parent, depth_of, tok, T, V, depth, mode, root_mode, temperature, eps, delta,
+                     u, u_index, u_stride, accept_len, path, best, next_root, emitted, margin, x,
+                     final_norm, h_last, d);
+  return hipGetLastError();
+}
+
 // Prefill: after a chain chunk, sequence b's last real row (cnt[b] - 1)
-// supplies h_last and the first root; n[b] += cnt[b].  cnt[b] == 0: nothing.
+// supplies h_last (its final RMSNorm) and the first root; n[b] += cnt[b].
+// cnt[b] == 0: nothing.
 __global__ __launch_bounds__(256) void prefill_select_kernel(
     const float* __restrict__ logits, const int32_t* __restrict__ amax, const int32_t* __restrict__ cnt,
-    int T, int V, int root_mode, float temperature, const double* __restrict__ u, int u_stride,
-    int32_t* __restrict__ root, int32_t* __restrict__ n_prefix, const u16* __restrict__ hn,
-    u16* __restrict__ h_last, int d) {
+    int T, int V, int root_mode, double temperature, const double* __restrict__ u,
+    int32_t* __restrict__ root, int32_t* __restrict__ n_prefix, const float* __restrict__ x,
+    const u16* __restrict__ final_norm, u16* __restrict__ h_last, int d) {
   const int b = blockIdx.x;
   const int c = cnt[b];
   if (c <= 0) return;
   const int row = b * T + c - 1;
-  for (int i = threadIdx.x; i < d; i += 256) h_last[(size_t)b * d + i] = hn[(size_t)row * d + i];
+  block_norm_row(x + (size_t)row * d, final_norm, h_last + (size_t)b * d, d);
   if (root_mode == MV_ROOT_ARGMAX) {
     if (threadIdx.x == 0) root[b] = amax[row];
   } else {
-    block_sample(logits + (size_t)row * V, V, amax[row], 1.0 / (double)temperature,
-                 u[(size_t)b], root + b, nullptr);
+    block_sample(logits + (size_t)row * V, V, amax[row], 1.0 / temperature, u[(size_t)b], root + b,
+                 nullptr);
   }
   __syncthreads();
   if (threadIdx.x == 0) n_prefix[b] += c;
 }
 
 hipError_t launch_prefill_select(const float* logits, const int32_t* amax, const int32_t* cnt,
-                                 int B, int T, int V, int root_mode, float temperature,
-                                 const double* u, int32_t* root, int32_t* n_prefix, const u16* hn,
-                                 u16* h_last, int d, hipStream_t s) {
+                                 int B, int T, int V, int root_mode, double temperature,
+                                 const double* u, int32_t* root, int32_t* n_prefix,
+                                 const float* x, const u16* final_norm, u16* h_last, int d,
+                                 hipStream_t s) {
   hipLaunchKernelGGL(prefill_select_kernel, dim3(B), dim3(256), 0, s, logits, amax, cnt, T, V,
-                     root_mode, temperature, u, 0, root, n_prefix, hn, h_last, d);
-  return hipGetLastError();
-}
-
-hipError_t launch_accept_finish(const float* logits, const int32_t* argmax, const double* stats,
-                                const int32_t* parent, const int32_t* depth_of,
-                                const int32_t* tok, int B, int T, int V, int depth, int mode,
-                                int root_mode, float temperature, float eps, float delta,
-                                const double* u, const int32_t* u_index, int u_stride,
-                                int32_t* accept_len, int32_t* path, int32_t* best,
-                                int32_t* next_root, int32_t* emitted, double* margin,
-                                const u16* hn, u16* h_last, int d, hipStream_t s) {
-  hipLaunchKernelGGL(accept_finish_kernel, dim3(B), dim3(256), 0, s, logits, argmax, stats,
-                     parent, depth_of, tok, T, V, depth, mode, root_mode, temperature, eps, delta,
-                     u, u_index, u_stride, accept_len, path, best, next_root, emitted, margin, hn,
-                     h_last, d);
+                     root_mode, temperature, u, root, n_prefix, x, final_norm, h_last, d);
   return hipGetLastError();
 }
 

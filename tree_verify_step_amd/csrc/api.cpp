@@ -1,6 +1,11 @@
 // C ABI of the Medusa tree-verify library: argument validation, workspace
 // carving, kernel sequencing for each operation, and the step driver that
 // captures one whole decoding step into a hipGraph.
+//
+// A decoder layer is eight launches: RMSNorm into the packed operand, QKV
+// GEMM (RoPE + KV-cache write epilogue), tree attention, range combine,
+// O-projection GEMM (residual add), RMSNorm, gate/up GEMM (SwiGLU epilogue),
+// down GEMM (residual add).  Split-K partials are reduced inside the GEMMs.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -11,13 +16,6 @@
 #include "common.hpp"
 #include "internal.hpp"
 #include "medusa_verify.h"
-
-namespace mvk {
-hipError_t launch_prefill_select(const float* logits, const int32_t* amax, const int32_t* cnt,
-                                 int B, int T, int V, int root_mode, float temperature,
-                                 const double* u, int32_t* root, int32_t* n_prefix, const u16* hn,
-                                 u16* h_last, int d, hipStream_t s);
-}
 
 namespace mv {
 
@@ -45,13 +43,16 @@ static int check_dims(const mv_dims* D) {
   if (D->hd != 16 && D->hd != 32 && D->hd != 64 && D->hd != 128)
     return fail(MV_EUNSUPPORTED, "head dim %d not in {16,32,64,128}", D->hd);
   if (D->K > MV_MAX_DEPTH) return fail(MV_EUNSUPPORTED, "K=%d > %d", D->K, MV_MAX_DEPTH);
+  if (D->d > 8192) return fail(MV_EUNSUPPORTED, "d=%d > 8192", D->d);
   return MV_OK;
 }
 
-static int check_tree(const mv_tree* t, bool need_anc) {
+// max_depth: MV_MAX_DEPTH where a depth indexes heads or paths; the forward
+// itself (attention, decoder layer) takes any depth < T (e.g. chain trees).
+static int check_tree(const mv_tree* t, bool need_anc, int max_depth = MV_MAX_DEPTH) {
   if (!t) return fail(MV_EINVAL, "tree is NULL");
   if (t->T < 1 || t->T > MV_MAX_T) return fail(MV_EUNSUPPORTED, "tree T=%d outside [1,%d]", t->T, MV_MAX_T);
-  if (t->depth < 0 || t->depth > MV_MAX_DEPTH || t->depth > t->T - 1)
+  if (t->depth < 0 || t->depth > max_depth || t->depth > t->T - 1)
     return fail(MV_ETREE, "tree depth %d invalid for T=%d", t->depth, t->T);
   if (t->mask_words != (t->T + 63) / 64)
     return fail(MV_EINVAL, "mask_words %d != ceil(T/64)", t->mask_words);
@@ -74,44 +75,55 @@ static int attn_nsplit(int B, int H, int T) {
   return std::max(1, std::min(ns, 31));
 }
 
-static int gemm_splits(int ntiles, int K) {
-  const int KB = K / 32;
-  int s = (320 + ntiles - 1) / ntiles;
-  s = std::min(s, std::max(1, KB / 8));
-  return std::max(1, std::min(s, 16));
+enum GemmKind { G_QKV = 0, G_O, G_GU, G_DOWN, G_LM, G_KINDS };
+
+struct GemmCfg {
+  int nbw, splits;
+};
+
+// Tile width and K splits per GEMM (measured on MI355X at M = 64 for the
+// 7B shapes); the split count shrinks when several M tiles already multiply
+// the grid and is capped so each split keeps >= 8 k-blocks.
+static GemmCfg gemm_cfg(const mv_dims& D, int kind, int Mp) {
+  static const GemmCfg base[G_KINDS] = {{4, 4}, {2, 2}, {4, 1}, {4, 4}, {4, 1}};
+  GemmCfg c = base[kind];
+  const int K = (kind == G_DOWN) ? D.F : D.d;
+  const int MB = Mp <= 16 ? 1 : (Mp <= 32 ? 2 : 4);
+  const int mtiles = (Mp / 16 + MB - 1) / MB;
+  c.splits = std::max(1, c.splits / mtiles);
+  c.splits = std::max(1, std::min(c.splits, (K / 32) / 8));
+  return c;
 }
 
-struct Gemms {
-  int qkv, o, gu, down, lm;
-};
-static Gemms gemm_plan(const mv_dims& D) {
-  Gemms g;
-  g.qkv = gemm_splits(3 * D.d / 64, D.d);
-  g.o = gemm_splits(D.d / 64, D.d);
-  g.gu = gemm_splits(D.F / 32, D.d);
-  g.down = gemm_splits(D.d / 64, D.F);
-  g.lm = 1;
-  return g;
+static size_t gemm_tile_elems(const mv_dims& D, int kind, int Mp, int* ntiles_out, int* mtiles_out) {
+  const GemmCfg c = gemm_cfg(D, kind, Mp);
+  const int MB = Mp <= 16 ? 1 : (Mp <= 32 ? 2 : 4);
+  const int mtiles = (Mp / 16 + MB - 1) / MB;
+  int N = (kind == G_QKV) ? 3 * D.d : (kind == G_GU) ? D.F : (kind == G_LM) ? D.V : D.d;
+  const int ntiles = (kind == G_GU) ? N / (c.nbw * 8) : N / (c.nbw * 16);
+  if (ntiles_out) *ntiles_out = ntiles;
+  if (mtiles_out) *mtiles_out = mtiles;
+  return (size_t)MB * 16 * c.nbw * 16;
 }
 
 struct Ws {
-  size_t x, xa, ha, q, rope, po, pml, part, hu, hz, topi, topv, amax, stats, hn, cnt, total;
+  size_t x, xa, ha, q, rope, po, pml, part, counters, hu, hz, topi, topv, tcv, tci, amax, stats,
+      cnt, total;
   int nsplit;
 };
 
 static Ws ws_layout(const mv_dims& D, int B, int T) {
   Ws w;
   const int M = B * T, Mp = round16(M);
-  const Gemms g = gemm_plan(D);
   w.nsplit = attn_nsplit(B, D.H, T);
-  size_t part = 0;
-  auto upd = [&](int s, size_t ncols) {
-    if (s > 1) part = std::max(part, (size_t)s * M * ncols * 4);
-  };
-  upd(g.qkv, 3 * (size_t)D.d);
-  upd(g.o, D.d);
-  upd(g.gu, 2 * (size_t)D.F);
-  upd(g.down, D.d);
+  size_t part = 0, max_tiles = 1;
+  for (int k = 0; k < G_KINDS; ++k) {
+    int nt, mt;
+    const size_t te = gemm_tile_elems(D, k, Mp, &nt, &mt);
+    const GemmCfg c = gemm_cfg(D, k, Mp);
+    if (c.splits > 1) part = std::max(part, (size_t)nt * mt * c.splits * te * 4);
+    max_tiles = std::max(max_tiles, (size_t)nt * mt);
+  }
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -126,13 +138,15 @@ static Ws ws_layout(const mv_dims& D, int B, int T) {
   w.po = take((size_t)(w.nsplit + 1) * M * D.d * 4);
   w.pml = take((size_t)(w.nsplit + 1) * M * D.H * 8);
   w.part = take(part);
+  w.counters = take(max_tiles * 4);
   w.hu = take((size_t)B * D.K * D.d * 4);
   w.hz = take((size_t)B * D.K * D.V * 4);
   w.topi = take((size_t)B * D.K * MV_MAX_TOPK * 4);
   w.topv = take((size_t)B * D.K * MV_MAX_TOPK * 4);
+  w.tcv = take((size_t)B * D.K * mvk::topk_waves(D.V) * MV_MAX_TOPK * 4);
+  w.tci = take((size_t)B * D.K * mvk::topk_waves(D.V) * MV_MAX_TOPK * 4);
   w.amax = take((size_t)M * 4);
   w.stats = take((size_t)M * 3 * 8);
-  w.hn = take((size_t)M * D.d * 2);
   w.cnt = take((size_t)B * 4);
   w.total = off;
   return w;
@@ -145,10 +159,17 @@ static inline T* at(void* base, size_t off) {
 
 static size_t kv_layer_elems(const mv_kv& kv) { return (size_t)kv.B * kv.H * kv.cap * kv.hd; }
 
-static hipError_t gemm(const mvk::GemmArgs& g, hipStream_t s) {
-  hipError_t e = mvk::launch_gemm(g, s);
-  if (e == hipSuccess && g.splits > 1) e = mvk::launch_gemm_reduce(g, s);
-  return e;
+static mvk::GemmArgs gemm_args(const mv_dims& D, int kind, int M, void* ws, const Ws& L) {
+  mvk::GemmArgs g{};
+  const int Mp = round16(M);
+  const GemmCfg c = gemm_cfg(D, kind, Mp);
+  g.M = M;
+  g.Mp = Mp;
+  g.nbw = c.nbw;
+  g.splits = c.splits;
+  g.partial = at<float>(ws, L.part);
+  g.counters = at<int>(ws, L.counters);
+  return g;
 }
 
 // ---------------------------------------------------------------------------
@@ -175,12 +196,6 @@ static inline void prof_end(int kind, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // Enqueue helpers (no validation)
 // ---------------------------------------------------------------------------
-static int enq_rope(const mv_dims& D, int B, const mv_tree& t, const int32_t* n_prefix, void* ws,
-                    const Ws& L, hipStream_t s) {
-  MV_HIP(mvk::launch_rope_table(n_prefix, t.depth_of, at<float2>(ws, L.rope), B, t.T, D.hd, s));
-  return MV_OK;
-}
-
 static int enq_attention(const mv_dims& D, int B, const mv_tree& t, const int32_t* n_prefix,
                          const u16* q, const mv_kv& kv, int layer, u16* out, int packed, void* ws,
                          const Ws& L, hipStream_t s) {
@@ -194,35 +209,29 @@ static int enq_attention(const mv_dims& D, int B, const mv_tree& t, const int32_
   return MV_OK;
 }
 
+// One decoder layer over the B*T rows of x (ws.rope holds the RoPE tables).
 static int enq_layer(const mv_dims& D, int B, const mv_tree& t, const int32_t* n_prefix,
                      const mv_layer_weights& w, const mv_kv& kv, int layer, float* x, void* ws,
                      const Ws& L, hipStream_t s) {
   const int M = B * t.T, Mp = round16(M);
-  const Gemms plan = gemm_plan(D);
   u16* xa = at<u16>(ws, L.xa);
   u16* ha = at<u16>(ws, L.ha);
   u16* q = at<u16>(ws, L.q);
-  float* part = at<float>(ws, L.part);
   const size_t le = kv_layer_elems(kv);
 
   prof_begin(s);
-  MV_HIP(mvk::launch_rmsnorm_pack(x, static_cast<const u16*>(w.attn_norm), xa, nullptr, M, Mp, D.d, s));
+  MV_HIP(mvk::launch_rmsnorm_pack(x, static_cast<const u16*>(w.attn_norm), xa, M, Mp, D.d, s));
   prof_end(MV_K_NORM, s);
-  mvk::GemmArgs g{};
+  mvk::GemmArgs g = gemm_args(D, G_QKV, M, ws, L);
   g.A = xa;
   g.W = static_cast<const u16*>(w.wqkv);
-  g.M = M;
-  g.Mp = Mp;
   g.N = 3 * D.d;
   g.K = D.d;
-  g.splits = plan.qkv;
   g.epi = mvk::EPI_QKV;
-  g.partial = part;
   g.qkv.q = q;
   g.qkv.kcache = static_cast<u16*>(kv.k) + (size_t)layer * le;
   g.qkv.vcache = static_cast<u16*>(kv.v) + (size_t)layer * le;
   g.qkv.n_prefix = n_prefix;
-  g.qkv.depth_of = t.depth_of;
   g.qkv.rope = at<float2>(ws, L.rope);
   g.qkv.B = B;
   g.qkv.T = t.T;
@@ -231,7 +240,7 @@ static int enq_layer(const mv_dims& D, int B, const mv_tree& t, const int32_t* n
   g.qkv.cap = kv.cap;
   g.qkv.d = D.d;
   prof_begin(s);
-  MV_HIP(gemm(g, s));
+  MV_HIP(mvk::launch_gemm(g, s));
   prof_end(MV_K_QKV, s);
 
   prof_begin(s);
@@ -239,74 +248,59 @@ static int enq_layer(const mv_dims& D, int B, const mv_tree& t, const int32_t* n
   if (rc) return rc;
   prof_end(MV_K_ATTN, s);
 
-  mvk::GemmArgs o{};
+  mvk::GemmArgs o = gemm_args(D, G_O, M, ws, L);
   o.A = xa;
   o.W = static_cast<const u16*>(w.wo);
-  o.M = M;
-  o.Mp = Mp;
   o.N = D.d;
   o.K = D.d;
-  o.splits = plan.o;
   o.epi = mvk::EPI_ADD;
   o.out_f32 = x;
-  o.partial = part;
   prof_begin(s);
-  MV_HIP(gemm(o, s));
+  MV_HIP(mvk::launch_gemm(o, s));
   prof_end(MV_K_O, s);
 
   prof_begin(s);
-  MV_HIP(mvk::launch_rmsnorm_pack(x, static_cast<const u16*>(w.ffn_norm), xa, nullptr, M, Mp, D.d, s));
+  MV_HIP(mvk::launch_rmsnorm_pack(x, static_cast<const u16*>(w.ffn_norm), xa, M, Mp, D.d, s));
   prof_end(MV_K_NORM, s);
-  mvk::GemmArgs gu{};
+  mvk::GemmArgs gu = gemm_args(D, G_GU, M, ws, L);
   gu.A = xa;
   gu.W = static_cast<const u16*>(w.wgate);
   gu.W2 = static_cast<const u16*>(w.wup);
-  gu.M = M;
-  gu.Mp = Mp;
   gu.N = D.F;
   gu.K = D.d;
-  gu.splits = plan.gu;
   gu.epi = mvk::EPI_SWIGLU;
   gu.out_bf16 = ha;
-  gu.partial = part;
   prof_begin(s);
-  MV_HIP(gemm(gu, s));
+  MV_HIP(mvk::launch_gemm(gu, s));
   prof_end(MV_K_GATE_UP, s);
 
-  mvk::GemmArgs dn{};
+  mvk::GemmArgs dn = gemm_args(D, G_DOWN, M, ws, L);
   dn.A = ha;
   dn.W = static_cast<const u16*>(w.wdown);
-  dn.M = M;
-  dn.Mp = Mp;
   dn.N = D.d;
   dn.K = D.F;
-  dn.splits = plan.down;
   dn.epi = mvk::EPI_ADD;
   dn.out_f32 = x;
-  dn.partial = part;
   prof_begin(s);
-  MV_HIP(gemm(dn, s));
+  MV_HIP(mvk::launch_gemm(dn, s));
   prof_end(MV_K_DOWN, s);
   return MV_OK;
 }
 
+// Final RMSNorm and LM head: logits [M][V] fp32.
 static int enq_lm_head(const mv_dims& D, int M, const float* x, const void* final_norm,
-                       const void* lm, float* logits, u16* hn_rows, void* ws, const Ws& L,
-                       hipStream_t s) {
-  const int Mp = round16(M);
+                       const void* lm, float* logits, void* ws, const Ws& L, hipStream_t s) {
   u16* xa = at<u16>(ws, L.xa);
-  MV_HIP(mvk::launch_rmsnorm_pack(x, static_cast<const u16*>(final_norm), xa, hn_rows, M, Mp, D.d, s));
-  mvk::GemmArgs g{};
+  MV_HIP(mvk::launch_rmsnorm_pack(x, static_cast<const u16*>(final_norm), xa, M, round16(M), D.d,
+                                  s));
+  mvk::GemmArgs g = gemm_args(D, G_LM, M, ws, L);
   g.A = xa;
   g.W = static_cast<const u16*>(lm);
-  g.M = M;
-  g.Mp = Mp;
   g.N = D.V;
   g.K = D.d;
-  g.splits = 1;
   g.epi = mvk::EPI_STORE;
   g.out_f32 = logits;
-  MV_HIP(gemm(g, s));
+  MV_HIP(mvk::launch_gemm(g, s));
   return MV_OK;
 }
 
@@ -318,7 +312,8 @@ static int enq_heads(const mv_dims& D, int B, int Dn, int s_top, const void* h, 
   MV_HIP(mvk::launch_heads_w1(static_cast<const u16*>(h), static_cast<const u16*>(w1), u, B, Dn,
                               D.d, s));
   MV_HIP(mvk::launch_heads_w2(u, static_cast<const u16*>(w2), z, B, Dn, D.d, D.V, s));
-  MV_HIP(mvk::launch_topk(z, B * Dn, D.V, s_top, top_ids, top_vals, s));
+  MV_HIP(mvk::launch_topk(z, B * Dn, D.V, s_top, top_ids, top_vals, at<float>(ws, L.tcv),
+                          at<int>(ws, L.tci), s));
   if (tree && tree_tok)
     MV_HIP(mvk::launch_tree_fill(top_ids, root, tree->depth_of, tree->rank, tree_tok, B, tree->T,
                                  Dn, s_top, s));
@@ -329,15 +324,14 @@ static int enq_accept(int B, int T, int V, int d, const float* logits, const mv_
                       const int32_t* tok, const mv_accept_params& p, const double* u,
                       const int32_t* u_index, int u_stride, int32_t* accept_len, int32_t* path,
                       int32_t* best, int32_t* next_root, int32_t* emitted, double* margin,
-                      const void* hn, void* h_last, void* ws, const Ws& L, hipStream_t s) {
-  int32_t* amax = at<int32_t>(ws, L.amax);
-  double* stats = at<double>(ws, L.stats);
+                      const float* x, const void* final_norm, void* h_last, int32_t* amax,
+                      double* stats, hipStream_t s) {
   MV_HIP(mvk::launch_row_stats(logits, B * T, V, p.mode, p.temperature, amax, stats, s));
   MV_HIP(mvk::launch_accept_finish(logits, amax, stats, t.parent, t.depth_of, tok, B, T, V,
                                    t.depth, p.mode, p.root_mode, p.temperature, p.eps, p.delta, u,
                                    u_index, u_stride, accept_len, path, best, next_root, emitted,
-                                   margin, static_cast<const u16*>(hn), static_cast<u16*>(h_last),
-                                   d, s));
+                                   margin, x, static_cast<const u16*>(final_norm),
+                                   static_cast<u16*>(h_last), d, s));
   return MV_OK;
 }
 
@@ -427,7 +421,7 @@ MV_API int mv_medusa_heads(const mv_dims* dims, int32_t B, int32_t D, int32_t s,
     if (tree->depth > D) return fail(MV_ETREE, "tree depth %d > heads used %d", tree->depth, D);
     if (!root_tok || !tree_tok) return fail(MV_EINVAL, "root_tok and tree_tok needed with a tree");
   }
-  if ((size_t)B * dims->d * 4 > 160 * 1024) return fail(MV_EUNSUPPORTED, "B*d too large for the head GEMV");
+  if ((size_t)B * dims->d * 4 > 64 * 1024) return fail(MV_EUNSUPPORTED, "B*d too large for the head GEMV");
   if ((rc = check_ws(dims, B, tree ? tree->T : 1, ws_bytes, ws))) return rc;
   const Ws L = ws_layout(*dims, B, tree ? tree->T : 1);
   float* z = head_logits ? head_logits : at<float>(ws, L.hz);
@@ -441,7 +435,7 @@ MV_API int mv_tree_attention(const mv_dims* dims, int32_t B, const mv_tree* tree
   int rc = check_dims(dims);
   if (rc) return rc;
   if ((rc = check_batch(B))) return rc;
-  if ((rc = check_tree(tree, true))) return rc;
+  if ((rc = check_tree(tree, true, MV_MAX_T - 1))) return rc;
   if ((rc = check_kv(kv, dims, B, tree->T))) return rc;
   if (layer < 0 || layer >= dims->L) return fail(MV_EINVAL, "layer %d outside [0,%d)", layer, dims->L);
   if (!n_prefix || !q || !out) return fail(MV_EINVAL, "mv_tree_attention: NULL pointer");
@@ -457,7 +451,7 @@ MV_API int mv_decoder_layer(const mv_dims* dims, int32_t B, const mv_tree* tree,
   int rc = check_dims(dims);
   if (rc) return rc;
   if ((rc = check_batch(B))) return rc;
-  if ((rc = check_tree(tree, true))) return rc;
+  if ((rc = check_tree(tree, true, MV_MAX_T - 1))) return rc;
   if ((rc = check_kv(kv, dims, B, tree->T))) return rc;
   if (layer < 0 || layer >= dims->L) return fail(MV_EINVAL, "layer %d outside [0,%d)", layer, dims->L);
   if (!w || !w->attn_norm || !w->wqkv || !w->wo || !w->ffn_norm || !w->wgate || !w->wup ||
@@ -465,8 +459,10 @@ MV_API int mv_decoder_layer(const mv_dims* dims, int32_t B, const mv_tree* tree,
     return fail(MV_EINVAL, "mv_decoder_layer: NULL pointer");
   if ((rc = check_ws(dims, B, tree->T, ws_bytes, ws))) return rc;
   const Ws L = ws_layout(*dims, B, tree->T);
-  if ((rc = enq_rope(*dims, B, *tree, n_prefix, ws, L, (hipStream_t)stream))) return rc;
-  return enq_layer(*dims, B, *tree, n_prefix, *w, *kv, layer, x, ws, L, (hipStream_t)stream);
+  const hipStream_t s = (hipStream_t)stream;
+  MV_HIP(mvk::launch_rope_table(n_prefix, tree->depth_of, at<float2>(ws, L.rope), B, tree->T,
+                                dims->hd, s));
+  return enq_layer(*dims, B, *tree, n_prefix, *w, *kv, layer, x, ws, L, s);
 }
 
 MV_API int mv_embed(const mv_dims* dims, int32_t M, const int32_t* tokens, const void* embed,
@@ -475,31 +471,32 @@ MV_API int mv_embed(const mv_dims* dims, int32_t M, const int32_t* tokens, const
   if (rc) return rc;
   if (M < 1) return fail(MV_EINVAL, "M=%d", M);
   if (!tokens || !embed || !x) return fail(MV_EINVAL, "mv_embed: NULL pointer");
-  MV_HIP(mvk::launch_embed(tokens, static_cast<const u16*>(embed), x, M, dims->d, dims->V,
-                           (hipStream_t)stream));
+  MV_HIP(mvk::launch_embed(tokens, static_cast<const u16*>(embed), x, nullptr, M, dims->d, dims->V,
+                           nullptr, nullptr, nullptr, 1, dims->hd, (hipStream_t)stream));
   return MV_OK;
 }
 
 MV_API int mv_lm_head(const mv_dims* dims, int32_t M, const float* x, const void* final_norm,
-                      const void* lm_head, float* logits, void* hn_rows, void* ws,
-                      size_t ws_bytes, void* stream) {
+                      const void* lm_head, float* logits, void* ws, size_t ws_bytes,
+                      void* stream) {
   int rc = check_dims(dims);
   if (rc) return rc;
   if (M < 1 || M > MV_MAX_BATCH * MV_MAX_T) return fail(MV_EUNSUPPORTED, "M=%d", M);
   if (!x || !final_norm || !lm_head || !logits) return fail(MV_EINVAL, "mv_lm_head: NULL pointer");
-  // any (B, T) with B*T >= M gives a large enough xa; use B=1, T=M when M fits
+  // any (B, T) with B*T >= M gives large enough buffers; use the smallest B
   const int B = (M + MV_MAX_T - 1) / MV_MAX_T, T = (M + B - 1) / B;
   if ((rc = check_ws(dims, B, T, ws_bytes, ws))) return rc;
   const Ws L = ws_layout(*dims, B, T);
-  return enq_lm_head(*dims, M, x, final_norm, lm_head, logits, static_cast<u16*>(hn_rows), ws, L,
-                     (hipStream_t)stream);
+  const hipStream_t s = (hipStream_t)stream;
+  return enq_lm_head(*dims, M, x, final_norm, lm_head, logits, ws, L, s);
 }
 
 MV_API int mv_accept(int32_t B, int32_t T, int32_t V, int32_t d, const float* logits,
                      const mv_tree* tree, const int32_t* tree_tok, const mv_accept_params* p,
                      const double* u, int32_t* accept_len, int32_t* path, int32_t* best,
-                     int32_t* next_root, int32_t* emitted, double* margin, const void* hn,
-                     void* h_last, void* ws, size_t ws_bytes, void* stream) {
+                     int32_t* next_root, int32_t* emitted, double* margin, const float* x,
+                     const void* final_norm, void* h_last, void* ws, size_t ws_bytes,
+                     void* stream) {
   int rc = check_batch(B);
   if (rc) return rc;
   if ((rc = check_tree(tree, false))) return rc;
@@ -509,19 +506,18 @@ MV_API int mv_accept(int32_t B, int32_t T, int32_t V, int32_t d, const float* lo
     return fail(MV_EINVAL, "mv_accept: NULL pointer");
   if (p->mode != MV_ACCEPT_GREEDY && p->mode != MV_ACCEPT_TYPICAL) return fail(MV_EINVAL, "accept mode %d", p->mode);
   if (p->root_mode != MV_ROOT_ARGMAX && p->root_mode != MV_ROOT_SAMPLE) return fail(MV_EINVAL, "root mode %d", p->root_mode);
-  if ((p->mode == MV_ACCEPT_TYPICAL || p->root_mode == MV_ROOT_SAMPLE) && !(p->temperature > 0.f))
+  if ((p->mode == MV_ACCEPT_TYPICAL || p->root_mode == MV_ROOT_SAMPLE) && !(p->temperature > 0.0))
     return fail(MV_EINVAL, "temperature must be > 0 for typical acceptance or sampled roots");
   if (p->root_mode == MV_ROOT_SAMPLE && !u) return fail(MV_EINVAL, "sampled root needs u");
-  if ((hn == nullptr) != (h_last == nullptr)) return fail(MV_EINVAL, "hn and h_last go together");
-  if (hn && (d < 1 || d % 8)) return fail(MV_EINVAL, "d=%d", d);
+  if ((x == nullptr) != (h_last == nullptr) || (x && !final_norm))
+    return fail(MV_EINVAL, "x, final_norm and h_last go together");
+  if (x && (d < 1 || d % 4)) return fail(MV_EINVAL, "d=%d", d);
   // workspace: amax [B*T] int32 + stats [B*T][3] double
   const size_t need = align256((size_t)B * T * 4) + (size_t)B * T * 24;
   if (!ws || ws_bytes < need) return fail(MV_EWORKSPACE, "workspace %zu < %zu", ws_bytes, need);
-  Ws L{};
-  L.amax = 0;
-  L.stats = align256((size_t)B * T * 4);
   return enq_accept(B, T, V, d, logits, *tree, tree_tok, *p, u, nullptr, B, accept_len, path, best,
-                    next_root, emitted, margin, hn, h_last, ws, L, (hipStream_t)stream);
+                    next_root, emitted, margin, x, final_norm, h_last, at<int32_t>(ws, 0),
+                    at<double>(ws, align256((size_t)B * T * 4)), (hipStream_t)stream);
 }
 
 MV_API int mv_kv_compact(const mv_kv* kv, const int32_t* path, int32_t path_stride,
@@ -579,19 +575,20 @@ static int enq_step(mv_ctx* c, hipStream_t s) {
   prof_end(MV_K_HEADS, s);
   float* x = at<float>(ws, L.x);
   prof_begin(s);
-  MV_HIP(mvk::launch_embed(d.tree_tok, static_cast<const u16*>(d.embed), x, M, D.d, D.V, s));
-  if ((rc = enq_rope(D, B, d.tree, d.n_prefix, ws, L, s))) return rc;
+  MV_HIP(mvk::launch_embed(d.tree_tok, static_cast<const u16*>(d.embed), x, nullptr,
+                           M, D.d, D.V, d.n_prefix, d.tree.depth_of, at<float2>(ws, L.rope), T,
+                           D.hd, s));
   prof_end(MV_K_EMBED, s);
   for (int l = 0; l < D.L; ++l)
     if ((rc = enq_layer(D, B, d.tree, d.n_prefix, c->layers[l], d.kv, l, x, ws, L, s))) return rc;
-  u16* hn = at<u16>(ws, L.hn);
   prof_begin(s);
-  if ((rc = enq_lm_head(D, M, x, d.final_norm, d.lm_head, d.logits, hn, ws, L, s))) return rc;
+  if ((rc = enq_lm_head(D, M, x, d.final_norm, d.lm_head, d.logits, ws, L, s))) return rc;
   prof_end(MV_K_LM_HEAD, s);
   prof_begin(s);
   if ((rc = enq_accept(B, T, D.V, D.d, d.logits, d.tree, d.tree_tok, d.accept, d.u_draws,
                        d.u_index, B, d.accept_len, d.path, d.best, d.root_tok, d.emitted, nullptr,
-                       hn, d.h_last, ws, L, s)))
+                       x, d.final_norm, d.h_last, at<int32_t>(ws, L.amax), at<double>(ws, L.stats),
+                       s)))
     return rc;
   prof_end(MV_K_ACCEPT, s);
   prof_begin(s);
@@ -627,11 +624,11 @@ MV_API int mv_ctx_create(mv_ctx** out, const mv_step_desc* desc) {
   const mv_accept_params& p = d.accept;
   if (p.mode != MV_ACCEPT_GREEDY && p.mode != MV_ACCEPT_TYPICAL) return fail(MV_EINVAL, "accept mode");
   if (p.root_mode != MV_ROOT_ARGMAX && p.root_mode != MV_ROOT_SAMPLE) return fail(MV_EINVAL, "root mode");
-  if ((p.mode == MV_ACCEPT_TYPICAL || p.root_mode == MV_ROOT_SAMPLE) && !(p.temperature > 0.f))
+  if ((p.mode == MV_ACCEPT_TYPICAL || p.root_mode == MV_ROOT_SAMPLE) && !(p.temperature > 0.0))
     return fail(MV_EINVAL, "temperature must be > 0");
   if (p.root_mode == MV_ROOT_SAMPLE && (!d.u_draws || !d.u_index || d.n_draws < 1))
     return fail(MV_EINVAL, "sampled roots need u_draws, u_index and n_draws");
-  if ((size_t)d.B * d.dims.d * 4 > 160 * 1024) return fail(MV_EUNSUPPORTED, "B*d too large");
+  if ((size_t)d.B * d.dims.d * 4 > 64 * 1024) return fail(MV_EUNSUPPORTED, "B*d too large");
   if ((rc = check_ws(&d.dims, d.B, d.T, d.ws_bytes, d.ws))) return rc;
 
   mv_ctx* c = new mv_ctx();
@@ -655,6 +652,9 @@ MV_API int mv_ctx_create(mv_ctx** out, const mv_step_desc* desc) {
   if (e == hipSuccess) e = hipMemcpy(c->chain, ch.data(), ch.size() * 4, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(c->chain_anc, ca.data(), ca.size() * 8, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemset(c->chunk_tok, 0, (size_t)B * T * 4);
+  // the GEMMs' arrival counters must start at zero (they reset themselves)
+  if (e == hipSuccess) e = hipMemset(at<char>(d.ws, c->L.counters), 0, c->L.hu - c->L.counters);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking);
   if (e != hipSuccess) {
     mv_ctx_destroy(c);
@@ -696,7 +696,6 @@ MV_API int mv_prefill(mv_ctx* c, const int32_t* ids, int32_t ld, const int32_t* 
                 c->chain + (size_t)2 * B * T, c->chain_anc};
   MV_HIP(mvk::launch_fill_i32(d.n_prefix, 0, B, s));
   float* x = at<float>(ws, L.x);
-  u16* hn = at<u16>(ws, L.hn);
   int32_t* cnt = at<int32_t>(ws, L.cnt);
   const int chunks = (nmax + T - 1) / T;
   std::vector<int32_t> hc(B);
@@ -710,17 +709,19 @@ MV_API int mv_prefill(mv_ctx* c, const int32_t* ids, int32_t ld, const int32_t* 
                               (size_t)m * 4, hipMemcpyDeviceToDevice, s));
     }
     MV_HIP(hipMemcpyAsync(cnt, hc.data(), (size_t)B * 4, hipMemcpyHostToDevice, s));
-    MV_HIP(mvk::launch_embed(c->chunk_tok, static_cast<const u16*>(d.embed), x, M, D.d, D.V, s));
-    if ((rc = enq_rope(D, B, chain, d.n_prefix, ws, L, s))) return rc;
+    MV_HIP(mvk::launch_embed(c->chunk_tok, static_cast<const u16*>(d.embed), x,
+                             nullptr, M, D.d, D.V, d.n_prefix, chain.depth_of,
+                             at<float2>(ws, L.rope), T, D.hd, s));
     for (int l = 0; l < D.L; ++l)
       if ((rc = enq_layer(D, B, chain, d.n_prefix, c->layers[l], d.kv, l, x, ws, L, s))) return rc;
-    if ((rc = enq_lm_head(D, M, x, d.final_norm, d.lm_head, d.logits, hn, ws, L, s))) return rc;
-    MV_HIP(mvk::launch_row_stats(d.logits, M, D.V, MV_ACCEPT_GREEDY, 1.f, at<int32_t>(ws, L.amax),
+    if ((rc = enq_lm_head(D, M, x, d.final_norm, d.lm_head, d.logits, ws, L, s))) return rc;
+    MV_HIP(mvk::launch_row_stats(d.logits, M, D.V, MV_ACCEPT_GREEDY, 1.0, at<int32_t>(ws, L.amax),
                                  at<double>(ws, L.stats), s));
     MV_HIP(mvk::launch_prefill_select(d.logits, at<int32_t>(ws, L.amax), cnt, B, T, D.V,
                                       d.accept.root_mode, d.accept.temperature, d.u_draws,
-                                      d.root_tok, d.n_prefix, hn, static_cast<u16*>(d.h_last), D.d,
-                                      s));
+                                      d.root_tok, d.n_prefix, x,
+                                      static_cast<const u16*>(d.final_norm),
+                                      static_cast<u16*>(d.h_last), D.d, s));
     // the host-side counts buffer is reused next chunk: wait for the copy
     MV_HIP(hipStreamSynchronize(s));
   }

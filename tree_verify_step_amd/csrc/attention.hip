@@ -13,13 +13,14 @@
 // from the device-side n (so one launch shape serves every n up to the
 // capacity); range `nsplit` is the tree itself.  The 4 waves each take 16
 // queries and walk the range in 64-key tiles, sharing K/V tiles through the
-// caches.  Per tile a wave computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16
-// (keys on rows, queries on columns: each lane then owns one query, so the
-// softmax statistics and the rescaling of the output are lane-local up to
-// a 4-lane reduction), updates an online softmax in the log2 domain, and
-// accumulates O^T = V^T P^T with the probabilities reused straight from the
-// S^T registers (the MFMA K index is permuted to match them).  Each range
-// writes an unnormalised partial (o, m, l); attn_combine merges the ranges.
+// caches.  Per tile a wave issues all K and V loads at once, computes
+// S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (keys on rows, queries on columns:
+// each lane then owns one query, so the softmax statistics and the rescaling
+// of the output are lane-local up to a 4-lane reduction), updates an online
+// softmax in the log2 domain, and accumulates O^T = V^T P^T with the
+// probabilities reused straight from the S^T registers (the MFMA K index is
+// permuted to match them).  Each range writes an unnormalised partial
+// (o, m, l); attn_combine merges the ranges.
 #include "common.hpp"
 
 namespace mvk {
@@ -54,6 +55,14 @@ __global__ __launch_bounds__(256) void tree_attention_kernel(
     lo = n;
     hi = n + T;
   }
+  const size_t row = ((size_t)split * B * T + (size_t)b * T + qidx) * H + h;
+  if (lo >= hi) {                    // empty range: marked by m = -inf alone
+    if (qvalid && g == 0) {
+      part_ml[row * 2 + 0] = -INFINITY;
+      part_ml[row * 2 + 1] = 0.f;
+    }
+    return;
+  }
   const size_t bh = (size_t)b * H + h;
   const u16* kbase = kc + bh * cap * HD;
   const u16* vbase = vc + bh * (size_t)(cap >> 2) * HD * 4;
@@ -63,11 +72,8 @@ __global__ __launch_bounds__(256) void tree_attention_kernel(
 #pragma unroll
   for (int db = 0; db < DB32; ++db) {
     const int dim = db * 32 + g * 8;
-    if (dim < HD) {
-      qf[db] = *reinterpret_cast<const bf16x8*>(q + ((size_t)(b * T + qrow) * d + h * HD + dim));
-    } else {
-      qf[db] = bf16x8{};
-    }
+    qf[db] = dim < HD ? *reinterpret_cast<const bf16x8*>(q + ((size_t)(b * T + qrow) * d + h * HD + dim))
+                      : bf16x8{};
   }
   uint64_t am[4] = {0, 0, 0, 0};
   if (split == nsplit) {
@@ -80,100 +86,110 @@ __global__ __launch_bounds__(256) void tree_attention_kernel(
 #pragma unroll
   for (int i = 0; i < DB16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (lo < hi) {
-    for (int s0 = lo & ~63; s0 < hi; s0 += 64) {
-      // ---- S^T = K Q^T for 64 keys (4 blocks of 16) ----
-      f32x4 st[4];
+  for (int s0 = lo & ~63; s0 < hi; s0 += 64) {
+    // ---- all loads of the tile first: K (A operand of S^T) and V (A of O^T) ----
+    bf16x8 kf[4][DB32];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        st[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int key = s0 + kb * 16 + qi;             // A operand row = key
+    for (int kb = 0; kb < 4; ++kb) {
+      const int key = s0 + kb * 16 + qi;
 #pragma unroll
-        for (int db = 0; db < DB32; ++db) {
-          const int dim = db * 32 + g * 8;
-          bf16x8 kf = bf16x8{};
-          if (dim < HD) kf = *reinterpret_cast<const bf16x8*>(kbase + (size_t)key * HD + dim);
-          st[kb] = mfma16x16x32(kf, qf[db], st[kb]);
-        }
+      for (int db = 0; db < DB32; ++db) {
+        const int dim = db * 32 + g * 8;
+        kf[kb][db] = dim < HD ? *reinterpret_cast<const bf16x8*>(kbase + (size_t)key * HD + dim)
+                              : bf16x8{};
       }
-      // ---- mask + online softmax (log2 domain); lane holds keys kb*16+4g+r ----
-      float tmax = -INFINITY;
+    }
+    // V^T operand, 32-key half kk: slot j<4 -> key kk*32 + 4g + j,
+    // j>=4 -> kk*32 + 16 + 4g + j-4 (matches the S^T register layout)
+    uint2 va[2][DB16], vb[2][DB16];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+    for (int kk = 0; kk < 2; ++kk) {
+      const int sa = s0 + kk * 32 + g * 4, sb = sa + 16;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int slot = s0 + kb * 16 + g * 4 + r;
-          bool ok = slot >= lo && slot < hi;
-          if (split == nsplit && ok) {
-            const int a = slot - n;
-            ok = (am[a >> 6] >> (a & 63)) & 1ull;
-          }
-          const float sv = ok ? st[kb][r] * scale : -INFINITY;
-          st[kb][r] = sv;
-          tmax = fmaxf(tmax, sv);
+      for (int i = 0; i < DB16; ++i) {
+        const int dim = i * 16 + qi;
+        va[kk][i] = *reinterpret_cast<const uint2*>(vbase + (((size_t)(sa >> 2) * HD + dim) << 2));
+        vb[kk][i] = *reinterpret_cast<const uint2*>(vbase + (((size_t)(sb >> 2) * HD + dim) << 2));
+      }
+    }
+    // ---- S^T = K Q^T for 64 keys (4 blocks of 16) ----
+    f32x4 st[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      st[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int db = 0; db < DB32; ++db) st[kb] = mfma16x16x32(kf[kb][db], qf[db], st[kb]);
+    }
+    // ---- mask + online softmax (log2 domain); lane holds keys kb*16+4g+r ----
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int slot = s0 + kb * 16 + g * 4 + r;
+        bool ok = slot >= lo && slot < hi;
+        if (split == nsplit && ok) {
+          const int a = slot - n;
+          ok = (am[a >> 6] >> (a & 63)) & 1ull;
         }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
-      float psum = 0.f;
+        const float sv = ok ? st[kb][r] * scale : -INFINITY;
+        st[kb][r] = sv;
+        tmax = fmaxf(tmax, sv);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+    float psum = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = (st[kb][r] == -INFINITY) ? 0.f : exp2f(st[kb][r] - m_new);
-          st[kb][r] = p;
-          psum += p;
-        }
-      psum += __shfl_xor(psum, 16, 64);
-      psum += __shfl_xor(psum, 32, 64);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
+      for (int r = 0; r < 4; ++r) {
+        const float p = (st[kb][r] == -INFINITY) ? 0.f : exp2f(st[kb][r] - m_new);
+        st[kb][r] = p;
+        psum += p;
+      }
+    psum += __shfl_xor(psum, 16, 64);
+    psum += __shfl_xor(psum, 32, 64);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
 #pragma unroll
-      for (int i = 0; i < DB16; ++i) o[i] *= alpha;
+    for (int i = 0; i < DB16; ++i) o[i] *= alpha;
 
-      // ---- O^T += V^T P^T over two 32-key halves ----
+    // ---- O^T += V^T P^T over the two 32-key halves ----
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        // B operand (P^T): slot j<4 -> key kk*32 + 4g + j, j>=4 -> kk*32 + 16 + 4g + j-4
-        bf16x8 pf;
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 pf;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          pf[j] = (__bf16)st[2 * kk][j];
-          pf[j + 4] = (__bf16)st[2 * kk + 1][j];
-        }
-        const int sa = s0 + kk * 32 + g * 4;          // first slot of each 4-group
-        const int sb = sa + 16;
+      for (int j = 0; j < 4; ++j) {
+        pf[j] = (__bf16)st[2 * kk][j];
+        pf[j + 4] = (__bf16)st[2 * kk + 1][j];
+      }
+      const int sa = s0 + kk * 32 + g * 4, sb = sa + 16;
+      // values of slots outside the range are zeroed: never-written cache
+      // memory could hold non-finite patterns and 0 * NaN would poison O
+      uint32_t keep[4];
 #pragma unroll
-        for (int i = 0; i < DB16; ++i) {
-          const int dim = i * 16 + qi;                  // A operand row = dim
-          const uint2 va = *reinterpret_cast<const uint2*>(vbase + (((size_t)(sa >> 2) * HD + dim) << 2));
-          const uint2 vb = *reinterpret_cast<const uint2*>(vbase + (((size_t)(sb >> 2) * HD + dim) << 2));
-          uint32_t w[4] = {va.x, va.y, vb.x, vb.y};
-          // zero values of slots outside the range (never-written cache memory
-          // could hold non-finite bit patterns; 0 * NaN would poison O)
+      for (int e = 0; e < 4; ++e) {
+        const int base = (e < 2 ? sa : sb) + (e & 1) * 2;
+        keep[e] = ((base >= lo && base < hi) ? 0x0000ffffu : 0u) |
+                  ((base + 1 >= lo && base + 1 < hi) ? 0xffff0000u : 0u);
+      }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int base = (e < 2 ? sa : sb) + (e & 1) * 2;
-            const uint32_t keep_lo = (base >= lo && base < hi) ? 0x0000ffffu : 0u;
-            const uint32_t keep_hi = (base + 1 >= lo && base + 1 < hi) ? 0xffff0000u : 0u;
-            w[e] &= (keep_lo | keep_hi);
-          }
-          bf16x8 vf = __builtin_bit_cast(bf16x8, (uint4){w[0], w[1], w[2], w[3]});
-          o[i] = mfma16x16x32(vf, pf, o[i]);
-        }
+      for (int i = 0; i < DB16; ++i) {
+        const uint4 w = {va[kk][i].x & keep[0], va[kk][i].y & keep[1], vb[kk][i].x & keep[2],
+                         vb[kk][i].y & keep[3]};
+        o[i] = mfma16x16x32(__builtin_bit_cast(bf16x8, w), pf, o[i]);
       }
     }
   }
 
   // ---- write the unnormalised partial of this range ----
   if (qvalid) {
-    const size_t row = ((size_t)split * B * T + (size_t)b * T + qidx) * H + h;
     float* po = part_o + row * HD;
 #pragma unroll
     for (int i = 0; i < DB16; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) po[i * 16 + g * 4 + r] = o[i][r];
+      *reinterpret_cast<float4*>(po + i * 16 + g * 4) = float4{o[i][0], o[i][1], o[i][2], o[i][3]};
     if (g == 0) {
       part_ml[row * 2 + 0] = m_run;
       part_ml[row * 2 + 1] = l_run;
@@ -181,37 +197,61 @@ __global__ __launch_bounds__(256) void tree_attention_kernel(
   }
 }
 
-// Merge the nsplit+1 range partials: o = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c.
-// One thread per (row, head, dim).  Output bf16, either row-major [B*T][d]
-// or fragment-packed [Mp][d] (the A operand of the O projection).
+// Merge the nsplit+1 range partials of one (row, head):
+//   o = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c.
+// One wave per (row, head): lane c reads range c's (m, l) (nsplit + 1 <= 64),
+// weights come from wave reductions, then each lane accumulates its dims of
+// the non-empty ranges.  Output bf16, row-major [B*T][d] or fragment-packed
+// [Mp][d] (the A operand of the O projection; pad rows written as zeros).
+template <int HD>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
                                                            u16* __restrict__ out, int packed,
-                                                           int BT, int H, int hd, int nsplit,
-                                                           int Mp) {
-  const int d = H * hd;
-  const size_t total = (size_t)Mp * d;
-  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
-    const int m = (int)(e / d), c = (int)(e % d);
-    float val = 0.f;
-    if (m < BT) {
-      const int h = c / hd, i = c % hd;
-      float M = -INFINITY;
-      for (int s = 0; s <= nsplit; ++s) M = fmaxf(M, part_ml[(((size_t)s * BT + m) * H + h) * 2]);
-      float num = 0.f, den = 0.f;
-      for (int s = 0; s <= nsplit; ++s) {
-        const size_t row = ((size_t)s * BT + m) * H + h;
-        const float ms = part_ml[row * 2];
-        if (ms == -INFINITY) continue;
-        const float w = exp2f(ms - M);
-        num += w * part_o[row * hd + i];
-        den += w * part_ml[row * 2 + 1];
-      }
-      val = num / den;
-    } else if (!packed) {
-      continue;
+                                                           int BT, int H, int nsplit, int rows) {
+  constexpr int PER = (HD + 63) / 64;            // dims per lane (hd 128 -> 2)
+  const int lane = threadIdx.x & 63;
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wid >= rows * H) return;
+  const int m = wid / H, h = wid % H;
+  const int d = H * HD;
+  float val[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) val[j] = 0.f;
+  if (m < BT) {
+    const int ns = nsplit + 1;
+    float ms = -INFINITY, ls = 0.f;
+    if (lane < ns) {
+      const size_t r = ((size_t)lane * BT + m) * H + h;
+      ms = part_ml[r * 2];
+      ls = part_ml[r * 2 + 1];
     }
-    const u16 ob = f32_to_bf16(val);
+    const float M = warp_max(ms);
+    const float w = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+    const float den = warp_sum(w * ls);
+    float acc[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+    for (int c = 0; c < ns; ++c) {
+      const float wc = __shfl(w, c, 64);
+      if (wc == 0.f) continue;
+      const float* po = part_o + (((size_t)c * BT + m) * H + h) * HD;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int i = j * 64 + lane;
+        if (i < HD) acc[j] += wc * po[i];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) val[j] = acc[j] / den;
+  } else if (!packed) {
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = j * 64 + lane;
+    if (i >= HD) continue;
+    const int c = h * HD + i;
+    const u16 ob = f32_to_bf16(val[j]);
     if (packed) out[packed_index(m, c, d)] = ob;
     else out[(size_t)m * d + c] = ob;
   }
@@ -234,11 +274,16 @@ hipError_t launch_attention(const u16* q, const u16* kc, const u16* vc, const in
 
 hipError_t launch_attn_combine(const float* part_o, const float* part_ml, u16* out, int packed,
                                int B, int T, int H, int hd, int nsplit, int Mp, hipStream_t s) {
-  const size_t total = (size_t)(packed ? Mp : B * T) * H * hd;
-  int blocks = (int)((total + 255) / 256);
-  if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(blocks), dim3(256), 0, s, part_o, part_ml, out,
-                     packed, B * T, H, hd, nsplit, Mp);
+  if (nsplit + 1 > 64) return hipErrorInvalidValue;
+  const int rows = packed ? Mp : B * T;
+  const int blocks = (rows * H + 3) / 4;
+  switch (hd) {
+    case 16: hipLaunchKernelGGL((attn_combine_kernel<16>), dim3(blocks), dim3(256), 0, s, part_o, part_ml, out, packed, B * T, H, nsplit, rows); break;
+    case 32: hipLaunchKernelGGL((attn_combine_kernel<32>), dim3(blocks), dim3(256), 0, s, part_o, part_ml, out, packed, B * T, H, nsplit, rows); break;
+    case 64: hipLaunchKernelGGL((attn_combine_kernel<64>), dim3(blocks), dim3(256), 0, s, part_o, part_ml, out, packed, B * T, H, nsplit, rows); break;
+    case 128: hipLaunchKernelGGL((attn_combine_kernel<128>), dim3(blocks), dim3(256), 0, s, part_o, part_ml, out, packed, B * T, H, nsplit, rows); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

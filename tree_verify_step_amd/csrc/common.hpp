@@ -30,17 +30,23 @@ __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w &
 // ---------------------------------------------------------------------------
 // Fragment-packed bf16 matrices.
 //
-// A matrix [R][C] (R % 16 == 0, C % 32 == 0) is stored as R/16 x C/32 blocks
-// of 16 rows x 32 columns, blocks ordered row-block-major; inside a block,
-// lane l (0..63) owns row (l % 16) and columns 8*(l/16) .. 8*(l/16)+7, and
-// the 64 lanes' 16-byte pieces are consecutive.  This is the operand layout of
-// v_mfma_f32_16x16x32_bf16 for both A (rows = M) and B (rows = N), so one
-// wave reads one 1 KiB block with one fully coalesced 16-byte load per lane.
+// A matrix [R][C] (R % 16 == 0, C % 32 == 0) is cut into blocks of 16 rows x
+// 32 columns; inside a block, lane l (0..63) owns row (l % 16) and columns
+// 8*(l/16) .. 8*(l/16)+7, and the 64 lanes' 16-byte pieces are consecutive
+// (1 KiB per block).  This is the operand layout of
+// v_mfma_f32_16x16x32_bf16 for both A (rows = M) and B (rows = N).
+//  * activations: row-block-major (block (rb, cb) at rb * C/32 + cb)
+//  * weights:     k-block-major   (block (rb, cb) at cb * R/16 + rb)
 // ---------------------------------------------------------------------------
 __host__ __device__ __forceinline__ size_t packed_index(int r, int c, int C) {
   const int rb = r >> 4, cb = c >> 5;
   const int lane = (r & 15) + 16 * ((c & 31) >> 3);
   return ((((size_t)rb * (C >> 5) + cb) * 64 + lane) << 3) + (c & 7);
+}
+__host__ __device__ __forceinline__ size_t packed_index_kmajor(int r, int c, int R) {
+  const int rb = r >> 4, cb = c >> 5;
+  const int lane = (r & 15) + 16 * ((c & 31) >> 3);
+  return ((((size_t)cb * (R >> 4) + rb) * 64 + lane) << 3) + (c & 7);
 }
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -73,10 +79,9 @@ namespace mvk {
 
 enum GemmEpi {
   EPI_STORE = 0,     // out_f32[m][n] = y
-  EPI_ADD = 1,       // out_f32[m][n] += y          (residual stream)
+  EPI_ADD = 1,       // out_f32[m][n] += y (residual stream)
   EPI_SWIGLU = 2,    // tile = [gate cols | up cols]; out_bf16 packed h = SiLU(g) * u
   EPI_QKV = 3,       // RoPE on q,k; q -> bf16 [M][d]; k,v -> KV cache slots
-  EPI_PARTIAL = 4,   // ws_f32[split][M][N] = y (reduced by gemm_reduce)
 };
 
 struct QkvArgs {
@@ -84,32 +89,34 @@ struct QkvArgs {
   u16* kcache;            // bf16 [B][H][cap][hd] of this layer
   u16* vcache;            // bf16 [B][H][cap/4][hd][4] of this layer
   const int32_t* n_prefix;   // device [B]
-  const int32_t* depth_of;   // device [B][T]
   const float2* rope;     // (cos, sin) [B*T][hd/2] at each row's position
   int B, T, H, hd, cap, d;
 };
 
 struct GemmArgs {
-  const u16* A;      // packed activations [Mp][K]
-  const u16* W;      // packed weights [N][K] (for SWIGLU: gate weights)
-  const u16* W2;     // SWIGLU: packed up weights [N][K]; else unused
-  int M, Mp, N, K;   // Mp = M rounded up to 16; for SWIGLU N = F (output cols)
-  int splits;        // K splits across workgroups (EPI_PARTIAL when > 1)
+  const u16* A;      // fragment-packed bf16 activations [Mp][K] (rows >= M zero)
+  const u16* W;      // k-major packed weights [N/16 blocks per k-block] (SWIGLU: gate)
+  const u16* W2;     // SWIGLU: up weights (same layout)
+  int M, Mp, N, K;   // SWIGLU: N = F (output columns)
+  int nbw;           // 16-column blocks per workgroup tile (2 or 4)
+  int splits;        // K splits across workgroups
   int epi;
   float* out_f32;    // STORE / ADD target [M][N]
   u16* out_bf16;     // SWIGLU target (packed [Mp][N])
-  float* partial;    // PARTIAL target [splits][M][Ncols]
+  float* partial;    // split-K partial tiles [tiles][splits][TM*TN]
+  int* counters;     // split-K arrival counters [tiles], zero between launches
   QkvArgs qkv;
 };
 
+int gemm_tiles(const GemmArgs& g, int* mtiles, int* ntiles);
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
-hipError_t launch_gemm_reduce(const GemmArgs& g, hipStream_t s);
 hipError_t launch_pack(const u16* src, u16* dst, int R, int C, int rope_hd, int rope_rows,
                        hipStream_t s);
-hipError_t launch_embed(const int32_t* tok, const u16* E, float* x, int M, int d,
-                        int V, hipStream_t s);
-hipError_t launch_rmsnorm_pack(const float* x, const u16* g, u16* out_packed, u16* out_rows,
-                               int M, int Mp, int d, hipStream_t s);
+hipError_t launch_embed(const int32_t* tok, const u16* E, float* x, float* ss, int M, int d,
+                        int V, const int32_t* n_prefix, const int32_t* depth_of, float2* rope,
+                        int T, int hd, hipStream_t s);
+hipError_t launch_rmsnorm_pack(const float* x, const u16* g, u16* out_packed, int M, int Mp,
+                               int d, hipStream_t s);
 hipError_t launch_rope_table(const int32_t* n_prefix, const int32_t* depth_of, float2* rope,
                              int B, int T, int hd, hipStream_t s);
 hipError_t launch_attention(const u16* q, const u16* kc, const u16* vc, const int32_t* n_prefix,
@@ -121,28 +128,33 @@ hipError_t launch_heads_w1(const u16* h, const u16* w1, float* u, int B, int D, 
                            hipStream_t s);
 hipError_t launch_heads_w2(const float* u, const u16* w2, float* z, int B, int D, int d, int V,
                            hipStream_t s);
+int topk_waves(int V);   // stage-1 waves per row (candidate slots = waves * s)
 hipError_t launch_topk(const float* z, int rows, int V, int s_top, int32_t* ids, float* vals,
-                       hipStream_t s);
+                       float* cand_v, int* cand_i, hipStream_t s);
 hipError_t launch_tree_fill(const int32_t* top_ids, const int32_t* root, const int32_t* depth_of,
                             const int32_t* rank, int32_t* tok, int B, int T, int D, int s_top,
                             hipStream_t s);
-hipError_t launch_row_stats(const float* logits, int rows, int V, int mode, float temperature,
+hipError_t launch_row_stats(const float* logits, int rows, int V, int mode, double temperature,
                             int32_t* argmax, double* stats, hipStream_t s);
 hipError_t launch_accept_finish(const float* logits, const int32_t* argmax, const double* stats,
                                 const int32_t* parent, const int32_t* depth_of,
                                 const int32_t* tok, int B, int T, int V, int depth, int mode,
-                                int root_mode, float temperature, float eps, float delta,
+                                int root_mode, double temperature, double eps, double delta,
                                 const double* u, const int32_t* u_index, int u_stride,
                                 int32_t* accept_len, int32_t* path, int32_t* best,
                                 int32_t* next_root, int32_t* emitted, double* margin,
-                                const u16* hn, u16* h_last, int d, hipStream_t s);
+                                const float* x, const u16* final_norm, u16* h_last, int d,
+                                hipStream_t s);
+hipError_t launch_prefill_select(const float* logits, const int32_t* amax, const int32_t* cnt,
+                                 int B, int T, int V, int root_mode, double temperature,
+                                 const double* u, int32_t* root, int32_t* n_prefix,
+                                 const float* x, const u16* final_norm, u16* h_last, int d,
+                                 hipStream_t s);
 hipError_t launch_compact(u16* kc, u16* vc, int L, int B, int H, int hd, int cap,
                           const int32_t* path, int path_stride, const int32_t* accept_len,
                           const int32_t* n_prefix, hipStream_t s);
 hipError_t launch_advance(int32_t* n_prefix, const int32_t* accept_len, int B,
                           int32_t* counter, hipStream_t s);
-hipError_t launch_copy_rows_bf16(const u16* src_packed, u16* dst, const int32_t* row_of_b,
-                                 int B, int d, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
 
 }  // namespace mvk

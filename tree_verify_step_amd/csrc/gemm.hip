@@ -1,23 +1,31 @@
-// Skinny bf16 GEMM for the tree-verify forward: Y[M][N] = X[M][K] * W[N][K]^T
+// Skinny bf16 GEMM for the tree-verify forward: Y[M][N] = A[M][K] * W[N][K]^T
 // with M = batch x tree nodes (16..256), N and K the model's widths.
 //
 // At M ~ 64 every weight byte is used 64 times, so the kernel is bound by
 // streaming W from HBM once; the MFMA units (v_mfma_f32_16x16x32_bf16) only
-// need to keep up.  Both operands are stored fragment-packed (see
-// common.hpp), so every load is a coalesced 1 KiB block per wave.
-//
-// Work decomposition: a workgroup (4 waves) owns an N tile of NBW x 16
-// columns, an M tile of MB x 16 rows and a contiguous range of the K blocks
-// (K split over `splits` workgroups).  Its 4 waves split that K range four
-// ways and stream their share with a two-stage register pipeline; the four
-// partial tiles are summed through LDS and an epilogue is applied:
-//   STORE   out = y                         (LM head logits)
-//   ADD     out += y                        (residual stream, O-proj / down)
-//   SWIGLU  h = SiLU(gate) * up -> bf16 packed activations of the down proj
-//   QKV     RoPE(q), RoPE(k) at each row's position; q -> bf16 rows;
-//           k, v -> the KV cache at slot n + node index
-//   PARTIAL fp32 partial tile per K split (reduced by gemm_reduce_kernel,
-//           which then applies STORE / ADD / SWIGLU / QKV).
+// need to keep up.  Three measured choices shape it:
+//  * Weights are fragment-packed k-block-major ([K/32][N/16][64 lanes][8]):
+//    the 1 KiB operand blocks of all columns for one 32-wide k-block are
+//    adjacent, and the 4 waves of a workgroup take interleaved k-blocks, so
+//    the whole grid sweeps a dense window of memory (as a plain streaming
+//    copy does) instead of thousands of streams at power-of-two strides that
+//    alias onto few HBM channels.
+//  * The main loop is a branch-free register pipeline (A and B fragments of
+//    D k-blocks in flight); out-of-range stages are zeroed by selects, so the
+//    compiler's wait counts stay partial.
+//  * K is split over `splits` workgroups when the N tiles alone cannot fill
+//    the chip.  Each split writes its partial tile with write-through
+//    (system-scope) stores, waits for them, and bumps the tile's arrival
+//    counter; the last workgroup to arrive reads the partials with
+//    cache-bypassing loads, sums them in split order and applies the
+//    epilogue: one kernel, a deterministic result, and no L2-wide
+//    invalidation (which would evict the other workgroups' operands).
+// Epilogues:
+//   STORE   out = y                          (LM head logits)
+//   ADD     out += y                         (residual stream: O-proj, down)
+//   SWIGLU  tile = [gate cols | up cols]; h = SiLU(g) * u -> bf16 packed
+//   QKV     RoPE on q, k at each row's position; q -> bf16 rows; k, v ->
+//           KV cache slot n + node index
 #include "common.hpp"
 
 namespace mvk {
@@ -32,15 +40,17 @@ __host__ __device__ __forceinline__ int qkv_feature(int p, int d, int hd, int P,
   return h * hd + (ee < P ? j * P + ee : hd / 2 + j * P + (ee - P));
 }
 
-struct EpiCtx {
-  const GemmArgs* g;
-};
+__device__ __forceinline__ int qkv_partner(int p, int f, int d, int hd, int P, bool perm) {
+  if (f >= 2 * d) return p;
+  if (perm) {
+    const int ee = (p % hd) % (2 * P);
+    return ee < P ? p + P : p - P;
+  }
+  const int i = (f % d) % hd;
+  return i < hd / 2 ? p + hd / 2 : p - hd / 2;
+}
 
-// Column permutation flag of the QKV tile for a given NBW.
-__host__ __device__ __forceinline__ bool qkv_perm(int NBW, int hd) { return 16 * NBW < hd; }
-
-// Apply the QKV epilogue to one output element (row m, packed column p) whose
-// value is y and whose RoPE partner value (packed column pp) is yp.
+// QKV epilogue of one element (row m, logical feature f) with RoPE partner yp.
 __device__ __forceinline__ void qkv_store(const QkvArgs& a, int m, int f, float y, float yp) {
   const int d = a.d, hd = a.hd;
   const int sec = f / d, c = f % d, h = c / hd, i = c % hd;
@@ -67,51 +77,49 @@ __device__ __forceinline__ void qkv_store(const QkvArgs& a, int m, int f, float 
   }
 }
 
-// Partner packed column of packed column p (global index) for RoPE.
-__device__ __forceinline__ int qkv_partner(int p, int f, int d, int hd, int P, bool perm) {
-  if (f >= 2 * d) return p;
-  if (perm) {
-    const int ee = (p % hd) % (2 * P);
-    return ee < P ? p + P : p - P;
-  }
-  const int i = (f % d) % hd;
-  return i < hd / 2 ? p + hd / 2 : p - hd / 2;
+// Split-K partial exchange between workgroups that may sit on different
+// XCDs (separate L2s): system-scope stores (written through to memory) and
+// 16-byte vector loads that bypass the caches (system-coherent sc0 sc1).
+// The compiler waits for every system-scope atomic load on its own, which
+// serialises them; these loads are issued as a batch and waited for once
+// (the compiler does not track inline-asm loads, hence the explicit vmcnt
+// wait).  Stores stay compiler-generated so that its hazard checks (store
+// data registers rewritten right after issue) still apply.
+__device__ __forceinline__ void store_sys(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
+__device__ __forceinline__ f32x4 load_nc16(const float* p) {
+  f32x4 v;
+  asm volatile("global_load_dwordx4 %0, %1, off sc0 sc1" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Orders a register's later uses after the preceding wait_vmem().
+__device__ __forceinline__ void after_wait(f32x4& v) { asm volatile("" : "+v"(v)); }
 
-template <int MB, int NBW, int U, int EPI>
+template <int MB, int NBW, int D, int EPI>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   constexpr int TM = MB * 16, TN = NBW * 16, LDT = TN + 1;
-  __shared__ float red[4][TM * LDT];
+  __shared__ float red[TM * LDT];
+  __shared__ int s_last;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int mt = blockIdx.x, nt = blockIdx.y, split = blockIdx.z;
   const int KB = g.K >> 5;
   const int kb_lo = (int)((long long)KB * split / g.splits);
   const int kb_hi = (int)((long long)KB * (split + 1) / g.splits);
-  const int len = kb_hi - kb_lo;
-  const int w_lo = kb_lo + len * wave / 4, w_hi = kb_lo + len * (wave + 1) / 4;
-  const int MBtot = g.Mp >> 4;
+  const int first = kb_lo + wave;
+  const int count = first < kb_hi ? (kb_hi - first + 3) / 4 : 0;
+  const int rounds = (count + D - 1) / D;
 
-  const bf16x8* A = reinterpret_cast<const bf16x8*>(g.A);
-  const bf16x8* Arow[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    int rb = mt * MB + mb;
-    rb = rb < MBtot ? rb : MBtot - 1;          // rows beyond M are ignored below
-    Arow[mb] = A + (size_t)rb * KB * 64 + lane;
-  }
-  const bf16x8* Brow[NBW];
-#pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) {
-    const u16* base = g.W;
-    int rb = nt * NBW + nb;
-    if (EPI == EPI_SWIGLU) {
-      // first half of the tile: gate rows, second half: the same up rows
-      base = nb < NBW / 2 ? g.W : g.W2;
-      rb = nt * (NBW / 2) + (nb % (NBW / 2));
-    }
-    Brow[nb] = reinterpret_cast<const bf16x8*>(base) + (size_t)rb * KB * 64 + lane;
-  }
+  // B block (kb, nb) at (kb * NBtot + nb) * 64 + lane
+  const int NBtot = g.N >> 4;
+  const bf16x8* Wg = reinterpret_cast<const bf16x8*>(g.W) + lane;
+  const bf16x8* Wu = reinterpret_cast<const bf16x8*>(g.W2) + lane;
+  const int nb0 = EPI == EPI_SWIGLU ? nt * (NBW / 2) : nt * NBW;   // gate/up share row blocks
+  // A block (rb, kb) at (rb * KB + kb) * 64 + lane (rows beyond M are zeros)
+  const bf16x8* Ap = reinterpret_cast<const bf16x8*>(g.A) + lane;
+  const int MBtot = g.Mp >> 4;
 
   f32x4 acc[MB][NBW];
 #pragma unroll
@@ -119,179 +127,195 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  bf16x8 a0[U][MB], b0[U][NBW], a1[U][MB], b1[U][NBW];
-  auto load = [&](bf16x8 (&a)[U][MB], bf16x8 (&b)[U][NBW], int kb) {
+  bf16x8 ab[D][MB], bb[D][NBW];
+  auto load = [&](int d, int j) {      // this wave's j-th k-block into stage d
+    const int k = min(first + 4 * j, kb_hi - 1);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = kb + u < w_hi ? kb + u : w_hi - 1;
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) b[u][nb] = Brow[nb][(size_t)k * 64];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) a[u][mb] = Arow[mb][(size_t)k * 64];
-    }
-  };
-  auto mma = [&](bf16x8 (&a)[U][MB], bf16x8 (&b)[U][NBW], int kb) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (kb + u < w_hi) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = mfma16x16x32(a[u][mb], b[u][nb], acc[mb][nb]);
+    for (int nb = 0; nb < NBW; ++nb) {
+      if (EPI == EPI_SWIGLU) {
+        const bf16x8* base = nb < NBW / 2 ? Wg : Wu;
+        bb[d][nb] = base[((size_t)k * NBtot + nb0 + (nb % (NBW / 2))) * 64];
+      } else {
+        bb[d][nb] = Wg[((size_t)k * NBtot + nb0 + nb) * 64];
       }
     }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int rb = min(mt * MB + mb, MBtot - 1);
+      ab[d][mb] = Ap[((size_t)rb * KB + k) * 64];
+    }
   };
 
-  int kb = w_lo;
-  if (kb < w_hi) load(a0, b0, kb);
-  for (; kb + U < w_hi; kb += 2 * U) {
-    load(a1, b1, kb + U);
-    mma(a0, b0, kb);
-    if (kb + 2 * U < w_hi) load(a0, b0, kb + 2 * U);
-    mma(a1, b1, kb + U);
+  if (count > 0) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) load(d, d);
   }
-  if (kb < w_hi) mma(a0, b0, kb);
+  for (int r = 0; r < rounds; ++r) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const bool valid = r * D + d < count;
+      bf16x8 av[MB], bv[NBW];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) av[mb] = valid ? ab[d][mb] : bf16x8{};
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) bv[nb] = bb[d][nb];
+      load(d, r * D + d + D);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = mfma16x16x32(av[mb], bv[nb], acc[mb][nb]);
+    }
+  }
 
-  // Partial tiles of the 4 waves -> LDS (row-major, padded).
-  float* my = red[wave];
+  // ---- sum the 4 waves' partial tiles in LDS (wave order: deterministic)
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb)
+        for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        my[(mb * 16 + (lane >> 4) * 4 + r) * LDT + nb * 16 + (lane & 15)] = acc[mb][nb][r];
-  __syncthreads();
+          for (int r = 0; r < 4; ++r) {
+            float* p = &red[(mb * 16 + (lane >> 4) * 4 + r) * LDT + nb * 16 + (lane & 15)];
+            *p = (w == 0 ? 0.f : *p) + acc[mb][nb][r];
+          }
+    }
+    __syncthreads();
+  }
 
+  // ---- split-K: the last workgroup of the tile sums the splits in order
+  if (g.splits > 1) {
+    constexpr int NQ = TM * TN / 4;            // float4 pieces per tile
+    constexpr int Q = (NQ + 255) / 256;        // pieces per thread
+    const int tile = mt * gridDim.y + nt;
+    float* part = g.partial + (size_t)tile * g.splits * (TM * TN);
+#pragma unroll
+    for (int i = 0; i < Q; ++i) {
+      const int e = (i * 256 + threadIdx.x) * 4, r = e / TN, c = e % TN;
+      if (e < TM * TN) {
+        const float* src = &red[r * LDT + c];
+        float* dst = part + (size_t)split * (TM * TN) + e;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) store_sys(dst + j, src[j]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);       // this thread's write-through stores are done
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int prev = __hip_atomic_fetch_add(g.counters + tile, 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+      s_last = prev == g.splits - 1;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    for (int s0 = 0; s0 < g.splits; s0 += 4) {
+      f32x4 v[4][Q];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < Q; ++i)
+          if (s0 + s < g.splits && (i * 256 + threadIdx.x) < NQ)
+            v[s][i] = load_nc16(part + (size_t)(s0 + s) * (TM * TN) + (i * 256 + threadIdx.x) * 4);
+      wait_vmem();
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < Q; ++i)
+          if (s0 + s < g.splits && (i * 256 + threadIdx.x) < NQ) after_wait(v[s][i]);
+#pragma unroll
+      for (int i = 0; i < Q; ++i) {
+        const int e = (i * 256 + threadIdx.x) * 4, r = e / TN, c = e % TN;
+        if (e >= TM * TN) continue;
+        float* dst = &red[r * LDT + c];
+        f32x4 y = s0 == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : f32x4{dst[0], dst[1], dst[2], dst[3]};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          if (s0 + s < g.splits) {
+            y += v[s][i];
+          }
+        dst[0] = y[0];
+        dst[1] = y[1];
+        dst[2] = y[2];
+        dst[3] = y[3];
+      }
+    }
+    if (threadIdx.x == 0)
+      __hip_atomic_store(g.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+  }
+
+  // ---- epilogues on the complete tile
   const int m0 = mt * TM;
   if (EPI == EPI_SWIGLU) {
     constexpr int P = TN / 2;
     for (int e = threadIdx.x; e < TM * P; e += 256) {
       const int r = e / P, c = e % P, m = m0 + r;
       if (m >= g.Mp) continue;
-      float gv = 0.f, uv = 0.f;
-      if (m < g.M) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          gv += red[w][r * LDT + c];
-          uv += red[w][r * LDT + c + P];
-        }
-      }
+      const float gv = red[r * LDT + c], uv = red[r * LDT + c + P];
       const float h = m < g.M ? silu_f(gv) * uv : 0.f;
       g.out_bf16[packed_index(m, nt * P + c, g.N)] = f32_to_bf16(h);
     }
-    return;
-  }
-  for (int e = threadIdx.x; e < TM * TN; e += 256) {
-    const int r = e / TN, c = e % TN, m = m0 + r;
-    if (m >= g.M) continue;
-    const int n = nt * TN + c;
-    float y = red[0][r * LDT + c] + red[1][r * LDT + c] + red[2][r * LDT + c] + red[3][r * LDT + c];
-    if (EPI == EPI_STORE) {
-      g.out_f32[(size_t)m * g.N + n] = y;
-    } else if (EPI == EPI_ADD) {
-      g.out_f32[(size_t)m * g.N + n] += y;
-    } else if (EPI == EPI_PARTIAL) {
-      g.partial[((size_t)split * g.M + m) * g.N + n] = y;
-    } else if (EPI == EPI_QKV) {
-      const QkvArgs& q = g.qkv;
-      const bool perm = qkv_perm(NBW, q.hd);
+  } else if (EPI == EPI_STORE || EPI == EPI_ADD) {
+    for (int e = threadIdx.x; e < TM * TN; e += 256) {
+      const int r = e / TN, c = e % TN, m = m0 + r;
+      if (m >= g.M) continue;
+      float* o = g.out_f32 + (size_t)m * g.N + nt * TN + c;
+      if (EPI == EPI_ADD) *o += red[r * LDT + c];
+      else *o = red[r * LDT + c];
+    }
+  } else if (EPI == EPI_QKV) {
+    const QkvArgs& q = g.qkv;
+    const bool perm = 16 * NBW < q.hd;
+    for (int e = threadIdx.x; e < TM * TN; e += 256) {
+      const int r = e / TN, c = e % TN, m = m0 + r;
+      if (m >= g.M) continue;
+      const int n = nt * TN + c;
       const int f = qkv_feature(n, q.d, q.hd, TN / 2, perm);
-      const int pn = qkv_partner(n, f, q.d, q.hd, TN / 2, perm);
-      const int pc = pn - nt * TN;
-      const float yp = red[0][r * LDT + pc] + red[1][r * LDT + pc] + red[2][r * LDT + pc] +
-                       red[3][r * LDT + pc];
-      qkv_store(q, m, f, y, yp);
+      const int pc = qkv_partner(n, f, q.d, q.hd, TN / 2, perm) - nt * TN;
+      qkv_store(q, m, f, red[r * LDT + c], red[r * LDT + pc]);
     }
   }
 }
 
-// Sums the K-split partials of a PARTIAL gemm and applies the final
-// epilogue (g.epi).  One thread per output element (pairs for SWIGLU).
-template <int NBW>
-__global__ __launch_bounds__(256) void gemm_reduce_kernel(GemmArgs g) {
-  const int epi = g.epi;
-  const size_t MN = (size_t)g.M * g.N;
-  if (epi == EPI_SWIGLU) {
-    // partial columns: tile t holds [gate P | up P], P = 8*NBW, for h cols t*P..
-    constexpr int P = NBW * 8;
-    const int F = g.N;                  // output columns
-    const size_t total = (size_t)g.Mp * F;
-    for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
-      const int m = (int)(e / F), j = (int)(e % F);
-      float h = 0.f;
-      if (m < g.M) {
-        const int t = j / P, c = j % P;
-        const size_t col_g = (size_t)t * 2 * P + c, col_u = col_g + P;
-        float gv = 0.f, uv = 0.f;
-        for (int s = 0; s < g.splits; ++s) {
-          const float* ps = g.partial + (size_t)s * g.M * (2 * F) + (size_t)m * (2 * F);
-          gv += ps[col_g];
-          uv += ps[col_u];
-        }
-        h = silu_f(gv) * uv;
-      }
-      g.out_bf16[packed_index(m, j, F)] = f32_to_bf16(h);
-    }
-    return;
-  }
-  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < MN; e += (size_t)gridDim.x * 256) {
-    const int m = (int)(e / g.N), n = (int)(e % g.N);
-    float y = 0.f;
-    for (int s = 0; s < g.splits; ++s) y += g.partial[(size_t)s * MN + e];
-    if (epi == EPI_STORE) {
-      g.out_f32[e] = y;
-    } else if (epi == EPI_ADD) {
-      g.out_f32[e] += y;
-    } else if (epi == EPI_QKV) {
-      const QkvArgs& q = g.qkv;
-      const bool perm = qkv_perm(NBW, q.hd);
-      const int f = qkv_feature(n, q.d, q.hd, NBW * 8, perm);
-      const int pn = qkv_partner(n, f, q.d, q.hd, NBW * 8, perm);
-      float yp = 0.f;
-      for (int s = 0; s < g.splits; ++s) yp += g.partial[(size_t)s * MN + (size_t)m * g.N + pn];
-      qkv_store(q, m, f, y, yp);
-    }
-  }
-}
-
-template <int MB, int NBW, int U>
-static hipError_t launch_mb(const GemmArgs& g, dim3 grid, hipStream_t s) {
-  const int epi = g.splits > 1 ? EPI_PARTIAL : g.epi;
-  switch (epi) {
-    case EPI_STORE: hipLaunchKernelGGL((gemm_kernel<MB, NBW, U, EPI_STORE>), grid, dim3(256), 0, s, g); break;
-    case EPI_ADD: hipLaunchKernelGGL((gemm_kernel<MB, NBW, U, EPI_ADD>), grid, dim3(256), 0, s, g); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_kernel<MB, NBW, U, EPI_SWIGLU>), grid, dim3(256), 0, s, g); break;
-    case EPI_QKV: hipLaunchKernelGGL((gemm_kernel<MB, NBW, U, EPI_QKV>), grid, dim3(256), 0, s, g); break;
-    default: hipLaunchKernelGGL((gemm_kernel<MB, NBW, U, EPI_PARTIAL>), grid, dim3(256), 0, s, g); break;
+template <int MB, int NBW, int D>
+static hipError_t launch_cfg(const GemmArgs& g, dim3 grid, hipStream_t s) {
+  const dim3 blk(256);
+  switch (g.epi) {
+    case EPI_STORE: hipLaunchKernelGGL((gemm_kernel<MB, NBW, D, EPI_STORE>), grid, blk, 0, s, g); break;
+    case EPI_ADD: hipLaunchKernelGGL((gemm_kernel<MB, NBW, D, EPI_ADD>), grid, blk, 0, s, g); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_kernel<MB, NBW, D, EPI_SWIGLU>), grid, blk, 0, s, g); break;
+    case EPI_QKV: hipLaunchKernelGGL((gemm_kernel<MB, NBW, D, EPI_QKV>), grid, blk, 0, s, g); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-// Number of 16-row blocks per M tile.
+// 16-row blocks per workgroup tile.
 static int gemm_mb(int Mp) { return Mp <= 16 ? 1 : (Mp <= 32 ? 2 : 4); }
 
-hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
-  constexpr int NBW = 4;
+int gemm_tiles(const GemmArgs& g, int* mtiles, int* ntiles) {
   const int MB = gemm_mb(g.Mp);
-  const int mtiles = (g.Mp / 16 + MB - 1) / MB;
-  // SWIGLU: N is the output width F; each tile produces 8*NBW columns
-  // from gate and up rows.  PARTIAL for SWIGLU writes 2F interleaved columns.
-  const int ncols = g.epi == EPI_SWIGLU ? g.N / (NBW * 8) : g.N / (NBW * 16);
-  dim3 grid(mtiles, ncols, g.splits);
-  GemmArgs a = g;
-  if (g.epi == EPI_SWIGLU && g.splits > 1) a.N = 2 * g.N;   // partial row width
-  if (MB == 1) return launch_mb<1, NBW, 2>(a, grid, s);
-  if (MB == 2) return launch_mb<2, NBW, 2>(a, grid, s);
-  return launch_mb<4, NBW, 1>(a, grid, s);
+  *mtiles = (g.Mp / 16 + MB - 1) / MB;
+  *ntiles = g.epi == EPI_SWIGLU ? g.N / (g.nbw * 8) : g.N / (g.nbw * 16);
+  return MB * 16 * g.nbw * 16;          // elements of one tile
 }
 
-hipError_t launch_gemm_reduce(const GemmArgs& g, hipStream_t s) {
-  const size_t total = g.epi == EPI_SWIGLU ? (size_t)g.Mp * g.N : (size_t)g.M * g.N;
-  int blocks = (int)((total + 255) / 256);
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL((gemm_reduce_kernel<4>), dim3(blocks), dim3(256), 0, s, g);
-  return hipGetLastError();
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
+  int mtiles, ntiles;
+  gemm_tiles(g, &mtiles, &ntiles);
+  const int MB = gemm_mb(g.Mp);
+  dim3 grid(mtiles, ntiles, g.splits);
+  if (g.nbw == 4) {
+    if (MB == 1) return launch_cfg<1, 4, 1>(g, grid, s);
+    if (MB == 2) return launch_cfg<2, 4, 1>(g, grid, s);
+    return launch_cfg<4, 4, 1>(g, grid, s);
+  }
+  if (g.nbw == 2) {
+    if (MB == 1) return launch_cfg<1, 2, 4>(g, grid, s);
+    if (MB == 2) return launch_cfg<2, 2, 4>(g, grid, s);
+    return launch_cfg<4, 2, 4>(g, grid, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace mvk

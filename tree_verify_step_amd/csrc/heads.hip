@@ -102,91 +102,117 @@ hipError_t launch_heads_w2(const float* u, const u16* w2, float* z, int B, int D
 }
 
 // ---------------------------------------------------------------------------
-// Top-s of one row of V logits: larger value first, lower id first on ties.
-// Each of the 256 threads keeps a sorted list of its best MAXS candidates
-// (fixed-size insertion, stays in registers); then s rounds of a block-wide
-// selection of the best list head.
+// Top-s of rows of V logits: larger value first, lower id first on ties.
+// Stage 1: each wave takes 1024 consecutive logits (16 per lane, coalesced
+// float4 loads) and selects its top s by s rounds of a wave-wide argmax over
+// the lanes' best remaining values (shuffles only, no barriers); it writes
+// s (value, id) candidates.  Stage 2: one wave per row selects the final s
+// from the row's candidates the same way.
 // ---------------------------------------------------------------------------
-template <int MAXS>
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ z, int V, int s_top,
-                                                   int32_t* __restrict__ ids,
-                                                   float* __restrict__ vals) {
-  __shared__ float sv[4];
-  __shared__ int si[4];
-  __shared__ int swin;
-  const int row = blockIdx.x;
-  const float* zr = z + (size_t)row * V;
-  float lv[MAXS];
-  int li[MAXS];
+__device__ __forceinline__ bool better_vi(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+// v/id: this lane's 16 candidates (id INT_MAX = empty).  Writes the wave's
+// top s into outv/outi (lane r writes round r's winner).
+__device__ __forceinline__ void wave_select(const float (&v)[16], const int (&id)[16], int s,
+                                            float* outv, int* outi) {
+  const int lane = threadIdx.x & 63;
+  unsigned taken = 0;
+  for (int r = 0; r < s; ++r) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff, bj = -1;
 #pragma unroll
-  for (int j = 0; j < MAXS; ++j) {
-    lv[j] = -INFINITY;
-    li[j] = 0x7fffffff;
-  }
-  for (int i = threadIdx.x; i < V; i += 256) {
-    float cv = zr[i];
-    int ci = i;
-#pragma unroll
-    for (int j = 0; j < MAXS; ++j) {
-      const bool better = cv > lv[j] || (cv == lv[j] && ci < li[j]);
-      const float tv = better ? lv[j] : cv;
-      const int ti = better ? li[j] : ci;
-      lv[j] = better ? cv : lv[j];
-      li[j] = better ? ci : li[j];
-      cv = tv;
-      ci = ti;
+    for (int j = 0; j < 16; ++j) {
+      if (!((taken >> j) & 1u) && better_vi(v[j], id[j], bv, bi)) {
+        bv = v[j];
+        bi = id[j];
+        bj = j;
+      }
     }
-  }
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int r = 0; r < s_top; ++r) {
-    float bv = lv[0];
-    int bi = li[0];
+    float wv = bv;
+    int wi = bi;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
+      const float ov = __shfl_xor(wv, o, 64);
+      const int oi = __shfl_xor(wi, o, 64);
+      if (better_vi(ov, oi, wv, wi)) {
+        wv = ov;
+        wi = oi;
       }
     }
-    if (lane == 0) {
-      sv[wave] = bv;
-      si[wave] = bi;
+    if (bj >= 0 && bi == wi) taken |= 1u << bj;     // ids are unique: one owner
+    if (lane == r) {
+      outv[0] = wv;
+      outi[0] = wi;
     }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float wv = sv[0];
-      int wi = si[0];
-      for (int w = 1; w < 4; ++w)
-        if (sv[w] > wv || (sv[w] == wv && si[w] < wi)) {
-          wv = sv[w];
-          wi = si[w];
-        }
-      ids[(size_t)row * s_top + r] = wi;
-      vals[(size_t)row * s_top + r] = wv;
-      swin = wi;
-    }
-    __syncthreads();
-    if (li[0] == swin) {            // the owner pops its head
-#pragma unroll
-      for (int j = 0; j < MAXS - 1; ++j) {
-        lv[j] = lv[j + 1];
-        li[j] = li[j + 1];
-      }
-      lv[MAXS - 1] = -INFINITY;
-      li[MAXS - 1] = 0x7fffffff;
-    }
-    __syncthreads();
   }
 }
 
+__global__ __launch_bounds__(256) void topk_partial_kernel(const float* __restrict__ z, int V,
+                                                           int s_top, float* __restrict__ cv,
+                                                           int* __restrict__ ci) {
+  const int row = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nw = gridDim.x * 4;                       // waves per row
+  const int w = blockIdx.x * 4 + wave;
+  const int base = w * 1024;
+  const float* zr = z + (size_t)row * V;
+  float v[16];
+  int id[16];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = base + j * 256 + lane * 4;
+    float4 x = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    if (i < V) x = *reinterpret_cast<const float4*>(zr + i);
+    v[4 * j + 0] = x.x; v[4 * j + 1] = x.y; v[4 * j + 2] = x.z; v[4 * j + 3] = x.w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) id[4 * j + e] = i + e < V ? i + e : 0x7fffffff;
+  }
+  float ov = 0.f;
+  int oi = 0;
+  wave_select(v, id, s_top, &ov, &oi);
+  if (lane < s_top) {
+    const size_t o = ((size_t)row * nw + w) * s_top + lane;
+    cv[o] = ov;
+    ci[o] = oi;
+  }
+}
+
+// One wave per row: up to 1024 candidates (16 per lane).
+__global__ __launch_bounds__(64) void topk_merge_kernel(const float* __restrict__ cv,
+                                                        const int* __restrict__ ci, int ncand,
+                                                        int s_top, int32_t* __restrict__ ids,
+                                                        float* __restrict__ vals) {
+  const int row = blockIdx.x, lane = threadIdx.x;
+  float v[16];
+  int id[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int c = j * 64 + lane;
+    v[j] = c < ncand ? cv[(size_t)row * ncand + c] : -INFINITY;
+    id[j] = c < ncand ? ci[(size_t)row * ncand + c] : 0x7fffffff;
+  }
+  float ov = 0.f;
+  int oi = 0;
+  wave_select(v, id, s_top, &ov, &oi);
+  if (lane < s_top) {
+    ids[(size_t)row * s_top + lane] = oi;
+    vals[(size_t)row * s_top + lane] = ov;
+  }
+}
+
+int topk_waves(int V) { return ((V + 4095) / 4096) * 4; }
+
 hipError_t launch_topk(const float* z, int rows, int V, int s_top, int32_t* ids, float* vals,
-                       hipStream_t s) {
-  if (s_top <= 16)
-    hipLaunchKernelGGL((topk_kernel<16>), dim3(rows), dim3(256), 0, s, z, V, s_top, ids, vals);
-  else
-    return hipErrorInvalidValue;
+                       float* cand_v, int* cand_i, hipStream_t s) {
+  if (s_top > 16 || s_top > 64) return hipErrorInvalidValue;
+  const int nw = topk_waves(V);
+  if (nw * s_top > 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(topk_partial_kernel, dim3(nw / 4, rows), dim3(256), 0, s, z, V, s_top, cand_v,
+                     cand_i);
+  hipLaunchKernelGGL(topk_merge_kernel, dim3(rows), dim3(64), 0, s, cand_v, cand_i, nw * s_top,
+                     s_top, ids, vals);
   return hipGetLastError();
 }
 

@@ -1,6 +1,6 @@
 // Row-wise kernels of the tree-verify forward: weight packing, embedding
-// gather, RMSNorm into the packed GEMM operand, RoPE tables, KV compaction
-// and small state updates.
+// gather (with the rows' sums of squares and RoPE tables), KV compaction and
+// small state updates.
 #include "common.hpp"
 
 namespace mvk {
@@ -11,11 +11,11 @@ __host__ __device__ __forceinline__ int qkv_feature_h(int p, int d, int hd, int 
   return h * hd + (ee < P ? j * P + ee : hd / 2 + j * P + (ee - P));
 }
 
-// dst (fragment-packed [R][C]) <- src (row-major [R][C]); when rope_hd > 0 the
-// first rope_rows rows (q and k of a fused QKV matrix) are reordered so that
-// each 64-row tile holds 32 first-half dims of a head and their RoPE partners
-// (the order the QKV GEMM's epilogue expects when a tile is narrower than a
-// head).  One thread per 16-byte piece.
+// dst (fragment-packed, k-block-major [R][C]) <- src (row-major [R][C]);
+// when rope_hd > 0 the first rope_rows rows (q and k of a fused QKV matrix)
+// are reordered so that each 64-row tile holds 32 first-half dims of a head
+// and their RoPE partners (the order the QKV GEMM's epilogue expects when a
+// tile is narrower than a head).  One thread per 16-byte piece.
 __global__ void pack_kernel(const u16* __restrict__ src, u16* __restrict__ dst, int R, int C,
                             int rope_hd, int rope_rows) {
   const size_t pieces = (size_t)R * (C / 8);
@@ -29,7 +29,7 @@ __global__ void pack_kernel(const u16* __restrict__ src, u16* __restrict__ dst, 
       r = qkv_feature_h(p, rope_rows / 2, rope_hd, 32, perm);
     }
     const uint4 v = *reinterpret_cast<const uint4*>(src + (size_t)r * C + c);
-    *reinterpret_cast<uint4*>(dst + packed_index(p, c, C)) = v;
+    *reinterpret_cast<uint4*>(dst + packed_index_kmajor(p, c, R)) = v;
   }
 }
 
@@ -43,84 +43,118 @@ hipError_t launch_pack(const u16* src, u16* dst, int R, int C, int rope_hd, int 
   return hipGetLastError();
 }
 
-// x[m][:] = E[tok[m]][:] widened to fp32.  Token ids outside [0, V) are
-// clamped (validated on the host for host-provided ids).
-__global__ void embed_kernel(const int32_t* __restrict__ tok, const u16* __restrict__ E,
-                             float* __restrict__ x, int M, int d, int V) {
+__device__ __forceinline__ float block_sum256(float v) {
+  __shared__ float red[4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  v = warp_sum(v);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  v = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  return v;
+}
+
+// One workgroup per row m: x[m][:] = E[tok[m]][:] widened to fp32, ss[m] =
+// sum of squares of the row; optionally the row's RoPE table: (cos, sin) of
+// position * 10000^(-2i/hd), position = n[b] + depth[m], angles in double.
+// Token ids outside [0, V) are clamped.
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tok,
+                                                    const u16* __restrict__ E,
+                                                    float* __restrict__ x, float* __restrict__ ss,
+                                                    int d, int V,
+                                                    const int32_t* __restrict__ n_prefix,
+                                                    const int32_t* __restrict__ depth_of,
+                                                    float2* __restrict__ rope, int T, int hd) {
   const int m = blockIdx.x;
   int t = tok[m];
   t = t < 0 ? 0 : (t >= V ? V - 1 : t);
   const u16* e = E + (size_t)t * d;
   float* xr = x + (size_t)m * d;
-  for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
+  float sq = 0.f;
+  for (int c = threadIdx.x * 8; c < d; c += 2048) {
     const uint4 w = *reinterpret_cast<const uint4*>(e + c);
     float4 a = {bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y)};
     float4 b = {bf16lo(w.z), bf16hi(w.z), bf16lo(w.w), bf16hi(w.w)};
     *reinterpret_cast<float4*>(xr + c) = a;
     *reinterpret_cast<float4*>(xr + c + 4) = b;
+    sq += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w + b.x * b.x + b.y * b.y + b.z * b.z +
+          b.w * b.w;
+  }
+  sq = block_sum256(sq);
+  if (threadIdx.x == 0 && ss) ss[m] = sq;
+  if (rope) {
+    const int half = hd >> 1;
+    const double pos = (double)(n_prefix[m / T] + depth_of[m]);
+    for (int i = threadIdx.x; i < half; i += 256) {
+      const double inv = pow(10000.0, -2.0 * (double)i / (double)hd);
+      double sv, cv;
+      sincos(pos * inv, &sv, &cv);
+      rope[(size_t)m * half + i] = make_float2((float)cv, (float)sv);
+    }
   }
 }
 
-hipError_t launch_embed(const int32_t* tok, const u16* E, float* x, int M, int d, int V,
-                        hipStream_t s) {
-  hipLaunchKernelGGL(embed_kernel, dim3(M), dim3(256), 0, s, tok, E, x, M, d, V);
+hipError_t launch_embed(const int32_t* tok, const u16* E, float* x, float* ss, int M, int d,
+                        int V, const int32_t* n_prefix, const int32_t* depth_of, float2* rope,
+                        int T, int hd, hipStream_t s) {
+  hipLaunchKernelGGL(embed_kernel, dim3(M), dim3(256), 0, s, tok, E, x, ss, d, V, n_prefix,
+                     depth_of, rope, T, hd);
   return hipGetLastError();
 }
 
-// out = g * x / sqrt(mean(x^2) + 1e-5), as bf16, into the fragment-packed
-// operand [Mp][d] (rows >= M written as zeros) and optionally row-major.
+// RMSNorm of row m of x [M][d] into the fragment-packed bf16 GEMM operand
+// [Mp][d]: out = g * x / sqrt(mean(x^2) + 1e-5); rows M..Mp-1 are zeros.
+// One workgroup per row; the row (d <= 8192) is held in registers, so it is
+// read once.
+#define MV_NORM_MAX_CHUNKS 4          // 8 columns per thread per chunk
 __global__ __launch_bounds__(256) void rmsnorm_pack_kernel(const float* __restrict__ x,
                                                            const u16* __restrict__ gain,
-                                                           u16* __restrict__ outp,
-                                                           u16* __restrict__ outr, int M,
-                                                           int d) {
-  __shared__ float red[4];
+                                                           u16* __restrict__ outp, int M, int d) {
   const int m = blockIdx.x;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  float rs = 0.f;
-  if (m < M) {
-    const float* xr = x + (size_t)m * d;
-    float ss = 0.f;
-    for (int c = threadIdx.x * 4; c < d; c += 1024) {
-      const float4 v = *reinterpret_cast<const float4*>(xr + c);
-      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-    }
-    ss = warp_sum(ss);
-    if (lane == 0) red[wave] = ss;
-    __syncthreads();
-    ss = red[0] + red[1] + red[2] + red[3];
-    rs = 1.0f / sqrtf(ss / (float)d + 1e-5f);
-  }
-  for (int c = threadIdx.x * 8; c < d; c += 2048) {
-    uint4 o = {0, 0, 0, 0};
-    if (m < M) {
-      const float* xr = x + (size_t)m * d + c;
-      const uint4 gw = *reinterpret_cast<const uint4*>(gain + c);
-      const float gv[8] = {bf16lo(gw.x), bf16hi(gw.x), bf16lo(gw.y), bf16hi(gw.y),
-                           bf16lo(gw.z), bf16hi(gw.z), bf16lo(gw.w), bf16hi(gw.w)};
-      uint32_t pk[4];
+  float v[MV_NORM_MAX_CHUNKS][8];
+  float sq = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u16 lo = f32_to_bf16(xr[2 * j] * rs * gv[2 * j]);
-        const u16 hi = f32_to_bf16(xr[2 * j + 1] * rs * gv[2 * j + 1]);
-        pk[j] = (uint32_t)lo | ((uint32_t)hi << 16);
-      }
-      o = {pk[0], pk[1], pk[2], pk[3]};
-      if (outr) *reinterpret_cast<uint4*>(outr + (size_t)m * d + c) = o;
+  for (int j = 0; j < MV_NORM_MAX_CHUNKS; ++j) {
+    const int c = (j * 256 + threadIdx.x) * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
+    if (m < M && c < d) {
+      const float4 a = *reinterpret_cast<const float4*>(x + (size_t)m * d + c);
+      const float4 b = *reinterpret_cast<const float4*>(x + (size_t)m * d + c + 4);
+      v[j][0] = a.x; v[j][1] = a.y; v[j][2] = a.z; v[j][3] = a.w;
+      v[j][4] = b.x; v[j][5] = b.y; v[j][6] = b.z; v[j][7] = b.w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sq += v[j][e] * v[j][e];
     }
-    *reinterpret_cast<uint4*>(outp + packed_index(m, c, d)) = o;
+  }
+  sq = block_sum256(sq);
+  const float rs = m < M ? 1.0f / sqrtf(sq / (float)d + 1e-5f) : 0.f;
+#pragma unroll
+  for (int j = 0; j < MV_NORM_MAX_CHUNKS; ++j) {
+    const int c = (j * 256 + threadIdx.x) * 8;
+    if (c >= d) continue;
+    const uint4 gw = *reinterpret_cast<const uint4*>(gain + c);
+    const float gv[8] = {bf16lo(gw.x), bf16hi(gw.x), bf16lo(gw.y), bf16hi(gw.y),
+                         bf16lo(gw.z), bf16hi(gw.z), bf16lo(gw.w), bf16hi(gw.w)};
+    uint32_t pk[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const u16 lo = f32_to_bf16(v[j][2 * e] * rs * gv[2 * e]);
+      const u16 hi = f32_to_bf16(v[j][2 * e + 1] * rs * gv[2 * e + 1]);
+      pk[e] = (uint32_t)lo | ((uint32_t)hi << 16);
+    }
+    *reinterpret_cast<uint4*>(outp + packed_index(m, c, d)) = uint4{pk[0], pk[1], pk[2], pk[3]};
   }
 }
 
-hipError_t launch_rmsnorm_pack(const float* x, const u16* g, u16* out_packed, u16* out_rows,
-                               int M, int Mp, int d, hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_pack_kernel, dim3(Mp), dim3(256), 0, s, x, g, out_packed, out_rows,
-                     M, d);
+hipError_t launch_rmsnorm_pack(const float* x, const u16* g, u16* out_packed, int M, int Mp,
+                               int d, hipStream_t s) {
+  if (d > MV_NORM_MAX_CHUNKS * 2048) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rmsnorm_pack_kernel, dim3(Mp), dim3(256), 0, s, x, g, out_packed, M, d);
   return hipGetLastError();
 }
 
-// (cos, sin) of position * 10000^(-2i/hd) for each tree row, position =
-// n[b] + depth[b][v]; angles in double precision.
+// (cos, sin) tables for all B*T rows (see embed_kernel).
 __global__ void rope_table_kernel(const int32_t* __restrict__ n_prefix,
                                   const int32_t* __restrict__ depth_of, float2* __restrict__ rope,
                                   int B, int T, int hd) {
@@ -128,8 +162,7 @@ __global__ void rope_table_kernel(const int32_t* __restrict__ n_prefix,
   const int total = B * T * half;
   for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < total; e += gridDim.x * blockDim.x) {
     const int m = e / half, i = e % half;
-    const int b = m / T;
-    const double pos = (double)(n_prefix[b] + depth_of[m]);
+    const double pos = (double)(n_prefix[m / T] + depth_of[m]);
     const double inv = pow(10000.0, -2.0 * (double)i / (double)hd);
     double sv, cv;
     sincos(pos * inv, &sv, &cv);
@@ -146,15 +179,14 @@ hipError_t launch_rope_table(const int32_t* n_prefix, const int32_t* depth_of, f
 }
 
 // KV compaction: for each (layer, sequence, head) and m = 0..accept_len,
-// slot n + m <- slot n + path[m], for K and V.  Each thread owns a set of
-// dims of one (layer, b, head) and reads every source row before writing any
-// row, so overlapping sources and destinations are safe.
-#define MV_MAX_PATH 17
+// slot n + m <- slot n + path[m], for K and V.  Each thread owns one dim of
+// one (layer, b, head) and reads every source row before writing any row, so
+// overlapping sources and destinations are safe.
+#define MV_MAX_PATH (MV_MAX_DEPTH + 1)
 __global__ void compact_kernel(u16* __restrict__ kc, u16* __restrict__ vc, int L, int B, int H,
                                int hd, int cap, const int32_t* __restrict__ path, int path_stride,
                                const int32_t* __restrict__ accept_len,
                                const int32_t* __restrict__ n_prefix) {
-  // thread -> (layer, b, h, dim)
   const size_t total = (size_t)L * B * H * hd;
   for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
        e += (size_t)gridDim.x * blockDim.x) {

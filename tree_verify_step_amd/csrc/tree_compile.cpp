@@ -41,7 +41,7 @@ extern "C" MV_API int mv_tree_compile(const int32_t* paths, const int32_t* path_
   std::vector<std::vector<int32_t>> ps(n_paths);
   for (int p = 0; p < n_paths; ++p) {
     const int len = path_len[p];
-    if (len < 1 || len > max_len || len > MV_MAX_DEPTH)
+    if (len < 1 || len > max_len || len > MV_MAX_T - 1)
       return mv::fail(MV_ETREE, "mv_tree_compile: path %d has length %d", p, len);
     ps[p].assign(paths + (size_t)p * max_len, paths + (size_t)p * max_len + len);
     for (int32_t r : ps[p])
