@@ -45,6 +45,85 @@ def bytes_model(D, B, T, depth, n_mean, acc_mean):
     return w + kv + tree_kv + logits + compact
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gate_up_llama7b_T64_traffic.md")
+CSRC = os.path.join(ROOT, "tree_verify_step_amd", "csrc")
+
+
+def gemm_source_hash() -> str:
+    """sha256 over the GEMM kernel source, the shared header and the GEMM
+    launch table: the counters in the traffic summary hold only while these
+    are unchanged."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.hpp"):
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    api = open(os.path.join(CSRC, "api.cpp")).read()
+    m = re.search(r"static GemmCfg gemm_cfg\(.*?\n}\n", api, re.S)
+    h.update((m.group(0) if m else "").encode())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per gate/up launch from the committed counter summary, or
+    None when it is missing or was taken on a different GEMM source."""
+    try:
+        txt = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    vals = dict(l.split("=", 1) for l in txt.splitlines() if l.startswith(("traffic_", "source_")))
+    vals = {k.strip(): v.strip() for k, v in vals.items()}
+    if vals.get("source_sha256") != gemm_source_hash():
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+COPY_BYTES = 256 << 20          # calibration copy: this many bytes read and written
+
+
+def calibrate_copy():
+    """A plain elementwise copy of known size (float32 negation, 256 MiB in,
+    256 MiB out), run three times so that hardware counters taken over the
+    program can be scaled to bytes."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def pmc_summary(dirs, gate_up_name="gemm_kernel<4, 4, 1, 2>"):
+    """Summarise rocprofv3 --pmc counter files (FETCH_SIZE / WRITE_SIZE, KiB
+    per dispatch) for the gate/up GEMM, scaled by what the same counter reads
+    for the calibration copy."""
+    import csv
+    import glob
+    import statistics
+    per = {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                name, ctr = r["Kernel_Name"], r["Counter_Name"]
+                kind = "copy" if "neg" in name else ("gate_up" if gate_up_name in name else None)
+                if kind:
+                    per.setdefault((kind, ctr), []).append(float(r["Counter_Value"]))
+    out = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        cp, gu = per.get(("copy", ctr)), per.get(("gate_up", ctr))
+        if not cp or not gu:
+            continue
+        scale = (COPY_BYTES / 1024) / statistics.median(cp)
+        out[ctr] = {"copy_kib": statistics.median(cp), "scale": scale,
+                    "gate_up_kib_mean": statistics.mean(gu), "gate_up_dispatches": len(gu),
+                    "gate_up_bytes": statistics.mean(gu) * 1024 * scale}
+    return out
+
+
 def gate_up_bytes(D, M):
     """Algorithmic bytes of one gate/up GEMM launch (one layer): gate and up
     weights, the normalised activations in, the SwiGLU output out."""
@@ -118,7 +197,27 @@ def main() -> int:
     ap.add_argument("--workload", default=None)
     ap.add_argument("--profile-steps", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a copy kernel of known size first (for --pmc counter scaling)")
+    ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
+                    help="summarise rocprofv3 --pmc FETCH_SIZE/WRITE_SIZE output dirs and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        from workloads import configs
+        D = configs.HEADLINE.dims
+        res = pmc_summary(args.pmc_summary)
+        algo = gate_up_bytes(D, configs.HEADLINE.batch * 64)
+        for ctr, v in res.items():
+            print(f"{ctr}: copy {v['copy_kib']:.0f} KiB for {COPY_BYTES // 1024} KiB moved "
+                  f"(scale {v['scale']:.4f}); gate/up {v['gate_up_kib_mean']:.0f} KiB/dispatch "
+                  f"over {v['gate_up_dispatches']} dispatches -> {v['gate_up_bytes'] / 1e6:.2f} MB")
+        if "FETCH_SIZE" in res and "WRITE_SIZE" in res:
+            tot = res["FETCH_SIZE"]["gate_up_bytes"] + res["WRITE_SIZE"]["gate_up_bytes"]
+            print(f"algorithmic_bytes_per_launch = {algo}")
+            print(f"traffic_bytes_per_launch = {int(round(tot))}")
+            print(f"traffic_over_algorithmic = {tot / algo:.4f}")
+            print(f"source_sha256 = {gemm_source_hash()}")
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the tree-verify "
               "step of one sequence batch is a single-GPU workload here", file=sys.stderr)
@@ -132,6 +231,8 @@ def main() -> int:
     from workloads import configs, synth
 
     tv.lib()
+    if args.calibrate_copy:
+        calibrate_copy()
     w = configs.get(args.workload) if args.workload else configs.HEADLINE
     D = w.dims
     B = w.batch
@@ -198,7 +299,7 @@ def main() -> int:
     gu_bytes = gate_up_bytes(D, B * T)
     achieved = gu_bytes / (gu["avg_launch_us"] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
                 "kernel": "gemm_kernel<4,4,1,EPI_SWIGLU> (gate/up + SwiGLU, one layer)",
                 "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu["avg_launch_us"], 2)}
 
