@@ -33,10 +33,17 @@ def sources():
                   if f.endswith((".hip", ".cpp")))
 
 
+# Per-source extra flags.  The GEMM keeps its MFMA accumulators in VGPRs:
+# with AGPR accumulators the register allocator rotates them through copies
+# that wait on each MFMA result.
+EXTRA = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str, obj: str) -> str:
     cmd = [hipcc(), "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
            "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           *EXTRA.get(os.path.basename(src), []),
            "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

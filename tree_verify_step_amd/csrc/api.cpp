@@ -2,10 +2,13 @@
 // carving, kernel sequencing for each operation, and the step driver that
 // captures one whole decoding step into a hipGraph.
 //
-// A decoder layer is eight launches: RMSNorm into the packed operand, QKV
-// GEMM (RoPE + KV-cache write epilogue), tree attention, range combine,
-// O-projection GEMM (residual add), RMSNorm, gate/up GEMM (SwiGLU epilogue),
-// down GEMM (residual add).  Split-K partials are reduced inside the GEMMs.
+// A decoder layer is six launches: QKV GEMM (row-norm scale, RoPE and
+// KV-cache write in its epilogue), tree attention, range combine, O-projection
+// GEMM (residual add; writes the FFN norm's operand and the rows' sums of
+// squares), gate/up GEMM (row-norm scale, SwiGLU), down GEMM (residual add;
+// writes the next norm's operand and sums of squares).  RMSNorm never runs as
+// a kernel of its own inside a step; split-K partials are reduced inside the
+// GEMMs.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -78,39 +81,48 @@ static int attn_nsplit(int B, int H, int T) {
 enum GemmKind { G_QKV = 0, G_O, G_GU, G_DOWN, G_LM, G_KINDS };
 
 struct GemmCfg {
-  int nbw, splits;
+  int w, nbw, splits, ntiles, mtiles, MB, N, K, epi;
 };
 
-// Tile width and K splits per GEMM (measured on MI355X at M = 64 for the
-// 7B shapes); the split count shrinks when several M tiles already multiply
-// the grid and is capped so each split keeps >= 8 k-blocks.
+// Waves per workgroup and column blocks per wave per GEMM (measured on
+// MI355X at M = 64 for the 7B shapes); K is split until the tiles cover the
+// 256 compute units, keeping at least two activation chunks per split.
 static GemmCfg gemm_cfg(const mv_dims& D, int kind, int Mp) {
-  static const GemmCfg base[G_KINDS] = {{4, 4}, {2, 2}, {4, 1}, {4, 4}, {4, 1}};
-  GemmCfg c = base[kind];
-  const int K = (kind == G_DOWN) ? D.F : D.d;
-  const int MB = Mp <= 16 ? 1 : (Mp <= 32 ? 2 : 4);
-  const int mtiles = (Mp / 16 + MB - 1) / MB;
-  c.splits = std::max(1, c.splits / mtiles);
-  c.splits = std::max(1, std::min(c.splits, (K / 32) / 8));
+  GemmCfg c;
+  switch (kind) {
+    case G_QKV: c.w = 4; c.nbw = 2; c.N = 3 * D.d; c.K = D.d; c.epi = mvk::EPI_QKV; break;
+    case G_O: c.w = 4; c.nbw = 1; c.N = D.d; c.K = D.d; c.epi = mvk::EPI_ADD; break;
+    case G_GU: c.w = 4; c.nbw = 2; c.N = D.F; c.K = D.d; c.epi = mvk::EPI_SWIGLU; break;
+    case G_DOWN: c.w = 4; c.nbw = 1; c.N = D.d; c.K = D.F; c.epi = mvk::EPI_ADD; break;
+    default:
+      c.w = D.V % 128 == 0 ? 8 : 4; c.nbw = 1; c.N = D.V; c.K = D.d; c.epi = mvk::EPI_STORE;
+      break;
+  }
+  c.MB = mvk::gemm_mb(Mp);
+  c.mtiles = (Mp / 16 + c.MB - 1) / c.MB;
+  c.ntiles = mvk::gemm_ntiles(c.epi, c.N, c.w, c.nbw);
+  const int KB = c.K / 32, KC = mvk::gemm_kc(c.MB);
+  c.splits = std::max(1, 256 / (c.ntiles * c.mtiles));
+  c.splits = std::max(1, std::min(c.splits, KB / (2 * KC)));
   return c;
 }
 
-static size_t gemm_tile_elems(const mv_dims& D, int kind, int Mp, int* ntiles_out, int* mtiles_out) {
-  const GemmCfg c = gemm_cfg(D, kind, Mp);
-  const int MB = Mp <= 16 ? 1 : (Mp <= 32 ? 2 : 4);
-  const int mtiles = (Mp / 16 + MB - 1) / MB;
-  int N = (kind == G_QKV) ? 3 * D.d : (kind == G_GU) ? D.F : (kind == G_LM) ? D.V : D.d;
-  const int ntiles = (kind == G_GU) ? N / (c.nbw * 8) : N / (c.nbw * 16);
-  if (ntiles_out) *ntiles_out = ntiles;
-  if (mtiles_out) *mtiles_out = mtiles;
-  return (size_t)MB * 16 * c.nbw * 16;
-}
-
 struct Ws {
-  size_t x, xa, ha, q, rope, po, pml, part, counters, hu, hz, topi, topv, tcv, tci, amax, stats,
-      cnt, total;
+  size_t x, xa, ao, ha, ss, q, rope, po, pml, part, counters, hu, hz, topi, topv, tcv, tci, amax,
+      stats, cnt, total;
   int nsplit;
+  int ss_ld;    // floats per row of the sums-of-squares buffer
 };
+
+// Row stride of the sums of squares: the residual GEMMs' column tiles, rounded to 4.
+static int ss_ld_of(const mv_dims& D, int Mp) {
+  int t = 1;
+  for (int k = 0; k < G_KINDS; ++k) {
+    const GemmCfg c = gemm_cfg(D, k, Mp);
+    if (c.epi == mvk::EPI_ADD) t = std::max(t, c.ntiles);
+  }
+  return (t + 3) & ~3;
+}
 
 static Ws ws_layout(const mv_dims& D, int B, int T) {
   Ws w;
@@ -118,12 +130,13 @@ static Ws ws_layout(const mv_dims& D, int B, int T) {
   w.nsplit = attn_nsplit(B, D.H, T);
   size_t part = 0, max_tiles = 1;
   for (int k = 0; k < G_KINDS; ++k) {
-    int nt, mt;
-    const size_t te = gemm_tile_elems(D, k, Mp, &nt, &mt);
     const GemmCfg c = gemm_cfg(D, k, Mp);
-    if (c.splits > 1) part = std::max(part, (size_t)nt * mt * c.splits * te * 4);
-    max_tiles = std::max(max_tiles, (size_t)nt * mt);
+    const size_t tiles = (size_t)c.ntiles * c.mtiles;
+    if (c.splits > 1)
+      part = std::max(part, tiles * c.splits * c.w * c.MB * c.nbw * 256 * sizeof(float));
+    max_tiles = std::max(max_tiles, tiles);
   }
+  w.ss_ld = ss_ld_of(D, Mp);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -132,7 +145,9 @@ static Ws ws_layout(const mv_dims& D, int B, int T) {
   };
   w.x = take((size_t)M * D.d * 4);
   w.xa = take((size_t)Mp * D.d * 2);
+  w.ao = take((size_t)Mp * D.d * 2);
   w.ha = take((size_t)Mp * D.F * 2);
+  w.ss = take((size_t)w.ss_ld * Mp * 4);
   w.q = take((size_t)M * D.d * 2);
   w.rope = take((size_t)M * (D.hd / 2) * 8);
   w.po = take((size_t)(w.nsplit + 1) * M * D.d * 4);
@@ -165,11 +180,21 @@ static mvk::GemmArgs gemm_args(const mv_dims& D, int kind, int M, void* ws, cons
   const GemmCfg c = gemm_cfg(D, kind, Mp);
   g.M = M;
   g.Mp = Mp;
+  g.N = c.N;
+  g.K = c.K;
+  g.w = c.w;
   g.nbw = c.nbw;
   g.splits = c.splits;
+  g.epi = c.epi;
+  g.ss_ld = L.ss_ld;
   g.partial = at<float>(ws, L.part);
   g.counters = at<int>(ws, L.counters);
   return g;
+}
+
+// Column tiles of a residual GEMM = entries per row of the sums of squares it writes.
+static int ss_tiles_of(const mv_dims& D, int kind, int M) {
+  return gemm_cfg(D, kind, round16(M)).ntiles;
 }
 
 // ---------------------------------------------------------------------------
@@ -209,25 +234,35 @@ static int enq_attention(const mv_dims& D, int B, const mv_tree& t, const int32_
   return MV_OK;
 }
 
-// One decoder layer over the B*T rows of x (ws.rope holds the RoPE tables).
+// Normalised-GEMM operand of x: xa = bf16(x * gain) packed, ss[0][m] = sum x^2.
+static int enq_norm_prep(const mv_dims& D, int M, const float* x, const void* gain, void* ws,
+                         const Ws& L, hipStream_t s) {
+  MV_HIP(mvk::launch_norm_prep(x, static_cast<const u16*>(gain), at<u16>(ws, L.xa),
+                               at<float>(ws, L.ss), L.ss_ld, M, D.d, s));
+  return MV_OK;
+}
+
+// One decoder layer over the B*T rows of x.  On entry ws.xa holds
+// bf16(x * attn_norm) and ws.ss the rows' sums of squares in ss_tiles_in
+// entries (ws.rope the RoPE tables).  With next_gain the down GEMM leaves the
+// same for the next norm (entries: ss_tiles_of(G_DOWN)).
 static int enq_layer(const mv_dims& D, int B, const mv_tree& t, const int32_t* n_prefix,
-                     const mv_layer_weights& w, const mv_kv& kv, int layer, float* x, void* ws,
-                     const Ws& L, hipStream_t s) {
-  const int M = B * t.T, Mp = round16(M);
+                     const mv_layer_weights& w, const mv_kv& kv, int layer, float* x,
+                     int ss_tiles_in, const void* next_gain, void* ws, const Ws& L,
+                     hipStream_t s) {
+  const int M = B * t.T;
   u16* xa = at<u16>(ws, L.xa);
+  u16* ao = at<u16>(ws, L.ao);
   u16* ha = at<u16>(ws, L.ha);
   u16* q = at<u16>(ws, L.q);
+  float* ss = at<float>(ws, L.ss);
   const size_t le = kv_layer_elems(kv);
 
-  prof_begin(s);
-  MV_HIP(mvk::launch_rmsnorm_pack(x, static_cast<const u16*>(w.attn_norm), xa, M, Mp, D.d, s));
-  prof_end(MV_K_NORM, s);
   mvk::GemmArgs g = gemm_args(D, G_QKV, M, ws, L);
   g.A = xa;
   g.W = static_cast<const u16*>(w.wqkv);
-  g.N = 3 * D.d;
-  g.K = D.d;
-  g.epi = mvk::EPI_QKV;
+  g.ss = ss;
+  g.ss_tiles = ss_tiles_in;
   g.qkv.q = q;
   g.qkv.kcache = static_cast<u16*>(kv.k) + (size_t)layer * le;
   g.qkv.vcache = static_cast<u16*>(kv.v) + (size_t)layer * le;
@@ -244,31 +279,27 @@ static int enq_layer(const mv_dims& D, int B, const mv_tree& t, const int32_t* n
   prof_end(MV_K_QKV, s);
 
   prof_begin(s);
-  int rc = enq_attention(D, B, t, n_prefix, q, kv, layer, xa, 1, ws, L, s);
+  int rc = enq_attention(D, B, t, n_prefix, q, kv, layer, ao, 1, ws, L, s);
   if (rc) return rc;
   prof_end(MV_K_ATTN, s);
 
   mvk::GemmArgs o = gemm_args(D, G_O, M, ws, L);
-  o.A = xa;
+  o.A = ao;
   o.W = static_cast<const u16*>(w.wo);
-  o.N = D.d;
-  o.K = D.d;
-  o.epi = mvk::EPI_ADD;
   o.out_f32 = x;
+  o.next_gain = static_cast<const u16*>(w.ffn_norm);
+  o.xn_out = xa;
+  o.ss_out = ss;
   prof_begin(s);
   MV_HIP(mvk::launch_gemm(o, s));
   prof_end(MV_K_O, s);
 
-  prof_begin(s);
-  MV_HIP(mvk::launch_rmsnorm_pack(x, static_cast<const u16*>(w.ffn_norm), xa, M, Mp, D.d, s));
-  prof_end(MV_K_NORM, s);
   mvk::GemmArgs gu = gemm_args(D, G_GU, M, ws, L);
   gu.A = xa;
   gu.W = static_cast<const u16*>(w.wgate);
   gu.W2 = static_cast<const u16*>(w.wup);
-  gu.N = D.F;
-  gu.K = D.d;
-  gu.epi = mvk::EPI_SWIGLU;
+  gu.ss = ss;
+  gu.ss_tiles = ss_tiles_of(D, G_O, M);
   gu.out_bf16 = ha;
   prof_begin(s);
   MV_HIP(mvk::launch_gemm(gu, s));
@@ -277,28 +308,32 @@ static int enq_layer(const mv_dims& D, int B, const mv_tree& t, const int32_t* n
   mvk::GemmArgs dn = gemm_args(D, G_DOWN, M, ws, L);
   dn.A = ha;
   dn.W = static_cast<const u16*>(w.wdown);
-  dn.N = D.d;
-  dn.K = D.F;
-  dn.epi = mvk::EPI_ADD;
   dn.out_f32 = x;
+  dn.next_gain = static_cast<const u16*>(next_gain);
+  dn.xn_out = xa;
+  dn.ss_out = ss;
   prof_begin(s);
   MV_HIP(mvk::launch_gemm(dn, s));
   prof_end(MV_K_DOWN, s);
   return MV_OK;
 }
 
-// Final RMSNorm and LM head: logits [M][V] fp32.
+// LM head: logits [M][V] fp32 of rmsnorm(x) * final_norm.  With ss_tiles > 0
+// ws.xa / ws.ss already hold the final norm's operand (left by the last
+// layer); otherwise it is prepared from x here.
 static int enq_lm_head(const mv_dims& D, int M, const float* x, const void* final_norm,
-                       const void* lm, float* logits, void* ws, const Ws& L, hipStream_t s) {
-  u16* xa = at<u16>(ws, L.xa);
-  MV_HIP(mvk::launch_rmsnorm_pack(x, static_cast<const u16*>(final_norm), xa, M, round16(M), D.d,
-                                  s));
+                       const void* lm, float* logits, int ss_tiles, void* ws, const Ws& L,
+                       hipStream_t s) {
+  if (ss_tiles <= 0) {
+    const int rc = enq_norm_prep(D, M, x, final_norm, ws, L, s);
+    if (rc) return rc;
+    ss_tiles = 1;
+  }
   mvk::GemmArgs g = gemm_args(D, G_LM, M, ws, L);
-  g.A = xa;
+  g.A = at<u16>(ws, L.xa);
   g.W = static_cast<const u16*>(lm);
-  g.N = D.V;
-  g.K = D.d;
-  g.epi = mvk::EPI_STORE;
+  g.ss = at<float>(ws, L.ss);
+  g.ss_tiles = ss_tiles;
   g.out_f32 = logits;
   MV_HIP(mvk::launch_gemm(g, s));
   return MV_OK;
@@ -462,7 +497,8 @@ MV_API int mv_decoder_layer(const mv_dims* dims, int32_t B, const mv_tree* tree,
   const hipStream_t s = (hipStream_t)stream;
   MV_HIP(mvk::launch_rope_table(n_prefix, tree->depth_of, at<float2>(ws, L.rope), B, tree->T,
                                 dims->hd, s));
-  return enq_layer(*dims, B, *tree, n_prefix, *w, *kv, layer, x, ws, L, s);
+  if ((rc = enq_norm_prep(*dims, B * tree->T, x, w->attn_norm, ws, L, s))) return rc;
+  return enq_layer(*dims, B, *tree, n_prefix, *w, *kv, layer, x, 1, nullptr, ws, L, s);
 }
 
 MV_API int mv_embed(const mv_dims* dims, int32_t M, const int32_t* tokens, const void* embed,
@@ -488,7 +524,7 @@ MV_API int mv_lm_head(const mv_dims* dims, int32_t M, const float* x, const void
   if ((rc = check_ws(dims, B, T, ws_bytes, ws))) return rc;
   const Ws L = ws_layout(*dims, B, T);
   const hipStream_t s = (hipStream_t)stream;
-  return enq_lm_head(*dims, M, x, final_norm, lm_head, logits, ws, L, s);
+  return enq_lm_head(*dims, M, x, final_norm, lm_head, logits, 0, ws, L, s);
 }
 
 MV_API int mv_accept(int32_t B, int32_t T, int32_t V, int32_t d, const float* logits,
@@ -554,6 +590,22 @@ struct mv_ctx {
   std::vector<hipEvent_t> prof_ev;
 };
 
+// All L layers; the last one leaves the final norm's operand in ws.xa / ws.ss.
+static int enq_layers(mv_ctx* c, const mv_tree& tree, float* x, hipStream_t s) {
+  const mv_step_desc& d = c->d;
+  const mv_dims& D = d.dims;
+  const int M = d.B * tree.T;
+  int rc;
+  for (int l = 0; l < D.L; ++l) {
+    const void* next_gain = l + 1 < D.L ? c->layers[l + 1].attn_norm : d.final_norm;
+    const int ss_in = l == 0 ? 1 : ss_tiles_of(D, G_DOWN, M);
+    if ((rc = enq_layer(D, d.B, tree, d.n_prefix, c->layers[l], d.kv, l, x, ss_in, next_gain,
+                        d.ws, c->L, s)))
+      return rc;
+  }
+  return MV_OK;
+}
+
 static int enq_step(mv_ctx* c, hipStream_t s) {
   const mv_step_desc& d = c->d;
   const mv_dims& D = d.dims;
@@ -578,11 +630,14 @@ static int enq_step(mv_ctx* c, hipStream_t s) {
   MV_HIP(mvk::launch_embed(d.tree_tok, static_cast<const u16*>(d.embed), x, nullptr,
                            M, D.d, D.V, d.n_prefix, d.tree.depth_of, at<float2>(ws, L.rope), T,
                            D.hd, s));
-  prof_end(MV_K_EMBED, s);
-  for (int l = 0; l < D.L; ++l)
-    if ((rc = enq_layer(D, B, d.tree, d.n_prefix, c->layers[l], d.kv, l, x, ws, L, s))) return rc;
   prof_begin(s);
-  if ((rc = enq_lm_head(D, M, x, d.final_norm, d.lm_head, d.logits, ws, L, s))) return rc;
+  if ((rc = enq_norm_prep(D, M, x, c->layers[0].attn_norm, ws, L, s))) return rc;
+  prof_end(MV_K_NORM, s);
+  if ((rc = enq_layers(c, d.tree, x, s))) return rc;
+  prof_begin(s);
+  if ((rc = enq_lm_head(D, M, x, d.final_norm, d.lm_head, d.logits, ss_tiles_of(D, G_DOWN, M),
+                        ws, L, s)))
+    return rc;
   prof_end(MV_K_LM_HEAD, s);
   prof_begin(s);
   if ((rc = enq_accept(B, T, D.V, D.d, d.logits, d.tree, d.tree_tok, d.accept, d.u_draws,
@@ -712,9 +767,11 @@ MV_API int mv_prefill(mv_ctx* c, const int32_t* ids, int32_t ld, const int32_t* 
     MV_HIP(mvk::launch_embed(c->chunk_tok, static_cast<const u16*>(d.embed), x,
                              nullptr, M, D.d, D.V, d.n_prefix, chain.depth_of,
                              at<float2>(ws, L.rope), T, D.hd, s));
-    for (int l = 0; l < D.L; ++l)
-      if ((rc = enq_layer(D, B, chain, d.n_prefix, c->layers[l], d.kv, l, x, ws, L, s))) return rc;
-    if ((rc = enq_lm_head(D, M, x, d.final_norm, d.lm_head, d.logits, ws, L, s))) return rc;
+    if ((rc = enq_norm_prep(D, M, x, c->layers[0].attn_norm, ws, L, s))) return rc;
+    if ((rc = enq_layers(c, chain, x, s))) return rc;
+    if ((rc = enq_lm_head(D, M, x, d.final_norm, d.lm_head, d.logits, ss_tiles_of(D, G_DOWN, M),
+                          ws, L, s)))
+      return rc;
     MV_HIP(mvk::launch_row_stats(d.logits, M, D.V, MV_ACCEPT_GREEDY, 1.0, at<int32_t>(ws, L.amax),
                                  at<double>(ws, L.stats), s));
     MV_HIP(mvk::launch_prefill_select(d.logits, at<int32_t>(ws, L.amax), cnt, B, T, D.V,

@@ -94,29 +94,37 @@ struct QkvArgs {
 };
 
 struct GemmArgs {
-  const u16* A;      // fragment-packed bf16 activations [Mp][K] (rows >= M zero)
-  const u16* W;      // k-major packed weights [N/16 blocks per k-block] (SWIGLU: gate)
+  const u16* A;      // fragment-packed bf16 activations [Mp][K] (row-block-major)
+  const u16* W;      // k-major packed weights [K/32][N/16] blocks (SWIGLU: gate)
   const u16* W2;     // SWIGLU: up weights (same layout)
-  int M, Mp, N, K;   // SWIGLU: N = F (output columns)
-  int nbw;           // 16-column blocks per workgroup tile (2 or 4)
+  int M, Mp, N, K;   // SWIGLU: N = F (features)
+  int w, nbw;        // waves per workgroup, 16-column blocks per wave (SWIGLU, QKV: 2)
   int splits;        // K splits across workgroups
   int epi;
+  const float* ss;   // nullable: rows' partial sums of squares [Mp][ss_ld] (first
+  int ss_tiles;      //   ss_tiles entries of a row used; ss_ld % 4 == 0) of the
+  int ss_ld;         //   un-normalised input; accumulators scaled by 1/sqrt(sum/K + 1e-5)
   float* out_f32;    // STORE / ADD target [M][N]
   u16* out_bf16;     // SWIGLU target (packed [Mp][N])
-  float* partial;    // split-K partial tiles [tiles][splits][TM*TN]
+  const u16* next_gain;  // ADD, nullable: gain of the norm that reads x next
+  u16* xn_out;           // ADD: packed bf16 [Mp][N] = x * next_gain
+  float* ss_out;         // ADD: [Mp][ss_ld] rows' sums of squares of x per column tile
+  float* partial;    // split-K partial tiles
   int* counters;     // split-K arrival counters [tiles], zero between launches
   QkvArgs qkv;
 };
 
-int gemm_tiles(const GemmArgs& g, int* mtiles, int* ntiles);
+int gemm_mb(int Mp);                                  // 16-row blocks per tile
+int gemm_kc(int MB);                                  // k-blocks per chunk
+int gemm_ntiles(int epi, int N, int w, int nbw);      // column tiles
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
 hipError_t launch_pack(const u16* src, u16* dst, int R, int C, int rope_hd, int rope_rows,
                        hipStream_t s);
 hipError_t launch_embed(const int32_t* tok, const u16* E, float* x, float* ss, int M, int d,
                         int V, const int32_t* n_prefix, const int32_t* depth_of, float2* rope,
                         int T, int hd, hipStream_t s);
-hipError_t launch_rmsnorm_pack(const float* x, const u16* g, u16* out_packed, int M, int Mp,
-                               int d, hipStream_t s);
+hipError_t launch_norm_prep(const float* x, const u16* g, u16* xn_packed, float* ss, int ss_ld,
+                            int M, int d, hipStream_t s);
 hipError_t launch_rope_table(const int32_t* n_prefix, const int32_t* depth_of, float2* rope,
                              int B, int T, int hd, hipStream_t s);
 hipError_t launch_attention(const u16* q, const u16* kc, const u16* vc, const int32_t* n_prefix,

@@ -1,29 +1,35 @@
 // Skinny bf16 GEMM for the tree-verify forward: Y[M][N] = A[M][K] * W[N][K]^T
-// with M = batch x tree nodes (16..256), N and K the model's widths.
+// with M = batch x tree nodes (16..1024), N and K the model's widths.
 //
 // At M ~ 64 every weight byte is used 64 times, so the kernel is bound by
 // streaming W from HBM once; the MFMA units (v_mfma_f32_16x16x32_bf16) only
-// need to keep up.  Three measured choices shape it:
+// need to keep up.  Layout of the work (measured on MI355X):
 //  * Weights are fragment-packed k-block-major ([K/32][N/16][64 lanes][8]):
-//    the 1 KiB operand blocks of all columns for one 32-wide k-block are
-//    adjacent, and the 4 waves of a workgroup take interleaved k-blocks, so
-//    the whole grid sweeps a dense window of memory (as a plain streaming
-//    copy does) instead of thousands of streams at power-of-two strides that
-//    alias onto few HBM channels.
-//  * The main loop is a branch-free register pipeline (A and B fragments of
-//    D k-blocks in flight); out-of-range stages are zeroed by selects, so the
+//    the 1 KiB operand blocks of all columns of one 32-wide k-block are
+//    adjacent, so the grid sweeps a dense window of memory.
+//  * Each wave owns NBW 16-column blocks over the workgroup's k-range and
+//    keeps a register ring of KC k-blocks of them in flight (consumed, then
+//    refilled in place; scheduling barriers keep the refill after the MFMAs
+//    that read the stage, so no register copies undo the prefetch).
+//  * The activation operand is staged once per workgroup in LDS, KC k-blocks
+//    per chunk, double-buffered, and shared by the W waves; k-blocks past the
+//    range are staged as zeros, so the main loop has no branches and the
 //    compiler's wait counts stay partial.
-//  * K is split over `splits` workgroups when the N tiles alone cannot fill
-//    the chip.  Each split writes its partial tile with write-through
+//  * K is split over `splits` workgroups when the column tiles alone cannot
+//    fill the chip.  Each split writes its partial tile with write-through
 //    (system-scope) stores, waits for them, and bumps the tile's arrival
-//    counter; the last workgroup to arrive reads the partials with
-//    cache-bypassing loads, sums them in split order and applies the
-//    epilogue: one kernel, a deterministic result, and no L2-wide
-//    invalidation (which would evict the other workgroups' operands).
+//    counter; the last workgroup to arrive reads all partials with batched
+//    cache-bypassing loads and sums them in split order (a deterministic
+//    result, no separate reduce launch, no L2-wide invalidation).
+// RMSNorm is folded in: the operand of a normalised GEMM is bf16(x * gain)
+// and the per-row factor 1/sqrt(mean(x^2) + 1e-5) is applied to the
+// accumulators, from row sums of squares that the producing GEMM wrote per
+// column tile (summed here in tile order).
 // Epilogues:
 //   STORE   out = y                          (LM head logits)
-//   ADD     out += y                         (residual stream: O-proj, down)
-//   SWIGLU  tile = [gate cols | up cols]; h = SiLU(g) * u -> bf16 packed
+//   ADD     x += y (residual stream: O-proj, down); optionally the next
+//           norm's operand bf16(x * gain) and the rows' sums of squares
+//   SWIGLU  wave owns gate block j and up block j; h = SiLU(g) * u -> bf16
 //   QKV     RoPE on q, k at each row's position; q -> bf16 rows; k, v ->
 //           KV cache slot n + node index
 #include "common.hpp"
@@ -31,23 +37,14 @@
 namespace mvk {
 
 // Logical output feature of packed weight row p of the fused QKV matrix.
-// When a tile (16*NBW columns) is narrower than a head, q/k rows are
-// permuted so that each tile holds P = 8*NBW first-half dims of one head and
-// their RoPE partners (dim + hd/2); v rows are never permuted.
-__host__ __device__ __forceinline__ int qkv_feature(int p, int d, int hd, int P, bool perm) {
-  if (!perm || p >= 2 * d) return p;
-  const int h = p / hd, e = p % hd, j = e / (2 * P), ee = e % (2 * P);
-  return h * hd + (ee < P ? j * P + ee : hd / 2 + j * P + (ee - P));
-}
-
-__device__ __forceinline__ int qkv_partner(int p, int f, int d, int hd, int P, bool perm) {
-  if (f >= 2 * d) return p;
-  if (perm) {
-    const int ee = (p % hd) % (2 * P);
-    return ee < P ? p + P : p - P;
-  }
-  const int i = (f % d) % hd;
-  return i < hd / 2 ? p + hd / 2 : p - hd / 2;
+// q/k rows are permuted (when the head is wider than 16) so that each pair
+// of 16-row blocks holds 16 first-half dims of one head and their RoPE
+// partners (dim + hd/2), which then meet in the same lane of one wave; v rows
+// are never permuted.
+__host__ __device__ __forceinline__ int qkv_feature(int p, int d, int hd) {
+  if (hd < 32 || p >= 2 * d) return p;
+  const int h = p / hd, e = p % hd, j = e / 32, ee = e % 32;
+  return h * hd + (ee < 16 ? j * 16 + ee : hd / 2 + j * 16 + (ee - 16));
 }
 
 // QKV epilogue of one element (row m, logical feature f) with RoPE partner yp.
@@ -78,128 +75,164 @@ __device__ __forceinline__ void qkv_store(const QkvArgs& a, int m, int f, float 
 }
 
 // Split-K partial exchange between workgroups that may sit on different
-// XCDs (separate L2s): system-scope stores (written through to memory) and
-// 16-byte vector loads that bypass the caches (system-coherent sc0 sc1).
-// The compiler waits for every system-scope atomic load on its own, which
-// serialises them; these loads are issued as a batch and waited for once
-// (the compiler does not track inline-asm loads, hence the explicit vmcnt
-// wait).  Stores stay compiler-generated so that its hazard checks (store
-// data registers rewritten right after issue) still apply.
-__device__ __forceinline__ void store_sys(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-__device__ __forceinline__ f32x4 load_nc16(const float* p) {
-  f32x4 v;
-  asm volatile("global_load_dwordx4 %0, %1, off sc0 sc1" : "=v"(v) : "v"(p) : "memory");
-  return v;
-}
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// Orders a register's later uses after the preceding wait_vmem().
-__device__ __forceinline__ void after_wait(f32x4& v) { asm volatile("" : "+v"(v)); }
+// XCDs (separate L2s): 16-byte buffer stores and loads with the system-scope
+// cache policy (sc0 sc1: stores written through to memory, loads bypassing
+// the caches, so no L2-wide invalidation is needed).  They are ordinary
+// compiler-tracked memory operations, so the loads of a batch are issued
+// together and waited for once.  Raw buffer accesses are range-checked by
+// the hardware: an offset past the resource's size reads zeros, which the
+// batches use for splits that do not exist.
+#define MV_CPOL_SYS 17              /* sc0 | sc1 */
+#define MV_BUF_DWORD3 0x00020000    /* raw (untyped) buffer resource */
+#define MV_BUF_NONE 0x7ffffff0      /* an offset past any partial buffer */
 
-template <int MB, int NBW, int D, int EPI>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
-  constexpr int TM = MB * 16, TN = NBW * 16, LDT = TN + 1;
-  __shared__ float red[TM * LDT];
+// k-blocks per activation chunk (= depth of the weight ring): the LDS chunk
+// holds KC * MB KiB per buffer.
+template <int MB>
+struct GemmShape {
+  static constexpr int KC = MB <= 4 ? 8 : (MB == 8 ? 4 : 2);
+};
+
+int gemm_kc(int MB) { return MB <= 4 ? 8 : (MB == 8 ? 4 : 2); }
+
+template <int MB, int W, int NBW, int EPI>
+__global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
+  constexpr int KC = GemmShape<MB>::KC;
+  constexpr int APC = KC * MB;                 // 1 KiB activation pieces per chunk
+  constexpr int AI = APC / W;                  // pieces staged per thread
+  static_assert(APC % W == 0, "chunk pieces must divide among the waves");
+  constexpr int TR = MB * 16;                  // rows of a tile
+  __shared__ bf16x8 As[2][APC][64];            // [buf][kl * MB + rb][lane]
+  __shared__ float rs_s[TR];
+  __shared__ float ssw[W][TR];
   __shared__ int s_last;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int mt = blockIdx.x, nt = blockIdx.y, split = blockIdx.z;
+  const int nt = blockIdx.x, split = blockIdx.y, mt = blockIdx.z;
   const int KB = g.K >> 5;
-  const int kb_lo = (int)((long long)KB * split / g.splits);
-  const int kb_hi = (int)((long long)KB * (split + 1) / g.splits);
-  const int first = kb_lo + wave;
-  const int count = first < kb_hi ? (kb_hi - first + 3) / 4 : 0;
-  const int rounds = (count + D - 1) / D;
-
-  // B block (kb, nb) at (kb * NBtot + nb) * 64 + lane
-  const int NBtot = g.N >> 4;
-  const bf16x8* Wg = reinterpret_cast<const bf16x8*>(g.W) + lane;
-  const bf16x8* Wu = reinterpret_cast<const bf16x8*>(g.W2) + lane;
-  const int nb0 = EPI == EPI_SWIGLU ? nt * (NBW / 2) : nt * NBW;   // gate/up share row blocks
-  // A block (rb, kb) at (rb * KB + kb) * 64 + lane (rows beyond M are zeros)
-  const bf16x8* Ap = reinterpret_cast<const bf16x8*>(g.A) + lane;
+  const int lo = (int)((long long)KB * split / g.splits);
+  const int hi = (int)((long long)KB * (split + 1) / g.splits);
+  const int nchunks = (hi - lo + KC - 1) / KC;
+  const int NBtot = g.N >> 4;                  // 16-column blocks of W (and of W2)
   const int MBtot = g.Mp >> 4;
+
+  // this wave's column blocks (waves past the last block compute on a
+  // clamped block and store nothing)
+  const int wb = nt * W + wave;
+  const int first_blk = EPI == EPI_SWIGLU ? wb : wb * NBW;
+  const int blk_cnt = EPI == EPI_SWIGLU ? 1 : NBW;
+  const bool active = first_blk + blk_cnt <= NBtot;
+  const int cb = min(first_blk, NBtot - blk_cnt);
+  const bf16x8* Bp[NBW];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) {
+    if (EPI == EPI_SWIGLU)
+      Bp[nb] = reinterpret_cast<const bf16x8*>(nb == 0 ? g.W : g.W2) + (size_t)cb * 64 + lane;
+    else
+      Bp[nb] = reinterpret_cast<const bf16x8*>(g.W) + (size_t)(cb + nb) * 64 + lane;
+  }
+  const bf16x8* Ap = reinterpret_cast<const bf16x8*>(g.A) + lane;
+
+  // per-row normalisation factors of this tile (row m's partial sums are
+  // contiguous: 16-byte loads, eight in flight, summed in tile order)
+  if (g.ss) {
+    for (int r = threadIdx.x; r < TR; r += W * 64) {
+      const int m = mt * TR + r;
+      float s = 0.f;
+      if (m < g.M) {
+        const float* row = g.ss + (size_t)m * g.ss_ld;
+        const f32x4* p4 = reinterpret_cast<const f32x4*>(row);
+        const int n4 = g.ss_tiles >> 2;
+        int t = 0;
+        for (; t + 8 <= n4; t += 8) {
+          f32x4 v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] = p4[t + u];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) s = s + v[u][0] + v[u][1] + v[u][2] + v[u][3];
+        }
+        for (; t < n4; ++t) {
+          const f32x4 v = p4[t];
+          s = s + v[0] + v[1] + v[2] + v[3];
+        }
+        for (int e = n4 * 4; e < g.ss_tiles; ++e) s += row[e];
+      }
+      rs_s[r] = 1.0f / sqrtf(s / (float)g.K + 1e-5f);
+    }
+  }
 
   f32x4 acc[MB][NBW];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+  for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < NBW; ++nb) acc[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  bf16x8 ab[D][MB], bb[D][NBW];
-  auto load = [&](int d, int j) {      // this wave's j-th k-block into stage d
-    const int k = min(first + 4 * j, kb_hi - 1);
+  bf16x8 ar[AI];
+  auto loadA = [&](int c) {
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) {
-      if (EPI == EPI_SWIGLU) {
-        const bf16x8* base = nb < NBW / 2 ? Wg : Wu;
-        bb[d][nb] = base[((size_t)k * NBtot + nb0 + (nb % (NBW / 2))) * 64];
-      } else {
-        bb[d][nb] = Wg[((size_t)k * NBtot + nb0 + nb) * 64];
-      }
-    }
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int rb = min(mt * MB + mb, MBtot - 1);
-      ab[d][mb] = Ap[((size_t)rb * KB + k) * 64];
+    for (int i = 0; i < AI; ++i) {
+      const int piece = i * W + wave;
+      const int kl = piece / MB, rb = piece % MB;
+      const int k = min(lo + c * KC + kl, hi - 1);
+      const int rbg = min(mt * MB + rb, MBtot - 1);
+      ar[i] = Ap[((size_t)rbg * KB + k) * 64];
     }
   };
-
-  if (count > 0) {
+  auto storeA = [&](int buf, int c) {          // k-blocks past the range are zeros
 #pragma unroll
-    for (int d = 0; d < D; ++d) load(d, d);
-  }
-  for (int r = 0; r < rounds; ++r) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      const bool valid = r * D + d < count;
-      bf16x8 av[MB], bv[NBW];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) av[mb] = valid ? ab[d][mb] : bf16x8{};
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) bv[nb] = bb[d][nb];
-      load(d, r * D + d + D);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) acc[mb][nb] = mfma16x16x32(av[mb], bv[nb], acc[mb][nb]);
+    for (int i = 0; i < AI; ++i) {
+      const int piece = i * W + wave;
+      const int kl = piece / MB;
+      As[buf][piece][lane] = (lo + c * KC + kl < hi) ? ar[i] : bf16x8{};
     }
-  }
+  };
+  bf16x8 br[KC][NBW];
+  auto loadB = [&](int s, int kb) {
+    const int k = min(kb, hi - 1);
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) br[s][nb] = Bp[nb][(size_t)k * NBtot * 64];
+  };
 
-  // ---- sum the 4 waves' partial tiles in LDS (wave order: deterministic)
-  for (int w = 0; w < 4; ++w) {
-    if (wave == w) {
+  loadA(0);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+  for (int s = 0; s < KC; ++s) loadB(s, lo + s);
+  storeA(0, 0);
+  __syncthreads();
+  for (int c = 0; c < nchunks; ++c) {
+    const int buf = c & 1;
+    loadA(c + 1);
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb)
+    for (int kk = 0; kk < KC; ++kk) {
+      bf16x8 a[MB];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float* p = &red[(mb * 16 + (lane >> 4) * 4 + r) * LDT + nb * 16 + (lane & 15)];
-            *p = (w == 0 ? 0.f : *p) + acc[mb][nb][r];
-          }
+      for (int rb = 0; rb < MB; ++rb) a[rb] = As[buf][kk * MB + rb][lane];
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) acc[rb][nb] = mfma16x16x32(a[rb], br[kk][nb], acc[rb][nb]);
+      __builtin_amdgcn_sched_barrier(0);
+      loadB(kk, lo + (c + 1) * KC + kk);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    storeA(buf ^ 1, c + 1);
     __syncthreads();
   }
 
   // ---- split-K: the last workgroup of the tile sums the splits in order
   if (g.splits > 1) {
-    constexpr int NQ = TM * TN / 4;            // float4 pieces per tile
-    constexpr int Q = (NQ + 255) / 256;        // pieces per thread
-    const int tile = mt * gridDim.y + nt;
-    float* part = g.partial + (size_t)tile * g.splits * (TM * TN);
+    constexpr int WQ = MB * NBW;               // f32x4 items per lane of one wave
+    constexpr int SB = WQ >= 16 ? 1 : 16 / WQ; // splits loaded per batch
+    const int tile = mt * gridDim.x + nt;
+    const int per_split = W * WQ * 256 * 4;    // bytes of one split's tile
+    const __amdgpu_buffer_rsrc_t part = __builtin_amdgcn_make_buffer_rsrc(
+        g.partial + (size_t)tile * g.splits * (per_split / 4), (short)0, g.splits * per_split,
+        MV_BUF_DWORD3);
+    const int lane_off = (wave * WQ * 256 + lane * 4) * 4;
 #pragma unroll
-    for (int i = 0; i < Q; ++i) {
-      const int e = (i * 256 + threadIdx.x) * 4, r = e / TN, c = e % TN;
-      if (e < TM * TN) {
-        const float* src = &red[r * LDT + c];
-        float* dst = part + (size_t)split * (TM * TN) + e;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) store_sys(dst + j, src[j]);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);       // this thread's write-through stores are done
+    for (int q = 0; q < WQ; ++q)
+      __builtin_amdgcn_raw_buffer_store_b128(acc[q / NBW][q % NBW], part,
+                                             split * per_split + lane_off + q * 1024, 0, MV_CPOL_SYS);
+    __builtin_amdgcn_s_waitcnt(0);           // this thread's write-through stores are done
     __syncthreads();
     if (threadIdx.x == 0) {
       const int prev = __hip_atomic_fetch_add(g.counters + tile, 1, __ATOMIC_RELAXED,
@@ -208,113 +241,196 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     }
     __syncthreads();
     if (!s_last) return;
-    for (int s0 = 0; s0 < g.splits; s0 += 4) {
-      f32x4 v[4][Q];
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+    for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
-        for (int i = 0; i < Q; ++i)
-          if (s0 + s < g.splits && (i * 256 + threadIdx.x) < NQ)
-            v[s][i] = load_nc16(part + (size_t)(s0 + s) * (TM * TN) + (i * 256 + threadIdx.x) * 4);
-      wait_vmem();
+      for (int nb = 0; nb < NBW; ++nb) acc[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < g.splits; s0 += SB) {
+      f32x4 v[SB][WQ];
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+      for (int s = 0; s < SB; ++s) {
+        const int base = s0 + s < g.splits ? (s0 + s) * per_split + lane_off : MV_BUF_NONE;
 #pragma unroll
-        for (int i = 0; i < Q; ++i)
-          if (s0 + s < g.splits && (i * 256 + threadIdx.x) < NQ) after_wait(v[s][i]);
-#pragma unroll
-      for (int i = 0; i < Q; ++i) {
-        const int e = (i * 256 + threadIdx.x) * 4, r = e / TN, c = e % TN;
-        if (e >= TM * TN) continue;
-        float* dst = &red[r * LDT + c];
-        f32x4 y = s0 == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : f32x4{dst[0], dst[1], dst[2], dst[3]};
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          if (s0 + s < g.splits) {
-            y += v[s][i];
-          }
-        dst[0] = y[0];
-        dst[1] = y[1];
-        dst[2] = y[2];
-        dst[3] = y[3];
+        for (int q = 0; q < WQ; ++q)
+          v[s][q] = __builtin_amdgcn_raw_buffer_load_b128(
+              part, base == MV_BUF_NONE ? MV_BUF_NONE : base + q * 1024, 0, MV_CPOL_SYS);
       }
+#pragma unroll
+      for (int s = 0; s < SB; ++s)
+#pragma unroll
+        for (int q = 0; q < WQ; ++q) acc[q / NBW][q % NBW] += v[s][q];
     }
     if (threadIdx.x == 0)
       __hip_atomic_store(g.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
   }
 
-  // ---- epilogues on the complete tile
-  const int m0 = mt * TM;
-  if (EPI == EPI_SWIGLU) {
-    constexpr int P = TN / 2;
-    for (int e = threadIdx.x; e < TM * P; e += 256) {
-      const int r = e / P, c = e % P, m = m0 + r;
-      if (m >= g.Mp) continue;
-      const float gv = red[r * LDT + c], uv = red[r * LDT + c + P];
-      const float h = m < g.M ? silu_f(gv) * uv : 0.f;
-      g.out_bf16[packed_index(m, nt * P + c, g.N)] = f32_to_bf16(h);
+  // ---- epilogues: lane holds rows rb*16 + 4*(lane/16) + r, column lane%16 of each block
+  const int col = lane & 15;
+  const int row0 = mt * TR + 4 * (lane >> 4);
+  if (g.ss) {
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float f = rs_s[rb * 16 + 4 * (lane >> 4) + r];
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) acc[rb][nb][r] *= f;
+      }
+  }
+  if (EPI == EPI_STORE) {
+    if (active) {
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int m = row0 + rb * 16 + r;
+            if (m < g.M) g.out_f32[(size_t)m * g.N + (first_blk + nb) * 16 + col] = acc[rb][nb][r];
+          }
     }
-  } else if (EPI == EPI_STORE || EPI == EPI_ADD) {
-    for (int e = threadIdx.x; e < TM * TN; e += 256) {
-      const int r = e / TN, c = e % TN, m = m0 + r;
-      if (m >= g.M) continue;
-      float* o = g.out_f32 + (size_t)m * g.N + nt * TN + c;
-      if (EPI == EPI_ADD) *o += red[r * LDT + c];
-      else *o = red[r * LDT + c];
+  } else if (EPI == EPI_ADD) {
+    const bool nxt = g.next_gain != nullptr;
+    float sq[MB][4];
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sq[rb][r] = 0.f;
+    if (active) {
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) {
+        const int n = (first_blk + nb) * 16 + col;
+        const float gn = nxt ? bf16_to_f32(g.next_gain[n]) : 0.f;
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int m = row0 + rb * 16 + r;
+            if (m < g.M) {
+              float* o = g.out_f32 + (size_t)m * g.N + n;
+              const float xv = *o + acc[rb][nb][r];
+              *o = xv;
+              if (nxt) {
+                g.xn_out[packed_index(m, n, g.N)] = f32_to_bf16(xv * gn);
+                sq[rb][r] += xv * xv;
+              }
+            }
+          }
+      }
+    }
+    if (nxt) {
+      // rows' sums of squares: over this lane group's 16 columns, then the waves
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = sq[rb][r];
+          v += __shfl_xor(v, 1, 64);
+          v += __shfl_xor(v, 2, 64);
+          v += __shfl_xor(v, 4, 64);
+          v += __shfl_xor(v, 8, 64);
+          if (col == 0) ssw[wave][rb * 16 + 4 * (lane >> 4) + r] = v;
+        }
+      __syncthreads();
+      for (int r = threadIdx.x; r < TR; r += W * 64) {
+        const int m = mt * TR + r;
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) s += ssw[w][r];
+        if (m < g.M) g.ss_out[(size_t)m * g.ss_ld + nt] = s;
+      }
+    }
+  } else if (EPI == EPI_SWIGLU) {
+    if (active) {
+      const int f = wb * 16 + col;
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = row0 + rb * 16 + r;
+          if (m < g.M) {
+            const float h = silu_f(acc[rb][0][r]) * acc[rb][1][r];
+            g.out_bf16[packed_index(m, f, g.N)] = f32_to_bf16(h);
+          }
+        }
     }
   } else if (EPI == EPI_QKV) {
     const QkvArgs& q = g.qkv;
-    const bool perm = 16 * NBW < q.hd;
-    for (int e = threadIdx.x; e < TM * TN; e += 256) {
-      const int r = e / TN, c = e % TN, m = m0 + r;
-      if (m >= g.M) continue;
-      const int n = nt * TN + c;
-      const int f = qkv_feature(n, q.d, q.hd, TN / 2, perm);
-      const int pc = qkv_partner(n, f, q.d, q.hd, TN / 2, perm) - nt * TN;
-      qkv_store(q, m, f, red[r * LDT + c], red[r * LDT + pc]);
-    }
+    const int p0 = first_blk * 16 + col;      // packed weight rows of the two blocks
+    const bool rot = p0 < 2 * q.d;
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = row0 + rb * 16 + r;
+        const float y0 = acc[rb][0][r], y1 = acc[rb][1][r];
+        // head dim 16: a block is one whole head, partners are 8 columns apart
+        const float s0 = __shfl_xor(y0, 8, 64), s1 = __shfl_xor(y1, 8, 64);
+        if (!active || m >= g.M) continue;
+        if (!rot) {
+          qkv_store(q, m, p0, y0, y0);
+          qkv_store(q, m, p0 + 16, y1, y1);
+        } else if (q.hd >= 32) {
+          const int f0 = qkv_feature(p0, q.d, q.hd);
+          qkv_store(q, m, f0, y0, y1);
+          qkv_store(q, m, f0 + q.hd / 2, y1, y0);
+        } else {
+          qkv_store(q, m, p0, y0, s0);
+          qkv_store(q, m, p0 + 16, y1, s1);
+        }
+      }
   }
 }
 
-template <int MB, int NBW, int D>
-static hipError_t launch_cfg(const GemmArgs& g, dim3 grid, hipStream_t s) {
-  const dim3 blk(256);
-  switch (g.epi) {
-    case EPI_STORE: hipLaunchKernelGGL((gemm_kernel<MB, NBW, D, EPI_STORE>), grid, blk, 0, s, g); break;
-    case EPI_ADD: hipLaunchKernelGGL((gemm_kernel<MB, NBW, D, EPI_ADD>), grid, blk, 0, s, g); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_kernel<MB, NBW, D, EPI_SWIGLU>), grid, blk, 0, s, g); break;
-    case EPI_QKV: hipLaunchKernelGGL((gemm_kernel<MB, NBW, D, EPI_QKV>), grid, blk, 0, s, g); break;
-    default: return hipErrorInvalidValue;
+int gemm_ntiles(int epi, int N, int w, int nbw) {
+  const int blocks = N / 16;
+  const int per_tile = epi == EPI_SWIGLU ? w : w * nbw;
+  return (blocks + per_tile - 1) / per_tile;
+}
+
+int gemm_mb(int Mp) {
+  const int rb = Mp / 16;
+  return rb <= 1 ? 1 : rb <= 2 ? 2 : rb <= 4 ? 4 : rb <= 8 ? 8 : 16;
+}
+
+template <int MB, int W, int NBW>
+static hipError_t launch_mb(const GemmArgs& g, dim3 grid, hipStream_t s) {
+  const dim3 blk(W * 64);
+  if constexpr (NBW == 1 && W == 8) {            // 8-wave tiles: LM head only
+    if (g.epi == EPI_STORE) hipLaunchKernelGGL((gemm_kernel<MB, 8, 1, EPI_STORE>), grid, blk, 0, s, g);
+    else return hipErrorInvalidValue;
+  } else if constexpr (NBW == 1) {
+    if (g.epi == EPI_STORE) hipLaunchKernelGGL((gemm_kernel<MB, W, 1, EPI_STORE>), grid, blk, 0, s, g);
+    else if (g.epi == EPI_ADD) hipLaunchKernelGGL((gemm_kernel<MB, W, 1, EPI_ADD>), grid, blk, 0, s, g);
+    else return hipErrorInvalidValue;
+  } else {
+    if (g.epi == EPI_SWIGLU) hipLaunchKernelGGL((gemm_kernel<MB, W, 2, EPI_SWIGLU>), grid, blk, 0, s, g);
+    else if (g.epi == EPI_QKV) hipLaunchKernelGGL((gemm_kernel<MB, W, 2, EPI_QKV>), grid, blk, 0, s, g);
+    else return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-// 16-row blocks per workgroup tile.
-static int gemm_mb(int Mp) { return Mp <= 16 ? 1 : (Mp <= 32 ? 2 : 4); }
-
-int gemm_tiles(const GemmArgs& g, int* mtiles, int* ntiles) {
-  const int MB = gemm_mb(g.Mp);
-  *mtiles = (g.Mp / 16 + MB - 1) / MB;
-  *ntiles = g.epi == EPI_SWIGLU ? g.N / (g.nbw * 8) : g.N / (g.nbw * 16);
-  return MB * 16 * g.nbw * 16;          // elements of one tile
+template <int W, int NBW>
+static hipError_t launch_w(const GemmArgs& g, int MB, dim3 grid, hipStream_t s) {
+  switch (MB) {
+    case 1: return launch_mb<1, W, NBW>(g, grid, s);
+    case 2: return launch_mb<2, W, NBW>(g, grid, s);
+    case 4: return launch_mb<4, W, NBW>(g, grid, s);
+    case 8: return launch_mb<8, W, NBW>(g, grid, s);
+    case 16: return launch_mb<16, W, NBW>(g, grid, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
-  int mtiles, ntiles;
-  gemm_tiles(g, &mtiles, &ntiles);
   const int MB = gemm_mb(g.Mp);
-  dim3 grid(mtiles, ntiles, g.splits);
-  if (g.nbw == 4) {
-    if (MB == 1) return launch_cfg<1, 4, 1>(g, grid, s);
-    if (MB == 2) return launch_cfg<2, 4, 1>(g, grid, s);
-    return launch_cfg<4, 4, 1>(g, grid, s);
-  }
-  if (g.nbw == 2) {
-    if (MB == 1) return launch_cfg<1, 2, 4>(g, grid, s);
-    if (MB == 2) return launch_cfg<2, 2, 4>(g, grid, s);
-    return launch_cfg<4, 2, 4>(g, grid, s);
-  }
+  const int mtiles = (g.Mp / 16 + MB - 1) / MB;
+  const int ntiles = gemm_ntiles(g.epi, g.N, g.w, g.nbw);
+  const dim3 grid(ntiles, g.splits, mtiles);
+  if (g.w == 4 && g.nbw == 1) return launch_w<4, 1>(g, MB, grid, s);
+  if (g.w == 8 && g.nbw == 1) return launch_w<8, 1>(g, MB, grid, s);
+  if (g.w == 4 && g.nbw == 2) return launch_w<4, 2>(g, MB, grid, s);
   return hipErrorInvalidValue;
 }
 

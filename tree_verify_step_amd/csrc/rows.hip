@@ -5,17 +5,18 @@
 
 namespace mvk {
 
-__host__ __device__ __forceinline__ int qkv_feature_h(int p, int d, int hd, int P, bool perm) {
-  if (!perm || p >= 2 * d) return p;
-  const int h = p / hd, e = p % hd, j = e / (2 * P), ee = e % (2 * P);
-  return h * hd + (ee < P ? j * P + ee : hd / 2 + j * P + (ee - P));
+// Logical q/k feature stored at packed row p (see the QKV GEMM epilogue):
+// with heads wider than 16, each group of 32 rows holds 16 first-half dims of
+// a head followed by their RoPE partners (dim + hd/2).
+__host__ __device__ __forceinline__ int qkv_feature_h(int p, int d, int hd) {
+  if (hd < 32 || p >= 2 * d) return p;
+  const int h = p / hd, e = p % hd, j = e / 32, ee = e % 32;
+  return h * hd + (ee < 16 ? j * 16 + ee : hd / 2 + j * 16 + (ee - 16));
 }
 
 // dst (fragment-packed, k-block-major [R][C]) <- src (row-major [R][C]);
 // when rope_hd > 0 the first rope_rows rows (q and k of a fused QKV matrix)
-// are reordered so that each 64-row tile holds 32 first-half dims of a head
-// and their RoPE partners (the order the QKV GEMM's epilogue expects when a
-// tile is narrower than a head).  One thread per 16-byte piece.
+// are reordered as qkv_feature_h says.  One thread per 16-byte piece.
 __global__ void pack_kernel(const u16* __restrict__ src, u16* __restrict__ dst, int R, int C,
                             int rope_hd, int rope_rows) {
   const size_t pieces = (size_t)R * (C / 8);
@@ -24,10 +25,7 @@ __global__ void pack_kernel(const u16* __restrict__ src, u16* __restrict__ dst, 
     const int p = (int)(e / (C / 8));            // packed row
     const int c = (int)(e % (C / 8)) * 8;
     int r = p;
-    if (rope_hd > 0 && p < rope_rows) {
-      const bool perm = 64 < rope_hd;             // tile width 64 narrower than a head
-      r = qkv_feature_h(p, rope_rows / 2, rope_hd, 32, perm);
-    }
+    if (rope_hd > 0 && p < rope_rows) r = qkv_feature_h(p, rope_rows / 2, rope_hd);
     const uint4 v = *reinterpret_cast<const uint4*>(src + (size_t)r * C + c);
     *reinterpret_cast<uint4*>(dst + packed_index_kmajor(p, c, R)) = v;
   }
@@ -102,14 +100,16 @@ hipError_t launch_embed(const int32_t* tok, const u16* E, float* x, float* ss, i
   return hipGetLastError();
 }
 
-// RMSNorm of row m of x [M][d] into the fragment-packed bf16 GEMM operand
-// [Mp][d]: out = g * x / sqrt(mean(x^2) + 1e-5); rows M..Mp-1 are zeros.
-// One workgroup per row; the row (d <= 8192) is held in registers, so it is
-// read once.
+// Operand of a normalised GEMM for row m of x [M][d]: the fragment-packed
+// bf16 row x * g and the row's sum of squares ss[m * ss_ld] (the GEMM applies
+// 1/sqrt(ss/d + 1e-5) to its accumulators).  One workgroup per row; the row
+// (d <= 8192) is held in registers, so it is read once.
 #define MV_NORM_MAX_CHUNKS 4          // 8 columns per thread per chunk
-__global__ __launch_bounds__(256) void rmsnorm_pack_kernel(const float* __restrict__ x,
-                                                           const u16* __restrict__ gain,
-                                                           u16* __restrict__ outp, int M, int d) {
+__global__ __launch_bounds__(256) void norm_prep_kernel(const float* __restrict__ x,
+                                                        const u16* __restrict__ gain,
+                                                        u16* __restrict__ outp,
+                                                        float* __restrict__ ss, int ss_ld,
+                                                        int d) {
   const int m = blockIdx.x;
   float v[MV_NORM_MAX_CHUNKS][8];
   float sq = 0.f;
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256) void rmsnorm_pack_kernel(const float* __restri
     const int c = (j * 256 + threadIdx.x) * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
-    if (m < M && c < d) {
+    if (c < d) {
       const float4 a = *reinterpret_cast<const float4*>(x + (size_t)m * d + c);
       const float4 b = *reinterpret_cast<const float4*>(x + (size_t)m * d + c + 4);
       v[j][0] = a.x; v[j][1] = a.y; v[j][2] = a.z; v[j][3] = a.w;
@@ -128,7 +128,7 @@ __global__ __launch_bounds__(256) void rmsnorm_pack_kernel(const float* __restri
     }
   }
   sq = block_sum256(sq);
-  const float rs = m < M ? 1.0f / sqrtf(sq / (float)d + 1e-5f) : 0.f;
+  if (threadIdx.x == 0) ss[(size_t)m * ss_ld] = sq;
 #pragma unroll
   for (int j = 0; j < MV_NORM_MAX_CHUNKS; ++j) {
     const int c = (j * 256 + threadIdx.x) * 8;
@@ -139,18 +139,18 @@ __global__ __launch_bounds__(256) void rmsnorm_pack_kernel(const float* __restri
     uint32_t pk[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const u16 lo = f32_to_bf16(v[j][2 * e] * rs * gv[2 * e]);
-      const u16 hi = f32_to_bf16(v[j][2 * e + 1] * rs * gv[2 * e + 1]);
+      const u16 lo = f32_to_bf16(v[j][2 * e] * gv[2 * e]);
+      const u16 hi = f32_to_bf16(v[j][2 * e + 1] * gv[2 * e + 1]);
       pk[e] = (uint32_t)lo | ((uint32_t)hi << 16);
     }
     *reinterpret_cast<uint4*>(outp + packed_index(m, c, d)) = uint4{pk[0], pk[1], pk[2], pk[3]};
   }
 }
 
-hipError_t launch_rmsnorm_pack(const float* x, const u16* g, u16* out_packed, int M, int Mp,
-                               int d, hipStream_t s) {
+hipError_t launch_norm_prep(const float* x, const u16* g, u16* xn_packed, float* ss, int ss_ld,
+                            int M, int d, hipStream_t s) {
   if (d > MV_NORM_MAX_CHUNKS * 2048) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(rmsnorm_pack_kernel, dim3(Mp), dim3(256), 0, s, x, g, out_packed, M, d);
+  hipLaunchKernelGGL(norm_prep_kernel, dim3(M), dim3(256), 0, s, x, g, xn_packed, ss, ss_ld, d);
   return hipGetLastError();
 }
 
