@@ -72,12 +72,6 @@ static int check_batch(int B) {
 // ---------------------------------------------------------------------------
 // Launch configuration and workspace
 // ---------------------------------------------------------------------------
-static int attn_nsplit(int B, int H, int T) {
-  const int QG = (T + 63) / 64;
-  int ns = 512 / (B * H * QG) - 1;
-  return std::max(1, std::min(ns, 31));
-}
-
 enum GemmKind { G_QKV = 0, G_O, G_GU, G_DOWN, G_LM, G_KINDS };
 
 struct GemmCfg {
@@ -108,9 +102,8 @@ static GemmCfg gemm_cfg(const mv_dims& D, int kind, int Mp) {
 }
 
 struct Ws {
-  size_t x, xa, ao, ha, ss, q, rope, po, pml, part, counters, hu, hz, topi, topv, tcv, tci, amax,
-      stats, cnt, total;
-  int nsplit;
+  size_t x, xa, ao, ha, ss, q, rope, part, counters, hu, hz, topi, topv, tcv, tci, amax, stats,
+      cnt, total;
   int ss_ld;    // floats per row of the sums-of-squares buffer
 };
 
@@ -127,7 +120,6 @@ static int ss_ld_of(const mv_dims& D, int Mp) {
 static Ws ws_layout(const mv_dims& D, int B, int T) {
   Ws w;
   const int M = B * T, Mp = round16(M);
-  w.nsplit = attn_nsplit(B, D.H, T);
   size_t part = 0, max_tiles = 1;
   for (int k = 0; k < G_KINDS; ++k) {
     const GemmCfg c = gemm_cfg(D, k, Mp);
@@ -150,8 +142,6 @@ static Ws ws_layout(const mv_dims& D, int B, int T) {
   w.ss = take((size_t)w.ss_ld * Mp * 4);
   w.q = take((size_t)M * D.d * 2);
   w.rope = take((size_t)M * (D.hd / 2) * 8);
-  w.po = take((size_t)(w.nsplit + 1) * M * D.d * 4);
-  w.pml = take((size_t)(w.nsplit + 1) * M * D.H * 8);
   w.part = take(part);
   w.counters = take(max_tiles * 4);
   w.hu = take((size_t)B * D.K * D.d * 4);
@@ -222,15 +212,13 @@ static inline void prof_end(int kind, hipStream_t s) {
 // Enqueue helpers (no validation)
 // ---------------------------------------------------------------------------
 static int enq_attention(const mv_dims& D, int B, const mv_tree& t, const int32_t* n_prefix,
-                         const u16* q, const mv_kv& kv, int layer, u16* out, int packed, void* ws,
-                         const Ws& L, hipStream_t s) {
+                         const u16* q, const mv_kv& kv, int layer, u16* out, int packed,
+                         hipStream_t s) {
   const size_t le = kv_layer_elems(kv);
   const u16* kc = static_cast<const u16*>(kv.k) + (size_t)layer * le;
   const u16* vc = static_cast<const u16*>(kv.v) + (size_t)layer * le;
   MV_HIP(mvk::launch_attention(q, kc, vc, n_prefix, t.anc, B, t.T, D.H, D.hd, kv.cap,
-                               t.mask_words, L.nsplit, at<float>(ws, L.po), at<float>(ws, L.pml), s));
-  MV_HIP(mvk::launch_attn_combine(at<float>(ws, L.po), at<float>(ws, L.pml), out, packed, B, t.T,
-                                  D.H, D.hd, L.nsplit, round16(B * t.T), s));
+                               t.mask_words, out, packed, s));
   return MV_OK;
 }
 
@@ -279,7 +267,7 @@ static int enq_layer(const mv_dims& D, int B, const mv_tree& t, const int32_t* n
   prof_end(MV_K_QKV, s);
 
   prof_begin(s);
-  int rc = enq_attention(D, B, t, n_prefix, q, kv, layer, ao, 1, ws, L, s);
+  int rc = enq_attention(D, B, t, n_prefix, q, kv, layer, ao, 1, s);
   if (rc) return rc;
   prof_end(MV_K_ATTN, s);
 
@@ -477,7 +465,7 @@ MV_API int mv_tree_attention(const mv_dims* dims, int32_t B, const mv_tree* tree
   if ((rc = check_ws(dims, B, tree->T, ws_bytes, ws))) return rc;
   const Ws L = ws_layout(*dims, B, tree->T);
   return enq_attention(*dims, B, *tree, n_prefix, static_cast<const u16*>(q), *kv, layer,
-                       static_cast<u16*>(out), 0, ws, L, (hipStream_t)stream);
+                       static_cast<u16*>(out), 0, (hipStream_t)stream);
 }
 
 MV_API int mv_decoder_layer(const mv_dims* dims, int32_t B, const mv_tree* tree,

@@ -129,9 +129,7 @@ hipError_t launch_rope_table(const int32_t* n_prefix, const int32_t* depth_of, f
                              int B, int T, int hd, hipStream_t s);
 hipError_t launch_attention(const u16* q, const u16* kc, const u16* vc, const int32_t* n_prefix,
                             const uint64_t* anc, int B, int T, int H, int hd, int cap, int mw,
-                            int nsplit, float* part_o, float* part_ml, hipStream_t s);
-hipError_t launch_attn_combine(const float* part_o, const float* part_ml, u16* out, int packed,
-                               int B, int T, int H, int hd, int nsplit, int Mp, hipStream_t s);
+                            u16* out, int packed, hipStream_t s);
 hipError_t launch_heads_w1(const u16* h, const u16* w1, float* u, int B, int D, int d,
                            hipStream_t s);
 hipError_t launch_heads_w2(const float* u, const u16* w2, float* z, int B, int D, int d, int V,

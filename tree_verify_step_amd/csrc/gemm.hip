@@ -47,31 +47,30 @@ __host__ __device__ __forceinline__ int qkv_feature(int p, int d, int hd) {
   return h * hd + (ee < 16 ? j * 16 + ee : hd / 2 + j * 16 + (ee - 16));
 }
 
-// QKV epilogue of one element (row m, logical feature f) with RoPE partner yp.
-__device__ __forceinline__ void qkv_store(const QkvArgs& a, int m, int f, float y, float yp) {
-  const int d = a.d, hd = a.hd;
-  const int sec = f / d, c = f % d, h = c / hd, i = c % hd;
-  const int b = m / a.T, v = m % a.T;
-  float out = y;
-  if (sec < 2) {
-    const int half = hd >> 1;
-    const float2 cs = a.rope[(size_t)m * half + (i % half)];
-    out = (i < half) ? (y * cs.x - yp * cs.y) : (y * cs.x + yp * cs.y);
+// Destination of one QKV output column (logical feature f): q column, or
+// the head / dim of a K or V cache row.
+struct QkvCol {
+  int sec, c, h, i;
+};
+__device__ __forceinline__ QkvCol qkv_col(const QkvArgs& a, int f) {
+  QkvCol k;
+  k.sec = f / a.d;
+  k.c = f - k.sec * a.d;
+  k.h = k.c / a.hd;
+  k.i = k.c - k.h * a.hd;
+  return k;
+}
+// q -> bf16 row-major; k / v -> KV cache slot `slot` of sequence b.
+__device__ __forceinline__ void qkv_put(const QkvArgs& a, const QkvCol& k, int m, int b, int slot,
+                                        float val) {
+  const u16 ob = f32_to_bf16(val);
+  if (k.sec == 0) {
+    a.q[(size_t)m * a.d + k.c] = ob;
+    return;
   }
-  const u16 ob = f32_to_bf16(out);
-  if (sec == 0) {
-    a.q[(size_t)m * d + c] = ob;
-  } else {
-    // n + T <= cap is the caller's contract; clamping keeps every store in bounds
-    const int n = min(max(a.n_prefix[b], 0), a.cap - a.T);
-    const int slot = n + v;
-    const size_t bh = (size_t)b * a.H + h;
-    if (sec == 1) {
-      a.kcache[(bh * a.cap + slot) * hd + i] = ob;
-    } else {
-      a.vcache[((bh * (a.cap >> 2) + (slot >> 2)) * hd + i) * 4 + (slot & 3)] = ob;
-    }
-  }
+  const size_t bh = (size_t)b * a.H + k.h;
+  if (k.sec == 1) a.kcache[(bh * a.cap + slot) * a.hd + k.i] = ob;
+  else a.vcache[((bh * (a.cap >> 2) + (slot >> 2)) * a.hd + k.i) * 4 + (slot & 3)] = ob;
 }
 
 // Split-K partial exchange between workgroups that may sit on different
@@ -290,33 +289,43 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
           }
     }
   } else if (EPI == EPI_ADD) {
+    // every load of the epilogue is issued first (rows past M and inactive
+    // waves read clamped, valid addresses), then the adds, then the stores
     const bool nxt = g.next_gain != nullptr;
+    float xo[MB][NBW][4], gn[NBW];
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+      const int n = (cb + nb) * 16 + col;
+      gn[nb] = nxt ? bf16_to_f32(g.next_gain[n]) : 0.f;
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = min(row0 + rb * 16 + r, g.M - 1);
+          xo[rb][nb][r] = g.out_f32[(size_t)m * g.N + n];
+        }
+    }
     float sq[MB][4];
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) sq[rb][r] = 0.f;
-    if (active) {
 #pragma unroll
-      for (int nb = 0; nb < NBW; ++nb) {
-        const int n = (first_blk + nb) * 16 + col;
-        const float gn = nxt ? bf16_to_f32(g.next_gain[n]) : 0.f;
+    for (int nb = 0; nb < NBW; ++nb) {
+      const int n = (cb + nb) * 16 + col;
 #pragma unroll
-        for (int rb = 0; rb < MB; ++rb)
+      for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int m = row0 + rb * 16 + r;
-            if (m < g.M) {
-              float* o = g.out_f32 + (size_t)m * g.N + n;
-              const float xv = *o + acc[rb][nb][r];
-              *o = xv;
-              if (nxt) {
-                g.xn_out[packed_index(m, n, g.N)] = f32_to_bf16(xv * gn);
-                sq[rb][r] += xv * xv;
-              }
-            }
+        for (int r = 0; r < 4; ++r) {
+          const int m = row0 + rb * 16 + r;
+          const float xv = xo[rb][nb][r] + acc[rb][nb][r];
+          const bool st = active && m < g.M;
+          sq[rb][r] += st ? xv * xv : 0.f;
+          if (st) {
+            g.out_f32[(size_t)m * g.N + n] = xv;
+            if (nxt) g.xn_out[packed_index(m, n, g.N)] = f32_to_bf16(xv * gn[nb]);
           }
-      }
+        }
     }
     if (nxt) {
       // rows' sums of squares: over this lane group's 16 columns, then the waves
@@ -355,28 +364,55 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
         }
     }
   } else if (EPI == EPI_QKV) {
+    // lane's two blocks: packed rows p0 (block 0) and p0 + 16 (block 1); with
+    // heads wider than 16 they hold dims i and i + hd/2 of one head (RoPE
+    // partners, same (cos, sin)); with 16-wide heads each block is one head
+    // and partners sit 8 lanes apart.  Loads first (clamped rows), then stores.
     const QkvArgs& q = g.qkv;
-    const int p0 = first_blk * 16 + col;      // packed weight rows of the two blocks
+    const int p0 = cb * 16 + col;
     const bool rot = p0 < 2 * q.d;
+    const bool wide = q.hd >= 32;
+    const int f0 = (rot && wide) ? qkv_feature(p0, q.d, q.hd) : p0;
+    const int f1 = (rot && wide) ? f0 + q.hd / 2 : p0 + 16;
+    const int half = q.hd >> 1;
+    const int ci = (f0 % q.d) % q.hd % half;          // RoPE frequency index of both blocks
+    const bool first = ((f0 % q.d) % q.hd) < half;    // block 0 holds the first half (narrow heads)
+    const QkvCol k0 = qkv_col(q, f0), k1 = qkv_col(q, f1);
+    float2 cs[MB][4];
+    int np[MB][4], bq[MB][4];
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = min(row0 + rb * 16 + r, g.M - 1);
+        bq[rb][r] = m / q.T;
+        cs[rb][r] = rot ? q.rope[(size_t)m * half + ci] : make_float2(1.f, 0.f);
+        np[rb][r] = q.n_prefix[bq[rb][r]];
+      }
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = row0 + rb * 16 + r;
         const float y0 = acc[rb][0][r], y1 = acc[rb][1][r];
-        // head dim 16: a block is one whole head, partners are 8 columns apart
         const float s0 = __shfl_xor(y0, 8, 64), s1 = __shfl_xor(y1, 8, 64);
-        if (!active || m >= g.M) continue;
-        if (!rot) {
-          qkv_store(q, m, p0, y0, y0);
-          qkv_store(q, m, p0 + 16, y1, y1);
-        } else if (q.hd >= 32) {
-          const int f0 = qkv_feature(p0, q.d, q.hd);
-          qkv_store(q, m, f0, y0, y1);
-          qkv_store(q, m, f0 + q.hd / 2, y1, y0);
-        } else {
-          qkv_store(q, m, p0, y0, s0);
-          qkv_store(q, m, p0 + 16, y1, s1);
+        const float c = cs[rb][r].x, sn = cs[rb][r].y;
+        float o0 = y0, o1 = y1;
+        if (rot) {
+          if (wide) {            // (x_i, x_{i+hd/2}) -> (x_i c - x_{i+h} s, x_{i+h} c + x_i s)
+            o0 = y0 * c - y1 * sn;
+            o1 = y1 * c + y0 * sn;
+          } else {               // partners 8 lanes apart inside each block
+            o0 = first ? y0 * c - s0 * sn : y0 * c + s0 * sn;
+            o1 = first ? y1 * c - s1 * sn : y1 * c + s1 * sn;
+          }
+        }
+        if (active && m < g.M) {
+          // n + T <= cap is the caller's contract; clamping keeps every store in bounds
+          const int b = bq[rb][r];
+          const int slot = min(max(np[rb][r], 0), q.cap - q.T) + (m - b * q.T);
+          qkv_put(q, k0, m, b, slot, o0);
+          qkv_put(q, k1, m, b, slot, o1);
         }
       }
   }
@@ -396,10 +432,7 @@ int gemm_mb(int Mp) {
 template <int MB, int W, int NBW>
 static hipError_t launch_mb(const GemmArgs& g, dim3 grid, hipStream_t s) {
   const dim3 blk(W * 64);
-  if constexpr (NBW == 1 && W == 8) {            // 8-wave tiles: LM head only
-    if (g.epi == EPI_STORE) hipLaunchKernelGGL((gemm_kernel<MB, 8, 1, EPI_STORE>), grid, blk, 0, s, g);
-    else return hipErrorInvalidValue;
-  } else if constexpr (NBW == 1) {
+  if constexpr (NBW == 1) {
     if (g.epi == EPI_STORE) hipLaunchKernelGGL((gemm_kernel<MB, W, 1, EPI_STORE>), grid, blk, 0, s, g);
     else if (g.epi == EPI_ADD) hipLaunchKernelGGL((gemm_kernel<MB, W, 1, EPI_ADD>), grid, blk, 0, s, g);
     else return hipErrorInvalidValue;
