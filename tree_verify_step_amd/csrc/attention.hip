@@ -38,7 +38,16 @@ __global__ __launch_bounds__(NW * 64) void tree_attention_kernel(
   __shared__ float s_o[NW][16 * LDO];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, qi = lane & 15;
-  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // XCD-aware placement: workgroups are dispatched round-robin over the 8
+  // XCDs (separate L2s), so workgroup L runs on XCD L % 8.  All query blocks
+  // of one (sequence, head) pair get ids congruent mod 8, so that pair's K/V
+  // tiles are fetched into a single L2 and shared from there.  (Placement
+  // only: any mapping computes the same result.)
+  const int QB = (T + 15) >> 4;
+  const int L = blockIdx.x, xcd = L & 7, j = L >> 3;
+  const int pair = xcd + 8 * (j / QB), qb = j % QB;
+  if (pair >= B * H) return;
+  const int b = pair / H, h = pair % H;
   const int qidx = qb * 16 + qi;                     // this lane's query (tree node)
   const int qrow = qidx < T ? qidx : T - 1;
 
@@ -205,7 +214,8 @@ hipError_t launch_attention(const u16* q, const u16* kc, const u16* vc, const in
                             const uint64_t* anc, int B, int T, int H, int hd, int cap, int mw,
                             u16* out, int packed, hipStream_t s) {
   constexpr int NW = 8;
-  dim3 grid((T + 15) / 16, H, B);
+  const int QB = (T + 15) / 16, pairs = B * H;
+  dim3 grid(8 * ((pairs + 7) / 8) * QB);
   const dim3 blk(NW * 64);
   switch (hd) {
     case 16: hipLaunchKernelGGL((tree_attention_kernel<16, NW>), grid, blk, 0, s, q, kc, vc, n_prefix, anc, B, T, H, cap, mw, out, packed); break;

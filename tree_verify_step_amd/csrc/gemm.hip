@@ -85,6 +85,18 @@ __device__ __forceinline__ void qkv_put(const QkvArgs& a, const QkvCol& k, int m
 #define MV_BUF_DWORD3 0x00020000    /* raw (untyped) buffer resource */
 #define MV_BUF_NONE 0x7ffffff0      /* an offset past any partial buffer */
 
+// Sum over the 16 lanes of a DPP row (every lane gets the row's total): quad
+// swaps (xor 1, xor 2), then half-row and row mirrors.  VALU lane moves, no
+// LDS round trips.
+#define MV_DPP(v, ctrl) __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xF, 0xF, false))
+__device__ __forceinline__ float row16_sum(float v) {
+  v += MV_DPP(v, 0xB1);     // quad_perm [1,0,3,2]
+  v += MV_DPP(v, 0x4E);     // quad_perm [2,3,0,1]
+  v += MV_DPP(v, 0x141);    // row_half_mirror
+  v += MV_DPP(v, 0x140);    // row_mirror
+  return v;
+}
+
 // k-blocks per activation chunk (= depth of the weight ring): the LDS chunk
 // holds KC * MB KiB per buffer.
 template <int MB>
@@ -217,6 +229,51 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
     __syncthreads();
   }
 
+  // ---- the epilogue's own memory operands, loaded before the split-K
+  // exchange so that their latency overlaps it (rows past M and inactive
+  // waves read clamped, valid addresses; the values are then unused)
+  const int col = lane & 15;
+  const int row0 = mt * TR + 4 * (lane >> 4);
+  float xo[MB][NBW][4], gn[NBW];              // ADD: residual x, next norm's gain
+  float2 cs[MB][4];                           // QKV: RoPE (cos, sin) per row
+  int np[MB][4], bq[MB][4];                   // QKV: row's prefix length and sequence
+  // QKV: the lane's two blocks are packed rows p0 (block 0) and p0 + 16
+  // (block 1); with heads wider than 16 they hold dims i and i + hd/2 of one
+  // head (RoPE partners, same (cos, sin)); with 16-wide heads each block is
+  // one head and partners sit 8 lanes apart
+  const int p0 = cb * 16 + col;
+  const bool rot = EPI == EPI_QKV && p0 < 2 * g.qkv.d;
+  const bool wide = g.qkv.hd >= 32;
+  const int f0 = (rot && wide) ? qkv_feature(p0, g.qkv.d, g.qkv.hd) : p0;
+  const int f1 = (rot && wide) ? f0 + g.qkv.hd / 2 : p0 + 16;
+  const int half = g.qkv.hd >> 1;
+  if constexpr (EPI == EPI_ADD) {
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+      const int n = (cb + nb) * 16 + col;
+      gn[nb] = g.next_gain ? bf16_to_f32(g.next_gain[n]) : 0.f;
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = min(row0 + rb * 16 + r, g.M - 1);
+          xo[rb][nb][r] = g.out_f32[(size_t)m * g.N + n];
+        }
+    }
+  }
+  if constexpr (EPI == EPI_QKV) {
+    const int ci = (f0 % g.qkv.d) % g.qkv.hd % half;  // RoPE frequency index of both blocks
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = min(row0 + rb * 16 + r, g.M - 1);
+        bq[rb][r] = m / g.qkv.T;
+        cs[rb][r] = rot ? g.qkv.rope[(size_t)m * half + ci] : make_float2(1.f, 0.f);
+        np[rb][r] = g.qkv.n_prefix[bq[rb][r]];
+      }
+  }
+
   // ---- split-K: the last workgroup of the tile sums the splits in order
   if (g.splits > 1) {
     constexpr int WQ = MB * NBW;               // f32x4 items per lane of one wave
@@ -264,8 +321,6 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
   }
 
   // ---- epilogues: lane holds rows rb*16 + 4*(lane/16) + r, column lane%16 of each block
-  const int col = lane & 15;
-  const int row0 = mt * TR + 4 * (lane >> 4);
   if (g.ss) {
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb)
@@ -289,22 +344,8 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
           }
     }
   } else if (EPI == EPI_ADD) {
-    // every load of the epilogue is issued first (rows past M and inactive
-    // waves read clamped, valid addresses), then the adds, then the stores
-    const bool nxt = g.next_gain != nullptr;
-    float xo[MB][NBW][4], gn[NBW];
-#pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) {
-      const int n = (cb + nb) * 16 + col;
-      gn[nb] = nxt ? bf16_to_f32(g.next_gain[n]) : 0.f;
-#pragma unroll
-      for (int rb = 0; rb < MB; ++rb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = min(row0 + rb * 16 + r, g.M - 1);
-          xo[rb][nb][r] = g.out_f32[(size_t)m * g.N + n];
-        }
-    }
+    const bool nxt = g.next_gain != nullptr && g.xn_out != nullptr;
+    const bool ssq = g.next_gain != nullptr && g.ss_out != nullptr;
     float sq[MB][4];
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb)
@@ -327,17 +368,13 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
           }
         }
     }
-    if (nxt) {
+    if (ssq) {
       // rows' sums of squares: over this lane group's 16 columns, then the waves
 #pragma unroll
       for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float v = sq[rb][r];
-          v += __shfl_xor(v, 1, 64);
-          v += __shfl_xor(v, 2, 64);
-          v += __shfl_xor(v, 4, 64);
-          v += __shfl_xor(v, 8, 64);
+          const float v = row16_sum(sq[rb][r]);
           if (col == 0) ssw[wave][rb * 16 + 4 * (lane >> 4) + r] = v;
         }
       __syncthreads();
@@ -364,38 +401,20 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
         }
     }
   } else if (EPI == EPI_QKV) {
-    // lane's two blocks: packed rows p0 (block 0) and p0 + 16 (block 1); with
-    // heads wider than 16 they hold dims i and i + hd/2 of one head (RoPE
-    // partners, same (cos, sin)); with 16-wide heads each block is one head
-    // and partners sit 8 lanes apart.  Loads first (clamped rows), then stores.
     const QkvArgs& q = g.qkv;
-    const int p0 = cb * 16 + col;
-    const bool rot = p0 < 2 * q.d;
-    const bool wide = q.hd >= 32;
-    const int f0 = (rot && wide) ? qkv_feature(p0, q.d, q.hd) : p0;
-    const int f1 = (rot && wide) ? f0 + q.hd / 2 : p0 + 16;
-    const int half = q.hd >> 1;
-    const int ci = (f0 % q.d) % q.hd % half;          // RoPE frequency index of both blocks
     const bool first = ((f0 % q.d) % q.hd) < half;    // block 0 holds the first half (narrow heads)
     const QkvCol k0 = qkv_col(q, f0), k1 = qkv_col(q, f1);
-    float2 cs[MB][4];
-    int np[MB][4], bq[MB][4];
-#pragma unroll
-    for (int rb = 0; rb < MB; ++rb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = min(row0 + rb * 16 + r, g.M - 1);
-        bq[rb][r] = m / q.T;
-        cs[rb][r] = rot ? q.rope[(size_t)m * half + ci] : make_float2(1.f, 0.f);
-        np[rb][r] = q.n_prefix[bq[rb][r]];
-      }
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = row0 + rb * 16 + r;
         const float y0 = acc[rb][0][r], y1 = acc[rb][1][r];
-        const float s0 = __shfl_xor(y0, 8, 64), s1 = __shfl_xor(y1, 8, 64);
+        float s0 = 0.f, s1 = 0.f;
+        if (!wide) {             // uniform: 16-wide heads only
+          s0 = __shfl_xor(y0, 8, 64);
+          s1 = __shfl_xor(y1, 8, 64);
+        }
         const float c = cs[rb][r].x, sn = cs[rb][r].y;
         float o0 = y0, o1 = y1;
         if (rot) {
@@ -432,7 +451,10 @@ int gemm_mb(int Mp) {
 template <int MB, int W, int NBW>
 static hipError_t launch_mb(const GemmArgs& g, dim3 grid, hipStream_t s) {
   const dim3 blk(W * 64);
-  if constexpr (NBW == 1) {
+  if constexpr (NBW == 1 && W == 8) {            // 8-wave tiles: LM head only
+    if (g.epi == EPI_STORE) hipLaunchKernelGGL((gemm_kernel<MB, 8, 1, EPI_STORE>), grid, blk, 0, s, g);
+    else return hipErrorInvalidValue;
+  } else if constexpr (NBW == 1) {
     if (g.epi == EPI_STORE) hipLaunchKernelGGL((gemm_kernel<MB, W, 1, EPI_STORE>), grid, blk, 0, s, g);
     else if (g.epi == EPI_ADD) hipLaunchKernelGGL((gemm_kernel<MB, W, 1, EPI_ADD>), grid, blk, 0, s, g);
     else return hipErrorInvalidValue;
