@@ -167,6 +167,7 @@ def _layer_case(D, B, ns, paths_per_seq, topk, seed, gain_std=0.1):
     ("tiny", 1, [32]),
     ("mid", 1, [77]),          # hd = 128: RoPE partners paired across 16-row blocks
     ("mid", 2, [64, 301]),     # 128 rows: split-K on the down projection
+    ("mid", 4, [64, 301, 5, 1000]),   # 256 rows (batch 4): 16-row-block tiles
     ("llama7b", 1, [512]),     # the bench's shapes, tree and launch configuration
 ])
 def test_decoder_layer_matches_oracle(name, B, ns):

@@ -51,36 +51,17 @@ __global__ __launch_bounds__(NW * 64) void tree_attention_kernel(
   const int qidx = qb * 16 + qi;                     // this lane's query (tree node)
   const int qrow = qidx < T ? qidx : T - 1;
 
-  // n + T <= cap is the caller's contract; clamping keeps every load in bounds
-  const int n = min(max(n_prefix[b], 0), cap - T);
-  const int d = H * HD;
-  const int lo = 0, hi = n + T;
-  const int ntiles = (hi + 63) >> 6;
+  const int n_raw = n_prefix[b];    // issued first: loads complete in issue order
   const size_t bh = (size_t)b * H + h;
   const u16* kbase = kc + bh * cap * HD;
   const u16* vbase = vc + bh * (size_t)(cap >> 2) * HD * 4;
 
-  // Q^T fragments (B operand): lane owns query qi, dims 32*db + 8*g .. +8.
-  bf16x8 qf[DB32];
-#pragma unroll
-  for (int db = 0; db < DB32; ++db) {
-    const int dim = db * 32 + g * 8;
-    qf[db] = dim < HD ? *reinterpret_cast<const bf16x8*>(q + ((size_t)(b * T + qrow) * d + h * HD + dim))
-                      : bf16x8{};
-  }
-  uint64_t am[4] = {0, 0, 0, 0};
-  for (int w = 0; w < mw && w < 4; ++w) am[w] = anc[((size_t)b * T + qrow) * mw + w];
-
-  const float scale = 1.4426950408889634f / sqrtf((float)HD);   // log2(e) / sqrt(hd)
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 o[DB16];
-#pragma unroll
-  for (int i = 0; i < DB16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int t = wave; t < ntiles; t += NW) {
-    const int s0 = t * 64;
-    // ---- all loads of the tile first: K (A operand of S^T) and V (A of O^T) ----
-    bf16x8 kf[4][DB32];
+  // ---- K (A operand of S^T) and V (A operand of O^T) of one 64-key tile ----
+  bf16x8 kf[4][DB32];
+  // V^T operand, 32-key half kk: slot j<4 -> key kk*32 + 4g + j,
+  // j>=4 -> kk*32 + 16 + 4g + j-4 (matches the S^T register layout)
+  uint2 va[2][DB16], vb[2][DB16];
+  auto load_tile = [&](int s0) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int key = s0 + kb * 16 + qi;
@@ -91,9 +72,6 @@ __global__ __launch_bounds__(NW * 64) void tree_attention_kernel(
                               : bf16x8{};
       }
     }
-    // V^T operand, 32-key half kk: slot j<4 -> key kk*32 + 4g + j,
-    // j>=4 -> kk*32 + 16 + 4g + j-4 (matches the S^T register layout)
-    uint2 va[2][DB16], vb[2][DB16];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int sa = s0 + kk * 32 + g * 4, sb = sa + 16;
@@ -103,6 +81,42 @@ __global__ __launch_bounds__(NW * 64) void tree_attention_kernel(
         va[kk][i] = *reinterpret_cast<const uint2*>(vbase + (((size_t)(sa >> 2) * HD + dim) << 2));
         vb[kk][i] = *reinterpret_cast<const uint2*>(vbase + (((size_t)(sb >> 2) * HD + dim) << 2));
       }
+    }
+  };
+  // this wave's first tile does not depend on n: its loads go out before n
+  // is known (clamped into the cache; unused if the tile is past n + T)
+  load_tile(min(wave, (cap >> 6) - 1) * 64);
+
+  // n + T <= cap is the caller's contract; clamping keeps every load in bounds
+  const int n = min(max(n_raw, 0), cap - T);
+  const int d = H * HD;
+  const int lo = 0, hi = n + T;
+  const int ntiles = (hi + 63) >> 6;
+
+  // Q^T fragments (B operand): lane owns query qi, dims 32*db + 8*g .. +8.
+  bf16x8 qf[DB32];
+#pragma unroll
+  for (int db = 0; db < DB32; ++db) {
+    const int dim = db * 32 + g * 8;
+    qf[db] = dim < HD ? *reinterpret_cast<const bf16x8*>(q + ((size_t)(b * T + qrow) * d + h * HD + dim))
+                      : bf16x8{};
+  }
+  uint64_t am[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w)                 // unrolled: no wait until the mask is used
+    am[w] = w < mw ? anc[((size_t)b * T + qrow) * mw + w] : 0ull;
+
+  const float scale = 1.4426950408889634f / sqrtf((float)HD);   // log2(e) / sqrt(hd)
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 o[DB16];
+#pragma unroll
+  for (int i = 0; i < DB16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int t = wave; t < ntiles; t += NW) {
+    const int s0 = t * 64;
+    if (t != wave) {           // later tiles: all K and V loads issued before the math
+      load_tile(s0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // ---- S^T = K Q^T for 64 keys (4 blocks of 16) ----
     f32x4 st[4];
@@ -215,7 +229,7 @@ hipError_t launch_attention(const u16* q, const u16* kc, const u16* vc, const in
                             u16* out, int packed, hipStream_t s) {
   constexpr int NW = 8;
   const int QB = (T + 15) / 16, pairs = B * H;
-  dim3 grid(8 * ((pairs + 7) / 8) * QB);
+  const dim3 grid(8 * ((pairs + 7) / 8) * QB);
   const dim3 blk(NW * 64);
   switch (hd) {
     case 16: hipLaunchKernelGGL((tree_attention_kernel<16, NW>), grid, blk, 0, s, q, kc, vc, n_prefix, anc, B, T, H, cap, mw, out, packed); break;

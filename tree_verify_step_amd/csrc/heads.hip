@@ -5,14 +5,16 @@
 // At batch size B the heads are matrix-vector products over bf16 weights
 // that are read exactly once, so they are HBM-bound GEMVs: each wave owns
 // whole weight rows, its 64 lanes read 16 contiguous bytes each (a 1 KiB
-// coalesced piece of a row per instruction), multiply by the fp32 input held
-// in LDS and reduce across the wave.
+// coalesced piece of a row per instruction; eight pieces of each of two rows
+// in flight), multiply by the fp32 input held in LDS and reduce across the
+// wave.
 #include "common.hpp"
 
 namespace mvk {
 
 constexpr int GEMV_RW = 2;            // rows per wave per iteration
 constexpr int GEMV_ROWS_PER_WG = 64;  // 16 rows per wave
+constexpr int GEMV_CH = 8;            // 1 KiB row pieces per lane in flight
 
 // mode 0: y = W1 x -> u[b][k][j] = h[b][j] + SiLU(y) (x = h, bf16 input)
 // mode 1: y = W2 x -> z[b][k][j] = y             (x = u[b][k], fp32 input)
@@ -39,26 +41,37 @@ __global__ __launch_bounds__(256) void heads_gemv_kernel(const u16* __restrict__
     for (int i = 0; i < GEMV_RW; ++i)
 #pragma unroll
       for (int b = 0; b < MAXB; ++b) acc[i][b] = 0.f;
-    for (int c = lane * 8; c < d; c += 512) {
-      uint4 w[GEMV_RW];
+    // GEMV_CH 1 KiB pieces of each of the wave's rows are loaded before any
+    // math, so 2 * GEMV_CH loads per lane are in flight
+    for (int c0 = 0; c0 < d; c0 += 512 * GEMV_CH) {
+      uint4 w[GEMV_CH][GEMV_RW];
 #pragma unroll
-      for (int i = 0; i < GEMV_RW; ++i) {
-        const int r = min(r0 + i, r_hi - 1);
-        w[i] = *reinterpret_cast<const uint4*>(Wk + (size_t)r * d + c);
-      }
-#pragma unroll
-      for (int b = 0; b < MAXB; ++b) {
-        if (b >= B) break;
-        const float4 x0 = *reinterpret_cast<const float4*>(xs + (size_t)b * d + c);
-        const float4 x1 = *reinterpret_cast<const float4*>(xs + (size_t)b * d + c + 4);
+      for (int j = 0; j < GEMV_CH; ++j) {
+        const int c = min(c0 + j * 512 + lane * 8, d - 8);      // clamped: in bounds
 #pragma unroll
         for (int i = 0; i < GEMV_RW; ++i) {
-          float a = acc[i][b];
-          a += bf16lo(w[i].x) * x0.x + bf16hi(w[i].x) * x0.y;
-          a += bf16lo(w[i].y) * x0.z + bf16hi(w[i].y) * x0.w;
-          a += bf16lo(w[i].z) * x1.x + bf16hi(w[i].z) * x1.y;
-          a += bf16lo(w[i].w) * x1.z + bf16hi(w[i].w) * x1.w;
-          acc[i][b] = a;
+          const int r = min(r0 + i, r_hi - 1);
+          w[j][i] = *reinterpret_cast<const uint4*>(Wk + (size_t)r * d + c);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < GEMV_CH; ++j) {
+        const int c = c0 + j * 512 + lane * 8;
+        if (c >= d) break;
+#pragma unroll
+        for (int b = 0; b < MAXB; ++b) {
+          if (b >= B) break;
+          const float4 x0 = *reinterpret_cast<const float4*>(xs + (size_t)b * d + c);
+          const float4 x1 = *reinterpret_cast<const float4*>(xs + (size_t)b * d + c + 4);
+#pragma unroll
+          for (int i = 0; i < GEMV_RW; ++i) {
+            float a = acc[i][b];
+            a += bf16lo(w[j][i].x) * x0.x + bf16hi(w[j][i].x) * x0.y;
+            a += bf16lo(w[j][i].y) * x0.z + bf16hi(w[j][i].y) * x0.w;
+            a += bf16lo(w[j][i].z) * x1.x + bf16hi(w[j][i].z) * x1.y;
+            a += bf16lo(w[j][i].w) * x1.z + bf16hi(w[j][i].w) * x1.w;
+            acc[i][b] = a;
+          }
         }
       }
     }
