@@ -169,8 +169,8 @@ MV_API int mv_tree_compile(const int32_t* paths, const int32_t* path_len, int32_
 /* Reorder a row-major bf16 weight [rows][cols] (out, in) into the
  * fragment-packed layout the backbone GEMMs read.  layout MV_PACK_QKV: the
  * matrix is the fused [3d][d] q|k|v projection with head size hd; q and k
- * rows are additionally permuted so that each 64-row tile holds RoPE pairs
- * (dims i and i + hd/2 of a head).  src and dst are device buffers of
+ * rows are additionally permuted (head size >= 32) in groups of 32 rows: 16
+ * first-half dims of a head, then their RoPE partners (dims + hd/2).  src and dst are device buffers of
  * rows*cols bf16 and must not overlap.  rows % 16 == 0, cols % 32 == 0. */
 MV_API int mv_pack_weight(const void* src, void* dst, int32_t rows, int32_t cols,
                           int32_t layout, int32_t hd, void* stream);
@@ -322,13 +322,13 @@ MV_API int mv_step(mv_ctx* ctx, int32_t graph, void* stream);
 /* Launch-group kinds reported by mv_step_profile. */
 #define MV_K_HEADS 0     /* Medusa heads: W1 block, vocab projection, top-s, tree fill */
 #define MV_K_EMBED 1     /* embedding gather and RoPE table */
-#define MV_K_NORM 2      /* RMSNorm into the packed GEMM operand (2 per layer) */
+#define MV_K_NORM 2      /* first layer's norm operand (later norms are GEMM epilogues) */
 #define MV_K_QKV 3       /* fused QKV GEMM with RoPE and KV-cache write */
-#define MV_K_ATTN 4      /* tree attention and range combine */
+#define MV_K_ATTN 4      /* tree attention */
 #define MV_K_O 5         /* output projection GEMM + residual */
 #define MV_K_GATE_UP 6   /* gate/up GEMM with SwiGLU */
 #define MV_K_DOWN 7      /* down projection GEMM + residual */
-#define MV_K_LM_HEAD 8   /* final RMSNorm and LM-head GEMM */
+#define MV_K_LM_HEAD 8   /* LM-head GEMM (final norm folded in) */
 #define MV_K_ACCEPT 9    /* acceptance and next root */
 #define MV_K_COUNT 11
 #define MV_K_COMPACT 10  /* KV compaction and n update */
@@ -339,6 +339,15 @@ MV_API int mv_step(mv_ctx* ctx, int32_t graph, void* stream);
  * count[MV_K_COUNT] (host arrays).  Same kernels and launch shapes as
  * mv_step. */
 MV_API int mv_step_profile(mv_ctx* ctx, float* ms, int32_t* count, void* stream);
+
+/* Average duration in microseconds (*us, host) of one launch of one kind --
+ * MV_K_QKV, MV_K_ATTN, MV_K_O, MV_K_GATE_UP, MV_K_DOWN (all L layers) or
+ * MV_K_LM_HEAD -- enqueued back to back `reps` times with the step's own
+ * arguments between two HIP events on `stream`, then waited for.  It reruns
+ * kernels of the step on the current state: it rewrites the residual stream
+ * and the workspace and the tree's KV slots past n, all of which the next
+ * step writes first, so the decode state is unchanged. */
+MV_API int mv_time_kernel(mv_ctx* ctx, int32_t kind, int32_t reps, float* us, void* stream);
 
 #ifdef __cplusplus
 }

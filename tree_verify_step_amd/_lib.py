@@ -26,7 +26,7 @@ PACK_PLAIN, PACK_QKV = 0, 1
 EXPORTS = ("mv_strerror", "mv_last_error", "mv_tree_compile", "mv_pack_weight",
            "mv_workspace_size", "mv_medusa_heads", "mv_tree_attention", "mv_decoder_layer",
            "mv_embed", "mv_lm_head", "mv_accept", "mv_kv_compact", "mv_ctx_create",
-           "mv_ctx_destroy", "mv_prefill", "mv_step", "mv_step_profile")
+           "mv_ctx_destroy", "mv_prefill", "mv_step", "mv_step_profile", "mv_time_kernel")
 
 # launch-group kinds of mv_step_profile
 KINDS = ("heads", "embed_rope", "norm", "gemm_qkv", "attention", "gemm_o", "gemm_gate_up",
@@ -114,6 +114,7 @@ def lib() -> C.CDLL:
         "mv_prefill": (C.c_int, [vp, vp, i32, vp, vp]),
         "mv_step": (C.c_int, [vp, i32, vp]),
         "mv_step_profile": (C.c_int, [vp, vp, vp, vp]),
+        "mv_time_kernel": (C.c_int, [vp, C.c_int32, C.c_int32, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -262,6 +263,16 @@ class Ctx:
         check(lib().mv_step_profile(self.h, ptr(ms), ptr(cnt), stream_ptr(stream)),
               "step_profile")
         return {k: (float(ms[i]), int(cnt[i])) for i, k in enumerate(KINDS)}
+
+    def time_kernel(self, kind: str, reps: int = 1, stream=None) -> float:
+        """Average microseconds of one launch of `kind` ("gemm_qkv",
+        "attention", "gemm_o", "gemm_gate_up", "gemm_down", "lm_head") run
+        back to back with the step's arguments (HIP events, library stream)."""
+        import numpy as np
+        us = np.zeros(1, np.float32)
+        check(lib().mv_time_kernel(self.h, KINDS.index(kind), reps, ptr(us), stream_ptr(stream)),
+              "time_kernel")
+        return float(us[0])
 
     def close(self) -> None:
         if self.h:

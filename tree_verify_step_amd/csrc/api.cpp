@@ -237,7 +237,8 @@ static int enq_norm_prep(const mv_dims& D, int M, const float* x, const void* ga
 static int enq_layer(const mv_dims& D, int B, const mv_tree& t, const int32_t* n_prefix,
                      const mv_layer_weights& w, const mv_kv& kv, int layer, float* x,
                      int ss_tiles_in, const void* next_gain, void* ws, const Ws& L,
-                     hipStream_t s) {
+                     hipStream_t s, int only_kind = -1) {
+  auto want = [&](int kind) { return only_kind < 0 || only_kind == kind; };
   const int M = B * t.T;
   u16* xa = at<u16>(ws, L.xa);
   u16* ao = at<u16>(ws, L.ao);
@@ -262,14 +263,18 @@ static int enq_layer(const mv_dims& D, int B, const mv_tree& t, const int32_t* n
   g.qkv.hd = D.hd;
   g.qkv.cap = kv.cap;
   g.qkv.d = D.d;
-  prof_begin(s);
-  MV_HIP(mvk::launch_gemm(g, s));
-  prof_end(MV_K_QKV, s);
+  if (want(MV_K_QKV)) {
+    prof_begin(s);
+    MV_HIP(mvk::launch_gemm(g, s));
+    prof_end(MV_K_QKV, s);
+  }
 
-  prof_begin(s);
-  int rc = enq_attention(D, B, t, n_prefix, q, kv, layer, ao, 1, s);
-  if (rc) return rc;
-  prof_end(MV_K_ATTN, s);
+  if (want(MV_K_ATTN)) {
+    prof_begin(s);
+    const int rc = enq_attention(D, B, t, n_prefix, q, kv, layer, ao, 1, s);
+    if (rc) return rc;
+    prof_end(MV_K_ATTN, s);
+  }
 
   mvk::GemmArgs o = gemm_args(D, G_O, M, ws, L);
   o.A = ao;
@@ -278,9 +283,11 @@ static int enq_layer(const mv_dims& D, int B, const mv_tree& t, const int32_t* n
   o.next_gain = static_cast<const u16*>(w.ffn_norm);
   o.xn_out = xa;
   o.ss_out = ss;
-  prof_begin(s);
-  MV_HIP(mvk::launch_gemm(o, s));
-  prof_end(MV_K_O, s);
+  if (want(MV_K_O)) {
+    prof_begin(s);
+    MV_HIP(mvk::launch_gemm(o, s));
+    prof_end(MV_K_O, s);
+  }
 
   mvk::GemmArgs gu = gemm_args(D, G_GU, M, ws, L);
   gu.A = xa;
@@ -289,9 +296,11 @@ static int enq_layer(const mv_dims& D, int B, const mv_tree& t, const int32_t* n
   gu.ss = ss;
   gu.ss_tiles = ss_tiles_of(D, G_O, M);
   gu.out_bf16 = ha;
-  prof_begin(s);
-  MV_HIP(mvk::launch_gemm(gu, s));
-  prof_end(MV_K_GATE_UP, s);
+  if (want(MV_K_GATE_UP)) {
+    prof_begin(s);
+    MV_HIP(mvk::launch_gemm(gu, s));
+    prof_end(MV_K_GATE_UP, s);
+  }
 
   mvk::GemmArgs dn = gemm_args(D, G_DOWN, M, ws, L);
   dn.A = ha;
@@ -300,9 +309,11 @@ static int enq_layer(const mv_dims& D, int B, const mv_tree& t, const int32_t* n
   dn.next_gain = static_cast<const u16*>(next_gain);
   dn.xn_out = xa;
   dn.ss_out = ss;
-  prof_begin(s);
-  MV_HIP(mvk::launch_gemm(dn, s));
-  prof_end(MV_K_DOWN, s);
+  if (want(MV_K_DOWN)) {
+    prof_begin(s);
+    MV_HIP(mvk::launch_gemm(dn, s));
+    prof_end(MV_K_DOWN, s);
+  }
   return MV_OK;
 }
 
@@ -579,7 +590,8 @@ struct mv_ctx {
 };
 
 // All L layers; the last one leaves the final norm's operand in ws.xa / ws.ss.
-static int enq_layers(mv_ctx* c, const mv_tree& tree, float* x, hipStream_t s) {
+static int enq_layers(mv_ctx* c, const mv_tree& tree, float* x, hipStream_t s,
+                      int only_kind = -1) {
   const mv_step_desc& d = c->d;
   const mv_dims& D = d.dims;
   const int M = d.B * tree.T;
@@ -588,7 +600,7 @@ static int enq_layers(mv_ctx* c, const mv_tree& tree, float* x, hipStream_t s) {
     const void* next_gain = l + 1 < D.L ? c->layers[l + 1].attn_norm : d.final_norm;
     const int ss_in = l == 0 ? 1 : ss_tiles_of(D, G_DOWN, M);
     if ((rc = enq_layer(D, d.B, tree, d.n_prefix, c->layers[l], d.kv, l, x, ss_in, next_gain,
-                        d.ws, c->L, s)))
+                        d.ws, c->L, s, only_kind)))
       return rc;
   }
   return MV_OK;
@@ -821,6 +833,48 @@ MV_API int mv_step_profile(mv_ctx* c, float* ms, int32_t* count, void* stream) {
     ms[p.kind[i]] += t;
     count[p.kind[i]] += 1;
   }
+  return MV_OK;
+}
+
+MV_API int mv_time_kernel(mv_ctx* c, int32_t kind, int32_t reps, float* us, void* stream) {
+  if (!c || !us) return fail(MV_EINVAL, "mv_time_kernel: NULL pointer");
+  if (reps < 1) return fail(MV_EINVAL, "mv_time_kernel: reps %d < 1", reps);
+  if (kind != MV_K_QKV && kind != MV_K_ATTN && kind != MV_K_O && kind != MV_K_GATE_UP &&
+      kind != MV_K_DOWN && kind != MV_K_LM_HEAD)
+    return fail(MV_EINVAL, "mv_time_kernel: kind %d is not a per-layer GEMM, attention or LM head",
+                kind);
+  const hipStream_t s = (hipStream_t)stream;
+  const mv_step_desc& d = c->d;
+  const mv_dims& D = d.dims;
+  const int M = d.B * d.T;
+  float* x = at<float>(d.ws, c->L.x);
+  hipEvent_t e0, e1;
+  MV_HIP(hipEventCreate(&e0));
+  if (hipEventCreate(&e1) != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return fail(MV_EHIP, "mv_time_kernel: event create");
+  }
+  int rc = MV_OK, launches = 0;
+  hipError_t e = hipEventRecord(e0, s);
+  for (int r = 0; r < reps && rc == MV_OK && e == hipSuccess; ++r) {
+    if (kind == MV_K_LM_HEAD) {
+      rc = enq_lm_head(D, M, x, d.final_norm, d.lm_head, d.logits, ss_tiles_of(D, G_DOWN, M),
+                       d.ws, c->L, s);
+      launches += 1;
+    } else {
+      rc = enq_layers(c, d.tree, x, s, kind);
+      launches += D.L;
+    }
+  }
+  if (e == hipSuccess) e = hipEventRecord(e1, s);
+  if (e == hipSuccess) e = hipEventSynchronize(e1);
+  float ms = 0.f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (rc) return rc;
+  if (e != hipSuccess) return fail(MV_EHIP, "mv_time_kernel: %s", hipGetErrorString(e));
+  *us = 1000.f * ms / (float)launches;
   return MV_OK;
 }
 
