@@ -127,21 +127,33 @@ __global__ __launch_bounds__(NW * 64) void tree_attention_kernel(
       for (int db = 0; db < DB32; ++db) st[kb] = mfma16x16x32(kf[kb][db], qf[db], st[kb]);
     }
     // ---- mask + online softmax (log2 domain); lane holds keys kb*16+4g+r ----
+    // prefix tiles (all keys below n) need no mask: a uniform fast path
+    const bool full = s0 + 64 <= n;
     float tmax = -INFINITY;
+    if (full) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int slot = s0 + kb * 16 + g * 4 + r;
-        bool ok = slot < n;
-        if (slot >= n && slot < hi) {
-          const int a = slot - n;
-          ok = (am[a >> 6] >> (a & 63)) & 1ull;
+        for (int r = 0; r < 4; ++r) {
+          st[kb][r] *= scale;
+          tmax = fmaxf(tmax, st[kb][r]);
         }
-        const float sv = ok ? st[kb][r] * scale : -INFINITY;
-        st[kb][r] = sv;
-        tmax = fmaxf(tmax, sv);
-      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int slot = s0 + kb * 16 + g * 4 + r;
+          bool ok = slot < n;
+          if (slot >= n && slot < hi) {
+            const int a = slot - n;
+            ok = (am[a >> 6] >> (a & 63)) & 1ull;
+          }
+          const float sv = ok ? st[kb][r] * scale : -INFINITY;
+          st[kb][r] = sv;
+          tmax = fmaxf(tmax, sv);
+        }
+    }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const float m_new = fmaxf(m_run, tmax);
@@ -171,21 +183,29 @@ __global__ __launch_bounds__(NW * 64) void tree_attention_kernel(
         pf[j] = (__bf16)st[2 * kk][j];
         pf[j + 4] = (__bf16)st[2 * kk + 1][j];
       }
-      const int sa = s0 + kk * 32 + g * 4, sb = sa + 16;
-      // values of slots outside the range are zeroed: never-written cache
-      // memory could hold non-finite patterns and 0 * NaN would poison O
-      uint32_t keep[4];
+      if (full) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int base = (e < 2 ? sa : sb) + (e & 1) * 2;
-        keep[e] = ((base >= lo && base < hi) ? 0x0000ffffu : 0u) |
-                  ((base + 1 >= lo && base + 1 < hi) ? 0xffff0000u : 0u);
-      }
+        for (int i = 0; i < DB16; ++i) {
+          const uint4 w = {va[kk][i].x, va[kk][i].y, vb[kk][i].x, vb[kk][i].y};
+          o[i] = mfma16x16x32(__builtin_bit_cast(bf16x8, w), pf, o[i]);
+        }
+      } else {
+        const int sa = s0 + kk * 32 + g * 4, sb = sa + 16;
+        // values of slots outside the range are zeroed: never-written cache
+        // memory could hold non-finite patterns and 0 * NaN would poison O
+        uint32_t keep[4];
 #pragma unroll
-      for (int i = 0; i < DB16; ++i) {
-        const uint4 w = {va[kk][i].x & keep[0], va[kk][i].y & keep[1], vb[kk][i].x & keep[2],
-                         vb[kk][i].y & keep[3]};
-        o[i] = mfma16x16x32(__builtin_bit_cast(bf16x8, w), pf, o[i]);
+        for (int e = 0; e < 4; ++e) {
+          const int base = (e < 2 ? sa : sb) + (e & 1) * 2;
+          keep[e] = ((base >= lo && base < hi) ? 0x0000ffffu : 0u) |
+                    ((base + 1 >= lo && base + 1 < hi) ? 0xffff0000u : 0u);
+        }
+#pragma unroll
+        for (int i = 0; i < DB16; ++i) {
+          const uint4 w = {va[kk][i].x & keep[0], va[kk][i].y & keep[1], vb[kk][i].x & keep[2],
+                           vb[kk][i].y & keep[3]};
+          o[i] = mfma16x16x32(__builtin_bit_cast(bf16x8, w), pf, o[i]);
+        }
       }
     }
   }
@@ -201,24 +221,32 @@ __global__ __launch_bounds__(NW * 64) void tree_attention_kernel(
     *reinterpret_cast<float4*>(&s_o[wave][qi * LDO + i * 16 + g * 4]) =
         float4{o[i][0], o[i][1], o[i][2], o[i][3]};
   __syncthreads();
+  // per query: each wave's weight 2^(m_w - M) / sum_w 2^(m_w - M) l_w
+  if (threadIdx.x < 16) {
+    const int qq = threadIdx.x;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][qq]);
+    float f[NW], den = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      f[w] = s_m[w][qq] == -INFINITY ? 0.f : exp2f(s_m[w][qq] - M);
+      den += f[w] * s_l[w][qq];
+    }
+    const float inv = 1.f / den;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) s_l[w][qq] = f[w] * inv;   // reused as the weight
+  }
+  __syncthreads();
   for (int e = threadIdx.x; e < 16 * HD; e += NW * 64) {
     const int qq = e / HD, dim = e % HD;
     const int node = qb * 16 + qq;
     if (node >= T) continue;
-    float M = -INFINITY;
+    float val = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][qq]);
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float mw_ = s_m[w][qq];
-      if (mw_ == -INFINITY) continue;
-      const float f = exp2f(mw_ - M);
-      den += f * s_l[w][qq];
-      num += f * s_o[w][qq * LDO + dim];
-    }
+    for (int w = 0; w < NW; ++w) val += s_l[w][qq] * s_o[w][qq * LDO + dim];
     const int m = b * T + node, c = h * HD + dim;
-    const u16 ob = f32_to_bf16(num / den);
+    const u16 ob = f32_to_bf16(val);
     if (packed) out[packed_index(m, c, d)] = ob;
     else out[(size_t)m * d + c] = ob;
   }
