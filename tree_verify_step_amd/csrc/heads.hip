@@ -23,7 +23,7 @@ __global__ __launch_bounds__(256) void heads_gemv_kernel(const u16* __restrict__
                                                          const float* __restrict__ uf,
                                                          const u16* __restrict__ W,
                                                          float* __restrict__ out, int B, int D,
-                                                         int d, int rows, int mode) {
+                                                         int d, int rows, int mode, int rpw) {
   extern __shared__ float xs[];                   // [B][d]
   const int k = blockIdx.y;                       // head index 0..D-1 (head k+1)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -33,8 +33,8 @@ __global__ __launch_bounds__(256) void heads_gemv_kernel(const u16* __restrict__
   }
   __syncthreads();
   const u16* Wk = W + (size_t)k * rows * d;
-  const int r_lo = blockIdx.x * GEMV_ROWS_PER_WG;
-  const int r_hi = min(rows, r_lo + GEMV_ROWS_PER_WG);
+  const int r_lo = blockIdx.x * rpw;
+  const int r_hi = min(rows, r_lo + rpw);
   for (int r0 = r_lo + wave * GEMV_RW; r0 < r_hi; r0 += 4 * GEMV_RW) {
     float acc[GEMV_RW][MAXB];
 #pragma unroll
@@ -91,14 +91,18 @@ __global__ __launch_bounds__(256) void heads_gemv_kernel(const u16* __restrict__
   }
 }
 
+// rpw rows per workgroup (a multiple of 4 waves x GEMV_RW): fewer rows per
+// workgroup when the matrix is short, so that the grid still covers the CUs.
 static hipError_t launch_gemv(const u16* hb, const float* uf, const u16* W, float* out, int B,
                               int D, int d, int rows, int mode, hipStream_t s) {
-  dim3 grid((rows + GEMV_ROWS_PER_WG - 1) / GEMV_ROWS_PER_WG, D);
+  int rpw = GEMV_ROWS_PER_WG;
+  while (rpw > 4 * GEMV_RW && (size_t)((rows + rpw - 1) / rpw) * D < 1024) rpw /= 2;
+  dim3 grid((rows + rpw - 1) / rpw, D);
   const size_t lds = (size_t)B * d * sizeof(float);
   if (B == 1)
-    hipLaunchKernelGGL((heads_gemv_kernel<1>), grid, dim3(256), lds, s, hb, uf, W, out, B, D, d, rows, mode);
+    hipLaunchKernelGGL((heads_gemv_kernel<1>), grid, dim3(256), lds, s, hb, uf, W, out, B, D, d, rows, mode, rpw);
   else if (B <= 4)
-    hipLaunchKernelGGL((heads_gemv_kernel<4>), grid, dim3(256), lds, s, hb, uf, W, out, B, D, d, rows, mode);
+    hipLaunchKernelGGL((heads_gemv_kernel<4>), grid, dim3(256), lds, s, hb, uf, W, out, B, D, d, rows, mode, rpw);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
