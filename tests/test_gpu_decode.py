@@ -22,7 +22,7 @@ from oracle import model as om
 from oracle import tree as otree
 from workloads import configs, synth
 
-from gpu_helpers import TOL
+from gpu_helpers import TOL, fill_prefix_kv
 
 pytestmark = pytest.mark.gpu
 
@@ -154,3 +154,112 @@ def test_tiny_decode_free_running_is_lossless():
             break
     assert emitted[:k] == ref[:k]
     assert k >= 8, f"only {k} tokens compared before a near-tie"
+
+
+def stages(layers: int) -> int:
+    """Rounding stages between the embedding and a quantity computed after
+    `layers` decoder layers: two per layer (attention and FFN blocks, each
+    ending in a bf16-operand GEMM whose output is checked to TOL on its own)
+    plus the one that produces the quantity."""
+    return 2 * layers + 1
+
+
+@pytest.mark.parametrize("wname", [configs.LLAMA7B_T64.name, configs.LLAMA7B_T64_LONG_TYPICAL.name])
+def test_full_dims_step_two_layers_teacher_forced(wname):
+    """Two steps at the 7B dims (d = 4096, 32 x 128 heads, FFN 11008,
+    V = 32000, K = 4 Medusa heads, the workload's 64-node sparse tree; prefix
+    512 with greedy acceptance, or prefix 4096 with typical acceptance and
+    sampled roots; captured graph): every kernel runs in the launch
+    configuration of the timed step, with 2 decoder layers instead of 32 (no
+    launch shape depends on the layer count) so that the oracle finishes in
+    seconds.  Float outputs within the stated bounds, index work bit-exact
+    given the GPU's own logits, the oracle following the GPU's decisions."""
+    w0 = configs.get(wname)
+    D = configs.Dims(L=2, d=w0.dims.d, H=w0.dims.H, hd=w0.dims.hd, F=w0.dims.F,
+                     V=w0.dims.V, K=w0.dims.K)
+    w = w0.with_(dims=D)
+    print(f"full-dims step: {w.name} with L=2", flush=True)
+    Wt = synth.TorchDrawnWeights(w)
+    s = synth.tree_topk(w)
+    paths = synth.tree_paths(w, 0)
+    t = otree.compile_tree(paths)
+    trees = rt.DeviceTrees([paths], s)
+    assert trees.T == 64 and t.max_depth == 4
+    n0 = synth.prefix_lengths(w)[0]
+    steps = 2
+    cap = ((n0 + t.T + steps * (t.max_depth + 1) + 63) // 64) * 64
+    dw = rt.DeviceWeights(D, Wt.get)
+    typical = w.accept == "typical"
+    p = tv.AcceptParams(mode=tv.ACCEPT_TYPICAL if typical else tv.ACCEPT_GREEDY,
+                        root_mode=tv.ROOT_SAMPLE if w.root == "sample" else tv.ROOT_ARGMAX,
+                        temperature=w.temperature, eps=w.eps, delta=w.delta)
+    u = synth.uniform_draws(w, steps + 1)
+    sess = rt.Session(D, 1, t.T, s, cap, dw, trees, p, u_draws=u, debug=True)
+    # the state a prefill of n0 tokens leaves: seeded bf16 prefix K/V, a
+    # post-norm hidden state of unit scale and a root token
+    rng = np.random.default_rng(77)
+    ocaches, kv = fill_prefix_kv(rng, D, 1, [n0], cap)
+    sess.kv.k.copy_(kv.k)
+    sess.kv.v.copy_(kv.v)
+    del kv
+    okv = ocaches[0]
+    h = synth.round_to_bf16(rng.standard_normal(D.d).astype(np.float32)).astype(np.float64)
+    sess.h_last.copy_(torch.from_numpy(h.astype(np.float32)).to(torch.bfloat16).unsqueeze(0))
+    t0 = int(rng.integers(D.V))
+    sess.root_tok.fill_(t0)
+    sess.n_prefix.fill_(n0)
+    sess.u_index.fill_(1)              # a prefill consumes draw 0 for the first root
+    torch.cuda.synchronize()
+    n = n0
+    for step in range(steps):
+        sess.step(graph=True)
+        torch.cuda.synchronize()
+        print(f"  step {step}: n={n}", flush=True)
+        hz = sess.head_logits[0].cpu().numpy()
+        want_z = oh.medusa_heads(Wt.get, h, t.max_depth)
+        assert np.abs(hz - want_z).max() <= TOL, (step, np.abs(hz - want_z).max())
+        top = sess.top_ids[0].cpu().numpy()
+        np.testing.assert_array_equal(top, oh.head_topk(hz, s))
+        tok = otree.fill_tokens(t, t0, top)
+        np.testing.assert_array_equal(sess.tree_tok[0].cpu().numpy(), tok)
+        hn, logits = om.tree_forward(Wt.get, D.L, D.H, t, tok, n, okv)
+        gl = sess.logits[0].cpu().numpy().astype(np.float64)
+        # each decoder layer adds two rounding stages (attention block, FFN
+        # block) whose errors reach the logits through the residual stream; the
+        # final norm + LM head is one more: the per-stage bound TOL adds up
+        lerr = np.abs(gl - logits).max()
+        print(f"  step {step}: head logits err {np.abs(hz - want_z).max():.2e}, tree logits err "
+              f"max {lerr:.4f} rms {np.sqrt(np.mean((gl - logits) ** 2)):.5f} (logits rms "
+              f"{np.sqrt(np.mean(logits ** 2)):.3f})", flush=True)
+        assert lerr <= TOL * stages(D.L), (step, lerr)
+        if typical:
+            res = oa.typical_accept(t, tok, gl, w.temperature, w.eps, w.delta)
+        else:
+            res = oa.greedy_accept(t, tok, gl)
+        L_acc = int(sess.accept_len[0])
+        assert L_acc == res.accept_len, step
+        np.testing.assert_array_equal(sess.path[0].cpu().numpy()[:L_acc + 1], res.path)
+        np.testing.assert_array_equal(sess.emitted[0].cpu().numpy()[:L_acc + 1], tok[res.path])
+        assert int(sess.best[0]) == res.best
+        if w.root == "sample":
+            want, margin = oa.sample_root(gl[res.best], w.temperature, u[step + 1, 0])
+            if margin > 1e-6:
+                assert int(sess.root_tok[0]) == want
+        else:
+            assert int(sess.root_tok[0]) == oa.argmax_lowest(gl[res.best])
+        t0 = int(sess.root_tok[0])
+        herr = np.abs(sess.h_last[0].float().cpu().numpy() - hn[res.best]).max()
+        assert herr <= TOL * stages(D.L), (step, herr)
+        h = sess.h_last[0].float().cpu().numpy().astype(np.float64)   # follow the GPU
+        od.compact_kv(okv, n, res.path)
+        n += len(res.path)
+        assert int(sess.n_prefix[0]) == n
+        kg = sess.kv.k[:, 0].float().cpu().numpy()
+        vg = sess.kv.v_rows()[:, 0].float().cpu().numpy()
+        for l in range(D.L):
+            np.testing.assert_array_equal(kg[l][:, :n0], okv.K[l][:, :n0])
+            np.testing.assert_array_equal(vg[l][:, :n0], okv.V[l][:, :n0])
+            # layer l's K/V rows come after l layers' stages plus their own rounding
+            kerr = np.abs(kg[l][:, :n] - okv.K[l][:, :n]).max()
+            verr = np.abs(vg[l][:, :n] - okv.V[l][:, :n]).max()
+            assert max(kerr, verr) <= TOL * stages(l), (step, l, kerr, verr)

@@ -32,3 +32,18 @@ def test_prefix_lengths_and_draws():
     assert ns == synth.prefix_lengths(w)
     u = synth.uniform_draws(configs.LLAMA7B_T64_LONG_TYPICAL, 5)
     assert u.shape == (5, 1) and np.all((u >= 0) & (u < 1))
+
+
+def test_torch_drawn_weights_are_seeded_and_bf16_valued():
+    w = configs.TINY.with_(weight_dtype="bf16", head_init="lm_copy_noise")
+    a = synth.TorchDrawnWeights(w, device="cpu")
+    b = synth.TorchDrawnWeights(w, device="cpu")
+    for name in ("layer1.wq", "lm_head", "head2.w2"):
+        x = a[name]
+        assert x.dtype == np.float32 and x.shape == synth.tensor_shape(w, name)
+        np.testing.assert_array_equal(x, b[name])
+        np.testing.assert_array_equal(synth.round_to_bf16(x), x)
+    assert abs(float(a["layer1.wq"].std()) - 0.02) < 0.002
+    assert not np.array_equal(a["layer0.wq"], a["layer1.wq"])
+    # lm_copy_noise heads: W2 = LM head + N(0, noise std)
+    assert abs(float((a["head2.w2"] - a["lm_head"]).std()) - w.head_noise_std) < 0.002

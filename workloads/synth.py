@@ -106,6 +106,9 @@ class Weights:
             return round_to_bf16(x)
         return x
 
+    def _normal(self, seed: int, shape, std: float) -> np.ndarray:
+        return _normal(seed, shape, std)
+
     def _make(self, name: str) -> np.ndarray:
         w = self.w
         shape = tensor_shape(w, name)
@@ -114,15 +117,15 @@ class Weights:
         if base in ("attn_norm", "ffn_norm", "final_norm"):
             if w.norm_gain_std == 0.0:
                 return np.ones(shape, np.float32)
-            return self._finish(1.0 + _normal(seed, shape, w.norm_gain_std))
+            return self._finish(1.0 + self._normal(seed, shape, w.norm_gain_std))
         if base == "w1" and self.zero_w1:
             return np.zeros(shape, np.float32)
         if base == "w2" and (self.head_w2_from_lm or self.zero_w1):
             return self.get("lm_head").copy()
         if base == "w2" and w.head_init == "lm_copy_noise":
             return self._finish(self.get("lm_head")
-                                + _normal(seed, shape, w.head_noise_std))
-        return self._finish(_normal(seed, shape, w.init_std))
+                                + self._normal(seed, shape, w.head_noise_std))
+        return self._finish(self._normal(seed, shape, w.init_std))
 
     def get(self, name: str) -> np.ndarray:
         if name in self._c:
@@ -140,6 +143,32 @@ class Weights:
     def drop(self, prefix: str = "") -> None:
         for k in [k for k in self._c if k.startswith(prefix)]:
             del self._c[k]
+
+
+class TorchDrawnWeights(Weights):
+    """Weights with the same names, shapes and distribution as `Weights`, drawn
+    with torch's seeded generator on `device` (seconds at 7B sizes, where the
+    host generator takes minutes); bf16 rounding is torch's round-to-nearest-
+    even cast.  The values differ from `Weights`' for the same seed; both sides
+    of a test read the same arrays from one instance."""
+
+    def __init__(self, w: Workload, device: str = "cuda", **kw):
+        super().__init__(w, **kw)
+        self.device = device
+
+    def _normal(self, seed: int, shape, std: float) -> np.ndarray:
+        import torch
+        g = torch.Generator(device=self.device)
+        g.manual_seed(seed)
+        t = torch.randn(tuple(shape), generator=g, device=self.device, dtype=torch.float32)
+        return t.mul_(std).cpu().numpy()
+
+    def _finish(self, x: np.ndarray) -> np.ndarray:
+        if self.w.weight_dtype != "bf16":
+            return x
+        import torch
+        t = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(self.device)
+        return t.to(torch.bfloat16).float().cpu().numpy()
 
 
 # --------------------------------------------------------------------------
