@@ -40,13 +40,14 @@
  *    zero-filled before its first use; the library keeps its internal
  *    arrival counters at zero between calls.  Calls sharing a workspace must
  *    be ordered on one stream.
- *  - KV cache (one buffer for K, one for V, all layers):
- *      K: bf16 [L][B][H][cap][hd]             (slot-major rows)
- *      V: bf16 [L][B][H][cap/4][hd][4]        (4 consecutive slots interleaved
- *                                              per dim)
- *    element (l, b, h, slot, i) of V sits at
- *      ((((l*B + b)*H + h)*(cap/4) + slot/4)*hd + i)*4 + slot%4.
- *    cap % 64 == 0.  Slots >= n + T may hold anything.
+ *  - KV cache (one buffer for K, one for V, all layers): one block of
+ *    cap*hd bf16 elements per (l, b, h), at ((l*B + b)*H + h)*cap*hd.
+ *    Inside a block, with o = slot % 32:
+ *      K: [cap/32][hd/8][32][8]: element (slot, i) at
+ *         (((slot/32)*(hd/8) + i/8)*32 + row(o))*8 + i%8,
+ *         row(o) = 16*((o/4)%2) + 4*(o/8) + o%4   (whole-line attention loads)
+ *      V: [cap/8][hd][8]: element (slot, i) at ((slot/8)*hd + i)*8 + slot%8
+ *    cap % 64 == 0, hd % 8 == 0.  Slots >= n + T may hold anything.
  *  - Tree (per sequence, T nodes, root = node 0, parents before children):
  *    parent[T] (root: -1), depth_of[T] (root: 0), rank[T] (rank of the node's
  *    token within its head's top-s list; root: 0), and the ancestor bitmask

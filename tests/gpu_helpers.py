@@ -41,8 +41,7 @@ def fill_prefix_kv(rng, D, B, ns, cap, scale=1.0):
             k_rows[l, b, :, :n] = torch.from_numpy(K.astype(np.float32))
             v_rows[l, b, :, :n] = torch.from_numpy(V.astype(np.float32))
         ocaches.append(oc)
-    kv.k.copy_(k_rows.to(DEV).to(torch.bfloat16))
-    kv.v.copy_(rt.KVCache.interleave_v(v_rows).to(DEV).to(torch.bfloat16))
+    kv.set_rows(k_rows, v_rows)
     return ocaches, kv
 
 

@@ -112,7 +112,7 @@ def test_tiny_decode_teacher_forced(graph, variant):
         st.t0 = int(sess.root_tok[0])
         st.h_last = hn[res.best]
         assert int(sess.n_prefix[0]) == st.n
-        kg = sess.kv.k[:, 0].float().cpu().numpy()
+        kg = sess.kv.k_rows()[:, 0].float().cpu().numpy()
         for l in range(D.L):
             assert np.abs(kg[l][:, :st.n] - st.kv.K[l][:, :st.n]).max() <= TOL
 
@@ -254,7 +254,7 @@ def test_full_dims_step_two_layers_teacher_forced(wname):
         od.compact_kv(okv, n, res.path)
         n += len(res.path)
         assert int(sess.n_prefix[0]) == n
-        kg = sess.kv.k[:, 0].float().cpu().numpy()
+        kg = sess.kv.k_rows()[:, 0].float().cpu().numpy()
         vg = sess.kv.v_rows()[:, 0].float().cpu().numpy()
         for l in range(D.L):
             np.testing.assert_array_equal(kg[l][:, :n0], okv.K[l][:, :n0])

@@ -65,15 +65,14 @@ def _attention_case(D, B, T, ns, depth, topk, seed, cap=None):
     q = bf16_values(rng.standard_normal((B, T, D.H, D.hd)))
     kt = bf16_values(rng.standard_normal((B, D.H, T, D.hd)))
     vt = bf16_values(rng.standard_normal((B, D.H, T, D.hd)))
-    krow = kv.k.float().cpu()
+    krow = kv.k_rows().float().cpu()
     vrow = kv.v_rows().float().cpu()
     for b, n in enumerate(ns):
         ocaches[b].K[0][:, n:n + T] = kt[b]
         ocaches[b].V[0][:, n:n + T] = vt[b]
         krow[0, b, :, n:n + T] = torch.from_numpy(kt[b].astype(np.float32))
         vrow[0, b, :, n:n + T] = torch.from_numpy(vt[b].astype(np.float32))
-    kv.k.copy_(krow.to(DEV).to(torch.bfloat16))
-    kv.v.copy_(rt.KVCache.interleave_v(vrow).to(DEV).to(torch.bfloat16))
+    kv.set_rows(krow, vrow)
     return rng, paths, trees, ocaches, kv, q, cap
 
 
@@ -118,10 +117,10 @@ def test_tree_attention_ignores_non_ancestors_bit_exact():
     v = T - 1
     others = [a for a in range(T) if not trees[0].anc[v, a]]
     slots = [ns[0] + a for a in others]
-    kv.k[0, 0, :, slots] = (kv.k[0, 0, :, slots].float() * -3.0 + 1.0).to(torch.bfloat16)
-    vr = kv.v_rows()
+    kr, vr = kv.k_rows(), kv.v_rows()
+    kr[0, 0, :, slots] = kr[0, 0, :, slots] * -3.0 + 1.0
     vr[0, 0, :, slots] = vr[0, 0, :, slots] * 5.0 - 2.0
-    kv.v.copy_(rt.KVCache.interleave_v(vr))
+    kv.set_rows(kr, vr)
     out2 = torch.zeros_like(out1)
     tv.tree_attention(dims_struct(D), B, dt.struct(), i32(ns), qt, kv.struct(), 0, out2, ws)
     torch.cuda.synchronize()
@@ -193,7 +192,7 @@ def test_decoder_layer_matches_oracle(name, B, ns):
                      xt, ws)
     torch.cuda.synchronize()
     got = xt.cpu().numpy()
-    kgot = kv.k.float().cpu().numpy()
+    kgot = kv.k_rows().float().cpu().numpy()
     vgot = kv.v_rows().float().cpu().numpy()
     Wl = Wt.layer(0)
     for b, n in enumerate(ns):
@@ -361,7 +360,7 @@ def test_kv_compact_bit_exact(B):
     cap = 320
     ns = [int(x) for x in rng.integers(1, 200, B)]
     _, kv = fill_prefix_kv(rng, D, B, [cap] * B, cap)
-    k0 = kv.k.clone()
+    k0 = kv.k_rows().clone()
     v0 = kv.v_rows().clone()
     P = 5
     paths = np.full((B, P), -1, np.int32)
@@ -373,7 +372,7 @@ def test_kv_compact_bit_exact(B):
     n_dev = i32(ns)
     tv.kv_compact(kv.struct(), i32(paths), P, i32(lens), n_dev)
     torch.cuda.synchronize()
-    k1, v1 = kv.k.cpu(), kv.v_rows().cpu()
+    k1, v1 = kv.k_rows().cpu(), kv.v_rows().cpu()
     k0, v0 = k0.cpu(), v0.cpu()
     for b in range(B):
         n = ns[b]

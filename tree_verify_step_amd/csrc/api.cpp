@@ -474,7 +474,6 @@ MV_API int mv_tree_attention(const mv_dims* dims, int32_t B, const mv_tree* tree
   if (layer < 0 || layer >= dims->L) return fail(MV_EINVAL, "layer %d outside [0,%d)", layer, dims->L);
   if (!n_prefix || !q || !out) return fail(MV_EINVAL, "mv_tree_attention: NULL pointer");
   if ((rc = check_ws(dims, B, tree->T, ws_bytes, ws))) return rc;
-  const Ws L = ws_layout(*dims, B, tree->T);
   return enq_attention(*dims, B, *tree, n_prefix, static_cast<const u16*>(q), *kv, layer,
                        static_cast<u16*>(out), 0, (hipStream_t)stream);
 }

@@ -2,11 +2,16 @@
 // (slots 0 .. n-1) and to the tree slots n + a of its own ancestors a (itself
 // included), with position ids already applied to q and k by RoPE.
 //
-// Data: q bf16 [B][T][H][hd] (rows of the fused QKV output); K cache bf16
-// [B][H][cap][hd]; V cache bf16 [B][H][cap/4][hd][4] (four consecutive slots
-// interleaved per dim, so that the four keys a lane needs for one dim are one
-// 8-byte load); ancestor bitmask uint64 [B][T][mask_words], bit a of node v's
-// words set iff a is v or an ancestor of v.
+// Data: q bf16 [B][T][H][hd] (rows of the fused QKV output); K and V caches
+// in the layouts of kv_k_off / kv_v_off, per (sequence, head) block of
+// cap * hd elements; ancestor bitmask uint64 [B][T][mask_words], bit a of
+// node v's words set iff a is v or an ancestor of v.
+//
+// Key order inside a 32-key half kk of a tile: row R of S^T block 2*kk + e
+// holds key 32*kk + 8*(R>>2) + 4*e + (R&3).  Lane group g then holds the
+// probabilities of keys 32*kk + 8*g .. +7, in order, which is one 16-byte V
+// load per dim, and the K operand rows of a block are 16 consecutive rows of
+// the K layout: every K and V load instruction reads whole cache lines.
 //
 // Decomposition: a workgroup owns 16 queries of one (sequence, head); its NW
 // waves split the key slots 0 .. n+T-1 (prefix, then tree) in 64-key tiles,
@@ -54,32 +59,35 @@ __global__ __launch_bounds__(NW * 64) void tree_attention_kernel(
   const int n_raw = n_prefix[b];    // issued first: loads complete in issue order
   const size_t bh = (size_t)b * H + h;
   const u16* kbase = kc + bh * cap * HD;
-  const u16* vbase = vc + bh * (size_t)(cap >> 2) * HD * 4;
+  const u16* vbase = vc + bh * cap * HD;
 
   // ---- K (A operand of S^T) and V (A operand of O^T) of one 64-key tile ----
   bf16x8 kf[4][DB32];
-  // V^T operand, 32-key half kk: slot j<4 -> key kk*32 + 4g + j,
-  // j>=4 -> kk*32 + 16 + 4g + j-4 (matches the S^T register layout)
+  // V^T operand of 32-key half kk: lane group g's keys 32*kk + 8g .. +7
+  // (va: the first four, vb: the last four)
   uint2 va[2][DB16], vb[2][DB16];
   auto load_tile = [&](int s0) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const int key = s0 + kb * 16 + qi;
+      // rows 16*(kb&1) .. +15 of the tile's 32-key group kb>>1
+      const size_t grp = (size_t)(s0 >> 5) + (kb >> 1);
 #pragma unroll
       for (int db = 0; db < DB32; ++db) {
         const int dim = db * 32 + g * 8;
-        kf[kb][db] = dim < HD ? *reinterpret_cast<const bf16x8*>(kbase + (size_t)key * HD + dim)
+        kf[kb][db] = dim < HD ? *reinterpret_cast<const bf16x8*>(
+                                    kbase + ((grp * (HD / 8) + (dim >> 3)) * 32 + (kb & 1) * 16 + qi) * 8)
                               : bf16x8{};
       }
     }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const int sa = s0 + kk * 32 + g * 4, sb = sa + 16;
+      const int sv = s0 + kk * 32 + g * 8;
 #pragma unroll
       for (int i = 0; i < DB16; ++i) {
         const int dim = i * 16 + qi;
-        va[kk][i] = *reinterpret_cast<const uint2*>(vbase + (((size_t)(sa >> 2) * HD + dim) << 2));
-        vb[kk][i] = *reinterpret_cast<const uint2*>(vbase + (((size_t)(sb >> 2) * HD + dim) << 2));
+        const uint4 w = *reinterpret_cast<const uint4*>(vbase + ((size_t)(sv >> 3) * HD + dim) * 8);
+        va[kk][i] = uint2{w.x, w.y};
+        vb[kk][i] = uint2{w.z, w.w};
       }
     }
   };
@@ -126,7 +134,8 @@ __global__ __launch_bounds__(NW * 64) void tree_attention_kernel(
 #pragma unroll
       for (int db = 0; db < DB32; ++db) st[kb] = mfma16x16x32(kf[kb][db], qf[db], st[kb]);
     }
-    // ---- mask + online softmax (log2 domain); lane holds keys kb*16+4g+r ----
+    // ---- mask + online softmax (log2 domain); lane holds keys
+    // s0 + 32*(kb>>1) + 8g + 4*(kb&1) + r ----
     // prefix tiles (all keys below n) need no mask: a uniform fast path
     const bool full = s0 + 64 <= n;
     float tmax = -INFINITY;
@@ -143,7 +152,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attention_kernel(
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int slot = s0 + kb * 16 + g * 4 + r;
+          const int slot = s0 + (kb >> 1) * 32 + g * 8 + (kb & 1) * 4 + r;
           bool ok = slot < n;
           if (slot >= n && slot < hi) {
             const int a = slot - n;
@@ -190,13 +199,13 @@ __global__ __launch_bounds__(NW * 64) void tree_attention_kernel(
           o[i] = mfma16x16x32(__builtin_bit_cast(bf16x8, w), pf, o[i]);
         }
       } else {
-        const int sa = s0 + kk * 32 + g * 4, sb = sa + 16;
+        const int sv = s0 + kk * 32 + g * 8;
         // values of slots outside the range are zeroed: never-written cache
         // memory could hold non-finite patterns and 0 * NaN would poison O
         uint32_t keep[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int base = (e < 2 ? sa : sb) + (e & 1) * 2;
+          const int base = sv + 2 * e;
           keep[e] = ((base >= lo && base < hi) ? 0x0000ffffu : 0u) |
                     ((base + 1 >= lo && base + 1 < hi) ? 0xffff0000u : 0u);
         }

@@ -49,6 +49,27 @@ __host__ __device__ __forceinline__ size_t packed_index_kmajor(int r, int c, int
   return ((((size_t)cb * (R >> 4) + rb) * 64 + lane) << 3) + (c & 7);
 }
 
+// ---------------------------------------------------------------------------
+// KV cache layouts.  Each (layer, sequence, head) owns cap * hd elements
+// (cap % 64 == 0, hd % 8 == 0):
+//  * K: [cap/32][hd/8][32][8] -- per 32-slot group and 8-dim piece, 32 rows
+//    of 16 bytes; slot offset o (0..31) in its group sits at row
+//    16*((o>>2)&1) + 4*(o>>3) + (o&3).  The tree-attention K operand of
+//    16 keys x 32 dims is then four 256-byte runs (whole cache lines), and
+//    the keys it holds match the probabilities' register order.
+//  * V: [cap/8][hd][8] -- 8 consecutive slots per dim (one 16-byte load per
+//    lane for the P*V operand).
+// ---------------------------------------------------------------------------
+__host__ __device__ __forceinline__ int kv_krow(int o) {
+  return ((o >> 2) & 1) * 16 + (o >> 3) * 4 + (o & 3);
+}
+__host__ __device__ __forceinline__ size_t kv_k_off(int slot, int dim, int hd) {
+  return (((size_t)(slot >> 5) * (hd >> 3) + (dim >> 3)) * 32 + kv_krow(slot & 31)) * 8 + (dim & 7);
+}
+__host__ __device__ __forceinline__ size_t kv_v_off(int slot, int dim, int hd) {
+  return ((size_t)(slot >> 3) * hd + dim) * 8 + (slot & 7);
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -86,8 +107,8 @@ enum GemmEpi {
 
 struct QkvArgs {
   u16* q;                 // bf16 [M][d] row-major, RoPE'd
-  u16* kcache;            // bf16 [B][H][cap][hd] of this layer
-  u16* vcache;            // bf16 [B][H][cap/4][hd][4] of this layer
+  u16* kcache;            // bf16 K of this layer, [B][H] blocks (kv_k_off inside)
+  u16* vcache;            // bf16 V of this layer, [B][H] blocks (kv_v_off inside)
   const int32_t* n_prefix;   // device [B]
   const float2* rope;     // (cos, sin) [B*T][hd/2] at each row's position
   int B, T, H, hd, cap, d;

@@ -68,9 +68,9 @@ __device__ __forceinline__ void qkv_put(const QkvArgs& a, const QkvCol& k, int m
     a.q[(size_t)m * a.d + k.c] = ob;
     return;
   }
-  const size_t bh = (size_t)b * a.H + k.h;
-  if (k.sec == 1) a.kcache[(bh * a.cap + slot) * a.hd + k.i] = ob;
-  else a.vcache[((bh * (a.cap >> 2) + (slot >> 2)) * a.hd + k.i) * 4 + (slot & 3)] = ob;
+  const size_t base = ((size_t)b * a.H + k.h) * a.cap * a.hd;
+  if (k.sec == 1) a.kcache[base + kv_k_off(slot, k.i, a.hd)] = ob;
+  else a.vcache[base + kv_v_off(slot, k.i, a.hd)] = ob;
 }
 
 // Split-K partial exchange between workgroups that may sit on different

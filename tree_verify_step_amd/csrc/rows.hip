@@ -199,17 +199,17 @@ __global__ void compact_kernel(u16* __restrict__ kc, u16* __restrict__ vc, int L
     const int32_t* pb = path + (size_t)b * path_stride;
     u16 kv[MV_MAX_PATH], vv[MV_MAX_PATH];
     u16* kp = kc + lbh * (size_t)cap * hd;
-    u16* vp = vc + lbh * (size_t)(cap >> 2) * hd * 4;
+    u16* vp = vc + lbh * (size_t)cap * hd;
     if (n + cnt > cap) continue;                  // out of contract: leave the cache alone
     for (int m = 0; m < cnt; ++m) {
       const int s = min(n + max(pb[m], 0), cap - 1);
-      kv[m] = kp[(size_t)s * hd + dim];
-      vv[m] = vp[((size_t)(s >> 2) * hd + dim) * 4 + (s & 3)];
+      kv[m] = kp[kv_k_off(s, dim, hd)];
+      vv[m] = vp[kv_v_off(s, dim, hd)];
     }
     for (int m = 0; m < cnt; ++m) {
       const int s = n + m;
-      kp[(size_t)s * hd + dim] = kv[m];
-      vp[((size_t)(s >> 2) * hd + dim) * 4 + (s & 3)] = vv[m];
+      kp[kv_k_off(s, dim, hd)] = kv[m];
+      vp[kv_v_off(s, dim, hd)] = vv[m];
     }
   }
 }

@@ -123,25 +123,59 @@ class KVCache:
     def __init__(self, D, B: int, cap: int, dev="cuda"):
         assert cap % 64 == 0
         shape = (D.L, B, D.H, cap, D.hd)
+        # the library's layouts inside each [cap][hd] block (see tile_k and
+        # interleave_v): use k_rows() / v_rows() to read slot-major rows
         self.k = torch.zeros(shape, device=dev, dtype=BF16)
-        self.v = torch.zeros(shape, device=dev, dtype=BF16)   # [L][B][H][cap/4][hd][4] inside
+        self.v = torch.zeros(shape, device=dev, dtype=BF16)
         self.D, self.B, self.cap = D, B, cap
 
     def struct(self) -> L.KV:
         return L.KV(k=self.k.data_ptr(), v=self.v.data_ptr(), L=self.D.L, B=self.B, H=self.D.H,
                     hd=self.D.hd, cap=self.cap)
 
+    def k_rows(self) -> torch.Tensor:
+        """K as slot-major [L][B][H][cap][hd] (copy)."""
+        return self.untile_k(self.k)
+
     def v_rows(self) -> torch.Tensor:
-        """V as [L][B][H][cap][hd] (de-interleaved copy)."""
-        D = self.D
-        v = self.v.view(D.L, self.B, D.H, self.cap // 4, D.hd, 4)
-        return v.permute(0, 1, 2, 3, 5, 4).reshape(D.L, self.B, D.H, self.cap, D.hd)
+        """V as slot-major [L][B][H][cap][hd] (copy)."""
+        return self.deinterleave_v(self.v)
+
+    def set_rows(self, k_rows: torch.Tensor, v_rows: torch.Tensor) -> None:
+        """Write slot-major K and V rows [L][B][H][cap][hd] into the cache."""
+        self.k.copy_(self.tile_k(k_rows.to(self.k.device, BF16)))
+        self.v.copy_(self.interleave_v(v_rows.to(self.v.device, BF16)))
+
+    # K: [cap/32][hd/8][32][8], slot offset o = 8a + 4e + r (a < 4, e < 2,
+    # r < 4) of a 32-slot group stored at row 16e + 4a + r
+    @staticmethod
+    def tile_k(rows: torch.Tensor) -> torch.Tensor:
+        """[..., cap, hd] slot-major -> the K layout (same shape back)."""
+        *lead, cap, hd = rows.shape
+        n = len(lead)
+        x = rows.reshape(*lead, cap // 32, 4, 2, 4, hd // 8, 8)       # (grp, a, e, r, piece, 8)
+        x = x.permute(*range(n), n, n + 4, n + 2, n + 1, n + 3, n + 5)  # (grp, piece, e, a, r, 8)
+        return x.reshape(*lead, cap, hd)
 
     @staticmethod
-    def interleave_v(v_rows: torch.Tensor) -> torch.Tensor:
-        """[..., cap, hd] slot-major -> [..., cap/4, hd, 4] interleaved (same shape back)."""
-        *lead, cap, hd = v_rows.shape
-        return v_rows.reshape(*lead, cap // 4, 4, hd).transpose(-1, -2).reshape(*lead, cap, hd)
+    def untile_k(tiled: torch.Tensor) -> torch.Tensor:
+        *lead, cap, hd = tiled.shape
+        n = len(lead)
+        x = tiled.reshape(*lead, cap // 32, hd // 8, 2, 4, 4, 8)      # (grp, piece, e, a, r, 8)
+        x = x.permute(*range(n), n, n + 3, n + 2, n + 4, n + 1, n + 5)  # (grp, a, e, r, piece, 8)
+        return x.reshape(*lead, cap, hd)
+
+    # V: [cap/8][hd][8], 8 consecutive slots per dim
+    @staticmethod
+    def interleave_v(rows: torch.Tensor) -> torch.Tensor:
+        """[..., cap, hd] slot-major -> the V layout (same shape back)."""
+        *lead, cap, hd = rows.shape
+        return rows.reshape(*lead, cap // 8, 8, hd).transpose(-1, -2).reshape(*lead, cap, hd)
+
+    @staticmethod
+    def deinterleave_v(inter: torch.Tensor) -> torch.Tensor:
+        *lead, cap, hd = inter.shape
+        return inter.reshape(*lead, cap // 8, hd, 8).transpose(-1, -2).reshape(*lead, cap, hd)
 
 
 class Session:
