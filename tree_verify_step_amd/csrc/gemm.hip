@@ -47,32 +47,6 @@ __host__ __device__ __forceinline__ int qkv_feature(int p, int d, int hd) {
   return h * hd + (ee < 16 ? j * 16 + ee : hd / 2 + j * 16 + (ee - 16));
 }
 
-// Destination of one QKV output column (logical feature f): q column, or
-// the head / dim of a K or V cache row.
-struct QkvCol {
-  int sec, c, h, i;
-};
-__device__ __forceinline__ QkvCol qkv_col(const QkvArgs& a, int f) {
-  QkvCol k;
-  k.sec = f / a.d;
-  k.c = f - k.sec * a.d;
-  k.h = k.c / a.hd;
-  k.i = k.c - k.h * a.hd;
-  return k;
-}
-// q -> bf16 row-major; k / v -> KV cache slot `slot` of sequence b.
-__device__ __forceinline__ void qkv_put(const QkvArgs& a, const QkvCol& k, int m, int b, int slot,
-                                        float val) {
-  const u16 ob = f32_to_bf16(val);
-  if (k.sec == 0) {
-    a.q[(size_t)m * a.d + k.c] = ob;
-    return;
-  }
-  const size_t base = ((size_t)b * a.H + k.h) * a.cap * a.hd;
-  if (k.sec == 1) a.kcache[base + kv_k_off(slot, k.i, a.hd)] = ob;
-  else a.vcache[base + kv_v_off(slot, k.i, a.hd)] = ob;
-}
-
 // Split-K partial exchange between workgroups that may sit on different
 // XCDs (separate L2s): 16-byte buffer stores and loads with the system-scope
 // cache policy (sc0 sc1: stores written through to memory, loads bypassing
@@ -117,6 +91,7 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
   __shared__ float rs_s[TR];
   __shared__ float ssw[W][TR];
   __shared__ int s_last;
+  __shared__ int s_slot0[MV_MAX_BATCH];        // QKV: cache slot of each sequence's node 0
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nt = blockIdx.x, split = blockIdx.y, mt = blockIdx.z;
@@ -204,10 +179,17 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
     for (int nb = 0; nb < NBW; ++nb) br[s][nb] = Bp[nb][(size_t)k * NBtot * 64];
   };
 
+  // QKV: prefix lengths (loaded first, stored to LDS once the operand loads
+  // are out; n + T <= cap is the caller's contract, clamping keeps every
+  // store in bounds)
+  int nraw = 0;
+  if (EPI == EPI_QKV && threadIdx.x < g.qkv.B) nraw = g.qkv.n_prefix[threadIdx.x];
   loadA(0);
 #pragma unroll
   for (int s = 0; s < KC; ++s) loadB(s, lo + s);
   storeA(0, 0);
+  if (EPI == EPI_QKV && threadIdx.x < g.qkv.B)
+    s_slot0[threadIdx.x] = min(max(nraw, 0), g.qkv.cap - g.qkv.T);
   __syncthreads();
   for (int c = 0; c < nchunks; ++c) {
     const int buf = c & 1;
@@ -236,7 +218,6 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
   const int row0 = mt * TR + 4 * (lane >> 4);
   float xo[MB][NBW][4], gn[NBW];              // ADD: residual x, next norm's gain
   float2 cs[MB][4];                           // QKV: RoPE (cos, sin) per row
-  int np[MB][4], bq[MB][4];                   // QKV: row's prefix length and sequence
   // QKV: the lane's two blocks are packed rows p0 (block 0) and p0 + 16
   // (block 1); with heads wider than 16 they hold dims i and i + hd/2 of one
   // head (RoPE partners, same (cos, sin)); with 16-wide heads each block is
@@ -245,7 +226,6 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
   const bool rot = EPI == EPI_QKV && p0 < 2 * g.qkv.d;
   const bool wide = g.qkv.hd >= 32;
   const int f0 = (rot && wide) ? qkv_feature(p0, g.qkv.d, g.qkv.hd) : p0;
-  const int f1 = (rot && wide) ? f0 + g.qkv.hd / 2 : p0 + 16;
   const int half = g.qkv.hd >> 1;
   if constexpr (EPI == EPI_ADD) {
 #pragma unroll
@@ -268,9 +248,7 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = min(row0 + rb * 16 + r, g.M - 1);
-        bq[rb][r] = m / g.qkv.T;
         cs[rb][r] = rot ? g.qkv.rope[(size_t)m * half + ci] : make_float2(1.f, 0.f);
-        np[rb][r] = g.qkv.n_prefix[bq[rb][r]];
       }
   }
 
@@ -386,7 +364,7 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
         if (m < g.M) g.ss_out[(size_t)m * g.ss_ld + nt] = s;
       }
     }
-  } else if (EPI == EPI_SWIGLU) {
+  } else if constexpr (EPI == EPI_SWIGLU) {
     if (active) {
       const int f = wb * 16 + col;
 #pragma unroll
@@ -400,15 +378,26 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
           }
         }
     }
-  } else if (EPI == EPI_QKV) {
+  } else if constexpr (EPI == EPI_QKV) {
+    // RoPE in registers, then the tile (TR rows x W*32 packed features) is
+    // staged as bf16 in the operand LDS and written out in 16-byte pieces:
+    // q rows, K pieces of 8 dims of one slot, V runs of 8 slots of one dim
+    // (single elements where a run is not whole in this tile)
     const QkvArgs& q = g.qkv;
+    constexpr int TC = W * 32;                   // packed features of the tile
+    constexpr int LDT = TC + 8;                  // padded staging row (u16)
+    u16* stg;
+    if constexpr (TR * LDT * 2 <= (int)sizeof(As)) {
+      stg = reinterpret_cast<u16*>(&As[0][0][0]);
+    } else {                                     // 256-row tiles: a buffer of its own
+      __shared__ u16 stg_own[TR * LDT];
+      stg = stg_own;
+    }
     const bool first = ((f0 % q.d) % q.hd) < half;    // block 0 holds the first half (narrow heads)
-    const QkvCol k0 = qkv_col(q, f0), k1 = qkv_col(q, f1);
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = row0 + rb * 16 + r;
         const float y0 = acc[rb][0][r], y1 = acc[rb][1][r];
         float s0 = 0.f, s1 = 0.f;
         if (!wide) {             // uniform: 16-wide heads only
@@ -426,14 +415,92 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
             o1 = first ? y1 * c - s1 * sn : y1 * c + s1 * sn;
           }
         }
-        if (active && m < g.M) {
-          // n + T <= cap is the caller's contract; clamping keeps every store in bounds
-          const int b = bq[rb][r];
-          const int slot = min(max(np[rb][r], 0), q.cap - q.T) + (m - b * q.T);
-          qkv_put(q, k0, m, b, slot, o0);
-          qkv_put(q, k1, m, b, slot, o1);
+        const int rl = rb * 16 + 4 * (lane >> 4) + r;
+        stg[rl * LDT + wave * 32 + col] = f32_to_bf16(o0);
+        stg[rl * LDT + wave * 32 + 16 + col] = f32_to_bf16(o1);
+      }
+    __syncthreads();
+    const int tc0 = nt * TC, mr0 = mt * TR;
+    const int p_end = min(tc0 + TC, g.N);
+    const int hs = __ffs(q.hd) - 1;              // hd is a power of two
+    // the sequences with rows in this tile (at most MV_MAX_BATCH): their
+    // first tile row, row count and the cache slot of that row
+    const int m_hi = min(mr0 + TR, g.M);
+    const int b_lo = mr0 / q.T;
+    int sr0[MV_MAX_BATCH], sn[MV_MAX_BATCH], ss0[MV_MAX_BATCH];
+#pragma unroll
+    for (int e = 0; e < MV_MAX_BATCH; ++e) {
+      const int b = b_lo + e;
+      const int lo_m = max(mr0, b * q.T), hi_m = min(m_hi, (b + 1) * q.T);
+      sn[e] = b < q.B ? max(hi_m - lo_m, 0) : 0;
+      sr0[e] = lo_m - mr0;
+      ss0[e] = sn[e] ? s_slot0[min(b, MV_MAX_BATCH - 1)] + (lo_m - b * q.T) : 0;
+    }
+    // q and K: 16-byte pieces of 8 consecutive features (8 consecutive packed
+    // rows of a 16-row block are 8 consecutive dims of one head)
+    if (tc0 < 2 * q.d) {
+      constexpr int CU = TC / 8;
+      const bool q_tile = tc0 + TC <= q.d;
+      for (int u = threadIdx.x; u < TR * CU; u += W * 64) {
+        // q: neighbouring threads take neighbouring pieces of a row;
+        // K: neighbouring threads take neighbouring rows (slots) of a piece
+        const int rl = q_tile ? u / CU : u % TR, cu = q_tile ? u % CU : u / TR;
+        const int p = tc0 + cu * 8, m = mr0 + rl;
+        if (p >= 2 * q.d || p >= p_end || m >= g.M) continue;
+        int f = p;                                // qkv_feature with shifts
+        if (q.hd >= 32) {
+          const int e = p & (q.hd - 1), jj = e >> 5, ee = e & 31;
+          f = (p - e) + (ee < 16 ? jj * 16 + ee : (q.hd >> 1) + jj * 16 + (ee - 16));
+        }
+        const uint4 v = *reinterpret_cast<const uint4*>(stg + rl * LDT + cu * 8);
+        if (f < q.d) {
+          *reinterpret_cast<uint4*>(q.q + (size_t)m * q.d + f) = v;
+        } else {
+          const int c = f - q.d, h = c >> hs, i = c & (q.hd - 1);
+          int b = b_lo, slot = 0;
+#pragma unroll
+          for (int e = 0; e < MV_MAX_BATCH; ++e)
+            if (rl >= sr0[e] && rl < sr0[e] + sn[e]) { b = b_lo + e; slot = ss0[e] + rl - sr0[e]; }
+          *reinterpret_cast<uint4*>(q.kcache + ((size_t)b * q.H + h) * q.cap * q.hd +
+                                    kv_k_off(slot, i, q.hd)) = v;
         }
       }
+    }
+    if (p_end > 2 * q.d) {
+      // V: 8-slot groups (8-aligned) of each sequence's slots in this tile; a
+      // whole group is one 16-byte store per dim, a partial one (first or
+      // last of a sequence) is written element by element
+      int gf[MV_MAX_BATCH], gc[MV_MAX_BATCH], G = 0;
+#pragma unroll
+      for (int e = 0; e < MV_MAX_BATCH; ++e) {
+        gf[e] = ss0[e] >> 3;
+        gc[e] = sn[e] ? ((ss0[e] + sn[e] - 1) >> 3) - gf[e] + 1 : 0;
+        G += gc[e];
+      }
+      for (int u = threadIdx.x; u < G * TC; u += W * 64) {
+        const int j = u % TC, p = tc0 + j;
+        if (p < 2 * q.d || p >= p_end) continue;
+        int k = u / TC, b = b_lo, r0 = 0, s0 = 0, n = 0, gs = 0;
+#pragma unroll
+        for (int e = 0; e < MV_MAX_BATCH; ++e) {
+          if (k >= 0 && k < gc[e]) { b = b_lo + e; r0 = sr0[e]; s0 = ss0[e]; n = sn[e]; gs = (gf[e] + k) * 8; }
+          k -= gc[e];
+        }
+        const int c = p - 2 * q.d, h = c >> hs, i = c & (q.hd - 1);
+        u16* vb = q.vcache + ((size_t)b * q.H + h) * q.cap * q.hd;
+        const int lo_s = max(gs, s0), hi_s = min(gs + 8, s0 + n);
+        const u16* src = stg + (r0 + lo_s - s0) * LDT + j;
+        if (lo_s == gs && hi_s == gs + 8) {
+          uint32_t w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            w[e] = (uint32_t)src[2 * e * LDT] | ((uint32_t)src[(2 * e + 1) * LDT] << 16);
+          *reinterpret_cast<uint4*>(vb + kv_v_off(gs, i, q.hd)) = uint4{w[0], w[1], w[2], w[3]};
+        } else {
+          for (int sl = lo_s; sl < hi_s; ++sl) vb[kv_v_off(sl, i, q.hd)] = src[(sl - lo_s) * LDT];
+        }
+      }
+    }
   }
 }
 
