@@ -321,18 +321,18 @@ MV_API int mv_prefill(mv_ctx* ctx, const int32_t* ids, int32_t ld, const int32_t
 MV_API int mv_step(mv_ctx* ctx, int32_t graph, void* stream);
 
 /* Launch-group kinds reported by mv_step_profile. */
-#define MV_K_HEADS 0     /* Medusa heads: W1 block, vocab projection, top-s, tree fill */
-#define MV_K_EMBED 1     /* embedding gather and RoPE table */
-#define MV_K_NORM 2      /* first layer's norm operand (later norms are GEMM epilogues) */
+#define MV_K_HEADS 0     /* Medusa heads: W1 block, vocab projection, top-s */
+#define MV_K_EMBED 1     /* tree tokens, embedding gather, RoPE table, first norm's operand */
+#define MV_K_NORM 2      /* standalone norm operand (in a step the embedding writes it) */
 #define MV_K_QKV 3       /* fused QKV GEMM with RoPE and KV-cache write */
 #define MV_K_ATTN 4      /* tree attention */
 #define MV_K_O 5         /* output projection GEMM + residual */
 #define MV_K_GATE_UP 6   /* gate/up GEMM with SwiGLU */
 #define MV_K_DOWN 7      /* down projection GEMM + residual */
 #define MV_K_LM_HEAD 8   /* LM-head GEMM (final norm folded in) */
-#define MV_K_ACCEPT 9    /* acceptance and next root */
+#define MV_K_ACCEPT 9    /* acceptance, next root, n update */
 #define MV_K_COUNT 11
-#define MV_K_COMPACT 10  /* KV compaction and n update */
+#define MV_K_COMPACT 10  /* KV compaction (and the draw counter) */
 
 /* One step enqueued directly (no graph) with a pair of HIP events on
  * `stream` around every launch group; waits for the step, then reports per

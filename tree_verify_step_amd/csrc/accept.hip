@@ -228,22 +228,34 @@ __device__ void block_sample(const float* __restrict__ z, int V, int amax_id, do
 }
 
 __global__ __launch_bounds__(256) void accept_finish_kernel(
-    const float* __restrict__ logits, const int32_t* __restrict__ amax,
-    const double* __restrict__ stats, const int32_t* __restrict__ parent,
+    const float* __restrict__ logits, const int32_t* __restrict__ amax_rows,
+    unsigned long long* __restrict__ amax_key, const double* __restrict__ stats, const int32_t* __restrict__ parent,
     const int32_t* __restrict__ depth_of, const int32_t* __restrict__ tok, int T, int V, int depth,
     int mode, int root_mode, double temperature, double eps, double delta,
     const double* __restrict__ u, const int32_t* __restrict__ u_index, int u_stride,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ path, int32_t* __restrict__ best_out,
     int32_t* __restrict__ next_root, int32_t* __restrict__ emitted, double* __restrict__ margin,
     const float* __restrict__ x, const u16* __restrict__ final_norm, u16* __restrict__ h_last,
-    int d) {
+    int d, int32_t* __restrict__ n_advance) {
   __shared__ unsigned char pass[MV_MAXT], ok[MV_MAXT];
   __shared__ double lq[MV_MAXT], score[MV_MAXT];
+  __shared__ int par[MV_MAXT], dep[MV_MAXT], tk[MV_MAXT];   // the tree, staged for the walk
+  __shared__ int amax[MV_MAXT];                              // argmax of each of the T rows
   __shared__ int s_best;
   const int b = blockIdx.x;
-  const int32_t* par = parent + (size_t)b * T;
-  const int32_t* dep = depth_of + (size_t)b * T;
-  const int32_t* tk = tok + (size_t)b * T;
+  for (int v = threadIdx.x; v < T; v += 256) {
+    par[v] = parent[(size_t)b * T + v];
+    dep[v] = depth_of[(size_t)b * T + v];
+    tk[v] = tok[(size_t)b * T + v];
+    if (amax_key) {         // the LM head's atomic argmax keys; cleared for the next step
+      const size_t r = (size_t)b * T + v;
+      amax[v] = argmax_key_col(amax_key[r]);
+      amax_key[r] = 0ull;
+    } else {
+      amax[v] = amax_rows[(size_t)b * T + v];
+    }
+  }
+  __syncthreads();
   const int row0 = b * T;
   const double inv_t = 1.0 / temperature;
 
@@ -257,7 +269,7 @@ __global__ __launch_bounds__(256) void accept_finish_kernel(
     }
     const int p = par[v];
     if (mode == MV_ACCEPT_GREEDY) {
-      pass[v] = tk[v] == amax[row0 + p];
+      pass[v] = tk[v] == amax[p];
       lq[v] = 0.0;
     } else {
       const double* st = stats + (size_t)(row0 + p) * 3;
@@ -271,32 +283,83 @@ __global__ __launch_bounds__(256) void accept_finish_kernel(
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    ok[0] = 1;
-    score[0] = 0.0;
-    int best = 0;
-    for (int v = 1; v < T; ++v) {
-      const int p = par[v];
-      ok[v] = ok[p] && pass[v];
-      score[v] = score[p] + lq[v];
-      if (ok[v]) {
-        if (dep[v] > dep[best] ||
-            (dep[v] == dep[best] && mode == MV_ACCEPT_TYPICAL && score[v] > score[best]))
-          best = v;
+  // every node walks its own ancestor chain (no dependence between nodes):
+  // ok = all edges on the root path pass, score = sum of log q from the root
+  // down; then the deepest ok node (typical: then the highest score), lowest
+  // index among equals, by a block reduction
+  {
+    const bool typ = mode == MV_ACCEPT_TYPICAL;
+    int bv = 0, bd = 0;                 // best node, its depth
+    double bs = 0.0;                    // its score
+    for (int v = threadIdx.x; v < T; v += 256) {
+      int ch[MV_MAX_DEPTH + 1];
+      int a = v;
+#pragma unroll
+      for (int i = 0; i <= MV_MAX_DEPTH; ++i) {
+        ch[i] = a;
+        if (a > 0) a = (par[a] >= 0 && par[a] < T) ? par[a] : 0;
+      }
+      bool okv = a == 0;                // reached the root within the depth limit
+      double sc = 0.0;
+#pragma unroll
+      for (int i = MV_MAX_DEPTH; i >= 0; --i)
+        if (ch[i] > 0) {
+          okv = okv && pass[ch[i]];
+          sc += lq[ch[i]];
+        }
+      ok[v] = okv;
+      score[v] = sc;
+      if (okv && (dep[v] > bd || (typ && dep[v] == bd && sc > bs))) {
+        bv = v;
+        bd = dep[v];
+        bs = sc;
       }
     }
+    // candidates of one thread come in index order, so ties already favour
+    // the lower index; across threads compare explicitly
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int ov = __shfl_xor(bv, o, 64), od = __shfl_xor(bd, o, 64);
+      const double os = __shfl_xor(bs, o, 64);
+      if (od > bd || (od == bd && ((typ && os > bs) || ((!typ || os == bs) && ov < bv)))) {
+        bv = ov;
+        bd = od;
+        bs = os;
+      }
+    }
+    __shared__ int w_v[4], w_d[4];
+    __shared__ double w_s[4];
+    if ((threadIdx.x & 63) == 0) {
+      w_v[threadIdx.x >> 6] = bv;
+      w_d[threadIdx.x >> 6] = bd;
+      w_s[threadIdx.x >> 6] = bs;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      for (int w = 1; w < 4; ++w)
+        if (w_d[w] > bd || (w_d[w] == bd && ((typ && w_s[w] > bs) || ((!typ || w_s[w] == bs) && w_v[w] < bv)))) {
+          bv = w_v[w];
+          bd = w_d[w];
+          bs = w_s[w];
+        }
+      s_best = bv;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int best = s_best;
     int nodes[MV_MAX_DEPTH + 1];
     int cnt = 0;
     for (int v = best; v >= 0 && cnt <= MV_MAX_DEPTH; v = (v == 0 ? -1 : par[v])) nodes[cnt++] = v;
     const int L = cnt - 1;
     accept_len[b] = L;
     best_out[b] = best;
+    if (n_advance) n_advance[b] += L + 1;       // the accepted tokens join the prefix
     for (int m = 0; m <= depth; ++m) {
       const int node = m <= L ? nodes[L - m] : -1;
       path[(size_t)b * (depth + 1) + m] = node;
       if (emitted) emitted[(size_t)b * (depth + 1) + m] = node >= 0 ? tk[node] : -1;
     }
-    s_best = best;
   }
   __syncthreads();
   const int best = s_best;
@@ -304,15 +367,16 @@ __global__ __launch_bounds__(256) void accept_finish_kernel(
 
   if (x && h_last) block_norm_row(x + (size_t)brow * d, final_norm, h_last + (size_t)b * d, d);
   if (root_mode == MV_ROOT_ARGMAX) {
-    if (threadIdx.x == 0) next_root[b] = amax[brow];
+    if (threadIdx.x == 0) next_root[b] = amax[best];
     return;
   }
   const double ub = u[(size_t)(u_index ? u_index[0] : 0) * u_stride + b];
-  block_sample(logits + (size_t)brow * V, V, amax[brow], inv_t, ub, next_root + b,
+  block_sample(logits + (size_t)brow * V, V, amax[best], inv_t, ub, next_root + b,
                margin ? margin + (size_t)b * (T + 1) + T : nullptr);
 }
 
-hipError_t launch_accept_finish(const float* logits, const int32_t* argmax, const double* stats,
+hipError_t launch_accept_finish(const float* logits, const int32_t* argmax, unsigned long long* amax_key,
+                                const double* stats,
                                 const int32_t* parent, const int32_t* depth_of,
                                 const int32_t* tok, int B, int T, int V, int depth, int mode,
                                 int root_mode, double temperature, double eps, double delta,
@@ -320,11 +384,12 @@ hipError_t launch_accept_finish(const float* logits, const int32_t* argmax, cons
                                 int32_t* accept_len, int32_t* path, int32_t* best,
                                 int32_t* next_root, int32_t* emitted, double* margin,
                                 const float* x, const u16* final_norm, u16* h_last, int d,
-                                hipStream_t s) {
-  hipLaunchKernelGGL(accept_finish_kernel, dim3(B), dim3(256), 0, s, logits, argmax, stats,
+                                hipStream_t s, int32_t* n_advance) {
+  hipLaunchKernelGGL(accept_finish_kernel, dim3(B), dim3(256), 0, s, logits, argmax, amax_key,
+                     stats,
                      parent, depth_of, tok, T, V, depth, mode, root_mode, temperature, eps, delta,
                      u, u_index, u_stride, accept_len, path, best, next_root, emitted, margin, x,
-                     final_norm, h_last, d);
+                     final_norm, h_last, d, n_advance);
   return hipGetLastError();
 }
 

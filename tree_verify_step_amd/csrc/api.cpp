@@ -102,8 +102,8 @@ static GemmCfg gemm_cfg(const mv_dims& D, int kind, int Mp) {
 }
 
 struct Ws {
-  size_t x, xa, ao, ha, ss, q, rope, part, counters, hu, hz, topi, topv, tcv, tci, amax, stats,
-      cnt, total;
+  size_t x, xa, ao, ha, ss, q, rope, part, counters, hu, hz, topi, topv, tcv, tci, amax, amaxp,
+      stats, cnt, total;
   int ss_ld;    // floats per row of the sums-of-squares buffer
 };
 
@@ -151,6 +151,7 @@ static Ws ws_layout(const mv_dims& D, int B, int T) {
   w.tcv = take((size_t)B * D.K * mvk::topk_waves(D.V) * MV_MAX_TOPK * 4);
   w.tci = take((size_t)B * D.K * mvk::topk_waves(D.V) * MV_MAX_TOPK * 4);
   w.amax = take((size_t)M * 4);
+  w.amaxp = take((size_t)M * 8);
   w.stats = take((size_t)M * 3 * 8);
   w.cnt = take((size_t)B * 4);
   w.total = off;
@@ -322,7 +323,7 @@ static int enq_layer(const mv_dims& D, int B, const mv_tree& t, const int32_t* n
 // layer); otherwise it is prepared from x here.
 static int enq_lm_head(const mv_dims& D, int M, const float* x, const void* final_norm,
                        const void* lm, float* logits, int ss_tiles, void* ws, const Ws& L,
-                       hipStream_t s) {
+                       hipStream_t s, unsigned long long* amax_key = nullptr) {
   if (ss_tiles <= 0) {
     const int rc = enq_norm_prep(D, M, x, final_norm, ws, L, s);
     if (rc) return rc;
@@ -334,6 +335,7 @@ static int enq_lm_head(const mv_dims& D, int M, const float* x, const void* fina
   g.ss = at<float>(ws, L.ss);
   g.ss_tiles = ss_tiles;
   g.out_f32 = logits;
+  g.amax_key = amax_key;
   MV_HIP(mvk::launch_gemm(g, s));
   return MV_OK;
 }
@@ -359,13 +361,19 @@ static int enq_accept(int B, int T, int V, int d, const float* logits, const mv_
                       const int32_t* u_index, int u_stride, int32_t* accept_len, int32_t* path,
                       int32_t* best, int32_t* next_root, int32_t* emitted, double* margin,
                       const float* x, const void* final_norm, void* h_last, int32_t* amax,
-                      double* stats, hipStream_t s) {
-  MV_HIP(mvk::launch_row_stats(logits, B * T, V, p.mode, p.temperature, amax, stats, s));
-  MV_HIP(mvk::launch_accept_finish(logits, amax, stats, t.parent, t.depth_of, tok, B, T, V,
+                      double* stats, hipStream_t s, unsigned long long* amax_key = nullptr,
+                      int32_t* n_advance = nullptr) {
+  // greedy acceptance with the LM head's argmax keys needs no pass over the
+  // logits; otherwise the rows' argmax (and typical statistics)
+  if (!(amax_key && p.mode == MV_ACCEPT_GREEDY)) {
+    amax_key = nullptr;
+    MV_HIP(mvk::launch_row_stats(logits, B * T, V, p.mode, p.temperature, amax, stats, s));
+  }
+  MV_HIP(mvk::launch_accept_finish(logits, amax, amax_key, stats, t.parent, t.depth_of, tok, B, T, V,
                                    t.depth, p.mode, p.root_mode, p.temperature, p.eps, p.delta, u,
                                    u_index, u_stride, accept_len, path, best, next_root, emitted,
                                    margin, x, static_cast<const u16*>(final_norm),
-                                   static_cast<u16*>(h_last), d, s));
+                                   static_cast<u16*>(h_last), d, s, n_advance));
   return MV_OK;
 }
 
@@ -613,42 +621,46 @@ static int enq_step(mv_ctx* c, hipStream_t s) {
   const Ws& L = c->L;
   int rc;
   const int Dn = d.tree.depth;
+  int32_t* top_ids = d.top_ids ? d.top_ids : at<int32_t>(ws, L.topi);
   prof_begin(s);
   if (Dn > 0) {
-    rc = enq_heads(D, B, Dn, d.s, d.h_last, d.w1, d.w2, &d.tree, d.root_tok,
-                   d.top_ids ? d.top_ids : at<int32_t>(ws, L.topi), at<float>(ws, L.topv),
-                   d.tree_tok, d.head_logits ? d.head_logits : at<float>(ws, L.hz), ws, L, s);
+    // the tree's tokens are filled in by the embedding launch below
+    rc = enq_heads(D, B, Dn, d.s, d.h_last, d.w1, d.w2, nullptr, d.root_tok, top_ids,
+                   at<float>(ws, L.topv), nullptr,
+                   d.head_logits ? d.head_logits : at<float>(ws, L.hz), ws, L, s);
     if (rc) return rc;
-  } else {
-    MV_HIP(mvk::launch_tree_fill(at<int32_t>(ws, L.topi), d.root_tok, d.tree.depth_of, d.tree.rank,
-                                 d.tree_tok, B, T, 1, d.s, s));
   }
   prof_end(MV_K_HEADS, s);
   float* x = at<float>(ws, L.x);
   prof_begin(s);
-  MV_HIP(mvk::launch_embed(d.tree_tok, static_cast<const u16*>(d.embed), x, nullptr,
-                           M, D.d, D.V, d.n_prefix, d.tree.depth_of, at<float2>(ws, L.rope), T,
-                           D.hd, s));
-  prof_begin(s);
-  if ((rc = enq_norm_prep(D, M, x, c->layers[0].attn_norm, ws, L, s))) return rc;
-  prof_end(MV_K_NORM, s);
+  // tree tokens, embedding rows, RoPE tables and the first norm's operand
+  const mvk::EmbedTree et{top_ids, d.root_tok, d.tree.rank, Dn > 0 ? Dn : 1, d.s, d.tree_tok};
+  const mvk::EmbedNorm en{static_cast<const u16*>(c->layers[0].attn_norm), at<u16>(ws, L.xa),
+                          at<float>(ws, L.ss), L.ss_ld};
+  MV_HIP(mvk::launch_embed(nullptr, static_cast<const u16*>(d.embed), x, nullptr, M, D.d, D.V,
+                           d.n_prefix, d.tree.depth_of, at<float2>(ws, L.rope), T, D.hd, s, et, en));
+  prof_end(MV_K_EMBED, s);
   if ((rc = enq_layers(c, d.tree, x, s))) return rc;
   prof_begin(s);
+  const bool greedy = d.accept.mode == MV_ACCEPT_GREEDY;
+  unsigned long long* amaxp = greedy ? at<unsigned long long>(ws, L.amaxp) : nullptr;
   if ((rc = enq_lm_head(D, M, x, d.final_norm, d.lm_head, d.logits, ss_tiles_of(D, G_DOWN, M),
-                        ws, L, s)))
+                        ws, L, s, amaxp)))
     return rc;
   prof_end(MV_K_LM_HEAD, s);
   prof_begin(s);
   if ((rc = enq_accept(B, T, D.V, D.d, d.logits, d.tree, d.tree_tok, d.accept, d.u_draws,
                        d.u_index, B, d.accept_len, d.path, d.best, d.root_tok, d.emitted, nullptr,
                        x, d.final_norm, d.h_last, at<int32_t>(ws, L.amax), at<double>(ws, L.stats),
-                       s)))
+                       s, amaxp, d.n_prefix)))
     return rc;
   prof_end(MV_K_ACCEPT, s);
   prof_begin(s);
+  // n_prefix was moved on by the acceptance kernel; the compaction bumps the
+  // draw counter
   MV_HIP(mvk::launch_compact(static_cast<u16*>(d.kv.k), static_cast<u16*>(d.kv.v), D.L, B, D.H,
-                             D.hd, d.kv.cap, d.path, d.tree.depth + 1, d.accept_len, d.n_prefix, s));
-  MV_HIP(mvk::launch_advance(d.n_prefix, d.accept_len, B, d.u_index, s));
+                             D.hd, d.kv.cap, d.path, d.tree.depth + 1, d.accept_len, d.n_prefix, s,
+                             1, d.u_index));
   prof_end(MV_K_COMPACT, s);
   return MV_OK;
 }
@@ -706,8 +718,10 @@ MV_API int mv_ctx_create(mv_ctx** out, const mv_step_desc* desc) {
   if (e == hipSuccess) e = hipMemcpy(c->chain, ch.data(), ch.size() * 4, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(c->chain_anc, ca.data(), ca.size() * 8, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemset(c->chunk_tok, 0, (size_t)B * T * 4);
-  // the GEMMs' arrival counters must start at zero (they reset themselves)
+  // the GEMMs' arrival counters and the LM head's argmax keys must start at
+  // zero (their consumers reset them)
   if (e == hipSuccess) e = hipMemset(at<char>(d.ws, c->L.counters), 0, c->L.hu - c->L.counters);
+  if (e == hipSuccess) e = hipMemset(at<char>(d.ws, c->L.amaxp), 0, c->L.stats - c->L.amaxp);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking);
   if (e != hipSuccess) {

@@ -70,6 +70,17 @@ __host__ __device__ __forceinline__ size_t kv_v_off(int slot, int dim, int hd) {
   return ((size_t)(slot >> 3) * hd + dim) * 8 + (slot & 7);
 }
 
+// Order-preserving 64-bit key of (value, column) for an argmax by atomic max:
+// larger values win, and among equal values the lower column (0 = no entry).
+__device__ __forceinline__ unsigned long long argmax_key(float v, int col) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)o << 32) | (uint32_t)~(uint32_t)col;
+}
+__device__ __forceinline__ int argmax_key_col(unsigned long long k) {
+  return (int)~(uint32_t)(k & 0xffffffffull);
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -130,6 +141,9 @@ struct GemmArgs {
   const u16* next_gain;  // ADD, nullable: gain of the norm that reads x next
   u16* xn_out;           // ADD: packed bf16 [Mp][N] = x * next_gain
   float* ss_out;         // ADD: [Mp][ss_ld] rows' sums of squares of x per column tile
+  unsigned long long* amax_key;   // STORE, nullable: per row, atomic max of
+                     //   argmax_key(value, column) over the row's columns; must
+                     //   hold 0 before the launch (the consumer clears it)
   float* partial;    // split-K partial tiles
   int* counters;     // split-K arrival counters [tiles], zero between launches
   QkvArgs qkv;
@@ -141,9 +155,26 @@ int gemm_ntiles(int epi, int N, int w, int nbw);      // column tiles
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
 hipError_t launch_pack(const u16* src, u16* dst, int R, int C, int rope_hd, int rope_rows,
                        hipStream_t s);
+// Embedding options: tree tokens from the heads' top-s lists (top_ids
+// [B][D][s_top], root [B], rank [B*T]; tokens written to tok_out), and the
+// first norm's GEMM operand (packed bf16(x * gain) [Mp][d], sums of squares at
+// ss[m * ss_ld]).  Null top_ids / gain: off.
+struct EmbedTree {
+  const int32_t* top_ids;
+  const int32_t* root;
+  const int32_t* rank;
+  int D, s_top;
+  int32_t* tok_out;
+};
+struct EmbedNorm {
+  const u16* gain;
+  u16* xn;
+  float* ss;
+  int ss_ld;
+};
 hipError_t launch_embed(const int32_t* tok, const u16* E, float* x, float* ss, int M, int d,
                         int V, const int32_t* n_prefix, const int32_t* depth_of, float2* rope,
-                        int T, int hd, hipStream_t s);
+                        int T, int hd, hipStream_t s, EmbedTree et = {}, EmbedNorm en = {});
 hipError_t launch_norm_prep(const float* x, const u16* g, u16* xn_packed, float* ss, int ss_ld,
                             int M, int d, hipStream_t s);
 hipError_t launch_rope_table(const int32_t* n_prefix, const int32_t* depth_of, float2* rope,
@@ -163,7 +194,8 @@ hipError_t launch_tree_fill(const int32_t* top_ids, const int32_t* root, const i
                             hipStream_t s);
 hipError_t launch_row_stats(const float* logits, int rows, int V, int mode, double temperature,
                             int32_t* argmax, double* stats, hipStream_t s);
-hipError_t launch_accept_finish(const float* logits, const int32_t* argmax, const double* stats,
+hipError_t launch_accept_finish(const float* logits, const int32_t* argmax, unsigned long long* amax_key,
+                                const double* stats,
                                 const int32_t* parent, const int32_t* depth_of,
                                 const int32_t* tok, int B, int T, int V, int depth, int mode,
                                 int root_mode, double temperature, double eps, double delta,
@@ -171,7 +203,7 @@ hipError_t launch_accept_finish(const float* logits, const int32_t* argmax, cons
                                 int32_t* accept_len, int32_t* path, int32_t* best,
                                 int32_t* next_root, int32_t* emitted, double* margin,
                                 const float* x, const u16* final_norm, u16* h_last, int d,
-                                hipStream_t s);
+                                hipStream_t s, int32_t* n_advance = nullptr);
 hipError_t launch_prefill_select(const float* logits, const int32_t* amax, const int32_t* cnt,
                                  int B, int T, int V, int root_mode, double temperature,
                                  const double* u, int32_t* root, int32_t* n_prefix,
@@ -179,7 +211,8 @@ hipError_t launch_prefill_select(const float* logits, const int32_t* amax, const
                                  hipStream_t s);
 hipError_t launch_compact(u16* kc, u16* vc, int L, int B, int H, int hd, int cap,
                           const int32_t* path, int path_stride, const int32_t* accept_len,
-                          const int32_t* n_prefix, hipStream_t s);
+                          const int32_t* n_prefix, hipStream_t s, int advanced = 0,
+                          int32_t* u_index = nullptr);
 hipError_t launch_advance(int32_t* n_prefix, const int32_t* accept_len, int B,
                           int32_t* counter, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);

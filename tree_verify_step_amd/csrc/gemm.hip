@@ -71,6 +71,18 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// One step of a (value, column) maximum over a DPP row: larger value, then
+// lower column.
+template <int CTRL>
+__device__ __forceinline__ void row16_best(float& bv, int& bi) {
+  const float ov = MV_DPP(bv, CTRL);
+  const int oi = __builtin_amdgcn_mov_dpp(bi, CTRL, 0xF, 0xF, false);
+  if (ov > bv || (ov == bv && oi < bi)) {
+    bv = ov;
+    bi = oi;
+  }
+}
+
 // k-blocks per activation chunk (= depth of the weight ring): the LDS chunk
 // holds KC * MB KiB per buffer.
 template <int MB>
@@ -320,6 +332,45 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
             const int m = row0 + rb * 16 + r;
             if (m < g.M) g.out_f32[(size_t)m * g.N + (first_blk + nb) * 16 + col] = acc[rb][nb][r];
           }
+    }
+    if (g.amax_key) {
+      // each row's argmax over this tile's columns: lanes of a 16-lane row
+      // group (shuffles), then the waves (LDS); ties go to the lower column
+      __shared__ float s_av[W][TR];
+      __shared__ int s_ai[W][TR];
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float bv = -INFINITY;
+          int bi = 0x7fffffff;
+#pragma unroll
+          for (int nb = 0; nb < NBW; ++nb) {
+            const float v = active ? acc[rb][nb][r] : -INFINITY;
+            const int i = (first_blk + nb) * 16 + col;
+            if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+          }
+          row16_best<0xB1>(bv, bi);     // quad swaps, half-row and row mirrors
+          row16_best<0x4E>(bv, bi);
+          row16_best<0x141>(bv, bi);
+          row16_best<0x140>(bv, bi);
+          if (col == 0) {
+            s_av[wave][rb * 16 + 4 * (lane >> 4) + r] = bv;
+            s_ai[wave][rb * 16 + 4 * (lane >> 4) + r] = bi;
+          }
+        }
+      __syncthreads();
+      for (int r = threadIdx.x; r < TR; r += W * 64) {
+        const int m = mt * TR + r;
+        if (m >= g.M) continue;
+        float bv = s_av[0][r];
+        int bi = s_ai[0][r];
+#pragma unroll
+        for (int w = 1; w < W; ++w)
+          if (s_av[w][r] > bv || (s_av[w][r] == bv && s_ai[w][r] < bi)) { bv = s_av[w][r]; bi = s_ai[w][r]; }
+        __hip_atomic_fetch_max(g.amax_key + m, argmax_key(bv, bi), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   } else if (EPI == EPI_ADD) {
     const bool nxt = g.next_gain != nullptr && g.xn_out != nullptr;

@@ -130,17 +130,47 @@ __device__ __forceinline__ bool better_vi(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
-// v/id: this lane's 16 candidates (id INT_MAX = empty).  Writes the wave's
-// top s into outv/outi (lane r writes round r's winner).
-__device__ __forceinline__ void wave_select(const float (&v)[16], const int (&id)[16], int s,
+// Best (value, id) of the wave in every lane: DPP lane moves inside each
+// 16-lane row (quad swaps, half-row and row mirrors), then two cross-row
+// shuffles.
+template <int CTRL>
+__device__ __forceinline__ void dpp_best(float& wv, int& wi) {
+  const float ov = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(wv), CTRL, 0xF, 0xF, false));
+  const int oi = __builtin_amdgcn_mov_dpp(wi, CTRL, 0xF, 0xF, false);
+  if (better_vi(ov, oi, wv, wi)) {
+    wv = ov;
+    wi = oi;
+  }
+}
+__device__ __forceinline__ void wave_best(float& wv, int& wi) {
+  dpp_best<0xB1>(wv, wi);     // quad_perm [1,0,3,2]
+  dpp_best<0x4E>(wv, wi);     // quad_perm [2,3,0,1]
+  dpp_best<0x141>(wv, wi);    // row_half_mirror
+  dpp_best<0x140>(wv, wi);    // row_mirror
+#pragma unroll
+  for (int o = 16; o <= 32; o <<= 1) {
+    const float ov = __shfl_xor(wv, o, 64);
+    const int oi = __shfl_xor(wi, o, 64);
+    if (better_vi(ov, oi, wv, wi)) {
+      wv = ov;
+      wi = oi;
+    }
+  }
+}
+
+// v/id: this lane's N (<= 32) candidates (id INT_MAX = empty).  Writes the
+// wave's top s into outv/outi (lane r writes round r's winner).
+template <int N>
+__device__ __forceinline__ void wave_select(const float (&v)[N], const int (&id)[N], int s,
                                             float* outv, int* outi) {
+  static_assert(N <= 32, "the taken mask holds 32 candidates");
   const int lane = threadIdx.x & 63;
   unsigned taken = 0;
   for (int r = 0; r < s; ++r) {
     float bv = -INFINITY;
     int bi = 0x7fffffff, bj = -1;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < N; ++j) {
       if (!((taken >> j) & 1u) && better_vi(v[j], id[j], bv, bi)) {
         bv = v[j];
         bi = id[j];
@@ -149,15 +179,7 @@ __device__ __forceinline__ void wave_select(const float (&v)[16], const int (&id
     }
     float wv = bv;
     int wi = bi;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(wv, o, 64);
-      const int oi = __shfl_xor(wi, o, 64);
-      if (better_vi(ov, oi, wv, wi)) {
-        wv = ov;
-        wi = oi;
-      }
-    }
+    wave_best(wv, wi);
     if (bj >= 0 && bi == wi) taken |= 1u << bj;     // ids are unique: one owner
     if (lane == r) {
       outv[0] = wv;

@@ -56,15 +56,29 @@ __device__ __forceinline__ float block_sum256(float v) {
 // sum of squares of the row; optionally the row's RoPE table: (cos, sin) of
 // position * 10000^(-2i/hd), position = n[b] + depth[m], angles in double.
 // Token ids outside [0, V) are clamped.
+// With et.top_ids the token is the tree's own (root for node 0, else the
+// node's rank in its depth's head top-s list) and is written to et.tok_out;
+// with en.gain the row also leaves the first norm's GEMM operand: packed
+// bf16(x * gain) and its sum of squares at en.ss[m * en.ss_ld].
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tok,
                                                     const u16* __restrict__ E,
                                                     float* __restrict__ x, float* __restrict__ ss,
                                                     int d, int V,
                                                     const int32_t* __restrict__ n_prefix,
                                                     const int32_t* __restrict__ depth_of,
-                                                    float2* __restrict__ rope, int T, int hd) {
+                                                    float2* __restrict__ rope, int T, int hd,
+                                                    EmbedTree et, EmbedNorm en) {
   const int m = blockIdx.x;
-  int t = tok[m];
+  int t;
+  if (et.top_ids) {
+    const int b = m / T, v = m - b * T;
+    const int dep = min(depth_of[m], et.D);
+    const int rk = min(max(et.rank[m], 0), et.s_top - 1);
+    t = (v == 0 || dep <= 0) ? et.root[b] : et.top_ids[((size_t)b * et.D + (dep - 1)) * et.s_top + rk];
+    if (threadIdx.x == 0) et.tok_out[m] = t;
+  } else {
+    t = tok[m];
+  }
   t = t < 0 ? 0 : (t >= V ? V - 1 : t);
   const u16* e = E + (size_t)t * d;
   float* xr = x + (size_t)m * d;
@@ -77,9 +91,19 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
     *reinterpret_cast<float4*>(xr + c + 4) = b;
     sq += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w + b.x * b.x + b.y * b.y + b.z * b.z +
           b.w * b.w;
+    if (en.gain) {
+      const uint4 gw = *reinterpret_cast<const uint4*>(en.gain + c);
+      uint4 o;
+      o.x = f32_to_bf16(a.x * bf16lo(gw.x)) | ((uint32_t)f32_to_bf16(a.y * bf16hi(gw.x)) << 16);
+      o.y = f32_to_bf16(a.z * bf16lo(gw.y)) | ((uint32_t)f32_to_bf16(a.w * bf16hi(gw.y)) << 16);
+      o.z = f32_to_bf16(b.x * bf16lo(gw.z)) | ((uint32_t)f32_to_bf16(b.y * bf16hi(gw.z)) << 16);
+      o.w = f32_to_bf16(b.z * bf16lo(gw.w)) | ((uint32_t)f32_to_bf16(b.w * bf16hi(gw.w)) << 16);
+      *reinterpret_cast<uint4*>(en.xn + packed_index(m, c, d)) = o;
+    }
   }
   sq = block_sum256(sq);
   if (threadIdx.x == 0 && ss) ss[m] = sq;
+  if (threadIdx.x == 0 && en.gain) en.ss[(size_t)m * en.ss_ld] = sq;
   if (rope) {
     const int half = hd >> 1;
     const double pos = (double)(n_prefix[m / T] + depth_of[m]);
@@ -94,9 +118,9 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
 
 hipError_t launch_embed(const int32_t* tok, const u16* E, float* x, float* ss, int M, int d,
                         int V, const int32_t* n_prefix, const int32_t* depth_of, float2* rope,
-                        int T, int hd, hipStream_t s) {
+                        int T, int hd, hipStream_t s, EmbedTree et, EmbedNorm en) {
   hipLaunchKernelGGL(embed_kernel, dim3(M), dim3(256), 0, s, tok, E, x, ss, d, V, n_prefix,
-                     depth_of, rope, T, hd);
+                     depth_of, rope, T, hd, et, en);
   return hipGetLastError();
 }
 
@@ -186,14 +210,18 @@ hipError_t launch_rope_table(const int32_t* n_prefix, const int32_t* depth_of, f
 __global__ void compact_kernel(u16* __restrict__ kc, u16* __restrict__ vc, int L, int B, int H,
                                int hd, int cap, const int32_t* __restrict__ path, int path_stride,
                                const int32_t* __restrict__ accept_len,
-                               const int32_t* __restrict__ n_prefix) {
+                               const int32_t* __restrict__ n_prefix, int advanced,
+                               int32_t* __restrict__ u_index) {
+  // advanced: n_prefix already holds n + accept_len + 1 (the acceptance
+  // kernel moved it on); the step's draw counter is bumped here
+  if (advanced && u_index && blockIdx.x == 0 && threadIdx.x == 0) u_index[0] += 1;
   const size_t total = (size_t)L * B * H * hd;
   for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
        e += (size_t)gridDim.x * blockDim.x) {
     const int dim = (int)(e % hd);
     const size_t lbh = e / hd;                    // (l*B + b)*H + h
     const int b = (int)((lbh / H) % B);
-    const int n = max(n_prefix[b], 0);
+    const int n = max(n_prefix[b] - (advanced ? accept_len[b] + 1 : 0), 0);
     int cnt = accept_len[b] + 1;
     cnt = cnt > path_stride ? path_stride : (cnt < 1 ? 1 : cnt);
     const int32_t* pb = path + (size_t)b * path_stride;
@@ -216,12 +244,13 @@ __global__ void compact_kernel(u16* __restrict__ kc, u16* __restrict__ vc, int L
 
 hipError_t launch_compact(u16* kc, u16* vc, int L, int B, int H, int hd, int cap,
                           const int32_t* path, int path_stride, const int32_t* accept_len,
-                          const int32_t* n_prefix, hipStream_t s) {
+                          const int32_t* n_prefix, hipStream_t s, int advanced,
+                          int32_t* u_index) {
   const size_t total = (size_t)L * B * H * hd;
   int blocks = (int)((total + 255) / 256);
   if (blocks > 8192) blocks = 8192;
   hipLaunchKernelGGL(compact_kernel, dim3(blocks), dim3(256), 0, s, kc, vc, L, B, H, hd, cap,
-                     path, path_stride, accept_len, n_prefix);
+                     path, path_stride, accept_len, n_prefix, advanced, u_index);
   return hipGetLastError();
 }
 
