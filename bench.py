@@ -124,6 +124,53 @@ def pmc_summary(dirs, gate_up_name="gemm_kernel<4, 4, 2, 2>"):
     return out
 
 
+MFMA_FILE = os.path.join(ROOT, "profiles", "gemm_mfma_llama7b_T64.md")
+GEMM_KINDS = (("QKV", "gemm_kernel<4, 4, 2, 3>"), ("O / down", "gemm_kernel<4, 4, 1, 1>"),
+              ("gate/up", "gemm_kernel<4, 4, 2, 2>"), ("LM head", "gemm_kernel<4, 8, 1, 0>"))
+
+
+def mfma_summary(dirs):
+    """Summarise a rocprofv3 --pmc MfmaUtil,MfmaFlopsBF16 pass per GEMM kind:
+    mean MFMA busy share of all SIMDs while the GPU was busy with the
+    dispatch, and bf16 MFMA flops per dispatch."""
+    import csv
+    import glob
+    import statistics
+    per = {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                for label, name in GEMM_KINDS:
+                    if name in r["Kernel_Name"]:
+                        per.setdefault((label, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    out = {}
+    for label, _ in GEMM_KINDS:
+        u, fl = per.get((label, "MfmaUtil")), per.get((label, "MfmaFlopsBF16"))
+        if u and fl:
+            out[label] = {"util_pct": statistics.mean(u), "flops": statistics.mean(fl),
+                          "dispatches": len(u)}
+    return out
+
+
+def recorded_mfma():
+    """Gate/up MFMA utilisation from the committed counter summary, or None
+    when it is missing or was taken on a different GEMM source."""
+    try:
+        txt = open(MFMA_FILE).read()
+    except OSError:
+        return None
+    vals = {k.strip(): v.strip() for k, v in
+            (l.split("=", 1) for l in txt.splitlines() if l.startswith(("gate_up_", "source_")))}
+    if vals.get("source_sha256") != gemm_source_hash():
+        return None
+    try:
+        return {"kernel": "gemm_kernel<4,4,2,EPI_SWIGLU>",
+                "util_pct": float(vals["gate_up_mfma_util_pct"]),
+                "flops_per_launch": float(vals["gate_up_mfma_flops_per_launch"])}
+    except (KeyError, ValueError):
+        return None
+
+
 def gate_up_bytes(D, M):
     """Algorithmic bytes of one gate/up GEMM launch (one layer): gate and up
     weights, the normalised activations in, the SwiGLU output out."""
@@ -201,6 +248,8 @@ def main() -> int:
                     help="run a copy kernel of known size first (for --pmc counter scaling)")
     ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
                     help="summarise rocprofv3 --pmc FETCH_SIZE/WRITE_SIZE output dirs and exit")
+    ap.add_argument("--mfma-summary", nargs="+", metavar="DIR",
+                    help="summarise rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 output dirs and exit")
     args = ap.parse_args()
     if args.pmc_summary:
         from workloads import configs
@@ -217,6 +266,25 @@ def main() -> int:
             print(f"traffic_bytes_per_launch = {int(round(tot))}")
             print(f"traffic_over_algorithmic = {tot / algo:.4f}")
             print(f"source_sha256 = {gemm_source_hash()}")
+        return 0
+    if args.mfma_summary:
+        from workloads import configs
+        D = configs.HEADLINE.dims
+        M = configs.HEADLINE.batch * 64
+        algo = {"QKV": 2 * M * D.d * 3 * D.d, "O / down": None,
+                "gate/up": 2 * M * D.d * 2 * D.F, "LM head": 2 * M * D.d * D.V}
+        od = (2 * M * D.d * D.d / 1e9, 2 * M * D.F * D.d / 1e9)
+        for label, v in mfma_summary(args.mfma_summary).items():
+            a = algo[label]
+            print(f"{label}: MFMA busy {v['util_pct']:.2f}% of SIMD cycles, "
+                  f"{v['flops'] / 1e9:.3f} GFLOP/dispatch"
+                  + (f" (algorithmic {a / 1e9:.3f})" if a else
+                     f" (algorithmic: O {od[0]:.3f}, down {od[1]:.3f}; mean {sum(od) / 2:.3f})")
+                  + f" over {v['dispatches']} dispatches")
+            if label == "gate/up":
+                print(f"gate_up_mfma_util_pct = {v['util_pct']:.3f}")
+                print(f"gate_up_mfma_flops_per_launch = {v['flops']:.0f}")
+        print(f"source_sha256 = {gemm_source_hash()}")
         return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the tree-verify "
@@ -262,15 +330,18 @@ def main() -> int:
         sess.step(graph=True)
     torch.cuda.synchronize()
     n_start = sess.n_prefix.cpu().numpy().astype(np.int64)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # events on the library's stream (the default stream) around every step
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     torch.cuda.synchronize()
-    ev0.record()
+    evs[0].record()
     t0 = time.perf_counter()
-    for _ in range(K):
+    for i in range(K):
         sess.step(graph=True)
-    ev1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    ev0, ev1 = evs[0], evs[K]
+    step_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(K))
     n_end = sess.n_prefix.cpu().numpy().astype(np.int64)
     wall = t1 - t0
     gpu_ms = ev0.elapsed_time(ev1)
@@ -306,7 +377,15 @@ def main() -> int:
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
                 "kernel": "gemm_kernel<4,4,2,EPI_SWIGLU> (gate/up + SwiGLU, one layer)",
-                "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_us, 2)}
+                "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_us, 2),
+                "mfma": recorded_mfma()}
+
+    # achievable streaming-read bandwidth of this device (plain read kernel)
+    probe = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    read_gbs = (1 << 30) / (tv.read_probe(probe, sink, reps=10) * 1e-6) / 1e9
+    del probe
+    log(f"[bench] plain streaming read: {read_gbs:.0f} GB/s")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -336,7 +415,11 @@ def main() -> int:
         "hbm_bytes_per_step": int(bstep),
         "hbm_gbs_end_to_end": round(hbm_gbs, 1),
         "hbm_frac_end_to_end": round(hbm_gbs / HBM_PEAK_GBS, 4),
+        "read_ceiling_gbs": round(read_gbs, 1),
+        "hbm_frac_of_read_ceiling": round(hbm_gbs / read_gbs, 4),
         "graph_event_ms_per_step": round(gpu_ms / K, 4),
+        "step_ms_median": round(step_ms[K // 2], 4),
+        "step_ms_mean": round(sum(step_ms) / K, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in kernels.items()},

@@ -350,6 +350,18 @@ MV_API int mv_step_profile(mv_ctx* ctx, float* ms, int32_t* count, void* stream)
  * step writes first, so the decode state is unchanged. */
 MV_API int mv_time_kernel(mv_ctx* ctx, int32_t kind, int32_t reps, float* us, void* stream);
 
+/* Measurement helper, not part of the method: the achievable streaming-read
+ * bandwidth of the device, against which the step's HBM share can be read
+ * beside the 8 TB/s peak.  Reads the device buffer buf (bytes >= 16 MiB;
+ * 4096 workgroups each sum a contiguous slice with sixteen 16-byte loads in
+ * flight per lane) reps times back to back and stores the average
+ * microseconds per pass in *us (host).  sink: device float, written only in
+ * the (never taken) case that a sum equals a sentinel.  Synchronises the
+ * stream.  Errors: MV_EINVAL for NULL pointers, reps < 1 or small buffers;
+ * MV_EHIP for launch or event failures. */
+MV_API int mv_read_probe(const void* buf, size_t bytes, int32_t reps, float* sink, float* us,
+                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,4 +9,4 @@ from . import _lib  # noqa: F401
 from ._lib import (ACCEPT_GREEDY, ACCEPT_TYPICAL, PACK_PLAIN, PACK_QKV, ROOT_ARGMAX,  # noqa: F401
                    ROOT_SAMPLE, AcceptParams, Ctx, Dims, KV, LayerWeights, MVError, StepDesc,
                    Tree, accept, decoder_layer, embed, kv_compact, lib, lm_head, medusa_heads,
-                   pack_weight, tree_attention, tree_compile, workspace_size)
+                   pack_weight, read_probe, tree_attention, tree_compile, workspace_size)

@@ -26,7 +26,7 @@ PACK_PLAIN, PACK_QKV = 0, 1
 EXPORTS = ("mv_strerror", "mv_last_error", "mv_tree_compile", "mv_pack_weight",
            "mv_workspace_size", "mv_medusa_heads", "mv_tree_attention", "mv_decoder_layer",
            "mv_embed", "mv_lm_head", "mv_accept", "mv_kv_compact", "mv_ctx_create",
-           "mv_ctx_destroy", "mv_prefill", "mv_step", "mv_step_profile", "mv_time_kernel")
+           "mv_ctx_destroy", "mv_prefill", "mv_step", "mv_step_profile", "mv_time_kernel", "mv_read_probe")
 
 # launch-group kinds of mv_step_profile
 KINDS = ("heads", "embed_rope", "norm", "gemm_qkv", "attention", "gemm_o", "gemm_gate_up",
@@ -115,6 +115,7 @@ def lib() -> C.CDLL:
         "mv_step": (C.c_int, [vp, i32, vp]),
         "mv_step_profile": (C.c_int, [vp, vp, vp, vp]),
         "mv_time_kernel": (C.c_int, [vp, C.c_int32, C.c_int32, vp, vp]),
+        "mv_read_probe": (C.c_int, [vp, C.c_size_t, C.c_int32, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -177,6 +178,16 @@ def pack_weight(src, dst, layout: int = PACK_PLAIN, hd: int = 0, stream=None) ->
     rows, cols = src.shape
     check(lib().mv_pack_weight(ptr(src), ptr(dst), rows, cols, layout, hd, stream_ptr(stream)),
           "pack_weight")
+
+
+def read_probe(buf, sink, reps: int = 10, stream=None) -> float:
+    """Average microseconds of one streaming read of the device tensor `buf`
+    (measurement helper; `sink`: a device float32 scalar)."""
+    import numpy as np
+    us = np.zeros(1, np.float32)
+    check(lib().mv_read_probe(ptr(buf), buf.numel() * buf.element_size(), reps, ptr(sink), ptr(us),
+                              stream_ptr(stream)), "read_probe")
+    return float(us[0])
 
 
 def workspace_size(dims: Dims, B: int, T: int, cap: int) -> int:

@@ -379,6 +379,12 @@ static int enq_accept(int B, int T, int V, int d, const float* logits, const mv_
 
 }  // namespace mv
 
+namespace mvk {
+// Streaming read of buf (rows.hip: 4096 workgroups, each its own contiguous
+// slice; the bytes of the last partial 64 KiB of a slice are skipped).
+hipError_t launch_read_probe(const void* buf, size_t bytes, float* sink, hipStream_t s);
+}  // namespace mvk
+
 using namespace mv;
 
 // ---------------------------------------------------------------------------
@@ -846,6 +852,32 @@ MV_API int mv_step_profile(mv_ctx* c, float* ms, int32_t* count, void* stream) {
     ms[p.kind[i]] += t;
     count[p.kind[i]] += 1;
   }
+  return MV_OK;
+}
+
+MV_API int mv_read_probe(const void* buf, size_t bytes, int32_t reps, float* sink, float* us,
+                         void* stream) {
+  if (!buf || !sink || !us) return fail(MV_EINVAL, "mv_read_probe: NULL pointer");
+  if (reps < 1 || bytes < ((size_t)16 << 20))
+    return fail(MV_EINVAL, "mv_read_probe: reps %d < 1 or bytes %zu < 16 MiB", reps, bytes);
+  const hipStream_t s = (hipStream_t)stream;
+  hipEvent_t e0, e1;
+  MV_HIP(hipEventCreate(&e0));
+  if (hipEventCreate(&e1) != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return fail(MV_EHIP, "mv_read_probe: event create");
+  }
+  hipError_t e = mvk::launch_read_probe(buf, bytes, sink, s);   // warm-up
+  if (e == hipSuccess) e = hipEventRecord(e0, s);
+  for (int r = 0; r < reps && e == hipSuccess; ++r) e = mvk::launch_read_probe(buf, bytes, sink, s);
+  if (e == hipSuccess) e = hipEventRecord(e1, s);
+  if (e == hipSuccess) e = hipEventSynchronize(e1);
+  float ms = 0.f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (e != hipSuccess) return fail(MV_EHIP, "mv_read_probe: %s", hipGetErrorString(e));
+  *us = 1000.f * ms / (float)reps;
   return MV_OK;
 }
 

@@ -242,6 +242,31 @@ __global__ void compact_kernel(u16* __restrict__ kc, u16* __restrict__ vc, int L
   }
 }
 
+// Streaming-read probe (measurement only): workgroup i sums the i-th slice
+// of buf with 16 16-byte loads in flight per lane; the sum is written only if
+// it equals a sentinel, so the reads cannot be dropped.
+__global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ p, size_t n16,
+                                                         float* __restrict__ out) {
+  constexpr int U = 16;
+  const size_t per = n16 / gridDim.x;
+  const uint4* q = p + per * blockIdx.x;
+  float s = 0.f;
+  for (size_t i = threadIdx.x; i + (U - 1) * 256 < per; i += U * 256) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = q[i + u * 256];
+#pragma unroll
+    for (int u = 0; u < U; ++u) s += __uint_as_float(v[u].x ^ v[u].y ^ v[u].z ^ v[u].w);
+  }
+  if (s == 1.2345f) out[0] = s;
+}
+
+hipError_t launch_read_probe(const void* buf, size_t bytes, float* sink, hipStream_t s) {
+  hipLaunchKernelGGL(read_probe_kernel, dim3(4096), dim3(256), 0, s,
+                     static_cast<const uint4*>(buf), bytes / 16, sink);
+  return hipGetLastError();
+}
+
 hipError_t launch_compact(u16* kc, u16* vc, int L, int B, int H, int hd, int cap,
                           const int32_t* path, int path_stride, const int32_t* accept_len,
                           const int32_t* n_prefix, hipStream_t s, int advanced,
