@@ -81,6 +81,7 @@ typedef enum {
 #define MV_MAX_DEPTH 16     /* tree depth (<= number of Medusa heads used) */
 #define MV_MAX_TOPK 16      /* candidates per head */
 #define MV_MAX_BATCH 4      /* sequences per call (Medusa head GEMV) */
+#define MV_HEADS_LDS_MAX (128 * 1024)  /* head GEMV: B * d * 4 bytes of input rows in LDS */
 
 #define MV_ACCEPT_GREEDY 0
 #define MV_ACCEPT_TYPICAL 1

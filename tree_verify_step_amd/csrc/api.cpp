@@ -469,7 +469,7 @@ MV_API int mv_medusa_heads(const mv_dims* dims, int32_t B, int32_t D, int32_t s,
     if (tree->depth > D) return fail(MV_ETREE, "tree depth %d > heads used %d", tree->depth, D);
     if (!root_tok || !tree_tok) return fail(MV_EINVAL, "root_tok and tree_tok needed with a tree");
   }
-  if ((size_t)B * dims->d * 4 > 64 * 1024) return fail(MV_EUNSUPPORTED, "B*d too large for the head GEMV");
+  if ((size_t)B * dims->d * 4 > MV_HEADS_LDS_MAX) return fail(MV_EUNSUPPORTED, "B*d too large for the head GEMV");
   if ((rc = check_ws(dims, B, tree ? tree->T : 1, ws_bytes, ws))) return rc;
   const Ws L = ws_layout(*dims, B, tree ? tree->T : 1);
   float* z = head_logits ? head_logits : at<float>(ws, L.hz);
@@ -700,7 +700,7 @@ MV_API int mv_ctx_create(mv_ctx** out, const mv_step_desc* desc) {
     return fail(MV_EINVAL, "temperature must be > 0");
   if (p.root_mode == MV_ROOT_SAMPLE && (!d.u_draws || !d.u_index || d.n_draws < 1))
     return fail(MV_EINVAL, "sampled roots need u_draws, u_index and n_draws");
-  if ((size_t)d.B * d.dims.d * 4 > 64 * 1024) return fail(MV_EUNSUPPORTED, "B*d too large");
+  if ((size_t)d.B * d.dims.d * 4 > MV_HEADS_LDS_MAX) return fail(MV_EUNSUPPORTED, "B*d too large");
   if ((rc = check_ws(&d.dims, d.B, d.T, d.ws_bytes, d.ws))) return rc;
 
   mv_ctx* c = new mv_ctx();

@@ -98,7 +98,18 @@ static hipError_t launch_gemv(const u16* hb, const float* uf, const u16* W, floa
   int rpw = GEMV_ROWS_PER_WG;
   while (rpw > 4 * GEMV_RW && (size_t)((rows + rpw - 1) / rpw) * D < 1024) rpw /= 2;
   dim3 grid((rows + rpw - 1) / rpw, D);
+  // the fp32 input rows live in LDS: up to 4 x 8192 x 4 B = 128 KiB (gfx950
+  // has 160 KiB per workgroup; above 64 KiB the launch must opt in)
   const size_t lds = (size_t)B * d * sizeof(float);
+  if (lds > MV_HEADS_LDS_MAX) return hipErrorInvalidValue;
+  if (lds > 65536) {
+    const hipError_t e = B == 1
+        ? hipFuncSetAttribute(reinterpret_cast<const void*>(&heads_gemv_kernel<1>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)MV_HEADS_LDS_MAX)
+        : hipFuncSetAttribute(reinterpret_cast<const void*>(&heads_gemv_kernel<4>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)MV_HEADS_LDS_MAX);
+    if (e != hipSuccess) return e;
+  }
   if (B == 1)
     hipLaunchKernelGGL((heads_gemv_kernel<1>), grid, dim3(256), lds, s, hb, uf, W, out, B, D, d, rows, mode, rpw);
   else if (B <= 4)
