@@ -59,17 +59,10 @@ __host__ __device__ __forceinline__ int qkv_feature(int p, int d, int hd) {
 #define MV_BUF_DWORD3 0x00020000    /* raw (untyped) buffer resource */
 #define MV_BUF_NONE 0x7ffffff0      /* an offset past any partial buffer */
 
-// Sum over the 16 lanes of a DPP row (every lane gets the row's total): quad
-// swaps (xor 1, xor 2), then half-row and row mirrors.  VALU lane moves, no
-// LDS round trips.
+// A float moved between lanes of a 16-lane DPP row (VALU lane moves, no LDS
+// round trips): quad_perm 0xB1 and 0x4E swap lanes xor 1 and xor 2,
+// row_half_mirror (0x141) and row_mirror (0x140) reverse 8 and 16 lanes.
 #define MV_DPP(v, ctrl) __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xF, 0xF, false))
-__device__ __forceinline__ float row16_sum(float v) {
-  v += MV_DPP(v, 0xB1);     // quad_perm [1,0,3,2]
-  v += MV_DPP(v, 0x4E);     // quad_perm [2,3,0,1]
-  v += MV_DPP(v, 0x141);    // row_half_mirror
-  v += MV_DPP(v, 0x140);    // row_mirror
-  return v;
-}
 
 // One step of a (value, column) maximum over a DPP row: larger value, then
 // lower column.
@@ -101,7 +94,6 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
   constexpr int TR = MB * 16;                  // rows of a tile
   __shared__ bf16x8 As[2][APC][64];            // [buf][kl * MB + rb][lane]
   __shared__ float rs_s[TR];
-  __shared__ float ssw[W][TR];
   __shared__ int s_last;
   __shared__ int s_slot0[MV_MAX_BATCH];        // QKV: cache slot of each sequence's node 0
 
@@ -228,7 +220,13 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
   // waves read clamped, valid addresses; the values are then unused)
   const int col = lane & 15;
   const int row0 = mt * TR + 4 * (lane >> 4);
-  float xo[MB][NBW][4], gn[NBW];              // ADD: residual x, next norm's gain
+  // ADD: the thread's 16-byte pieces of the tile (8 columns of one row):
+  // residual x and the next norm's gains
+  constexpr int ATC = W * NBW * 16;           // columns of an ADD tile
+  constexpr int APR = ATC / 8;                // pieces per row (8 or 16)
+  constexpr int ANP = (TR * APR + W * 64 - 1) / (W * 64);
+  f32x4 xr[ANP][2];
+  uint4 gr[ANP];
   float2 cs[MB][4];                           // QKV: RoPE (cos, sin) per row
   // QKV: the lane's two blocks are packed rows p0 (block 0) and p0 + 16
   // (block 1); with heads wider than 16 they hold dims i and i + hd/2 of one
@@ -241,16 +239,14 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
   const int half = g.qkv.hd >> 1;
   if constexpr (EPI == EPI_ADD) {
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) {
-      const int n = (cb + nb) * 16 + col;
-      gn[nb] = g.next_gain ? bf16_to_f32(g.next_gain[n]) : 0.f;
-#pragma unroll
-      for (int rb = 0; rb < MB; ++rb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = min(row0 + rb * 16 + r, g.M - 1);
-          xo[rb][nb][r] = g.out_f32[(size_t)m * g.N + n];
-        }
+    for (int i = 0; i < ANP; ++i) {
+      const int p = i * W * 64 + threadIdx.x;
+      const int m = min(mt * TR + p / APR, g.M - 1);
+      const int c = min(nt * ATC + 8 * (p % APR), g.N - 8);
+      const f32x4* xp = reinterpret_cast<const f32x4*>(g.out_f32 + (size_t)m * g.N + c);
+      xr[i][0] = xp[0];
+      xr[i][1] = xp[1];
+      gr[i] = g.next_gain ? *reinterpret_cast<const uint4*>(g.next_gain + c) : uint4{0, 0, 0, 0};
     }
   }
   if constexpr (EPI == EPI_QKV) {
@@ -372,47 +368,63 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
                                __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-  } else if (EPI == EPI_ADD) {
+  } else if constexpr (EPI == EPI_ADD) {
+    // x += y, staged through LDS as fp32 so that every thread then owns
+    // whole 16-byte pieces (8 columns of one row): x and the next norm's
+    // operand are written as 16-byte stores, and a row's sum of squares over
+    // the tile is a reduction over the APR adjacent lanes holding its pieces
+    constexpr int LDF = ATC + 4;                 // padded staging row (floats)
+    float* stg;
+    if constexpr (TR * LDF * 4 <= (int)sizeof(As)) {
+      stg = reinterpret_cast<float*>(&As[0][0][0]);
+    } else {                                     // 256-row tiles: a buffer of its own
+      __shared__ float stg_add[TR * LDF];
+      stg = stg_add;
+    }
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          stg[(rb * 16 + 4 * (lane >> 4) + r) * LDF + (wave * NBW + nb) * 16 + col] = acc[rb][nb][r];
+    __syncthreads();
     const bool nxt = g.next_gain != nullptr && g.xn_out != nullptr;
     const bool ssq = g.next_gain != nullptr && g.ss_out != nullptr;
-    float sq[MB][4];
 #pragma unroll
-    for (int rb = 0; rb < MB; ++rb)
+    for (int i = 0; i < ANP; ++i) {
+      const int p = i * W * 64 + threadIdx.x;
+      const int rl = p / APR, m = mt * TR + rl;
+      const int c = nt * ATC + 8 * (p % APR);
+      const bool st = p < TR * APR && m < g.M && c < g.N;
+      const f32x4* sp = reinterpret_cast<const f32x4*>(stg + (p < TR * APR ? rl : 0) * LDF + 8 * (p % APR));
+      const f32x4 x0 = xr[i][0] + sp[0], x1 = xr[i][1] + sp[1];
+      float sq = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sq[rb][r] = 0.f;
+      for (int e = 0; e < 4; ++e) sq += x0[e] * x0[e] + x1[e] * x1[e];
+      if (st) {
+        f32x4* xp = reinterpret_cast<f32x4*>(g.out_f32 + (size_t)m * g.N + c);
+        xp[0] = x0;
+        xp[1] = x1;
+        if (nxt) {
+          const uint32_t gw[4] = {gr[i].x, gr[i].y, gr[i].z, gr[i].w};
+          uint32_t o[4];
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) {
-      const int n = (cb + nb) * 16 + col;
-#pragma unroll
-      for (int rb = 0; rb < MB; ++rb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = row0 + rb * 16 + r;
-          const float xv = xo[rb][nb][r] + acc[rb][nb][r];
-          const bool st = active && m < g.M;
-          sq[rb][r] += st ? xv * xv : 0.f;
-          if (st) {
-            g.out_f32[(size_t)m * g.N + n] = xv;
-            if (nxt) g.xn_out[packed_index(m, n, g.N)] = f32_to_bf16(xv * gn[nb]);
+          for (int e = 0; e < 4; ++e) {
+            const float a = (e < 2 ? x0 : x1)[(2 * e) & 3], b = (e < 2 ? x0 : x1)[(2 * e + 1) & 3];
+            o[e] = (uint32_t)f32_to_bf16(a * bf16_to_f32((u16)(gw[e] & 0xffff))) |
+                   ((uint32_t)f32_to_bf16(b * bf16_to_f32((u16)(gw[e] >> 16))) << 16);
           }
+          *reinterpret_cast<uint4*>(g.xn_out + packed_index(m, c, g.N)) = uint4{o[0], o[1], o[2], o[3]};
         }
-    }
-    if (ssq) {
-      // rows' sums of squares: over this lane group's 16 columns, then the waves
-#pragma unroll
-      for (int rb = 0; rb < MB; ++rb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float v = row16_sum(sq[rb][r]);
-          if (col == 0) ssw[wave][rb * 16 + 4 * (lane >> 4) + r] = v;
-        }
-      __syncthreads();
-      for (int r = threadIdx.x; r < TR; r += W * 64) {
-        const int m = mt * TR + r;
-        float s = 0.f;
-#pragma unroll
-        for (int w = 0; w < W; ++w) s += ssw[w][r];
-        if (m < g.M) g.ss_out[(size_t)m * g.ss_ld + nt] = s;
+      }
+      if (ssq) {
+        sq = st ? sq : 0.f;
+        sq += MV_DPP(sq, 0xB1);      // quad_perm [1,0,3,2]
+        sq += MV_DPP(sq, 0x4E);      // quad_perm [2,3,0,1]
+        sq += MV_DPP(sq, 0x141);     // row_half_mirror: the 8 lanes of a row's pieces
+        if constexpr (APR == 16) sq += MV_DPP(sq, 0x140);   // row_mirror
+        if (p % APR == 0 && p < TR * APR && m < g.M) g.ss_out[(size_t)m * g.ss_ld + nt] = sq;
       }
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
