@@ -230,9 +230,13 @@ __global__ __launch_bounds__(NW * 64) void tree_attention_kernel(
     *reinterpret_cast<float4*>(&s_o[wave][qi * LDO + i * 16 + g * 4]) =
         float4{o[i][0], o[i][1], o[i][2], o[i][3]};
   __syncthreads();
-  // per query: each wave's weight 2^(m_w - M) / sum_w 2^(m_w - M) l_w
-  if (threadIdx.x < 16) {
-    const int qq = threadIdx.x;
+  // per query: wave w's weight 2^(m_w - M) / sum_w 2^(m_w - M) l_w; each
+  // thread forms 8 consecutive output dims of one query (one 16-byte store)
+  constexpr int PPQ = HD / 8;                   // output pieces per query
+  for (int e = threadIdx.x; e < 16 * PPQ; e += NW * 64) {
+    const int qq = e / PPQ, c8 = (e % PPQ) * 8;
+    const int node = qb * 16 + qq;
+    if (node >= T) continue;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][qq]);
@@ -243,21 +247,24 @@ __global__ __launch_bounds__(NW * 64) void tree_attention_kernel(
       den += f[w] * s_l[w][qq];
     }
     const float inv = 1.f / den;
+    float val[8];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) s_l[w][qq] = f[w] * inv;   // reused as the weight
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < 16 * HD; e += NW * 64) {
-    const int qq = e / HD, dim = e % HD;
-    const int node = qb * 16 + qq;
-    if (node >= T) continue;
-    float val = 0.f;
+    for (int t = 0; t < 8; ++t) val[t] = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) val += s_l[w][qq] * s_o[w][qq * LDO + dim];
-    const int m = b * T + node, c = h * HD + dim;
-    const u16 ob = f32_to_bf16(val);
-    if (packed) out[packed_index(m, c, d)] = ob;
-    else out[(size_t)m * d + c] = ob;
+    for (int w = 0; w < NW; ++w) {
+      const float wt = f[w] * inv;
+      const float4 a = *reinterpret_cast<const float4*>(&s_o[w][qq * LDO + c8]);
+      const float4 c = *reinterpret_cast<const float4*>(&s_o[w][qq * LDO + c8 + 4]);
+      val[0] += wt * a.x; val[1] += wt * a.y; val[2] += wt * a.z; val[3] += wt * a.w;
+      val[4] += wt * c.x; val[5] += wt * c.y; val[6] += wt * c.z; val[7] += wt * c.w;
+    }
+    uint32_t pk[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      pk[t] = (uint32_t)f32_to_bf16(val[2 * t]) | ((uint32_t)f32_to_bf16(val[2 * t + 1]) << 16);
+    const int m = b * T + node, c = h * HD + c8;
+    u16* dst = packed ? out + packed_index(m, c, d) : out + (size_t)m * d + c;
+    *reinterpret_cast<uint4*>(dst) = uint4{pk[0], pk[1], pk[2], pk[3]};
   }
 }
 

@@ -318,7 +318,25 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
       }
   }
   if (EPI == EPI_STORE) {
-    if (active) {
+    if constexpr (NBW == 1 && W * TR * 16 * 4 <= (int)sizeof(As)) {
+      // staged per wave in the operand LDS, then written as 16-byte pieces
+      // (4 columns of one row)
+      float* stg = reinterpret_cast<float*>(&As[0][0][0]) + wave * TR * 16;
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) stg[(rb * 16 + 4 * (lane >> 4) + r) * 16 + col] = acc[rb][0][r];
+      __syncthreads();
+      if (active) {
+#pragma unroll
+        for (int p = lane; p < TR * 4; p += 64) {
+          const int rl = p >> 2, m = mt * TR + rl;
+          if (m < g.M)
+            *reinterpret_cast<f32x4*>(g.out_f32 + (size_t)m * g.N + first_blk * 16 + 4 * (p & 3)) =
+                *reinterpret_cast<const f32x4*>(stg + rl * 16 + 4 * (p & 3));
+        }
+      }
+    } else if (active) {
 #pragma unroll
       for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
@@ -428,18 +446,25 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
       }
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
+    // h = SiLU(gate) * up, staged per wave in the operand LDS as bf16 so that
+    // each lane then writes whole 16-byte pieces (8 features of one row)
+    static_assert(W * TR * 16 * 2 <= (int)sizeof(As), "SwiGLU staging fits the operand LDS");
+    u16* stg = reinterpret_cast<u16*>(&As[0][0][0]) + wave * TR * 16;
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        stg[(rb * 16 + 4 * (lane >> 4) + r) * 16 + col] =
+            f32_to_bf16(silu_f(acc[rb][0][r]) * acc[rb][1][r]);
+    __syncthreads();
     if (active) {
-      const int f = wb * 16 + col;
 #pragma unroll
-      for (int rb = 0; rb < MB; ++rb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = row0 + rb * 16 + r;
-          if (m < g.M) {
-            const float h = silu_f(acc[rb][0][r]) * acc[rb][1][r];
-            g.out_bf16[packed_index(m, f, g.N)] = f32_to_bf16(h);
-          }
-        }
+      for (int p = lane; p < TR * 2; p += 64) {
+        const int rl = p >> 1, m = mt * TR + rl;
+        if (m < g.M)
+          *reinterpret_cast<uint4*>(g.out_bf16 + packed_index(m, wb * 16 + 8 * (p & 1), g.N)) =
+              *reinterpret_cast<const uint4*>(stg + rl * 16 + 8 * (p & 1));
+      }
     }
   } else if constexpr (EPI == EPI_QKV) {
     // RoPE in registers, then the tile (TR rows x W*32 packed features) is

@@ -27,33 +27,39 @@ __global__ __launch_bounds__(256) void heads_gemv_kernel(const u16* __restrict__
   extern __shared__ float xs[];                   // [B][d]
   const int k = blockIdx.y;                       // head index 0..D-1 (head k+1)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const u16* Wk = W + (size_t)k * rows * d;
+  const int r_lo = blockIdx.x * rpw;
+  const int r_hi = min(rows, r_lo + rpw);
+  // GEMV_CH 1 KiB pieces of each of the wave's GEMV_RW rows per block
+  uint4 w[GEMV_CH][GEMV_RW];
+  auto load = [&](int r0, int c0) {
+#pragma unroll
+    for (int j = 0; j < GEMV_CH; ++j) {
+      const int c = min(c0 + j * 512 + lane * 8, d - 8);      // clamped: in bounds
+#pragma unroll
+      for (int i = 0; i < GEMV_RW; ++i) {
+        const int r = min(r0 + i, r_hi - 1);
+        w[j][i] = *reinterpret_cast<const uint4*>(Wk + (size_t)r * d + c);
+      }
+    }
+  };
+  // the wave's first block of weights is requested before the input rows
+  // are staged, and every later block right after the previous one's math,
+  // so that 2 * GEMV_CH loads per lane stay in flight across the reductions
+  int r0 = r_lo + wave * GEMV_RW;
+  if (r0 < r_hi) load(r0, 0);
   for (int i = threadIdx.x; i < B * d; i += 256) {
     const int b = i / d, c = i % d;
     xs[i] = mode == 0 ? bf16_to_f32(hb[(size_t)b * d + c]) : uf[((size_t)b * D + k) * d + c];
   }
   __syncthreads();
-  const u16* Wk = W + (size_t)k * rows * d;
-  const int r_lo = blockIdx.x * rpw;
-  const int r_hi = min(rows, r_lo + rpw);
-  for (int r0 = r_lo + wave * GEMV_RW; r0 < r_hi; r0 += 4 * GEMV_RW) {
+  for (; r0 < r_hi; r0 += 4 * GEMV_RW) {
     float acc[GEMV_RW][MAXB];
 #pragma unroll
     for (int i = 0; i < GEMV_RW; ++i)
 #pragma unroll
       for (int b = 0; b < MAXB; ++b) acc[i][b] = 0.f;
-    // GEMV_CH 1 KiB pieces of each of the wave's rows are loaded before any
-    // math, so 2 * GEMV_CH loads per lane are in flight
     for (int c0 = 0; c0 < d; c0 += 512 * GEMV_CH) {
-      uint4 w[GEMV_CH][GEMV_RW];
-#pragma unroll
-      for (int j = 0; j < GEMV_CH; ++j) {
-        const int c = min(c0 + j * 512 + lane * 8, d - 8);      // clamped: in bounds
-#pragma unroll
-        for (int i = 0; i < GEMV_RW; ++i) {
-          const int r = min(r0 + i, r_hi - 1);
-          w[j][i] = *reinterpret_cast<const uint4*>(Wk + (size_t)r * d + c);
-        }
-      }
 #pragma unroll
       for (int j = 0; j < GEMV_CH; ++j) {
         const int c = c0 + j * 512 + lane * 8;
@@ -74,6 +80,12 @@ __global__ __launch_bounds__(256) void heads_gemv_kernel(const u16* __restrict__
           }
         }
       }
+      int nr = r0, nc = c0 + 512 * GEMV_CH;
+      if (nc >= d) {
+        nr = r0 + 4 * GEMV_RW;
+        nc = 0;
+      }
+      if (nr < r_hi) load(nr, nc);
     }
 #pragma unroll
     for (int i = 0; i < GEMV_RW; ++i) {
