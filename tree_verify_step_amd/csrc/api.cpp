@@ -264,6 +264,10 @@ static int enq_layer(const mv_dims& D, int B, const mv_tree& t, const int32_t* n
   g.qkv.hd = D.hd;
   g.qkv.cap = kv.cap;
   g.qkv.d = D.d;
+  {   // compute units the QKV tiles leave idle read the prefix K/V ahead
+    const GemmCfg c = gemm_cfg(D, G_QKV, round16(M));
+    g.prefetch = std::max(0, (256 - c.ntiles * c.splits * c.mtiles) / (c.splits * c.mtiles));
+  }
   if (want(MV_K_QKV)) {
     prof_begin(s);
     MV_HIP(mvk::launch_gemm(g, s));

@@ -147,6 +147,8 @@ struct GemmArgs {
   float* partial;    // split-K partial tiles
   int* counters;     // split-K arrival counters [tiles], zero between launches
   QkvArgs qkv;
+  int prefetch;      // QKV: extra grid columns of workgroups that read this
+                     //   layer's cached prefix K/V ahead of the attention launch
 };
 
 int gemm_mb(int Mp);                                  // 16-row blocks per tile

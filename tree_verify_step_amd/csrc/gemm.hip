@@ -85,6 +85,35 @@ struct GemmShape {
 
 int gemm_kc(int MB) { return MB <= 4 ? 8 : (MB == 8 ? 4 : 2); }
 
+// Reads the cached prefix K and V of one layer (slots 0 .. n-1 of every
+// (sequence, head) block: the first ceil(n/32) K groups and ceil(n/8) V runs,
+// contiguous at the start of the block) and discards the values.  Workgroups
+// appended to the QKV launch, on compute units its tiles leave idle, do this
+// so that the attention launch that follows finds the prefix in the
+// memory-side cache instead of waiting on HBM.
+__device__ __forceinline__ void prefetch_prefix_kv(const QkvArgs& q, int p, int P) {
+  uint32_t sink = 0;
+  const int ranges = 2 * q.B * q.H;
+  for (int r = p; r < ranges; r += P) {
+    const int pair = r >> 1, b = pair / q.H;
+    const int n = min(max(q.n_prefix[b], 0), q.cap - q.T);
+    const int slots = (r & 1) ? ((n + 7) & ~7) : ((n + 31) & ~31);
+    const uint4* src = reinterpret_cast<const uint4*>(((r & 1) ? q.vcache : q.kcache) +
+                                                      (size_t)pair * q.cap * q.hd);
+    const int n16 = slots * q.hd / 8;                 // 16-byte pieces
+    int i = threadIdx.x;
+    for (; i + 7 * (int)blockDim.x < n16; i += 8 * blockDim.x) {
+      uint4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = src[i + u * blockDim.x];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sink ^= v[u].x ^ v[u].w;
+    }
+    for (; i < n16; i += blockDim.x) sink ^= src[i].x;
+  }
+  asm volatile("" ::"v"(sink));
+}
+
 template <int MB, int W, int NBW, int EPI>
 __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
   constexpr int KC = GemmShape<MB>::KC;
@@ -97,6 +126,15 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
   __shared__ int s_last;
   __shared__ int s_slot0[MV_MAX_BATCH];        // QKV: cache slot of each sequence's node 0
 
+  constexpr int PER_TILE = EPI == EPI_SWIGLU ? W : W * NBW;   // 16-column blocks per tile
+  const int NT = (g.N / 16 + PER_TILE - 1) / PER_TILE;          // column tiles
+  if constexpr (EPI == EPI_QKV) {
+    if ((int)blockIdx.x >= NT) {               // appended prefetch workgroups
+      prefetch_prefix_kv(g.qkv, ((int)blockIdx.x - NT) * gridDim.y + blockIdx.y,
+                         ((int)gridDim.x - NT) * gridDim.y);
+      return;
+    }
+  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nt = blockIdx.x, split = blockIdx.y, mt = blockIdx.z;
   const int KB = g.K >> 5;
@@ -264,7 +302,7 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
   if (g.splits > 1) {
     constexpr int WQ = MB * NBW;               // f32x4 items per lane of one wave
     constexpr int SB = WQ >= 16 ? 1 : 16 / WQ; // splits loaded per batch
-    const int tile = mt * gridDim.x + nt;
+    const int tile = mt * NT + nt;
     const int per_split = W * WQ * 256 * 4;    // bytes of one split's tile
     const __amdgpu_buffer_rsrc_t part = __builtin_amdgcn_make_buffer_rsrc(
         g.partial + (size_t)tile * g.splits * (per_split / 4), (short)0, g.splits * per_split,
@@ -637,7 +675,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   const int MB = gemm_mb(g.Mp);
   const int mtiles = (g.Mp / 16 + MB - 1) / MB;
   const int ntiles = gemm_ntiles(g.epi, g.N, g.w, g.nbw);
-  const dim3 grid(ntiles, g.splits, mtiles);
+  const dim3 grid(ntiles + (g.epi == EPI_QKV ? g.prefetch : 0), g.splits, mtiles);
   if (g.w == 4 && g.nbw == 1) return launch_w<4, 1>(g, MB, grid, s);
   if (g.w == 8 && g.nbw == 1) return launch_w<8, 1>(g, MB, grid, s);
   if (g.w == 4 && g.nbw == 2) return launch_w<4, 2>(g, MB, grid, s);
