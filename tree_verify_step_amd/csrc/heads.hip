@@ -143,138 +143,186 @@ hipError_t launch_heads_w2(const float* u, const u16* w2, float* z, int B, int D
 
 // ---------------------------------------------------------------------------
 // Top-s of rows of V logits: larger value first, lower id first on ties.
+// A (value, id) pair is ranked by one 64-bit key: an order-preserving map of
+// the float (with -0 read as +0) in the high word and ~id in the low word, so
+// that one unsigned comparison gives the order; NaNs get the key of an empty
+// slot (-inf, id INT_MAX) and are never chosen over a number.
+// Selection inside one wave: each lane sorts its (up to) 16 keys descending
+// with a bitonic network and parks them in LDS; then s rounds each take the
+// wave-wide maximum of the lanes' current heads (DPP inside 16-lane rows, row
+// broadcasts across rows, lane 63 read into a scalar) and the winning lane
+// moves to its next key.
 // Stage 1: each wave takes 1024 consecutive logits (16 per lane, coalesced
-// float4 loads) and selects its top s by s rounds of a wave-wide argmax over
-// the lanes' best remaining values (shuffles only, no barriers); it writes
-// s (value, id) candidates.  Stage 2: one wave per row selects the final s
-// from the row's candidates the same way.
+// float4 loads) and writes its top s.  Stage 2: one wave per row selects the
+// final s from the row's candidates the same way.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bool better_vi(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
-}
+typedef unsigned long long u64;
+constexpr u64 TOPK_EMPTY = ((u64)0x007fffffu << 32) | 0x80000000u;   // (-inf, INT_MAX)
 
-// Best (value, id) of the wave in every lane: DPP lane moves inside each
-// 16-lane row (quad swaps, half-row and row mirrors), then two cross-row
-// shuffles.
-template <int CTRL>
-__device__ __forceinline__ void dpp_best(float& wv, int& wi) {
-  const float ov = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(wv), CTRL, 0xF, 0xF, false));
-  const int oi = __builtin_amdgcn_mov_dpp(wi, CTRL, 0xF, 0xF, false);
-  if (better_vi(ov, oi, wv, wi)) {
-    wv = ov;
-    wi = oi;
+__device__ __forceinline__ u64 topk_key(float v, int id) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;                          // -0 ranks as +0
+  const uint32_t o = (u >> 31) ? ~u : (u | 0x80000000u);
+  return v != v ? TOPK_EMPTY : (((u64)o << 32) | (uint32_t)~id);
+}
+__device__ __forceinline__ float topk_value(u64 k) {
+  const uint32_t o = (uint32_t)(k >> 32);
+  return __uint_as_float((o >> 31) ? (o & 0x7fffffffu) : ~o);
+}
+__device__ __forceinline__ int topk_id(u64 k) { return (int)~(uint32_t)k; }
+
+template <int CTRL, bool BCAST>
+__device__ __forceinline__ void key_max_step(uint32_t& hi, uint32_t& lo) {
+  uint32_t ohi, olo;
+  if constexpr (BCAST) {      // lanes without a source lane keep their own key
+    ohi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, 0xF, 0xF, false);
+    olo = __builtin_amdgcn_update_dpp(lo, lo, CTRL, 0xF, 0xF, false);
+  } else {
+    ohi = __builtin_amdgcn_mov_dpp(hi, CTRL, 0xF, 0xF, false);
+    olo = __builtin_amdgcn_mov_dpp(lo, CTRL, 0xF, 0xF, false);
+  }
+  if ((((u64)ohi << 32) | olo) > (((u64)hi << 32) | lo)) {
+    hi = ohi;
+    lo = olo;
   }
 }
-__device__ __forceinline__ void wave_best(float& wv, int& wi) {
-  dpp_best<0xB1>(wv, wi);     // quad_perm [1,0,3,2]
-  dpp_best<0x4E>(wv, wi);     // quad_perm [2,3,0,1]
-  dpp_best<0x141>(wv, wi);    // row_half_mirror
-  dpp_best<0x140>(wv, wi);    // row_mirror
-#pragma unroll
-  for (int o = 16; o <= 32; o <<= 1) {
-    const float ov = __shfl_xor(wv, o, 64);
-    const int oi = __shfl_xor(wi, o, 64);
-    if (better_vi(ov, oi, wv, wi)) {
-      wv = ov;
-      wi = oi;
-    }
-  }
+// The wave's largest key, in every lane.
+__device__ __forceinline__ u64 wave_max_key(u64 k) {
+  uint32_t hi = (uint32_t)(k >> 32), lo = (uint32_t)k;
+  key_max_step<0xB1, false>(hi, lo);     // quad_perm [1,0,3,2]
+  key_max_step<0x4E, false>(hi, lo);     // quad_perm [2,3,0,1]
+  key_max_step<0x141, false>(hi, lo);    // row_half_mirror
+  key_max_step<0x140, false>(hi, lo);    // row_mirror: every lane holds its row's maximum
+  key_max_step<0x142, true>(hi, lo);     // row_bcast:15: row r-1 folded into row r
+  key_max_step<0x143, true>(hi, lo);     // row_bcast:31: rows 0-1 folded into rows 2-3
+  return ((u64)__builtin_amdgcn_readlane(hi, 63) << 32) | (uint32_t)__builtin_amdgcn_readlane(lo, 63);
 }
 
-// v/id: this lane's N (<= 32) candidates (id INT_MAX = empty).  Writes the
-// wave's top s into outv/outi (lane r writes round r's winner).
-template <int N>
-__device__ __forceinline__ void wave_select(const float (&v)[N], const int (&id)[N], int s,
-                                            float* outv, int* outi) {
-  static_assert(N <= 32, "the taken mask holds 32 candidates");
+// key: this lane's N keys (TOPK_EMPTY = no candidate), already in descending
+// order when SORTED; lst: the wave's LDS area [N][64].  Returns round r's
+// winner in lane r (r < s <= 64).
+template <int N, bool SORTED>
+__device__ __forceinline__ u64 wave_top_keys(u64 (&key)[N], int s, u64 (*lst)[64]) {
   const int lane = threadIdx.x & 63;
-  unsigned taken = 0;
-  for (int r = 0; r < s; ++r) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff, bj = -1;
+  if constexpr (!SORTED) {
 #pragma unroll
-    for (int j = 0; j < N; ++j) {
-      if (!((taken >> j) & 1u) && better_vi(v[j], id[j], bv, bi)) {
-        bv = v[j];
-        bi = id[j];
-        bj = j;
-      }
-    }
-    float wv = bv;
-    int wi = bi;
-    wave_best(wv, wi);
-    if (bj >= 0 && bi == wi) taken |= 1u << bj;     // ids are unique: one owner
-    if (lane == r) {
-      outv[0] = wv;
-      outi[0] = wi;
-    }
+    for (int k = 2; k <= N; k <<= 1)         // bitonic sort, descending
+#pragma unroll
+      for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          const int l = i ^ j;
+          if (l > i) {
+            const bool desc = (i & k) == 0;
+            const u64 x = key[i], y = key[l];
+            const bool sw = desc ? x < y : x > y;
+            key[i] = sw ? y : x;
+            key[l] = sw ? x : y;
+          }
+        }
   }
+#pragma unroll
+  for (int j = 0; j < N; ++j) lst[j][lane] = key[j];
+  u64 head = key[0], nxt = key[1], mine = TOPK_EMPTY;
+  int ptr = 1;                               // index of nxt
+  for (int r = 0; r < s; ++r) {
+    const u64 best = wave_max_key(head);
+    if (head == best) {                      // keys are unique: one lane
+      head = nxt;
+      ++ptr;
+      nxt = ptr < N ? lst[ptr][lane] : TOPK_EMPTY;
+    }
+    if (lane == r) mine = best;
+  }
+  return mine;
 }
 
+// Stage 1: wave w of a row takes logits [w * 64 * KPL, (w + 1) * 64 * KPL),
+// KPL per lane in float4 pieces.
+template <int KPL>
 __global__ __launch_bounds__(256) void topk_partial_kernel(const float* __restrict__ z, int V,
                                                            int s_top, float* __restrict__ cv,
                                                            int* __restrict__ ci) {
+  __shared__ u64 lst[4][KPL][64];
   const int row = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nw = gridDim.x * 4;                       // waves per row
   const int w = blockIdx.x * 4 + wave;
-  const int base = w * 1024;
+  const int base = w * 64 * KPL;
   const float* zr = z + (size_t)row * V;
-  float v[16];
-  int id[16];
+  u64 key[KPL];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < KPL / 4; ++j) {
     const int i = base + j * 256 + lane * 4;
     float4 x = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-    if (i < V) x = *reinterpret_cast<const float4*>(zr + i);
-    v[4 * j + 0] = x.x; v[4 * j + 1] = x.y; v[4 * j + 2] = x.z; v[4 * j + 3] = x.w;
+    if (i + 3 < V) {
+      x = *reinterpret_cast<const float4*>(zr + i);
+    } else {
+      if (i < V) x.x = zr[i];
+      if (i + 1 < V) x.y = zr[i + 1];
+      if (i + 2 < V) x.z = zr[i + 2];
+    }
+    const float xv[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) id[4 * j + e] = i + e < V ? i + e : 0x7fffffff;
+    for (int e = 0; e < 4; ++e) key[4 * j + e] = i + e < V ? topk_key(xv[e], i + e) : TOPK_EMPTY;
   }
-  float ov = 0.f;
-  int oi = 0;
-  wave_select(v, id, s_top, &ov, &oi);
+  const u64 mine = wave_top_keys<KPL, false>(key, s_top, lst[wave]);
   if (lane < s_top) {
     const size_t o = ((size_t)row * nw + w) * s_top + lane;
-    cv[o] = ov;
-    ci[o] = oi;
+    cv[o] = topk_value(mine);
+    ci[o] = topk_id(mine);
   }
 }
 
-// One wave per row: up to 1024 candidates (16 per lane).
+// Stage 2, one wave per row.  RUNS: lane L takes stage-1 wave L's s
+// candidates, which are already in order (nw <= 64, s <= 16); otherwise the
+// lanes take the ncand <= 1024 candidates 16 apiece and sort them.
+template <bool RUNS>
 __global__ __launch_bounds__(64) void topk_merge_kernel(const float* __restrict__ cv,
-                                                        const int* __restrict__ ci, int ncand,
+                                                        const int* __restrict__ ci, int nw,
                                                         int s_top, int32_t* __restrict__ ids,
                                                         float* __restrict__ vals) {
+  __shared__ u64 lst[16][64];
   const int row = blockIdx.x, lane = threadIdx.x;
-  float v[16];
-  int id[16];
+  const int ncand = nw * s_top;
+  u64 key[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const int c = j * 64 + lane;
-    v[j] = c < ncand ? cv[(size_t)row * ncand + c] : -INFINITY;
-    id[j] = c < ncand ? ci[(size_t)row * ncand + c] : 0x7fffffff;
+    const int c = RUNS ? lane * s_top + j : j * 64 + lane;
+    const bool ok = RUNS ? (lane < nw && j < s_top) : c < ncand;
+    key[j] = ok ? topk_key(cv[(size_t)row * ncand + c], ci[(size_t)row * ncand + c]) : TOPK_EMPTY;
   }
-  float ov = 0.f;
-  int oi = 0;
-  wave_select(v, id, s_top, &ov, &oi);
+  const u64 mine = wave_top_keys<16, RUNS>(key, s_top, lst);
   if (lane < s_top) {
-    ids[(size_t)row * s_top + lane] = oi;
-    vals[(size_t)row * s_top + lane] = ov;
+    ids[(size_t)row * s_top + lane] = topk_id(mine);
+    vals[(size_t)row * s_top + lane] = topk_value(mine);
   }
 }
 
-int topk_waves(int V) { return ((V + 4095) / 4096) * 4; }
+// logits per stage-1 lane: 8 up to a 32768-entry vocabulary, else 16
+static int topk_kpl(int V) { return V <= 32768 ? 8 : 16; }
+int topk_waves(int V) {
+  const int span = 4 * 64 * topk_kpl(V);              // logits per workgroup
+  return ((V + span - 1) / span) * 4;
+}
 
 hipError_t launch_topk(const float* z, int rows, int V, int s_top, int32_t* ids, float* vals,
                        float* cand_v, int* cand_i, hipStream_t s) {
-  if (s_top > 16 || s_top > 64) return hipErrorInvalidValue;
+  if (s_top < 1 || s_top > 16) return hipErrorInvalidValue;
   const int nw = topk_waves(V);
   if (nw * s_top > 1024) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(topk_partial_kernel, dim3(nw / 4, rows), dim3(256), 0, s, z, V, s_top, cand_v,
-                     cand_i);
-  hipLaunchKernelGGL(topk_merge_kernel, dim3(rows), dim3(64), 0, s, cand_v, cand_i, nw * s_top,
-                     s_top, ids, vals);
+  if (topk_kpl(V) == 8)
+    hipLaunchKernelGGL((topk_partial_kernel<8>), dim3(nw / 4, rows), dim3(256), 0, s, z, V, s_top,
+                       cand_v, cand_i);
+  else
+    hipLaunchKernelGGL((topk_partial_kernel<16>), dim3(nw / 4, rows), dim3(256), 0, s, z, V, s_top,
+                       cand_v, cand_i);
+  if (nw <= 64)
+    hipLaunchKernelGGL((topk_merge_kernel<true>), dim3(rows), dim3(64), 0, s, cand_v, cand_i, nw,
+                       s_top, ids, vals);
+  else
+    hipLaunchKernelGGL((topk_merge_kernel<false>), dim3(rows), dim3(64), 0, s, cand_v, cand_i, nw,
+                       s_top, ids, vals);
   return hipGetLastError();
 }
 
