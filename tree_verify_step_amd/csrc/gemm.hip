@@ -161,29 +161,36 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
   }
   const bf16x8* Ap = reinterpret_cast<const bf16x8*>(g.A) + lane;
 
-  // per-row normalisation factors of this tile (row m's partial sums are
-  // contiguous: 16-byte loads, eight in flight, summed in tile order)
-  if (g.ss) {
+  // per-row normalisation factors of this tile.  Row m's partial sums of
+  // squares are contiguous.  Usually LPR adjacent lanes share a row: their
+  // 16-byte loads go out right after the first weight chunk's, and the sums
+  // are formed after the main loop (they only scale the accumulators), so no
+  // wave waits on them before streaming.  Otherwise (few lanes per row, or
+  // many tiles) one lane per row sums them here, before the main loop.
+  constexpr int SS_Q = 4;                              // f32x4 per lane
+  constexpr int LPR = TR <= W * 64 ? ((W * 64) / TR < 16 ? (W * 64) / TR : 16) : 0;   // lanes per row
+  const int ss_n4 = g.ss_tiles >> 2;
+  const bool ss_late = g.ss != nullptr && LPR > 0 && ss_n4 <= LPR * SS_Q;
+  if (g.ss && !ss_late) {
     for (int r = threadIdx.x; r < TR; r += W * 64) {
       const int m = mt * TR + r;
       float s = 0.f;
       if (m < g.M) {
         const float* row = g.ss + (size_t)m * g.ss_ld;
         const f32x4* p4 = reinterpret_cast<const f32x4*>(row);
-        const int n4 = g.ss_tiles >> 2;
         int t = 0;
-        for (; t + 8 <= n4; t += 8) {
+        for (; t + 8 <= ss_n4; t += 8) {
           f32x4 v[8];
 #pragma unroll
           for (int u = 0; u < 8; ++u) v[u] = p4[t + u];
 #pragma unroll
           for (int u = 0; u < 8; ++u) s = s + v[u][0] + v[u][1] + v[u][2] + v[u][3];
         }
-        for (; t < n4; ++t) {
+        for (; t < ss_n4; ++t) {
           const f32x4 v = p4[t];
           s = s + v[0] + v[1] + v[2] + v[3];
         }
-        for (int e = n4 * 4; e < g.ss_tiles; ++e) s += row[e];
+        for (int e = ss_n4 * 4; e < g.ss_tiles; ++e) s += row[e];
       }
       rs_s[r] = 1.0f / sqrtf(s / (float)g.K + 1e-5f);
     }
@@ -229,6 +236,19 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
   loadA(0);
 #pragma unroll
   for (int s = 0; s < KC; ++s) loadB(s, lo + s);
+  f32x4 ssv[SS_Q];
+  float ss_rest = 0.f;
+  if (ss_late) {
+    // lanes past the tile's rows (when the lane count caps LPR) load nothing
+    const int r = (int)threadIdx.x / max(LPR, 1), j = (int)threadIdx.x % max(LPR, 1);
+    const float* row = g.ss + (size_t)min(mt * TR + min(r, TR - 1), g.M - 1) * g.ss_ld;
+#pragma unroll
+    for (int q = 0; q < SS_Q; ++q) {
+      const int t = j + q * LPR;
+      ssv[q] = (r < TR && t < ss_n4) ? reinterpret_cast<const f32x4*>(row)[t] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int e = ss_n4 * 4 + j; r < TR && e < g.ss_tiles; e += LPR) ss_rest += row[e];
+  }
   storeA(0, 0);
   if (EPI == EPI_QKV && threadIdx.x < g.qkv.B)
     s_slot0[threadIdx.x] = min(max(nraw, 0), g.qkv.cap - g.qkv.T);
@@ -250,6 +270,20 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
       __builtin_amdgcn_sched_barrier(0);
     }
     storeA(buf ^ 1, c + 1);
+    __syncthreads();
+  }
+
+  if (ss_late) {      // the row's sum: each lane's quads in order, then over its LPR lanes
+    float sm = ss_rest;
+#pragma unroll
+    for (int q = 0; q < SS_Q; ++q) sm = sm + ssv[q][0] + ssv[q][1] + ssv[q][2] + ssv[q][3];
+    if constexpr (LPR >= 2) sm += MV_DPP(sm, 0xB1);     // quad_perm [1,0,3,2]
+    if constexpr (LPR >= 4) sm += MV_DPP(sm, 0x4E);     // quad_perm [2,3,0,1]
+    if constexpr (LPR >= 8) sm += MV_DPP(sm, 0x141);    // row_half_mirror
+    if constexpr (LPR >= 16) sm += MV_DPP(sm, 0x140);   // row_mirror
+    static_assert(LPR <= 16, "a row's lanes lie inside one DPP row");
+    const int r = (int)threadIdx.x / max(LPR, 1);
+    if ((int)threadIdx.x % max(LPR, 1) == 0 && r < TR) rs_s[r] = 1.0f / sqrtf(sm / (float)g.K + 1e-5f);
     __syncthreads();
   }
 
