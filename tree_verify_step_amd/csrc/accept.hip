@@ -64,14 +64,44 @@ __device__ __forceinline__ double block_sum_d(double v) {
 
 // h[c] = bf16(x[c] * rsqrt(mean(x^2) + 1e-5) * g[c]) for one row of width d
 // (the final RMSNorm of the carried hidden state).  Whole workgroup calls it.
+// Thread t owns columns 4t + 1024i .. +3; up to NORM_PASSES passes are held
+// in registers, so the row is read once, and the gains (which do not depend
+// on the row) can be requested before the row is known (norm_gains).
+constexpr int NORM_PASSES = 8;                 // d <= 8192 on the register path
+struct NormGains {
+  uint2 g[NORM_PASSES];
+};
+__device__ __forceinline__ NormGains norm_gains(const u16* __restrict__ g, int d) {
+  NormGains ng;
+#pragma unroll
+  for (int i = 0; i < NORM_PASSES; ++i) {
+    const int c = threadIdx.x * 4 + i * 1024;
+    ng.g[i] = (g && c < d && d <= NORM_PASSES * 1024) ? *reinterpret_cast<const uint2*>(g + c)
+                                                      : uint2{0u, 0u};
+  }
+  return ng;
+}
 __device__ void block_norm_row(const float* __restrict__ xr, const u16* __restrict__ g,
-                               u16* __restrict__ h, int d) {
+                               const NormGains& ng, u16* __restrict__ h, int d) {
   __shared__ float rf[4];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const bool regs = d <= NORM_PASSES * 1024;
+  float4 xv[NORM_PASSES];
   float sq = 0.f;
-  for (int c = threadIdx.x * 4; c < d; c += 1024) {
-    const float4 v = *reinterpret_cast<const float4*>(xr + c);
-    sq += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  if (regs) {
+#pragma unroll
+    for (int i = 0; i < NORM_PASSES; ++i) {
+      const int c = threadIdx.x * 4 + i * 1024;
+      xv[i] = c < d ? *reinterpret_cast<const float4*>(xr + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < NORM_PASSES; ++i)
+      sq += xv[i].x * xv[i].x + xv[i].y * xv[i].y + xv[i].z * xv[i].z + xv[i].w * xv[i].w;
+  } else {
+    for (int c = threadIdx.x * 4; c < d; c += 1024) {
+      const float4 v = *reinterpret_cast<const float4*>(xr + c);
+      sq += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
   }
   sq = warp_sum(sq);
   if (lane == 0) rf[wave] = sq;
@@ -79,7 +109,21 @@ __device__ void block_norm_row(const float* __restrict__ xr, const u16* __restri
   sq = rf[0] + rf[1] + rf[2] + rf[3];
   __syncthreads();
   const float rs = 1.0f / sqrtf(sq / (float)d + 1e-5f);
-  for (int c = threadIdx.x; c < d; c += 256) h[c] = f32_to_bf16(xr[c] * rs * bf16_to_f32(g[c]));
+  if (regs) {
+#pragma unroll
+    for (int i = 0; i < NORM_PASSES; ++i) {
+      const int c = threadIdx.x * 4 + i * 1024;
+      if (c >= d) continue;
+      const uint2 gw = ng.g[i];
+      const uint32_t lo = (uint32_t)f32_to_bf16(xv[i].x * rs * bf16lo(gw.x)) |
+                          ((uint32_t)f32_to_bf16(xv[i].y * rs * bf16hi(gw.x)) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16(xv[i].z * rs * bf16lo(gw.y)) |
+                          ((uint32_t)f32_to_bf16(xv[i].w * rs * bf16hi(gw.y)) << 16);
+      *reinterpret_cast<uint2*>(h + c) = uint2{lo, hi};
+    }
+  } else {
+    for (int c = threadIdx.x; c < d; c += 256) h[c] = f32_to_bf16(xr[c] * rs * bf16_to_f32(g[c]));
+  }
 }
 
 // Rows are read as float4 (V % 4 == 0), 4 independent loads in flight per
@@ -243,6 +287,7 @@ __global__ __launch_bounds__(256) void accept_finish_kernel(
   __shared__ int amax[MV_MAXT];                              // argmax of each of the T rows
   __shared__ int s_best;
   const int b = blockIdx.x;
+  const NormGains ng = norm_gains(x && h_last ? final_norm : nullptr, d);
   for (int v = threadIdx.x; v < T; v += 256) {
     par[v] = parent[(size_t)b * T + v];
     dep[v] = depth_of[(size_t)b * T + v];
@@ -365,7 +410,7 @@ __global__ __launch_bounds__(256) void accept_finish_kernel(
   const int best = s_best;
   const int brow = row0 + best;
 
-  if (x && h_last) block_norm_row(x + (size_t)brow * d, final_norm, h_last + (size_t)b * d, d);
+  if (x && h_last) block_norm_row(x + (size_t)brow * d, final_norm, ng, h_last + (size_t)b * d, d);
   if (root_mode == MV_ROOT_ARGMAX) {
     if (threadIdx.x == 0) next_root[b] = amax[best];
     return;
@@ -405,7 +450,7 @@ __global__ __launch_bounds__(256) void prefill_select_kernel(
   const int c = cnt[b];
   if (c <= 0) return;
   const int row = b * T + c - 1;
-  block_norm_row(x + (size_t)row * d, final_norm, h_last + (size_t)b * d, d);
+  block_norm_row(x + (size_t)row * d, final_norm, norm_gains(final_norm, d), h_last + (size_t)b * d, d);
   if (root_mode == MV_ROOT_ARGMAX) {
     if (threadIdx.x == 0) root[b] = amax[row];
   } else {

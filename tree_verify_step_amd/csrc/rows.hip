@@ -69,44 +69,35 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
                                                     float2* __restrict__ rope, int T, int hd,
                                                     EmbedTree et, EmbedNorm en) {
   const int m = blockIdx.x;
+  // requests that depend on nothing go out first: the node's depth and rank,
+  // the root, the prefix length, the norm's gains
+  constexpr int EC = 4;                         // 8-column chunks per thread (d <= 8192)
+  const bool regs = d <= EC * 2048;
+  uint4 gw[EC];
+#pragma unroll
+  for (int j = 0; j < EC; ++j) {
+    const int c = threadIdx.x * 8 + j * 2048;
+    gw[j] = (en.gain && regs && c < d) ? *reinterpret_cast<const uint4*>(en.gain + c)
+                                        : uint4{0u, 0u, 0u, 0u};
+  }
+  const int T_ = T > 0 ? T : 1;
+  const int b = m / T_, v = m - b * T_;
+  const int dep_m = depth_of ? depth_of[m] : 0;
+  const int npre = rope ? n_prefix[b] : 0;
   int t;
   if (et.top_ids) {
-    const int b = m / T, v = m - b * T;
-    const int dep = min(depth_of[m], et.D);
+    const int dep = min(dep_m, et.D);
     const int rk = min(max(et.rank[m], 0), et.s_top - 1);
-    t = (v == 0 || dep <= 0) ? et.root[b] : et.top_ids[((size_t)b * et.D + (dep - 1)) * et.s_top + rk];
-    if (threadIdx.x == 0) et.tok_out[m] = t;
+    const int rt = et.root[b];
+    t = (v == 0 || dep <= 0) ? rt : et.top_ids[((size_t)b * et.D + (dep - 1)) * et.s_top + rk];
   } else {
     t = tok[m];
   }
-  t = t < 0 ? 0 : (t >= V ? V - 1 : t);
-  const u16* e = E + (size_t)t * d;
-  float* xr = x + (size_t)m * d;
-  float sq = 0.f;
-  for (int c = threadIdx.x * 8; c < d; c += 2048) {
-    const uint4 w = *reinterpret_cast<const uint4*>(e + c);
-    float4 a = {bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y)};
-    float4 b = {bf16lo(w.z), bf16hi(w.z), bf16lo(w.w), bf16hi(w.w)};
-    *reinterpret_cast<float4*>(xr + c) = a;
-    *reinterpret_cast<float4*>(xr + c + 4) = b;
-    sq += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w + b.x * b.x + b.y * b.y + b.z * b.z +
-          b.w * b.w;
-    if (en.gain) {
-      const uint4 gw = *reinterpret_cast<const uint4*>(en.gain + c);
-      uint4 o;
-      o.x = f32_to_bf16(a.x * bf16lo(gw.x)) | ((uint32_t)f32_to_bf16(a.y * bf16hi(gw.x)) << 16);
-      o.y = f32_to_bf16(a.z * bf16lo(gw.y)) | ((uint32_t)f32_to_bf16(a.w * bf16hi(gw.y)) << 16);
-      o.z = f32_to_bf16(b.x * bf16lo(gw.z)) | ((uint32_t)f32_to_bf16(b.y * bf16hi(gw.z)) << 16);
-      o.w = f32_to_bf16(b.z * bf16lo(gw.w)) | ((uint32_t)f32_to_bf16(b.w * bf16hi(gw.w)) << 16);
-      *reinterpret_cast<uint4*>(en.xn + packed_index(m, c, d)) = o;
-    }
-  }
-  sq = block_sum256(sq);
-  if (threadIdx.x == 0 && ss) ss[m] = sq;
-  if (threadIdx.x == 0 && en.gain) en.ss[(size_t)m * en.ss_ld] = sq;
+  // the RoPE table row needs only the position: computed while the token's
+  // id is in flight
   if (rope) {
     const int half = hd >> 1;
-    const double pos = (double)(n_prefix[m / T] + depth_of[m]);
+    const double pos = (double)(npre + dep_m);
     for (int i = threadIdx.x; i < half; i += 256) {
       const double inv = pow(10000.0, -2.0 * (double)i / (double)hd);
       double sv, cv;
@@ -114,6 +105,41 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
       rope[(size_t)m * half + i] = make_float2((float)cv, (float)sv);
     }
   }
+  if (et.top_ids && threadIdx.x == 0) et.tok_out[m] = t;
+  t = t < 0 ? 0 : (t >= V ? V - 1 : t);
+  const u16* e = E + (size_t)t * d;
+  float* xr = x + (size_t)m * d;
+  float sq = 0.f;
+  auto one_chunk = [&](int c, const uint4& gwc) {
+    const uint4 w = *reinterpret_cast<const uint4*>(e + c);
+    float4 a = {bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y)};
+    float4 bb = {bf16lo(w.z), bf16hi(w.z), bf16lo(w.w), bf16hi(w.w)};
+    *reinterpret_cast<float4*>(xr + c) = a;
+    *reinterpret_cast<float4*>(xr + c + 4) = bb;
+    sq += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w + bb.x * bb.x + bb.y * bb.y + bb.z * bb.z +
+          bb.w * bb.w;
+    if (en.gain) {
+      uint4 o;
+      o.x = f32_to_bf16(a.x * bf16lo(gwc.x)) | ((uint32_t)f32_to_bf16(a.y * bf16hi(gwc.x)) << 16);
+      o.y = f32_to_bf16(a.z * bf16lo(gwc.y)) | ((uint32_t)f32_to_bf16(a.w * bf16hi(gwc.y)) << 16);
+      o.z = f32_to_bf16(bb.x * bf16lo(gwc.z)) | ((uint32_t)f32_to_bf16(bb.y * bf16hi(gwc.z)) << 16);
+      o.w = f32_to_bf16(bb.z * bf16lo(gwc.w)) | ((uint32_t)f32_to_bf16(bb.w * bf16hi(gwc.w)) << 16);
+      *reinterpret_cast<uint4*>(en.xn + packed_index(m, c, d)) = o;
+    }
+  };
+  if (regs) {
+#pragma unroll
+    for (int j = 0; j < EC; ++j) {
+      const int c = threadIdx.x * 8 + j * 2048;
+      if (c < d) one_chunk(c, gw[j]);
+    }
+  } else {
+    for (int c = threadIdx.x * 8; c < d; c += 2048)
+      one_chunk(c, en.gain ? *reinterpret_cast<const uint4*>(en.gain + c) : uint4{0u, 0u, 0u, 0u});
+  }
+  sq = block_sum256(sq);
+  if (threadIdx.x == 0 && ss) ss[m] = sq;
+  if (threadIdx.x == 0 && en.gain) en.ss[(size_t)m * en.ss_ld] = sq;
 }
 
 hipError_t launch_embed(const int32_t* tok, const u16* E, float* x, float* ss, int M, int d,
