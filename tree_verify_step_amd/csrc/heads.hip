@@ -103,6 +103,86 @@ __global__ __launch_bounds__(256) void heads_gemv_kernel(const u16* __restrict__
   }
 }
 
+// Batch 1 with d <= 512 * GEMV_CH: the input row lives in registers (each
+// lane holds the 8 values under each of its GEMV_CH weight pieces), so there
+// is no LDS staging and no barrier before the first weight bytes are used;
+// mode 0's residual input h[r] is requested with the weights of its rows.
+__global__ __launch_bounds__(256) void heads_gemv1_kernel(const u16* __restrict__ hb,
+                                                          const float* __restrict__ uf,
+                                                          const u16* __restrict__ W,
+                                                          float* __restrict__ out, int D, int d,
+                                                          int rows, int mode, int rpw) {
+  const int k = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const u16* Wk = W + (size_t)k * rows * d;
+  const int r_lo = blockIdx.x * rpw;
+  const int r_hi = min(rows, r_lo + rpw);
+  uint4 w[GEMV_CH][GEMV_RW];
+  float hres[GEMV_RW];
+  auto load = [&](int r0) {
+#pragma unroll
+    for (int j = 0; j < GEMV_CH; ++j) {
+      const int c = min(j * 512 + lane * 8, d - 8);            // clamped: in bounds
+#pragma unroll
+      for (int i = 0; i < GEMV_RW; ++i) {
+        const int r = min(r0 + i, r_hi - 1);
+        w[j][i] = *reinterpret_cast<const uint4*>(Wk + (size_t)r * d + c);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < GEMV_RW; ++i)
+      hres[i] = mode == 0 ? bf16_to_f32(hb[min(r0 + i, r_hi - 1)]) : 0.f;
+  };
+  int r0 = r_lo + wave * GEMV_RW;
+  if (r0 < r_hi) load(r0);
+  float xv[GEMV_CH][8];
+#pragma unroll
+  for (int j = 0; j < GEMV_CH; ++j) {
+    const int c = j * 512 + lane * 8;
+    if (c < d && mode == 0) {
+      const uint4 h8 = *reinterpret_cast<const uint4*>(hb + c);
+      xv[j][0] = bf16lo(h8.x); xv[j][1] = bf16hi(h8.x); xv[j][2] = bf16lo(h8.y); xv[j][3] = bf16hi(h8.y);
+      xv[j][4] = bf16lo(h8.z); xv[j][5] = bf16hi(h8.z); xv[j][6] = bf16lo(h8.w); xv[j][7] = bf16hi(h8.w);
+    } else if (c < d) {
+      const float4 a = *reinterpret_cast<const float4*>(uf + (size_t)k * d + c);
+      const float4 b = *reinterpret_cast<const float4*>(uf + (size_t)k * d + c + 4);
+      xv[j][0] = a.x; xv[j][1] = a.y; xv[j][2] = a.z; xv[j][3] = a.w;
+      xv[j][4] = b.x; xv[j][5] = b.y; xv[j][6] = b.z; xv[j][7] = b.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xv[j][e] = 0.f;
+    }
+  }
+  for (; r0 < r_hi; r0 += 4 * GEMV_RW) {
+    float acc[GEMV_RW];
+#pragma unroll
+    for (int i = 0; i < GEMV_RW; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < GEMV_CH; ++j) {
+      if (j * 512 + lane * 8 >= d) break;
+#pragma unroll
+      for (int i = 0; i < GEMV_RW; ++i) {
+        float a = acc[i];
+        a += bf16lo(w[j][i].x) * xv[j][0] + bf16hi(w[j][i].x) * xv[j][1];
+        a += bf16lo(w[j][i].y) * xv[j][2] + bf16hi(w[j][i].y) * xv[j][3];
+        a += bf16lo(w[j][i].z) * xv[j][4] + bf16hi(w[j][i].z) * xv[j][5];
+        a += bf16lo(w[j][i].w) * xv[j][6] + bf16hi(w[j][i].w) * xv[j][7];
+        acc[i] = a;
+      }
+    }
+    float hcur[GEMV_RW];
+#pragma unroll
+    for (int i = 0; i < GEMV_RW; ++i) hcur[i] = hres[i];
+    if (r0 + 4 * GEMV_RW < r_hi) load(r0 + 4 * GEMV_RW);     // next rows before the reductions
+#pragma unroll
+    for (int i = 0; i < GEMV_RW; ++i) {
+      const int r = r0 + i;
+      const float y = warp_sum(acc[i]);
+      if (lane == 0 && r < r_hi) out[(size_t)k * rows + r] = mode == 0 ? hcur[i] + silu_f(y) : y;
+    }
+  }
+}
+
 // rpw rows per workgroup (a multiple of 4 waves x GEMV_RW): fewer rows per
 // workgroup when the matrix is short, so that the grid still covers the CUs.
 static hipError_t launch_gemv(const u16* hb, const float* uf, const u16* W, float* out, int B,
@@ -122,7 +202,9 @@ static hipError_t launch_gemv(const u16* hb, const float* uf, const u16* W, floa
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)MV_HEADS_LDS_MAX);
     if (e != hipSuccess) return e;
   }
-  if (B == 1)
+  if (B == 1 && d <= 512 * GEMV_CH)
+    hipLaunchKernelGGL(heads_gemv1_kernel, grid, dim3(256), 0, s, hb, uf, W, out, D, d, rows, mode, rpw);
+  else if (B == 1)
     hipLaunchKernelGGL((heads_gemv_kernel<1>), grid, dim3(256), lds, s, hb, uf, W, out, B, D, d, rows, mode, rpw);
   else if (B <= 4)
     hipLaunchKernelGGL((heads_gemv_kernel<4>), grid, dim3(256), lds, s, hb, uf, W, out, B, D, d, rows, mode, rpw);
