@@ -11,10 +11,12 @@
 //    keeps a register ring of KC k-blocks of them in flight (consumed, then
 //    refilled in place; scheduling barriers keep the refill after the MFMAs
 //    that read the stage, so no register copies undo the prefetch).
-//  * The activation operand is staged once per workgroup in LDS, KC k-blocks
-//    per chunk, double-buffered, and shared by the W waves; k-blocks past the
-//    range are staged as zeros, so the main loop has no branches and the
-//    compiler's wait counts stay partial.
+//  * The activation operand is staged once per workgroup in LDS, AH ring
+//    lengths (AH * KC k-blocks) per chunk, double-buffered, and shared by the
+//    W waves; k-blocks past the range are staged as zeros, so the main loop
+//    has no branches and the compiler's wait counts stay partial.  The
+//    unsplit gate/up GEMM takes two ring lengths per chunk (half the
+//    barriers); the split GEMMs, whose k-ranges are short, take one.
 //  * K is split over `splits` workgroups when the column tiles alone cannot
 //    fill the chip.  Each split writes its partial tile with write-through
 //    (system-scope) stores, waits for them, and bumps the tile's arrival
@@ -76,8 +78,8 @@ __device__ __forceinline__ void row16_best(float& bv, int& bi) {
   }
 }
 
-// k-blocks per activation chunk (= depth of the weight ring): the LDS chunk
-// holds KC * MB KiB per buffer.
+// depth of the weight ring in k-blocks; an activation chunk of AH ring
+// lengths holds AH * KC * MB KiB per LDS buffer.
 template <int MB>
 struct GemmShape {
   static constexpr int KC = MB <= 4 ? 8 : (MB == 8 ? 4 : 2);
@@ -116,10 +118,12 @@ __device__ __forceinline__ void prefetch_prefix_kv(const QkvArgs& q, int p, int 
 
 template <int MB, int W, int NBW, int EPI>
 __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
-  constexpr int KC = GemmShape<MB>::KC;
-  constexpr int APC = KC * MB;                 // 1 KiB activation pieces per chunk
-  constexpr int AI = APC / W;                  // pieces staged per thread
-  static_assert(APC % W == 0, "chunk pieces must divide among the waves");
+  constexpr int KC = GemmShape<MB>::KC;        // weight ring depth (k-blocks)
+  constexpr int AH = EPI == EPI_SWIGLU ? 2 : 1; // ring lengths per activation chunk
+  constexpr int APH = KC * MB;                 // 1 KiB activation pieces per ring length
+  constexpr int APC = AH * APH;                // ... per chunk (one barrier per chunk)
+  constexpr int AI = APH / W;                  // pieces staged per thread per ring length
+  static_assert(APH % W == 0, "chunk pieces must divide among the waves");
   constexpr int TR = MB * 16;                  // rows of a tile
   __shared__ bf16x8 As[2][APC][64];            // [buf][kl * MB + rb][lane]
   __shared__ float rs_s[TR];
@@ -140,7 +144,7 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
   const int KB = g.K >> 5;
   const int lo = (int)((long long)KB * split / g.splits);
   const int hi = (int)((long long)KB * (split + 1) / g.splits);
-  const int nchunks = (hi - lo + KC - 1) / KC;
+  const int nchunks = (hi - lo + AH * KC - 1) / (AH * KC);
   const int NBtot = g.N >> 4;                  // 16-column blocks of W (and of W2)
   const int MBtot = g.Mp >> 4;
 
@@ -202,23 +206,24 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) acc[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // the activation chunk is staged one ring length (KC k-blocks) at a time
   bf16x8 ar[AI];
-  auto loadA = [&](int c) {
+  auto loadA = [&](bf16x8 (&dst)[AI], int c, int h) {
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
       const int piece = i * W + wave;
-      const int kl = piece / MB, rb = piece % MB;
-      const int k = min(lo + c * KC + kl, hi - 1);
+      const int kl = h * KC + piece / MB, rb = piece % MB;
+      const int k = min(lo + c * AH * KC + kl, hi - 1);
       const int rbg = min(mt * MB + rb, MBtot - 1);
-      ar[i] = Ap[((size_t)rbg * KB + k) * 64];
+      dst[i] = Ap[((size_t)rbg * KB + k) * 64];
     }
   };
-  auto storeA = [&](int buf, int c) {          // k-blocks past the range are zeros
+  auto storeA = [&](const bf16x8 (&src)[AI], int buf, int c, int h) {   // past the range: zeros
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
       const int piece = i * W + wave;
-      const int kl = piece / MB;
-      As[buf][piece][lane] = (lo + c * KC + kl < hi) ? ar[i] : bf16x8{};
+      const int kl = h * KC + piece / MB;
+      As[buf][h * APH + piece][lane] = (lo + c * AH * KC + kl < hi) ? src[i] : bf16x8{};
     }
   };
   bf16x8 br[KC][NBW];
@@ -233,9 +238,18 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
   // store in bounds)
   int nraw = 0;
   if (EPI == EPI_QKV && threadIdx.x < g.qkv.B) nraw = g.qkv.n_prefix[threadIdx.x];
-  loadA(0);
+  if constexpr (AH == 2) {
+    bf16x8 a0[AI];
+    loadA(a0, 0, 0);
 #pragma unroll
-  for (int s = 0; s < KC; ++s) loadB(s, lo + s);
+    for (int s = 0; s < KC; ++s) loadB(s, lo + s);
+    loadA(ar, 0, 1);
+    storeA(a0, 0, 0, 0);
+  } else {
+    loadA(ar, 0, 0);
+#pragma unroll
+    for (int s = 0; s < KC; ++s) loadB(s, lo + s);
+  }
   f32x4 ssv[SS_Q];
   float ss_rest = 0.f;
   if (ss_late) {
@@ -249,27 +263,30 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
     }
     for (int e = ss_n4 * 4 + j; r < TR && e < g.ss_tiles; e += LPR) ss_rest += row[e];
   }
-  storeA(0, 0);
+  storeA(ar, 0, 0, AH - 1);
   if (EPI == EPI_QKV && threadIdx.x < g.qkv.B)
     s_slot0[threadIdx.x] = min(max(nraw, 0), g.qkv.cap - g.qkv.T);
   __syncthreads();
   for (int c = 0; c < nchunks; ++c) {
     const int buf = c & 1;
-    loadA(c + 1);
 #pragma unroll
-    for (int kk = 0; kk < KC; ++kk) {
-      bf16x8 a[MB];
+    for (int h = 0; h < AH; ++h) {
+      loadA(ar, c + 1, h);
 #pragma unroll
-      for (int rb = 0; rb < MB; ++rb) a[rb] = As[buf][kk * MB + rb][lane];
+      for (int kk = 0; kk < KC; ++kk) {
+        bf16x8 a[MB];
 #pragma unroll
-      for (int rb = 0; rb < MB; ++rb)
+        for (int rb = 0; rb < MB; ++rb) a[rb] = As[buf][(h * KC + kk) * MB + rb][lane];
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) acc[rb][nb] = mfma16x16x32(a[rb], br[kk][nb], acc[rb][nb]);
-      __builtin_amdgcn_sched_barrier(0);
-      loadB(kk, lo + (c + 1) * KC + kk);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+          for (int nb = 0; nb < NBW; ++nb) acc[rb][nb] = mfma16x16x32(a[rb], br[kk][nb], acc[rb][nb]);
+        __builtin_amdgcn_sched_barrier(0);
+        loadB(kk, lo + (c * AH + h + 1) * KC + kk);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      storeA(ar, buf ^ 1, c + 1, h);
     }
-    storeA(buf ^ 1, c + 1);
     __syncthreads();
   }
 
