@@ -78,14 +78,21 @@ __device__ __forceinline__ void row16_best(float& bv, int& bi) {
   }
 }
 
-// depth of the weight ring in k-blocks; an activation chunk of AH ring
-// lengths holds AH * KC * MB KiB per LDS buffer.
-template <int MB>
+// KC: depth of the weight ring in k-blocks (per wave, KC * NBW KiB in
+// flight).  KCA: k-blocks per activation chunk (KCA * MB KiB per LDS
+// buffer, one barrier per chunk).  Up to 64 rows: an 8-deep ring, with two
+// ring lengths per chunk for the unsplit gate/up GEMM and one otherwise.
+// 128- and 256-row tiles with one column block per wave keep the 8-deep ring
+// and stage 32 KiB chunks (a half or a quarter of a ring length); with two
+// blocks per wave their accumulators leave registers for a 4- or 2-deep ring
+// only, one ring length per chunk.
+template <int MB, int NBW, int EPI>
 struct GemmShape {
-  static constexpr int KC = MB <= 4 ? 8 : (MB == 8 ? 4 : 2);
+  static constexpr int KC = MB <= 4 || NBW == 1 ? 8 : 32 / MB;
+  static constexpr int KCA = MB <= 4 ? (EPI == EPI_SWIGLU ? 2 * KC : KC) : 32 / MB;
 };
 
-int gemm_kc(int MB) { return MB <= 4 ? 8 : (MB == 8 ? 4 : 2); }
+int gemm_kc(int MB) { return MB <= 4 ? 8 : 32 / MB; }   // k-blocks per activation chunk
 
 // Reads the cached prefix K and V of one layer (slots 0 .. n-1 of every
 // (sequence, head) block: the first ceil(n/32) K groups and ceil(n/8) V runs,
@@ -118,12 +125,19 @@ __device__ __forceinline__ void prefetch_prefix_kv(const QkvArgs& q, int p, int 
 
 template <int MB, int W, int NBW, int EPI>
 __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
-  constexpr int KC = GemmShape<MB>::KC;        // weight ring depth (k-blocks)
-  constexpr int AH = EPI == EPI_SWIGLU ? 2 : 1; // ring lengths per activation chunk
-  constexpr int APH = KC * MB;                 // 1 KiB activation pieces per ring length
-  constexpr int APC = AH * APH;                // ... per chunk (one barrier per chunk)
-  constexpr int AI = APH / W;                  // pieces staged per thread per ring length
-  static_assert(APH % W == 0, "chunk pieces must divide among the waves");
+  constexpr int KC = GemmShape<MB, NBW, EPI>::KC;     // weight ring depth (k-blocks)
+  constexpr int KCA = GemmShape<MB, NBW, EPI>::KCA;   // k-blocks per activation chunk
+  // the main loop runs in segments of SG k-blocks; each stages SG k-blocks of
+  // the next activation chunk (PARTS segments fill one chunk)
+  constexpr int SG = KCA < KC ? KCA : KC;
+  constexpr int UO = KCA < KC ? KC : KCA;      // k-blocks per outer iteration
+  constexpr int NSEG = UO / SG;
+  constexpr int PARTS = KCA / SG;
+  constexpr int APS = SG * MB;                 // 1 KiB activation pieces per segment
+  constexpr int APC = KCA * MB;                // ... per chunk
+  constexpr int AI = APS / W;                  // pieces staged per thread per segment
+  static_assert(APS % W == 0, "segment pieces must divide among the waves");
+  static_assert(PARTS <= 2 && (KCA < KC ? KC % KCA == 0 : KCA % KC == 0), "chunk and ring align");
   constexpr int TR = MB * 16;                  // rows of a tile
   __shared__ bf16x8 As[2][APC][64];            // [buf][kl * MB + rb][lane]
   __shared__ float rs_s[TR];
@@ -144,7 +158,7 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
   const int KB = g.K >> 5;
   const int lo = (int)((long long)KB * split / g.splits);
   const int hi = (int)((long long)KB * (split + 1) / g.splits);
-  const int nchunks = (hi - lo + AH * KC - 1) / (AH * KC);
+  const int nouter = (hi - lo + UO - 1) / UO;
   const int NBtot = g.N >> 4;                  // 16-column blocks of W (and of W2)
   const int MBtot = g.Mp >> 4;
 
@@ -206,14 +220,14 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) acc[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // the activation chunk is staged one ring length (KC k-blocks) at a time
+  // part h (SG k-blocks) of activation chunk c
   bf16x8 ar[AI];
   auto loadA = [&](bf16x8 (&dst)[AI], int c, int h) {
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
       const int piece = i * W + wave;
-      const int kl = h * KC + piece / MB, rb = piece % MB;
-      const int k = min(lo + c * AH * KC + kl, hi - 1);
+      const int kl = h * SG + piece / MB, rb = piece % MB;
+      const int k = min(lo + c * KCA + kl, hi - 1);
       const int rbg = min(mt * MB + rb, MBtot - 1);
       dst[i] = Ap[((size_t)rbg * KB + k) * 64];
     }
@@ -222,8 +236,8 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
       const int piece = i * W + wave;
-      const int kl = h * KC + piece / MB;
-      As[buf][h * APH + piece][lane] = (lo + c * AH * KC + kl < hi) ? src[i] : bf16x8{};
+      const int kl = h * SG + piece / MB;
+      As[buf][h * APS + piece][lane] = (lo + c * KCA + kl < hi) ? src[i] : bf16x8{};
     }
   };
   bf16x8 br[KC][NBW];
@@ -238,7 +252,7 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
   // store in bounds)
   int nraw = 0;
   if (EPI == EPI_QKV && threadIdx.x < g.qkv.B) nraw = g.qkv.n_prefix[threadIdx.x];
-  if constexpr (AH == 2) {
+  if constexpr (PARTS == 2) {
     bf16x8 a0[AI];
     loadA(a0, 0, 0);
 #pragma unroll
@@ -263,31 +277,37 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
     }
     for (int e = ss_n4 * 4 + j; r < TR && e < g.ss_tiles; e += LPR) ss_rest += row[e];
   }
-  storeA(ar, 0, 0, AH - 1);
+  storeA(ar, 0, 0, PARTS - 1);
   if (EPI == EPI_QKV && threadIdx.x < g.qkv.B)
     s_slot0[threadIdx.x] = min(max(nraw, 0), g.qkv.cap - g.qkv.T);
   __syncthreads();
-  for (int c = 0; c < nchunks; ++c) {
-    const int buf = c & 1;
+  // the weight k-block consumed at (o, sg, kk) is lo + o*UO + sg*SG + kk; its
+  // ring stage is refilled with the k-block KC further on
+  for (int o = 0; o < nouter; ++o) {
 #pragma unroll
-    for (int h = 0; h < AH; ++h) {
+    for (int sg = 0; sg < NSEG; ++sg) {
+      const int c = PARTS == 1 ? o * NSEG + sg : o;        // chunk being read
+      const int h = PARTS == 1 ? 0 : sg;                   // part staged for chunk c + 1
+      const int buf = c & 1;
       loadA(ar, c + 1, h);
 #pragma unroll
-      for (int kk = 0; kk < KC; ++kk) {
+      for (int kk = 0; kk < SG; ++kk) {
+        const int stage = PARTS == 1 ? sg * SG + kk : kk;
+        const int apos = PARTS == 1 ? kk : sg * SG + kk;
         bf16x8 a[MB];
 #pragma unroll
-        for (int rb = 0; rb < MB; ++rb) a[rb] = As[buf][(h * KC + kk) * MB + rb][lane];
+        for (int rb = 0; rb < MB; ++rb) a[rb] = As[buf][apos * MB + rb][lane];
 #pragma unroll
         for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
-          for (int nb = 0; nb < NBW; ++nb) acc[rb][nb] = mfma16x16x32(a[rb], br[kk][nb], acc[rb][nb]);
+          for (int nb = 0; nb < NBW; ++nb) acc[rb][nb] = mfma16x16x32(a[rb], br[stage][nb], acc[rb][nb]);
         __builtin_amdgcn_sched_barrier(0);
-        loadB(kk, lo + (c * AH + h + 1) * KC + kk);
+        loadB(stage, lo + o * UO + sg * SG + kk + KC);
         __builtin_amdgcn_sched_barrier(0);
       }
       storeA(ar, buf ^ 1, c + 1, h);
+      if (PARTS == 1 || sg == NSEG - 1) __syncthreads();
     }
-    __syncthreads();
   }
 
   if (ss_late) {      // the row's sum: each lane's quads in order, then over its LPR lanes
