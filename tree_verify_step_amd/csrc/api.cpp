@@ -83,16 +83,24 @@ struct GemmCfg {
 // 256 compute units, keeping at least two activation chunks per split.
 static GemmCfg gemm_cfg(const mv_dims& D, int kind, int Mp) {
   GemmCfg c;
+  c.MB = mvk::gemm_mb(Mp);
   switch (kind) {
     case G_QKV: c.w = 4; c.nbw = 2; c.N = 3 * D.d; c.K = D.d; c.epi = mvk::EPI_QKV; break;
     case G_O: c.w = 4; c.nbw = 1; c.N = D.d; c.K = D.d; c.epi = mvk::EPI_ADD; break;
-    case G_GU: c.w = 4; c.nbw = 2; c.N = D.F; c.K = D.d; c.epi = mvk::EPI_SWIGLU; break;
+    case G_GU: {
+      // 128- and 256-row tiles: gate and up blocks in separate 8-wave
+      // workgroups' waves (deeper weight ring) while those tiles fit the
+      // compute units in one round; otherwise two blocks per wave
+      const bool split = c.MB >= 8 && (D.F / 16 + 3) / 4 <= 256;
+      c.w = split ? 8 : 4; c.nbw = split ? 1 : 2; c.N = D.F; c.K = D.d;
+      c.epi = mvk::EPI_SWIGLU;
+      break;
+    }
     case G_DOWN: c.w = 4; c.nbw = 1; c.N = D.d; c.K = D.F; c.epi = mvk::EPI_ADD; break;
     default:
       c.w = D.V % 128 == 0 ? 8 : 4; c.nbw = 1; c.N = D.V; c.K = D.d; c.epi = mvk::EPI_STORE;
       break;
   }
-  c.MB = mvk::gemm_mb(Mp);
   c.mtiles = (Mp / 16 + c.MB - 1) / c.MB;
   c.ntiles = mvk::gemm_ntiles(c.epi, c.N, c.w, c.nbw);
   const int KB = c.K / 32, KC = mvk::gemm_kc(c.MB);

@@ -144,7 +144,11 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
   __shared__ int s_last;
   __shared__ int s_slot0[MV_MAX_BATCH];        // QKV: cache slot of each sequence's node 0
 
-  constexpr int PER_TILE = EPI == EPI_SWIGLU ? W : W * NBW;   // 16-column blocks per tile
+  // SwiGLU with one block per wave: waves 0 .. FW-1 take gate blocks, waves
+  // FW .. W-1 the up blocks of the same features (FW feature blocks a tile)
+  constexpr bool SPLIT_GU = EPI == EPI_SWIGLU && NBW == 1;
+  constexpr int FW = SPLIT_GU ? W / 2 : W;
+  constexpr int PER_TILE = EPI == EPI_SWIGLU ? FW : W * NBW;  // 16-column blocks per tile
   const int NT = (g.N / 16 + PER_TILE - 1) / PER_TILE;          // column tiles
   if constexpr (EPI == EPI_QKV) {
     if ((int)blockIdx.x >= NT) {               // appended prefetch workgroups
@@ -164,7 +168,7 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
 
   // this wave's column blocks (waves past the last block compute on a
   // clamped block and store nothing)
-  const int wb = nt * W + wave;
+  const int wb = SPLIT_GU ? nt * FW + wave % FW : nt * W + wave;
   const int first_blk = EPI == EPI_SWIGLU ? wb : wb * NBW;
   const int blk_cnt = EPI == EPI_SWIGLU ? 1 : NBW;
   const bool active = first_blk + blk_cnt <= NBtot;
@@ -172,7 +176,9 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
   const bf16x8* Bp[NBW];
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb) {
-    if (EPI == EPI_SWIGLU)
+    if (SPLIT_GU)
+      Bp[nb] = reinterpret_cast<const bf16x8*>(wave < FW ? g.W : g.W2) + (size_t)cb * 64 + lane;
+    else if (EPI == EPI_SWIGLU)
       Bp[nb] = reinterpret_cast<const bf16x8*>(nb == 0 ? g.W : g.W2) + (size_t)cb * 64 + lane;
     else
       Bp[nb] = reinterpret_cast<const bf16x8*>(g.W) + (size_t)(cb + nb) * 64 + lane;
@@ -554,6 +560,47 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
         if (p % APR == 0 && p < TR * APR && m < g.M) g.ss_out[(size_t)m * g.ss_ld + nt] = sq;
       }
     }
+  } else if constexpr (SPLIT_GU) {
+    // gate wave w and up wave w + FW hold the same rows and columns in the
+    // same lanes: the up waves park their accumulators in the operand LDS,
+    // the gate waves form h = SiLU(gate) * up and stage it as bf16, then
+    // write whole 16-byte pieces (8 features of one row)
+    static_assert(FW * MB * 4 * 64 * 4 <= (int)sizeof(As) && FW * TR * 16 * 2 <= (int)sizeof(As),
+                  "SwiGLU pairing fits the operand LDS");
+    float* upv = reinterpret_cast<float*>(&As[0][0][0]);
+    if (wave >= FW) {
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) upv[(((wave - FW) * MB + rb) * 4 + r) * 64 + lane] = acc[rb][0][r];
+    }
+    __syncthreads();
+    u16 hv[MB][4];
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        hv[rb][r] = wave < FW ? f32_to_bf16(silu_f(acc[rb][0][r]) *
+                                            upv[((wave * MB + rb) * 4 + r) * 64 + lane])
+                              : (u16)0;
+    __syncthreads();
+    u16* stg = reinterpret_cast<u16*>(&As[0][0][0]) + (wave % FW) * TR * 16;
+    if (wave < FW) {
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) stg[(rb * 16 + 4 * (lane >> 4) + r) * 16 + col] = hv[rb][r];
+    }
+    __syncthreads();
+    if (wave < FW && active) {
+#pragma unroll
+      for (int p = lane; p < TR * 2; p += 64) {
+        const int rl = p >> 1, m = mt * TR + rl;
+        if (m < g.M)
+          *reinterpret_cast<uint4*>(g.out_bf16 + packed_index(m, wb * 16 + 8 * (p & 1), g.N)) =
+              *reinterpret_cast<const uint4*>(stg + rl * 16 + 8 * (p & 1));
+      }
+    }
   } else if constexpr (EPI == EPI_SWIGLU) {
     // h = SiLU(gate) * up, staged per wave in the operand LDS as bf16 so that
     // each lane then writes whole 16-byte pieces (8 features of one row)
@@ -703,7 +750,7 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
 
 int gemm_ntiles(int epi, int N, int w, int nbw) {
   const int blocks = N / 16;
-  const int per_tile = epi == EPI_SWIGLU ? w : w * nbw;
+  const int per_tile = epi == EPI_SWIGLU ? (nbw == 2 ? w : w / 2) : w * nbw;
   return (blocks + per_tile - 1) / per_tile;
 }
 
@@ -715,8 +762,10 @@ int gemm_mb(int Mp) {
 template <int MB, int W, int NBW>
 static hipError_t launch_mb(const GemmArgs& g, dim3 grid, hipStream_t s) {
   const dim3 blk(W * 64);
-  if constexpr (NBW == 1 && W == 8) {            // 8-wave tiles: LM head only
+  if constexpr (NBW == 1 && W == 8) {            // 8-wave tiles: LM head; gate/up of wide tiles
     if (g.epi == EPI_STORE) hipLaunchKernelGGL((gemm_kernel<MB, 8, 1, EPI_STORE>), grid, blk, 0, s, g);
+    else if (MB >= 8 && g.epi == EPI_SWIGLU)
+      hipLaunchKernelGGL((gemm_kernel<(MB >= 8 ? MB : 8), 8, 1, EPI_SWIGLU>), grid, blk, 0, s, g);
     else return hipErrorInvalidValue;
   } else if constexpr (NBW == 1) {
     if (g.epi == EPI_STORE) hipLaunchKernelGGL((gemm_kernel<MB, W, 1, EPI_STORE>), grid, blk, 0, s, g);
