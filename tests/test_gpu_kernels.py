@@ -169,11 +169,12 @@ def _layer_case(D, B, ns, paths_per_seq, topk, seed, gain_std=0.1):
     ("mid", 4, [64, 301, 5, 1000]),   # 256 rows (batch 4): 16-row-block tiles
     ("mid_f480", 1, [40]),     # F % 64 == 32: the last gate/up tile has idle waves
     ("mid_f480", 4, [40, 9, 100, 3]),   # ... with gate and up blocks in separate waves
+    ("tiny_b4", 4, [20, 3, 50, 7]),     # 16-wide heads in 256-row tiles (one block per wave)
     ("llama7b", 1, [512]),     # the bench's shapes, tree and launch configuration
 ])
 def test_decoder_layer_matches_oracle(name, B, ns):
     _flush(f"decoder_layer {name} B={B} ns={ns}")
-    D = {"tiny": configs.TINY.dims,
+    D = {"tiny": configs.TINY.dims, "tiny_b4": configs.TINY.dims,
          "mid": configs.Dims(L=1, d=256, H=2, hd=128, F=512, V=512, K=3),
          "mid_f480": configs.Dims(L=1, d=256, H=2, hd=128, F=480, V=512, K=3),
          "llama7b": configs.LLAMA7B_T64.dims}[name]

@@ -85,7 +85,11 @@ static GemmCfg gemm_cfg(const mv_dims& D, int kind, int Mp) {
   GemmCfg c;
   c.MB = mvk::gemm_mb(Mp);
   switch (kind) {
-    case G_QKV: c.w = 4; c.nbw = 2; c.N = 3 * D.d; c.K = D.d; c.epi = mvk::EPI_QKV; break;
+    case G_QKV: {   // 128- and 256-row tiles: one block per wave, RoPE partners across waves
+      const bool split = c.MB >= 8 && (3 * D.d / 16 + 7) / 8 <= 256;
+      c.w = split ? 8 : 4; c.nbw = split ? 1 : 2; c.N = 3 * D.d; c.K = D.d; c.epi = mvk::EPI_QKV;
+      break;
+    }
     case G_O: c.w = 4; c.nbw = 1; c.N = D.d; c.K = D.d; c.epi = mvk::EPI_ADD; break;
     case G_GU: {
       // 128- and 256-row tiles: gate and up blocks in separate 8-wave

@@ -364,7 +364,10 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
       gr[i] = g.next_gain ? *reinterpret_cast<const uint4*>(g.next_gain + c) : uint4{0, 0, 0, 0};
     }
   }
-  if constexpr (EPI == EPI_QKV) {
+  // RoPE (cos, sin) of the lane's rows; 256-row tiles with one block per
+  // wave have no registers to hold them across the split-K exchange and load
+  // them after it
+  auto load_cs = [&]() {
     const int ci = (f0 % g.qkv.d) % g.qkv.hd % half;  // RoPE frequency index of both blocks
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb)
@@ -373,7 +376,9 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
         const int m = min(row0 + rb * 16 + r, g.M - 1);
         cs[rb][r] = rot ? g.qkv.rope[(size_t)m * half + ci] : make_float2(1.f, 0.f);
       }
-  }
+  };
+  constexpr bool CS_LATE = EPI == EPI_QKV && NBW == 1 && MB == 16;
+  if constexpr (EPI == EPI_QKV && !CS_LATE) load_cs();
 
   // ---- split-K: the last workgroup of the tile sums the splits in order
   if (g.splits > 1) {
@@ -628,41 +633,86 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
     // q rows, K pieces of 8 dims of one slot, V runs of 8 slots of one dim
     // (single elements where a run is not whole in this tile)
     const QkvArgs& q = g.qkv;
-    constexpr int TC = W * 32;                   // packed features of the tile
+    constexpr int TC = W * NBW * 16;             // packed features of the tile
     constexpr int LDT = TC + 8;                  // padded staging row (u16)
     u16* stg;
-    if constexpr (TR * LDT * 2 <= (int)sizeof(As)) {
+    if constexpr (NBW == 2 && TR * LDT * 2 <= (int)sizeof(As)) {
       stg = reinterpret_cast<u16*>(&As[0][0][0]);
-    } else {                                     // 256-row tiles: a buffer of its own
+    } else {        // 256-row tiles, or the RoPE partners parked in the operand LDS: a buffer of its own
       __shared__ u16 stg_own[TR * LDT];
       stg = stg_own;
     }
     const bool first = ((f0 % q.d) % q.hd) < half;    // block 0 holds the first half (narrow heads)
+    if constexpr (CS_LATE) load_cs();
+    if constexpr (NBW == 2) {
 #pragma unroll
-    for (int rb = 0; rb < MB; ++rb)
+      for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float y0 = acc[rb][0][r], y1 = acc[rb][1][r];
-        float s0 = 0.f, s1 = 0.f;
-        if (!wide) {             // uniform: 16-wide heads only
-          s0 = __shfl_xor(y0, 8, 64);
-          s1 = __shfl_xor(y1, 8, 64);
-        }
-        const float c = cs[rb][r].x, sn = cs[rb][r].y;
-        float o0 = y0, o1 = y1;
-        if (rot) {
-          if (wide) {            // (x_i, x_{i+hd/2}) -> (x_i c - x_{i+h} s, x_{i+h} c + x_i s)
-            o0 = y0 * c - y1 * sn;
-            o1 = y1 * c + y0 * sn;
-          } else {               // partners 8 lanes apart inside each block
-            o0 = first ? y0 * c - s0 * sn : y0 * c + s0 * sn;
-            o1 = first ? y1 * c - s1 * sn : y1 * c + s1 * sn;
+        for (int r = 0; r < 4; ++r) {
+          const float y0 = acc[rb][0][r], y1 = acc[rb][1][r];
+          float s0 = 0.f, s1 = 0.f;
+          if (!wide) {             // uniform: 16-wide heads only
+            s0 = __shfl_xor(y0, 8, 64);
+            s1 = __shfl_xor(y1, 8, 64);
           }
+          const float c = cs[rb][r].x, sn = cs[rb][r].y;
+          float o0 = y0, o1 = y1;
+          if (rot) {
+            if (wide) {            // (x_i, x_{i+hd/2}) -> (x_i c - x_{i+h} s, x_{i+h} c + x_i s)
+              o0 = y0 * c - y1 * sn;
+              o1 = y1 * c + y0 * sn;
+            } else {               // partners 8 lanes apart inside each block
+              o0 = first ? y0 * c - s0 * sn : y0 * c + s0 * sn;
+              o1 = first ? y1 * c - s1 * sn : y1 * c + s1 * sn;
+            }
+          }
+          const int rl = rb * 16 + 4 * (lane >> 4) + r;
+          stg[rl * LDT + wave * 32 + col] = f32_to_bf16(o0);
+          stg[rl * LDT + wave * 32 + 16 + col] = f32_to_bf16(o1);
         }
-        const int rl = rb * 16 + 4 * (lane >> 4) + r;
-        stg[rl * LDT + wave * 32 + col] = f32_to_bf16(o0);
-        stg[rl * LDT + wave * 32 + 16 + col] = f32_to_bf16(o1);
+    } else {
+      // one block per wave: with heads wider than 16 the RoPE partners of an
+      // even wave's block are the next (odd) wave's, in the same lanes; the
+      // odd waves park their accumulators in the operand LDS and the even
+      // waves rotate both blocks
+      static_assert(NBW == 2 || (W % 2 == 0 && (W / 2) * MB * 4 * 64 * 4 <= (int)sizeof(As)),
+                    "RoPE pairing fits the operand LDS");
+      float* pv = reinterpret_cast<float*>(&As[0][0][0]);
+      if (wide) {                // uniform
+        if (wave & 1) {
+#pragma unroll
+          for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pv[(((wave >> 1) * MB + rb) * 4 + r) * 64 + lane] = acc[rb][0][r];
+        }
+        __syncthreads();
+        if (!(wave & 1)) {
+#pragma unroll
+          for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float y0 = acc[rb][0][r], y1 = pv[(((wave >> 1) * MB + rb) * 4 + r) * 64 + lane];
+              const float c = cs[rb][r].x, sn = cs[rb][r].y;
+              const float o0 = rot ? y0 * c - y1 * sn : y0, o1 = rot ? y1 * c + y0 * sn : y1;
+              const int rl = rb * 16 + 4 * (lane >> 4) + r;
+              stg[rl * LDT + wave * 16 + col] = f32_to_bf16(o0);
+              stg[rl * LDT + wave * 16 + 16 + col] = f32_to_bf16(o1);
+            }
+        }
+      } else {
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float y0 = acc[rb][0][r];
+            const float s0 = __shfl_xor(y0, 8, 64);
+            const float c = cs[rb][r].x, sn = cs[rb][r].y;
+            const float o0 = rot ? (first ? y0 * c - s0 * sn : y0 * c + s0 * sn) : y0;
+            const int rl = rb * 16 + 4 * (lane >> 4) + r;
+            stg[rl * LDT + wave * 16 + col] = f32_to_bf16(o0);
+          }
       }
+    }
     __syncthreads();
     const int tc0 = nt * TC, mr0 = mt * TR;
     const int p_end = min(tc0 + TC, g.N);
@@ -766,6 +816,8 @@ static hipError_t launch_mb(const GemmArgs& g, dim3 grid, hipStream_t s) {
     if (g.epi == EPI_STORE) hipLaunchKernelGGL((gemm_kernel<MB, 8, 1, EPI_STORE>), grid, blk, 0, s, g);
     else if (MB >= 8 && g.epi == EPI_SWIGLU)
       hipLaunchKernelGGL((gemm_kernel<(MB >= 8 ? MB : 8), 8, 1, EPI_SWIGLU>), grid, blk, 0, s, g);
+    else if (MB >= 8 && g.epi == EPI_QKV)
+      hipLaunchKernelGGL((gemm_kernel<(MB >= 8 ? MB : 8), 8, 1, EPI_QKV>), grid, blk, 0, s, g);
     else return hipErrorInvalidValue;
   } else if constexpr (NBW == 1) {
     if (g.epi == EPI_STORE) hipLaunchKernelGGL((gemm_kernel<MB, W, 1, EPI_STORE>), grid, blk, 0, s, g);
