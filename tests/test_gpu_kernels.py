@@ -84,6 +84,10 @@ def _attention_case(D, B, T, ns, depth, topk, seed, cap=None):
     (64, 2, 1, 256, [300]),          # four mask words
     (128, 1, 1, 1, [100]),           # root only: a vanilla decode step
     (32, 2, 2, 17, [0, 5]),          # empty prefix for one sequence
+    # many (sequence, head, query block) triples, long trees
+    (128, 40, 1, 256, [1024]),       # 13B-width heads, 256-node tree
+    (64, 33, 1, 250, [17]),          # ragged last query block
+    (16, 64, 2, 80, [33, 7]),        # odd query-block count
 ])
 def test_tree_attention_matches_oracle(hd, H, B, T, ns):
     _flush(f"tree_attention hd={hd} H={H} B={B} T={T} ns={ns}")
