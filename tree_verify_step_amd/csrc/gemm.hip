@@ -296,13 +296,32 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
       const int h = PARTS == 1 ? 0 : sg;                   // part staged for chunk c + 1
       const int buf = c & 1;
       loadA(ar, c + 1, h);
+      // the next step's activation fragments are read from LDS before this
+      // step's MFMAs, so their latency hides behind them (tiles up to 64
+      // rows but gate/up, where it measured slower; the wider tiles have no
+      // registers to spare)
+      constexpr bool PIPE = MB <= 4 && EPI != EPI_SWIGLU;
+      const int apos0 = PARTS == 1 ? 0 : sg * SG;
+      bf16x8 a[MB];
+      if constexpr (PIPE) {
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb) a[rb] = As[buf][apos0 * MB + rb][lane];
+      }
 #pragma unroll
       for (int kk = 0; kk < SG; ++kk) {
         const int stage = PARTS == 1 ? sg * SG + kk : kk;
-        const int apos = PARTS == 1 ? kk : sg * SG + kk;
-        bf16x8 a[MB];
+        const int apos = apos0 + kk;
+        bf16x8 an[MB];
+        if constexpr (PIPE) {
+          if (kk + 1 < SG) {
 #pragma unroll
-        for (int rb = 0; rb < MB; ++rb) a[rb] = As[buf][apos * MB + rb][lane];
+            for (int rb = 0; rb < MB; ++rb) an[rb] = As[buf][(apos + 1) * MB + rb][lane];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        } else {
+#pragma unroll
+          for (int rb = 0; rb < MB; ++rb) a[rb] = As[buf][apos * MB + rb][lane];
+        }
 #pragma unroll
         for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
@@ -310,6 +329,12 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
         __builtin_amdgcn_sched_barrier(0);
         loadB(stage, lo + o * UO + sg * SG + kk + KC);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (PIPE) {
+          if (kk + 1 < SG) {
+#pragma unroll
+            for (int rb = 0; rb < MB; ++rb) a[rb] = an[rb];
+          }
+        }
       }
       storeA(ar, buf ^ 1, c + 1, h);
       if (PARTS == 1 || sg == NSEG - 1) __syncthreads();
