@@ -279,6 +279,8 @@ static int enq_layer(const mv_dims& D, int B, const mv_tree& t, const int32_t* n
   {   // compute units the QKV tiles leave idle read the prefix K/V ahead
     const GemmCfg c = gemm_cfg(D, G_QKV, round16(M));
     g.prefetch = std::max(0, (256 - c.ntiles * c.splits * c.mtiles) / (c.splits * c.mtiles));
+    // half the weight bytes one tile workgroup streams
+    g.pf_budget16 = (int)((size_t)c.N * c.K * 2 / ((size_t)c.ntiles * c.splits * c.mtiles) / 2 / 16);
   }
   if (want(MV_K_QKV)) {
     prof_begin(s);

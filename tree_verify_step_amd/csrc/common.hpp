@@ -148,7 +148,8 @@ struct GemmArgs {
   int* counters;     // split-K arrival counters [tiles], zero between launches
   QkvArgs qkv;
   int prefetch;      // QKV: extra grid columns of workgroups that read this
-                     //   layer's cached prefix K/V ahead of the attention launch
+                     //   layer's cached prefix K/V ahead of the attention launch,
+  int pf_budget16;   //   at most this many 16-byte pieces each
 };
 
 int gemm_mb(int Mp);                                  // 16-row blocks per tile

@@ -99,17 +99,20 @@ int gemm_kc(int MB) { return MB <= 4 ? 8 : 32 / MB; }   // k-blocks per activati
 // contiguous at the start of the block) and discards the values.  Workgroups
 // appended to the QKV launch, on compute units its tiles leave idle, do this
 // so that the attention launch that follows finds the prefix in the
-// memory-side cache instead of waiting on HBM.
-__device__ __forceinline__ void prefetch_prefix_kv(const QkvArgs& q, int p, int P) {
+// memory-side cache instead of waiting on HBM.  Each reads at most budget16
+// 16-byte pieces, so that it ends well before the tiles do (long prefixes
+// are then read in part).
+__device__ __forceinline__ void prefetch_prefix_kv(const QkvArgs& q, int p, int P, int budget16) {
   uint32_t sink = 0;
   const int ranges = 2 * q.B * q.H;
-  for (int r = p; r < ranges; r += P) {
+  for (int r = p; r < ranges && budget16 > 0; r += P) {
     const int pair = r >> 1, b = pair / q.H;
     const int n = min(max(q.n_prefix[b], 0), q.cap - q.T);
     const int slots = (r & 1) ? ((n + 7) & ~7) : ((n + 31) & ~31);
     const uint4* src = reinterpret_cast<const uint4*>(((r & 1) ? q.vcache : q.kcache) +
                                                       (size_t)pair * q.cap * q.hd);
-    const int n16 = slots * q.hd / 8;                 // 16-byte pieces
+    const int n16 = min(slots * q.hd / 8, budget16);  // 16-byte pieces (within the budget)
+    budget16 -= n16;
     int i = threadIdx.x;
     for (; i + 7 * (int)blockDim.x < n16; i += 8 * blockDim.x) {
       uint4 v[8];
@@ -153,7 +156,7 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
   if constexpr (EPI == EPI_QKV) {
     if ((int)blockIdx.x >= NT) {               // appended prefetch workgroups
       prefetch_prefix_kv(g.qkv, ((int)blockIdx.x - NT) * gridDim.y + blockIdx.y,
-                         ((int)gridDim.x - NT) * gridDim.y);
+                         ((int)gridDim.x - NT) * gridDim.y, g.pf_budget16);
       return;
     }
   }
