@@ -11,12 +11,17 @@
 //    keeps a register ring of KC k-blocks of them in flight (consumed, then
 //    refilled in place; scheduling barriers keep the refill after the MFMAs
 //    that read the stage, so no register copies undo the prefetch).
-//  * The activation operand is staged once per workgroup in LDS, AH ring
-//    lengths (AH * KC k-blocks) per chunk, double-buffered, and shared by the
-//    W waves; k-blocks past the range are staged as zeros, so the main loop
-//    has no branches and the compiler's wait counts stay partial.  The
-//    unsplit gate/up GEMM takes two ring lengths per chunk (half the
-//    barriers); the split GEMMs, whose k-ranges are short, take one.
+//  * The activation operand is staged once per workgroup in LDS in chunks of
+//    KCA k-blocks, double-buffered, and shared by the W waves; k-blocks past
+//    the range are staged as zeros, so the main loop has no branches and the
+//    compiler's wait counts stay partial.  The unsplit gate/up GEMM takes two
+//    ring lengths per chunk (half the barriers), the split GEMMs, whose
+//    k-ranges are short, one, and the 128- and 256-row tiles 32 KiB chunks
+//    inside a ring length.  In 64-row tiles the next step's fragments are
+//    read from LDS before the current step's MFMAs.
+//  * 128- and 256-row tiles give each wave one column block (gate/up: gate
+//    and up blocks in different waves; QKV: RoPE partners in neighbouring
+//    waves, exchanged through LDS), which leaves registers for an 8-deep ring.
 //  * K is split over `splits` workgroups when the column tiles alone cannot
 //    fill the chip.  Each split writes its partial tile with write-through
 //    (system-scope) stores, waits for them, and bumps the tile's arrival
@@ -26,12 +31,14 @@
 // RMSNorm is folded in: the operand of a normalised GEMM is bf16(x * gain)
 // and the per-row factor 1/sqrt(mean(x^2) + 1e-5) is applied to the
 // accumulators, from row sums of squares that the producing GEMM wrote per
-// column tile (summed here in tile order).
+// column tile (requested with the first weight chunk, summed after the main
+// loop).
 // Epilogues:
 //   STORE   out = y                          (LM head logits)
 //   ADD     x += y (residual stream: O-proj, down); optionally the next
 //           norm's operand bf16(x * gain) and the rows' sums of squares
-//   SWIGLU  wave owns gate block j and up block j; h = SiLU(g) * u -> bf16
+//   SWIGLU  h = SiLU(g) * u -> bf16 (gate block j and up block j in one
+//           wave, or in waves j and j + W/2)
 //   QKV     RoPE on q, k at each row's position; q -> bf16 rows; k, v ->
 //           KV cache slot n + node index
 #include "common.hpp"
