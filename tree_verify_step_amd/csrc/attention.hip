@@ -268,18 +268,31 @@ __global__ __launch_bounds__(NW * 64) void tree_attention_kernel(
   }
 }
 
+// Launches with many (sequence, head, query block) triples use 4-wave
+// workgroups: two of them fit a compute unit where one 8-wave workgroup does
+// (212 registers a lane), so more K/V tiles are in flight per unit.
+template <int HD>
+static void launch_attention_hd(const u16* q, const u16* kc, const u16* vc, const int32_t* n_prefix,
+                                const uint64_t* anc, int B, int T, int H, int cap, int mw,
+                                u16* out, int packed, hipStream_t s) {
+  const int QB = (T + 15) / 16, pairs = B * H;
+  const dim3 grid(8 * ((pairs + 7) / 8) * QB);
+  if ((size_t)pairs * QB > 512)
+    hipLaunchKernelGGL((tree_attention_kernel<HD, 4>), grid, dim3(256), 0, s, q, kc, vc, n_prefix,
+                       anc, B, T, H, cap, mw, out, packed);
+  else
+    hipLaunchKernelGGL((tree_attention_kernel<HD, 8>), grid, dim3(512), 0, s, q, kc, vc, n_prefix,
+                       anc, B, T, H, cap, mw, out, packed);
+}
+
 hipError_t launch_attention(const u16* q, const u16* kc, const u16* vc, const int32_t* n_prefix,
                             const uint64_t* anc, int B, int T, int H, int hd, int cap, int mw,
                             u16* out, int packed, hipStream_t s) {
-  constexpr int NW = 8;
-  const int QB = (T + 15) / 16, pairs = B * H;
-  const dim3 grid(8 * ((pairs + 7) / 8) * QB);
-  const dim3 blk(NW * 64);
   switch (hd) {
-    case 16: hipLaunchKernelGGL((tree_attention_kernel<16, NW>), grid, blk, 0, s, q, kc, vc, n_prefix, anc, B, T, H, cap, mw, out, packed); break;
-    case 32: hipLaunchKernelGGL((tree_attention_kernel<32, NW>), grid, blk, 0, s, q, kc, vc, n_prefix, anc, B, T, H, cap, mw, out, packed); break;
-    case 64: hipLaunchKernelGGL((tree_attention_kernel<64, NW>), grid, blk, 0, s, q, kc, vc, n_prefix, anc, B, T, H, cap, mw, out, packed); break;
-    case 128: hipLaunchKernelGGL((tree_attention_kernel<128, NW>), grid, blk, 0, s, q, kc, vc, n_prefix, anc, B, T, H, cap, mw, out, packed); break;
+    case 16: launch_attention_hd<16>(q, kc, vc, n_prefix, anc, B, T, H, cap, mw, out, packed, s); break;
+    case 32: launch_attention_hd<32>(q, kc, vc, n_prefix, anc, B, T, H, cap, mw, out, packed, s); break;
+    case 64: launch_attention_hd<64>(q, kc, vc, n_prefix, anc, B, T, H, cap, mw, out, packed, s); break;
+    case 128: launch_attention_hd<128>(q, kc, vc, n_prefix, anc, B, T, H, cap, mw, out, packed, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
