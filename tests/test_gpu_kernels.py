@@ -223,7 +223,9 @@ def test_decoder_layer_matches_oracle(name, B, ns):
 # ---------------------------------------------------------------- heads
 
 @pytest.mark.parametrize("B,d,V,K,s", [(1, 64, 512, 3, 2), (1, 256, 1024, 4, 10), (4, 128, 640, 4, 10),
-                                        (4, 6656, 640, 2, 10)])   # 33B width: 104 KiB of inputs in LDS
+                                        (4, 6656, 640, 2, 10),    # 33B width: 104 KiB of inputs in LDS
+                                        (1, 64, 40960, 2, 10),    # 16 logits a lane in top-s stage 1
+                                        (1, 64, 131072, 2, 8)])   # > 64 stage-1 waves: sorted merge
 def test_medusa_heads_match_oracle(B, d, V, K, s):
     _flush(f"medusa_heads B={B} d={d} V={V} K={K} s={s}")
     D = configs.Dims(L=1, d=d, H=d // 64, hd=64, F=64, V=V, K=K)
