@@ -174,6 +174,7 @@ def _layer_case(D, B, ns, paths_per_seq, topk, seed, gain_std=0.1):
     ("mid_f480", 1, [40]),     # F % 64 == 32: the last gate/up tile has idle waves
     ("mid_f480", 4, [40, 9, 100, 3]),   # ... with gate and up blocks in separate waves
     ("tiny_b4", 4, [20, 3, 50, 7]),     # 16-wide heads in 256-row tiles (one block per wave)
+    ("wide_f", 2, [30, 9]),    # 1026 gate/up blocks: 10-wave tiles of 5 feature blocks
     ("llama7b", 1, [512]),     # the bench's shapes, tree and launch configuration
 ])
 def test_decoder_layer_matches_oracle(name, B, ns):
@@ -181,6 +182,7 @@ def test_decoder_layer_matches_oracle(name, B, ns):
     D = {"tiny": configs.TINY.dims, "tiny_b4": configs.TINY.dims,
          "mid": configs.Dims(L=1, d=256, H=2, hd=128, F=512, V=512, K=3),
          "mid_f480": configs.Dims(L=1, d=256, H=2, hd=128, F=480, V=512, K=3),
+         "wide_f": configs.Dims(L=1, d=128, H=1, hd=128, F=16416, V=512, K=3),
          "llama7b": configs.LLAMA7B_T64.dims}[name]
     D = configs.Dims(L=1, d=D.d, H=D.H, hd=D.hd, F=D.F, V=D.V, K=D.K)
     rng = np.random.default_rng(11)

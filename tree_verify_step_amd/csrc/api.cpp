@@ -92,11 +92,13 @@ static GemmCfg gemm_cfg(const mv_dims& D, int kind, int Mp) {
     }
     case G_O: c.w = 4; c.nbw = 1; c.N = D.d; c.K = D.d; c.epi = mvk::EPI_ADD; break;
     case G_GU: {
-      // 128- and 256-row tiles: gate and up blocks in separate 8-wave
-      // workgroups' waves (deeper weight ring) while those tiles fit the
-      // compute units in one round; otherwise two blocks per wave
-      const bool split = c.MB >= 8 && (D.F / 16 + 3) / 4 <= 256;
-      c.w = split ? 8 : 4; c.nbw = split ? 1 : 2; c.N = D.F; c.K = D.d;
+      // 128- and 256-row tiles: gate and up blocks in separate waves of 8-
+      // or 10-wave workgroups (4 or 5 feature blocks a tile; deeper weight
+      // ring) while those tiles fit the compute units in one round;
+      // otherwise two blocks per wave
+      const int fw = (D.F / 16 + 3) / 4 <= 256 ? 4 : (D.F / 16 + 4) / 5 <= 256 ? 5 : 0;
+      const bool split = c.MB >= 8 && fw > 0;
+      c.w = split ? 2 * fw : 4; c.nbw = split ? 1 : 2; c.N = D.F; c.K = D.d;
       c.epi = mvk::EPI_SWIGLU;
       break;
     }

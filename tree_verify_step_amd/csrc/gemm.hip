@@ -145,8 +145,7 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
   constexpr int PARTS = KCA / SG;
   constexpr int APS = SG * MB;                 // 1 KiB activation pieces per segment
   constexpr int APC = KCA * MB;                // ... per chunk
-  constexpr int AI = APS / W;                  // pieces staged per thread per segment
-  static_assert(APS % W == 0, "segment pieces must divide among the waves");
+  constexpr int AI = (APS + W - 1) / W;        // pieces staged per thread per segment
   static_assert(PARTS <= 2 && (KCA < KC ? KC % KCA == 0 : KCA % KC == 0), "chunk and ring align");
   constexpr int TR = MB * 16;                  // rows of a tile
   __shared__ bf16x8 As[2][APC][64];            // [buf][kl * MB + rb][lane]
@@ -202,7 +201,10 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
   // wave waits on them before streaming.  Otherwise (few lanes per row, or
   // many tiles) one lane per row sums them here, before the main loop.
   constexpr int SS_Q = 4;                              // f32x4 per lane
-  constexpr int LPR = TR <= W * 64 ? ((W * 64) / TR < 16 ? (W * 64) / TR : 16) : 0;   // lanes per row
+  // lanes per row: a power of two up to one DPP row (16), as the reduction
+  // below assumes; rows per pass = W * 64 / LPR >= TR
+  constexpr int LPR_MAX = TR <= W * 64 ? (W * 64) / TR : 0;
+  constexpr int LPR = LPR_MAX >= 16 ? 16 : LPR_MAX >= 8 ? 8 : LPR_MAX >= 4 ? 4 : LPR_MAX >= 2 ? 2 : LPR_MAX;
   const int ss_n4 = g.ss_tiles >> 2;
   const bool ss_late = g.ss != nullptr && LPR > 0 && ss_n4 <= LPR * SS_Q;
   if (g.ss && !ss_late) {
@@ -241,7 +243,8 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
   auto loadA = [&](bf16x8 (&dst)[AI], int c, int h) {
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
-      const int piece = i * W + wave;
+      // waves past the segment's pieces (when W does not divide them) repeat the last
+      const int piece = APS % W == 0 ? i * W + wave : min(i * W + wave, APS - 1);
       const int kl = h * SG + piece / MB, rb = piece % MB;
       const int k = min(lo + c * KCA + kl, hi - 1);
       const int rbg = min(mt * MB + rb, MBtot - 1);
@@ -253,7 +256,8 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
     for (int i = 0; i < AI; ++i) {
       const int piece = i * W + wave;
       const int kl = h * SG + piece / MB;
-      As[buf][h * APS + piece][lane] = (lo + c * KCA + kl < hi) ? src[i] : bf16x8{};
+      if (APS % W == 0 || piece < APS)
+        As[buf][h * APS + piece][lane] = (lo + c * KCA + kl < hi) ? src[i] : bf16x8{};
     }
   };
   bf16x8 br[KC][NBW];
@@ -605,9 +609,14 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
     // same lanes: the up waves park their accumulators in the operand LDS,
     // the gate waves form h = SiLU(gate) * up and stage it as bf16, then
     // write whole 16-byte pieces (8 features of one row)
-    static_assert(FW * MB * 4 * 64 * 4 <= (int)sizeof(As) && FW * TR * 16 * 2 <= (int)sizeof(As),
-                  "SwiGLU pairing fits the operand LDS");
-    float* upv = reinterpret_cast<float*>(&As[0][0][0]);
+    static_assert(FW * TR * 16 * 2 <= (int)sizeof(As), "SwiGLU staging fits the operand LDS");
+    float* upv;
+    if constexpr (FW * MB * 4 * 64 * 4 <= (int)sizeof(As)) {
+      upv = reinterpret_cast<float*>(&As[0][0][0]);
+    } else {                                     // 10-wave 256-row tiles: a buffer of its own
+      __shared__ float upv_own[FW * MB * 4 * 64];
+      upv = upv_own;
+    }
     if (wave >= FW) {
 #pragma unroll
       for (int rb = 0; rb < MB; ++rb)
@@ -854,6 +863,10 @@ static hipError_t launch_mb(const GemmArgs& g, dim3 grid, hipStream_t s) {
     else if (MB >= 8 && g.epi == EPI_QKV)
       hipLaunchKernelGGL((gemm_kernel<(MB >= 8 ? MB : 8), 8, 1, EPI_QKV>), grid, blk, 0, s, g);
     else return hipErrorInvalidValue;
+  } else if constexpr (NBW == 1 && W == 10) {    // gate/up of wide tiles, 5 features blocks a tile
+    if (MB >= 8 && g.epi == EPI_SWIGLU)
+      hipLaunchKernelGGL((gemm_kernel<(MB >= 8 ? MB : 8), 10, 1, EPI_SWIGLU>), grid, blk, 0, s, g);
+    else return hipErrorInvalidValue;
   } else if constexpr (NBW == 1) {
     if (g.epi == EPI_STORE) hipLaunchKernelGGL((gemm_kernel<MB, W, 1, EPI_STORE>), grid, blk, 0, s, g);
     else if (g.epi == EPI_ADD) hipLaunchKernelGGL((gemm_kernel<MB, W, 1, EPI_ADD>), grid, blk, 0, s, g);
@@ -885,6 +898,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   const dim3 grid(ntiles + (g.epi == EPI_QKV ? g.prefetch : 0), g.splits, mtiles);
   if (g.w == 4 && g.nbw == 1) return launch_w<4, 1>(g, MB, grid, s);
   if (g.w == 8 && g.nbw == 1) return launch_w<8, 1>(g, MB, grid, s);
+  if (g.w == 10 && g.nbw == 1) return launch_w<10, 1>(g, MB, grid, s);
   if (g.w == 4 && g.nbw == 2) return launch_w<4, 2>(g, MB, grid, s);
   return hipErrorInvalidValue;
 }
