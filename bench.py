@@ -181,8 +181,8 @@ def cpu_baseline(w, n0, sample_layers=2):
     """The oracle (float64 NumPy, as it stands) on a bounded sample of one
     step of workload `w`: all Medusa heads with top-s and tree fill,
     `sample_layers` of the L decoder layers over the whole tree against an
-    n0-token prefix cache, final norm + LM head, greedy acceptance.  The step
-    time is scaled to all L layers."""
+    n0-token prefix cache, final norm + LM head, the workload's acceptance
+    rule.  The step time is scaled to all L layers."""
     import numpy as np
     from oracle import accept as oa
     from oracle import heads as oh
@@ -220,7 +220,12 @@ def cpu_baseline(w, n0, sample_layers=2):
     t2 = time.perf_counter()
     hn = om.rmsnorm(x, Wt.get("final_norm"))
     logits = hn @ om.f64(Wt.get("lm_head")).T
-    oa.greedy_accept(t, tok, logits)
+    if w.accept == "greedy":
+        oa.greedy_accept(t, tok, logits)
+    elif w.accept == "typical":
+        oa.typical_accept(t, tok, logits, w.temperature, w.eps, w.delta)
+    else:
+        oa.reject_accept(t, tok, logits, w.temperature, rng.random(t.T))
     t3 = time.perf_counter()
     per_layer = (t2 - t1) / sample_layers
     step = (t1 - t0) + D.L * per_layer + (t3 - t2)
@@ -317,10 +322,12 @@ def main() -> int:
         f"B={B} n0={n0} cap={cap}")
     t_setup = time.perf_counter()
     dw = rt.DeviceWeights(D, None, seed=w.seed_weights, std=w.init_std)
-    acc = tv.AcceptParams(mode=tv.ACCEPT_GREEDY if w.accept == "greedy" else tv.ACCEPT_TYPICAL,
+    mode = {"greedy": tv.ACCEPT_GREEDY, "typical": tv.ACCEPT_TYPICAL,
+            "reject": tv.ACCEPT_REJECT}[w.accept]
+    acc = tv.AcceptParams(mode=mode,
                           root_mode=tv.ROOT_ARGMAX if w.root == "argmax" else tv.ROOT_SAMPLE,
                           temperature=w.temperature, eps=w.eps, delta=w.delta)
-    u = synth.uniform_draws(w, K + W + P + 4)
+    u = synth.uniform_draws(w, K + W + P + 4, T if w.accept == "reject" else 0)
     sess = rt.Session(D, B, T, s, cap, dw, trees, acc, u_draws=u)
     sess.prefill(ids)
     torch.cuda.synchronize()

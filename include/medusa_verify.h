@@ -71,7 +71,7 @@ typedef enum {
   MV_OK = 0,
   MV_EINVAL = -1,        /* bad scalar argument or null required pointer */
   MV_EUNSUPPORTED = -2,  /* shape outside what the kernels implement */
-  MV_ECAPACITY = -3,     /* n + T would exceed the cache capacity */
+  MV_ECAPACITY = -3,     /* n + T would exceed the cache capacity, or u_draws ran out */
   MV_EWORKSPACE = -4,    /* workspace smaller than mv_workspace_size() */
   MV_EHIP = -5,          /* a HIP runtime call failed (detail in mv_last_error) */
   MV_ETREE = -6          /* invalid tree (not prefix-closed, too deep, ...) */
@@ -81,10 +81,12 @@ typedef enum {
 #define MV_MAX_DEPTH 16     /* tree depth (<= number of Medusa heads used) */
 #define MV_MAX_TOPK 16      /* candidates per head */
 #define MV_MAX_BATCH 4      /* sequences per call (Medusa head GEMV) */
+#define MV_MAX_VOCAB 262144 /* vocabulary (inverse-CDF draws scan 1024 blocks of 256 ids) */
 #define MV_HEADS_LDS_MAX (128 * 1024)  /* head GEMV: B * d * 4 bytes of input rows in LDS */
 
 #define MV_ACCEPT_GREEDY 0
 #define MV_ACCEPT_TYPICAL 1
+#define MV_ACCEPT_REJECT 2
 #define MV_ROOT_ARGMAX 0
 #define MV_ROOT_SAMPLE 1
 
@@ -92,7 +94,8 @@ typedef enum {
 #define MV_PACK_QKV 1
 
 /* Backbone and head shapes.  Multi-head attention: H * hd == d.
- * Supported: d % 64 == 0, F % 32 == 0, V % 64 == 0, hd in {16,32,64,128},
+ * Supported: d % 64 == 0, F % 32 == 0, V % 64 == 0, V <= MV_MAX_VOCAB,
+ * hd in {16,32,64,128},
  * 1 <= K <= MV_MAX_DEPTH. */
 typedef struct {
   int32_t L, d, H, hd, F, V, K;
@@ -136,7 +139,11 @@ typedef struct {
  * temperature) of the parent's row and H(q) = -sum q log(q + 1e-5).
  * root_mode ARGMAX: next root = argmax of the best node's row; SAMPLE: the
  * smallest id whose cumulative softmax(z / temperature) mass (id order)
- * exceeds the step's uniform draw.  temperature > 0 for TYPICAL / SAMPLE. */
+ * exceeds the step's uniform draw.  temperature > 0 for TYPICAL / SAMPLE.
+ * REJECT: rejection sampling (speculative sampling: lecture note section
+ * 二.3; speculative-decoding tutorial, Maths) with the fixed top-s
+ * candidates as point-mass drafts (see mv_accept_reject); the next root is
+ * the walk's final draw and root_mode is not used; temperature > 0. */
 typedef struct {
   int32_t mode;
   int32_t root_mode;
@@ -239,7 +246,10 @@ MV_API int mv_lm_head(const mv_dims* dims, int32_t M, const float* x, const void
  * best node v* = deepest accepted node (TYPICAL: then larger summed
  * log-probability of the accepted candidates; then lower index).
  * logits: device fp32 [B][T][V]; tree_tok: device int32 [B][T];
- * u: device double [B] uniform draws in [0,1) (SAMPLE only, else NULL).
+ * u: device double [B] uniform draws in [0,1) (SAMPLE only, else NULL);
+ * REJECT: device double [B][T], as mv_accept_reject takes them.
+ * REJECT is mv_accept_reject with no draft logits (the margin holds its
+ * values); eps, delta and root_mode are not read.
  * Outputs (device): accept_len [B] (= depth of v*), path [B][depth+1] (node
  * indices root..v*, then -1), best [B], next_root [B]; optional: emitted
  * [B][depth+1] (tokens of the path, then -1), margin double [B][T+1]
@@ -254,6 +264,44 @@ MV_API int mv_accept(int32_t B, int32_t T, int32_t V, int32_t d, const float* lo
                      const void* final_norm, void* h_last, void* ws, size_t ws_bytes,
                      void* stream);
 
+/* Rejection-sampling acceptance (speculative sampling: lecture note section
+ * 二.3, two-word example; speculative-decoding tutorial, Concept and Maths).
+ * The pages give the chain rule: a draft x drawn from q is kept against the
+ * target p with probability min(1, p(x)/q(x)); the first rejection is
+ * replaced by a draw from max(0, p - q) normalised and ends the pass; when
+ * all are kept a bonus token is drawn from the target.  Tree reading: at
+ * the current node (p = softmax(logits[node] / temperature)) the children
+ * are tried in node order against the running residual r (p at first); a
+ * kept child becomes the current node, a rejection sets r to the
+ * correction's residual and the next sibling is tried; with no child kept
+ * (or at a leaf) the next root is the inverse-CDF draw (id order) from r.
+ * A residual with no mass left falls back to the node's p.  Candidate
+ * tokens outside [0, V) are never kept.
+ * draft_logits NULL: candidates are fixed (top-s), their draft a point mass:
+ *   x is kept with probability r(x) and a rejection removes x from r.
+ * draft_logits device fp32 [B][tree->depth][V]: children at depth k use
+ *   q = softmax(draft_logits[b][k-1] / temperature) (candidates drawn from
+ *   the heads).
+ * u: device double [B][T] uniform draws in [0,1): u[b][v] decides candidate
+ * v (kept iff u < keep probability), u[b][0] makes the final draw.
+ * Outputs as mv_accept: accept_len [B], path [B][depth+1], best [B] (the
+ * last kept node), next_root [B]; optional emitted [B][depth+1], margin
+ * double [B][T+1] (u - keep probability for tested candidates, +inf
+ * elsewhere; [T]: the final draw's distance to its bracketing cumulative
+ * sums) and h_last (given x, final_norm) as mv_accept.
+ * Workspace (each part 256-aligned): row argmax int32 [B*T] and row stats
+ * double [B*T][3]; with draft logits also argmax int32 [B*depth], stats
+ * double [B*depth][3] of the draft rows and residuals double [B][2][V]:
+ * align256(4*B*T) + align256(24*B*T), plus align256(4*B*depth) +
+ * align256(24*B*depth) + 16*B*V with draft logits.  temperature > 0.
+ * Work is one workgroup per sequence after a pass over the T rows. */
+MV_API int mv_accept_reject(int32_t B, int32_t T, int32_t V, int32_t d, const float* logits,
+                            const mv_tree* tree, const int32_t* tree_tok, double temperature,
+                            const float* draft_logits, const double* u, int32_t* accept_len,
+                            int32_t* path, int32_t* best, int32_t* next_root, int32_t* emitted,
+                            double* margin, const float* x, const void* final_norm, void* h_last,
+                            void* ws, size_t ws_bytes, void* stream);
+
 /* KV compaction (Algorithm step 6; Medusa paper digest, Pitfalls): for every
  * layer, sequence b and m = 0..accept_len[b]: slot n[b] + m <- slot n[b] +
  * path[b][m] (K and V; all sources read before any destination is written),
@@ -266,8 +314,11 @@ MV_API int mv_kv_compact(const mv_kv* kv, const int32_t* path, int32_t path_stri
 
 /* Everything one decode step reads and writes (all device, caller-owned).
  * State carried between steps: n_prefix [B], root_tok [B], h_last bf16
- * [B][d], the KV cache, and (SAMPLE roots) the draw counter u_index (int32,
- * device) into u_draws double [n_draws][B]. */
+ * [B][d], the KV cache, and (SAMPLE roots, REJECT acceptance) the draw
+ * counter u_index (int32, device) into u_draws: double [n_draws][B] for
+ * SAMPLE roots, [n_draws][B][T] for REJECT (draw i feeds step i's
+ * candidates and final draw as mv_accept_reject's u; draw 0, entry
+ * [0][b][0], samples the root after prefill). */
 typedef struct {
   mv_dims dims;
   int32_t B, T, s;                 /* s: candidates per head (topk) */
@@ -283,8 +334,8 @@ typedef struct {
   int32_t* n_prefix;
   int32_t* root_tok;
   void* h_last;
-  const double* u_draws;           /* SAMPLE only */
-  int32_t* u_index;                /* SAMPLE only */
+  const double* u_draws;           /* SAMPLE roots or REJECT only */
+  int32_t* u_index;                /* SAMPLE roots or REJECT only */
   int32_t n_draws;
   /* per-step outputs */
   int32_t* tree_tok;               /* [B][T] */
@@ -311,14 +362,18 @@ MV_API void mv_ctx_destroy(mv_ctx* ctx);
 /* Prefill: run the prompts through the backbone in chunks of up to T tokens
  * as chain trees (parent = previous token, so the tree mask is the causal
  * mask), filling KV slots [0, n), then set h_last, root_tok (ARGMAX or SAMPLE
- * with draw u_draws[u_index]) and n_prefix = n.  ids: device int32 [B][ld];
+ * with draw 0 of u_draws; REJECT acceptance always samples) and
+ * n_prefix = n.  ids: device int32 [B][ld];
  * n_ids: host int32 [B] (1 <= n <= cap - T); counter u_index is set to 1. */
 MV_API int mv_prefill(mv_ctx* ctx, const int32_t* ids, int32_t ld, const int32_t* n_ids,
                       void* stream);
 
 /* One tree-verify step from the device-resident state.  graph != 0: the
  * step is captured into a hipGraph on the first call and replayed after;
- * graph == 0: the kernels are enqueued directly. */
+ * graph == 0: the kernels are enqueued directly.  A step that draws
+ * (SAMPLE roots, REJECT acceptance) uses the next row of u_draws; once the
+ * prefill's row and one row per step have used all n_draws rows, the call
+ * fails with MV_ECAPACITY and enqueues nothing. */
 MV_API int mv_step(mv_ctx* ctx, int32_t graph, void* stream);
 
 /* Launch-group kinds reported by mv_step_profile. */

@@ -34,7 +34,9 @@ def _session(w, cap, debug=True, u=None):
     paths = [synth.tree_paths(w, b) for b in range(w.batch)]
     trees = rt.DeviceTrees(paths, s)
     dw = rt.DeviceWeights(D, Wt.get)
-    p = tv.AcceptParams(mode=tv.ACCEPT_GREEDY if w.accept == "greedy" else tv.ACCEPT_TYPICAL,
+    mode = {"greedy": tv.ACCEPT_GREEDY, "typical": tv.ACCEPT_TYPICAL,
+            "reject": tv.ACCEPT_REJECT}[w.accept]
+    p = tv.AcceptParams(mode=mode,
                         root_mode=tv.ROOT_ARGMAX if w.root == "argmax" else tv.ROOT_SAMPLE,
                         temperature=w.temperature, eps=w.eps, delta=w.delta)
     sess = rt.Session(D, w.batch, trees.T, s, cap, dw, trees, p, u_draws=u, debug=debug)
@@ -47,21 +49,26 @@ def _params(w):
 
 
 @pytest.mark.parametrize("graph", [False, True])
-@pytest.mark.parametrize("variant", ["greedy", "typical_sample"])
+@pytest.mark.parametrize("variant", ["greedy", "typical_sample", "reject"])
 def test_tiny_decode_teacher_forced(graph, variant):
     w = configs.TINY.with_(weight_dtype="bf16")
     if variant == "typical_sample":
         w = w.with_(accept="typical", root="sample", temperature=0.7, eps=0.09, delta=0.3)
+    if variant == "reject":
+        w = w.with_(accept="reject", root="sample", temperature=0.7)
+    reject = w.accept == "reject"
     print(f"tiny decode teacher-forced graph={graph} {variant}", flush=True)
     D = w.dims
     cap = 256
-    u = synth.uniform_draws(w, w.steps + 1)
+    nodes = otree.compile_tree(synth.tree_paths(w, 0)).T if reject else 0
+    u = synth.uniform_draws(w, w.steps + 1, nodes)
+    u_root = u[:, :, 0] if reject else u          # [draw][b]: the prefill root's draw
     Wt, paths, sess = _session(w, cap, u=u)
     ids = synth.prefix_ids(w)[0]
     sess.prefill([ids])
     torch.cuda.synchronize()
     p = _params(w)
-    st = od.prefill(Wt.get, D.L, D.H, ids, cap, D.hd, p, u=u[0, 0])
+    st = od.prefill(Wt.get, D.L, D.H, ids, cap, D.hd, p, u=u_root[0, 0])
     t = otree.compile_tree(paths[0])
     assert int(sess.n_prefix[0]) == len(ids)
     np.testing.assert_allclose(sess.h_last[0].float().cpu().numpy(), st.h_last, atol=TOL)
@@ -71,10 +78,11 @@ def test_tiny_decode_teacher_forced(graph, variant):
     if w.root == "argmax":
         assert int(sess.root_tok[0]) == oa.argmax_lowest(last)
     else:
-        want, margin = oa.sample_root(last, w.temperature, u[0, 0])
+        want, margin = oa.sample_root(last, w.temperature, u_root[0, 0])
         if margin > 1e-6:
             assert int(sess.root_tok[0]) == want
     st.t0 = int(sess.root_tok[0])            # follow the GPU's root (checked below per step)
+    near = 0
     for step in range(w.steps):
         sess.step(graph=graph)
         torch.cuda.synchronize()
@@ -94,13 +102,27 @@ def test_tiny_decode_teacher_forced(graph, variant):
         # acceptance on the GPU's logits is bit-exact
         if w.accept == "greedy":
             res = oa.greedy_accept(t, tok, gl)
+        elif reject:
+            res = oa.reject_accept(t, tok, gl, w.temperature, u[step + 1, 0])
+            m = res.margin
+            if np.any(np.abs(m[np.isfinite(m)]) <= 1e-9):   # a tie up to rounding: follow the GPU
+                near += 1
+                assert near <= 2
+                res = None
         else:
             res = oa.typical_accept(t, tok, gl, w.temperature, w.eps, w.delta)
+        if res is None:
+            L_ = int(sess.accept_len[0])
+            pth = [int(v) for v in sess.path[0].cpu().numpy()[:L_ + 1]]
+            res = oa.AcceptResult(ok=None, best=pth[-1], path=pth, accept_len=L_)
         assert int(sess.accept_len[0]) == res.accept_len, step
         np.testing.assert_array_equal(sess.path[0].cpu().numpy()[:res.accept_len + 1], res.path)
         np.testing.assert_array_equal(sess.emitted[0].cpu().numpy()[:res.accept_len + 1],
                                       tok[res.path])
-        if w.root == "argmax":
+        if reject:
+            if res.next_root is not None:
+                assert int(sess.root_tok[0]) == res.next_root, step
+        elif w.root == "argmax":
             assert int(sess.root_tok[0]) == oa.argmax_lowest(gl[res.best])
         else:
             want, margin = oa.sample_root(gl[res.best], w.temperature, u[step + 1, 0])
@@ -164,7 +186,8 @@ def stages(layers: int) -> int:
     return 2 * layers + 1
 
 
-@pytest.mark.parametrize("wname", [configs.LLAMA7B_T64.name, configs.LLAMA7B_T64_LONG_TYPICAL.name])
+@pytest.mark.parametrize("wname", [configs.LLAMA7B_T64.name, configs.LLAMA7B_T64_LONG_TYPICAL.name,
+                                   configs.LLAMA7B_T64_REJECT.name])
 def test_full_dims_step_two_layers_teacher_forced(wname):
     """Two steps at the 7B dims (d = 4096, 32 x 128 heads, FFN 11008,
     V = 32000, K = 4 Medusa heads, the workload's 64-node sparse tree; prefix
@@ -190,10 +213,13 @@ def test_full_dims_step_two_layers_teacher_forced(wname):
     cap = ((n0 + t.T + steps * (t.max_depth + 1) + 63) // 64) * 64
     dw = rt.DeviceWeights(D, Wt.get)
     typical = w.accept == "typical"
-    p = tv.AcceptParams(mode=tv.ACCEPT_TYPICAL if typical else tv.ACCEPT_GREEDY,
+    reject = w.accept == "reject"
+    mode = {"greedy": tv.ACCEPT_GREEDY, "typical": tv.ACCEPT_TYPICAL,
+            "reject": tv.ACCEPT_REJECT}[w.accept]
+    p = tv.AcceptParams(mode=mode,
                         root_mode=tv.ROOT_SAMPLE if w.root == "sample" else tv.ROOT_ARGMAX,
                         temperature=w.temperature, eps=w.eps, delta=w.delta)
-    u = synth.uniform_draws(w, steps + 1)
+    u = synth.uniform_draws(w, steps + 1, t.T if reject else 0)
     sess = rt.Session(D, 1, t.T, s, cap, dw, trees, p, u_draws=u, debug=True)
     # the state a prefill of n0 tokens leaves: seeded bf16 prefix K/V, a
     # post-norm hidden state of unit scale and a root token
@@ -234,6 +260,10 @@ def test_full_dims_step_two_layers_teacher_forced(wname):
         assert lerr <= TOL * stages(D.L), (step, lerr)
         if typical:
             res = oa.typical_accept(t, tok, gl, w.temperature, w.eps, w.delta)
+        elif reject:
+            res = oa.reject_accept(t, tok, gl, w.temperature, u[step + 1, 0])
+            m = res.margin
+            assert not np.any(np.abs(m[np.isfinite(m)]) <= 1e-9), "tie up to rounding"
         else:
             res = oa.greedy_accept(t, tok, gl)
         L_acc = int(sess.accept_len[0])
@@ -241,7 +271,9 @@ def test_full_dims_step_two_layers_teacher_forced(wname):
         np.testing.assert_array_equal(sess.path[0].cpu().numpy()[:L_acc + 1], res.path)
         np.testing.assert_array_equal(sess.emitted[0].cpu().numpy()[:L_acc + 1], tok[res.path])
         assert int(sess.best[0]) == res.best
-        if w.root == "sample":
+        if reject:
+            assert int(sess.root_tok[0]) == res.next_root
+        elif w.root == "sample":
             want, margin = oa.sample_root(gl[res.best], w.temperature, u[step + 1, 0])
             if margin > 1e-6:
                 assert int(sess.root_tok[0]) == want

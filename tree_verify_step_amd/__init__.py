@@ -6,7 +6,7 @@ point names, and `runtime` allocates device buffers with PyTorch and wires
 them to the library.  Nothing here computes the method in Python.
 """
 from . import _lib  # noqa: F401
-from ._lib import (ACCEPT_GREEDY, ACCEPT_TYPICAL, PACK_PLAIN, PACK_QKV, ROOT_ARGMAX,  # noqa: F401
-                   ROOT_SAMPLE, AcceptParams, Ctx, Dims, KV, LayerWeights, MVError, StepDesc,
-                   Tree, accept, decoder_layer, embed, kv_compact, lib, lm_head, medusa_heads,
+from ._lib import (ACCEPT_GREEDY, ACCEPT_REJECT, ACCEPT_TYPICAL, PACK_PLAIN,  # noqa: F401
+                   PACK_QKV, ROOT_ARGMAX, ROOT_SAMPLE, AcceptParams, Ctx, Dims, KV, LayerWeights,
+                   MVError, StepDesc, Tree, accept, accept_reject, decoder_layer, embed, kv_compact, lib, lm_head, medusa_heads,
                    pack_weight, read_probe, tree_attention, tree_compile, workspace_size)

@@ -19,13 +19,13 @@ MV_MAX_T = 256
 MV_MAX_DEPTH = 16
 MV_MAX_TOPK = 16
 MV_MAX_BATCH = 4
-ACCEPT_GREEDY, ACCEPT_TYPICAL = 0, 1
+ACCEPT_GREEDY, ACCEPT_TYPICAL, ACCEPT_REJECT = 0, 1, 2
 ROOT_ARGMAX, ROOT_SAMPLE = 0, 1
 PACK_PLAIN, PACK_QKV = 0, 1
 
 EXPORTS = ("mv_strerror", "mv_last_error", "mv_tree_compile", "mv_pack_weight",
            "mv_workspace_size", "mv_medusa_heads", "mv_tree_attention", "mv_decoder_layer",
-           "mv_embed", "mv_lm_head", "mv_accept", "mv_kv_compact", "mv_ctx_create",
+           "mv_embed", "mv_lm_head", "mv_accept", "mv_accept_reject", "mv_kv_compact", "mv_ctx_create",
            "mv_ctx_destroy", "mv_prefill", "mv_step", "mv_step_profile", "mv_time_kernel", "mv_read_probe")
 
 # launch-group kinds of mv_step_profile
@@ -108,6 +108,8 @@ def lib() -> C.CDLL:
         "mv_accept": (C.c_int, [i32, i32, i32, i32, vp, C.POINTER(Tree), vp,
                                 C.POINTER(AcceptParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                 vp, sz, vp]),
+        "mv_accept_reject": (C.c_int, [i32, i32, i32, i32, vp, C.POINTER(Tree), vp, C.c_double,
+                                       vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "mv_kv_compact": (C.c_int, [C.POINTER(KV), vp, i32, vp, vp, vp]),
         "mv_ctx_create": (C.c_int, [C.POINTER(vp), C.POINTER(StepDesc)]),
         "mv_ctx_destroy": (None, [vp]),
@@ -239,6 +241,18 @@ def accept(B: int, T: int, V: int, d: int, logits, tree: Tree, tree_tok, p: Acce
                           ptr(u), ptr(accept_len), ptr(path), ptr(best), ptr(next_root),
                           ptr(emitted), ptr(margin), ptr(x), ptr(final_norm), ptr(h_last),
                           ptr(ws), ws.numel() * ws.element_size(), stream_ptr(stream)), "accept")
+
+
+def accept_reject(B: int, T: int, V: int, d: int, logits, tree: Tree, tree_tok,
+                  temperature: float, draft_logits, u, accept_len, path, best, next_root,
+                  emitted=None, margin=None, x=None, final_norm=None, h_last=None, ws=None,
+                  stream=None) -> None:
+    check(lib().mv_accept_reject(B, T, V, d, ptr(logits), C.byref(tree), ptr(tree_tok),
+                                 float(temperature), ptr(draft_logits), ptr(u), ptr(accept_len),
+                                 ptr(path), ptr(best), ptr(next_root), ptr(emitted), ptr(margin),
+                                 ptr(x), ptr(final_norm), ptr(h_last), ptr(ws),
+                                 ws.numel() * ws.element_size(), stream_ptr(stream)),
+          "accept_reject")
 
 
 def kv_compact(kv: KV, path, path_stride: int, accept_len, n_prefix, stream=None) -> None:

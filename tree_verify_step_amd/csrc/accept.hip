@@ -13,6 +13,8 @@
 // emitted tokens, the next root (argmax of the best row, or inverse-CDF
 // sampling of its tempered softmax with the step's uniform draw) and the
 // carried hidden state (that row of the final-normed hidden states).
+// reject_accept: one workgroup per sequence walks the tree with the
+// speculative-sampling correction (see the kernel).
 // All decision arithmetic (thresholds, probabilities, sums) is double.
 #include "common.hpp"
 
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict_
   }
   block_argmax(bv, bi);
   if (threadIdx.x == 0) amax[row] = bi;
-  if (mode != MV_ACCEPT_TYPICAL) return;
+  if (mode == MV_ACCEPT_GREEDY) return;
 
   const double inv_t = 1.0 / temperature;
   const double m = (double)bv;
@@ -173,6 +175,14 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict_
            exp(((double)v[u].z - m) * inv_t) + exp(((double)v[u].w - m) * inv_t);
   }
   S = block_sum_d(S);
+  if (mode != MV_ACCEPT_TYPICAL) {            // rejection sampling: max and normaliser only
+    if (threadIdx.x == 0) {
+      stats[(size_t)row * 3 + 0] = m;
+      stats[(size_t)row * 3 + 1] = S;
+      stats[(size_t)row * 3 + 2] = 0.0;
+    }
+    return;
+  }
   double Hs = 0.0;
   for (int i0 = threadIdx.x; i0 < V4; i0 += 1024) {
     float4 v[4];
@@ -208,67 +218,173 @@ hipError_t launch_row_stats(const float* logits, int rows, int V, int mode, doub
 
 #define MV_MAXT 256
 
-// Inverse-CDF sample of softmax(z * inv_t) over ids in increasing order:
-// the smallest id whose cumulative mass exceeds u (if rounding leaves none,
-// the largest id of nonzero mass).  Whole workgroup (256 threads) calls it;
-// each thread sums a contiguous chunk of ids (multiple of 4), an exclusive
-// prefix over the chunk sums locates the crossing.  Writes *out (and
-// |cdf - u| to *margin).
-__device__ void block_sample(const float* __restrict__ z, int V, int amax_id, double inv_t,
-                             double u, int32_t* out, double* margin) {
-  __shared__ double csum[256];
+// Weighted inverse-CDF draw over ids 0..V-1 (V % 4 == 0) with weights >= 0:
+// the smallest id whose cumulative weight (id order) exceeds u times the
+// total; if rounding leaves none, the largest id of nonzero weight.  The
+// whole workgroup (256 threads) calls it.  w4(i0, w) fills the weights of
+// ids i0..i0+3.  Three passes, all reads coalesced: each wave sums 256-id
+// blocks (a lane takes 4 consecutive ids) into LDS; an exclusive scan of the
+// block sums finds the block where the cumulative weight crosses; one wave
+// rescans that block.  Returns false (writing nothing) when the total is 0.
+#define MV_DRAW_MAXB (MV_MAX_VOCAB / 256)   // 256-id blocks
+template <class W4>
+__device__ __forceinline__ bool block_draw(int V, double u, W4 w4, int32_t* out, double* margin) {
+  __shared__ double bsum[MV_DRAW_MAXB], bpre[MV_DRAW_MAXB];   // block sums, exclusive prefixes
+  __shared__ double wtot[4];
+  __shared__ int s_blk, s_last;
   __shared__ double s_total;
-  __shared__ int s_found;
-  const double m = (double)z[amax_id];
-  const int chunk = (((V + 255) / 256) + 3) & ~3;
-  const int c0 = min(V, (int)threadIdx.x * chunk), c1 = min(V, c0 + chunk);
-  double part = 0.0;
-  for (int i = c0; i < c1; i += 4) {
-    const float4 v = *reinterpret_cast<const float4*>(z + i);
-    part += exp(((double)v.x - m) * inv_t) + exp(((double)v.y - m) * inv_t) +
-            exp(((double)v.z - m) * inv_t) + exp(((double)v.w - m) * inv_t);
-  }
-  csum[threadIdx.x] = part;
-  if (threadIdx.x == 0) s_found = 0x7fffffff;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double tot = 0.0;
-    for (int t = 0; t < 256; ++t) {
-      const double x = csum[t];
-      csum[t] = tot;
-      tot += x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nb = (V + 255) >> 8;
+  // pass 1: block sums, lane partials in id order, then a fixed-order wave sum
+  constexpr int UB = 8;               // blocks per wave in flight
+  for (int b0 = wave; b0 < nb; b0 += 4 * UB) {
+    double part[UB];
+#pragma unroll
+    for (int j = 0; j < UB; ++j) {
+      const int b = b0 + 4 * j;
+      const int i0 = (b << 8) + 4 * lane;
+      double w[4] = {0.0, 0.0, 0.0, 0.0};
+      if (b < nb && i0 < V) w4(i0, w);
+      part[j] = (w[0] + w[1]) + (w[2] + w[3]);
     }
-    s_total = tot;
+#pragma unroll
+    for (int j = 0; j < UB; ++j) {
+      double v = part[j];
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+      v = __shfl(v, 0, 64);
+      const int b = b0 + 4 * j;
+      if (lane == 0 && b < nb) bsum[b] = v;
+    }
   }
+  if (tid == 0) {
+    s_blk = 0x7fffffff;
+    s_last = -1;
+  }
+  __syncthreads();
+  // pass 2: exclusive scan of the block sums (each thread a run of them)
+  const int per = (nb + 255) >> 8;
+  const int r0 = min(nb, tid * per), r1 = min(nb, r0 + per);
+  double run = 0.0;
+  for (int b = r0; b < r1; ++b) run += bsum[b];
+  double inc = run;                  // inclusive scan over the threads
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double t = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += t;
+  }
+  if (lane == 63) wtot[wave] = inc;
+  __syncthreads();
+  double base = 0.0;
+  for (int k = 0; k < wave; ++k) base += wtot[k];
+  if (tid == 0) s_total = ((wtot[0] + wtot[1]) + wtot[2]) + wtot[3];
   __syncthreads();
   const double S = s_total;
-  double cum = csum[threadIdx.x];
-  int found = -1;
-  double mg = INFINITY;
-  if (c0 < c1 && cum / S <= u) {
-    for (int i = c0; i < c1; ++i) {
-      const double prev = cum / S;
-      cum += exp(((double)z[i] - m) * inv_t);
-      if (cum / S > u) {
-        found = i;
-        mg = fmin(cum / S - u, u - prev);
-        break;
+  if (!(S > 0.0)) {
+    __syncthreads();
+    return false;
+  }
+  double cum = base + inc - run;     // exclusive prefix of this thread's run
+  bool hit = false;
+  for (int b = r0; b < r1; ++b) {
+    bpre[b] = cum;
+    const double nxt = cum + bsum[b];
+    if (!hit && nxt / S > u) {       // crossing: cumulative / S > u
+      atomicMin(&s_blk, b);
+      hit = true;
+    }
+    cum = nxt;
+  }
+  for (int b = r1 - 1; b >= r0; --b)
+    if (bsum[b] > 0.0) {
+      atomicMax(&s_last, b);
+      break;
+    }
+  __syncthreads();
+  // pass 3: one wave resolves the id inside the block
+  if (wave == 0) {
+    const int blk = s_blk;
+    if (blk != 0x7fffffff) {
+      const double before = bpre[blk];   // cumulative weight before the block
+      const int i0 = (blk << 8) + 4 * lane;
+      double w[4] = {0.0, 0.0, 0.0, 0.0};
+      if (i0 < V) w4(i0, w);
+      const double lsum = (w[0] + w[1]) + (w[2] + w[3]);
+      double linc = lsum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const double t = __shfl_up(linc, o, 64);
+        if (lane >= o) linc += t;
       }
+      double c = before + (linc - lsum);
+      int found = -1;
+      double mg = INFINITY;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const double prev = c;
+        c += w[j];
+        if (found < 0 && i0 < V && c / S > u) {
+          found = i0 + j;
+          mg = fmin(c / S - u, u - prev / S);
+        }
+      }
+      const unsigned long long hit = __ballot(found >= 0);
+      if (hit) {
+        const int first = __ffsll((long long)hit) - 1;
+        if (lane == first) {
+          *out = found;
+          if (margin) *margin = mg;
+        }
+      } else if (lane == 0) {        // rounding between the two scans: the block's last nonzero id
+        int last = -1;
+        for (int i = min(V, (blk + 1) << 8) - 1; i >= (blk << 8) && last < 0; i -= 4) {
+          double ww[4];
+          w4(i - 3, ww);
+#pragma unroll
+          for (int j = 3; j >= 0; --j)
+            if (last < 0 && ww[j] > 0.0) last = i - 3 + j;
+        }
+        *out = last >= 0 ? last : (blk << 8);
+        if (margin) *margin = 0.0;
+      }
+    } else if (lane == 0) {          // no crossing: the largest id of nonzero weight
+      const int lb = s_last;
+      int last = 0;
+      if (lb >= 0) {
+        for (int i = min(V, (lb + 1) << 8) - 1; i >= (lb << 8); i -= 4) {
+          double ww[4];
+          w4(i - 3, ww);
+          int hitj = -1;
+#pragma unroll
+          for (int j = 3; j >= 0; --j)
+            if (hitj < 0 && ww[j] > 0.0) hitj = j;
+          if (hitj >= 0) {
+            last = i - 3 + hitj;
+            break;
+          }
+        }
+      }
+      *out = last;
+      if (margin) *margin = 0.0;
     }
   }
-  if (found >= 0) atomicMin(&s_found, found);
   __syncthreads();
-  if (found >= 0 && found == s_found) {
-    *out = found;
-    if (margin) *margin = mg;
-  }
-  if (threadIdx.x == 0 && s_found == 0x7fffffff) {
-    int last = V - 1;
-    while (last > 0 && exp(((double)z[last] - m) * inv_t) == 0.0) --last;
-    *out = last;
-    if (margin) *margin = 0.0;
-  }
-  __syncthreads();
+  return true;
+}
+
+// Inverse-CDF sample of softmax(z * inv_t): block_draw over the unnormalised
+// weights exp((z_i - max) * inv_t).  Writes *out (and |cdf - u| to *margin).
+__device__ __forceinline__ void block_sample(const float* __restrict__ z, int V, int amax_id, double inv_t,
+                             double u, int32_t* out, double* margin) {
+  const double m = (double)z[amax_id];
+  auto w4 = [&](int i0, double (&w)[4]) {
+    const float4 v = *reinterpret_cast<const float4*>(z + i0);
+    w[0] = exp(((double)v.x - m) * inv_t);
+    w[1] = exp(((double)v.y - m) * inv_t);
+    w[2] = exp(((double)v.z - m) * inv_t);
+    w[3] = exp(((double)v.w - m) * inv_t);
+  };
+  block_draw(V, u, w4, out, margin);
 }
 
 __global__ __launch_bounds__(256) void accept_finish_kernel(
@@ -438,12 +554,255 @@ hipError_t launch_accept_finish(const float* logits, const int32_t* argmax, unsi
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Rejection-sampling acceptance (speculative sampling: the lecture note's
+// section 二.3 and the speculative-decoding tutorial's Maths section).  A
+// draft token x drawn from q is kept against the target p with probability
+// min(1, p(x)/q(x)); a rejected one is replaced by a draw from the positive
+// part of p - q, normalised.  Over a tree: at the current node (target p =
+// softmax(logits/temperature) of its row) the children are tried in node
+// order against the running residual r (p at first); a kept child becomes
+// the current node; a rejection turns r into the correction's residual and
+// the next sibling is tried; when none is kept (or at a leaf) the next root
+// is drawn from r by inverse CDF.  Drafts: without draft logits a candidate
+// is a point mass (top-s candidates are fixed), so x is kept with
+// probability r(x) and a rejection removes x from r; with draft logits
+// [B][depth][V] the children at depth k use q = softmax(draft[k-1] / temp).
+// A residual with no mass left (rejection of probability 0 up to rounding)
+// falls back to the node's p.  Draws: u[c] decides child c (kept iff
+// u[c] < a), u[0] makes the final draw.
+//
+// The walk is sequential (one decision at a time) but every thread runs it
+// in lockstep on the same shared values; the V-wide passes (draft row
+// statistics, residual updates, the final draw) use the whole workgroup.
+
+// A residual value written by another wave of this workgroup: read at
+// device scope, past the compute unit's vector cache.
+__device__ __forceinline__ double ld_resid(const double* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ __launch_bounds__(256) void reject_accept_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ amax_rows,
+    const double* __restrict__ stats, const int32_t* __restrict__ parent,
+    const int32_t* __restrict__ tok, int T, int V, int depth, double inv_t,
+    const float* __restrict__ draft, const double* __restrict__ dstats,
+    const double* __restrict__ u, const int32_t* __restrict__ u_index, long long u_stride,
+    double* resid, int32_t* __restrict__ accept_len, int32_t* __restrict__ path,
+    int32_t* __restrict__ best_out, int32_t* __restrict__ next_root,
+    int32_t* __restrict__ emitted, double* __restrict__ margin, const float* __restrict__ x,
+    const u16* __restrict__ final_norm, u16* __restrict__ h_last, int d,
+    int32_t* __restrict__ n_advance) {
+  // the tree and every per-candidate quantity the walk needs, in LDS
+  __shared__ int par[MV_MAXT], tk[MV_MAXT];
+  __shared__ int fch[MV_MAXT], nsib[MV_MAXT];   // first child, next sibling (T: none)
+  __shared__ int dupp[MV_MAXT];                 // nearest earlier sibling with the same token
+  __shared__ double mrow[MV_MAXT], srow[MV_MAXT];   // row max and normaliser
+  __shared__ double esel[MV_MAXT];   // exp((z_parent[tok] - max) / temp) of each candidate
+  __shared__ double qsel[MV_MAXT];   // draft probability of each candidate
+  __shared__ double usel[MV_MAXT];   // the step's draws
+  __shared__ int xs[MV_MAXT];        // tokens removed from the final residual
+  __shared__ int s_nx;
+  __shared__ int s_nodes[MV_MAX_DEPTH + 1];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const NormGains ng = norm_gains(x && h_last ? final_norm : nullptr, d);
+  const size_t row0 = (size_t)b * T;
+  const double* ub = u + (size_t)(u_index ? u_index[0] : 0) * u_stride + row0;
+  for (int v = tid; v < T; v += 256) {
+    const int pv = parent[row0 + v];
+    usel[v] = ub[v];
+    par[v] = v > 0 && pv >= 0 && pv < v ? pv : -1;   // other parents: not in the tree
+    tk[v] = tok[row0 + v];
+    fch[v] = T;
+    const size_t row = row0 + v;
+    mrow[v] = (double)logits[row * V + amax_rows[row]];
+    srow[v] = stats[row * 3 + 1];
+  }
+  if (margin)
+    for (int v = tid; v <= T; v += 256) margin[row0 + b + v] = INFINITY;
+  __syncthreads();
+  for (int v = tid; v < T; v += 256) {
+    const int pv = par[v];
+    int ns = T, dp = -1;
+    double e = 0.0, q = 0.0;
+    if (pv >= 0) {
+      atomicMin(&fch[pv], v);
+      for (int c = v + 1; c < T && ns == T; ++c)
+        if (par[c] == pv) ns = c;
+      for (int c = v - 1; c > pv && dp < 0; --c)
+        if (par[c] == pv && tk[c] == tk[v]) dp = c;
+      const int xt = tk[v];
+      if ((unsigned)xt < (unsigned)V) {       // other ids are never kept
+        e = exp(((double)logits[(row0 + pv) * V + xt] - mrow[pv]) * inv_t);
+        if (draft) {
+          int k = 0;                           // depth of v
+          for (int a = v; a > 0 && k <= MV_MAX_DEPTH; a = par[a]) ++k;
+          if (k >= 1 && k <= depth) {
+            const size_t dr = (size_t)b * depth + (k - 1);
+            q = exp(((double)draft[dr * V + xt] - dstats[dr * 3]) * inv_t) / dstats[dr * 3 + 1];
+          }
+        }
+      }
+    }
+    nsib[v] = ns;
+    dupp[v] = dp;
+    esel[v] = e;
+    qsel[v] = q;
+  }
+  __syncthreads();
+  double* R = draft ? resid + (size_t)b * 2 * V : nullptr;   // two residual buffers [2][V]
+  const int max_len = min(depth, MV_MAX_DEPTH);
+  if (tid == 0) s_nodes[0] = 0;
+  int cur = 0, L = 0;
+  for (;;) {
+    const float* z = logits + (row0 + cur) * V;
+    const double m = mrow[cur], S = srow[cur];
+    auto e_of4 = [&](int i0, double (&w)[4]) {
+      const float4 v = *reinterpret_cast<const float4*>(z + i0);
+      w[0] = exp(((double)v.x - m) * inv_t);
+      w[1] = exp(((double)v.y - m) * inv_t);
+      w[2] = exp(((double)v.z - m) * inv_t);
+      w[3] = exp(((double)v.w - m) * inv_t);
+    };
+    const int first = L < max_len ? fch[cur] : T;
+    const float* zd = draft && first < T ? draft + ((size_t)b * depth + L) * V : nullptr;
+    const double md = zd ? dstats[((size_t)b * depth + L) * 3] : 0.0;
+    const double Sd = zd ? dstats[((size_t)b * depth + L) * 3 + 1] : 1.0;
+    int rb = -1;              // draft: residual buffer in use (-1: r is p)
+    double rs = 1.0;          // its total
+    double ex_e = 0.0;        // point drafts: removed mass (units of S) ...
+    int ex_from = cur + 1;    // ... of the rejected siblings from this node index on
+    int acc = -1;
+    for (int c = first; c < T; c = nsib[c]) {
+      const bool valid = (unsigned)tk[c] < (unsigned)V;
+      double a = 0.0;
+      const bool seen = !valid || dupp[c] >= ex_from;
+      if (!draft) {
+        if (!seen) a = fmin(1.0, esel[c] / (S - ex_e));
+      } else if (valid) {
+        const double qx = qsel[c];
+        const double rx = rb >= 0 ? ld_resid(R + (size_t)rb * V + tk[c]) / rs : esel[c] / S;
+        a = qx > 0.0 ? fmin(1.0, rx / qx) : (rx > 0.0 ? 1.0 : 0.0);
+      }
+      const double uc = usel[c];
+      if (margin && tid == 0) margin[row0 + b + c] = uc - a;
+      if (uc < a) {
+        acc = c;
+        break;
+      }
+      if (!draft) {
+        if (!seen) {
+          if (S - ex_e - esel[c] > 0.0) {
+            ex_e += esel[c];
+          } else {            // nothing left: back to p
+            ex_e = 0.0;
+            ex_from = c + 1;
+          }
+        }
+      } else {
+        // r <- max(0, r - q) into the other buffer; each thread rewrites the
+        // ids it wrote last time, so only the scalar reads above and the
+        // final draw cross waves
+        const int nb = rb == 0 ? 1 : 0;
+        double part = 0.0;
+        for (int i = tid; i < V; i += 256) {
+          const double ri = rb >= 0 ? R[(size_t)rb * V + i] / rs : exp(((double)z[i] - m) * inv_t) / S;
+          const double qi = exp(((double)zd[i] - md) * inv_t) / Sd;
+          const double ni = fmax(ri - qi, 0.0);
+          R[(size_t)nb * V + i] = ni;
+          part += ni;
+        }
+        __threadfence();
+        const double sum = block_sum_d(part);
+        if (sum > 0.0) {
+          rb = nb;
+          rs = sum;
+        } else {
+          rb = -1;
+          rs = 1.0;
+        }
+      }
+    }
+    if (acc >= 0) {
+      cur = acc;
+      ++L;
+      if (tid == 0) s_nodes[L] = cur;
+      continue;
+    }
+    // final draw from the residual at cur
+    const double u0 = usel[0];
+    double* mg = margin ? margin + row0 + b + T : nullptr;
+    int32_t* out = next_root + b;
+    if (!draft) {
+      if (tid == 0) {
+        int n = 0;
+        for (int c = first; c < T; c = nsib[c])
+          if (c >= ex_from && (unsigned)tk[c] < (unsigned)V && dupp[c] < ex_from) xs[n++] = tk[c];
+        s_nx = n;
+      }
+      __syncthreads();
+      const int nx = s_nx;
+      auto w_res = [&](int i0, double (&w)[4]) {
+        e_of4(i0, w);
+        for (int j = 0; j < nx; ++j) {
+          const int k = xs[j] - i0;
+          if (k == 0) w[0] = 0.0;
+          if (k == 1) w[1] = 0.0;
+          if (k == 2) w[2] = 0.0;
+          if (k == 3) w[3] = 0.0;
+        }
+      };
+      if (!block_draw(V, u0, w_res, out, mg)) block_draw(V, u0, e_of4, out, mg);
+    } else if (rb >= 0) {
+      const double* Rb = R + (size_t)rb * V;
+      auto w_r = [&](int i0, double (&w)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = ld_resid(Rb + i0 + j);
+      };
+      block_draw(V, u0, w_r, out, mg);
+    } else {
+      block_draw(V, u0, e_of4, out, mg);
+    }
+    break;
+  }
+  if (tid == 0) {
+    accept_len[b] = L;
+    best_out[b] = cur;
+    if (n_advance) n_advance[b] += L + 1;
+    for (int k = 0; k <= depth; ++k) {
+      const int node = k <= L ? s_nodes[k] : -1;
+      path[(size_t)b * (depth + 1) + k] = node;
+      if (emitted) emitted[(size_t)b * (depth + 1) + k] = node >= 0 ? tk[node] : -1;
+    }
+  }
+  if (x && h_last)
+    block_norm_row(x + (row0 + cur) * d, final_norm, ng, h_last + (size_t)b * d, d);
+}
+
+hipError_t launch_reject_accept(const float* logits, const int32_t* argmax, const double* stats,
+                                const int32_t* parent, const int32_t* tok, int B, int T, int V,
+                                int depth, double temperature, const float* draft,
+                                const double* dstats, const double* u, const int32_t* u_index,
+                                long long u_stride, double* resid, int32_t* accept_len,
+                                int32_t* path, int32_t* best, int32_t* next_root,
+                                int32_t* emitted, double* margin, const float* x,
+                                const u16* final_norm, u16* h_last, int d, hipStream_t s,
+                                int32_t* n_advance) {
+  if (T > MV_MAXT) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(reject_accept_kernel, dim3(B), dim3(256), 0, s, logits, argmax, stats, parent,
+                     tok, T, V, depth, 1.0 / temperature, draft, dstats, u, u_index, u_stride, resid,
+                     accept_len, path, best, next_root, emitted, margin, x, final_norm, h_last, d,
+                     n_advance);
+  return hipGetLastError();
+}
+
 // Prefill: after a chain chunk, sequence b's last real row (cnt[b] - 1)
 // supplies h_last (its final RMSNorm) and the first root; n[b] += cnt[b].
 // cnt[b] == 0: nothing.
 __global__ __launch_bounds__(256) void prefill_select_kernel(
     const float* __restrict__ logits, const int32_t* __restrict__ amax, const int32_t* __restrict__ cnt,
-    int T, int V, int root_mode, double temperature, const double* __restrict__ u,
+    int T, int V, int root_mode, double temperature, const double* __restrict__ u, int u_bstride,
     int32_t* __restrict__ root, int32_t* __restrict__ n_prefix, const float* __restrict__ x,
     const u16* __restrict__ final_norm, u16* __restrict__ h_last, int d) {
   const int b = blockIdx.x;
@@ -454,8 +813,8 @@ __global__ __launch_bounds__(256) void prefill_select_kernel(
   if (root_mode == MV_ROOT_ARGMAX) {
     if (threadIdx.x == 0) root[b] = amax[row];
   } else {
-    block_sample(logits + (size_t)row * V, V, amax[row], 1.0 / temperature, u[(size_t)b], root + b,
-                 nullptr);
+    block_sample(logits + (size_t)row * V, V, amax[row], 1.0 / temperature,
+                 u[(size_t)b * u_bstride], root + b, nullptr);
   }
   __syncthreads();
   if (threadIdx.x == 0) n_prefix[b] += c;
@@ -463,11 +822,11 @@ __global__ __launch_bounds__(256) void prefill_select_kernel(
 
 hipError_t launch_prefill_select(const float* logits, const int32_t* amax, const int32_t* cnt,
                                  int B, int T, int V, int root_mode, double temperature,
-                                 const double* u, int32_t* root, int32_t* n_prefix,
+                                 const double* u, int u_bstride, int32_t* root, int32_t* n_prefix,
                                  const float* x, const u16* final_norm, u16* h_last, int d,
                                  hipStream_t s) {
   hipLaunchKernelGGL(prefill_select_kernel, dim3(B), dim3(256), 0, s, logits, amax, cnt, T, V,
-                     root_mode, temperature, u, root, n_prefix, x, final_norm, h_last, d);
+                     root_mode, temperature, u, u_bstride, root, n_prefix, x, final_norm, h_last, d);
   return hipGetLastError();
 }
 

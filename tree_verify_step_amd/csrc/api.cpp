@@ -41,6 +41,7 @@ static int check_dims(const mv_dims* D) {
     return fail(MV_EINVAL, "dims out of range (L=%d d=%d H=%d hd=%d F=%d V=%d K=%d)", D->L, D->d,
                 D->H, D->hd, D->F, D->V, D->K);
   if (D->H * D->hd != D->d) return fail(MV_EUNSUPPORTED, "H*hd (%d) != d (%d)", D->H * D->hd, D->d);
+  if (D->V > MV_MAX_VOCAB) return fail(MV_EUNSUPPORTED, "V=%d > %d", D->V, MV_MAX_VOCAB);
   if (D->d % 64 || D->F % 32 || D->V % 64)
     return fail(MV_EUNSUPPORTED, "need d%%64==0, F%%32==0, V%%64==0 (d=%d F=%d V=%d)", D->d, D->F, D->V);
   if (D->hd != 16 && D->hd != 32 && D->hd != 64 && D->hd != 128)
@@ -383,6 +384,15 @@ static int enq_accept(int B, int T, int V, int d, const float* logits, const mv_
                       const float* x, const void* final_norm, void* h_last, int32_t* amax,
                       double* stats, hipStream_t s, unsigned long long* amax_key = nullptr,
                       int32_t* n_advance = nullptr) {
+  if (p.mode == MV_ACCEPT_REJECT) {
+    MV_HIP(mvk::launch_row_stats(logits, B * T, V, p.mode, p.temperature, amax, stats, s));
+    MV_HIP(mvk::launch_reject_accept(logits, amax, stats, t.parent, tok, B, T, V, t.depth,
+                                     p.temperature, nullptr, nullptr, u, u_index, (long long)u_stride,
+                                     nullptr, accept_len, path, best, next_root, emitted, margin,
+                                     x, static_cast<const u16*>(final_norm),
+                                     static_cast<u16*>(h_last), d, s, n_advance));
+    return MV_OK;
+  }
   // greedy acceptance with the LM head's argmax keys needs no pass over the
   // logits; otherwise the rows' argmax (and typical statistics)
   if (!(amax_key && p.mode == MV_ACCEPT_GREEDY)) {
@@ -569,9 +579,13 @@ MV_API int mv_accept(int32_t B, int32_t T, int32_t V, int32_t d, const float* lo
   if (rc) return rc;
   if ((rc = check_tree(tree, false))) return rc;
   if (tree->T != T) return fail(MV_EINVAL, "T=%d != tree T=%d", T, tree->T);
-  if (V < 64 || V % 64) return fail(MV_EUNSUPPORTED, "V=%d", V);
+  if (V < 64 || V % 64 || V > MV_MAX_VOCAB) return fail(MV_EUNSUPPORTED, "V=%d", V);
   if (!p || !logits || !tree_tok || !accept_len || !path || !best || !next_root)
     return fail(MV_EINVAL, "mv_accept: NULL pointer");
+  if (p->mode == MV_ACCEPT_REJECT)
+    return mv_accept_reject(B, T, V, d, logits, tree, tree_tok, p->temperature, nullptr, u,
+                            accept_len, path, best, next_root, emitted, margin, x, final_norm,
+                            h_last, ws, ws_bytes, stream);
   if (p->mode != MV_ACCEPT_GREEDY && p->mode != MV_ACCEPT_TYPICAL) return fail(MV_EINVAL, "accept mode %d", p->mode);
   if (p->root_mode != MV_ROOT_ARGMAX && p->root_mode != MV_ROOT_SAMPLE) return fail(MV_EINVAL, "root mode %d", p->root_mode);
   if ((p->mode == MV_ACCEPT_TYPICAL || p->root_mode == MV_ROOT_SAMPLE) && !(p->temperature > 0.0))
@@ -586,6 +600,49 @@ MV_API int mv_accept(int32_t B, int32_t T, int32_t V, int32_t d, const float* lo
   return enq_accept(B, T, V, d, logits, *tree, tree_tok, *p, u, nullptr, B, accept_len, path, best,
                     next_root, emitted, margin, x, final_norm, h_last, at<int32_t>(ws, 0),
                     at<double>(ws, align256((size_t)B * T * 4)), (hipStream_t)stream);
+}
+
+MV_API int mv_accept_reject(int32_t B, int32_t T, int32_t V, int32_t d, const float* logits,
+                            const mv_tree* tree, const int32_t* tree_tok, double temperature,
+                            const float* draft_logits, const double* u, int32_t* accept_len,
+                            int32_t* path, int32_t* best, int32_t* next_root, int32_t* emitted,
+                            double* margin, const float* x, const void* final_norm, void* h_last,
+                            void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_batch(B);
+  if (rc) return rc;
+  if ((rc = check_tree(tree, false))) return rc;
+  if (tree->T != T) return fail(MV_EINVAL, "T=%d != tree T=%d", T, tree->T);
+  if (V < 64 || V % 64 || V > MV_MAX_VOCAB) return fail(MV_EUNSUPPORTED, "V=%d", V);
+  if (!logits || !tree_tok || !u || !accept_len || !path || !best || !next_root)
+    return fail(MV_EINVAL, "mv_accept_reject: NULL pointer");
+  if (!(temperature > 0.0)) return fail(MV_EINVAL, "temperature must be > 0");
+  if (draft_logits && tree->depth < 1) return fail(MV_EINVAL, "draft logits need a tree of depth >= 1");
+  if ((x == nullptr) != (h_last == nullptr) || (x && !final_norm))
+    return fail(MV_EINVAL, "x, final_norm and h_last go together");
+  if (x && (d < 1 || d % 4)) return fail(MV_EINVAL, "d=%d", d);
+  // workspace: row argmax and stats of the tree rows, then (draft logits)
+  // those of the draft rows and two residual rows per sequence
+  const int Dr = draft_logits ? B * tree->depth : 0;
+  const size_t o_stats = align256((size_t)B * T * 4);
+  const size_t o_damax = o_stats + align256((size_t)B * T * 24);
+  const size_t o_dstats = o_damax + align256((size_t)Dr * 4);
+  const size_t o_res = o_dstats + align256((size_t)Dr * 24);
+  const size_t need = draft_logits ? o_res + (size_t)B * 2 * V * 8 : o_damax;
+  if (!ws || ws_bytes < need) return fail(MV_EWORKSPACE, "workspace %zu < %zu", ws_bytes, need);
+  const hipStream_t s = (hipStream_t)stream;
+  MV_HIP(mvk::launch_row_stats(logits, B * T, V, MV_ACCEPT_REJECT, temperature, at<int32_t>(ws, 0),
+                               at<double>(ws, o_stats), s));
+  if (draft_logits)
+    MV_HIP(mvk::launch_row_stats(draft_logits, Dr, V, MV_ACCEPT_REJECT, temperature,
+                                 at<int32_t>(ws, o_damax), at<double>(ws, o_dstats), s));
+  MV_HIP(mvk::launch_reject_accept(logits, at<int32_t>(ws, 0), at<double>(ws, o_stats), tree->parent,
+                                   tree_tok, B, T, V, tree->depth, temperature, draft_logits,
+                                   draft_logits ? at<double>(ws, o_dstats) : nullptr, u,
+                                   nullptr, 0, draft_logits ? at<double>(ws, o_res) : nullptr,
+                                   accept_len, path, best, next_root, emitted, margin, x,
+                                   static_cast<const u16*>(final_norm), static_cast<u16*>(h_last),
+                                   d, s));
+  return MV_OK;
 }
 
 MV_API int mv_kv_compact(const mv_kv* kv, const int32_t* path, int32_t path_stride,
@@ -620,7 +677,20 @@ struct mv_ctx {
   uint64_t* chain_anc = nullptr; // [B][T][mask_words]
   int32_t* chunk_tok = nullptr;  // [B][T]
   std::vector<hipEvent_t> prof_ev;
+  int64_t draws_used = 1;        // draws of u_draws consumed (draw 0: the prefill's root)
 };
+
+// A step that draws (sampled roots, rejection sampling) takes the next row of
+// u_draws: refuse to run past the last one.
+static int take_draw(mv_ctx* c) {
+  const mv_accept_params& p = c->d.accept;
+  if (p.root_mode != MV_ROOT_SAMPLE && p.mode != MV_ACCEPT_REJECT) return MV_OK;
+  if (c->draws_used >= c->d.n_draws)
+    return fail(MV_ECAPACITY, "all %d rows of u_draws are used (prefill again or pass more)",
+                c->d.n_draws);
+  ++c->draws_used;
+  return MV_OK;
+}
 
 // All L layers; the last one leaves the final norm's operand in ws.xa / ws.ss.
 static int enq_layers(mv_ctx* c, const mv_tree& tree, float* x, hipStream_t s,
@@ -675,8 +745,9 @@ static int enq_step(mv_ctx* c, hipStream_t s) {
     return rc;
   prof_end(MV_K_LM_HEAD, s);
   prof_begin(s);
+  const int u_stride = d.accept.mode == MV_ACCEPT_REJECT ? B * T : B;
   if ((rc = enq_accept(B, T, D.V, D.d, d.logits, d.tree, d.tree_tok, d.accept, d.u_draws,
-                       d.u_index, B, d.accept_len, d.path, d.best, d.root_tok, d.emitted, nullptr,
+                       d.u_index, u_stride, d.accept_len, d.path, d.best, d.root_tok, d.emitted, nullptr,
                        x, d.final_norm, d.h_last, at<int32_t>(ws, L.amax), at<double>(ws, L.stats),
                        s, amaxp, d.n_prefix)))
     return rc;
@@ -714,12 +785,14 @@ MV_API int mv_ctx_create(mv_ctx** out, const mv_step_desc* desc) {
       return fail(MV_EINVAL, "layer %d has a NULL weight", l);
   }
   const mv_accept_params& p = d.accept;
-  if (p.mode != MV_ACCEPT_GREEDY && p.mode != MV_ACCEPT_TYPICAL) return fail(MV_EINVAL, "accept mode");
+  if (p.mode != MV_ACCEPT_GREEDY && p.mode != MV_ACCEPT_TYPICAL && p.mode != MV_ACCEPT_REJECT)
+    return fail(MV_EINVAL, "accept mode");
   if (p.root_mode != MV_ROOT_ARGMAX && p.root_mode != MV_ROOT_SAMPLE) return fail(MV_EINVAL, "root mode");
-  if ((p.mode == MV_ACCEPT_TYPICAL || p.root_mode == MV_ROOT_SAMPLE) && !(p.temperature > 0.0))
+  const bool draws = p.root_mode == MV_ROOT_SAMPLE || p.mode == MV_ACCEPT_REJECT;
+  if ((p.mode != MV_ACCEPT_GREEDY || p.root_mode == MV_ROOT_SAMPLE) && !(p.temperature > 0.0))
     return fail(MV_EINVAL, "temperature must be > 0");
-  if (p.root_mode == MV_ROOT_SAMPLE && (!d.u_draws || !d.u_index || d.n_draws < 1))
-    return fail(MV_EINVAL, "sampled roots need u_draws, u_index and n_draws");
+  if (draws && (!d.u_draws || !d.u_index || d.n_draws < 1))
+    return fail(MV_EINVAL, "sampled roots and rejection sampling need u_draws, u_index and n_draws");
   if ((size_t)d.B * d.dims.d * 4 > MV_HEADS_LDS_MAX) return fail(MV_EUNSUPPORTED, "B*d too large");
   if ((rc = check_ws(&d.dims, d.B, d.T, d.ws_bytes, d.ws))) return rc;
 
@@ -776,6 +849,7 @@ MV_API int mv_prefill(mv_ctx* c, const int32_t* ids, int32_t ld, const int32_t* 
   const mv_step_desc& d = c->d;
   const mv_dims& D = d.dims;
   const int B = d.B, T = d.T, M = B * T;
+  const bool reject = d.accept.mode == MV_ACCEPT_REJECT;   // draws [n][B][T]: root from [0][b][0]
   int nmax = 0;
   for (int b = 0; b < B; ++b) {
     if (n_ids[b] < 1 || n_ids[b] > d.kv.cap - T || n_ids[b] > ld)
@@ -814,20 +888,22 @@ MV_API int mv_prefill(mv_ctx* c, const int32_t* ids, int32_t ld, const int32_t* 
     MV_HIP(mvk::launch_row_stats(d.logits, M, D.V, MV_ACCEPT_GREEDY, 1.0, at<int32_t>(ws, L.amax),
                                  at<double>(ws, L.stats), s));
     MV_HIP(mvk::launch_prefill_select(d.logits, at<int32_t>(ws, L.amax), cnt, B, T, D.V,
-                                      d.accept.root_mode, d.accept.temperature, d.u_draws,
-                                      d.root_tok, d.n_prefix, x,
+                                      reject ? MV_ROOT_SAMPLE : d.accept.root_mode,
+                                      d.accept.temperature, d.u_draws, reject ? T : 1, d.root_tok, d.n_prefix, x,
                                       static_cast<const u16*>(d.final_norm),
                                       static_cast<u16*>(d.h_last), D.d, s));
     // the host-side counts buffer is reused next chunk: wait for the copy
     MV_HIP(hipStreamSynchronize(s));
   }
   if (d.u_index) MV_HIP(mvk::launch_fill_i32(d.u_index, 1, 1, s));
+  c->draws_used = 1;
   return MV_OK;
 }
 
 MV_API int mv_step(mv_ctx* c, int32_t use_graph, void* stream) {
   if (!c) return fail(MV_EINVAL, "mv_step: NULL context");
   const hipStream_t s = (hipStream_t)stream;
+  if (int rc = take_draw(c)) return rc;
   if (!use_graph) return enq_step(c, s);
   if (!c->exec) {
     MV_HIP(hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal));
@@ -849,6 +925,7 @@ MV_API int mv_step(mv_ctx* c, int32_t use_graph, void* stream) {
 MV_API int mv_step_profile(mv_ctx* c, float* ms, int32_t* count, void* stream) {
   if (!c || !ms || !count) return fail(MV_EINVAL, "mv_step_profile: NULL pointer");
   const hipStream_t s = (hipStream_t)stream;
+  if (int rc = take_draw(c)) return rc;
   if (c->prof_ev.empty()) {
     c->prof_ev.resize(2 * 1024);
     for (auto& e : c->prof_ev) MV_HIP(hipEventCreate(&e));

@@ -209,9 +209,18 @@ hipError_t launch_accept_finish(const float* logits, const int32_t* argmax, unsi
                                 hipStream_t s, int32_t* n_advance = nullptr);
 hipError_t launch_prefill_select(const float* logits, const int32_t* amax, const int32_t* cnt,
                                  int B, int T, int V, int root_mode, double temperature,
-                                 const double* u, int32_t* root, int32_t* n_prefix,
+                                 const double* u, int u_bstride, int32_t* root, int32_t* n_prefix,
                                  const float* x, const u16* final_norm, u16* h_last, int d,
                                  hipStream_t s);
+hipError_t launch_reject_accept(const float* logits, const int32_t* argmax, const double* stats,
+                                const int32_t* parent, const int32_t* tok, int B, int T, int V,
+                                int depth, double temperature, const float* draft,
+                                const double* dstats, const double* u, const int32_t* u_index,
+                                long long u_stride, double* resid, int32_t* accept_len,
+                                int32_t* path, int32_t* best, int32_t* next_root,
+                                int32_t* emitted, double* margin, const float* x,
+                                const u16* final_norm, u16* h_last, int d, hipStream_t s,
+                                int32_t* n_advance = nullptr);
 hipError_t launch_compact(u16* kc, u16* vc, int L, int B, int H, int hd, int cap,
                           const int32_t* path, int path_stride, const int32_t* accept_len,
                           const int32_t* n_prefix, hipStream_t s, int advanced = 0,

@@ -56,7 +56,7 @@ class Workload:
     tree: TreeSpec
     prefix: Tuple[int, int]        # prefix length range [lo, hi] (lo == hi: fixed)
     batch: int
-    accept: str                    # "greedy" | "typical"
+    accept: str                    # "greedy" | "typical" | "reject" (rejection sampling)
     root: str = "argmax"           # "argmax" | "sample" (typical with T > 0)
     temperature: float = 0.0
     eps: float = 0.0               # hard threshold of typical acceptance
@@ -121,6 +121,15 @@ LLAMA7B_T64_LONG_TYPICAL = Workload(
                 "eps=0.09 delta=0.3 T=0.7 with seeded draws, KV compaction",
 )
 
+LLAMA7B_T64_REJECT = LLAMA7B_T64.with_(
+    name="llama7b_shape_T64_n512_reject",
+    accept="reject",
+    root="sample",
+    temperature=0.7,
+    description="7B shape, prefix 512, 64-node sparse tree, rejection-sampling "
+                "acceptance (top-s candidates as point drafts) at T=0.7 with "
+                "seeded draws, bs1")
+
 _D13 = Dims(L=40, d=5120, H=40, hd=128, F=13824, V=32000, K=5)
 LLAMA13B_T16 = Workload(
     name="llama13b_shape_T16_n1024_greedy", dims=_D13, weight_dtype="bf16",
@@ -151,7 +160,7 @@ LLAMA33B_B4 = Workload(
                 "per-sequence compaction",
 )
 
-ALL = {w.name: w for w in (TINY, LLAMA7B_T64, LLAMA7B_T64_LONG_TYPICAL,
+ALL = {w.name: w for w in (TINY, LLAMA7B_T64, LLAMA7B_T64_LONG_TYPICAL, LLAMA7B_T64_REJECT,
                            LLAMA13B_T16, LLAMA13B_T64, LLAMA13B_T256,
                            LLAMA33B_B4)}
 

@@ -191,10 +191,11 @@ def prefix_ids(w: Workload) -> List[np.ndarray]:
     return out
 
 
-def uniform_draws(w: Workload, steps: int) -> np.ndarray:
-    """[steps][batch] uniforms in [0, 1) for sampled roots."""
+def uniform_draws(w: Workload, steps: int, nodes: int = 0) -> np.ndarray:
+    """[steps][batch] uniforms in [0, 1) for sampled roots, or
+    [steps][batch][nodes] for rejection sampling (one per tree node)."""
     g = np.random.Generator(np.random.PCG64(tensor_seed(w.seed_draws, "u")))
-    return g.random(size=(steps, w.batch))
+    return g.random(size=(steps, w.batch) + ((nodes,) if nodes else ()))
 
 
 def random_tokens(seed: int, n: int, V: int) -> np.ndarray:
