@@ -249,7 +249,10 @@ MV_API int mv_lm_head(const mv_dims* dims, int32_t M, const float* x, const void
  * u: device double [B] uniform draws in [0,1) (SAMPLE only, else NULL);
  * REJECT: device double [B][T], as mv_accept_reject takes them.
  * REJECT is mv_accept_reject with no draft logits (the margin holds its
- * values); eps, delta and root_mode are not read.
+ * values, its workspace is mv_accept_reject's); eps, delta and root_mode
+ * are not read.  Workspace (256-aligned parts): argmax int32 [B*T], row
+ * stats double [B*T][3] and, for TYPICAL, the rows' 256-id block sums
+ * double [B*T][ceil(V/256)] (used by the sampled root's draw).
  * Outputs (device): accept_len [B] (= depth of v*), path [B][depth+1] (node
  * indices root..v*, then -1), best [B], next_root [B]; optional: emitted
  * [B][depth+1] (tokens of the path, then -1), margin double [B][T+1]
@@ -289,11 +292,13 @@ MV_API int mv_accept(int32_t B, int32_t T, int32_t V, int32_t d, const float* lo
  * double [B][T+1] (u - keep probability for tested candidates, +inf
  * elsewhere; [T]: the final draw's distance to its bracketing cumulative
  * sums) and h_last (given x, final_norm) as mv_accept.
- * Workspace (each part 256-aligned): row argmax int32 [B*T] and row stats
- * double [B*T][3]; with draft logits also argmax int32 [B*depth], stats
+ * Workspace (each part 256-aligned): row argmax int32 [B*T], row stats
+ * double [B*T][3] and the rows' 256-id block sums double
+ * [B*T][ceil(V/256)]; with draft logits also argmax int32 [B*depth], stats
  * double [B*depth][3] of the draft rows and residuals double [B][2][V]:
- * align256(4*B*T) + align256(24*B*T), plus align256(4*B*depth) +
- * align256(24*B*depth) + 16*B*V with draft logits.  temperature > 0.
+ * align256(4*B*T) + align256(24*B*T) + align256(8*B*T*ceil(V/256)), plus
+ * align256(4*B*depth) + align256(24*B*depth) + 16*B*V with draft logits.
+ * temperature > 0.
  * Work is one workgroup per sequence after a pass over the T rows. */
 MV_API int mv_accept_reject(int32_t B, int32_t T, int32_t V, int32_t d, const float* logits,
                             const mv_tree* tree, const int32_t* tree_tok, double temperature,

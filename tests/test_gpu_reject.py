@@ -49,7 +49,7 @@ def _case(rng, B, T, V, depth, topk, bias=0.7):
 
 def _ws_bytes(B, T, V, depth, draft):
     a = lambda n: (n + 255) // 256 * 256
-    return a(4 * B * T) + a(24 * B * T) + (
+    return a(4 * B * T) + a(24 * B * T) + a(8 * B * T * ((V + 255) // 256)) + (
         a(4 * B * depth) + a(24 * B * depth) + 16 * B * V if draft else 0)
 
 

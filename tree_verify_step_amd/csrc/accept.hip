@@ -24,10 +24,11 @@ __device__ __forceinline__ bool better_iv(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
-// Block-wide (256 threads) argmax with lowest-index ties; result in all threads.
+// Block-wide (NW waves) argmax with lowest-index ties; result in all threads.
+template <int NW = 4>
 __device__ __forceinline__ void block_argmax(float& bv, int& bi) {
-  __shared__ float rv[4];
-  __shared__ int ri[4];
+  __shared__ float rv[NW];
+  __shared__ int ri[NW];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -45,7 +46,7 @@ __device__ __forceinline__ void block_argmax(float& bv, int& bi) {
   __syncthreads();
   bv = rv[0];
   bi = ri[0];
-  for (int w = 1; w < 4; ++w)
+  for (int w = 1; w < NW; ++w)
     if (better_iv(rv[w], ri[w], bv, bi)) {
       bv = rv[w];
       bi = ri[w];
@@ -53,15 +54,24 @@ __device__ __forceinline__ void block_argmax(float& bv, int& bi) {
   __syncthreads();
 }
 
+template <int NW = 4>
 __device__ __forceinline__ double block_sum_d(double v) {
-  __shared__ double rd[4];
+  __shared__ double rd[NW];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   v = warp_sum_d(v);
   if (lane == 0) rd[wave] = v;
   __syncthreads();
-  v = rd[0] + rd[1] + rd[2] + rd[3];
+  v = rd[0];
+  for (int w = 1; w < NW; ++w) v += rd[w];
   __syncthreads();
   return v;
+}
+
+// Sum over a wave in a fixed order, the same value in every lane.
+__device__ __forceinline__ double wave_total_d(double v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+  return __shfl(v, 0, 64);
 }
 
 // h[c] = bf16(x[c] * rsqrt(mean(x^2) + 1e-5) * g[c]) for one row of width d
@@ -128,53 +138,68 @@ __device__ void block_norm_row(const float* __restrict__ xr, const u16* __restri
   }
 }
 
-// Rows are read as float4 (V % 4 == 0), 4 independent loads in flight per
-// thread per iteration.
-__global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict__ logits, int V,
-                                                        int mode, double temperature,
-                                                        int32_t* __restrict__ amax,
-                                                        double* __restrict__ stats) {
+// Rows are read as float4 (V % 4 == 0) by 1024 threads (four waves per SIMD
+// hide the double-precision exp latency), 4 independent loads in flight per
+// thread per iteration.  Each wave-iteration covers one 256-id block (a lane
+// takes 4 consecutive ids), so the pass that sums the tempered exponentials
+// can also store each block's sum (bsum [rows][ceil(V/256)], optional) for
+// the inverse-CDF draws.
+constexpr int RS_NT = 1024, RS_NW = RS_NT / 64;
+__global__ __launch_bounds__(RS_NT) void row_stats_kernel(const float* __restrict__ logits, int V,
+                                                          int mode, double temperature,
+                                                          int32_t* __restrict__ amax,
+                                                          double* __restrict__ stats,
+                                                          double* __restrict__ bsum) {
   const int row = blockIdx.x;
   const float4* z4 = reinterpret_cast<const float4*>(logits + (size_t)row * V);
   const int V4 = V >> 2;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  for (int i0 = threadIdx.x; i0 < V4; i0 += 1024) {
+  for (int i0 = threadIdx.x; i0 < V4; i0 += 4 * RS_NT) {
     float4 v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * 256;
+      const int i = i0 + u * RS_NT;
       v[u] = i < V4 ? z4[i] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int id = (i0 + u * 256) * 4;
+      const int id = (i0 + u * RS_NT) * 4;
       if (better_iv(v[u].x, id, bv, bi)) { bv = v[u].x; bi = id; }
       if (better_iv(v[u].y, id + 1, bv, bi)) { bv = v[u].y; bi = id + 1; }
       if (better_iv(v[u].z, id + 2, bv, bi)) { bv = v[u].z; bi = id + 2; }
       if (better_iv(v[u].w, id + 3, bv, bi)) { bv = v[u].w; bi = id + 3; }
     }
   }
-  block_argmax(bv, bi);
+  block_argmax<RS_NW>(bv, bi);
   if (threadIdx.x == 0) amax[row] = bi;
   if (mode == MV_ACCEPT_GREEDY) return;
 
   const double inv_t = 1.0 / temperature;
   const double m = (double)bv;
+  const int nb = (V + 255) >> 8;
+  const int lane = threadIdx.x & 63;
   double S = 0.0;
-  for (int i0 = threadIdx.x; i0 < V4; i0 += 1024) {
+  for (int i0 = threadIdx.x; i0 < V4; i0 += 4 * RS_NT) {
     float4 v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * 256;
+      const int i = i0 + u * RS_NT;
       v[u] = i < V4 ? z4[i] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      S += exp(((double)v[u].x - m) * inv_t) + exp(((double)v[u].y - m) * inv_t) +
-           exp(((double)v[u].z - m) * inv_t) + exp(((double)v[u].w - m) * inv_t);
+    for (int u = 0; u < 4; ++u) {
+      const double part = (exp(((double)v[u].x - m) * inv_t) + exp(((double)v[u].y - m) * inv_t)) +
+                          (exp(((double)v[u].z - m) * inv_t) + exp(((double)v[u].w - m) * inv_t));
+      S += part;
+      const int blk = (i0 + u * RS_NT) >> 6;          // the same for the whole wave
+      if (bsum && blk < nb) {
+        const double t = wave_total_d(part);
+        if (lane == 0) bsum[(size_t)row * nb + blk] = t;
+      }
+    }
   }
-  S = block_sum_d(S);
+  S = block_sum_d<RS_NW>(S);
   if (mode != MV_ACCEPT_TYPICAL) {            // rejection sampling: max and normaliser only
     if (threadIdx.x == 0) {
       stats[(size_t)row * 3 + 0] = m;
@@ -184,11 +209,11 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict_
     return;
   }
   double Hs = 0.0;
-  for (int i0 = threadIdx.x; i0 < V4; i0 += 1024) {
+  for (int i0 = threadIdx.x; i0 < V4; i0 += 4 * RS_NT) {
     float4 v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * 256;
+      const int i = i0 + u * RS_NT;
       v[u] = i < V4 ? z4[i] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
     }
 #pragma unroll
@@ -201,7 +226,7 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict_
       }
     }
   }
-  Hs = block_sum_d(Hs);
+  Hs = block_sum_d<RS_NW>(Hs);
   if (threadIdx.x == 0) {
     stats[(size_t)row * 3 + 0] = m;
     stats[(size_t)row * 3 + 1] = S;
@@ -210,9 +235,9 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict_
 }
 
 hipError_t launch_row_stats(const float* logits, int rows, int V, int mode, double temperature,
-                            int32_t* argmax, double* stats, hipStream_t s) {
-  hipLaunchKernelGGL(row_stats_kernel, dim3(rows), dim3(256), 0, s, logits, V, mode, temperature,
-                     argmax, stats);
+                            int32_t* argmax, double* stats, hipStream_t s, double* bsum) {
+  hipLaunchKernelGGL(row_stats_kernel, dim3(rows), dim3(RS_NT), 0, s, logits, V, mode, temperature,
+                     argmax, stats, bsum);
   return hipGetLastError();
 }
 
@@ -227,8 +252,14 @@ hipError_t launch_row_stats(const float* logits, int rows, int V, int mode, doub
 // block sums finds the block where the cumulative weight crosses; one wave
 // rescans that block.  Returns false (writing nothing) when the total is 0.
 #define MV_DRAW_MAXB (MV_MAX_VOCAB / 256)   // 256-id blocks
-template <class W4>
-__device__ __forceinline__ bool block_draw(int V, double u, W4 w4, int32_t* out, double* margin) {
+// pre (optional): the 256-id block sums of the same weights, computed
+// elsewhere (row_stats); fix(bsum) lets thread 0 adjust them (removed ids).
+struct NoFix {
+  __device__ void operator()(double*) const {}
+};
+template <class W4, class Fix = NoFix>
+__device__ __forceinline__ bool block_draw(int V, double u, W4 w4, int32_t* out, double* margin,
+                                           const double* pre = nullptr, Fix fix = Fix()) {
   __shared__ double bsum[MV_DRAW_MAXB], bpre[MV_DRAW_MAXB];   // block sums, exclusive prefixes
   __shared__ double wtot[4];
   __shared__ int s_blk, s_last;
@@ -237,7 +268,9 @@ __device__ __forceinline__ bool block_draw(int V, double u, W4 w4, int32_t* out,
   const int nb = (V + 255) >> 8;
   // pass 1: block sums, lane partials in id order, then a fixed-order wave sum
   constexpr int UB = 8;               // blocks per wave in flight
-  for (int b0 = wave; b0 < nb; b0 += 4 * UB) {
+  if (pre)
+    for (int b = tid; b < nb; b += 256) bsum[b] = pre[b];
+  for (int b0 = wave; !pre && b0 < nb; b0 += 4 * UB) {
     double part[UB];
 #pragma unroll
     for (int j = 0; j < UB; ++j) {
@@ -257,7 +290,9 @@ __device__ __forceinline__ bool block_draw(int V, double u, W4 w4, int32_t* out,
       if (lane == 0 && b < nb) bsum[b] = v;
     }
   }
+  __syncthreads();
   if (tid == 0) {
+    fix(bsum);
     s_blk = 0x7fffffff;
     s_last = -1;
   }
@@ -375,7 +410,7 @@ __device__ __forceinline__ bool block_draw(int V, double u, W4 w4, int32_t* out,
 // Inverse-CDF sample of softmax(z * inv_t): block_draw over the unnormalised
 // weights exp((z_i - max) * inv_t).  Writes *out (and |cdf - u| to *margin).
 __device__ __forceinline__ void block_sample(const float* __restrict__ z, int V, int amax_id, double inv_t,
-                             double u, int32_t* out, double* margin) {
+                             double u, int32_t* out, double* margin, const double* pre = nullptr) {
   const double m = (double)z[amax_id];
   auto w4 = [&](int i0, double (&w)[4]) {
     const float4 v = *reinterpret_cast<const float4*>(z + i0);
@@ -384,7 +419,14 @@ __device__ __forceinline__ void block_sample(const float* __restrict__ z, int V,
     w[2] = exp(((double)v.z - m) * inv_t);
     w[3] = exp(((double)v.w - m) * inv_t);
   };
-  block_draw(V, u, w4, out, margin);
+  // no mass in the given block sums: recompute them; none at all (cannot
+  // happen for finite logits): the argmax
+  if (!block_draw(V, u, w4, out, margin, pre) && !(pre && block_draw(V, u, w4, out, margin)) &&
+      threadIdx.x == 0) {
+    *out = amax_id;
+    if (margin) *margin = 0.0;
+  }
+  __syncthreads();
 }
 
 __global__ __launch_bounds__(256) void accept_finish_kernel(
@@ -396,7 +438,7 @@ __global__ __launch_bounds__(256) void accept_finish_kernel(
     int32_t* __restrict__ accept_len, int32_t* __restrict__ path, int32_t* __restrict__ best_out,
     int32_t* __restrict__ next_root, int32_t* __restrict__ emitted, double* __restrict__ margin,
     const float* __restrict__ x, const u16* __restrict__ final_norm, u16* __restrict__ h_last,
-    int d, int32_t* __restrict__ n_advance) {
+    int d, int32_t* __restrict__ n_advance, const double* __restrict__ bsum) {
   __shared__ unsigned char pass[MV_MAXT], ok[MV_MAXT];
   __shared__ double lq[MV_MAXT], score[MV_MAXT];
   __shared__ int par[MV_MAXT], dep[MV_MAXT], tk[MV_MAXT];   // the tree, staged for the walk
@@ -533,7 +575,8 @@ __global__ __launch_bounds__(256) void accept_finish_kernel(
   }
   const double ub = u[(size_t)(u_index ? u_index[0] : 0) * u_stride + b];
   block_sample(logits + (size_t)brow * V, V, amax[best], inv_t, ub, next_root + b,
-               margin ? margin + (size_t)b * (T + 1) + T : nullptr);
+               margin ? margin + (size_t)b * (T + 1) + T : nullptr,
+               bsum ? bsum + (size_t)brow * ((V + 255) >> 8) : nullptr);
 }
 
 hipError_t launch_accept_finish(const float* logits, const int32_t* argmax, unsigned long long* amax_key,
@@ -545,12 +588,12 @@ hipError_t launch_accept_finish(const float* logits, const int32_t* argmax, unsi
                                 int32_t* accept_len, int32_t* path, int32_t* best,
                                 int32_t* next_root, int32_t* emitted, double* margin,
                                 const float* x, const u16* final_norm, u16* h_last, int d,
-                                hipStream_t s, int32_t* n_advance) {
+                                hipStream_t s, int32_t* n_advance, const double* bsum) {
   hipLaunchKernelGGL(accept_finish_kernel, dim3(B), dim3(256), 0, s, logits, argmax, amax_key,
                      stats,
                      parent, depth_of, tok, T, V, depth, mode, root_mode, temperature, eps, delta,
                      u, u_index, u_stride, accept_len, path, best, next_root, emitted, margin, x,
-                     final_norm, h_last, d, n_advance);
+                     final_norm, h_last, d, n_advance, bsum);
   return hipGetLastError();
 }
 
@@ -592,7 +635,7 @@ __global__ __launch_bounds__(256) void reject_accept_kernel(
     int32_t* __restrict__ best_out, int32_t* __restrict__ next_root,
     int32_t* __restrict__ emitted, double* __restrict__ margin, const float* __restrict__ x,
     const u16* __restrict__ final_norm, u16* __restrict__ h_last, int d,
-    int32_t* __restrict__ n_advance) {
+    int32_t* __restrict__ n_advance, const double* __restrict__ bsum) {
   // the tree and every per-candidate quantity the walk needs, in LDS
   __shared__ int par[MV_MAXT], tk[MV_MAXT];
   __shared__ int fch[MV_MAXT], nsib[MV_MAXT];   // first child, next sibling (T: none)
@@ -730,7 +773,9 @@ __global__ __launch_bounds__(256) void reject_accept_kernel(
       if (tid == 0) s_nodes[L] = cur;
       continue;
     }
-    // final draw from the residual at cur
+    // final draw from the residual at cur (the row's block sums, when
+    // given, replace the first pass over the row)
+    const double* pre = bsum ? bsum + (row0 + cur) * ((V + 255) >> 8) : nullptr;
     const double u0 = usel[0];
     double* mg = margin ? margin + row0 + b + T : nullptr;
     int32_t* out = next_root + b;
@@ -753,7 +798,14 @@ __global__ __launch_bounds__(256) void reject_accept_kernel(
           if (k == 3) w[3] = 0.0;
         }
       };
-      if (!block_draw(V, u0, w_res, out, mg)) block_draw(V, u0, e_of4, out, mg);
+      auto fix = [&](double* bs) {            // take the removed ids out of their blocks
+        for (int j = 0; j < nx; ++j) {
+          const int k = xs[j];
+          bs[k >> 8] = fmax(bs[k >> 8] - exp(((double)z[k] - m) * inv_t), 0.0);
+        }
+      };
+      if (!(pre ? block_draw(V, u0, w_res, out, mg, pre, fix) : block_draw(V, u0, w_res, out, mg)))
+        block_sample(z, V, amax_rows[row0 + cur], inv_t, u0, out, mg, pre);
     } else if (rb >= 0) {
       const double* Rb = R + (size_t)rb * V;
       auto w_r = [&](int i0, double (&w)[4]) {
@@ -762,7 +814,7 @@ __global__ __launch_bounds__(256) void reject_accept_kernel(
       };
       block_draw(V, u0, w_r, out, mg);
     } else {
-      block_draw(V, u0, e_of4, out, mg);
+      block_sample(z, V, amax_rows[row0 + cur], inv_t, u0, out, mg, pre);
     }
     break;
   }
@@ -788,12 +840,12 @@ hipError_t launch_reject_accept(const float* logits, const int32_t* argmax, cons
                                 int32_t* path, int32_t* best, int32_t* next_root,
                                 int32_t* emitted, double* margin, const float* x,
                                 const u16* final_norm, u16* h_last, int d, hipStream_t s,
-                                int32_t* n_advance) {
+                                int32_t* n_advance, const double* bsum) {
   if (T > MV_MAXT) return hipErrorInvalidValue;
   hipLaunchKernelGGL(reject_accept_kernel, dim3(B), dim3(256), 0, s, logits, argmax, stats, parent,
                      tok, T, V, depth, 1.0 / temperature, draft, dstats, u, u_index, u_stride, resid,
                      accept_len, path, best, next_root, emitted, margin, x, final_norm, h_last, d,
-                     n_advance);
+                     n_advance, bsum);
   return hipGetLastError();
 }
 

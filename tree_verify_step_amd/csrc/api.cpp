@@ -118,7 +118,7 @@ static GemmCfg gemm_cfg(const mv_dims& D, int kind, int Mp) {
 
 struct Ws {
   size_t x, xa, ao, ha, ss, q, rope, part, counters, hu, hz, topi, topv, tcv, tci, amax, amaxp,
-      stats, cnt, total;
+      stats, bsum, cnt, total;
   int ss_ld;    // floats per row of the sums-of-squares buffer
 };
 
@@ -168,6 +168,7 @@ static Ws ws_layout(const mv_dims& D, int B, int T) {
   w.amax = take((size_t)M * 4);
   w.amaxp = take((size_t)M * 8);
   w.stats = take((size_t)M * 3 * 8);
+  w.bsum = take((size_t)M * ((D.V + 255) / 256) * 8);   // rows' 256-id block sums
   w.cnt = take((size_t)B * 4);
   w.total = off;
   return w;
@@ -382,28 +383,30 @@ static int enq_accept(int B, int T, int V, int d, const float* logits, const mv_
                       const int32_t* u_index, int u_stride, int32_t* accept_len, int32_t* path,
                       int32_t* best, int32_t* next_root, int32_t* emitted, double* margin,
                       const float* x, const void* final_norm, void* h_last, int32_t* amax,
-                      double* stats, hipStream_t s, unsigned long long* amax_key = nullptr,
-                      int32_t* n_advance = nullptr) {
+                      double* stats, double* bsum, hipStream_t s,
+                      unsigned long long* amax_key = nullptr, int32_t* n_advance = nullptr) {
   if (p.mode == MV_ACCEPT_REJECT) {
-    MV_HIP(mvk::launch_row_stats(logits, B * T, V, p.mode, p.temperature, amax, stats, s));
+    MV_HIP(mvk::launch_row_stats(logits, B * T, V, p.mode, p.temperature, amax, stats, s, bsum));
     MV_HIP(mvk::launch_reject_accept(logits, amax, stats, t.parent, tok, B, T, V, t.depth,
                                      p.temperature, nullptr, nullptr, u, u_index, (long long)u_stride,
                                      nullptr, accept_len, path, best, next_root, emitted, margin,
                                      x, static_cast<const u16*>(final_norm),
-                                     static_cast<u16*>(h_last), d, s, n_advance));
+                                     static_cast<u16*>(h_last), d, s, n_advance, bsum));
     return MV_OK;
   }
   // greedy acceptance with the LM head's argmax keys needs no pass over the
   // logits; otherwise the rows' argmax (and typical statistics)
   if (!(amax_key && p.mode == MV_ACCEPT_GREEDY)) {
     amax_key = nullptr;
-    MV_HIP(mvk::launch_row_stats(logits, B * T, V, p.mode, p.temperature, amax, stats, s));
+    MV_HIP(mvk::launch_row_stats(logits, B * T, V, p.mode, p.temperature, amax, stats, s,
+                                 p.mode == MV_ACCEPT_GREEDY ? nullptr : bsum));
   }
   MV_HIP(mvk::launch_accept_finish(logits, amax, amax_key, stats, t.parent, t.depth_of, tok, B, T, V,
                                    t.depth, p.mode, p.root_mode, p.temperature, p.eps, p.delta, u,
                                    u_index, u_stride, accept_len, path, best, next_root, emitted,
                                    margin, x, static_cast<const u16*>(final_norm),
-                                   static_cast<u16*>(h_last), d, s, n_advance));
+                                   static_cast<u16*>(h_last), d, s, n_advance,
+                                   p.mode == MV_ACCEPT_GREEDY ? nullptr : bsum));
   return MV_OK;
 }
 
@@ -594,12 +597,17 @@ MV_API int mv_accept(int32_t B, int32_t T, int32_t V, int32_t d, const float* lo
   if ((x == nullptr) != (h_last == nullptr) || (x && !final_norm))
     return fail(MV_EINVAL, "x, final_norm and h_last go together");
   if (x && (d < 1 || d % 4)) return fail(MV_EINVAL, "d=%d", d);
-  // workspace: amax [B*T] int32 + stats [B*T][3] double
-  const size_t need = align256((size_t)B * T * 4) + (size_t)B * T * 24;
+  // workspace: amax [B*T] int32, stats [B*T][3] double, then (typical)
+  // the rows' 256-id block sums [B*T][ceil(V/256)] double
+  const size_t o_stats = align256((size_t)B * T * 4);
+  const size_t o_bsum = o_stats + align256((size_t)B * T * 24);
+  const bool sums = p->mode == MV_ACCEPT_TYPICAL;
+  const size_t need = o_bsum + (sums ? (size_t)B * T * ((V + 255) / 256) * 8 : 0);
   if (!ws || ws_bytes < need) return fail(MV_EWORKSPACE, "workspace %zu < %zu", ws_bytes, need);
   return enq_accept(B, T, V, d, logits, *tree, tree_tok, *p, u, nullptr, B, accept_len, path, best,
                     next_root, emitted, margin, x, final_norm, h_last, at<int32_t>(ws, 0),
-                    at<double>(ws, align256((size_t)B * T * 4)), (hipStream_t)stream);
+                    at<double>(ws, o_stats), sums ? at<double>(ws, o_bsum) : nullptr,
+                    (hipStream_t)stream);
 }
 
 MV_API int mv_accept_reject(int32_t B, int32_t T, int32_t V, int32_t d, const float* logits,
@@ -624,14 +632,15 @@ MV_API int mv_accept_reject(int32_t B, int32_t T, int32_t V, int32_t d, const fl
   // those of the draft rows and two residual rows per sequence
   const int Dr = draft_logits ? B * tree->depth : 0;
   const size_t o_stats = align256((size_t)B * T * 4);
-  const size_t o_damax = o_stats + align256((size_t)B * T * 24);
+  const size_t o_bsum = o_stats + align256((size_t)B * T * 24);
+  const size_t o_damax = o_bsum + align256((size_t)B * T * ((V + 255) / 256) * 8);
   const size_t o_dstats = o_damax + align256((size_t)Dr * 4);
   const size_t o_res = o_dstats + align256((size_t)Dr * 24);
   const size_t need = draft_logits ? o_res + (size_t)B * 2 * V * 8 : o_damax;
   if (!ws || ws_bytes < need) return fail(MV_EWORKSPACE, "workspace %zu < %zu", ws_bytes, need);
   const hipStream_t s = (hipStream_t)stream;
   MV_HIP(mvk::launch_row_stats(logits, B * T, V, MV_ACCEPT_REJECT, temperature, at<int32_t>(ws, 0),
-                               at<double>(ws, o_stats), s));
+                               at<double>(ws, o_stats), s, at<double>(ws, o_bsum)));
   if (draft_logits)
     MV_HIP(mvk::launch_row_stats(draft_logits, Dr, V, MV_ACCEPT_REJECT, temperature,
                                  at<int32_t>(ws, o_damax), at<double>(ws, o_dstats), s));
@@ -641,7 +650,7 @@ MV_API int mv_accept_reject(int32_t B, int32_t T, int32_t V, int32_t d, const fl
                                    nullptr, 0, draft_logits ? at<double>(ws, o_res) : nullptr,
                                    accept_len, path, best, next_root, emitted, margin, x,
                                    static_cast<const u16*>(final_norm), static_cast<u16*>(h_last),
-                                   d, s));
+                                   d, s, nullptr, at<double>(ws, o_bsum)));
   return MV_OK;
 }
 
@@ -749,7 +758,7 @@ static int enq_step(mv_ctx* c, hipStream_t s) {
   if ((rc = enq_accept(B, T, D.V, D.d, d.logits, d.tree, d.tree_tok, d.accept, d.u_draws,
                        d.u_index, u_stride, d.accept_len, d.path, d.best, d.root_tok, d.emitted, nullptr,
                        x, d.final_norm, d.h_last, at<int32_t>(ws, L.amax), at<double>(ws, L.stats),
-                       s, amaxp, d.n_prefix)))
+                       at<double>(ws, L.bsum), s, amaxp, d.n_prefix)))
     return rc;
   prof_end(MV_K_ACCEPT, s);
   prof_begin(s);

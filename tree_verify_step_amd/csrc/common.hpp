@@ -196,7 +196,7 @@ hipError_t launch_tree_fill(const int32_t* top_ids, const int32_t* root, const i
                             const int32_t* rank, int32_t* tok, int B, int T, int D, int s_top,
                             hipStream_t s);
 hipError_t launch_row_stats(const float* logits, int rows, int V, int mode, double temperature,
-                            int32_t* argmax, double* stats, hipStream_t s);
+                            int32_t* argmax, double* stats, hipStream_t s, double* bsum = nullptr);
 hipError_t launch_accept_finish(const float* logits, const int32_t* argmax, unsigned long long* amax_key,
                                 const double* stats,
                                 const int32_t* parent, const int32_t* depth_of,
@@ -206,7 +206,8 @@ hipError_t launch_accept_finish(const float* logits, const int32_t* argmax, unsi
                                 int32_t* accept_len, int32_t* path, int32_t* best,
                                 int32_t* next_root, int32_t* emitted, double* margin,
                                 const float* x, const u16* final_norm, u16* h_last, int d,
-                                hipStream_t s, int32_t* n_advance = nullptr);
+                                hipStream_t s, int32_t* n_advance = nullptr,
+                                const double* bsum = nullptr);
 hipError_t launch_prefill_select(const float* logits, const int32_t* amax, const int32_t* cnt,
                                  int B, int T, int V, int root_mode, double temperature,
                                  const double* u, int u_bstride, int32_t* root, int32_t* n_prefix,
@@ -220,7 +221,7 @@ hipError_t launch_reject_accept(const float* logits, const int32_t* argmax, cons
                                 int32_t* path, int32_t* best, int32_t* next_root,
                                 int32_t* emitted, double* margin, const float* x,
                                 const u16* final_norm, u16* h_last, int d, hipStream_t s,
-                                int32_t* n_advance = nullptr);
+                                int32_t* n_advance = nullptr, const double* bsum = nullptr);
 hipError_t launch_compact(u16* kc, u16* vc, int L, int B, int H, int hd, int cap,
                           const int32_t* path, int path_stride, const int32_t* accept_len,
                           const int32_t* n_prefix, hipStream_t s, int advanced = 0,
