@@ -175,6 +175,43 @@ MV_API int mv_tree_compile(const int32_t* paths, const int32_t* path_len, int32_
                            int32_t mask_words, int32_t* parent, int32_t* depth_of,
                            int32_t* rank, uint64_t* anc, int32_t* T_out);
 
+/* Calibrated sparse tree (Medusa paper digest, Method 4 "Optimized sparse
+ * tree", paper section 2.3.3; Pitfalls: heads taken as independent).
+ * acc: host double [K][s], acc[k][i] = measured accuracy of head k+1's
+ * i-th top prediction alone (see mv_head_accuracy), each in [0, 1].  A
+ * node with rank path (i_1..i_k) is estimated as acc[0][i_1] * ... *
+ * acc[k-1][i_k] (formed left to right); the tree grows from the root by
+ * repeatedly taking the connected node with the highest estimate (ties:
+ * the lexicographically smaller path) until n_nodes candidates or no node
+ * of depth <= min(max_depth, K) is left.  Outputs (host): paths
+ * [n_nodes][max_depth] (ranks, -1 padded) and path_len [n_nodes] in the
+ * flattened tree order (depth, then path; ready for mv_tree_compile),
+ * *n_out = nodes built, *expected_len (nullable) = the sum of their
+ * estimates (expected accepted candidates per step).  n_nodes <= MV_MAX_T-1,
+ * 1 <= max_depth <= MV_MAX_DEPTH, K <= MV_MAX_DEPTH, s <= MV_MAX_TOPK.
+ * Errors: MV_EINVAL. */
+MV_API int mv_tree_build_sparse(const double* acc, int32_t K, int32_t s, int32_t n_nodes,
+                                int32_t max_depth, int32_t* paths, int32_t* path_len,
+                                int32_t* n_out, double* expected_len);
+
+/* Calibration of the heads (Medusa paper digest, Method 4): for N
+ * calibration positions with the heads' ranked candidates top_ids (device
+ * int32 [N][K][s], e.g. mv_medusa_heads' top_ids) and the true tokens
+ * labels (device int32 [N][K], the token k+1 positions ahead for head
+ * k+1), add to counts (device int32 [K][s], caller-zeroed, accumulated
+ * across calls) the number of positions whose label equals head k+1's i-th
+ * candidate.  acc[k][i] = counts[k][i] / N.  N * K <= 2^30. */
+MV_API int mv_head_accuracy(int32_t N, int32_t K, int32_t s, const int32_t* top_ids,
+                            const int32_t* labels, int32_t* counts, void* stream);
+
+/* Expected acceptance length of a given tree under acc (as above): the sum
+ * over its n_paths nodes (host paths [n_paths][ld], path_len [n_paths]) of
+ * the products of accuracies along their rank paths.  Errors: MV_EINVAL,
+ * MV_ETREE (a rank >= s or a path longer than K). */
+MV_API int mv_tree_expected_length(const double* acc, int32_t K, int32_t s, const int32_t* paths,
+                                   const int32_t* path_len, int32_t n_paths, int32_t ld,
+                                   double* out);
+
 /* Reorder a row-major bf16 weight [rows][cols] (out, in) into the
  * fragment-packed layout the backbone GEMMs read.  layout MV_PACK_QKV: the
  * matrix is the fused [3d][d] q|k|v projection with head size hd; q and k

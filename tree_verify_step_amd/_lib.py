@@ -25,6 +25,7 @@ PACK_PLAIN, PACK_QKV = 0, 1
 
 EXPORTS = ("mv_strerror", "mv_last_error", "mv_tree_compile", "mv_pack_weight",
            "mv_workspace_size", "mv_medusa_heads", "mv_tree_attention", "mv_decoder_layer",
+           "mv_tree_build_sparse", "mv_tree_expected_length", "mv_head_accuracy",
            "mv_embed", "mv_lm_head", "mv_accept", "mv_accept_reject", "mv_kv_compact", "mv_ctx_create",
            "mv_ctx_destroy", "mv_prefill", "mv_step", "mv_step_profile", "mv_time_kernel", "mv_read_probe")
 
@@ -111,6 +112,9 @@ def lib() -> C.CDLL:
         "mv_accept_reject": (C.c_int, [i32, i32, i32, i32, vp, C.POINTER(Tree), vp, C.c_double,
                                        vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "mv_kv_compact": (C.c_int, [C.POINTER(KV), vp, i32, vp, vp, vp]),
+        "mv_tree_build_sparse": (C.c_int, [vp, i32, i32, i32, i32, vp, vp, vp, vp]),
+        "mv_tree_expected_length": (C.c_int, [vp, i32, i32, vp, vp, i32, i32, vp]),
+        "mv_head_accuracy": (C.c_int, [i32, i32, i32, vp, vp, vp, vp]),
         "mv_ctx_create": (C.c_int, [C.POINTER(vp), C.POINTER(StepDesc)]),
         "mv_ctx_destroy": (None, [vp]),
         "mv_prefill": (C.c_int, [vp, vp, i32, vp, vp]),
@@ -253,6 +257,42 @@ def accept_reject(B: int, T: int, V: int, d: int, logits, tree: Tree, tree_tok,
                                  ptr(x), ptr(final_norm), ptr(h_last), ptr(ws),
                                  ws.numel() * ws.element_size(), stream_ptr(stream)),
           "accept_reject")
+
+
+def tree_build_sparse(acc, n_nodes: int, max_depth: int):
+    """Greedy calibrated sparse tree (host): returns (paths, expected_len)."""
+    import numpy as np
+    a = np.ascontiguousarray(acc, dtype=np.float64)
+    K, s = a.shape
+    paths = np.zeros((max(n_nodes, 1), max_depth), dtype=np.int32)
+    lens = np.zeros(max(n_nodes, 1), dtype=np.int32)
+    n_out = C.c_int32(0)
+    e = C.c_double(0.0)
+    check(lib().mv_tree_build_sparse(a.ctypes.data, K, s, n_nodes, max_depth, paths.ctypes.data,
+                                     lens.ctypes.data, C.byref(n_out), C.byref(e)),
+          "tree_build_sparse")
+    return [tuple(int(r) for r in paths[v, :lens[v]]) for v in range(n_out.value)], e.value
+
+
+def tree_expected_length(acc, paths) -> float:
+    import numpy as np
+    a = np.ascontiguousarray(acc, dtype=np.float64)
+    K, s = a.shape
+    ld = max([len(p) for p in paths] + [1])
+    P = np.full((max(len(paths), 1), ld), -1, dtype=np.int32)
+    lens = np.zeros(max(len(paths), 1), dtype=np.int32)
+    for v, p in enumerate(paths):
+        P[v, :len(p)] = p
+        lens[v] = len(p)
+    out = C.c_double(0.0)
+    check(lib().mv_tree_expected_length(a.ctypes.data, K, s, P.ctypes.data, lens.ctypes.data,
+                                        len(paths), ld, C.byref(out)), "tree_expected_length")
+    return out.value
+
+
+def head_accuracy(N: int, K: int, s: int, top_ids, labels, counts, stream=None) -> None:
+    check(lib().mv_head_accuracy(N, K, s, ptr(top_ids), ptr(labels), ptr(counts),
+                                 stream_ptr(stream)), "head_accuracy")
 
 
 def kv_compact(kv: KV, path, path_stride: int, accept_len, n_prefix, stream=None) -> None:

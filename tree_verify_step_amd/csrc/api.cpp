@@ -413,6 +413,9 @@ static int enq_accept(int B, int T, int V, int d, const float* logits, const mv_
 }  // namespace mv
 
 namespace mvk {
+// heads.hip: calibration counts of the heads' ranks
+hipError_t launch_head_accuracy(const int32_t* top_ids, const int32_t* labels, int N, int K, int s,
+                                int32_t* counts, hipStream_t st);
 // Streaming read of buf (rows.hip: 4096 workgroups, each its own contiguous
 // slice; the bytes of the last partial 64 KiB of a slice are skipped).
 hipError_t launch_read_probe(const void* buf, size_t bytes, float* sink, hipStream_t s);
@@ -483,6 +486,17 @@ static int check_kv(const mv_kv* kv, const mv_dims* D, int B, int T) {
   if (kv->L != D->L || kv->B != B || kv->H != D->H || kv->hd != D->hd)
     return fail(MV_EINVAL, "kv shape (L=%d B=%d H=%d hd=%d) does not match", kv->L, kv->B, kv->H, kv->hd);
   if (kv->cap < T || kv->cap % 64) return fail(MV_ECAPACITY, "kv cap %d must be a multiple of 64 >= T", kv->cap);
+  return MV_OK;
+}
+
+MV_API int mv_head_accuracy(int32_t N, int32_t K, int32_t s, const int32_t* top_ids,
+                            const int32_t* labels, int32_t* counts, void* stream) {
+  if (N < 0 || K < 1 || K > MV_MAX_DEPTH || s < 1 || s > MV_MAX_TOPK)
+    return fail(MV_EINVAL, "mv_head_accuracy: N=%d K=%d s=%d", N, K, s);
+  if ((int64_t)N * K > ((int64_t)1 << 30)) return fail(MV_EINVAL, "N*K too large");
+  if (N > 0 && (!top_ids || !labels || !counts))
+    return fail(MV_EINVAL, "mv_head_accuracy: NULL pointer");
+  MV_HIP(mvk::launch_head_accuracy(top_ids, labels, N, K, s, counts, (hipStream_t)stream));
   return MV_OK;
 }
 

@@ -409,6 +409,31 @@ hipError_t launch_topk(const float* z, int rows, int V, int s_top, int32_t* ids,
 }
 
 // tok[b][v] = root[b] for v = 0, else top_ids[b][depth(v)-1][rank(v)].
+// Calibration counts of the heads' ranks (Medusa paper digest, Method 4:
+// accuracy of the i-th top prediction of head k alone): one thread per
+// (position, head) adds 1 to counts[k][i] for every rank i whose candidate
+// equals the label.  Integer atomics: the counts do not depend on order.
+__global__ __launch_bounds__(256) void head_accuracy_kernel(const int32_t* __restrict__ top_ids,
+                                                            const int32_t* __restrict__ labels,
+                                                            int NK, int K, int s,
+                                                            int32_t* __restrict__ counts) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= NK) return;
+  const int k = t % K;
+  const int lab = labels[t];
+  for (int i = 0; i < s; ++i)
+    if (top_ids[(size_t)t * s + i] == lab) atomicAdd(&counts[k * s + i], 1);
+}
+
+hipError_t launch_head_accuracy(const int32_t* top_ids, const int32_t* labels, int N, int K, int s,
+                                int32_t* counts, hipStream_t st) {
+  const int NK = N * K;
+  if (NK > 0)
+    hipLaunchKernelGGL(head_accuracy_kernel, dim3((NK + 255) / 256), dim3(256), 0, st, top_ids,
+                       labels, NK, K, s, counts);
+  return hipGetLastError();
+}
+
 __global__ void tree_fill_kernel(const int32_t* __restrict__ top_ids,
                                  const int32_t* __restrict__ root,
                                  const int32_t* __restrict__ depth_of,
