@@ -332,6 +332,18 @@ def main() -> int:
     sess.prefill(ids)
     torch.cuda.synchronize()
     log(f"[bench] setup + prefill {time.perf_counter() - t_setup:.1f} s")
+    # prefill throughput: the prompts again (the first pass loaded the kernels);
+    # the library waits for each chunk's host-side counts, so wall time is the
+    # device time plus that per-chunk round trip
+    t_pf = time.perf_counter()
+    sess.prefill(ids)
+    torch.cuda.synchronize()
+    prefill_ms = (time.perf_counter() - t_pf) * 1e3
+    n_chunks = (max(n0) + T - 1) // T
+    prefill = {"prompt_tokens": int(sum(n0)), "chunk_rows": T, "chunks": n_chunks,
+               "ms": round(prefill_ms, 3), "tokens_per_s": round(sum(n0) / prefill_ms * 1e3, 1)}
+    log(f"[bench] prefill of {sum(n0)} tokens in {n_chunks} chunks of {T} rows: "
+        f"{prefill_ms:.1f} ms ({prefill['tokens_per_s']:.0f} tokens/s)")
 
     for _ in range(W):
         sess.step(graph=True)
@@ -429,6 +441,7 @@ def main() -> int:
         "step_ms_mean": round(sum(step_ms) / K, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "prefill": prefill,
         "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in kernels.items()},
     }
     sess.close()
