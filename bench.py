@@ -49,6 +49,11 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_gate_up_llama7b_T64_traffic.
 CSRC = os.path.join(ROOT, "tree_verify_step_amd", "csrc")
 
 
+# prefill chunk rows (the most the tree-attention kernel takes): 256 rows per
+# pass over the weights instead of the tree's 64
+PREFILL_ROWS = 256
+
+
 def gemm_source_hash() -> str:
     """sha256 over the GEMM kernel source, the shared header and the GEMM
     launch table: the counters in the traffic summary hold only while these
@@ -317,7 +322,8 @@ def main() -> int:
     n0 = [len(x) for x in ids]
     trees = rt.DeviceTrees(paths, s)
     T, depth = trees.T, trees.depth
-    cap = ((max(n0) + T + (K + W + P + 4) * (depth + 1) + 63) // 64) * 64
+    chunk = max(T, PREFILL_ROWS)
+    cap = ((max(n0) + max(T, chunk) + (K + W + P + 4) * (depth + 1) + 63) // 64) * 64
     log(f"[bench] workload {w.name}: L={D.L} d={D.d} F={D.F} V={D.V} T={T} depth={depth} "
         f"B={B} n0={n0} cap={cap}")
     t_setup = time.perf_counter()
@@ -328,7 +334,7 @@ def main() -> int:
                           root_mode=tv.ROOT_ARGMAX if w.root == "argmax" else tv.ROOT_SAMPLE,
                           temperature=w.temperature, eps=w.eps, delta=w.delta)
     u = synth.uniform_draws(w, K + W + P + 4, T if w.accept == "reject" else 0)
-    sess = rt.Session(D, B, T, s, cap, dw, trees, acc, u_draws=u)
+    sess = rt.Session(D, B, T, s, cap, dw, trees, acc, u_draws=u, prefill_rows=chunk)
     sess.prefill(ids)
     torch.cuda.synchronize()
     log(f"[bench] setup + prefill {time.perf_counter() - t_setup:.1f} s")
@@ -339,10 +345,10 @@ def main() -> int:
     sess.prefill(ids)
     torch.cuda.synchronize()
     prefill_ms = (time.perf_counter() - t_pf) * 1e3
-    n_chunks = (max(n0) + T - 1) // T
-    prefill = {"prompt_tokens": int(sum(n0)), "chunk_rows": T, "chunks": n_chunks,
+    n_chunks = (max(n0) + chunk - 1) // chunk
+    prefill = {"prompt_tokens": int(sum(n0)), "chunk_rows": chunk, "chunks": n_chunks,
                "ms": round(prefill_ms, 3), "tokens_per_s": round(sum(n0) / prefill_ms * 1e3, 1)}
-    log(f"[bench] prefill of {sum(n0)} tokens in {n_chunks} chunks of {T} rows: "
+    log(f"[bench] prefill of {sum(n0)} tokens in {n_chunks} chunks of {chunk} rows: "
         f"{prefill_ms:.1f} ms ({prefill['tokens_per_s']:.0f} tokens/s)")
 
     for _ in range(W):

@@ -226,6 +226,11 @@ MV_API int mv_pack_weight(const void* src, void* dst, int32_t rows, int32_t cols
 MV_API int mv_workspace_size(const mv_dims* dims, int32_t B, int32_t T, int32_t cap,
                              size_t* bytes);
 
+/* Workspace bytes of a step context whose prefill runs in chunks of
+ * prefill_rows rows (0, or T <= prefill_rows <= MV_MAX_T). */
+MV_API int mv_workspace_size_prefill(const mv_dims* dims, int32_t B, int32_t T,
+                                     int32_t prefill_rows, size_t* bytes);
+
 /* ---- the step's operations ----------------------------------------------- */
 
 /* Medusa heads (Medusa paper digest, Method 1-2, Algorithm steps 1-2):
@@ -391,6 +396,11 @@ typedef struct {
   int32_t* top_ids;                /* [B][depth][s] per-head candidates */
   void* ws;
   size_t ws_bytes;
+  /* prefill chunk rows: 0 (chunks of T rows) or T..MV_MAX_T; a larger chunk
+   * raises the GEMMs' rows per weight byte.  With prefill_rows > T the
+   * workspace is mv_workspace_size_prefill's and the prefill's logits stay
+   * in it (the logits buffer holds only the step's). */
+  int32_t prefill_rows;
 } mv_step_desc;
 
 typedef struct mv_ctx mv_ctx;
@@ -402,11 +412,13 @@ MV_API int mv_ctx_create(mv_ctx** out, const mv_step_desc* desc);
 MV_API void mv_ctx_destroy(mv_ctx* ctx);
 
 /* Prefill: run the prompts through the backbone in chunks of up to T tokens
+ * (prefill_rows, when set)
  * as chain trees (parent = previous token, so the tree mask is the causal
  * mask), filling KV slots [0, n), then set h_last, root_tok (ARGMAX or SAMPLE
  * with draw 0 of u_draws; REJECT acceptance always samples) and
  * n_prefix = n.  ids: device int32 [B][ld];
- * n_ids: host int32 [B] (1 <= n <= cap - T); counter u_index is set to 1. */
+ * n_ids: host int32 [B] (1 <= n <= cap - chunk rows); counter u_index is
+ * set to 1. */
 MV_API int mv_prefill(mv_ctx* ctx, const int32_t* ids, int32_t ld, const int32_t* n_ids,
                       void* stream);
 

@@ -297,41 +297,49 @@ def test_full_dims_step_two_layers_teacher_forced(wname):
             assert max(kerr, verr) <= TOL * stages(l), (step, l, kerr, verr)
 
 
-def test_full_dims_prefill_two_layers_matches_causal_decoding():
-    """Prefill of a 200-token prompt at the 7B dims (2 of the 32 decoder
-    layers) through 64-row chain-tree chunks (64, 64, 64, 8: a ragged last
-    chunk): every prompt position's K/V rows, the last chunk's per-token
-    logits, h_last and the first root against the oracle's plain causal
-    forward (a chain tree is causal attention)."""
+@pytest.mark.parametrize("prefill_rows,n", [(0, 200), (256, 300)])
+def test_full_dims_prefill_two_layers_matches_causal_decoding(prefill_rows, n):
+    """Prefill of a prompt at the 7B dims (2 of the 32 decoder layers)
+    through chain-tree chunks with a ragged last chunk: 64-row chunks (64,
+    64, 64, 8), or 256-row chunks (256, 44).  Every prompt position's K/V
+    rows, h_last and the first root, and (64-row chunks, whose logits land in
+    the step's buffer) the last chunk's per-token logits, against the
+    oracle's plain causal forward (a chain tree is causal attention)."""
     w0 = configs.LLAMA7B_T64
     D = configs.Dims(L=2, d=w0.dims.d, H=w0.dims.H, hd=w0.dims.hd, F=w0.dims.F,
                      V=w0.dims.V, K=w0.dims.K)
     w = w0.with_(dims=D)
-    print("full-dims prefill: 200 tokens, L=2", flush=True)
+    print(f"full-dims prefill: {n} tokens, chunk rows {prefill_rows}, L=2", flush=True)
     Wt = synth.TorchDrawnWeights(w)
     s = synth.tree_topk(w)
     paths = synth.tree_paths(w, 0)
     trees = rt.DeviceTrees([paths], s)
-    n = 200
     ids = synth.random_tokens(4321, n, D.V)
-    cap = ((n + trees.T + 63) // 64) * 64
+    chunk = max(trees.T, prefill_rows)
+    cap = ((n + chunk + 63) // 64) * 64
     dw = rt.DeviceWeights(D, Wt.get)
     p = tv.AcceptParams(mode=tv.ACCEPT_GREEDY, root_mode=tv.ROOT_ARGMAX, temperature=0.0,
                         eps=0.0, delta=0.0)
-    sess = rt.Session(D, 1, trees.T, s, cap, dw, trees, p, debug=True)
+    sess = rt.Session(D, 1, trees.T, s, cap, dw, trees, p, debug=True, prefill_rows=prefill_rows)
     sess.prefill([ids])
     torch.cuda.synchronize()
     assert int(sess.n_prefix[0]) == n
     okv = om.KVCache(D.L, D.H, D.hd, cap)
     hn, logits = om.causal_forward(Wt.get, D.L, D.H, ids, 0, okv)
-    c0 = (n - 1) // trees.T * trees.T                 # first position of the last chunk
-    gl = sess.logits[0, :n - c0].cpu().numpy().astype(np.float64)
-    lerr = np.abs(gl - logits[c0:n]).max()
-    print(f"  last-chunk logits err {lerr:.4f}", flush=True)
-    assert lerr <= TOL * stages(D.L), lerr
+    bound = TOL * stages(D.L)
+    if prefill_rows == 0:
+        c0 = (n - 1) // chunk * chunk                 # first position of the last chunk
+        gl = sess.logits[0, :n - c0].cpu().numpy().astype(np.float64)
+        lerr = np.abs(gl - logits[c0:n]).max()
+        print(f"  last-chunk logits err {lerr:.4f}", flush=True)
+        assert lerr <= bound, lerr
+        assert int(sess.root_tok[0]) == oa.argmax_lowest(gl[n - 1 - c0])
+    else:                                             # the root is the argmax of the last row
+        top2 = np.sort(logits[n - 1])[-2:]
+        if top2[1] - top2[0] > 2 * bound:
+            assert int(sess.root_tok[0]) == oa.argmax_lowest(logits[n - 1])
     herr = np.abs(sess.h_last[0].float().cpu().numpy() - hn[n - 1]).max()
-    assert herr <= TOL * stages(D.L), herr
-    assert int(sess.root_tok[0]) == oa.argmax_lowest(gl[n - 1 - c0])
+    assert herr <= bound, herr
     kg = sess.kv.k_rows()[:, 0].float().cpu().numpy()
     vg = sess.kv.v_rows()[:, 0].float().cpu().numpy()
     for l in range(D.L):

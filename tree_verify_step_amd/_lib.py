@@ -26,6 +26,7 @@ PACK_PLAIN, PACK_QKV = 0, 1
 EXPORTS = ("mv_strerror", "mv_last_error", "mv_tree_compile", "mv_pack_weight",
            "mv_workspace_size", "mv_medusa_heads", "mv_tree_attention", "mv_decoder_layer",
            "mv_tree_build_sparse", "mv_tree_expected_length", "mv_head_accuracy",
+           "mv_workspace_size_prefill",
            "mv_embed", "mv_lm_head", "mv_accept", "mv_accept_reject", "mv_kv_compact", "mv_ctx_create",
            "mv_ctx_destroy", "mv_prefill", "mv_step", "mv_step_profile", "mv_time_kernel", "mv_read_probe")
 
@@ -75,7 +76,7 @@ class StepDesc(C.Structure):
                 ("tree_tok", C.c_void_p), ("logits", C.c_void_p), ("accept_len", C.c_void_p),
                 ("path", C.c_void_p), ("emitted", C.c_void_p), ("best", C.c_void_p),
                 ("head_logits", C.c_void_p), ("top_ids", C.c_void_p),
-                ("ws", C.c_void_p), ("ws_bytes", C.c_size_t)]
+                ("ws", C.c_void_p), ("ws_bytes", C.c_size_t), ("prefill_rows", C.c_int32)]
 
 
 _lib: Optional[C.CDLL] = None
@@ -113,6 +114,7 @@ def lib() -> C.CDLL:
                                        vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "mv_kv_compact": (C.c_int, [C.POINTER(KV), vp, i32, vp, vp, vp]),
         "mv_tree_build_sparse": (C.c_int, [vp, i32, i32, i32, i32, vp, vp, vp, vp]),
+        "mv_workspace_size_prefill": (C.c_int, [C.POINTER(Dims), i32, i32, i32, C.POINTER(sz)]),
         "mv_tree_expected_length": (C.c_int, [vp, i32, i32, vp, vp, i32, i32, vp]),
         "mv_head_accuracy": (C.c_int, [i32, i32, i32, vp, vp, vp, vp]),
         "mv_ctx_create": (C.c_int, [C.POINTER(vp), C.POINTER(StepDesc)]),
@@ -196,9 +198,13 @@ def read_probe(buf, sink, reps: int = 10, stream=None) -> float:
     return float(us[0])
 
 
-def workspace_size(dims: Dims, B: int, T: int, cap: int) -> int:
+def workspace_size(dims: Dims, B: int, T: int, cap: int, prefill_rows: int = 0) -> int:
     out = C.c_size_t(0)
-    check(lib().mv_workspace_size(C.byref(dims), B, T, cap, C.byref(out)), "workspace_size")
+    if prefill_rows > T:
+        check(lib().mv_workspace_size_prefill(C.byref(dims), B, T, prefill_rows, C.byref(out)),
+              "workspace_size_prefill")
+    else:
+        check(lib().mv_workspace_size(C.byref(dims), B, T, cap, C.byref(out)), "workspace_size")
     return out.value
 
 

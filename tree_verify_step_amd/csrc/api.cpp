@@ -118,7 +118,7 @@ static GemmCfg gemm_cfg(const mv_dims& D, int kind, int Mp) {
 
 struct Ws {
   size_t x, xa, ao, ha, ss, q, rope, part, counters, hu, hz, topi, topv, tcv, tci, amax, amaxp,
-      stats, bsum, cnt, total;
+      stats, bsum, cnt, plog, total;
   int ss_ld;    // floats per row of the sums-of-squares buffer
 };
 
@@ -132,18 +132,25 @@ static int ss_ld_of(const mv_dims& D, int Mp) {
   return (t + 3) & ~3;
 }
 
-static Ws ws_layout(const mv_dims& D, int B, int T) {
+// Row buffers hold B * max(T, P) rows: the step's T-row trees and, when it is
+// larger, the prefill's P-row chunks (P <= T: prefill uses T-row chunks).
+static Ws ws_layout(const mv_dims& D, int B, int T, int P = 0) {
   Ws w;
-  const int M = B * T, Mp = round16(M);
+  const int R = std::max(T, P);
+  const int M = B * R, Mp = round16(M);
   size_t part = 0, max_tiles = 1;
-  for (int k = 0; k < G_KINDS; ++k) {
-    const GemmCfg c = gemm_cfg(D, k, Mp);
-    const size_t tiles = (size_t)c.ntiles * c.mtiles;
-    if (c.splits > 1)
-      part = std::max(part, tiles * c.splits * c.w * c.MB * c.nbw * 256 * sizeof(float));
-    max_tiles = std::max(max_tiles, tiles);
+  w.ss_ld = 1;
+  for (const int Mq : {round16(B * T), P > T ? Mp : 0}) {
+    if (!Mq) continue;
+    for (int k = 0; k < G_KINDS; ++k) {
+      const GemmCfg c = gemm_cfg(D, k, Mq);
+      const size_t tiles = (size_t)c.ntiles * c.mtiles;
+      if (c.splits > 1)
+        part = std::max(part, tiles * c.splits * c.w * c.MB * c.nbw * 256 * sizeof(float));
+      max_tiles = std::max(max_tiles, tiles);
+    }
+    w.ss_ld = std::max(w.ss_ld, ss_ld_of(D, Mq));
   }
-  w.ss_ld = ss_ld_of(D, Mp);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -170,6 +177,7 @@ static Ws ws_layout(const mv_dims& D, int B, int T) {
   w.stats = take((size_t)M * 3 * 8);
   w.bsum = take((size_t)M * ((D.V + 255) / 256) * 8);   // rows' 256-id block sums
   w.cnt = take((size_t)B * 4);
+  w.plog = P > T ? take((size_t)B * P * D.V * 4) : 0;   // prefill chunks' logits
   w.total = off;
   return w;
 }
@@ -474,8 +482,21 @@ MV_API int mv_workspace_size(const mv_dims* dims, int32_t B, int32_t T, int32_t 
   return MV_OK;
 }
 
-static int check_ws(const mv_dims* dims, int B, int T, size_t ws_bytes, const void* ws) {
-  const size_t need = ws_layout(*dims, B, T).total;
+MV_API int mv_workspace_size_prefill(const mv_dims* dims, int32_t B, int32_t T,
+                                     int32_t prefill_rows, size_t* bytes) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_batch(B))) return rc;
+  if (T < 1 || T > MV_MAX_T) return fail(MV_EUNSUPPORTED, "T=%d outside [1,%d]", T, MV_MAX_T);
+  if (prefill_rows != 0 && (prefill_rows < T || prefill_rows > MV_MAX_T))
+    return fail(MV_EUNSUPPORTED, "prefill_rows=%d outside {0} or [T=%d, %d]", prefill_rows, T, MV_MAX_T);
+  if (!bytes) return fail(MV_EINVAL, "bytes is NULL");
+  *bytes = ws_layout(*dims, B, T, prefill_rows).total;
+  return MV_OK;
+}
+
+static int check_ws(const mv_dims* dims, int B, int T, size_t ws_bytes, const void* ws, int P = 0) {
+  const size_t need = ws_layout(*dims, B, T, P).total;
   if (!ws || ws_bytes < need)
     return fail(MV_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
   return MV_OK;
@@ -700,6 +721,7 @@ struct mv_ctx {
   uint64_t* chain_anc = nullptr; // [B][T][mask_words]
   int32_t* chunk_tok = nullptr;  // [B][T]
   std::vector<hipEvent_t> prof_ev;
+  int P = 0;                     // prefill chunk rows (>= T)
   int64_t draws_used = 1;        // draws of u_draws consumed (draw 0: the prefill's root)
 };
 
@@ -817,14 +839,21 @@ MV_API int mv_ctx_create(mv_ctx** out, const mv_step_desc* desc) {
   if (draws && (!d.u_draws || !d.u_index || d.n_draws < 1))
     return fail(MV_EINVAL, "sampled roots and rejection sampling need u_draws, u_index and n_draws");
   if ((size_t)d.B * d.dims.d * 4 > MV_HEADS_LDS_MAX) return fail(MV_EUNSUPPORTED, "B*d too large");
-  if ((rc = check_ws(&d.dims, d.B, d.T, d.ws_bytes, d.ws))) return rc;
+  if (d.prefill_rows != 0 && (d.prefill_rows < d.T || d.prefill_rows > MV_MAX_T))
+    return fail(MV_EUNSUPPORTED, "prefill_rows=%d outside {0} or [T=%d, %d]", d.prefill_rows, d.T,
+                MV_MAX_T);
+  const int Pr = std::max(d.T, (int)d.prefill_rows);
+  if (d.kv.cap < Pr) return fail(MV_ECAPACITY, "kv cap %d < prefill rows %d", d.kv.cap, Pr);
+  if ((rc = check_ws(&d.dims, d.B, d.T, d.ws_bytes, d.ws, Pr))) return rc;
 
   mv_ctx* c = new mv_ctx();
   c->d = d;
   c->layers.assign(d.layers, d.layers + d.dims.L);
   c->d.layers = nullptr;
-  c->L = ws_layout(d.dims, d.B, d.T);
-  const int B = d.B, T = d.T, mw = d.tree.mask_words;
+  c->L = ws_layout(d.dims, d.B, d.T, Pr);
+  c->P = Pr;
+  // the prefill chain tree: P rows per sequence
+  const int B = d.B, T = Pr, mw = (Pr + 63) / 64;
   std::vector<int32_t> ch(3 * (size_t)B * T);
   std::vector<uint64_t> ca((size_t)B * T * mw, 0);
   for (int b = 0; b < B; ++b)
@@ -871,20 +900,22 @@ MV_API int mv_prefill(mv_ctx* c, const int32_t* ids, int32_t ld, const int32_t* 
   if (!c || !ids || !n_ids) return fail(MV_EINVAL, "mv_prefill: NULL pointer");
   const mv_step_desc& d = c->d;
   const mv_dims& D = d.dims;
-  const int B = d.B, T = d.T, M = B * T;
+  // chunks of P rows (P = T unless a larger prefill chunk was asked for)
+  const int B = d.B, T = c->P, M = B * T;
   const bool reject = d.accept.mode == MV_ACCEPT_REJECT;   // draws [n][B][T]: root from [0][b][0]
   int nmax = 0;
   for (int b = 0; b < B; ++b) {
     if (n_ids[b] < 1 || n_ids[b] > d.kv.cap - T || n_ids[b] > ld)
-      return fail(MV_ECAPACITY, "prefix length %d of sequence %d outside [1, min(cap-T=%d, ld=%d)]",
+      return fail(MV_ECAPACITY, "prefix length %d of sequence %d outside [1, min(cap-P=%d, ld=%d)]",
                   n_ids[b], b, d.kv.cap - T, ld);
     nmax = std::max(nmax, (int)n_ids[b]);
   }
   const hipStream_t s = (hipStream_t)stream;
   void* ws = d.ws;
   const Ws& L = c->L;
-  mv_tree chain{T, T - 1, d.tree.mask_words, c->chain, c->chain + (size_t)B * T,
+  mv_tree chain{T, T - 1, (T + 63) / 64, c->chain, c->chain + (size_t)B * T,
                 c->chain + (size_t)2 * B * T, c->chain_anc};
+  float* logits = T > d.T ? at<float>(ws, L.plog) : d.logits;   // larger chunks: logits in ws
   MV_HIP(mvk::launch_fill_i32(d.n_prefix, 0, B, s));
   float* x = at<float>(ws, L.x);
   int32_t* cnt = at<int32_t>(ws, L.cnt);
@@ -905,14 +936,14 @@ MV_API int mv_prefill(mv_ctx* c, const int32_t* ids, int32_t ld, const int32_t* 
                              at<float2>(ws, L.rope), T, D.hd, s));
     if ((rc = enq_norm_prep(D, M, x, c->layers[0].attn_norm, ws, L, s))) return rc;
     if ((rc = enq_layers(c, chain, x, s))) return rc;
-    if ((rc = enq_lm_head(D, M, x, d.final_norm, d.lm_head, d.logits, ss_tiles_of(D, G_DOWN, M),
+    if ((rc = enq_lm_head(D, M, x, d.final_norm, d.lm_head, logits, ss_tiles_of(D, G_DOWN, M),
                           ws, L, s)))
       return rc;
-    MV_HIP(mvk::launch_row_stats(d.logits, M, D.V, MV_ACCEPT_GREEDY, 1.0, at<int32_t>(ws, L.amax),
+    MV_HIP(mvk::launch_row_stats(logits, M, D.V, MV_ACCEPT_GREEDY, 1.0, at<int32_t>(ws, L.amax),
                                  at<double>(ws, L.stats), s));
-    MV_HIP(mvk::launch_prefill_select(d.logits, at<int32_t>(ws, L.amax), cnt, B, T, D.V,
+    MV_HIP(mvk::launch_prefill_select(logits, at<int32_t>(ws, L.amax), cnt, B, T, D.V,
                                       reject ? MV_ROOT_SAMPLE : d.accept.root_mode,
-                                      d.accept.temperature, d.u_draws, reject ? T : 1, d.root_tok, d.n_prefix, x,
+                                      d.accept.temperature, d.u_draws, reject ? d.T : 1, d.root_tok, d.n_prefix, x,
                                       static_cast<const u16*>(d.final_norm),
                                       static_cast<u16*>(d.h_last), D.d, s));
     // the host-side counts buffer is reused next chunk: wait for the copy

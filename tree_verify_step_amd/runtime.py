@@ -183,7 +183,7 @@ class Session:
 
     def __init__(self, D, B: int, T: int, s_top: int, cap: int, weights: DeviceWeights,
                  trees: DeviceTrees, accept: L.AcceptParams, u_draws: Optional[np.ndarray] = None,
-                 dev="cuda", debug: bool = False):
+                 dev="cuda", debug: bool = False, prefill_rows: int = 0):
         self.D, self.B, self.T, self.s, self.cap = D, B, T, s_top, cap
         self.w, self.trees = weights, trees
         self.dims = dims_of(D)
@@ -203,7 +203,7 @@ class Session:
         self.path = torch.zeros(B, P, **i32)
         self.emitted = torch.zeros(B, P, **i32)
         self.best = torch.zeros(B, **i32)
-        nbytes = L.workspace_size(self.dims, B, T, cap)
+        nbytes = L.workspace_size(self.dims, B, T, cap, prefill_rows)
         self.ws = torch.zeros(nbytes, device=dev, dtype=torch.uint8)
         self.accept_params = accept
         desc = L.StepDesc()
@@ -230,6 +230,7 @@ class Session:
         desc.path = self.path.data_ptr()
         desc.emitted = self.emitted.data_ptr()
         desc.best = self.best.data_ptr()
+        desc.prefill_rows = prefill_rows
         if debug:
             self.head_logits = torch.zeros(B, max(trees.depth, 1), D.V, device=dev)
             self.top_ids = torch.zeros(B, max(trees.depth, 1), s_top, **i32)
