@@ -347,3 +347,31 @@ def test_full_dims_prefill_two_layers_matches_causal_decoding(prefill_rows, n):
         verr = np.abs(vg[l][:, :n] - okv.V[l][:, :n]).max()
         assert kerr <= TOL * stages(l) and verr <= TOL * stages(l), (l, kerr, verr)
     sess.close()
+
+
+@pytest.mark.parametrize("accept", ["typical", "reject"])
+def test_step_refuses_to_run_past_the_draws(accept):
+    """Sampled roots and rejection sampling take one row of u_draws per step
+    after the prefill's row 0: with 3 rows, two steps run and the third call
+    fails with MV_ECAPACITY before enqueuing anything; a new prefill starts
+    over."""
+    print(f"draw limit: {accept}", flush=True)
+    w = configs.TINY.with_(weight_dtype="bf16", accept=accept, root="sample", temperature=0.7,
+                           eps=0.09, delta=0.3)
+    nodes = otree.compile_tree(synth.tree_paths(w, 0)).T if accept == "reject" else 0
+    u = synth.uniform_draws(w, 3, nodes)
+    Wt, paths, sess = _session(w, 256, u=u)
+    ids = synth.prefix_ids(w)[0]
+    sess.prefill([ids])
+    sess.step(graph=True)
+    sess.step(graph=True)
+    torch.cuda.synchronize()
+    n2 = int(sess.n_prefix[0])
+    with pytest.raises(tv.MVError):
+        sess.step(graph=True)
+    torch.cuda.synchronize()
+    assert int(sess.n_prefix[0]) == n2          # nothing ran
+    sess.prefill([ids])
+    sess.step(graph=False)
+    torch.cuda.synchronize()
+    sess.close()

@@ -726,15 +726,21 @@ struct mv_ctx {
 };
 
 // A step that draws (sampled roots, rejection sampling) takes the next row of
-// u_draws: refuse to run past the last one.
-static int take_draw(mv_ctx* c) {
+// u_draws: refuse to run past the last one.  The row counts as used once the
+// step is enqueued (note_draw).
+static bool draws_rows(const mv_ctx* c) {
   const mv_accept_params& p = c->d.accept;
-  if (p.root_mode != MV_ROOT_SAMPLE && p.mode != MV_ACCEPT_REJECT) return MV_OK;
-  if (c->draws_used >= c->d.n_draws)
+  return p.root_mode == MV_ROOT_SAMPLE || p.mode == MV_ACCEPT_REJECT;
+}
+static int check_draw(const mv_ctx* c) {
+  if (draws_rows(c) && c->draws_used >= c->d.n_draws)
     return fail(MV_ECAPACITY, "all %d rows of u_draws are used (prefill again or pass more)",
                 c->d.n_draws);
-  ++c->draws_used;
   return MV_OK;
+}
+static int note_draw(mv_ctx* c, int rc) {
+  if (rc == MV_OK && draws_rows(c)) ++c->draws_used;
+  return rc;
 }
 
 // All L layers; the last one leaves the final norm's operand in ws.xa / ws.ss.
@@ -957,8 +963,8 @@ MV_API int mv_prefill(mv_ctx* c, const int32_t* ids, int32_t ld, const int32_t* 
 MV_API int mv_step(mv_ctx* c, int32_t use_graph, void* stream) {
   if (!c) return fail(MV_EINVAL, "mv_step: NULL context");
   const hipStream_t s = (hipStream_t)stream;
-  if (int rc = take_draw(c)) return rc;
-  if (!use_graph) return enq_step(c, s);
+  if (int rc = check_draw(c)) return rc;
+  if (!use_graph) return note_draw(c, enq_step(c, s));
   if (!c->exec) {
     MV_HIP(hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal));
     const int rc = enq_step(c, c->cap_stream);
@@ -973,13 +979,13 @@ MV_API int mv_step(mv_ctx* c, int32_t use_graph, void* stream) {
     MV_HIP(hipGraphInstantiate(&c->exec, c->graph, nullptr, nullptr, 0));
   }
   MV_HIP(hipGraphLaunch(c->exec, s));
-  return MV_OK;
+  return note_draw(c, MV_OK);
 }
 
 MV_API int mv_step_profile(mv_ctx* c, float* ms, int32_t* count, void* stream) {
   if (!c || !ms || !count) return fail(MV_EINVAL, "mv_step_profile: NULL pointer");
   const hipStream_t s = (hipStream_t)stream;
-  if (int rc = take_draw(c)) return rc;
+  if (int rc = check_draw(c)) return rc;
   if (c->prof_ev.empty()) {
     c->prof_ev.resize(2 * 1024);
     for (auto& e : c->prof_ev) MV_HIP(hipEventCreate(&e));
@@ -989,7 +995,7 @@ MV_API int mv_step_profile(mv_ctx* c, float* ms, int32_t* count, void* stream) {
   p.cap = 1024;
   p.n = 0;
   g_prof = &p;
-  const int rc = enq_step(c, s);
+  const int rc = note_draw(c, enq_step(c, s));
   g_prof = nullptr;
   if (rc) return rc;
   MV_HIP(hipEventSynchronize(p.ev[2 * p.n - 1]));
