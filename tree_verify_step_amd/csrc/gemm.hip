@@ -541,8 +541,11 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int w = 1; w < W; ++w)
           if (s_av[w][r] > bv || (s_av[w][r] == bv && s_ai[w][r] < bi)) { bv = s_av[w][r]; bi = s_ai[w][r]; }
-        __hip_atomic_fetch_max(g.amax_key + m, argmax_key(bv, bi), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+        // the max only grows: a key at or below the stored one cannot win,
+        // so most tiles skip the atomic (250 tiles share each row's key)
+        const unsigned long long key = argmax_key(bv, bi);
+        if (key > __hip_atomic_load(g.amax_key + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+          __hip_atomic_fetch_max(g.amax_key + m, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   } else if constexpr (EPI == EPI_ADD) {
