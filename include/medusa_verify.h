@@ -93,6 +93,14 @@ typedef enum {
 #define MV_PACK_PLAIN 0
 #define MV_PACK_QKV 1
 
+/* Bits of the step's device status word (mv_step_desc.status), OR-ed in by
+ * the step's kernels and never cleared by the library. */
+#define MV_STATUS_NONFINITE 1  /* the LM head wrote a non-finite logit for a tree row */
+#define MV_STATUS_CAPACITY 2   /* a step ran with n + T > cap on the device: its K/V
+                                * writes were clamped into the cache and its outputs
+                                * are not valid (only reachable when the host-side
+                                * bound given to mv_ctx_resume was wrong) */
+
 /* Backbone and head shapes.  Multi-head attention: H * hd == d.
  * Supported: d % 64 == 0, F % 32 == 0, V % 64 == 0, V <= MV_MAX_VOCAB,
  * hd in {16,32,64,128},
@@ -401,6 +409,9 @@ typedef struct {
    * workspace is mv_workspace_size_prefill's and the prefill's logits stay
    * in it (the logits buffer holds only the step's). */
   int32_t prefill_rows;
+  /* optional (NULL: none): device int32 status word, MV_STATUS_* bits OR-ed
+   * in by each step; the caller clears it. */
+  int32_t* status;
 } mv_step_desc;
 
 typedef struct mv_ctx mv_ctx;
@@ -422,13 +433,37 @@ MV_API void mv_ctx_destroy(mv_ctx* ctx);
 MV_API int mv_prefill(mv_ctx* ctx, const int32_t* ids, int32_t ld, const int32_t* n_ids,
                       void* stream);
 
+/* Declare a decode state that the caller placed in the bound buffers
+ * itself (KV cache, n_prefix, root_tok, h_last, u_index), instead of
+ * mv_prefill, e.g. to resume from a saved state.  n_host: host int32 [B],
+ * the values the caller wrote to n_prefix; they become the host-side bound
+ * on n that mv_step checks.  draws_used: rows of u_draws already consumed
+ * (the value in u_index; 1 after a prefill).  Errors: MV_EINVAL (NULL, or
+ * draws_used outside [0, n_draws]), MV_ECAPACITY (some n < 0 or n + T >
+ * cap); nothing is enqueued. */
+MV_API int mv_ctx_resume(mv_ctx* ctx, const int32_t* n_host, int32_t draws_used);
+
 /* One tree-verify step from the device-resident state.  graph != 0: the
  * step is captured into a hipGraph on the first call and replayed after;
- * graph == 0: the kernels are enqueued directly.  A step that draws
- * (SAMPLE roots, REJECT acceptance) uses the next row of u_draws; once the
- * prefill's row and one row per step have used all n_draws rows, the call
- * fails with MV_ECAPACITY and enqueues nothing. */
+ * graph == 0: the kernels are enqueued directly.
+ * Capacity: n lives on the device, so the context keeps a host-side upper
+ * bound on it -- the largest prefix length after mv_prefill (or
+ * mv_ctx_resume), plus depth + 1 (the most a step can accept) for every
+ * step enqueued since.  While bound + T > cap the call fails with
+ * MV_ECAPACITY and enqueues nothing (the bound is conservative: a step may
+ * be refused although the actual n would still fit).  Before the first
+ * mv_prefill or mv_ctx_resume the call fails with MV_EINVAL.
+ * A step that draws (SAMPLE roots, REJECT acceptance) uses the next row of
+ * u_draws; once the prefill's row and one row per step have used all
+ * n_draws rows, the call fails with MV_ECAPACITY and enqueues nothing. */
 MV_API int mv_step(mv_ctx* ctx, int32_t graph, void* stream);
+
+/* Device address of the verify pass's fp32 residual rows [B*T][d] inside
+ * the context's workspace: after a step (and until the next call that uses
+ * the workspace) they hold the rows after the last decoder layer, the input
+ * of the final RMSNorm and LM head.  For inspection only; NULL for a NULL
+ * context. */
+MV_API const float* mv_ctx_residual(const mv_ctx* ctx);
 
 /* Launch-group kinds reported by mv_step_profile. */
 #define MV_K_HEADS 0     /* Medusa heads: W1 block, vocab projection, top-s */

@@ -134,8 +134,10 @@ def greedy_accept_by_paths(tree: Tree, tok: np.ndarray, logits: np.ndarray):
 
 
 def typical_accept(tree: Tree, tok: np.ndarray, logits: np.ndarray, temperature: float,
-                   eps: float, delta: float) -> AcceptResult:
-    """Typical acceptance over the flattened tree (float64)."""
+                   eps: float, delta: float, given: Optional[dict] = None) -> AcceptResult:
+    """Typical acceptance over the flattened tree (float64).  `given` maps
+    node v to a decision of its edge taken as given instead of the threshold
+    test (tests pass the other side's decision at a declared near-tie)."""
     T = tree.T
     ok = np.zeros(T, dtype=bool)
     ok[0] = True
@@ -154,7 +156,8 @@ def typical_accept(tree: Tree, tok: np.ndarray, logits: np.ndarray, temperature:
         p = tree.parent[v]
         pv = float(np.exp(logq[p][tok[v]]))
         margin[v] = (pv - thr[p]) / thr[p] if thr[p] != 0 else np.inf
-        ok[v] = ok[p] and pv > thr[p]
+        passes = given[v] if given is not None and v in given else pv > thr[p]
+        ok[v] = ok[p] and passes
         score[v] = score[p] + logq[p][tok[v]]
     best = _best_node(tree, ok, score)
     path = tree.path_to(best)

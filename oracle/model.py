@@ -127,6 +127,12 @@ def forward_rows(get: WeightFn, L: int, H: int, tokens: np.ndarray, positions: n
     for l in range(L):
         x = decoder_layer(x, _layer_weights(get, l), kv.K[l], kv.V[l],
                           positions, slots, visible, H)
+    return final_head(get, x)
+
+
+def final_head(get: WeightFn, x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Final RMSNorm and LM head ("head 0") of residual rows x [M][d]:
+    (hn, logits = hn @ lm_head.T)."""
     hn = rmsnorm(x, get("final_norm"))
     return hn, hn @ f64(get("lm_head")).T
 

@@ -186,33 +186,25 @@ def stages(layers: int) -> int:
     return 2 * layers + 1
 
 
-@pytest.mark.parametrize("wname", [configs.LLAMA7B_T64.name, configs.LLAMA7B_T64_LONG_TYPICAL.name,
-                                   configs.LLAMA7B_T64_REJECT.name])
-def test_full_dims_step_two_layers_teacher_forced(wname):
-    """Two steps at the 7B dims (d = 4096, 32 x 128 heads, FFN 11008,
-    V = 32000, K = 4 Medusa heads, the workload's 64-node sparse tree; prefix
-    512 with greedy acceptance, or prefix 4096 with typical acceptance and
-    sampled roots; captured graph): every kernel runs in the launch
-    configuration of the timed step, with 2 decoder layers instead of 32 (no
-    launch shape depends on the layer count) so that the oracle finishes in
-    seconds.  Float outputs within the stated bounds, index work bit-exact
-    given the GPU's own logits, the oracle following the GPU's decisions."""
+def _full_dims_session(wname, L, steps, cache_weights=True):
+    """A step context at a 7B workload's dims with L decoder layers, holding
+    the state a prefill of the workload's prompt length leaves: seeded bf16
+    prefix K/V, a post-norm hidden state of unit scale and a root token
+    (declared to the context with resume).  Returns the pieces both sides
+    need."""
     w0 = configs.get(wname)
-    D = configs.Dims(L=2, d=w0.dims.d, H=w0.dims.H, hd=w0.dims.hd, F=w0.dims.F,
+    D = configs.Dims(L=L, d=w0.dims.d, H=w0.dims.H, hd=w0.dims.hd, F=w0.dims.F,
                      V=w0.dims.V, K=w0.dims.K)
     w = w0.with_(dims=D)
-    print(f"full-dims step: {w.name} with L=2", flush=True)
-    Wt = synth.TorchDrawnWeights(w)
+    Wt = synth.TorchDrawnWeights(w, cache=cache_weights)
     s = synth.tree_topk(w)
     paths = synth.tree_paths(w, 0)
     t = otree.compile_tree(paths)
     trees = rt.DeviceTrees([paths], s)
     assert trees.T == 64 and t.max_depth == 4
     n0 = synth.prefix_lengths(w)[0]
-    steps = 2
     cap = ((n0 + t.T + steps * (t.max_depth + 1) + 63) // 64) * 64
     dw = rt.DeviceWeights(D, Wt.get)
-    typical = w.accept == "typical"
     reject = w.accept == "reject"
     mode = {"greedy": tv.ACCEPT_GREEDY, "typical": tv.ACCEPT_TYPICAL,
             "reject": tv.ACCEPT_REJECT}[w.accept]
@@ -221,22 +213,34 @@ def test_full_dims_step_two_layers_teacher_forced(wname):
                         temperature=w.temperature, eps=w.eps, delta=w.delta)
     u = synth.uniform_draws(w, steps + 1, t.T if reject else 0)
     sess = rt.Session(D, 1, t.T, s, cap, dw, trees, p, u_draws=u, debug=True)
-    # the state a prefill of n0 tokens leaves: seeded bf16 prefix K/V, a
-    # post-norm hidden state of unit scale and a root token
     rng = np.random.default_rng(77)
     ocaches, kv = fill_prefix_kv(rng, D, 1, [n0], cap)
     sess.kv.k.copy_(kv.k)
     sess.kv.v.copy_(kv.v)
     del kv
-    okv = ocaches[0]
     h = synth.round_to_bf16(rng.standard_normal(D.d).astype(np.float32)).astype(np.float64)
     sess.h_last.copy_(torch.from_numpy(h.astype(np.float32)).to(torch.bfloat16).unsqueeze(0))
     t0 = int(rng.integers(D.V))
     sess.root_tok.fill_(t0)
     sess.n_prefix.fill_(n0)
     sess.u_index.fill_(1)              # a prefill consumes draw 0 for the first root
+    sess.resume([n0], 1)
     torch.cuda.synchronize()
-    n = n0
+    return dict(w=w, D=D, Wt=Wt, s=s, t=t, sess=sess, okv=ocaches[0], h=h, t0=t0, n0=n0, u=u)
+
+
+def _teacher_forced_steps(c, steps, exact_head=True):
+    """Run `steps` graph steps from the state of _full_dims_session and
+    compare each with the oracle, the oracle following the GPU's decisions.
+    Per-stage checks with identical inputs hold TOL: the head logits (from
+    the GPU's h_last) and the LM head (from the GPU's final residual rows).
+    The whole-forward drift of the tree logits, h_last and the K/V rows is
+    returned per step and held to the stage bound TOL * (2l + 1)."""
+    w, D, Wt, s, t, sess, okv = c["w"], c["D"], c["Wt"], c["s"], c["t"], c["sess"], c["okv"]
+    h, t0, n, u = c["h"], c["t0"], c["n0"], c["u"]
+    n0 = n
+    reject = w.accept == "reject"
+    drift = []
     for step in range(steps):
         sess.step(graph=True)
         torch.cuda.synchronize()
@@ -248,17 +252,21 @@ def test_full_dims_step_two_layers_teacher_forced(wname):
         np.testing.assert_array_equal(top, oh.head_topk(hz, s))
         tok = otree.fill_tokens(t, t0, top)
         np.testing.assert_array_equal(sess.tree_tok[0].cpu().numpy(), tok)
-        hn, logits = om.tree_forward(Wt.get, D.L, D.H, t, tok, n, okv)
         gl = sess.logits[0].cpu().numpy().astype(np.float64)
-        # each decoder layer adds two rounding stages (attention block, FFN
-        # block) whose errors reach the logits through the residual stream; the
-        # final norm + LM head is one more: the per-stage bound TOL adds up
+        # the LM-head stage on the GPU's own final residual rows
+        xg = sess.residual().cpu().numpy().astype(np.float64)
+        _, lm_want = om.final_head(Wt.get, xg)
+        lm_err = np.abs(gl - lm_want).max()
+        assert lm_err <= TOL, (step, lm_err)
+        # the whole forward against the oracle's own
+        hn, logits = om.tree_forward(Wt.get, D.L, D.H, t, tok, n, okv)
         lerr = np.abs(gl - logits).max()
-        print(f"  step {step}: head logits err {np.abs(hz - want_z).max():.2e}, tree logits err "
-              f"max {lerr:.4f} rms {np.sqrt(np.mean((gl - logits) ** 2)):.5f} (logits rms "
+        print(f"  step {step}: head logits err {np.abs(hz - want_z).max():.2e}, LM-head stage err "
+              f"{lm_err:.2e}, tree logits drift max {lerr:.4f} rms "
+              f"{np.sqrt(np.mean((gl - logits) ** 2)):.5f} (logits rms "
               f"{np.sqrt(np.mean(logits ** 2)):.3f})", flush=True)
         assert lerr <= TOL * stages(D.L), (step, lerr)
-        if typical:
+        if w.accept == "typical":
             res = oa.typical_accept(t, tok, gl, w.temperature, w.eps, w.delta)
         elif reject:
             res = oa.reject_accept(t, tok, gl, w.temperature, u[step + 1, 0])
@@ -288,6 +296,7 @@ def test_full_dims_step_two_layers_teacher_forced(wname):
         assert int(sess.n_prefix[0]) == n
         kg = sess.kv.k_rows()[:, 0].float().cpu().numpy()
         vg = sess.kv.v_rows()[:, 0].float().cpu().numpy()
+        kvd = []
         for l in range(D.L):
             np.testing.assert_array_equal(kg[l][:, :n0], okv.K[l][:, :n0])
             np.testing.assert_array_equal(vg[l][:, :n0], okv.V[l][:, :n0])
@@ -295,6 +304,73 @@ def test_full_dims_step_two_layers_teacher_forced(wname):
             kerr = np.abs(kg[l][:, :n] - okv.K[l][:, :n]).max()
             verr = np.abs(vg[l][:, :n] - okv.V[l][:, :n]).max()
             assert max(kerr, verr) <= TOL * stages(l), (step, l, kerr, verr)
+            kvd.append(max(kerr, verr))
+        drift.append(dict(logits=lerr, h_last=herr, kv_last_layer=kvd[-1]))
+        print(f"  step {step}: h_last drift {herr:.4f}, K/V drift of the last layer "
+              f"{kvd[-1]:.4f}", flush=True)
+    assert int(sess.status[0]) == 0
+    return drift
+
+
+@pytest.mark.parametrize("wname", [configs.LLAMA7B_T64.name, configs.LLAMA7B_T64_LONG_TYPICAL.name,
+                                   configs.LLAMA7B_T64_REJECT.name])
+def test_full_dims_step_two_layers_teacher_forced(wname):
+    """Two steps at the 7B dims (d = 4096, 32 x 128 heads, FFN 11008,
+    V = 32000, K = 4 Medusa heads, the workload's 64-node sparse tree; prefix
+    512 with greedy acceptance, or prefix 4096 with typical acceptance and
+    sampled roots; captured graph): every kernel runs in the launch
+    configuration of the timed step, with 2 decoder layers instead of 32 (no
+    launch shape depends on the layer count) so that the oracle finishes in
+    seconds.  Float outputs within the stated bounds, index work bit-exact
+    given the GPU's own logits, the oracle following the GPU's decisions."""
+    print(f"full-dims step: {wname} with L=2", flush=True)
+    c = _full_dims_session(wname, 2, 2)
+    _teacher_forced_steps(c, 2)
+    c["sess"].close()
+
+
+@pytest.mark.timeout(900)
+def test_full_dims_step_32_layers_teacher_forced():
+    """The headline workload at full depth: 32 decoder layers at the 7B dims,
+    two graph steps against the oracle.  Head logits and the LM-head stage
+    hold TOL on identical inputs; index work is bit-exact given the GPU's
+    logits; the drift of the tree logits, h_last and K/V after 32 layers is
+    printed and held to the stage bound."""
+    print("full-dims step: 32 layers", flush=True)
+    c = _full_dims_session(configs.LLAMA7B_T64.name, 32, 2)
+    drift = _teacher_forced_steps(c, 2)
+    print(f"  32-layer drift: {drift}", flush=True)
+    c["sess"].close()
+
+
+@pytest.mark.parametrize("wname", [configs.LLAMA7B_T64.name, configs.LLAMA7B_T64_LONG_TYPICAL.name])
+def test_step_replay_is_bit_identical(wname):
+    """Determinism: the captured step replayed twice from the same saved
+    decode state gives bit-identical head logits, tree logits, residual rows,
+    acceptance outputs, next root, h_last and KV cache (the split-K exchange
+    sums partials in split order; the LM head's argmax keys are an exact
+    maximum)."""
+    print(f"replay determinism: {wname} with L=2", flush=True)
+    c = _full_dims_session(wname, 2, 4)
+    sess = c["sess"]
+    state = [x.clone() for x in (sess.kv.k, sess.kv.v, sess.n_prefix, sess.root_tok, sess.h_last,
+                                 sess.u_index)]
+    outs = []
+    for rep in range(2):
+        for dst, src in zip((sess.kv.k, sess.kv.v, sess.n_prefix, sess.root_tok, sess.h_last,
+                             sess.u_index), state):
+            dst.copy_(src)
+        sess.resume([c["n0"]], 1)
+        for _ in range(2):
+            sess.step(graph=True)
+        torch.cuda.synchronize()
+        outs.append([x.clone() for x in (sess.head_logits, sess.top_ids, sess.tree_tok,
+                                         sess.logits, sess.residual(), sess.accept_len, sess.path,
+                                         sess.best, sess.root_tok, sess.h_last, sess.n_prefix,
+                                         sess.kv.k, sess.kv.v)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    sess.close()
 
 
 @pytest.mark.parametrize("prefill_rows,n", [(0, 200), (256, 300)])
@@ -374,4 +450,74 @@ def test_step_refuses_to_run_past_the_draws(accept):
     sess.prefill([ids])
     sess.step(graph=False)
     torch.cuda.synchronize()
+    sess.close()
+
+
+def test_step_refuses_to_overrun_the_cache():
+    """n lives on the device, so the context bounds it on the host: the
+    prefill's length plus depth + 1 per step.  With a 32-token prompt, a
+    15-node tree of depth 3 and 64 cache slots, five steps fit (bound 52 + 15
+    > 64 after them); the sixth call fails with MV_ECAPACITY before enqueuing
+    anything, and the status word stays clean."""
+    print("capacity bound", flush=True)
+    w = configs.TINY.with_(weight_dtype="bf16")
+    Wt, paths, sess = _session(w, 64, debug=False)
+    ids = synth.prefix_ids(w)[0]
+    assert len(ids) == 32 and sess.T == 15 and sess.trees.depth == 3
+    sess.prefill([ids])
+    for _ in range(5):
+        sess.step(graph=True)
+    torch.cuda.synchronize()
+    n5 = int(sess.n_prefix[0])
+    assert 32 + 5 <= n5 <= 32 + 5 * 4
+    with pytest.raises(tv.MVError) as e:
+        sess.step(graph=True)
+    assert e.value.status == tv._lib.ECAPACITY
+    torch.cuda.synchronize()
+    assert int(sess.n_prefix[0]) == n5          # nothing ran
+    assert int(sess.status[0]) == 0
+    sess.prefill([ids])                          # a new prefill starts over
+    sess.step(graph=True)
+    torch.cuda.synchronize()
+    assert int(sess.status[0]) == 0
+    sess.close()
+
+
+def test_step_without_state_is_refused():
+    print("no decode state", flush=True)
+    w = configs.TINY.with_(weight_dtype="bf16")
+    Wt, paths, sess = _session(w, 128, debug=False)
+    with pytest.raises(tv.MVError) as e:
+        sess.step(graph=False)
+    assert e.value.status == -1
+    with pytest.raises(tv.MVError):
+        sess.resume([128 - 15 + 1], 1)          # n + T > cap
+    sess.close()
+
+
+def test_status_word_flags_capacity_and_nonfinite_logits():
+    """The status word, forced from the host without any out-of-bounds
+    access: (1) a device prefix length past cap - T under a host bound that
+    says otherwise (the kernels clamp their cache indices) sets
+    MV_STATUS_CAPACITY; (2) an LM head of NaNs sets MV_STATUS_NONFINITE."""
+    print("status word", flush=True)
+    w = configs.TINY.with_(weight_dtype="bf16")
+    Wt, paths, sess = _session(w, 64, debug=False)
+    ids = synth.prefix_ids(w)[0]
+    sess.prefill([ids])
+    sess.step(graph=False)
+    torch.cuda.synchronize()
+    assert int(sess.status[0]) == 0
+    sess.n_prefix.fill_(64 - 15 + 3)             # the device n, past cap - T
+    sess.resume([0], 1)                          # ... while the host is told 0
+    sess.step(graph=False)
+    torch.cuda.synchronize()
+    assert int(sess.status[0]) == tv._lib.STATUS_CAPACITY
+    sess.status.zero_()
+    sess.prefill([ids])
+    sess.w.lm_head.fill_(float("nan"))
+    sess.step(graph=False)
+    torch.cuda.synchronize()
+    assert int(sess.status[0]) & tv._lib.STATUS_NONFINITE
+    assert not (int(sess.status[0]) & tv._lib.STATUS_CAPACITY)
     sess.close()

@@ -12,6 +12,7 @@ import torch
 import tree_verify_step_amd as tv
 from tree_verify_step_amd import runtime as rt
 from oracle import accept as oa
+from oracle import decode as od
 from oracle import heads as oh
 from oracle import model as om
 from oracle import tree as otree
@@ -176,20 +177,30 @@ def _layer_case(D, B, ns, paths_per_seq, topk, seed, gain_std=0.1):
     ("tiny_b4", 4, [20, 3, 50, 7]),     # 16-wide heads in 256-row tiles (one block per wave)
     ("wide_f", 2, [30, 9]),    # 1026 gate/up blocks: 10-wave tiles of 5 feature blocks
     ("llama7b", 1, [512]),     # the bench's shapes, tree and launch configuration
+    # the 13B workload's 256-node Cartesian tree (4 mask words, 256-row tiles)
+    ("llama13b_T256", 1, [1024]),
+    # the 33B batch: four sequences, their own sparse trees and ragged prefixes
+    ("llama33b_B4", 4, None),
 ])
 def test_decoder_layer_matches_oracle(name, B, ns):
+    wl = {"llama7b": configs.LLAMA7B_T64, "llama13b_T256": configs.LLAMA13B_T256,
+          "llama33b_B4": configs.LLAMA33B_B4}.get(name)
+    if ns is None:
+        ns = synth.prefix_lengths(wl)
     _flush(f"decoder_layer {name} B={B} ns={ns}")
     D = {"tiny": configs.TINY.dims, "tiny_b4": configs.TINY.dims,
          "mid": configs.Dims(L=1, d=256, H=2, hd=128, F=512, V=512, K=3),
          "mid_f480": configs.Dims(L=1, d=256, H=2, hd=128, F=480, V=512, K=3),
-         "wide_f": configs.Dims(L=1, d=128, H=1, hd=128, F=16416, V=512, K=3),
-         "llama7b": configs.LLAMA7B_T64.dims}[name]
-    D = configs.Dims(L=1, d=D.d, H=D.H, hd=D.hd, F=D.F, V=D.V, K=D.K)
+         "wide_f": configs.Dims(L=1, d=128, H=1, hd=128, F=16416, V=512, K=3)}.get(name)
+    if wl is not None:
+        D = wl.dims
+    # one layer; a small vocabulary (the layer reads no vocab-sized weight)
+    D = configs.Dims(L=1, d=D.d, H=D.H, hd=D.hd, F=D.F, V=512, K=D.K)
     rng = np.random.default_rng(11)
     if name == "tiny":
         paths = [synth.cartesian_paths((2, 2, 2))] * B
-    elif name == "llama7b":
-        paths = [synth.tree_paths(configs.LLAMA7B_T64, 0)]
+    elif wl is not None:
+        paths = [synth.tree_paths(wl, b) for b in range(B)]
     else:
         paths = random_trees(rng, B, 63, 4, 6)
     Wt, trees, ocaches, kv, x, cap = _layer_case(D, B, ns, paths, 10, 2024 + B)
@@ -341,11 +352,17 @@ def test_accept_matches_oracle_given_gpu_logits(mode, root, B, T):
             res = oa.greedy_accept(t, tok, logits[b])
         else:
             res = oa.typical_accept(t, tok, logits[b], temp, eps, delta)
-            m = res.margin[1:]
-            if np.any(np.abs(m[np.isfinite(m)]) <= 1e-5):
-                near += 1
-                continue
-            np.testing.assert_allclose(o["margin"][b, 1:T], res.margin[1:], rtol=1e-9, atol=1e-12)
+            # a declared near-tie (|q - thr| <= 1e-5 thr): the oracle takes the
+            # GPU's decision of that edge (the sign of its margin), and every
+            # other output of the sequence is still compared
+            tie = {v: bool(o["margin"][b, v] > 0) for v in range(1, T)
+                   if abs(res.margin[v]) <= 1e-5}
+            if tie:
+                near += len(tie)
+                res = oa.typical_accept(t, tok, logits[b], temp, eps, delta, given=tie)
+            keep = np.array([v not in tie for v in range(1, T)])
+            np.testing.assert_allclose(o["margin"][b, 1:T][keep], res.margin[1:][keep], rtol=1e-9,
+                                       atol=1e-12)
         assert o["accept_len"][b] == res.accept_len
         assert o["best"][b] == res.best
         np.testing.assert_array_equal(o["path"][b, :res.accept_len + 1], res.path)
@@ -361,7 +378,7 @@ def test_accept_matches_oracle_given_gpu_logits(mode, root, B, T):
         want_h = om.rmsnorm(xres[b * T + res.best].astype(np.float64), gain)
         got_h = outs["h_last"][b].float().cpu().numpy()
         np.testing.assert_allclose(got_h, want_h, rtol=8e-3, atol=1e-6)
-    assert near <= max(1, B // 4)
+    assert near <= 1          # near-ties are rare: at most one edge of the <= 1024 here
 
 
 # ---------------------------------------------------------------- compaction
@@ -388,12 +405,14 @@ def test_kv_compact_bit_exact(B):
     k1, v1 = kv.k_rows().cpu(), kv.v_rows().cpu()
     k0, v0 = k0.cpu(), v0.cpu()
     for b in range(B):
-        n = ns[b]
-        ek, ev = k0.clone(), v0.clone()
-        src = [n + int(p) for p in paths[b, :lens[b] + 1]]
-        dst = [n + m for m in range(lens[b] + 1)]
-        ek[:, b, :, dst] = k0[:, b, :, src]
-        ev[:, b, :, dst] = v0[:, b, :, src]
-        assert torch.equal(k1[:, b], ek[:, b])
-        assert torch.equal(v1[:, b], ev[:, b])
+        # the oracle's compaction of this sequence's cache (bf16 values are
+        # exact in float64)
+        oc = om.KVCache(D.L, D.H, D.hd, cap)
+        for l in range(D.L):
+            oc.K[l][:] = k0[l, b].double().numpy()
+            oc.V[l][:] = v0[l, b].double().numpy()
+        od.compact_kv(oc, ns[b], [int(p) for p in paths[b, :lens[b] + 1]])
+        for l in range(D.L):
+            np.testing.assert_array_equal(k1[l, b].double().numpy(), oc.K[l])
+            np.testing.assert_array_equal(v1[l, b].double().numpy(), oc.V[l])
     np.testing.assert_array_equal(n_dev.cpu().numpy(), np.array(ns) + 1 + lens)

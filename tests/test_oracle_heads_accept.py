@@ -242,3 +242,26 @@ def test_speedup_reported_value_is_rounding_of_identity():
     g = _gold("speedup.json")
     got = metrics.speedup(3.47, 1.22)
     assert abs(got - g["table_value_medusa2_7b"]) <= g["table_rounding_tol"]
+
+
+def test_overhead_is_step_latency_over_vanilla_latency():
+    """overhead = t_step / t_vanilla (a step that costs more than a vanilla
+    step has an overhead above 1), and speedup(tokens, overhead) is the
+    blog's A * T_base / T_tree written with times: an inverted ratio fails
+    every case."""
+    g = _gold("overhead.json")
+    for c in g["ratio_cases"]:
+        o = metrics.overhead(c["t_step"], c["t_vanilla"])
+        assert abs(o - c["overhead"]) <= 1e-12
+        assert abs(metrics.speedup(c["tokens_per_step"], o) - c["speedup"]) <= c["tol"]
+    for c in g["blog_formula_cases"]:
+        o = metrics.overhead(c["t_tree_ms"], c["t_base_ms"])
+        assert o > 1.0
+        want = c["accepted"] * c["t_base_ms"] / c["t_tree_ms"]
+        assert abs(metrics.speedup(c["accepted"], o) - want) <= 1e-12
+    assert metrics.overhead(7.0, 7.0) == 1.0        # a step as fast as vanilla: speedup = tokens
+    assert metrics.speedup(2.5, metrics.overhead(7.0, 7.0)) == 2.5
+    # the faster tree round of the blog (70 ms instead of 110 ms) is the larger speedup
+    a, b = g["blog_formula_cases"]
+    assert metrics.speedup(2.9, metrics.overhead(a["t_tree_ms"], 42.0)) > \
+        metrics.speedup(2.9, metrics.overhead(b["t_tree_ms"], 42.0))

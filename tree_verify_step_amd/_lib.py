@@ -22,13 +22,16 @@ MV_MAX_BATCH = 4
 ACCEPT_GREEDY, ACCEPT_TYPICAL, ACCEPT_REJECT = 0, 1, 2
 ROOT_ARGMAX, ROOT_SAMPLE = 0, 1
 PACK_PLAIN, PACK_QKV = 0, 1
+STATUS_NONFINITE, STATUS_CAPACITY = 1, 2
+ECAPACITY = -3
 
 EXPORTS = ("mv_strerror", "mv_last_error", "mv_tree_compile", "mv_pack_weight",
            "mv_workspace_size", "mv_medusa_heads", "mv_tree_attention", "mv_decoder_layer",
            "mv_tree_build_sparse", "mv_tree_expected_length", "mv_head_accuracy",
            "mv_workspace_size_prefill",
            "mv_embed", "mv_lm_head", "mv_accept", "mv_accept_reject", "mv_kv_compact", "mv_ctx_create",
-           "mv_ctx_destroy", "mv_prefill", "mv_step", "mv_step_profile", "mv_time_kernel", "mv_read_probe")
+           "mv_ctx_destroy", "mv_prefill", "mv_ctx_resume", "mv_ctx_residual", "mv_step", "mv_step_profile",
+           "mv_time_kernel", "mv_read_probe")
 
 # launch-group kinds of mv_step_profile
 KINDS = ("heads", "embed_rope", "norm", "gemm_qkv", "attention", "gemm_o", "gemm_gate_up",
@@ -76,7 +79,8 @@ class StepDesc(C.Structure):
                 ("tree_tok", C.c_void_p), ("logits", C.c_void_p), ("accept_len", C.c_void_p),
                 ("path", C.c_void_p), ("emitted", C.c_void_p), ("best", C.c_void_p),
                 ("head_logits", C.c_void_p), ("top_ids", C.c_void_p),
-                ("ws", C.c_void_p), ("ws_bytes", C.c_size_t), ("prefill_rows", C.c_int32)]
+                ("ws", C.c_void_p), ("ws_bytes", C.c_size_t), ("prefill_rows", C.c_int32),
+                ("status", C.c_void_p)]
 
 
 _lib: Optional[C.CDLL] = None
@@ -120,6 +124,8 @@ def lib() -> C.CDLL:
         "mv_ctx_create": (C.c_int, [C.POINTER(vp), C.POINTER(StepDesc)]),
         "mv_ctx_destroy": (None, [vp]),
         "mv_prefill": (C.c_int, [vp, vp, i32, vp, vp]),
+        "mv_ctx_resume": (C.c_int, [vp, vp, i32]),
+        "mv_ctx_residual": (vp, [vp]),
         "mv_step": (C.c_int, [vp, i32, vp]),
         "mv_step_profile": (C.c_int, [vp, vp, vp, vp]),
         "mv_time_kernel": (C.c_int, [vp, C.c_int32, C.c_int32, vp, vp]),
@@ -322,8 +328,18 @@ class Ctx:
         check(lib().mv_prefill(self.h, ptr(ids), ids.shape[1], ptr(n), stream_ptr(stream)),
               "prefill")
 
+    def resume(self, n_host, draws_used: int) -> None:
+        """Declare a decode state written into the bound buffers by the caller."""
+        import numpy as np
+        n = np.ascontiguousarray(n_host, dtype=np.int32)
+        check(lib().mv_ctx_resume(self.h, ptr(n), int(draws_used)), "ctx_resume")
+
     def step(self, graph: bool = True, stream=None) -> None:
         check(lib().mv_step(self.h, 1 if graph else 0, stream_ptr(stream)), "step")
+
+    def residual_ptr(self) -> int:
+        """Device address of the last verify pass's fp32 residual rows."""
+        return lib().mv_ctx_residual(self.h)
 
     def step_profile(self, stream=None):
         """One eager step timed per launch-group kind with HIP events on the

@@ -172,7 +172,8 @@ __global__ __launch_bounds__(RS_NT) void row_stats_kernel(const float* __restric
     }
   }
   block_argmax<RS_NW>(bv, bi);
-  if (threadIdx.x == 0) amax[row] = bi;
+  // a row of NaNs has no maximum: id 0 keeps every later index in the row
+  if (threadIdx.x == 0) amax[row] = (unsigned)bi < (unsigned)V ? bi : 0;
   if (mode == MV_ACCEPT_GREEDY) return;
 
   const double inv_t = 1.0 / temperature;
@@ -429,6 +430,15 @@ __device__ __forceinline__ void block_sample(const float* __restrict__ z, int V,
   __syncthreads();
 }
 
+// The step's capacity check: thread 0 reads the prefix length before this
+// kernel moves it on (the same thread's later update is ordered after it).
+__device__ __forceinline__ void step_guard(const StepGuard& g, const int32_t* n, int b) {
+  if (g.status && n && threadIdx.x == 0) {
+    const int n0 = n[b];
+    if (n0 < 0 || n0 > g.cap - g.T) atomicOr(g.status, MV_STATUS_CAPACITY);
+  }
+}
+
 __global__ __launch_bounds__(256) void accept_finish_kernel(
     const float* __restrict__ logits, const int32_t* __restrict__ amax_rows,
     unsigned long long* __restrict__ amax_key, const double* __restrict__ stats, const int32_t* __restrict__ parent,
@@ -438,7 +448,7 @@ __global__ __launch_bounds__(256) void accept_finish_kernel(
     int32_t* __restrict__ accept_len, int32_t* __restrict__ path, int32_t* __restrict__ best_out,
     int32_t* __restrict__ next_root, int32_t* __restrict__ emitted, double* __restrict__ margin,
     const float* __restrict__ x, const u16* __restrict__ final_norm, u16* __restrict__ h_last,
-    int d, int32_t* __restrict__ n_advance, const double* __restrict__ bsum) {
+    int d, int32_t* __restrict__ n_advance, const double* __restrict__ bsum, StepGuard guard) {
   __shared__ unsigned char pass[MV_MAXT], ok[MV_MAXT];
   __shared__ double lq[MV_MAXT], score[MV_MAXT];
   __shared__ int par[MV_MAXT], dep[MV_MAXT], tk[MV_MAXT];   // the tree, staged for the walk
@@ -446,13 +456,15 @@ __global__ __launch_bounds__(256) void accept_finish_kernel(
   __shared__ int s_best;
   const int b = blockIdx.x;
   const NormGains ng = norm_gains(x && h_last ? final_norm : nullptr, d);
+  step_guard(guard, n_advance, b);
   for (int v = threadIdx.x; v < T; v += 256) {
     par[v] = parent[(size_t)b * T + v];
     dep[v] = depth_of[(size_t)b * T + v];
     tk[v] = tok[(size_t)b * T + v];
     if (amax_key) {         // the LM head's atomic argmax keys; cleared for the next step
       const size_t r = (size_t)b * T + v;
-      amax[v] = argmax_key_col(amax_key[r]);
+      const int col = argmax_key_col(amax_key[r]);
+      amax[v] = (unsigned)col < (unsigned)V ? col : 0;   // NaN rows: no maximum, id 0
       amax_key[r] = 0ull;
     } else {
       amax[v] = amax_rows[(size_t)b * T + v];
@@ -474,6 +486,10 @@ __global__ __launch_bounds__(256) void accept_finish_kernel(
     if (mode == MV_ACCEPT_GREEDY) {
       pass[v] = tk[v] == amax[p];
       lq[v] = 0.0;
+    } else if ((unsigned)tk[v] >= (unsigned)V) {   // not a token: never accepted
+      pass[v] = 0;
+      lq[v] = -INFINITY;
+      if (margin) margin[(size_t)b * (T + 1) + v] = -INFINITY;
     } else {
       const double* st = stats + (size_t)(row0 + p) * 3;
       const double zt = (double)logits[(size_t)(row0 + p) * V + tk[v]];
@@ -588,12 +604,13 @@ hipError_t launch_accept_finish(const float* logits, const int32_t* argmax, unsi
                                 int32_t* accept_len, int32_t* path, int32_t* best,
                                 int32_t* next_root, int32_t* emitted, double* margin,
                                 const float* x, const u16* final_norm, u16* h_last, int d,
-                                hipStream_t s, int32_t* n_advance, const double* bsum) {
+                                hipStream_t s, int32_t* n_advance, const double* bsum,
+                                StepGuard guard) {
   hipLaunchKernelGGL(accept_finish_kernel, dim3(B), dim3(256), 0, s, logits, argmax, amax_key,
                      stats,
                      parent, depth_of, tok, T, V, depth, mode, root_mode, temperature, eps, delta,
                      u, u_index, u_stride, accept_len, path, best, next_root, emitted, margin, x,
-                     final_norm, h_last, d, n_advance, bsum);
+                     final_norm, h_last, d, n_advance, bsum, guard);
   return hipGetLastError();
 }
 
@@ -635,7 +652,7 @@ __global__ __launch_bounds__(256) void reject_accept_kernel(
     int32_t* __restrict__ best_out, int32_t* __restrict__ next_root,
     int32_t* __restrict__ emitted, double* __restrict__ margin, const float* __restrict__ x,
     const u16* __restrict__ final_norm, u16* __restrict__ h_last, int d,
-    int32_t* __restrict__ n_advance, const double* __restrict__ bsum) {
+    int32_t* __restrict__ n_advance, const double* __restrict__ bsum, StepGuard guard) {
   // the tree and every per-candidate quantity the walk needs, in LDS
   __shared__ int par[MV_MAXT], tk[MV_MAXT];
   __shared__ int fch[MV_MAXT], nsib[MV_MAXT];   // first child, next sibling (T: none)
@@ -650,6 +667,7 @@ __global__ __launch_bounds__(256) void reject_accept_kernel(
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const NormGains ng = norm_gains(x && h_last ? final_norm : nullptr, d);
+  step_guard(guard, n_advance, b);
   const size_t row0 = (size_t)b * T;
   const double* ub = u + (size_t)(u_index ? u_index[0] : 0) * u_stride + row0;
   for (int v = tid; v < T; v += 256) {
@@ -771,6 +789,10 @@ __global__ __launch_bounds__(256) void reject_accept_kernel(
       cur = acc;
       ++L;
       if (tid == 0) s_nodes[L] = cur;
+      // draft residuals: the next node's first rejection rewrites buffer 0,
+      // which a slower wave may still be reading for the decision just taken
+      // (every wave takes the same branch, so the barrier is uniform)
+      if (draft) __syncthreads();
       continue;
     }
     // final draw from the residual at cur (the row's block sums, when
@@ -840,12 +862,12 @@ hipError_t launch_reject_accept(const float* logits, const int32_t* argmax, cons
                                 int32_t* path, int32_t* best, int32_t* next_root,
                                 int32_t* emitted, double* margin, const float* x,
                                 const u16* final_norm, u16* h_last, int d, hipStream_t s,
-                                int32_t* n_advance, const double* bsum) {
+                                int32_t* n_advance, const double* bsum, StepGuard guard) {
   if (T > MV_MAXT) return hipErrorInvalidValue;
   hipLaunchKernelGGL(reject_accept_kernel, dim3(B), dim3(256), 0, s, logits, argmax, stats, parent,
                      tok, T, V, depth, 1.0 / temperature, draft, dstats, u, u_index, u_stride, resid,
                      accept_len, path, best, next_root, emitted, margin, x, final_norm, h_last, d,
-                     n_advance, bsum);
+                     n_advance, bsum, guard);
   return hipGetLastError();
 }
 

@@ -353,7 +353,8 @@ static int enq_layer(const mv_dims& D, int B, const mv_tree& t, const int32_t* n
 // layer); otherwise it is prepared from x here.
 static int enq_lm_head(const mv_dims& D, int M, const float* x, const void* final_norm,
                        const void* lm, float* logits, int ss_tiles, void* ws, const Ws& L,
-                       hipStream_t s, unsigned long long* amax_key = nullptr) {
+                       hipStream_t s, unsigned long long* amax_key = nullptr,
+                       int32_t* status = nullptr) {
   if (ss_tiles <= 0) {
     const int rc = enq_norm_prep(D, M, x, final_norm, ws, L, s);
     if (rc) return rc;
@@ -366,6 +367,7 @@ static int enq_lm_head(const mv_dims& D, int M, const float* x, const void* fina
   g.ss_tiles = ss_tiles;
   g.out_f32 = logits;
   g.amax_key = amax_key;
+  g.status = status;
   MV_HIP(mvk::launch_gemm(g, s));
   return MV_OK;
 }
@@ -392,14 +394,15 @@ static int enq_accept(int B, int T, int V, int d, const float* logits, const mv_
                       int32_t* best, int32_t* next_root, int32_t* emitted, double* margin,
                       const float* x, const void* final_norm, void* h_last, int32_t* amax,
                       double* stats, double* bsum, hipStream_t s,
-                      unsigned long long* amax_key = nullptr, int32_t* n_advance = nullptr) {
+                      unsigned long long* amax_key = nullptr, int32_t* n_advance = nullptr,
+                      mvk::StepGuard guard = {}) {
   if (p.mode == MV_ACCEPT_REJECT) {
     MV_HIP(mvk::launch_row_stats(logits, B * T, V, p.mode, p.temperature, amax, stats, s, bsum));
     MV_HIP(mvk::launch_reject_accept(logits, amax, stats, t.parent, tok, B, T, V, t.depth,
                                      p.temperature, nullptr, nullptr, u, u_index, (long long)u_stride,
                                      nullptr, accept_len, path, best, next_root, emitted, margin,
                                      x, static_cast<const u16*>(final_norm),
-                                     static_cast<u16*>(h_last), d, s, n_advance, bsum));
+                                     static_cast<u16*>(h_last), d, s, n_advance, bsum, guard));
     return MV_OK;
   }
   // greedy acceptance with the LM head's argmax keys needs no pass over the
@@ -414,7 +417,7 @@ static int enq_accept(int B, int T, int V, int d, const float* logits, const mv_
                                    u_index, u_stride, accept_len, path, best, next_root, emitted,
                                    margin, x, static_cast<const u16*>(final_norm),
                                    static_cast<u16*>(h_last), d, s, n_advance,
-                                   p.mode == MV_ACCEPT_GREEDY ? nullptr : bsum));
+                                   p.mode == MV_ACCEPT_GREEDY ? nullptr : bsum, guard));
   return MV_OK;
 }
 
@@ -723,6 +726,10 @@ struct mv_ctx {
   std::vector<hipEvent_t> prof_ev;
   int P = 0;                     // prefill chunk rows (>= T)
   int64_t draws_used = 1;        // draws of u_draws consumed (draw 0: the prefill's root)
+  // host-side upper bound on the device prefix lengths: the largest n after
+  // mv_prefill / mv_ctx_resume plus depth + 1 per step enqueued since
+  bool have_state = false;
+  int64_t n_hi = 0;
 };
 
 // A step that draws (sampled roots, rejection sampling) takes the next row of
@@ -741,6 +748,22 @@ static int check_draw(const mv_ctx* c) {
 static int note_draw(mv_ctx* c, int rc) {
   if (rc == MV_OK && draws_rows(c)) ++c->draws_used;
   return rc;
+}
+
+// A step writes the tree's K/V at slots n .. n+T-1 of every sequence: refuse
+// it while the host-side bound on n leaves fewer than T free slots.
+static int check_capacity(const mv_ctx* c) {
+  if (!c->have_state)
+    return fail(MV_EINVAL, "no decode state: call mv_prefill or mv_ctx_resume first");
+  if (c->n_hi + c->d.T > c->d.kv.cap)
+    return fail(MV_ECAPACITY, "KV capacity: prefix length may reach %lld, + T=%d > cap=%d",
+                (long long)c->n_hi, c->d.T, c->d.kv.cap);
+  return MV_OK;
+}
+// A step moves n on by at most depth + 1 (the root and its accepted path).
+static int note_step(mv_ctx* c, int rc) {
+  if (rc == MV_OK) c->n_hi += c->d.tree.depth + 1;
+  return note_draw(c, rc);
 }
 
 // All L layers; the last one leaves the final norm's operand in ws.xa / ws.ss.
@@ -792,7 +815,7 @@ static int enq_step(mv_ctx* c, hipStream_t s) {
   const bool greedy = d.accept.mode == MV_ACCEPT_GREEDY;
   unsigned long long* amaxp = greedy ? at<unsigned long long>(ws, L.amaxp) : nullptr;
   if ((rc = enq_lm_head(D, M, x, d.final_norm, d.lm_head, d.logits, ss_tiles_of(D, G_DOWN, M),
-                        ws, L, s, amaxp)))
+                        ws, L, s, amaxp, d.status)))
     return rc;
   prof_end(MV_K_LM_HEAD, s);
   prof_begin(s);
@@ -800,7 +823,8 @@ static int enq_step(mv_ctx* c, hipStream_t s) {
   if ((rc = enq_accept(B, T, D.V, D.d, d.logits, d.tree, d.tree_tok, d.accept, d.u_draws,
                        d.u_index, u_stride, d.accept_len, d.path, d.best, d.root_tok, d.emitted, nullptr,
                        x, d.final_norm, d.h_last, at<int32_t>(ws, L.amax), at<double>(ws, L.stats),
-                       at<double>(ws, L.bsum), s, amaxp, d.n_prefix)))
+                       at<double>(ws, L.bsum), s, amaxp, d.n_prefix,
+                       mvk::StepGuard{d.status, d.kv.cap, T})))
     return rc;
   prof_end(MV_K_ACCEPT, s);
   prof_begin(s);
@@ -922,6 +946,7 @@ MV_API int mv_prefill(mv_ctx* c, const int32_t* ids, int32_t ld, const int32_t* 
   mv_tree chain{T, T - 1, (T + 63) / 64, c->chain, c->chain + (size_t)B * T,
                 c->chain + (size_t)2 * B * T, c->chain_anc};
   float* logits = T > d.T ? at<float>(ws, L.plog) : d.logits;   // larger chunks: logits in ws
+  c->have_state = false;          // until the whole prefill is enqueued
   MV_HIP(mvk::launch_fill_i32(d.n_prefix, 0, B, s));
   float* x = at<float>(ws, L.x);
   int32_t* cnt = at<int32_t>(ws, L.cnt);
@@ -957,14 +982,36 @@ MV_API int mv_prefill(mv_ctx* c, const int32_t* ids, int32_t ld, const int32_t* 
   }
   if (d.u_index) MV_HIP(mvk::launch_fill_i32(d.u_index, 1, 1, s));
   c->draws_used = 1;
+  c->have_state = true;
+  c->n_hi = nmax;
+  return MV_OK;
+}
+
+MV_API int mv_ctx_resume(mv_ctx* c, const int32_t* n_host, int32_t draws_used) {
+  if (!c || !n_host) return fail(MV_EINVAL, "mv_ctx_resume: NULL pointer");
+  const mv_step_desc& d = c->d;
+  if (draws_used < 0 || (draws_rows(c) ? draws_used > d.n_draws : draws_used > 1))
+    return fail(MV_EINVAL, "mv_ctx_resume: draws_used %d outside [0, %d]", draws_used,
+                draws_rows(c) ? d.n_draws : 1);
+  int64_t nmax = 0;
+  for (int b = 0; b < d.B; ++b) {
+    if (n_host[b] < 0 || n_host[b] > d.kv.cap - d.T)
+      return fail(MV_ECAPACITY, "mv_ctx_resume: n[%d] = %d outside [0, cap - T = %d]", b,
+                  n_host[b], d.kv.cap - d.T);
+    nmax = std::max<int64_t>(nmax, n_host[b]);
+  }
+  c->draws_used = draws_used;
+  c->have_state = true;
+  c->n_hi = nmax;
   return MV_OK;
 }
 
 MV_API int mv_step(mv_ctx* c, int32_t use_graph, void* stream) {
   if (!c) return fail(MV_EINVAL, "mv_step: NULL context");
   const hipStream_t s = (hipStream_t)stream;
+  if (int rc = check_capacity(c)) return rc;
   if (int rc = check_draw(c)) return rc;
-  if (!use_graph) return note_draw(c, enq_step(c, s));
+  if (!use_graph) return note_step(c, enq_step(c, s));
   if (!c->exec) {
     MV_HIP(hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal));
     const int rc = enq_step(c, c->cap_stream);
@@ -979,12 +1026,17 @@ MV_API int mv_step(mv_ctx* c, int32_t use_graph, void* stream) {
     MV_HIP(hipGraphInstantiate(&c->exec, c->graph, nullptr, nullptr, 0));
   }
   MV_HIP(hipGraphLaunch(c->exec, s));
-  return note_draw(c, MV_OK);
+  return note_step(c, MV_OK);
+}
+
+MV_API const float* mv_ctx_residual(const mv_ctx* c) {
+  return c ? at<const float>(c->d.ws, c->L.x) : nullptr;
 }
 
 MV_API int mv_step_profile(mv_ctx* c, float* ms, int32_t* count, void* stream) {
   if (!c || !ms || !count) return fail(MV_EINVAL, "mv_step_profile: NULL pointer");
   const hipStream_t s = (hipStream_t)stream;
+  if (int rc = check_capacity(c)) return rc;
   if (int rc = check_draw(c)) return rc;
   if (c->prof_ev.empty()) {
     c->prof_ev.resize(2 * 1024);
@@ -995,7 +1047,7 @@ MV_API int mv_step_profile(mv_ctx* c, float* ms, int32_t* count, void* stream) {
   p.cap = 1024;
   p.n = 0;
   g_prof = &p;
-  const int rc = note_draw(c, enq_step(c, s));
+  const int rc = note_step(c, enq_step(c, s));
   g_prof = nullptr;
   if (rc) return rc;
   MV_HIP(hipEventSynchronize(p.ev[2 * p.n - 1]));
@@ -1045,6 +1097,7 @@ MV_API int mv_time_kernel(mv_ctx* c, int32_t kind, int32_t reps, float* us, void
       kind != MV_K_DOWN && kind != MV_K_LM_HEAD)
     return fail(MV_EINVAL, "mv_time_kernel: kind %d is not a per-layer GEMM, attention or LM head",
                 kind);
+  if (int rc = check_capacity(c)) return rc;   // the kernels write the tree's K/V slots
   const hipStream_t s = (hipStream_t)stream;
   const mv_step_desc& d = c->d;
   const mv_dims& D = d.dims;

@@ -144,6 +144,8 @@ struct GemmArgs {
   unsigned long long* amax_key;   // STORE, nullable: per row, atomic max of
                      //   argmax_key(value, column) over the row's columns; must
                      //   hold 0 before the launch (the consumer clears it)
+  int* status;       // STORE, nullable: MV_STATUS_NONFINITE OR-ed in when a
+                     //   stored value (rows < M) is not finite
   float* partial;    // split-K partial tiles
   int* counters;     // split-K arrival counters [tiles], zero between launches
   QkvArgs qkv;
@@ -197,6 +199,14 @@ hipError_t launch_tree_fill(const int32_t* top_ids, const int32_t* root, const i
                             hipStream_t s);
 hipError_t launch_row_stats(const float* logits, int rows, int V, int mode, double temperature,
                             int32_t* argmax, double* stats, hipStream_t s, double* bsum = nullptr);
+// Capacity check of a step, done by its acceptance kernel: with status
+// non-null, MV_STATUS_CAPACITY is OR-ed into *status when a sequence's prefix
+// length at the start of the step (before the kernel moves it on) was
+// negative or left fewer than T free slots below cap.
+struct StepGuard {
+  int* status;
+  int cap, T;
+};
 hipError_t launch_accept_finish(const float* logits, const int32_t* argmax, unsigned long long* amax_key,
                                 const double* stats,
                                 const int32_t* parent, const int32_t* depth_of,
@@ -207,7 +217,7 @@ hipError_t launch_accept_finish(const float* logits, const int32_t* argmax, unsi
                                 int32_t* next_root, int32_t* emitted, double* margin,
                                 const float* x, const u16* final_norm, u16* h_last, int d,
                                 hipStream_t s, int32_t* n_advance = nullptr,
-                                const double* bsum = nullptr);
+                                const double* bsum = nullptr, StepGuard guard = {});
 hipError_t launch_prefill_select(const float* logits, const int32_t* amax, const int32_t* cnt,
                                  int B, int T, int V, int root_mode, double temperature,
                                  const double* u, int u_bstride, int32_t* root, int32_t* n_prefix,
@@ -221,7 +231,8 @@ hipError_t launch_reject_accept(const float* logits, const int32_t* argmax, cons
                                 int32_t* path, int32_t* best, int32_t* next_root,
                                 int32_t* emitted, double* margin, const float* x,
                                 const u16* final_norm, u16* h_last, int d, hipStream_t s,
-                                int32_t* n_advance = nullptr, const double* bsum = nullptr);
+                                int32_t* n_advance = nullptr, const double* bsum = nullptr,
+                                StepGuard guard = {});
 hipError_t launch_compact(u16* kc, u16* vc, int L, int B, int H, int hd, int cap,
                           const int32_t* path, int path_stride, const int32_t* accept_len,
                           const int32_t* n_prefix, hipStream_t s, int advanced = 0,

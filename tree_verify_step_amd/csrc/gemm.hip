@@ -477,6 +477,17 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
       }
   }
   if (EPI == EPI_STORE) {
+    if (g.status) {      // non-finite logits of real rows are flagged (one atomic a wave)
+      bool bad = false;
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            bad |= active && row0 + rb * 16 + r < g.M && !__builtin_isfinite(acc[rb][nb][r]);
+      if (__ballot(bad) != 0ull && lane == 0) atomicOr(g.status, MV_STATUS_NONFINITE);
+    }
     if constexpr (NBW == 1 && W * TR * 16 * 4 <= (int)sizeof(As)) {
       // staged per wave in the operand LDS, then written as 16-byte pieces
       // (4 columns of one row)

@@ -196,6 +196,7 @@ class Session:
                         if u_draws is not None else torch.zeros(1, B, device=dev,
                                                                  dtype=torch.float64))
         self.u_index = torch.zeros(1, **i32)
+        self.status = torch.zeros(1, **i32)       # MV_STATUS_* bits of the steps
         self.tree_tok = torch.zeros(B, T, **i32)
         self.logits = torch.zeros(B, T, D.V, device=dev, dtype=torch.float32)
         P = trees.depth + 1
@@ -231,6 +232,7 @@ class Session:
         desc.emitted = self.emitted.data_ptr()
         desc.best = self.best.data_ptr()
         desc.prefill_rows = prefill_rows
+        desc.status = self.status.data_ptr()
         if debug:
             self.head_logits = torch.zeros(B, max(trees.depth, 1), D.V, device=dev)
             self.top_ids = torch.zeros(B, max(trees.depth, 1), s_top, **i32)
@@ -249,8 +251,21 @@ class Session:
         self._ids = torch.from_numpy(ids).to(self.n_prefix.device)
         self.ctx.prefill(self._ids, n)
 
+    def resume(self, n_host, draws_used: int = 1) -> None:
+        """The caller has written a decode state (KV, n_prefix, root_tok,
+        h_last, u_index) into this session's buffers: n_host are the prefix
+        lengths it wrote, draws_used the rows of u_draws already consumed."""
+        self.ctx.resume(n_host, draws_used)
+
     def step(self, graph: bool = True) -> None:
         self.ctx.step(graph)
+
+    def residual(self) -> torch.Tensor:
+        """Copy of the last verify pass's fp32 residual rows [B*T][d] (the
+        final norm's input), read from the workspace."""
+        off = self.ctx.residual_ptr() - self.ws.data_ptr()
+        n = self.B * self.T * self.D.d * 4
+        return self.ws[off:off + n].view(torch.float32).view(self.B * self.T, self.D.d).clone()
 
     def close(self) -> None:
         self.ctx.close()
