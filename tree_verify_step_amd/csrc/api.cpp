@@ -2,13 +2,13 @@
 // carving, kernel sequencing for each operation, and the step driver that
 // captures one whole decoding step into a hipGraph.
 //
-// A decoder layer is six launches: QKV GEMM (row-norm scale, RoPE and
-// KV-cache write in its epilogue), tree attention, range combine, O-projection
-// GEMM (residual add; writes the FFN norm's operand and the rows' sums of
-// squares), gate/up GEMM (row-norm scale, SwiGLU), down GEMM (residual add;
-// writes the next norm's operand and sums of squares).  RMSNorm never runs as
-// a kernel of its own inside a step; split-K partials are reduced inside the
-// GEMMs.
+// A decoder layer is five launches, six when the attention merges split
+// key ranges: QKV GEMM (row-norm scale, RoPE and KV-cache write in its
+// epilogue), tree attention (and its merge), O-projection GEMM (residual
+// add; writes the FFN norm's operand and the rows' sums of squares), gate/up
+// GEMM (row-norm scale, SwiGLU), down GEMM (residual add; writes the next
+// norm's operand and sums of squares).  RMSNorm never runs as a kernel of
+// its own inside a step; split-K partials are reduced inside the GEMMs.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -117,8 +117,8 @@ static GemmCfg gemm_cfg(const mv_dims& D, int kind, int Mp) {
 }
 
 struct Ws {
-  size_t x, xa, ao, ha, ss, q, rope, part, counters, hu, hz, topi, topv, tcv, tci, amax, amaxp,
-      stats, bsum, cnt, plog, total;
+  size_t x, xa, ao, ha, ss, q, rope, part, counters, apo, apml, hu, hz, topi, topv, tcv,
+      tci, amax, amaxp, stats, bsum, cnt, plog, total;
   int ss_ld;    // floats per row of the sums-of-squares buffer
 };
 
@@ -166,6 +166,16 @@ static Ws ws_layout(const mv_dims& D, int B, int T, int P = 0) {
   w.rope = take((size_t)M * (D.hd / 2) * 8);
   w.part = take(part);
   w.counters = take(max_tiles * 4);
+  // tree attention's split states (the step's T-row trees and the prefill's
+  // R-row chains)
+  size_t apo = 0, apml = 0;
+  for (const int Tq : {T, R}) {
+    const size_t ps = (size_t)B * D.H * mvk::attention_splits(B, D.H, Tq);
+    apo = std::max(apo, ps * (size_t)round16(Tq) * D.hd * 4);
+    apml = std::max(apml, ps * Tq * 8);
+  }
+  w.apo = take(apo);
+  w.apml = take(apml);
   w.hu = take((size_t)B * D.K * D.d * 4);
   w.hz = take((size_t)B * D.K * D.V * 4);
   w.topi = take((size_t)B * D.K * MV_MAX_TOPK * 4);
@@ -238,12 +248,13 @@ static inline void prof_end(int kind, hipStream_t s) {
 // ---------------------------------------------------------------------------
 static int enq_attention(const mv_dims& D, int B, const mv_tree& t, const int32_t* n_prefix,
                          const u16* q, const mv_kv& kv, int layer, u16* out, int packed,
-                         hipStream_t s) {
+                         void* ws, const Ws& L, hipStream_t s) {
   const size_t le = kv_layer_elems(kv);
   const u16* kc = static_cast<const u16*>(kv.k) + (size_t)layer * le;
   const u16* vc = static_cast<const u16*>(kv.v) + (size_t)layer * le;
   MV_HIP(mvk::launch_attention(q, kc, vc, n_prefix, t.anc, B, t.T, D.H, D.hd, kv.cap,
-                               t.mask_words, out, packed, s));
+                               t.mask_words, out, packed, at<float>(ws, L.apo),
+                               at<float2>(ws, L.apml), s));
   return MV_OK;
 }
 
@@ -302,7 +313,7 @@ static int enq_layer(const mv_dims& D, int B, const mv_tree& t, const int32_t* n
 
   if (want(MV_K_ATTN)) {
     prof_begin(s);
-    const int rc = enq_attention(D, B, t, n_prefix, q, kv, layer, ao, 1, s);
+    const int rc = enq_attention(D, B, t, n_prefix, q, kv, layer, ao, 1, ws, L, s);
     if (rc) return rc;
     prof_end(MV_K_ATTN, s);
   }
@@ -559,8 +570,9 @@ MV_API int mv_tree_attention(const mv_dims* dims, int32_t B, const mv_tree* tree
   if (layer < 0 || layer >= dims->L) return fail(MV_EINVAL, "layer %d outside [0,%d)", layer, dims->L);
   if (!n_prefix || !q || !out) return fail(MV_EINVAL, "mv_tree_attention: NULL pointer");
   if ((rc = check_ws(dims, B, tree->T, ws_bytes, ws))) return rc;
+  const Ws L = ws_layout(*dims, B, tree->T);
   return enq_attention(*dims, B, *tree, n_prefix, static_cast<const u16*>(q), *kv, layer,
-                       static_cast<u16*>(out), 0, (hipStream_t)stream);
+                       static_cast<u16*>(out), 0, ws, L, (hipStream_t)stream);
 }
 
 MV_API int mv_decoder_layer(const mv_dims* dims, int32_t B, const mv_tree* tree,

@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include <algorithm>
+
 #include "medusa_verify.h"
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -184,9 +186,17 @@ hipError_t launch_norm_prep(const float* x, const u16* g, u16* xn_packed, float*
                             int M, int d, hipStream_t s);
 hipError_t launch_rope_table(const int32_t* n_prefix, const int32_t* depth_of, float2* rope,
                              int B, int T, int hd, hipStream_t s);
+// Tree attention with the key range of each (sequence, head) split over up
+// to attention_splits(B, H, T) workgroups; with more than one split the
+// partial states go to part_o [B*H][S][round16(T)][hd] fp32 and part_ml
+// [B*H][S][T] in the caller's workspace, and a second launch merges them.
+int attention_splits(int B, int H, int T);
+// Whether a launch of this shape splits key ranges (else one workgroup per
+// 16 queries of a (sequence, head) reads the pair's whole cache).
+bool attention_uses_splits(int B, int H, int T, int cap);
 hipError_t launch_attention(const u16* q, const u16* kc, const u16* vc, const int32_t* n_prefix,
                             const uint64_t* anc, int B, int T, int H, int hd, int cap, int mw,
-                            u16* out, int packed, hipStream_t s);
+                            u16* out, int packed, float* part_o, float2* part_ml, hipStream_t s);
 hipError_t launch_heads_w1(const u16* h, const u16* w1, float* u, int B, int D, int d,
                            hipStream_t s);
 hipError_t launch_heads_w2(const float* u, const u16* w2, float* z, int B, int D, int d, int V,
