@@ -317,6 +317,27 @@ MV_API int mv_accept(int32_t B, int32_t T, int32_t V, int32_t d, const float* lo
                      const void* final_norm, void* h_last, void* ws, size_t ws_bytes,
                      void* stream);
 
+/* mv_accept for callers that cannot allocate device memory (code under
+ * hipGraph capture, tight serving loops, harnesses that forbid it): the same
+ * operation, arguments and outputs as mv_accept, without the workspace.  Its
+ * scratch (row argmax, row statistics and, for TYPICAL and REJECT, the rows'
+ * 256-id block sums: align256(4*B*T) + align256(24*B*T) [+ 8*B*T*ceil(V/256)]
+ * bytes) is a static device array of MV_NOALLOC_SCRATCH_BYTES in the library,
+ * one per GPU, held until the process ends; its address is looked up once
+ * per device on the first call with that device current.  The call
+ * allocates nothing.  Every byte of scratch it reads it first writes in the
+ * same call, so nothing needs clearing, but all calls on one GPU share the
+ * array: calls that overlap on one GPU (e.g. on different streams) race.
+ * Errors: as mv_accept, and MV_EWORKSPACE (before anything is enqueued)
+ * when the shape needs more than MV_NOALLOC_SCRATCH_BYTES. */
+#define MV_NOALLOC_SCRATCH_BYTES (8u << 20)
+MV_API int mv_accept_noalloc(int32_t B, int32_t T, int32_t V, int32_t d, const float* logits,
+                             const mv_tree* tree, const int32_t* tree_tok,
+                             const mv_accept_params* p, const double* u, int32_t* accept_len,
+                             int32_t* path, int32_t* best, int32_t* next_root, int32_t* emitted,
+                             double* margin, const float* x, const void* final_norm,
+                             void* h_last, void* stream);
+
 /* Rejection-sampling acceptance (speculative sampling: lecture note section
  * 二.3, two-word example; speculative-decoding tutorial, Concept and Maths).
  * The pages give the chain rule: a draft x drawn from q is kept against the

@@ -8,6 +8,6 @@ them to the library.  Nothing here computes the method in Python.
 from . import _lib  # noqa: F401
 from ._lib import (ACCEPT_GREEDY, ACCEPT_REJECT, ACCEPT_TYPICAL, PACK_PLAIN,  # noqa: F401
                    PACK_QKV, ROOT_ARGMAX, ROOT_SAMPLE, AcceptParams, Ctx, Dims, KV, LayerWeights,
-                   MVError, StepDesc, Tree, accept, accept_reject, decoder_layer, head_accuracy,
+                   MVError, StepDesc, Tree, accept, accept_noalloc, accept_reject, decoder_layer, head_accuracy,
                    tree_build_sparse, tree_expected_length, embed, kv_compact, lib, lm_head, medusa_heads,
                    pack_weight, read_probe, tree_attention, tree_compile, workspace_size)

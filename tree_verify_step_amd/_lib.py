@@ -29,7 +29,8 @@ EXPORTS = ("mv_strerror", "mv_last_error", "mv_tree_compile", "mv_pack_weight",
            "mv_workspace_size", "mv_medusa_heads", "mv_tree_attention", "mv_decoder_layer",
            "mv_tree_build_sparse", "mv_tree_expected_length", "mv_head_accuracy",
            "mv_workspace_size_prefill",
-           "mv_embed", "mv_lm_head", "mv_accept", "mv_accept_reject", "mv_kv_compact", "mv_ctx_create",
+           "mv_embed", "mv_lm_head", "mv_accept", "mv_accept_noalloc", "mv_accept_reject",
+           "mv_kv_compact", "mv_ctx_create",
            "mv_ctx_destroy", "mv_prefill", "mv_ctx_resume", "mv_ctx_residual", "mv_step", "mv_step_profile",
            "mv_time_kernel", "mv_read_probe")
 
@@ -114,6 +115,9 @@ def lib() -> C.CDLL:
         "mv_accept": (C.c_int, [i32, i32, i32, i32, vp, C.POINTER(Tree), vp,
                                 C.POINTER(AcceptParams), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                 vp, sz, vp]),
+        "mv_accept_noalloc": (C.c_int, [i32, i32, i32, i32, vp, C.POINTER(Tree), vp,
+                                        C.POINTER(AcceptParams), vp, vp, vp, vp, vp, vp, vp, vp,
+                                        vp, vp, vp]),
         "mv_accept_reject": (C.c_int, [i32, i32, i32, i32, vp, C.POINTER(Tree), vp, C.c_double,
                                        vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "mv_kv_compact": (C.c_int, [C.POINTER(KV), vp, i32, vp, vp, vp]),
@@ -257,6 +261,16 @@ def accept(B: int, T: int, V: int, d: int, logits, tree: Tree, tree_tok, p: Acce
                           ptr(u), ptr(accept_len), ptr(path), ptr(best), ptr(next_root),
                           ptr(emitted), ptr(margin), ptr(x), ptr(final_norm), ptr(h_last),
                           ptr(ws), ws.numel() * ws.element_size(), stream_ptr(stream)), "accept")
+
+
+def accept_noalloc(B: int, T: int, V: int, d: int, logits, tree: Tree, tree_tok, p: AcceptParams,
+                   u, accept_len, path, best, next_root, emitted=None, margin=None, x=None,
+                   final_norm=None, h_last=None, stream=None) -> None:
+    check(lib().mv_accept_noalloc(B, T, V, d, ptr(logits), C.byref(tree), ptr(tree_tok),
+                                  C.byref(p), ptr(u), ptr(accept_len), ptr(path), ptr(best),
+                                  ptr(next_root), ptr(emitted), ptr(margin), ptr(x),
+                                  ptr(final_norm), ptr(h_last), stream_ptr(stream)),
+          "accept_noalloc")
 
 
 def accept_reject(B: int, T: int, V: int, d: int, logits, tree: Tree, tree_tok,

@@ -14,6 +14,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "common.hpp"
@@ -622,6 +623,29 @@ MV_API int mv_lm_head(const mv_dims* dims, int32_t M, const float* x, const void
   return enq_lm_head(*dims, M, x, final_norm, lm_head, logits, 0, ws, L, s);
 }
 
+// ---------------------------------------------------------------------------
+// Acceptance without a caller workspace (mv_accept_noalloc): the scratch
+// lives in a static device array of this library, one per GPU, found by its
+// symbol address once per device.  Host code passes only that address to the
+// kernels (the array's name is a host-side stand-in, not a device address).
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[MV_NOALLOC_SCRATCH_BYTES];
+
+#define MV_NOALLOC_MAX_DEVICES 64
+static std::once_flag g_scratch_once[MV_NOALLOC_MAX_DEVICES];
+static void* g_scratch_ptr[MV_NOALLOC_MAX_DEVICES];
+static hipError_t g_scratch_err[MV_NOALLOC_MAX_DEVICES];
+
+// Bytes of acceptance scratch: row argmax int32 [B*T] and row stats double
+// [B*T][3] (each part 256-aligned), then for typical acceptance and
+// rejection sampling the rows' 256-id block sums double [B*T][ceil(V/256)].
+static size_t accept_ws_need(int B, int T, int V, int mode) {
+  const size_t head = align256((size_t)B * T * 4) + align256((size_t)B * T * 24);
+  const size_t sums = (size_t)B * T * ((V + 255) / 256) * 8;
+  if (mode == MV_ACCEPT_GREEDY) return head;
+  return head + (mode == MV_ACCEPT_REJECT ? align256(sums) : sums);
+}
+
 MV_API int mv_accept(int32_t B, int32_t T, int32_t V, int32_t d, const float* logits,
                      const mv_tree* tree, const int32_t* tree_tok, const mv_accept_params* p,
                      const double* u, int32_t* accept_len, int32_t* path, int32_t* best,
@@ -658,6 +682,41 @@ MV_API int mv_accept(int32_t B, int32_t T, int32_t V, int32_t d, const float* lo
                     next_root, emitted, margin, x, final_norm, h_last, at<int32_t>(ws, 0),
                     at<double>(ws, o_stats), sums ? at<double>(ws, o_bsum) : nullptr,
                     (hipStream_t)stream);
+}
+
+MV_API int mv_accept_noalloc(int32_t B, int32_t T, int32_t V, int32_t d, const float* logits,
+                             const mv_tree* tree, const int32_t* tree_tok,
+                             const mv_accept_params* p, const double* u, int32_t* accept_len,
+                             int32_t* path, int32_t* best, int32_t* next_root, int32_t* emitted,
+                             double* margin, const float* x, const void* final_norm,
+                             void* h_last, void* stream) {
+  int rc = check_batch(B);
+  if (rc) return rc;
+  if (!p) return fail(MV_EINVAL, "mv_accept_noalloc: NULL params");
+  if (T < 1 || T > MV_MAX_T) return fail(MV_EUNSUPPORTED, "T=%d outside [1,%d]", T, MV_MAX_T);
+  if (V < 64 || V % 64 || V > MV_MAX_VOCAB) return fail(MV_EUNSUPPORTED, "V=%d", V);
+  if (p->mode != MV_ACCEPT_GREEDY && p->mode != MV_ACCEPT_TYPICAL && p->mode != MV_ACCEPT_REJECT)
+    return fail(MV_EINVAL, "accept mode %d", p->mode);
+  const size_t need = accept_ws_need(B, T, V, p->mode);
+  if (need > MV_NOALLOC_SCRATCH_BYTES)
+    return fail(MV_EWORKSPACE,
+                "mv_accept_noalloc: B=%d T=%d V=%d needs %zu bytes of scratch, more than the "
+                "library's static %u bytes (use mv_accept with a workspace)",
+                B, T, V, need, (unsigned)MV_NOALLOC_SCRATCH_BYTES);
+  int dev = 0;
+  MV_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= MV_NOALLOC_MAX_DEVICES)
+    return fail(MV_EUNSUPPORTED, "mv_accept_noalloc: device %d >= %d", dev, MV_NOALLOC_MAX_DEVICES);
+  // once per device, with that device current: the array's device address
+  std::call_once(g_scratch_once[dev], [dev] {
+    g_scratch_err[dev] = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+  });
+  if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev])
+    return fail(MV_EHIP, "mv_accept_noalloc: hipGetSymbolAddress: %s",
+                hipGetErrorString(g_scratch_err[dev]));
+  return mv_accept(B, T, V, d, logits, tree, tree_tok, p, u, accept_len, path, best, next_root,
+                   emitted, margin, x, final_norm, h_last, g_scratch_ptr[dev],
+                   MV_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 MV_API int mv_accept_reject(int32_t B, int32_t T, int32_t V, int32_t d, const float* logits,
