@@ -18,9 +18,10 @@ Modules:
   decode  -- KV compaction, one full step, prefill, vanilla greedy decoding
              (Algorithm step 6)
   metrics -- the speedup identity (Results, app. B.1)
+  train   -- the Medusa-1 head loss and its gradients (Method 6, eq. 1)
 
 Every function here is pinned by a `-m "not gpu"` test against something other
 than itself (a library implementation, a closed form, a brute force, or a
 worked example from the pages); see tests/test_oracle_*.py.
 """
-from . import accept, decode, heads, metrics, model, tree  # noqa: F401
+from . import accept, decode, heads, metrics, model, train, tree  # noqa: F401
