@@ -246,6 +246,51 @@ def cpu_baseline(w, n0, sample_layers=2):
             "tree_tokens_per_s": t.T / step, "seconds_per_step": step}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_medusa1(D, N=2048, K=4, reps=3):
+    """Medusa-1 head training pass (loss and the gradients of W1 and W2) of
+    K heads at the workload's width over N positions of seeded bf16 hidden
+    states: wall time of the library call between HIP events, and its
+    algorithmic bf16 flops over the MFMA peak.  Flops per pass:
+    K * 2N (2 d^2 + 3 d V) -- a = H W1^T and dW1 (N d^2 each), z = s W2^T,
+    dW2 and ds (N d V each)."""
+    import numpy as np
+    import torch
+    import tree_verify_step_amd as tv
+    from tree_verify_step_amd import runtime as rt
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9)
+    h = torch.randn(N, D.d, generator=g, device="cuda").to(torch.bfloat16)
+    w1 = (torch.randn(K, D.d, D.d, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    w2 = (torch.randn(K, D.V, D.d, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    labels = torch.randint(0, D.V, (N, K), generator=g, device="cuda", dtype=torch.int32)
+    dims = rt.dims_of(D)
+    ws = torch.empty(tv.medusa1_workspace_size(dims, N), device="cuda", dtype=torch.uint8)
+    loss = torch.zeros(1, device="cuda", dtype=torch.float64)
+    dw1 = torch.empty(K, D.d, D.d, device="cuda")
+    dw2 = torch.empty(K, D.V, D.d, device="cuda")
+    tv.medusa1_loss(dims, N, K, h, labels, None, w1, w2, loss, None, dw1, dw2, ws)   # warm-up
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        tv.medusa1_loss(dims, N, K, h, labels, None, w1, w2, loss, None, dw1, dw2, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = K * 2.0 * N * (2 * D.d * D.d + 3 * D.d * D.V)
+    tflops = flops / (ms * 1e-3) / 1e12
+    out = {"positions": N, "heads": K, "width": D.d, "vocab": D.V, "ms": round(ms, 3),
+           "tflops": round(tflops, 1), "flops_per_pass": flops,
+           "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+           "loss_per_label": round(float(loss.item()) / (N * float(np.sum(0.8 ** np.arange(1, K + 1)))), 4)}
+    del ws, dw1, dw2, w1, w2, h
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -254,6 +299,8 @@ def main() -> int:
     ap.add_argument("--workload", default=None)
     ap.add_argument("--profile-steps", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-train", action="store_true",
+                    help="skip the Medusa-1 head-training pass measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a copy kernel of known size first (for --pmc counter scaling)")
     ap.add_argument("--pmc-summary", nargs="+", metavar="DIR",
@@ -412,6 +459,13 @@ def main() -> int:
     del probe
     log(f"[bench] plain streaming read: {read_gbs:.0f} GB/s")
 
+    train = None
+    if not args.no_train:
+        train = bench_medusa1(D)
+        log(f"[bench] Medusa-1 head training pass (N={train['positions']}, K={train['heads']}): "
+            f"{train['ms']:.2f} ms, {train['tflops']:.0f} TFLOP/s "
+            f"({100 * train['mfma_frac']:.1f}% of the bf16 MFMA peak)")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
@@ -448,6 +502,7 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "prefill": prefill,
+        "medusa1_train": train,
         "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in kernels.items()},
     }
     sess.close()

@@ -386,6 +386,36 @@ MV_API int mv_accept_reject(int32_t B, int32_t T, int32_t V, int32_t d, const fl
 MV_API int mv_kv_compact(const mv_kv* kv, const int32_t* path, int32_t path_stride,
                          const int32_t* accept_len, int32_t* n_prefix, void* stream);
 
+/* ---- Medusa-1 head training (frozen backbone) ---------------------------- */
+
+/* Bytes of device workspace for mv_medusa1_loss over N positions. */
+MV_API int mv_medusa1_workspace_size(const mv_dims* dims, int32_t N, size_t* bytes);
+
+/* Medusa-1 head loss and its gradients (Medusa paper digest, Method 6,
+ * eq. 1 with lambda_k = 0.8^k of app. B.2; wq-win lecture note, 二.1):
+ *   L = sum_t sum_{k=1..K} -lambda_k log p_t^(k)(y_{t+k+1}),
+ *   p_t^(k) = softmax(W2_k (SiLU(W1_k h_t) + h_t)),
+ * with the backbone frozen: dL/dW1_k and dL/dW2_k.
+ * h: device bf16 [N][d] (the hidden states the LM head reads, i.e. after
+ * the final RMSNorm); labels: device int32 [N][K], labels[t][k-1] = the
+ * token k+1 positions after t (a shift of 2 + i for 0-indexed head i, as
+ * the released trainer does), -1 (or any id outside [0, V)) = no label;
+ * lambda: host double [K] (NULL: 0.8^k; ones give the released trainer's
+ * unweighted sum); w1: device bf16 [K'][d][d], w2: device bf16 [K'][V][d]
+ * row-major (out, in), the first K of K' = dims.K heads are used.
+ * Outputs (device): loss double [1] (the sum over positions and heads, in a
+ * fixed order); optional: loss_tk fp32 [N][K] (each term, lambda applied),
+ * dw1 fp32 [K][d][d] and dw2 fp32 [K][V][d] (NULL: not computed).
+ * Requires N % 64 == 0 (64 <= N <= 2^20); workspace of
+ * mv_medusa1_workspace_size bytes.  The contractions (a = h W1^T, z = s
+ * W2^T, dW2 = g^T s, ds = g W2, dW1 = da^T h) run on bf16 MFMA with fp32
+ * accumulation; s, the logits' gradient g and da are rounded to bf16 as
+ * GEMM operands. */
+MV_API int mv_medusa1_loss(const mv_dims* dims, int32_t N, int32_t K, const void* h,
+                           const int32_t* labels, const double* lambda, const void* w1,
+                           const void* w2, double* loss, float* loss_tk, float* dw1, float* dw2,
+                           void* ws, size_t ws_bytes, void* stream);
+
 /* ---- whole step ---------------------------------------------------------- */
 
 /* Everything one decode step reads and writes (all device, caller-owned).

@@ -1,0 +1,128 @@
+"""GPU parity of the Medusa-1 head loss and gradients (mv_medusa1_loss)
+against the oracle (Medusa paper digest, Method 6, eq. 1; app. B.2
+weights; lecture note 二.1).
+
+Inputs are seeded: bf16-valued hidden states of unit scale, heads drawn as
+the workloads draw them (W1 ~ N(0, 0.02), W2 ~ N(0, 0.02)), labels shifted
+from a random token stream with the last positions unlabelled.  The loss
+terms are differences of logits and are held to the logits' tolerance; the
+gradients go through bf16 GEMM operands (s, the logits' gradient g, da),
+so they are held to a relative bound derived from that rounding."""
+import numpy as np
+import pytest
+import torch
+
+import tree_verify_step_amd as tv
+from tree_verify_step_amd import runtime as rt
+from oracle import train as otr
+from workloads import synth
+
+from gpu_helpers import DEV, TOL, bf16_values
+
+pytestmark = pytest.mark.gpu
+
+# Gradient bound: the GPU rounds three GEMM operands on the way to each
+# gradient (s or da, the logits' gradient g, and for dW1 the ds product
+# rounded into da), each a relative error uniform in +-2^-9 (rms
+# 2^-9/sqrt(3)); together about 2^-8.7 of the gradient's rms.  The rms
+# error is held to REL_RMS = 2^-7 of the reference's rms and the largest
+# error to REL_MAX = 2^-6 of the reference's largest entry.
+REL_RMS = 2.0 ** -7
+REL_MAX = 2.0 ** -6
+
+
+def _inputs(seed, N, d, V, K):
+    rng = np.random.default_rng(seed)
+    H = bf16_values(rng.standard_normal((N, d)))
+    W1 = np.stack([bf16_values(0.02 * rng.standard_normal((d, d))) for _ in range(K)])
+    W2 = np.stack([bf16_values(0.02 * rng.standard_normal((V, d))) for _ in range(K)])
+    y = synth.random_tokens(seed + 1, N + K + 1 - 3, V)   # the last 3 positions lack labels
+    labels = otr.shifted_labels(y, N, K)
+    return H, W1, W2, labels
+
+
+def _run(D, N, K, H, W1, W2, labels, lam, grads=True):
+    dims = rt.dims_of(D)
+    ws = torch.zeros(tv.medusa1_workspace_size(dims, N), device=DEV, dtype=torch.uint8)
+    h = rt.upload_bf16(H.astype(np.float32))
+    w1 = rt.upload_bf16(W1.astype(np.float32))
+    w2 = rt.upload_bf16(W2.astype(np.float32))
+    lab = torch.from_numpy(labels.astype(np.int32)).to(DEV)
+    loss = torch.zeros(1, device=DEV, dtype=torch.float64)
+    ltk = torch.zeros(N, K, device=DEV)
+    dw1 = torch.zeros(K, D.d, D.d, device=DEV) if grads else None
+    dw2 = torch.zeros(K, D.V, D.d, device=DEV) if grads else None
+    tv.medusa1_loss(dims, N, K, h, lab, lam, w1, w2, loss, ltk, dw1, dw2, ws)
+    torch.cuda.synchronize()
+    return (float(loss.item()), ltk.cpu().numpy(), None if dw1 is None else dw1.cpu().numpy(),
+            None if dw2 is None else dw2.cpu().numpy())
+
+
+def _check_grad(name, got, want):
+    e = got - want
+    rms_e, rms_w = np.sqrt(np.mean(e ** 2)), np.sqrt(np.mean(want ** 2))
+    max_e, max_w = np.abs(e).max(), np.abs(want).max()
+    print(f"  {name}: err rms {rms_e:.3e} (ref rms {rms_w:.3e}, ratio {rms_e / rms_w:.4f}), "
+          f"err max {max_e:.3e} (ref max {max_w:.3e}, ratio {max_e / max_w:.4f})", flush=True)
+    assert rms_e <= REL_RMS * rms_w, (name, rms_e, rms_w)
+    assert max_e <= REL_MAX * max_w, (name, max_e, max_w)
+
+
+@pytest.mark.parametrize("N,d,V,K,lam_kind", [
+    (64, 64, 512, 3, "paper"),        # one tile per GEMM
+    (128, 192, 640, 4, "paper"),      # ragged last tile in d (192 = 1.5 tiles)
+    (192, 256, 1088, 2, "ones"),      # the released trainer's unweighted sum; ragged tiles in V
+    (256, 1024, 4096, 4, "paper"),    # several tiles in every dimension
+])
+def test_medusa1_loss_and_gradients_match_oracle(N, d, V, K, lam_kind):
+    print(f"medusa1 N={N} d={d} V={V} K={K} lambda={lam_kind}", flush=True)
+    from workloads import configs
+    D = configs.Dims(L=1, d=d, H=d // 64, hd=64, F=64, V=V, K=K)
+    H, W1, W2, labels = _inputs(N + d + V, N, d, V, K)
+    lam = otr.default_lambdas(K) if lam_kind == "paper" else np.ones(K)
+    loss, ltk, dw1, dw2 = _run(D, N, K, H, W1, W2, labels, None if lam_kind == "paper" else lam)
+    ref = otr.medusa1_backward(H, labels, W1, W2, lam)
+    fwd_tk = otr.medusa1_forward(H, labels, W1, W2, lam)["loss_tk"]
+    print(f"  loss {loss:.6f} vs {ref['loss']:.6f}; per-term err {np.abs(ltk - fwd_tk).max():.2e}",
+          flush=True)
+    assert np.abs(ltk - fwd_tk).max() <= TOL
+    assert abs(loss - ref["loss"]) <= 1e-4 * abs(ref["loss"])
+    assert np.all(ltk[labels < 0] == 0)
+    _check_grad("dW1", dw1, ref["dW1"])
+    _check_grad("dW2", dw2, ref["dW2"])
+
+
+def test_medusa1_loss_at_7b_width():
+    """The 7B head shapes (d = 4096, V = 32000, K = 4 heads) over 512
+    positions, every kernel in the launch configuration of the benchmark:
+    the loss terms, the loss, and the gradients against the oracle."""
+    print("medusa1 at 7B width: N=512 d=4096 V=32000 K=4", flush=True)
+    from workloads import configs
+    D = configs.LLAMA7B_T64.dims
+    N, K = 512, 4
+    H, W1, W2, labels = _inputs(7, N, D.d, D.V, K)
+    loss, ltk, dw1, dw2 = _run(D, N, K, H, W1, W2, labels, None)
+    lam = otr.default_lambdas(K)
+    ref = otr.medusa1_backward(H, labels, W1, W2, lam)
+    fwd_tk = otr.medusa1_forward(H, labels, W1, W2, lam)["loss_tk"]
+    print(f"  loss {loss:.4f} vs {ref['loss']:.4f}; per-term err {np.abs(ltk - fwd_tk).max():.2e}",
+          flush=True)
+    assert np.abs(ltk - fwd_tk).max() <= TOL
+    assert abs(loss - ref["loss"]) <= 1e-4 * abs(ref["loss"])
+    _check_grad("dW1", dw1, ref["dW1"])
+    _check_grad("dW2", dw2, ref["dW2"])
+
+
+def test_medusa1_forward_only_and_determinism():
+    """Without gradient buffers only the loss is computed; two calls give
+    bit-identical results."""
+    from workloads import configs
+    D = configs.Dims(L=1, d=128, H=2, hd=64, F=64, V=512, K=2)
+    H, W1, W2, labels = _inputs(3, 64, 128, 512, 2)
+    a = _run(D, 64, 2, H, W1, W2, labels, None, grads=False)
+    b = _run(D, 64, 2, H, W1, W2, labels, None, grads=False)
+    assert a[0] == b[0] and np.array_equal(a[1], b[1])
+    full = _run(D, 64, 2, H, W1, W2, labels, None)
+    assert full[0] == a[0]
+    g2 = _run(D, 64, 2, H, W1, W2, labels, None)
+    assert np.array_equal(full[2], g2[2]) and np.array_equal(full[3], g2[3])

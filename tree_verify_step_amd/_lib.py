@@ -32,7 +32,7 @@ EXPORTS = ("mv_strerror", "mv_last_error", "mv_tree_compile", "mv_pack_weight",
            "mv_embed", "mv_lm_head", "mv_accept", "mv_accept_noalloc", "mv_accept_reject",
            "mv_kv_compact", "mv_ctx_create",
            "mv_ctx_destroy", "mv_prefill", "mv_ctx_resume", "mv_ctx_residual", "mv_step", "mv_step_profile",
-           "mv_time_kernel", "mv_read_probe")
+           "mv_time_kernel", "mv_read_probe", "mv_medusa1_workspace_size", "mv_medusa1_loss")
 
 # launch-group kinds of mv_step_profile
 KINDS = ("heads", "embed_rope", "norm", "gemm_qkv", "attention", "gemm_o", "gemm_gate_up",
@@ -134,6 +134,9 @@ def lib() -> C.CDLL:
         "mv_step_profile": (C.c_int, [vp, vp, vp, vp]),
         "mv_time_kernel": (C.c_int, [vp, C.c_int32, C.c_int32, vp, vp]),
         "mv_read_probe": (C.c_int, [vp, C.c_size_t, C.c_int32, vp, vp, vp]),
+        "mv_medusa1_workspace_size": (C.c_int, [C.POINTER(Dims), i32, C.POINTER(C.c_size_t)]),
+        "mv_medusa1_loss": (C.c_int, [C.POINTER(Dims), i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -319,6 +322,24 @@ def tree_expected_length(acc, paths) -> float:
 def head_accuracy(N: int, K: int, s: int, top_ids, labels, counts, stream=None) -> None:
     check(lib().mv_head_accuracy(N, K, s, ptr(top_ids), ptr(labels), ptr(counts),
                                  stream_ptr(stream)), "head_accuracy")
+
+
+def medusa1_workspace_size(dims: Dims, N: int) -> int:
+    out = C.c_size_t(0)
+    check(lib().mv_medusa1_workspace_size(C.byref(dims), N, C.byref(out)), "medusa1_workspace_size")
+    return out.value
+
+
+def medusa1_loss(dims: Dims, N: int, K: int, h, labels, lam, w1, w2, loss, loss_tk=None, dw1=None,
+                 dw2=None, ws=None, stream=None) -> None:
+    """Medusa-1 head loss (and gradients when dw1 / dw2 are given); lam: a
+    host sequence of K floats or None (0.8^k)."""
+    import numpy as np
+    lam_h = None if lam is None else np.ascontiguousarray(lam, dtype=np.float64)
+    check(lib().mv_medusa1_loss(C.byref(dims), N, K, ptr(h), ptr(labels),
+                                None if lam_h is None else lam_h.ctypes.data, ptr(w1), ptr(w2),
+                                ptr(loss), ptr(loss_tk), ptr(dw1), ptr(dw2), ptr(ws),
+                                ws.numel() * ws.element_size(), stream_ptr(stream)), "medusa1_loss")
 
 
 def kv_compact(kv: KV, path, path_stride: int, accept_len, n_prefix, stream=None) -> None:

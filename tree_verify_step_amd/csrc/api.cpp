@@ -763,6 +763,110 @@ MV_API int mv_accept_reject(int32_t B, int32_t T, int32_t V, int32_t d, const fl
   return MV_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Medusa-1 head loss and gradients (train.hip)
+// ---------------------------------------------------------------------------
+struct TrainWs {
+  size_t a, s, z, g, gt, st, w2t, ds, da, dat, ht, ltk, total;
+};
+
+static TrainWs train_ws(const mv_dims& D, int N) {
+  TrainWs w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  const size_t Nd = (size_t)N * D.d, NV = (size_t)N * D.V;
+  w.a = take(Nd * 4);                     // a = H W1^T (fp32)
+  w.s = take(Nd * 2);                     // s = SiLU(a) + H (bf16)
+  w.z = take(NV * 4);                     // logits (fp32)
+  w.g = take(NV * 2);                     // logits' gradient (bf16)
+  w.gt = take(NV * 2);                    // ... transposed [V][N]
+  w.st = take(Nd * 2);                    // s transposed [d][N]
+  w.w2t = take((size_t)D.V * D.d * 2);    // W2 transposed [d][V]
+  w.ds = take(Nd * 4);                    // ds (fp32)
+  w.da = take(Nd * 2);                    // da (bf16)
+  w.dat = take(Nd * 2);                   // da transposed [d][N]
+  w.ht = take(Nd * 2);                    // H transposed [d][N]
+  w.ltk = take((size_t)N * D.K * 4);      // per-position losses when the caller keeps none
+  w.total = off;
+  return w;
+}
+
+static int check_train(const mv_dims* dims, int N) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (N < 64 || N % 64 || N > (1 << 20))
+    return fail(MV_EUNSUPPORTED, "positions N=%d: need a multiple of 64 in [64, 2^20]", N);
+  return MV_OK;
+}
+
+MV_API int mv_medusa1_workspace_size(const mv_dims* dims, int32_t N, size_t* bytes) {
+  int rc = check_train(dims, N);
+  if (rc) return rc;
+  if (!bytes) return fail(MV_EINVAL, "bytes is NULL");
+  *bytes = train_ws(*dims, N).total;
+  return MV_OK;
+}
+
+MV_API int mv_medusa1_loss(const mv_dims* dims, int32_t N, int32_t K, const void* h,
+                           const int32_t* labels, const double* lambda, const void* w1,
+                           const void* w2, double* loss, float* loss_tk, float* dw1, float* dw2,
+                           void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_train(dims, N);
+  if (rc) return rc;
+  const mv_dims& D = *dims;
+  if (K < 1 || K > D.K) return fail(MV_EINVAL, "heads K=%d outside [1, dims.K=%d]", K, D.K);
+  if (!h || !labels || !w1 || !w2 || !loss) return fail(MV_EINVAL, "mv_medusa1_loss: NULL pointer");
+  double lam[MV_MAX_DEPTH];
+  for (int k = 0; k < K; ++k) {
+    lam[k] = lambda ? lambda[k] : 0.8;
+    if (!lambda)
+      for (int j = 0; j < k; ++j) lam[k] *= 0.8;        // 0.8^(k+1) for head k+1
+    if (!(lam[k] >= 0.0) || !(lam[k] < 1e30)) return fail(MV_EINVAL, "lambda[%d] = %g", k, lam[k]);
+  }
+  const TrainWs L = train_ws(D, N);
+  if (!ws || ws_bytes < L.total)
+    return fail(MV_EWORKSPACE, "workspace %zu < %zu", ws_bytes, L.total);
+  const hipStream_t s = (hipStream_t)stream;
+  const int d = D.d, V = D.V;
+  const u16* H = static_cast<const u16*>(h);
+  float* a = at<float>(ws, L.a);
+  u16* sb = at<u16>(ws, L.s);
+  float* z = at<float>(ws, L.z);
+  u16* g = at<u16>(ws, L.g);
+  float* ltk = loss_tk ? loss_tk : at<float>(ws, L.ltk);
+  if (dw1) MV_HIP(mvk::launch_transpose_bf16(H, 0, at<u16>(ws, L.ht), 0, N, d, 1, s));
+  for (int k = 0; k < K; ++k) {
+    const u16* W1 = static_cast<const u16*>(w1) + (size_t)k * d * d;
+    const u16* W2 = static_cast<const u16*>(w2) + (size_t)k * V * d;
+    // forward: a = H W1^T, s = SiLU(a) + H, z = s W2^T, loss and dL/dz
+    MV_HIP(mvk::launch_gemm_nt(H, d, 0, W1, d, 0, a, d, 0, N, d, d, 1, s));
+    MV_HIP(mvk::launch_medusa1_act(a, H, sb, (size_t)N * d, s));
+    MV_HIP(mvk::launch_gemm_nt(sb, d, 0, W2, d, 0, z, V, 0, N, V, d, 1, s));
+    MV_HIP(mvk::launch_medusa1_ce(z, labels, K, k, (float)lam[k], N, V, ltk, g, s));
+    if (dw2) {   // dW2 = g^T s: (g^T [V][N]) (s^T [d][N])^T
+      MV_HIP(mvk::launch_transpose_bf16(g, 0, at<u16>(ws, L.gt), 0, N, V, 1, s));
+      MV_HIP(mvk::launch_transpose_bf16(sb, 0, at<u16>(ws, L.st), 0, N, d, 1, s));
+      MV_HIP(mvk::launch_gemm_nt(at<u16>(ws, L.gt), N, 0, at<u16>(ws, L.st), N, 0,
+                                 dw2 + (size_t)k * V * d, d, 0, V, d, N, 1, s));
+    }
+    if (dw1) {   // ds = g W2 = g (W2^T [d][V])^T; da = ds SiLU'(a); dW1 = (da^T) (H^T)^T
+      MV_HIP(mvk::launch_transpose_bf16(W2, 0, at<u16>(ws, L.w2t), 0, V, d, 1, s));
+      MV_HIP(mvk::launch_gemm_nt(g, V, 0, at<u16>(ws, L.w2t), V, 0, at<float>(ws, L.ds), d, 0, N,
+                                 d, V, 1, s));
+      MV_HIP(mvk::launch_medusa1_dact(at<float>(ws, L.ds), a, at<u16>(ws, L.da), (size_t)N * d, s));
+      MV_HIP(mvk::launch_transpose_bf16(at<u16>(ws, L.da), 0, at<u16>(ws, L.dat), 0, N, d, 1, s));
+      MV_HIP(mvk::launch_gemm_nt(at<u16>(ws, L.dat), N, 0, at<u16>(ws, L.ht), N, 0,
+                                 dw1 + (size_t)k * d * d, d, 0, d, d, N, 1, s));
+    }
+  }
+  MV_HIP(mvk::launch_medusa1_sum(ltk, N * K, loss, s));
+  return MV_OK;
+}
+
 MV_API int mv_kv_compact(const mv_kv* kv, const int32_t* path, int32_t path_stride,
                          const int32_t* accept_len, int32_t* n_prefix, void* stream) {
   if (!kv || !kv->k || !kv->v || !path || !accept_len || !n_prefix)

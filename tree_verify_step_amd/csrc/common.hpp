@@ -251,4 +251,16 @@ hipError_t launch_advance(int32_t* n_prefix, const int32_t* accept_len, int B,
                           int32_t* counter, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
 
+// train.hip: Medusa-1 head loss and gradients
+hipError_t launch_gemm_nt(const u16* A, int lda, size_t sa, const u16* B, int ldb, size_t sb,
+                          float* C, int ldc, size_t sc, int M, int N, int K, int batch,
+                          hipStream_t s);
+hipError_t launch_transpose_bf16(const u16* in, size_t s_in, u16* out, size_t s_out, int R, int C,
+                                 int batch, hipStream_t s);
+hipError_t launch_medusa1_act(const float* a, const u16* h, u16* s, size_t n, hipStream_t st);
+hipError_t launch_medusa1_dact(const float* ds, const float* a, u16* da, size_t n, hipStream_t st);
+hipError_t launch_medusa1_ce(const float* z, const int32_t* labels, int ldl, int k, float lambda,
+                             int N, int V, float* loss_tk, u16* g, hipStream_t st);
+hipError_t launch_medusa1_sum(const float* v, int n, double* out, hipStream_t st);
+
 }  // namespace mvk
