@@ -79,26 +79,36 @@ def _attention_case(D, B, T, ns, depth, topk, seed, cap=None):
     return rng, paths, trees, ocaches, kv, q, cap
 
 
+# Caches of up to 2048 slots, and grids of at least 256 query-block
+# workgroups, run one workgroup per 16 queries; longer caches under smaller
+# grids split the keys (marked "split").
 @pytest.mark.parametrize("hd,H,B,T,ns,cap", [
     (16, 4, 1, 15, [32], None),            # tiny shape
     (128, 2, 1, 64, [512], None),          # 7B head dim, one mask word
     (128, 2, 1, 64, [37], None),           # ragged prefix, not a multiple of 4 or 64
-    (128, 2, 4, 64, [1030, 64, 7, 2047], None),  # batch with ragged prefixes (split keys)
-    (64, 2, 1, 256, [300], None),          # four mask words (split keys)
+    (128, 2, 4, 64, [1030, 64, 7, 2047], None),  # split: batch with ragged prefixes
+    (64, 2, 1, 256, [300], None),          # four mask words
     (128, 1, 1, 1, [100], None),           # root only: a vanilla decode step
     (32, 2, 2, 17, [0, 5], None),          # empty prefix for one sequence
-    # many (sequence, head, query block) triples, long trees (split keys)
+    # many (sequence, head, query block) triples, long trees
     (128, 40, 1, 256, [1024], None),       # 13B-width heads, 256-node tree
     (64, 33, 1, 250, [17], None),          # ragged last query block
     (16, 64, 2, 80, [33, 7], None),        # odd query-block count
-    # the 7B head count with a long cache: split keys at short and long n,
-    # one split (the whole range) at n = 0, and 16-query blocks for cap 640
+    # split: the 7B head count with a long cache at short and long n, one
+    # split (the whole range) at n = 0; 16-query blocks for cap 640
     (128, 32, 1, 64, [512], 4096),
     (128, 32, 1, 64, [4000], 4096),
     (128, 32, 1, 64, [0], 4096),
     (128, 32, 1, 64, [576], 640),
-    # the 33B batch: 208 (sequence, head) pairs, one split each
+    # the 33B batch: 208 (sequence, head) pairs
     (128, 52, 4, 64, [1619, 1964, 1651, 1155], None),
+    # split: wider query blocks (two and four per wave), a batch, a
+    # root-only step and a single query block
+    (128, 8, 1, 128, [3000], 4096),
+    (64, 9, 1, 250, [2000], 2560),
+    (128, 20, 2, 64, [2100, 3000], 3072),
+    (128, 32, 1, 1, [3000], 4096),
+    (128, 32, 1, 16, [2500], 4096),
 ])
 def test_tree_attention_matches_oracle(hd, H, B, T, ns, cap):
     _flush(f"tree_attention hd={hd} H={H} B={B} T={T} ns={ns} cap={cap}")

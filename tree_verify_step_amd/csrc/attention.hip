@@ -8,9 +8,9 @@
 // node v's words set iff a is v or an ancestor of v.
 //
 // Two decompositions, chosen per launch shape on the host
-// (attention_uses_splits): one workgroup per 16 queries for short caches
-// and trees of up to 64 nodes (tree_attention_qb_kernel, further below), and
-// split key ranges otherwise:
+// (attention_uses_splits): one workgroup per 16 queries for caches of up
+// to 2048 slots or grids that fill the chip (tree_attention_qb_kernel,
+// further below), and split key ranges for long caches under small grids:
 //
 // Split-KV: the key slots 0 .. n+T-1 of one (sequence, head) pair are cut
 // into 64-key tiles, and the S workgroups of the pair take every S-th tile
@@ -664,13 +664,13 @@ static void launch_attention_qb(const u16* q, const u16* kc, const u16* vc, cons
                        anc, B, T, H, cap, mw, out, packed);
 }
 
-// Key splits per (sequence, head): about one workgroup per compute unit, at
-// most 16 (the partial states grow with S); the kernel uses fewer when the
-// tiles at the current n do not need them.
+// Key splits per (sequence, head): about two workgroups per compute unit
+// for trees of up to 64 nodes (one for the wider query blocks of larger
+// trees), at most 16 (the partial states grow with S); the kernel uses fewer
+// when the tiles at the current n do not need them.
 int attention_splits(int B, int H, int T) {
-  (void)T;
   const int pairs = B * H;
-  return std::max(1, std::min(16, 256 / std::max(pairs, 1)));
+  return std::max(1, std::min(16, (T <= 64 ? 512 : 256) / std::max(pairs, 1)));
 }
 
 template <int HD, int QPW>
@@ -693,10 +693,13 @@ static void launch_attention_hd(const AttnArgs& a, hipStream_t s) {
 }
 
 bool attention_uses_splits(int B, int H, int T, int cap) {
-  // per query block while its grid fits the chip in one round, the tree has
-  // at most 64 nodes and the cache at most 2048 slots (about where splitting
-  // the keys overtakes re-reading them per query block)
-  return !(T <= 64 && B * H * ((T + 15) / 16) <= 256 && cap <= 2048);
+  // Per query block while the cache holds at most 2048 slots or that grid
+  // already gives every compute unit a workgroup; split keys for long caches
+  // under a small grid.  Measured per launch: 8.7 against 14 us at the 7B
+  // shape with n = 512, 34 against 55 us for 256-node trees at the 13B shape
+  // (640 workgroups), 57 against 86 us for the 33B batch of four (832); the
+  // split kernel wins for 32 heads of a 64-node tree at n = 4096.
+  return cap > 2048 && B * H * ((T + 15) / 16) < 256;
 }
 
 hipError_t launch_attention(const u16* q, const u16* kc, const u16* vc, const int32_t* n_prefix,
