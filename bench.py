@@ -182,14 +182,19 @@ def gate_up_bytes(D, M):
     return 2 * D.F * D.d * 2 + M * D.d * 2 + M * D.F * 2
 
 
-def cpu_baseline(w, n0, sample_layers=2):
-    """The oracle (float64 NumPy, as it stands) on a bounded sample of one
-    step of workload `w`: all Medusa heads with top-s and tree fill,
-    `sample_layers` of the L decoder layers over the whole tree against an
-    n0-token prefix cache, final norm + LM head, the workload's acceptance
-    rule.  The step time is scaled to all L layers."""
+def cpu_baseline(w, n0, steps=3, distinct_layers=2):
+    """The oracle (float64 NumPy, as it stands) running `steps` whole steps
+    of workload `w` for one sequence: all Medusa heads with top-s and tree
+    fill, every one of the L decoder layers over the whole tree against an
+    n0-token prefix cache (each layer upcasting its float32-held bf16 weights
+    to float64, as the oracle does), final norm + LM head, the workload's
+    acceptance rule, KV compaction and the next root.  Layer l uses the
+    weights of layer l mod `distinct_layers`: the oracle's work does not
+    depend on the values, and drawing 32 distinct 7B-sized layers on the host
+    would take minutes of input generation."""
     import numpy as np
     from oracle import accept as oa
+    from oracle import decode as od
     from oracle import heads as oh
     from oracle import model as om
     from oracle import tree as otree
@@ -197,52 +202,59 @@ def cpu_baseline(w, n0, sample_layers=2):
 
     D = w.dims
     Wt = synth.Weights(w)
+
+    def get(name):
+        if name.startswith("layer"):
+            l, rest = name[len("layer"):].split(".", 1)
+            name = f"layer{int(l) % distinct_layers}.{rest}"
+        return Wt.get(name)
+
     paths = synth.tree_paths(w, 0)
     t = otree.compile_tree(paths)
     s = synth.tree_topk(w)
     rng = np.random.default_rng(0)
-    cap = n0 + t.T
-    kv = om.KVCache(sample_layers, D.H, D.hd, cap)
-    for l in range(sample_layers):
+    cap = n0 + steps * (t.max_depth + 1) + t.T
+    kv = om.KVCache(D.L, D.H, D.hd, cap)
+    for l in range(D.L):
         kv.K[l][:, :n0] = rng.standard_normal((D.H, n0, D.hd))
         kv.V[l][:, :n0] = rng.standard_normal((D.H, n0, D.hd))
     h = rng.standard_normal(D.d)
-    # generate the sampled weights up front (input generation is not timed)
+    t0_tok, n = 1, n0
+    # draw the weights up front (input generation is not timed)
     for k in range(1, t.max_depth + 1):
-        Wt.get(f"head{k}.w1"), Wt.get(f"head{k}.w2")
-    for l in range(sample_layers):
+        get(f"head{k}.w1"), get(f"head{k}.w2")
+    for l in range(distinct_layers):
         Wt.layer(l)
-    Wt.get("embed"), Wt.get("lm_head"), Wt.get("final_norm")
-    t0 = time.perf_counter()
-    z = oh.medusa_heads(Wt.get, h, t.max_depth)
-    top = oh.head_topk(z, s)
-    tok = otree.fill_tokens(t, 0, top)
-    x = om.f64(Wt.get("embed"))[tok]
-    t1 = time.perf_counter()
-    pos, slots, vis = om.tree_positions(t, n0), n0 + np.arange(t.T), om.tree_visibility(t, n0, cap)
-    for l in range(sample_layers):
-        x = om.decoder_layer(x, Wt.layer(l), kv.K[l], kv.V[l], pos, slots, vis, D.H)
-    t2 = time.perf_counter()
-    hn = om.rmsnorm(x, Wt.get("final_norm"))
-    logits = hn @ om.f64(Wt.get("lm_head")).T
-    if w.accept == "greedy":
-        oa.greedy_accept(t, tok, logits)
-    elif w.accept == "typical":
-        oa.typical_accept(t, tok, logits, w.temperature, w.eps, w.delta)
-    else:
-        oa.reject_accept(t, tok, logits, w.temperature, rng.random(t.T))
-    t3 = time.perf_counter()
-    per_layer = (t2 - t1) / sample_layers
-    step = (t1 - t0) + D.L * per_layer + (t3 - t2)
+    get("embed"), get("lm_head"), get("final_norm")
+    u = rng.random((steps, t.T))
+    t_start = time.perf_counter()
+    accepted = 0
+    for i in range(steps):
+        z = oh.medusa_heads(get, h, t.max_depth)
+        tok = otree.fill_tokens(t, t0_tok, oh.head_topk(z, s))
+        hn, logits = om.tree_forward(get, D.L, D.H, t, tok, n, kv)
+        if w.accept == "greedy":
+            res = oa.greedy_accept(t, tok, logits)
+        elif w.accept == "typical":
+            res = oa.typical_accept(t, tok, logits, w.temperature, w.eps, w.delta)
+        else:
+            res = oa.reject_accept(t, tok, logits, w.temperature, u[i])
+        od.compact_kv(kv, n, res.path)
+        n += len(res.path)
+        accepted += len(res.path)
+        t0_tok = oa.argmax_lowest(logits[res.best])
+        h = hn[res.best].copy()
+    step = (time.perf_counter() - t_start) / steps
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         cores = len(os.sched_getaffinity(0))
     return {"value": 1.0 / step, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": (f"one step with {sample_layers} of {D.L} decoder layers timed "
-                       f"({per_layer:.2f} s/layer) plus heads, LM head and acceptance, "
-                       f"scaled to {D.L} layers; float64 NumPy; T={t.T}, n={n0}"),
+            "sample": (f"{steps} whole steps of one sequence: heads and top-s, all {D.L} decoder "
+                       f"layers (layer l with layer l mod {distinct_layers}'s weights), final norm "
+                       f"and LM head, {w.accept} acceptance, KV compaction; float64 NumPy with "
+                       f"the per-layer weight upcast; T={t.T}, n={n0}; {accepted} tokens accepted"),
             "tree_tokens_per_s": t.T / step, "seconds_per_step": step}
 
 
