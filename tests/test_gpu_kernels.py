@@ -271,6 +271,9 @@ def test_decoder_layer_matches_oracle(name, B, ns):
 
 @pytest.mark.parametrize("B,d,V,K,s", [(1, 64, 512, 3, 2), (1, 256, 1024, 4, 10), (4, 128, 640, 4, 10),
                                         (4, 6656, 640, 2, 10),    # 33B width: 104 KiB of inputs in LDS
+                                        (4, 8192, 512, 1, 4),     # the 128 KiB LDS limit, one head
+                                        (1, 5120, 2048, 2, 10),   # batch 1 past 4096: LDS-staged input
+                                        (3, 1024, 32000, 2, 10),  # full vocabulary, a batch of 3
                                         (1, 64, 40960, 2, 10),    # 16 logits a lane in top-s stage 1
                                         (1, 64, 131072, 2, 8)])   # > 64 stage-1 waves: sorted merge
 def test_medusa_heads_match_oracle(B, d, V, K, s):

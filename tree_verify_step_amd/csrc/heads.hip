@@ -5,100 +5,180 @@
 // At batch size B the heads are matrix-vector products over bf16 weights
 // that are read exactly once, so they are HBM-bound GEMVs: each wave owns
 // whole weight rows, its 64 lanes read 16 contiguous bytes each (a 1 KiB
-// coalesced piece of a row per instruction; eight pieces of each of two rows
-// in flight), multiply by the fp32 input held in LDS and reduce across the
-// wave.
+// coalesced piece of a row per instruction, several rows and pieces in
+// flight), multiply by the input and reduce across the wave.  At batch 1
+// with d <= 4096 the input lives in registers (heads_gemv1_kernel); else it
+// is staged once per workgroup in LDS as fp32 and each workgroup streams a
+// long run of rows (heads_gemv_kernel).
 #include "common.hpp"
 
 namespace mvk {
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));   // a 16-byte register piece
 
-constexpr int GEMV_RW = 2;            // rows per wave per iteration
+constexpr int GEMV_RW = 2;            // rows per wave per iteration (batch-1 kernel)
 constexpr int GEMV_ROWS_PER_WG = 64;  // 16 rows per wave
 constexpr int GEMV_CH = 8;            // 1 KiB row pieces per lane in flight
+
+// Batches (and batch 1 with d > 512 * GEMV_CH): the fp32 input rows [B][d]
+// are staged once per workgroup in LDS, and the workgroup then streams a long
+// run of rows of one head.  Eight waves; each takes GB_R rows at a time in
+// blocks of GB_CH 1 KiB pieces of each, the next block's loads in flight
+// during this block's math, so one LDS read of the input serves GB_R rows.
+// The staging issues all its 16-byte loads before its first LDS store (a
+// single memory round trip).  Measured at the 33B heads (B = 4, d = 6656,
+// 2.06 GB): 1.55 ms with a per-element staging loop in 64-row workgroups,
+// 0.45 ms with this layout and one block in flight, 0.42 ms with two.
+constexpr int GB_WAVES = 8;
+constexpr int GB_R = 4;
+constexpr int GB_CH = 4;
+
+// GB_CH pieces of GB_R rows from row r0, column c0 (rows clamped to r_last,
+// columns to d - 8: always in bounds)
+__device__ __forceinline__ void gb_load(u32x4v (&w)[GB_CH][GB_R], const u16* Wk, int r0, int c0,
+                                        int r_last, int d, int lane) {
+#pragma unroll
+  for (int j = 0; j < GB_CH; ++j) {
+    const int c = min(c0 + j * 512 + lane * 8, d - 8);
+#pragma unroll
+    for (int i = 0; i < GB_R; ++i) {
+      const int r = min(r0 + i, r_last);
+      w[j][i] = *reinterpret_cast<const u32x4v*>(Wk + (size_t)r * d + c);
+    }
+  }
+}
+
+// acc[i][b] += the block's pieces of row i against input row b
+template <int MAXB>
+__device__ __forceinline__ void gb_math(const u32x4v (&w)[GB_CH][GB_R], const float* xs, int d, int B,
+                                        int c0, int lane, float (&acc)[GB_R][MAXB]) {
+#pragma unroll
+  for (int j = 0; j < GB_CH; ++j) {
+    const int c = c0 + j * 512 + lane * 8;
+    if (c >= d) break;
+#pragma unroll
+    for (int b = 0; b < MAXB; ++b) {
+      if (b >= B) break;
+      const float4 x0 = *reinterpret_cast<const float4*>(xs + (size_t)b * d + c);
+      const float4 x1 = *reinterpret_cast<const float4*>(xs + (size_t)b * d + c + 4);
+#pragma unroll
+      for (int i = 0; i < GB_R; ++i) {
+        float a = acc[i][b];
+        a += bf16lo(w[j][i][0]) * x0.x + bf16hi(w[j][i][0]) * x0.y;
+        a += bf16lo(w[j][i][1]) * x0.z + bf16hi(w[j][i][1]) * x0.w;
+        a += bf16lo(w[j][i][2]) * x1.x + bf16hi(w[j][i][2]) * x1.y;
+        a += bf16lo(w[j][i][3]) * x1.z + bf16hi(w[j][i][3]) * x1.w;
+        acc[i][b] = a;
+      }
+    }
+  }
+}
+
+// wave sums of the accumulators of rows r0 .. r0+GB_R-1; lane 0 stores the
+// rows below r_end; the accumulators are cleared for the next row group
+template <int MAXB>
+__device__ __forceinline__ void gb_reduce(float (&acc)[GB_R][MAXB], const float* xs, float* out, int B,
+                                          int D, int k, int d, int rows, int r0, int r_end, int mode,
+                                          int lane) {
+#pragma unroll
+  for (int i = 0; i < GB_R; ++i) {
+    const int r = r0 + i;
+#pragma unroll
+    for (int b = 0; b < MAXB; ++b) {
+      if (b >= B) break;
+      const float y = warp_sum(acc[i][b]);
+      if (lane == 0 && r < r_end) {
+        const size_t o = ((size_t)b * D + k) * rows + r;
+        out[o] = mode == 0 ? xs[(size_t)b * d + r] + silu_f(y) : y;
+      }
+      acc[i][b] = 0.f;
+    }
+  }
+}
 
 // mode 0: y = W1 x -> u[b][k][j] = h[b][j] + SiLU(y) (x = h, bf16 input)
 // mode 1: y = W2 x -> z[b][k][j] = y             (x = u[b][k], fp32 input)
 template <int MAXB>
-__global__ __launch_bounds__(256) void heads_gemv_kernel(const u16* __restrict__ hb,
-                                                         const float* __restrict__ uf,
-                                                         const u16* __restrict__ W,
-                                                         float* __restrict__ out, int B, int D,
-                                                         int d, int rows, int mode, int rpw) {
-  extern __shared__ float xs[];                   // [B][d]
-  const int k = blockIdx.y;                       // head index 0..D-1 (head k+1)
+__global__ __launch_bounds__(GB_WAVES * 64) void heads_gemv_kernel(
+    const u16* __restrict__ hb, const float* __restrict__ uf, const u16* __restrict__ W,
+    float* __restrict__ out, int B, int D, int d, int rows, int mode, int rpw) {
+  extern __shared__ float xs[];
+  constexpr int NT = GB_WAVES * 64, RG = GB_WAVES * GB_R;
+  const int k = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const u16* Wk = W + (size_t)k * rows * d;
-  const int r_lo = blockIdx.x * rpw;
-  const int r_hi = min(rows, r_lo + rpw);
-  // GEMV_CH 1 KiB pieces of each of the wave's GEMV_RW rows per block
-  uint4 w[GEMV_CH][GEMV_RW];
-  auto load = [&](int r0, int c0) {
+  // the workgroup's rows r_lo .. r_hi-1 in groups of RG; wave w takes rows
+  // w * GB_R .. +GB_R-1 of each group
+  const int r_lo = blockIdx.x * rpw, r_hi = min(rows, r_lo + rpw);
+  const int my_groups = r_hi > r_lo ? (r_hi - r_lo + RG - 1) / RG : 0;
+  auto grp_row = [&](int g) { return r_lo + g * RG + wave * GB_R; };
+  const int nch = (d + 512 * GB_CH - 1) / (512 * GB_CH);
+  const int nblk = my_groups * nch;
+  u32x4v wa[GB_CH][GB_R];
+  u32x4v wb[GB_CH][GB_R];
+  if (nblk > 0) gb_load(wa, Wk, grp_row(0), 0, rows - 1, d, lane);
+  // ---- stage the input rows: d % 8 == 0, so a row is whole 16-byte pieces
+  // (in rounds of SR pieces a thread, at most one round at 4 x 8192 fp32:
+  // the loads of a round go out together; vector-typed registers and clamped
+  // indexes keep the round in registers)
+  constexpr int SR = 16;
+  if (mode == 0) {
+    const int n8 = B * d / 8;
+    for (int base = 0; base < n8; base += SR * NT) {
+      u32x4v t[SR];
 #pragma unroll
-    for (int j = 0; j < GEMV_CH; ++j) {
-      const int c = min(c0 + j * 512 + lane * 8, d - 8);      // clamped: in bounds
+      for (int it = 0; it < SR; ++it) {
+        const int i = base + threadIdx.x + it * NT;
+        t[it] = i < n8 ? reinterpret_cast<const u32x4v*>(hb)[i] : u32x4v{0u, 0u, 0u, 0u};
+      }
 #pragma unroll
-      for (int i = 0; i < GEMV_RW; ++i) {
-        const int r = min(r0 + i, r_hi - 1);
-        w[j][i] = *reinterpret_cast<const uint4*>(Wk + (size_t)r * d + c);
+      for (int it = 0; it < SR; ++it) {
+        const int i = base + threadIdx.x + it * NT;
+        if (i < n8) {
+          float4* dst = reinterpret_cast<float4*>(xs + 8 * i);
+          dst[0] = float4{bf16lo(t[it][0]), bf16hi(t[it][0]), bf16lo(t[it][1]), bf16hi(t[it][1])};
+          dst[1] = float4{bf16lo(t[it][2]), bf16hi(t[it][2]), bf16lo(t[it][3]), bf16hi(t[it][3])};
+        }
       }
     }
-  };
-  // the wave's first block of weights is requested before the input rows
-  // are staged, and every later block right after the previous one's math,
-  // so that 2 * GEMV_CH loads per lane stay in flight across the reductions
-  int r0 = r_lo + wave * GEMV_RW;
-  if (r0 < r_hi) load(r0, 0);
-  for (int i = threadIdx.x; i < B * d; i += 256) {
-    const int b = i / d, c = i % d;
-    xs[i] = mode == 0 ? bf16_to_f32(hb[(size_t)b * d + c]) : uf[((size_t)b * D + k) * d + c];
+  } else {
+    const int q = d / 4, n4 = B * q;
+    for (int base = 0; base < n4; base += SR * NT) {
+      f32x4 t[SR];
+#pragma unroll
+      for (int it = 0; it < SR; ++it) {
+        const int i = base + threadIdx.x + it * NT;
+        const int ii = min(i, n4 - 1);
+        const int b = ii / q, c4 = ii - b * q;
+        t[it] = reinterpret_cast<const f32x4*>(uf + ((size_t)b * D + k) * d)[c4];
+      }
+#pragma unroll
+      for (int it = 0; it < SR; ++it) {
+        const int i = base + threadIdx.x + it * NT;
+        if (i < n4) reinterpret_cast<f32x4*>(xs)[i] = t[it];
+      }
+    }
   }
   __syncthreads();
-  for (; r0 < r_hi; r0 += 4 * GEMV_RW) {
-    float acc[GEMV_RW][MAXB];
+  float acc[GB_R][MAXB];
 #pragma unroll
-    for (int i = 0; i < GEMV_RW; ++i)
+  for (int i = 0; i < GB_R; ++i)
 #pragma unroll
-      for (int b = 0; b < MAXB; ++b) acc[i][b] = 0.f;
-    for (int c0 = 0; c0 < d; c0 += 512 * GEMV_CH) {
-#pragma unroll
-      for (int j = 0; j < GEMV_CH; ++j) {
-        const int c = c0 + j * 512 + lane * 8;
-        if (c >= d) break;
-#pragma unroll
-        for (int b = 0; b < MAXB; ++b) {
-          if (b >= B) break;
-          const float4 x0 = *reinterpret_cast<const float4*>(xs + (size_t)b * d + c);
-          const float4 x1 = *reinterpret_cast<const float4*>(xs + (size_t)b * d + c + 4);
-#pragma unroll
-          for (int i = 0; i < GEMV_RW; ++i) {
-            float a = acc[i][b];
-            a += bf16lo(w[j][i].x) * x0.x + bf16hi(w[j][i].x) * x0.y;
-            a += bf16lo(w[j][i].y) * x0.z + bf16hi(w[j][i].y) * x0.w;
-            a += bf16lo(w[j][i].z) * x1.x + bf16hi(w[j][i].z) * x1.y;
-            a += bf16lo(w[j][i].w) * x1.z + bf16hi(w[j][i].w) * x1.w;
-            acc[i][b] = a;
-          }
-        }
-      }
-      int nr = r0, nc = c0 + 512 * GEMV_CH;
-      if (nc >= d) {
-        nr = r0 + 4 * GEMV_RW;
-        nc = 0;
-      }
-      if (nr < r_hi) load(nr, nc);
+    for (int b = 0; b < MAXB; ++b) acc[i][b] = 0.f;
+  // blocks (row group, column chunk) in order, ping-ponging between two
+  // register sets: the next block's loads go out before this block's math
+  for (int bi = 0; bi < nblk; bi += 2) {
+    {
+      const int n1 = bi + 1;
+      if (n1 < nblk) gb_load(wb, Wk, grp_row(n1 / nch), (n1 % nch) * 512 * GB_CH, rows - 1, d, lane);
+      gb_math<MAXB>(wa, xs, d, B, (bi % nch) * 512 * GB_CH, lane, acc);
+      if (bi % nch == nch - 1) gb_reduce<MAXB>(acc, xs, out, B, D, k, d, rows, grp_row(bi / nch), r_hi, mode, lane);
     }
-#pragma unroll
-    for (int i = 0; i < GEMV_RW; ++i) {
-      const int r = r0 + i;
-#pragma unroll
-      for (int b = 0; b < MAXB; ++b) {
-        if (b >= B) break;
-        const float y = warp_sum(acc[i][b]);
-        if (lane == 0 && r < r_hi) {
-          const size_t o = ((size_t)b * D + k) * rows + r;
-          out[o] = mode == 0 ? xs[(size_t)b * d + r] + silu_f(y) : y;
-        }
-      }
+    if (bi + 1 >= nblk) break;
+    {
+      const int n2 = bi + 2, b1 = bi + 1;
+      if (n2 < nblk) gb_load(wa, Wk, grp_row(n2 / nch), (n2 % nch) * 512 * GB_CH, rows - 1, d, lane);
+      gb_math<MAXB>(wb, xs, d, B, (b1 % nch) * 512 * GB_CH, lane, acc);
+      if (b1 % nch == nch - 1) gb_reduce<MAXB>(acc, xs, out, B, D, k, d, rows, grp_row(b1 / nch), r_hi, mode, lane);
     }
   }
 }
@@ -183,12 +263,24 @@ __global__ __launch_bounds__(256) void heads_gemv1_kernel(const u16* __restrict_
   }
 }
 
-// rpw rows per workgroup (a multiple of 4 waves x GEMV_RW): fewer rows per
-// workgroup when the matrix is short, so that the grid still covers the CUs.
+// The batch-1 kernel (input in registers) takes rpw rows per workgroup, a
+// multiple of 4 waves x GEMV_RW, fewer when the matrix is short so that the
+// grid still covers the CUs.  The staged kernel takes long row runs: about
+// one workgroup per compute unit over all D heads (its LDS input allows no
+// more), rpw a multiple of its 8 waves x GB_R.
 static hipError_t launch_gemv(const u16* hb, const float* uf, const u16* W, float* out, int B,
                               int D, int d, int rows, int mode, hipStream_t s) {
-  int rpw = GEMV_ROWS_PER_WG;
-  while (rpw > 4 * GEMV_RW && (size_t)((rows + rpw - 1) / rpw) * D < 1024) rpw /= 2;
+  if (B == 1 && d <= 512 * GEMV_CH) {
+    int rpw = GEMV_ROWS_PER_WG;
+    while (rpw > 4 * GEMV_RW && (size_t)((rows + rpw - 1) / rpw) * D < 1024) rpw /= 2;
+    dim3 grid((rows + rpw - 1) / rpw, D);
+    hipLaunchKernelGGL(heads_gemv1_kernel, grid, dim3(256), 0, s, hb, uf, W, out, D, d, rows, mode, rpw);
+    return hipGetLastError();
+  }
+  if (B < 1 || B > 4 || d % 8 || d > 8192) return hipErrorInvalidValue;
+  constexpr int RG = GB_WAVES * GB_R;
+  const long per_cu = ((long)rows * D + 255) / 256;
+  const int rpw = (int)std::max<long>(RG, (per_cu + RG - 1) / RG * RG);
   dim3 grid((rows + rpw - 1) / rpw, D);
   // the fp32 input rows live in LDS: up to 4 x 8192 x 4 B = 128 KiB (gfx950
   // has 160 KiB per workgroup; above 64 KiB the launch must opt in)
@@ -202,14 +294,12 @@ static hipError_t launch_gemv(const u16* hb, const float* uf, const u16* W, floa
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)MV_HEADS_LDS_MAX);
     if (e != hipSuccess) return e;
   }
-  if (B == 1 && d <= 512 * GEMV_CH)
-    hipLaunchKernelGGL(heads_gemv1_kernel, grid, dim3(256), 0, s, hb, uf, W, out, D, d, rows, mode, rpw);
-  else if (B == 1)
-    hipLaunchKernelGGL((heads_gemv_kernel<1>), grid, dim3(256), lds, s, hb, uf, W, out, B, D, d, rows, mode, rpw);
-  else if (B <= 4)
-    hipLaunchKernelGGL((heads_gemv_kernel<4>), grid, dim3(256), lds, s, hb, uf, W, out, B, D, d, rows, mode, rpw);
+  if (B == 1)
+    hipLaunchKernelGGL((heads_gemv_kernel<1>), grid, dim3(GB_WAVES * 64), lds, s, hb, uf, W, out, B, D,
+                       d, rows, mode, rpw);
   else
-    return hipErrorInvalidValue;
+    hipLaunchKernelGGL((heads_gemv_kernel<4>), grid, dim3(GB_WAVES * 64), lds, s, hb, uf, W, out, B, D,
+                       d, rows, mode, rpw);
   return hipGetLastError();
 }
 
