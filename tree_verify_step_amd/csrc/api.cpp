@@ -78,6 +78,7 @@ enum GemmKind { G_QKV = 0, G_O, G_GU, G_DOWN, G_LM, G_KINDS };
 
 struct GemmCfg {
   int w, nbw, splits, ntiles, mtiles, MB, N, K, epi;
+  int wide;     // 0, or the wide-tile kernel's column blocks per wave
 };
 
 // Waves per workgroup and column blocks per wave per GEMM (measured on
@@ -110,11 +111,33 @@ static GemmCfg gemm_cfg(const mv_dims& D, int kind, int Mp) {
       break;
   }
   c.mtiles = (Mp / 16 + c.MB - 1) / c.MB;
+  const int KB = c.K / 32;
+  c.wide = 0;
+  // More than 128 rows: the wide-tile kernel (256 rows x 128 columns, or x
+  // 160 for gate/up when 64-feature tiles would not fit the compute units in
+  // one round), whose range-checked operand loads need each operand below 2 GiB
+  if (c.MB == 16 && (size_t)c.N * c.K * 2 < (1ull << 31) && (size_t)Mp * c.K * 2 < (1ull << 31)) {
+    c.wide = 4;
+    if (c.epi == mvk::EPI_SWIGLU && mvk::gemm_wide_ntiles(c.epi, c.N, 4) * c.mtiles > 256) c.wide = 5;
+    c.w = 8;
+    c.nbw = 1;
+    c.ntiles = mvk::gemm_wide_ntiles(c.epi, c.N, c.wide);
+    // K splits while the tiles leave compute units idle, each split at least
+    // four 2-k-block stages
+    c.splits = std::max(1, std::min(256 / (c.ntiles * c.mtiles), KB / 8));
+    return c;
+  }
   c.ntiles = mvk::gemm_ntiles(c.epi, c.N, c.w, c.nbw);
-  const int KB = c.K / 32, KC = mvk::gemm_kc(c.MB);
+  const int KC = mvk::gemm_kc(c.MB);
   c.splits = std::max(1, 256 / (c.ntiles * c.mtiles));
   c.splits = std::max(1, std::min(c.splits, KB / (2 * KC)));
   return c;
+}
+
+// Bytes of one K split's partial tile.
+static size_t gemm_partial_bytes(const GemmCfg& c) {
+  if (c.wide) return (size_t)c.wide * 32768;     // 8 waves x 4 x wide accumulators of 1 KiB
+  return (size_t)c.w * c.MB * c.nbw * 256 * sizeof(float);
 }
 
 struct Ws {
@@ -146,8 +169,7 @@ static Ws ws_layout(const mv_dims& D, int B, int T, int P = 0) {
     for (int k = 0; k < G_KINDS; ++k) {
       const GemmCfg c = gemm_cfg(D, k, Mq);
       const size_t tiles = (size_t)c.ntiles * c.mtiles;
-      if (c.splits > 1)
-        part = std::max(part, tiles * c.splits * c.w * c.MB * c.nbw * 256 * sizeof(float));
+      if (c.splits > 1) part = std::max(part, tiles * c.splits * gemm_partial_bytes(c));
       max_tiles = std::max(max_tiles, tiles);
     }
     w.ss_ld = std::max(w.ss_ld, ss_ld_of(D, Mq));
@@ -212,6 +234,7 @@ static mvk::GemmArgs gemm_args(const mv_dims& D, int kind, int M, void* ws, cons
   g.nbw = c.nbw;
   g.splits = c.splits;
   g.epi = c.epi;
+  g.wide = c.wide;
   g.ss_ld = L.ss_ld;
   g.partial = at<float>(ws, L.part);
   g.counters = at<int>(ws, L.counters);
@@ -302,7 +325,7 @@ static int enq_layer(const mv_dims& D, int B, const mv_tree& t, const int32_t* n
   g.qkv.d = D.d;
   {   // compute units the QKV tiles leave idle read the prefix K/V ahead
     const GemmCfg c = gemm_cfg(D, G_QKV, round16(M));
-    g.prefetch = std::max(0, (256 - c.ntiles * c.splits * c.mtiles) / (c.splits * c.mtiles));
+    g.prefetch = c.wide ? 0 : std::max(0, (256 - c.ntiles * c.splits * c.mtiles) / (c.splits * c.mtiles));
     // half the weight bytes one tile workgroup streams
     g.pf_budget16 = (int)((size_t)c.N * c.K * 2 / ((size_t)c.ntiles * c.splits * c.mtiles) / 2 / 16);
   }

@@ -151,6 +151,8 @@ struct GemmArgs {
   float* partial;    // split-K partial tiles
   int* counters;     // split-K arrival counters [tiles], zero between launches
   QkvArgs qkv;
+  int wide;          // 0, or the wide-tile kernel's column blocks per wave (4 or
+                     //   5; more than 128 rows): tiles of 256 rows x 32*wide columns
   int prefetch;      // QKV: extra grid columns of workgroups that read this
                      //   layer's cached prefix K/V ahead of the attention launch,
   int pf_budget16;   //   at most this many 16-byte pieces each
@@ -159,6 +161,7 @@ struct GemmArgs {
 int gemm_mb(int Mp);                                  // 16-row blocks per tile
 int gemm_kc(int MB);                                  // k-blocks per chunk
 int gemm_ntiles(int epi, int N, int w, int nbw);      // column tiles
+int gemm_wide_ntiles(int epi, int N, int nbh);        // column tiles of the wide kernel
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
 hipError_t launch_pack(const u16* src, u16* dst, int R, int C, int rope_hd, int rope_rows,
                        hipStream_t s);

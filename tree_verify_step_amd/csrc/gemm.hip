@@ -856,6 +856,533 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Wide tiles for launches of more than 128 rows (a 256-node tree, a batch of
+// four 64-node trees, 256-row prefill chunks).  There each weight byte meets
+// 256 rows, next to the MFMA ridge, and the 16-row-block tiles above -- whose
+// waves each read the whole 256-row operand from LDS for one 16-column block
+// -- are bound by LDS reads.  Here a workgroup of 8 waves owns 256 rows x
+// 32*NBH columns: wave (wm, wn) computes rows 64*wm .. +63 against column
+// blocks NBH*wn .. +NBH-1 of the tile (4 x NBH accumulators of 16 x 16), so
+// every fragment read from LDS feeds NBH or 4 MFMAs.  Both operands are staged
+// through LDS, WIDE_KS k-blocks a stage, double-buffered, from a register
+// prefetch WIDE_P stages deep (each thread issues 4 activation and up to 3
+// weight loads of 16 bytes a stage); one barrier a stage.  The epilogues work
+// on the tile staged in LDS as fp32 (SwiGLU: the up accumulators parked
+// there), so that every global store is a whole 16-byte piece.
+// SwiGLU tiles take gate blocks NBH*nt .. +NBH-1 (waves wn = 0) and the same
+// up blocks (wn = 1); the others take column blocks 2*NBH*nt .. +2*NBH-1.
+// ---------------------------------------------------------------------------
+constexpr int WIDE_KS = 2;       // k-blocks per stage
+constexpr int WIDE_P = 3;        // stages of loads in flight
+constexpr int WIDE_TR = 256;     // rows of a tile
+
+template <int NBH, int EPI>
+struct WideShape {
+  static constexpr int NB = 2 * NBH;                  // 16-column blocks of a tile
+  static constexpr int TC = 16 * NB;                  // columns of a tile
+  static constexpr int AP = 16 * WIDE_KS;             // activation pieces (1 KiB) a stage
+  static constexpr int WP = NB * WIDE_KS;             // weight pieces a stage
+  static constexpr int AL = AP / 8;                   // ... loaded per thread
+  static constexpr int WL = (WP + 7) / 8;
+  static constexpr int OPB = (AP + WP) * 64;          // bf16x8 of one stage buffer
+  static constexpr int NBUF = 3;                      // stage buffers in LDS
+  static constexpr int LDF = TC + 4;                  // fp32 staging row (floats)
+  static constexpr int FT = 16 * NBH;                 // SwiGLU: features of a tile
+  static constexpr int LDH = FT + 8;                  // SwiGLU: bf16 staging row (u16)
+  static constexpr int STG_BYTES = EPI == EPI_SWIGLU ? WIDE_TR * FT * 4 + WIDE_TR * LDH * 2
+                                                     : WIDE_TR * LDF * 4;
+  static constexpr int SMEM16 = (NBUF * OPB * 16 > STG_BYTES ? NBUF * OPB * 16 : STG_BYTES) / 16;
+};
+
+template <int NBH, int EPI>
+__global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g) {
+  using S = WideShape<NBH, EPI>;
+  constexpr int NB = S::NB, TC = S::TC, AP = S::AP, WP = S::WP, AL = S::AL, WL = S::WL;
+  constexpr int OPB = S::OPB, LDF = S::LDF;
+  static_assert(AP % 8 == 0, "activation pieces divide over the waves");
+  __shared__ bf16x8 smem[S::SMEM16];
+  __shared__ float rs_s[WIDE_TR];
+  __shared__ int s_last;
+  __shared__ int s_slot0[MV_MAX_BATCH];
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave & 3, wn = wave >> 2;
+  const int nt = blockIdx.x, split = blockIdx.y, mt = blockIdx.z;
+  const int KB = g.K >> 5;
+  const int lo = (int)((long long)KB * split / g.splits);
+  const int hi = (int)((long long)KB * (split + 1) / g.splits);
+  const int nst = (hi - lo + WIDE_KS - 1) / WIDE_KS;
+  const int NBtot = g.N >> 4;                  // 16-column blocks of W (SwiGLU: of gate and of up)
+  const int MBtot = g.Mp >> 4;
+  const int NT = EPI == EPI_SWIGLU ? (NBtot + NBH - 1) / NBH : (NBtot + NB - 1) / NB;
+
+  // Operand loads are range-checked buffer loads: k-blocks past the split's
+  // range get an offset past the buffer and read zeros, so the LDS stores
+  // are plain copies (no selects on loaded registers, which the compiler
+  // would hoist to where they wait on the youngest loads).
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u16*>(g.A), (short)0, MBtot * KB * 1024, MV_BUF_DWORD3);
+  const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u16*>(g.W), (short)0, KB * NBtot * 1024, MV_BUF_DWORD3);
+  const __amdgpu_buffer_rsrc_t rW2 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u16*>(EPI == EPI_SWIGLU ? g.W2 : g.W), (short)0, KB * NBtot * 1024, MV_BUF_DWORD3);
+  constexpr uint32_t OOB = 0x80000000u;        // past every operand (each < 2 GiB)
+  // the weight block of tile block j (clamped: blocks past the matrix load
+  // valid memory and are never stored)
+  auto wblk = [&](int j) {
+    const int blk = EPI == EPI_SWIGLU ? nt * NBH + (j < NBH ? j : j - NBH) : nt * NB + j;
+    return min(blk, NBtot - 1);
+  };
+
+  // the wave's i-th weight piece of a stage: 8i + wave, or (past the WP
+  // pieces) its own previous piece again, loaded and stored twice with the
+  // same data, so that every load has a slot and no branch
+  auto wpiece = [&](int i) { return i * 8 + wave < WP ? i * 8 + wave : (i - 1) * 8 + wave; };
+  // stage st's loads: activation piece p = 8i + wave is (kl = p / 16, row
+  // block p % 16), weight piece p = 8i + wave is (kl = p / NB, block p % NB)
+  auto issue = [&](bf16x8 (&ra)[AL], bf16x8 (&rw)[WL], int st) {
+    const int kb0 = lo + st * WIDE_KS;
+#pragma unroll
+    for (int i = 0; i < AL; ++i) {
+      const int pc = i * 8 + wave;
+      const int k = kb0 + pc / 16;
+      const int rbg = min(mt * 16 + pc % 16, MBtot - 1);
+      const uint32_t off = k < hi ? (uint32_t)((rbg * KB + k) * 64 + lane) * 16u : OOB;
+      ra[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rA, off, 0, 0));
+    }
+#pragma unroll
+    for (int i = 0; i < WL; ++i) {
+      const int pc = wpiece(i);
+      const int k = kb0 + pc / NB, j = pc % NB;
+      const uint32_t off = k < hi ? (uint32_t)((k * NBtot + wblk(j)) * 64 + lane) * 16u : OOB;
+      rw[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                             EPI == EPI_SWIGLU && j >= NBH ? rW2 : rW, off, 0, 0));
+    }
+  };
+  // ... and their LDS stores
+  auto stash = [&](const bf16x8 (&ra)[AL], const bf16x8 (&rw)[WL], int buf) {
+    bf16x8* sb = smem + buf * OPB;
+#pragma unroll
+    for (int i = 0; i < AL; ++i) sb[(i * 8 + wave) * 64 + lane] = ra[i];
+#pragma unroll
+    for (int i = 0; i < WL; ++i) sb[(AP + wpiece(i)) * 64 + lane] = rw[i];
+  };
+
+  f32x4 acc[4][NBH];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NBH; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // one k-block's fragments of this wave from stage buffer buf, and its MFMAs
+  auto read_frags = [&](int buf, int kl, bf16x8 (&af)[4], bf16x8 (&wf)[NBH]) {
+    const bf16x8* sb = smem + buf * OPB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[i] = sb[(kl * 16 + 4 * wm + i) * 64 + lane];
+#pragma unroll
+    for (int j = 0; j < NBH; ++j) wf[j] = sb[(AP + kl * NB + NBH * wn + j) * 64 + lane];
+  };
+  auto mfma_kb = [&](const bf16x8 (&af)[4], const bf16x8 (&wf)[NBH]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NBH; ++j) acc[i][j] = mfma16x16x32(af[i], wf[j], acc[i][j]);
+  };
+
+  // norm factors: two threads a row, up to WIDE_SSQ f32x4 of partial sums
+  // each, requested before the weight prefetch so that their wait does not
+  // drain it (longer rows of partials: summed serially below)
+  constexpr int WIDE_SSQ = 8;
+  const bool ss_fast = g.ss != nullptr && g.ss_tiles <= 2 * 4 * WIDE_SSQ;
+  f32x4 ssv[WIDE_SSQ];
+  {
+    const int r = threadIdx.x >> 1, hf = threadIdx.x & 1;
+    const int m = min(mt * WIDE_TR + r, g.M - 1);
+    const f32x4* p4 = reinterpret_cast<const f32x4*>(g.ss + (size_t)m * g.ss_ld);
+#pragma unroll
+    for (int u = 0; u < WIDE_SSQ; ++u) {
+      const int t = 2 * u + hf;
+      ssv[u] = ss_fast && 4 * t < g.ss_tiles ? p4[t] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  int nraw = 0;
+  if (EPI == EPI_QKV && threadIdx.x < g.qkv.B) nraw = g.qkv.n_prefix[threadIdx.x];
+  // WIDE_P stages of loads in flight; fewer where the registers do not hold
+  // them (SwiGLU: 3 with 4-block waves, 2 with 5-block waves)
+  constexpr int P = EPI == EPI_SWIGLU ? 2 : WIDE_P;
+  bf16x8 ra0[AL], rw0[WL], ra1[AL], rw1[WL], ra2[P >= 3 ? AL : 1], rw2[P >= 3 ? WL : 1];
+  issue(ra0, rw0, 0);
+  issue(ra1, rw1, 1);
+  if constexpr (P >= 3) issue(ra2, rw2, 2);
+  if (ss_fast) {
+    const int r = threadIdx.x >> 1, hf = threadIdx.x & 1;
+    float sm = 0.f;
+#pragma unroll
+    for (int u = 0; u < WIDE_SSQ; ++u) {
+      const int t = 2 * u + hf;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm += 4 * t + e < g.ss_tiles ? ssv[u][e] : 0.f;
+    }
+    sm += __shfl_xor(sm, 1, 64);
+    if (hf == 0) rs_s[r] = mt * WIDE_TR + r < g.M ? 1.0f / sqrtf(sm / (float)g.K + 1e-5f) : 1.f;
+  } else if (g.ss) {
+    for (int r = threadIdx.x; r < WIDE_TR; r += 512) {
+      const int m = mt * WIDE_TR + r;
+      float sm = 0.f;
+      if (m < g.M) {
+        const float* row = g.ss + (size_t)m * g.ss_ld;
+        for (int e = 0; e < g.ss_tiles; ++e) sm += row[e];
+      }
+      rs_s[r] = m < g.M ? 1.0f / sqrtf(sm / (float)g.K + 1e-5f) : 1.f;
+    }
+  }
+  if (EPI == EPI_QKV && threadIdx.x < g.qkv.B)
+    s_slot0[threadIdx.x] = min(max(nraw, 0), g.qkv.cap - g.qkv.T);
+  stash(ra0, rw0, 0);
+  issue(ra0, rw0, P);
+  stash(ra1, rw1, 1);
+  issue(ra1, rw1, P + 1);
+  __syncthreads();
+  // Three stage buffers in LDS.  Step s computes stage s (buffer s % 3):
+  // its second k-block's fragments are read while the first k-block's
+  // MFMAs run, stage s + 2 goes from its register set (st % P) into buffer
+  // (s + 2) % 3 -- last read in step s - 1 -- and the set is refilled with
+  // stage s + 2 + P; then the first k-block of stage s + 1 (buffer (s + 1)
+  // % 3, complete since the previous barrier) is read before the barrier,
+  // so each step's MFMAs start on fragments already in registers.  The step
+  // count is padded to a multiple of P (stages past the range compute on
+  // zeros) and every step issues its loads (past the range: offsets past the
+  // buffers), so the loop has no branches and each stage waits only on its
+  // own loads.
+  // (5-block waves have registers for one fragment set: their second
+  // k-block is read after the first one's MFMAs)
+  constexpr bool DBF = NBH == 4;
+  bf16x8 f0a[4], f0w[NBH], f1a[DBF ? 4 : 1], f1w[DBF ? NBH : 1];
+  read_frags(0, 0, f0a, f0w);
+  const int nst_pad = (nst + P - 1) / P * P;
+  int buf = 0;                                   // s % 3
+#define MV_WIDE_STEP(S_, RA, RW)                                             \
+  {                                                                          \
+    const int b2 = buf == 0 ? 2 : buf - 1, b1 = buf == 2 ? 0 : buf + 1;      \
+    if constexpr (DBF) {                                                     \
+      read_frags(buf, 1, f1a, f1w);                                          \
+      mfma_kb(f0a, f0w);                                                     \
+      stash(RA, RW, b2);                                                     \
+      issue(RA, RW, (S_) + 2 + P);                                           \
+      mfma_kb(f1a, f1w);                                                     \
+    } else {                                                                 \
+      mfma_kb(f0a, f0w);                                                     \
+      read_frags(buf, 1, f0a, f0w);                                          \
+      stash(RA, RW, b2);                                                     \
+      issue(RA, RW, (S_) + 2 + P);                                           \
+      mfma_kb(f0a, f0w);                                                     \
+    }                                                                        \
+    read_frags(b1, 0, f0a, f0w);                                             \
+    buf = b1;                                                                \
+    __syncthreads();                                                         \
+  }
+  if constexpr (P == 3) {
+    for (int s0 = 0; s0 < nst_pad; s0 += 3) {
+      MV_WIDE_STEP(s0, ra2, rw2)
+      MV_WIDE_STEP(s0 + 1, ra0, rw0)
+      MV_WIDE_STEP(s0 + 2, ra1, rw1)
+    }
+  } else {
+    for (int s0 = 0; s0 < nst_pad; s0 += 2) {
+      MV_WIDE_STEP(s0, ra0, rw0)
+      MV_WIDE_STEP(s0 + 1, ra1, rw1)
+    }
+  }
+#undef MV_WIDE_STEP
+
+  // ---- split-K: the last workgroup of the tile sums the splits in order
+  if (g.splits > 1) {
+    constexpr int WQ = 4 * NBH;                // f32x4 items per lane of one wave
+    const int tile = mt * NT + nt;
+    const int per_split = 8 * WQ * 256 * 4;    // bytes of one split's tile
+    const __amdgpu_buffer_rsrc_t part = __builtin_amdgcn_make_buffer_rsrc(
+        g.partial + (size_t)tile * g.splits * (per_split / 4), (short)0, g.splits * per_split,
+        MV_BUF_DWORD3);
+    const int lane_off = (wave * WQ * 256 + lane * 4) * 4;
+#pragma unroll
+    for (int q = 0; q < WQ; ++q)
+      __builtin_amdgcn_raw_buffer_store_b128(acc[q / NBH][q % NBH], part,
+                                             split * per_split + lane_off + q * 1024, 0, MV_CPOL_SYS);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int prev = __hip_atomic_fetch_add(g.counters + tile, 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+      s_last = prev == g.splits - 1;
+    }
+    __syncthreads();
+    if (!s_last) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NBH; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < g.splits; ++sp) {
+      f32x4 v[WQ];
+#pragma unroll
+      for (int q = 0; q < WQ; ++q)
+        v[q] = __builtin_amdgcn_raw_buffer_load_b128(part, sp * per_split + lane_off + q * 1024, 0,
+                                                     MV_CPOL_SYS);
+#pragma unroll
+      for (int q = 0; q < WQ; ++q) acc[q / NBH][q % NBH] += v[q];
+    }
+    if (threadIdx.x == 0)
+      __hip_atomic_store(g.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // ---- epilogues: lane holds tile rows 64*wm + 16*i + 4*(lane/16) + r,
+  // tile column 16*(NBH*wn + j) + lane%16
+  if (g.ss) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float f = rs_s[64 * wm + 16 * i + 4 * (lane >> 4) + r];
+#pragma unroll
+        for (int j = 0; j < NBH; ++j) acc[i][j][r] *= f;
+      }
+  }
+  const int col = lane & 15;
+  const int mr0 = mt * WIDE_TR;
+  if constexpr (EPI == EPI_SWIGLU) {
+    // up waves park their accumulators; gate waves form h = SiLU(gate) * up
+    // as bf16 [row][feature]; then 16-byte pieces (8 features of one row)
+    constexpr int FT = S::FT, LDH = S::LDH;
+    float* park = reinterpret_cast<float*>(smem);                       // [wm][i][j][r][lane]
+    u16* hs = reinterpret_cast<u16*>(park + WIDE_TR * FT);              // [row][LDH]
+    if (wn == 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NBH; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) park[(((wm * 4 + i) * NBH + j) * 4 + r) * 64 + lane] = acc[i][j][r];
+    }
+    __syncthreads();
+    if (wn == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NBH; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float u = park[(((wm * 4 + i) * NBH + j) * 4 + r) * 64 + lane];
+            hs[(64 * wm + 16 * i + 4 * (lane >> 4) + r) * LDH + 16 * j + col] =
+                f32_to_bf16(silu_f(acc[i][j][r]) * u);
+          }
+    }
+    __syncthreads();
+    constexpr int PPR = FT / 8;                // pieces per row
+    for (int p = threadIdx.x; p < WIDE_TR * PPR; p += 512) {
+      const int rl = p / PPR, f = nt * FT + 8 * (p % PPR), m = mr0 + rl;
+      if (m < g.M && f < g.N)
+        *reinterpret_cast<uint4*>(g.out_bf16 + packed_index(m, f, g.N)) =
+            *reinterpret_cast<const uint4*>(hs + rl * LDH + 8 * (p % PPR));
+    }
+    return;
+  } else {
+    float* stg = reinterpret_cast<float*>(smem);   // [row][LDF] fp32 tile
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NBH; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          stg[(64 * wm + 16 * i + 4 * (lane >> 4) + r) * LDF + 16 * (NBH * wn + j) + col] = acc[i][j][r];
+    __syncthreads();
+    const int tc0 = nt * TC;
+    if constexpr (EPI == EPI_STORE) {
+      constexpr int PPR = TC / 4;              // float4 pieces per row
+      bool bad = false;
+      for (int p = threadIdx.x; p < WIDE_TR * PPR; p += 512) {
+        const int rl = p / PPR, c = tc0 + 4 * (p % PPR), m = mr0 + rl;
+        if (m < g.M && c < g.N) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(stg + rl * LDF + 4 * (p % PPR));
+          *reinterpret_cast<f32x4*>(g.out_f32 + (size_t)m * g.N + c) = v;
+          bad |= !(__builtin_isfinite(v[0]) && __builtin_isfinite(v[1]) && __builtin_isfinite(v[2]) &&
+                   __builtin_isfinite(v[3]));
+        }
+      }
+      if (g.status && __ballot(bad) != 0ull && lane == 0) atomicOr(g.status, MV_STATUS_NONFINITE);
+      if (g.amax_key) {
+        // two threads a row, each over half the tile's columns; ties go to
+        // the lower column, NaNs never win
+        const int rl = threadIdx.x >> 1, hf = threadIdx.x & 1, m = mr0 + rl;
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+        for (int c = hf * (TC / 2); c < (hf + 1) * (TC / 2); ++c) {
+          if (tc0 + c >= g.N) break;
+          const float v = stg[rl * LDF + c];
+          if (v > bv) { bv = v; bi = tc0 + c; }
+        }
+        const float ov = __shfl_xor(bv, 1, 64);
+        const int oi = __shfl_xor(bi, 1, 64);
+        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+        if (hf == 0 && m < g.M) {
+          const unsigned long long key = argmax_key(bv, bi);
+          if (key > __hip_atomic_load(g.amax_key + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            __hip_atomic_fetch_max(g.amax_key + m, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    } else if constexpr (EPI == EPI_ADD) {
+      // 16 adjacent lanes own the 16 pieces of 8 columns of one row: x += y,
+      // the next norm's operand, and the row's sum of squares over the tile
+      static_assert(TC == 128, "a row's pieces fill one DPP row");
+      const bool nxt = g.next_gain != nullptr && g.xn_out != nullptr;
+      const bool ssq = g.next_gain != nullptr && g.ss_out != nullptr;
+      for (int p = threadIdx.x; p < WIDE_TR * 16; p += 512) {
+        const int rl = p >> 4, c = tc0 + 8 * (p & 15), m = mr0 + rl;
+        const bool st = m < g.M && c < g.N;
+        const f32x4* sp = reinterpret_cast<const f32x4*>(stg + rl * LDF + 8 * (p & 15));
+        f32x4 x0 = sp[0], x1 = sp[1];
+        float sq = 0.f;
+        if (st) {
+          f32x4* xp = reinterpret_cast<f32x4*>(g.out_f32 + (size_t)m * g.N + c);
+          x0 += xp[0];
+          x1 += xp[1];
+          xp[0] = x0;
+          xp[1] = x1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sq += x0[e] * x0[e] + x1[e] * x1[e];
+          if (nxt) {
+            const uint4 gr = *reinterpret_cast<const uint4*>(g.next_gain + c);
+            const uint32_t gw[4] = {gr.x, gr.y, gr.z, gr.w};
+            uint32_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float a = (e < 2 ? x0 : x1)[(2 * e) & 3], b = (e < 2 ? x0 : x1)[(2 * e + 1) & 3];
+              o[e] = (uint32_t)f32_to_bf16(a * bf16_to_f32((u16)(gw[e] & 0xffff))) |
+                     ((uint32_t)f32_to_bf16(b * bf16_to_f32((u16)(gw[e] >> 16))) << 16);
+            }
+            *reinterpret_cast<uint4*>(g.xn_out + packed_index(m, c, g.N)) = uint4{o[0], o[1], o[2], o[3]};
+          }
+        }
+        if (ssq) {
+          sq += MV_DPP(sq, 0xB1);
+          sq += MV_DPP(sq, 0x4E);
+          sq += MV_DPP(sq, 0x141);
+          sq += MV_DPP(sq, 0x140);
+          if ((p & 15) == 0 && m < g.M) g.ss_out[(size_t)m * g.ss_ld + nt] = sq;
+        }
+      }
+    } else if constexpr (EPI == EPI_QKV) {
+      const QkvArgs& q = g.qkv;
+      const int half = q.hd >> 1;
+      const bool wide = q.hd >= 32;
+      // RoPE in place on the q and k columns: packed column pairs (c, c + 16)
+      // of each 32-group (heads of 32+ dims: dims i and i + hd/2 of one head)
+      // or (c, c + 8) of each 16-block (16-dim heads)
+      const int pw = wide ? 16 : 8;
+      for (int it = threadIdx.x; it < WIDE_TR * (TC / 2); it += 512) {
+        const int rl = it / (TC / 2), pr = it % (TC / 2);
+        const int c = (pr / pw) * 2 * pw + pr % pw;   // first column of the pair
+        const int pcol = tc0 + c, m = mr0 + rl;
+        if (pcol >= 2 * q.d || m >= g.M) continue;
+        const int f = wide ? qkv_feature(pcol, q.d, q.hd) : pcol;
+        const int ci = (f % q.d) % q.hd % half;
+        const float2 cs = q.rope[(size_t)m * half + ci];
+        float* a = stg + rl * LDF + c;
+        const float y0 = a[0], y1 = a[pw];
+        a[0] = y0 * cs.x - y1 * cs.y;
+        a[pw] = y1 * cs.x + y0 * cs.y;
+      }
+      __syncthreads();
+      const int hs_ = __ffs(q.hd) - 1;           // hd is a power of two
+      // q and K: 16-byte pieces of 8 consecutive features (8 consecutive
+      // packed columns of a 16-block are 8 consecutive dims of one head)
+      if (tc0 < 2 * q.d) {
+        for (int u = threadIdx.x; u < WIDE_TR * (TC / 8); u += 512) {
+          const int rl = u / (TC / 8), cu = u % (TC / 8);
+          const int pcol = tc0 + cu * 8, m = mr0 + rl;
+          if (pcol >= 2 * q.d || pcol >= g.N || m >= g.M) continue;
+          const int f = wide ? qkv_feature(pcol, q.d, q.hd) : pcol;
+          const f32x4* sp = reinterpret_cast<const f32x4*>(stg + rl * LDF + cu * 8);
+          const f32x4 v0 = sp[0], v1 = sp[1];
+          uint4 o;
+          o.x = (uint32_t)f32_to_bf16(v0[0]) | ((uint32_t)f32_to_bf16(v0[1]) << 16);
+          o.y = (uint32_t)f32_to_bf16(v0[2]) | ((uint32_t)f32_to_bf16(v0[3]) << 16);
+          o.z = (uint32_t)f32_to_bf16(v1[0]) | ((uint32_t)f32_to_bf16(v1[1]) << 16);
+          o.w = (uint32_t)f32_to_bf16(v1[2]) | ((uint32_t)f32_to_bf16(v1[3]) << 16);
+          if (f < q.d) {
+            *reinterpret_cast<uint4*>(q.q + (size_t)m * q.d + f) = o;
+          } else {
+            const int b = min(m / q.T, MV_MAX_BATCH - 1), node = m - b * q.T;
+            const int cc = f - q.d, h = cc >> hs_, i = cc & (q.hd - 1);
+            *reinterpret_cast<uint4*>(q.kcache + ((size_t)b * q.H + h) * q.cap * q.hd +
+                                      kv_k_off(s_slot0[b] + node, i, q.hd)) = o;
+          }
+        }
+      }
+      // V: each thread one (8-slot group, dim) of a sequence's slots in this
+      // tile: a whole group is one 16-byte store, a partial one (first or
+      // last of a sequence) element by element
+      if (tc0 + TC > 2 * q.d) {
+        const int m_hi = min(mr0 + WIDE_TR, g.M);
+        const int b_lo = mr0 / q.T;
+        for (int e = 0; e < MV_MAX_BATCH; ++e) {
+          const int b = b_lo + e;
+          if (b >= q.B) break;
+          const int lo_m = max(mr0, b * q.T), hi_m = min(m_hi, (b + 1) * q.T);
+          if (lo_m >= hi_m) continue;
+          const int s0 = s_slot0[b] + (lo_m - b * q.T), ns = hi_m - lo_m;
+          const int gf = s0 >> 3, gc = ((s0 + ns - 1) >> 3) - gf + 1;
+          for (int u = threadIdx.x; u < gc * TC; u += 512) {
+            const int j = u % TC, pcol = tc0 + j;
+            if (pcol < 2 * q.d || pcol >= g.N) continue;
+            const int gs = (gf + u / TC) * 8;
+            const int cc = pcol - 2 * q.d, h = cc >> hs_, i = cc & (q.hd - 1);
+            u16* vb = q.vcache + ((size_t)b * q.H + h) * q.cap * q.hd;
+            const int lo_s = max(gs, s0), hi_s = min(gs + 8, s0 + ns);
+            const float* src = stg + (lo_m - mr0 + lo_s - s0) * LDF + j;
+            if (lo_s == gs && hi_s == gs + 8) {
+              uint32_t w4[4];
+#pragma unroll
+              for (int t = 0; t < 4; ++t)
+                w4[t] = (uint32_t)f32_to_bf16(src[2 * t * LDF]) |
+                        ((uint32_t)f32_to_bf16(src[(2 * t + 1) * LDF]) << 16);
+              *reinterpret_cast<uint4*>(vb + kv_v_off(gs, i, q.hd)) = uint4{w4[0], w4[1], w4[2], w4[3]};
+            } else {
+              for (int sl = lo_s; sl < hi_s; ++sl)
+                vb[kv_v_off(sl, i, q.hd)] = f32_to_bf16(src[(sl - lo_s) * LDF]);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int NBH>
+static hipError_t launch_wide_nbh(const GemmArgs& g, dim3 grid, hipStream_t s) {
+  switch (g.epi) {
+    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_wide_kernel<NBH, EPI_SWIGLU>), grid, dim3(512), 0, s, g); break;
+    case EPI_STORE:
+      if (NBH != 4) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((gemm_wide_kernel<4, EPI_STORE>), grid, dim3(512), 0, s, g);
+      break;
+    case EPI_ADD:
+      if (NBH != 4) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((gemm_wide_kernel<4, EPI_ADD>), grid, dim3(512), 0, s, g);
+      break;
+    case EPI_QKV:
+      if (NBH != 4) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((gemm_wide_kernel<4, EPI_QKV>), grid, dim3(512), 0, s, g);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+int gemm_wide_ntiles(int epi, int N, int nbh) {
+  const int blocks = N / 16;
+  const int per_tile = epi == EPI_SWIGLU ? nbh : 2 * nbh;
+  return (blocks + per_tile - 1) / per_tile;
+}
+
 int gemm_ntiles(int epi, int N, int w, int nbw) {
   const int blocks = N / 16;
   const int per_tile = epi == EPI_SWIGLU ? (nbw == 2 ? w : w / 2) : w * nbw;
@@ -906,6 +1433,12 @@ static hipError_t launch_w(const GemmArgs& g, int MB, dim3 grid, hipStream_t s) 
 }
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
+  if (g.wide) {
+    const dim3 grid(gemm_wide_ntiles(g.epi, g.N, g.wide), g.splits, (g.Mp + WIDE_TR - 1) / WIDE_TR);
+    if (g.wide == 4) return launch_wide_nbh<4>(g, grid, s);
+    if (g.wide == 5 && g.epi == EPI_SWIGLU) return launch_wide_nbh<5>(g, grid, s);
+    return hipErrorInvalidValue;
+  }
   const int MB = gemm_mb(g.Mp);
   const int mtiles = (g.Mp / 16 + MB - 1) / MB;
   const int ntiles = gemm_ntiles(g.epi, g.N, g.w, g.nbw);
