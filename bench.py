@@ -129,6 +129,39 @@ def pmc_summary(dirs, gate_up_name="gemm_kernel<4, 4, 2, 2>"):
     return out
 
 
+ATTN_KINDS = (("per query block", "tree_attention_qb_kernel"), ("split keys", "tree_attention_kernel<"),
+              ("split merge", "attention_merge_kernel"))
+
+
+def attn_summary(dirs):
+    """Summarise rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes for the
+    tree-attention kernels (KiB per dispatch), scaled by what the same
+    counter reads for the calibration copy."""
+    import csv
+    import glob
+    import statistics
+    per = {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                name, ctr = r["Kernel_Name"], r["Counter_Name"]
+                kind = "copy" if "neg" in name else next((lab for lab, k in ATTN_KINDS if k in name), None)
+                if kind:
+                    per.setdefault((kind, ctr), []).append(float(r["Counter_Value"]))
+    out = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        cp = per.get(("copy", ctr))
+        if not cp:
+            continue
+        scale = (COPY_BYTES / 1024) / statistics.median(cp)
+        for lab, _ in ATTN_KINDS:
+            v = per.get((lab, ctr))
+            if v:
+                out[(lab, ctr)] = {"kib_mean": statistics.mean(v), "dispatches": len(v),
+                                   "bytes": statistics.mean(v) * 1024 * scale, "scale": scale}
+    return out
+
+
 MFMA_FILE = os.path.join(ROOT, "profiles", "gemm_mfma_llama7b_T64.md")
 GEMM_KINDS = (("QKV", "gemm_kernel<4, 4, 2, 3>"), ("O / down", "gemm_kernel<4, 4, 1, 1>"),
               ("gate/up", "gemm_kernel<4, 4, 2, 2>"), ("LM head", "gemm_kernel<4, 8, 1, 0>"))
@@ -319,6 +352,9 @@ def main() -> int:
                     help="summarise rocprofv3 --pmc FETCH_SIZE/WRITE_SIZE output dirs and exit")
     ap.add_argument("--mfma-summary", nargs="+", metavar="DIR",
                     help="summarise rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 output dirs and exit")
+    ap.add_argument("--attn-summary", nargs="+", metavar="DIR",
+                    help="summarise rocprofv3 --pmc FETCH_SIZE/WRITE_SIZE output dirs for the "
+                         "tree-attention kernels of --workload and exit")
     args = ap.parse_args()
     if args.pmc_summary:
         from workloads import configs
@@ -335,6 +371,22 @@ def main() -> int:
             print(f"traffic_bytes_per_launch = {int(round(tot))}")
             print(f"traffic_over_algorithmic = {tot / algo:.4f}")
             print(f"source_sha256 = {gemm_source_hash()}")
+        return 0
+    if args.attn_summary:
+        from workloads import configs, synth
+        w = configs.get(args.workload) if args.workload else configs.HEADLINE
+        D = w.dims
+        n = sum(w.prefix) / 2
+        T = len(synth.tree_paths(w, 0)) + 1
+        # algorithmic bytes of one launch (one layer): the prefix K and V
+        # once, the tree's K and V, q read and the output written, bf16
+        algo = w.batch * (2 * n * D.d * 2 + 2 * T * D.d * 2 + 2 * T * D.d * 2)
+        res = attn_summary(args.attn_summary)
+        print(f"workload {w.name}: algorithmic bytes per launch at the initial prefix "
+              f"{algo / 1e6:.2f} MB (n = {n:.0f}, T = {T}, batch {w.batch})")
+        for (lab, ctr), v in res.items():
+            print(f"{lab} {ctr}: {v['kib_mean']:.0f} KiB/dispatch (scale {v['scale']:.4f}) over "
+                  f"{v['dispatches']} dispatches -> {v['bytes'] / 1e6:.2f} MB")
         return 0
     if args.mfma_summary:
         from workloads import configs

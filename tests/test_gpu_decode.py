@@ -186,22 +186,22 @@ def stages(layers: int) -> int:
     return 2 * layers + 1
 
 
-def _full_dims_session(wname, L, steps, cache_weights=True):
-    """A step context at a 7B workload's dims with L decoder layers, holding
-    the state a prefill of the workload's prompt length leaves: seeded bf16
-    prefix K/V, a post-norm hidden state of unit scale and a root token
-    (declared to the context with resume).  Returns the pieces both sides
-    need."""
+def _full_dims_session(wname, L, steps, cache_weights=True, dims=None):
+    """A step context at a workload's dims (or `dims`) with L decoder layers,
+    holding the state a prefill of the workload's prompt length leaves:
+    seeded bf16 prefix K/V, a post-norm hidden state of unit scale and a root
+    token (declared to the context with resume).  Returns the pieces both
+    sides need."""
     w0 = configs.get(wname)
-    D = configs.Dims(L=L, d=w0.dims.d, H=w0.dims.H, hd=w0.dims.hd, F=w0.dims.F,
-                     V=w0.dims.V, K=w0.dims.K)
+    b = dims or w0.dims
+    D = configs.Dims(L=L, d=b.d, H=b.H, hd=b.hd, F=b.F, V=b.V, K=b.K)
     w = w0.with_(dims=D)
     Wt = synth.TorchDrawnWeights(w, cache=cache_weights)
     s = synth.tree_topk(w)
     paths = synth.tree_paths(w, 0)
     t = otree.compile_tree(paths)
     trees = rt.DeviceTrees([paths], s)
-    assert trees.T == 64 and t.max_depth == 4
+    assert trees.T == t.T
     n0 = synth.prefix_lengths(w)[0]
     cap = ((n0 + t.T + steps * (t.max_depth + 1) + 63) // 64) * 64
     dw = rt.DeviceWeights(D, Wt.get)
@@ -326,6 +326,23 @@ def test_full_dims_step_two_layers_teacher_forced(wname):
     print(f"full-dims step: {wname} with L=2", flush=True)
     c = _full_dims_session(wname, 2, 2)
     _teacher_forced_steps(c, 2)
+    c["sess"].close()
+
+
+@pytest.mark.timeout(900)
+def test_full_dims_step_wide_tiles_at_33b_width():
+    """One graph step with 256 tree rows at the 33B width (d = 6656, 52 x 128
+    heads, FFN 17920, V = 32000; the 13B workload's 256-node Cartesian tree,
+    5 Medusa heads, prefix 1024) and 1 decoder layer: every GEMM of the step
+    runs in the wide-tile kernel (QKV with RoPE and the cache write, O and
+    down with split K, gate/up in 80-feature tiles, the LM head with the
+    fused row argmax of greedy acceptance), against the oracle as above."""
+    print("full-dims step: 33B width, 256-node tree, L=1", flush=True)
+    d33 = configs.LLAMA33B_B4.dims
+    dims = configs.Dims(L=1, d=d33.d, H=d33.H, hd=d33.hd, F=d33.F, V=d33.V,
+                        K=configs.LLAMA13B_T256.dims.K)
+    c = _full_dims_session(configs.LLAMA13B_T256.name, 1, 1, dims=dims)
+    _teacher_forced_steps(c, 1)
     c["sess"].close()
 
 

@@ -115,17 +115,23 @@ static GemmCfg gemm_cfg(const mv_dims& D, int kind, int Mp) {
   c.wide = 0;
   // More than 128 rows: the wide-tile kernel (256 rows x 128 columns, or x
   // 160 for gate/up when 64-feature tiles would not fit the compute units in
-  // one round), whose range-checked operand loads need each operand below 2 GiB
+  // one round), whose range-checked operand loads need each operand below
+  // 2 GiB.  It takes the launches where it measured faster at 256 rows: K of
+  // 6144 and more with fewer than 8 K splits (every 33B GEMM, 13B down:
+  // 90 against 137 us at 33B down), and gate/up from K = 5120 (13B: 95
+  // against 104 us); the 16-row-block tiles keep the 7B shapes (prefill 14.7
+  // against 15.7 ms) and 13B QKV and O (67 against 71 us, 37.5 against 40).
   if (c.MB == 16 && (size_t)c.N * c.K * 2 < (1ull << 31) && (size_t)Mp * c.K * 2 < (1ull << 31)) {
-    c.wide = 4;
-    if (c.epi == mvk::EPI_SWIGLU && mvk::gemm_wide_ntiles(c.epi, c.N, 4) * c.mtiles > 256) c.wide = 5;
-    c.w = 8;
-    c.nbw = 1;
-    c.ntiles = mvk::gemm_wide_ntiles(c.epi, c.N, c.wide);
+    GemmCfg w = c;
+    w.wide = 4;
+    if (w.epi == mvk::EPI_SWIGLU && mvk::gemm_wide_ntiles(w.epi, w.N, 4) * w.mtiles > 256) w.wide = 5;
+    w.w = 8;
+    w.nbw = 1;
+    w.ntiles = mvk::gemm_wide_ntiles(w.epi, w.N, w.wide);
     // K splits while the tiles leave compute units idle, each split at least
     // four 2-k-block stages
-    c.splits = std::max(1, std::min(256 / (c.ntiles * c.mtiles), KB / 8));
-    return c;
+    w.splits = std::max(1, std::min(256 / (w.ntiles * w.mtiles), KB / 8));
+    if ((c.K >= 6144 && w.splits < 8) || (c.epi == mvk::EPI_SWIGLU && c.K >= 5120)) return w;
   }
   c.ntiles = mvk::gemm_ntiles(c.epi, c.N, c.w, c.nbw);
   const int KC = mvk::gemm_kc(c.MB);
