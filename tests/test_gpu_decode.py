@@ -235,7 +235,8 @@ def _teacher_forced_steps(c, steps, exact_head=True):
     Per-stage checks with identical inputs hold TOL: the head logits (from
     the GPU's h_last) and the LM head (from the GPU's final residual rows).
     The whole-forward drift of the tree logits, h_last and the K/V rows is
-    returned per step and held to the stage bound TOL * (2l + 1)."""
+    returned per step and held to the stage bound TOL * (2l + 1), for the
+    logits times max(1, their rms)."""
     w, D, Wt, s, t, sess, okv = c["w"], c["D"], c["Wt"], c["s"], c["t"], c["sess"], c["okv"]
     h, t0, n, u = c["h"], c["t0"], c["n0"], c["u"]
     n0 = n
@@ -265,7 +266,11 @@ def _teacher_forced_steps(c, steps, exact_head=True):
               f"{lm_err:.2e}, tree logits drift max {lerr:.4f} rms "
               f"{np.sqrt(np.mean((gl - logits) ** 2)):.5f} (logits rms "
               f"{np.sqrt(np.mean(logits ** 2)):.3f})", flush=True)
-        assert lerr <= TOL * stages(D.L), (step, lerr)
+        # the drift bound TOL per stage is for unit-scale values: bf16 rounding
+        # is relative, so the logits' bound scales with their rms (1.28 at
+        # the 7B width, 1.63 at 33B with N(0, 0.02) weights)
+        lscale = max(1.0, float(np.sqrt(np.mean(logits ** 2))))
+        assert lerr <= TOL * stages(D.L) * lscale, (step, lerr, lscale)
         if w.accept == "typical":
             res = oa.typical_accept(t, tok, gl, w.temperature, w.eps, w.delta)
         elif reject:
