@@ -201,6 +201,9 @@ def _layer_case(D, B, ns, paths_per_seq, topk, seed, gain_std=0.1):
     ("llama13b_T256", 1, [1024]),
     # the 33B batch: four sequences, their own sparse trees and ragged prefixes
     ("llama33b_B4", 4, None),
+    # four 256-node trees at width 6144: M = 1024, every GEMM in wide tiles
+    # with four 256-row tiles (as a batch-4 prefill chunk runs them)
+    pytest.param("wide_b4", 4, [64, 100, 7, 300], marks=pytest.mark.timeout(600)),
 ])
 def test_decoder_layer_matches_oracle(name, B, ns):
     wl = {"llama7b": configs.LLAMA7B_T64, "llama13b_T256": configs.LLAMA13B_T256,
@@ -211,7 +214,8 @@ def test_decoder_layer_matches_oracle(name, B, ns):
     D = {"tiny": configs.TINY.dims, "tiny_b4": configs.TINY.dims,
          "mid": configs.Dims(L=1, d=256, H=2, hd=128, F=512, V=512, K=3),
          "mid_f480": configs.Dims(L=1, d=256, H=2, hd=128, F=480, V=512, K=3),
-         "wide_f": configs.Dims(L=1, d=128, H=1, hd=128, F=16416, V=512, K=3)}.get(name)
+         "wide_f": configs.Dims(L=1, d=128, H=1, hd=128, F=16416, V=512, K=3),
+         "wide_b4": configs.Dims(L=1, d=6144, H=48, hd=128, F=6144, V=512, K=3)}.get(name)
     if wl is not None:
         D = wl.dims
     # one layer; a small vocabulary (the layer reads no vocab-sized weight)
@@ -221,6 +225,8 @@ def test_decoder_layer_matches_oracle(name, B, ns):
         paths = [synth.cartesian_paths((2, 2, 2))] * B
     elif wl is not None:
         paths = [synth.tree_paths(wl, b) for b in range(B)]
+    elif name == "wide_b4":
+        paths = random_trees(rng, B, 255, 4, 6)
     else:
         paths = random_trees(rng, B, 63, 4, 6)
     Wt, trees, ocaches, kv, x, cap = _layer_case(D, B, ns, paths, 10, 2024 + B)
