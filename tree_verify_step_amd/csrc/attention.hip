@@ -48,6 +48,30 @@
 
 namespace mvk {
 
+// Visibility of the 64 key slots s0 .. s0+63 for one query: bit j is set iff
+// slot s0 + j lies below hi = n + T and is either a prefix slot (below n) or
+// the tree slot n + a of an ancestor a of the query (am: the query's
+// ancestor words, bit a of word a / 64, zero past the tree).  The tree part
+// is the 64-bit window of the ancestor mask that starts at index s0 - n: a
+// funnel shift of two neighbouring words, indices below zero reading as
+// zero.  s0, n and hi are the same for the whole wave, so the selects below
+// are uniform; the per-key tests then become constant bit positions (the
+// per-key form, with a branch and a dynamic word index per key, cost more
+// than the tile's whole softmax).
+__host__ __device__ __forceinline__ uint64_t slot_visibility(const uint64_t (&am)[4], int s0, int n, int hi) {
+  auto low_bits = [](int c) { return c >= 64 ? ~0ull : c <= 0 ? 0ull : (1ull << c) - 1ull; };
+  auto word = [&](int i) { return i == 0 ? am[0] : i == 1 ? am[1] : i == 2 ? am[2] : i == 3 ? am[3] : 0ull; };
+  const int dl = s0 - n;                        // ancestor index of the tile's first slot
+  uint64_t tree = 0ull;
+  if (dl > -64 && dl < 0) {
+    tree = am[0] << (-dl);
+  } else if (dl >= 0 && dl < 256) {
+    const int wi = dl >> 6, sh = dl & 63;
+    tree = sh == 0 ? word(wi) : (word(wi) >> sh) | (word(wi + 1) << (64 - sh));
+  }
+  return low_bits(n - s0) | (tree & low_bits(hi - s0));
+}
+
 struct AttnArgs {
   const u16* q;
   const u16* kc;
@@ -222,16 +246,14 @@ __global__ __launch_bounds__(256) void tree_attention_kernel(AttnArgs a) {
             tmax = fmaxf(tmax, st[kb][r]);
           }
       } else {
+        // lane group g's keys: bits 8g .. 8g+7 (kk = 0) and 32+8g .. (kk = 1)
+        const uint64_t vis = slot_visibility(am[j], s0, n, hi);
+        const uint32_t vbits[2] = {(uint32_t)(vis >> (8 * g)) & 0xffu, (uint32_t)(vis >> (32 + 8 * g)) & 0xffu};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int slot = s0 + (kb >> 1) * 32 + g * 8 + (kb & 1) * 4 + r;
-            bool ok = slot < n;
-            if (slot >= n && slot < hi) {
-              const int an = slot - n;
-              ok = (am[j][an >> 6] >> (an & 63)) & 1ull;
-            }
+            const bool ok = (vbits[kb >> 1] >> ((kb & 1) * 4 + r)) & 1u;
             const float sv = ok ? st[kb][r] * scale : -INFINITY;
             st[kb][r] = sv;
             tmax = fmaxf(tmax, sv);
@@ -527,16 +549,14 @@ __global__ __launch_bounds__(NW * 64) void tree_attention_qb_kernel(
           tmax = fmaxf(tmax, st[kb][r]);
         }
     } else {
+      // lane group g's keys: bits 8g .. 8g+7 (kk = 0) and 32+8g .. (kk = 1)
+      const uint64_t vis = slot_visibility(am, s0, n, hi);
+      const uint32_t vbits[2] = {(uint32_t)(vis >> (8 * g)) & 0xffu, (uint32_t)(vis >> (32 + 8 * g)) & 0xffu};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int slot = s0 + (kb >> 1) * 32 + g * 8 + (kb & 1) * 4 + r;
-          bool ok = slot < n;
-          if (slot >= n && slot < hi) {
-            const int a = slot - n;
-            ok = (am[a >> 6] >> (a & 63)) & 1ull;
-          }
+          const bool ok = (vbits[kb >> 1] >> ((kb & 1) * 4 + r)) & 1u;
           const float sv = ok ? st[kb][r] * scale : -INFINITY;
           st[kb][r] = sv;
           tmax = fmaxf(tmax, sv);
@@ -571,7 +591,9 @@ __global__ __launch_bounds__(NW * 64) void tree_attention_qb_kernel(
         pf[j] = (__bf16)st[2 * kk][j];
         pf[j + 4] = (__bf16)st[2 * kk + 1][j];
       }
-      if (full) {
+      // every slot below hi holds written K/V (the prefix and this tree):
+      // only a tile that runs past n + T has values to clip
+      if (s0 + 64 <= hi) {
 #pragma unroll
         for (int i = 0; i < DB16; ++i) {
           const uint4 w = {va[kk][i].x, va[kk][i].y, vb[kk][i].x, vb[kk][i].y};
