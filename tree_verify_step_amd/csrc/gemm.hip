@@ -488,10 +488,24 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
             bad |= active && row0 + rb * 16 + r < g.M && !__builtin_isfinite(acc[rb][nb][r]);
       if (__ballot(bad) != 0ull && lane == 0) atomicOr(g.status, MV_STATUS_NONFINITE);
     }
-    if constexpr (NBW == 1 && W * TR * 16 * 4 <= (int)sizeof(As)) {
+    // each row's argmax over this tile's columns; ties go to the lower
+    // column, NaNs never win.  Tiles staged in LDS: W adjacent lanes take one
+    // row, lane w scanning wave w's 16 columns (four 16-byte reads), then a
+    // 3-step shuffle over the W lanes.  Otherwise the lanes of a 16-lane row
+    // group reduce their registers (DPP), then the waves (LDS).
+    constexpr bool STAGED = NBW == 1 && W * TR * 16 * 4 <= (int)sizeof(As);
+    auto publish = [&](int m, float bv, int bi) {
+      // the max only grows: a key at or below the stored one cannot win, so
+      // most tiles skip the atomic (all column tiles share each row's key)
+      const unsigned long long key = argmax_key(bv, bi);
+      if (key > __hip_atomic_load(g.amax_key + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+        __hip_atomic_fetch_max(g.amax_key + m, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    if constexpr (STAGED) {
       // staged per wave in the operand LDS, then written as 16-byte pieces
       // (4 columns of one row)
-      float* stg = reinterpret_cast<float*>(&As[0][0][0]) + wave * TR * 16;
+      float* stg_all = reinterpret_cast<float*>(&As[0][0][0]);
+      float* stg = stg_all + wave * TR * 16;
 #pragma unroll
       for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
@@ -506,57 +520,84 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
                 *reinterpret_cast<const f32x4*>(stg + rl * 16 + 4 * (p & 3));
         }
       }
-    } else if (active) {
-#pragma unroll
-      for (int rb = 0; rb < MB; ++rb)
-#pragma unroll
-        for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int m = row0 + rb * 16 + r;
-            if (m < g.M) g.out_f32[(size_t)m * g.N + (first_blk + nb) * 16 + col] = acc[rb][nb][r];
-          }
-    }
-    if (g.amax_key) {
-      // each row's argmax over this tile's columns: lanes of a 16-lane row
-      // group (shuffles), then the waves (LDS); ties go to the lower column
-      __shared__ float s_av[W][TR];
-      __shared__ int s_ai[W][TR];
-#pragma unroll
-      for (int rb = 0; rb < MB; ++rb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
+      if (g.amax_key) {
+        static_assert((TR * W) % 64 == 0 && 64 % W == 0, "whole waves of W-lane row groups");
+        for (int e = threadIdx.x; e < TR * W; e += W * 64) {      // uniform trip count
+          const int rl = e / W, w = e % W;
+          const int blk = nt * W + w;                 // column block of wave w
           float bv = -INFINITY;
           int bi = 0x7fffffff;
+          if (blk < NBtot) {
+            const f32x4* src = reinterpret_cast<const f32x4*>(stg_all + (w * TR + rl) * 16);
 #pragma unroll
-          for (int nb = 0; nb < NBW; ++nb) {
-            const float v = active ? acc[rb][nb][r] : -INFINITY;
-            const int i = (first_blk + nb) * 16 + col;
-            if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+            for (int q = 0; q < 4; ++q) {
+              const f32x4 v = src[q];
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                const int i = blk * 16 + 4 * q + c;
+                if (v[c] > bv || (v[c] == bv && i < bi)) { bv = v[c]; bi = i; }
+              }
+            }
           }
-          row16_best<0xB1>(bv, bi);     // quad swaps, half-row and row mirrors
-          row16_best<0x4E>(bv, bi);
-          row16_best<0x141>(bv, bi);
-          row16_best<0x140>(bv, bi);
-          if (col == 0) {
-            s_av[wave][rb * 16 + 4 * (lane >> 4) + r] = bv;
-            s_ai[wave][rb * 16 + 4 * (lane >> 4) + r] = bi;
+#pragma unroll
+          for (int o = 1; o < W; o <<= 1) {
+            const float ov = __shfl_xor(bv, o, 64);
+            const int oi = __shfl_xor(bi, o, 64);
+            if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
           }
+          const int m = mt * TR + rl;
+          if (w == 0 && m < g.M) publish(m, bv, bi);
         }
-      __syncthreads();
-      for (int r = threadIdx.x; r < TR; r += W * 64) {
-        const int m = mt * TR + r;
-        if (m >= g.M) continue;
-        float bv = s_av[0][r];
-        int bi = s_ai[0][r];
+      }
+    } else {
+      __shared__ float s_av[W][TR];
+      __shared__ int s_ai[W][TR];
+      if (g.amax_key) {
 #pragma unroll
-        for (int w = 1; w < W; ++w)
-          if (s_av[w][r] > bv || (s_av[w][r] == bv && s_ai[w][r] < bi)) { bv = s_av[w][r]; bi = s_ai[w][r]; }
-        // the max only grows: a key at or below the stored one cannot win,
-        // so most tiles skip the atomic (250 tiles share each row's key)
-        const unsigned long long key = argmax_key(bv, bi);
-        if (key > __hip_atomic_load(g.amax_key + m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-          __hip_atomic_fetch_max(g.amax_key + m, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float bv = -INFINITY;
+            int bi = 0x7fffffff;
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb) {
+              const float v = active ? acc[rb][nb][r] : -INFINITY;
+              const int i = (first_blk + nb) * 16 + col;
+              if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+            }
+            row16_best<0xB1>(bv, bi);     // quad swaps, half-row and row mirrors
+            row16_best<0x4E>(bv, bi);
+            row16_best<0x141>(bv, bi);
+            row16_best<0x140>(bv, bi);
+            if (col == 0) {
+              s_av[wave][rb * 16 + 4 * (lane >> 4) + r] = bv;
+              s_ai[wave][rb * 16 + 4 * (lane >> 4) + r] = bi;
+            }
+          }
+      }
+      if (active) {
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+          for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int m = row0 + rb * 16 + r;
+              if (m < g.M) g.out_f32[(size_t)m * g.N + (first_blk + nb) * 16 + col] = acc[rb][nb][r];
+            }
+      }
+      if (g.amax_key) {
+        __syncthreads();                  // uniform: the waves' row maxima are in LDS
+        for (int r = threadIdx.x; r < TR; r += W * 64) {
+          const int m = mt * TR + r;
+          if (m >= g.M) continue;
+          float bv = s_av[0][r];
+          int bi = s_ai[0][r];
+#pragma unroll
+          for (int w = 1; w < W; ++w)
+            if (s_av[w][r] > bv || (s_av[w][r] == bv && s_ai[w][r] < bi)) { bv = s_av[w][r]; bi = s_ai[w][r]; }
+          publish(m, bv, bi);
+        }
       }
     }
   } else if constexpr (EPI == EPI_ADD) {
