@@ -57,14 +57,16 @@ namespace mvk {
 // zero.  s0, n and hi are the same for the whole wave, so the selects below
 // are uniform; the per-key tests then become constant bit positions (the
 // per-key form, with a branch and a dynamic word index per key, cost more
-// than the tile's whole softmax).
-__host__ __device__ __forceinline__ uint64_t slot_visibility(const uint64_t (&am)[4], int s0, int n, int hi) {
+// than the tile's whole softmax).  The words come in by value: picked from
+// an array by a computed index, they were placed in scratch memory.
+__host__ __device__ __forceinline__ uint64_t slot_visibility(uint64_t a0, uint64_t a1, uint64_t a2,
+                                                             uint64_t a3, int s0, int n, int hi) {
   auto low_bits = [](int c) { return c >= 64 ? ~0ull : c <= 0 ? 0ull : (1ull << c) - 1ull; };
-  auto word = [&](int i) { return i == 0 ? am[0] : i == 1 ? am[1] : i == 2 ? am[2] : i == 3 ? am[3] : 0ull; };
+  auto word = [&](int i) { return i == 0 ? a0 : i == 1 ? a1 : i == 2 ? a2 : i == 3 ? a3 : 0ull; };
   const int dl = s0 - n;                        // ancestor index of the tile's first slot
   uint64_t tree = 0ull;
   if (dl > -64 && dl < 0) {
-    tree = am[0] << (-dl);
+    tree = a0 << (-dl);
   } else if (dl >= 0 && dl < 256) {
     const int wi = dl >> 6, sh = dl & 63;
     tree = sh == 0 ? word(wi) : (word(wi) >> sh) | (word(wi + 1) << (64 - sh));
@@ -247,7 +249,7 @@ __global__ __launch_bounds__(256) void tree_attention_kernel(AttnArgs a) {
           }
       } else {
         // lane group g's keys: bits 8g .. 8g+7 (kk = 0) and 32+8g .. (kk = 1)
-        const uint64_t vis = slot_visibility(am[j], s0, n, hi);
+        const uint64_t vis = slot_visibility(am[j][0], am[j][1], am[j][2], am[j][3], s0, n, hi);
         const uint32_t vbits[2] = {(uint32_t)(vis >> (8 * g)) & 0xffu, (uint32_t)(vis >> (32 + 8 * g)) & 0xffu};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
@@ -433,7 +435,7 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(AttnArgs a) {
 // range, whose merge costs a launch.
 // ---------------------------------------------------------------------------
 template <int HD, int NW>
-__global__ __launch_bounds__(NW * 64) void tree_attention_qb_kernel(
+__global__ __launch_bounds__(NW * 64, 2) void tree_attention_qb_kernel(
     const u16* __restrict__ q, const u16* __restrict__ kc, const u16* __restrict__ vc,
     const int32_t* __restrict__ n_prefix, const uint64_t* __restrict__ anc, int B, int T, int H,
     int cap, int mw, u16* __restrict__ out, int packed) {
@@ -550,7 +552,7 @@ __global__ __launch_bounds__(NW * 64) void tree_attention_qb_kernel(
         }
     } else {
       // lane group g's keys: bits 8g .. 8g+7 (kk = 0) and 32+8g .. (kk = 1)
-      const uint64_t vis = slot_visibility(am, s0, n, hi);
+      const uint64_t vis = slot_visibility(am[0], am[1], am[2], am[3], s0, n, hi);
       const uint32_t vbits[2] = {(uint32_t)(vis >> (8 * g)) & 0xffu, (uint32_t)(vis >> (32 + 8 * g)) & 0xffu};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
