@@ -125,6 +125,11 @@ static GemmCfg gemm_cfg(const mv_dims& D, int kind, int Mp) {
     GemmCfg w = c;
     w.wide = 4;
     if (w.epi == mvk::EPI_SWIGLU && mvk::gemm_wide_ntiles(w.epi, w.N, 4) * w.mtiles > 256) w.wide = 5;
+    // QKV: 96-column tiles when 128-column tiles would leave more than 30% of
+    // the compute units idle and the narrower ones still fit in one round
+    if (w.epi == mvk::EPI_QKV && mvk::gemm_wide_ntiles(w.epi, w.N, 4) * w.mtiles < 180 &&
+        mvk::gemm_wide_ntiles(w.epi, w.N, 3) * w.mtiles <= 256)
+      w.wide = 3;
     w.w = 8;
     w.nbw = 1;
     w.ntiles = mvk::gemm_wide_ntiles(w.epi, w.N, w.wide);
