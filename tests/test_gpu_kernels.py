@@ -199,6 +199,10 @@ def _layer_case(D, B, ns, paths_per_seq, topk, seed, gain_std=0.1):
     ("llama7b", 1, [512]),     # the bench's shapes, tree and launch configuration
     # the 13B workload's 256-node Cartesian tree (4 mask words, 256-row tiles)
     ("llama13b_T256", 1, [1024]),
+    # 13B width at 64 and 16 rows: O and down split K = 5120 three ways (53-54
+    # k-blocks a split, a ragged last chunk in each)
+    ("llama13b_T64", 1, [1024]),
+    ("llama13b_T16", 1, [1024]),
     # the 33B batch: four sequences, their own sparse trees and ragged prefixes
     ("llama33b_B4", 4, None),
     # four 256-node trees at width 6144: M = 1024, every GEMM in wide tiles
@@ -207,6 +211,7 @@ def _layer_case(D, B, ns, paths_per_seq, topk, seed, gain_std=0.1):
 ])
 def test_decoder_layer_matches_oracle(name, B, ns):
     wl = {"llama7b": configs.LLAMA7B_T64, "llama13b_T256": configs.LLAMA13B_T256,
+          "llama13b_T64": configs.LLAMA13B_T64, "llama13b_T16": configs.LLAMA13B_T16,
           "llama33b_B4": configs.LLAMA33B_B4}.get(name)
     if ns is None:
         ns = synth.prefix_lengths(wl)
