@@ -673,7 +673,9 @@ __global__ __launch_bounds__(NW * 64, 2) void tree_attention_qb_kernel(
 
 // Launches with many (sequence, head, query block) triples use 4-wave
 // workgroups: two of them fit a compute unit where one 8-wave workgroup does
-// (212 registers a lane), so more K/V tiles are in flight per unit.
+// (212 registers a lane; the kernel's launch bounds ask for two waves per
+// SIMD, which keeps the 4-wave variant under 256), so more K/V tiles are in
+// flight per unit.
 template <int HD>
 static void launch_attention_qb(const u16* q, const u16* kc, const u16* vc, const int32_t* n_prefix,
                                 const uint64_t* anc, int B, int T, int H, int cap, int mw,
