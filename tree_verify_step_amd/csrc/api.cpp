@@ -118,25 +118,33 @@ static GemmCfg gemm_cfg(const mv_dims& D, int kind, int Mp) {
   // one round), whose range-checked operand loads need each operand below
   // 2 GiB.  It takes the launches where it measured faster at 256 rows: K of
   // 6144 and more with fewer than 8 K splits (every 33B GEMM, 13B down:
-  // 90 against 137 us at 33B down), and gate/up from K = 5120 (13B: 95
-  // against 104 us); the 16-row-block tiles keep the 7B shapes (prefill 14.7
-  // against 15.7 ms) and 13B QKV and O (67 against 71 us, 37.5 against 40).
+  // 90 against 137 us at 33B down), gate/up from K = 5120 (13B: 95 against
+  // 104 us) and gate/up in the narrow tiles below (7B); the 16-row-block
+  // tiles keep the other 7B shapes (prefill 14.7 against 15.7 ms) and 13B
+  // QKV and O (67 against 71 us, 37.5 against 40).
   if (c.MB == 16 && (size_t)c.N * c.K * 2 < (1ull << 31) && (size_t)Mp * c.K * 2 < (1ull << 31)) {
     GemmCfg w = c;
     w.wide = 4;
     if (w.epi == mvk::EPI_SWIGLU && mvk::gemm_wide_ntiles(w.epi, w.N, 4) * w.mtiles > 256) w.wide = 5;
-    // QKV: 96-column tiles when 128-column tiles would leave more than 30% of
-    // the compute units idle and the narrower ones still fit in one round
-    if (w.epi == mvk::EPI_QKV && mvk::gemm_wide_ntiles(w.epi, w.N, 4) * w.mtiles < 180 &&
-        mvk::gemm_wide_ntiles(w.epi, w.N, 3) * w.mtiles <= 256)
+    // QKV and gate/up: tiles of 3 column blocks a wave (96 columns; 48
+    // features) when those of 4 would leave more than 30% of the compute
+    // units idle and the narrower ones still fit in one round (33B QKV: 116
+    // against 111 us; 7B gate/up at 256 rows: 77 against 69.5 us)
+    bool narrow = false;
+    if ((w.epi == mvk::EPI_QKV || w.epi == mvk::EPI_SWIGLU) &&
+        mvk::gemm_wide_ntiles(w.epi, w.N, 4) * w.mtiles < 180 &&
+        mvk::gemm_wide_ntiles(w.epi, w.N, 3) * w.mtiles <= 256) {
       w.wide = 3;
+      narrow = true;
+    }
     w.w = 8;
     w.nbw = 1;
     w.ntiles = mvk::gemm_wide_ntiles(w.epi, w.N, w.wide);
     // K splits while the tiles leave compute units idle, each split at least
     // four 2-k-block stages
     w.splits = std::max(1, std::min(256 / (w.ntiles * w.mtiles), KB / 8));
-    if ((c.K >= 6144 && w.splits < 8) || (c.epi == mvk::EPI_SWIGLU && c.K >= 5120)) return w;
+    if ((c.K >= 6144 && w.splits < 8) || (c.epi == mvk::EPI_SWIGLU && (c.K >= 5120 || narrow)))
+      return w;
   }
   c.ntiles = mvk::gemm_ntiles(c.epi, c.N, c.w, c.nbw);
   const int KC = mvk::gemm_kc(c.MB);

@@ -1383,9 +1383,11 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g) {
 
 template <int NBH>
 static hipError_t launch_wide_nbh(const GemmArgs& g, dim3 grid, hipStream_t s) {
-  if constexpr (NBH == 3) {       // 96-column tiles: QKV only
-    if (g.epi != EPI_QKV) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_wide_kernel<3, EPI_QKV>), grid, dim3(512), 0, s, g);
+  if constexpr (NBH == 3) {       // narrow tiles: QKV and gate/up only
+    if (g.epi == EPI_QKV) hipLaunchKernelGGL((gemm_wide_kernel<3, EPI_QKV>), grid, dim3(512), 0, s, g);
+    else if (g.epi == EPI_SWIGLU)
+      hipLaunchKernelGGL((gemm_wide_kernel<3, EPI_SWIGLU>), grid, dim3(512), 0, s, g);
+    else return hipErrorInvalidValue;
   } else {
     switch (g.epi) {
       case EPI_SWIGLU:
@@ -1469,7 +1471,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
     const dim3 grid(gemm_wide_ntiles(g.epi, g.N, g.wide), g.splits, (g.Mp + WIDE_TR - 1) / WIDE_TR);
     if (g.wide == 4) return launch_wide_nbh<4>(g, grid, s);
     if (g.wide == 5 && g.epi == EPI_SWIGLU) return launch_wide_nbh<5>(g, grid, s);
-    if (g.wide == 3 && g.epi == EPI_QKV) return launch_wide_nbh<3>(g, grid, s);
+    if (g.wide == 3) return launch_wide_nbh<3>(g, grid, s);
     return hipErrorInvalidValue;
   }
   const int MB = gemm_mb(g.Mp);
