@@ -362,11 +362,14 @@ def _accept_case(rng, B, T, V, depth, topk, bias):
 
 @pytest.mark.parametrize("mode,root", [("greedy", "argmax"), ("typical", "argmax"),
                                        ("typical", "sample"), ("greedy", "sample")])
-@pytest.mark.parametrize("B,T", [(1, 64), (4, 64), (1, 256), (2, 15)])
-def test_accept_matches_oracle_given_gpu_logits(mode, root, B, T):
-    _flush(f"accept {mode}/{root} B={B} T={T}")
-    rng = np.random.default_rng(T * 7 + B + len(mode) + len(root))
-    V, depth, topk, d = 1024, 5, 6, 64
+# V = 32000 and 32768 take the register-resident row statistics at the 7B
+# vocabulary and at its limit; V = 40000 takes the looping kernel
+@pytest.mark.parametrize("B,T,V", [(1, 64, 1024), (4, 64, 1024), (1, 256, 1024), (2, 15, 1024),
+                                   (1, 64, 32000), (2, 16, 32768), (1, 64, 40000)])
+def test_accept_matches_oracle_given_gpu_logits(mode, root, B, T, V):
+    _flush(f"accept {mode}/{root} B={B} T={T} V={V}")
+    rng = np.random.default_rng(T * 7 + B + len(mode) + len(root) + (0 if V == 1024 else V))
+    depth, topk, d = 5, 6, 64
     paths, trees, toks, logits = _accept_case(rng, B, T, V, depth, topk, 0.7)
     dt = device_tree(paths, topk)
     temp, eps, delta = 0.7, 0.09, 0.3

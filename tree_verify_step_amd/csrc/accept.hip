@@ -5,6 +5,11 @@
 // normaliser and entropy in double precision:
 //   q_i = exp((z_i - max)/temp) / S,  S = sum_i exp((z_i - max)/temp),
 //   H = -sum_i q_i log(q_i + 1e-5).
+// With e_i = exp((z_i - max)/temp) the entropy is evaluated as
+//   H = log S - (1/S) sum_i e_i log(e_i + 1e-5 S),
+// the same sum without a division per id.  H only enters the threshold
+// through exp(-H), so its absolute error is what counts: a few ulps of
+// log S + H, since the subtracted mean is log S - H.
 // accept_finish: one workgroup per sequence: per-edge decisions (greedy:
 // token == argmax of the parent row; typical: q_parent(token) >
 // min(eps, delta * exp(-H_parent))), accepted-prefix propagation in node order
@@ -209,6 +214,7 @@ __global__ __launch_bounds__(RS_NT) void row_stats_kernel(const float* __restric
     }
     return;
   }
+  const double c = 1e-5 * S;
   double Hs = 0.0;
   for (int i0 = threadIdx.x; i0 < V4; i0 += 4 * RS_NT) {
     float4 v[4];
@@ -219,11 +225,11 @@ __global__ __launch_bounds__(RS_NT) void row_stats_kernel(const float* __restric
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      const float z[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const double q = exp(((double)e[j] - m) * inv_t) / S;
-        Hs += q * log(q + 1e-5);
+        const double e = exp(((double)z[j] - m) * inv_t);
+        Hs += e * log(e + c);
       }
     }
   }
@@ -231,14 +237,98 @@ __global__ __launch_bounds__(RS_NT) void row_stats_kernel(const float* __restric
   if (threadIdx.x == 0) {
     stats[(size_t)row * 3 + 0] = m;
     stats[(size_t)row * 3 + 1] = S;
-    stats[(size_t)row * 3 + 2] = -Hs;
+    stats[(size_t)row * 3 + 2] = log(S) - Hs / S;
   }
 }
 
+// The same statistics for rows of at most NT·J·4 logits, held in registers:
+// thread t reads float4 pieces t + j·NT (j < J) once, and keeps the tempered
+// exponentials of the normaliser pass for the entropy pass, which then costs
+// a division and a log per id, not a second read and a second exp.  The
+// per-thread sums run over j in the same order as the loop above.
+template <int NT, int J>
+__global__ __launch_bounds__(NT) void row_stats_regs_kernel(const float* __restrict__ logits,
+                                                            int V, int mode, double temperature,
+                                                            int32_t* __restrict__ amax,
+                                                            double* __restrict__ stats,
+                                                            double* __restrict__ bsum) {
+  constexpr int NW = NT / 64;
+  const int row = blockIdx.x;
+  const float4* z4 = reinterpret_cast<const float4*>(logits + (size_t)row * V);
+  const int V4 = V >> 2;
+  float4 v[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int i = threadIdx.x + j * NT;
+    v[j] = i < V4 ? z4[i] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+  }
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int id = (threadIdx.x + j * NT) * 4;
+    if (better_iv(v[j].x, id, bv, bi)) { bv = v[j].x; bi = id; }
+    if (better_iv(v[j].y, id + 1, bv, bi)) { bv = v[j].y; bi = id + 1; }
+    if (better_iv(v[j].z, id + 2, bv, bi)) { bv = v[j].z; bi = id + 2; }
+    if (better_iv(v[j].w, id + 3, bv, bi)) { bv = v[j].w; bi = id + 3; }
+  }
+  block_argmax<NW>(bv, bi);
+  if (threadIdx.x == 0) amax[row] = (unsigned)bi < (unsigned)V ? bi : 0;
+  if (mode == MV_ACCEPT_GREEDY) return;
+
+  const double inv_t = 1.0 / temperature;
+  const double m = (double)bv;
+  const int nb = (V + 255) >> 8;
+  const int lane = threadIdx.x & 63;
+  double e[J][4];
+  double S = 0.0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    e[j][0] = exp(((double)v[j].x - m) * inv_t);
+    e[j][1] = exp(((double)v[j].y - m) * inv_t);
+    e[j][2] = exp(((double)v[j].z - m) * inv_t);
+    e[j][3] = exp(((double)v[j].w - m) * inv_t);
+    const double part = (e[j][0] + e[j][1]) + (e[j][2] + e[j][3]);
+    S += part;
+    const int blk = (threadIdx.x + j * NT) >> 6;        // the same for the whole wave
+    if (bsum && blk < nb) {
+      const double t = wave_total_d(part);
+      if (lane == 0) bsum[(size_t)row * nb + blk] = t;
+    }
+  }
+  S = block_sum_d<NW>(S);
+  if (mode != MV_ACCEPT_TYPICAL) {
+    if (threadIdx.x == 0) {
+      stats[(size_t)row * 3 + 0] = m;
+      stats[(size_t)row * 3 + 1] = S;
+      stats[(size_t)row * 3 + 2] = 0.0;
+    }
+    return;
+  }
+  const double c = 1e-5 * S;
+  double Hs = 0.0;
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) Hs += e[j][k] * log(e[j][k] + c);
+  Hs = block_sum_d<NW>(Hs);
+  if (threadIdx.x == 0) {
+    stats[(size_t)row * 3 + 0] = m;
+    stats[(size_t)row * 3 + 1] = S;
+    stats[(size_t)row * 3 + 2] = log(S) - Hs / S;
+  }
+}
+
+constexpr int RSR_NT = 1024, RSR_J = 8;
+
 hipError_t launch_row_stats(const float* logits, int rows, int V, int mode, double temperature,
                             int32_t* argmax, double* stats, hipStream_t s, double* bsum) {
-  hipLaunchKernelGGL(row_stats_kernel, dim3(rows), dim3(RS_NT), 0, s, logits, V, mode, temperature,
-                     argmax, stats, bsum);
+  if ((V >> 2) <= RSR_NT * RSR_J)
+    hipLaunchKernelGGL((row_stats_regs_kernel<RSR_NT, RSR_J>), dim3(rows), dim3(RSR_NT), 0, s,
+                       logits, V, mode, temperature, argmax, stats, bsum);
+  else
+    hipLaunchKernelGGL(row_stats_kernel, dim3(rows), dim3(RS_NT), 0, s, logits, V, mode,
+                       temperature, argmax, stats, bsum);
   return hipGetLastError();
 }
 
