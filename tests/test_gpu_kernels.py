@@ -85,6 +85,10 @@ def _attention_case(D, B, T, ns, depth, topk, seed, cap=None):
 @pytest.mark.parametrize("hd,H,B,T,ns,cap", [
     (16, 4, 1, 15, [32], None),            # tiny shape
     (128, 2, 1, 64, [512], None),          # 7B head dim, one mask word
+    # the 7B heads past a multiple of 512: waves 0 and 1 take a second tile
+    # (the last one partly past n + T); at n = 1100 some waves take three
+    (128, 32, 1, 64, [530], None),
+    (128, 8, 1, 64, [1100], None),
     (128, 2, 1, 64, [37], None),           # ragged prefix, not a multiple of 4 or 64
     (128, 2, 4, 64, [1030, 64, 7, 2047], None),  # split: batch with ragged prefixes
     (64, 2, 1, 256, [300], None),          # four mask words
