@@ -73,6 +73,8 @@ def _check_grad(name, got, want):
     (128, 192, 640, 4, "paper"),      # ragged last tile in d (192 = 1.5 tiles)
     (192, 256, 1088, 2, "ones"),      # the released trainer's unweighted sum; ragged tiles in V
     (256, 1024, 4096, 4, "paper"),    # several tiles in every dimension
+    (576, 1024, 30016, 2, "paper"),   # z and dW2 in 256 x 256 tiles, ragged in both dimensions
+    (2048, 1024, 8192, 2, "paper"),   # a and ds split 8 ways along K, z in 256 x 256 tiles
 ])
 def test_medusa1_loss_and_gradients_match_oracle(N, d, V, K, lam_kind):
     print(f"medusa1 N={N} d={d} V={V} K={K} lambda={lam_kind}", flush=True)

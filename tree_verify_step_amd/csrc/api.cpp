@@ -885,7 +885,7 @@ MV_API int mv_medusa1_loss(const mv_dims* dims, int32_t N, int32_t K, const void
     const u16* W1 = static_cast<const u16*>(w1) + (size_t)k * d * d;
     const u16* W2 = static_cast<const u16*>(w2) + (size_t)k * V * d;
     // forward: a = H W1^T, s = SiLU(a) + H, z = s W2^T, loss and dL/dz
-    MV_HIP(mvk::launch_gemm_nt(H, d, 0, W1, d, 0, a, d, 0, N, d, d, 1, s));
+    MV_HIP(mvk::launch_gemm_nt_splitk(H, d, W1, d, a, N, d, d, z, (size_t)N * V, s));
     MV_HIP(mvk::launch_medusa1_act(a, H, sb, (size_t)N * d, s));
     MV_HIP(mvk::launch_gemm_nt(sb, d, 0, W2, d, 0, z, V, 0, N, V, d, 1, s));
     MV_HIP(mvk::launch_medusa1_ce(z, labels, K, k, (float)lam[k], N, V, ltk, g, s));
@@ -897,8 +897,8 @@ MV_API int mv_medusa1_loss(const mv_dims* dims, int32_t N, int32_t K, const void
     }
     if (dw1) {   // ds = g W2 = g (W2^T [d][V])^T; da = ds SiLU'(a); dW1 = (da^T) (H^T)^T
       MV_HIP(mvk::launch_transpose_bf16(W2, 0, at<u16>(ws, L.w2t), 0, V, d, 1, s));
-      MV_HIP(mvk::launch_gemm_nt(g, V, 0, at<u16>(ws, L.w2t), V, 0, at<float>(ws, L.ds), d, 0, N,
-                                 d, V, 1, s));
+      MV_HIP(mvk::launch_gemm_nt_splitk(g, V, at<u16>(ws, L.w2t), V, at<float>(ws, L.ds), N, d, V,
+                                        z, (size_t)N * V, s));     // z is free after the loss
       MV_HIP(mvk::launch_medusa1_dact(at<float>(ws, L.ds), a, at<u16>(ws, L.da), (size_t)N * d, s));
       MV_HIP(mvk::launch_transpose_bf16(at<u16>(ws, L.da), 0, at<u16>(ws, L.dat), 0, N, d, 1, s));
       MV_HIP(mvk::launch_gemm_nt(at<u16>(ws, L.dat), N, 0, at<u16>(ws, L.ht), N, 0,

@@ -258,6 +258,8 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t n, hipStream_t s);
 hipError_t launch_gemm_nt(const u16* A, int lda, size_t sa, const u16* B, int ldb, size_t sb,
                           float* C, int ldc, size_t sc, int M, int N, int K, int batch,
                           hipStream_t s);
+hipError_t launch_gemm_nt_splitk(const u16* A, int lda, const u16* B, int ldb, float* C, int M,
+                                 int N, int K, float* part, size_t part_elems, hipStream_t s);
 hipError_t launch_transpose_bf16(const u16* in, size_t s_in, u16* out, size_t s_out, int R, int C,
                                  int batch, hipStream_t s);
 hipError_t launch_medusa1_act(const float* a, const u16* h, u16* s, size_t n, hipStream_t st);
