@@ -147,8 +147,8 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const u16* __restrict__ A,
 //    one need not wait for the copies into the other; the chunk loop takes
 //    two chunks a turn, copying chunk k + 1 while chunk k is multiplied, with
 //    one barrier a chunk.
-// Measured at the 7B head shapes: 530-545 us for a 2048 x 32000 x 4096
-// product (40% of the bf16 peak), against 700 us in 128 x 128 tiles.
+// Measured at the 7B head shapes: about 495 us for a 2048 x 32000 x 4096
+// product (44% of the bf16 peak), against 700 us in 128 x 128 tiles.
 constexpr int TB_BM = 256, TB_BK = 64;
 constexpr int MV_BUF_RAW = 0x00020000;   // buffer resource word 3: raw (untyped) access
 
@@ -215,19 +215,64 @@ __global__ __launch_bounds__(512) void gemm_nt_big_kernel(const u16* __restrict_
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Fragment reads run ahead of the MFMAs that use them, in a pinned order
+  // (left to itself the scheduler waits for each read just before its row):
+  // a chunk starts with the first half's four B fragments and first two A
+  // fragments; each row of 4 MFMAs is followed by the read of the A fragment
+  // two rows ahead; the last two rows of the first half are followed by the
+  // second half's B fragments (a second set) and first A fragments.
   auto chunk = [&](const u16* as, const u16* bs) {
+    bf16x8 a[8], b0[4], b1[4];
+    auto ra = [&](int ks, int i) {
+      a[i] = *reinterpret_cast<const bf16x8*>(as + fo_a[ks] + i * 16 * TB_BK);
+    };
+    auto rb = [&](int ks, bf16x8 (&b)[4], int j) {
+      b[j] = *reinterpret_cast<const bf16x8*>(bs + fo_b[ks] + j * 16 * TB_BK);
+    };
+    auto row = [&](const bf16x8 (&b)[4], int i) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 a[8], b[4];
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
+    };
 #pragma unroll
-      for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const bf16x8*>(as + fo_a[ks] + i * 16 * TB_BK);
+    for (int j = 0; j < 4; ++j) rb(0, b0, j);
+    ra(0, 0);
+    ra(0, 1);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const bf16x8*>(bs + fo_b[ks] + j * 16 * TB_BK);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
+    for (int i = 0; i < 6; ++i) {
+      row(b0, i);
+      ra(0, i + 2);
     }
+    row(b0, 6);
+    rb(1, b1, 0);
+    rb(1, b1, 1);
+    ra(1, 0);
+    row(b0, 7);
+    rb(1, b1, 2);
+    rb(1, b1, 3);
+    ra(1, 1);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      row(b1, i);
+      ra(1, i + 2);
+    }
+    row(b1, 6);
+    row(b1, 7);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   };
 
   // chunk kt lives in buffers kt & 1 (the launcher asks for an even count)
