@@ -75,6 +75,7 @@ def _check_grad(name, got, want):
     (256, 1024, 4096, 4, "paper"),    # several tiles in every dimension
     (576, 1024, 30016, 2, "paper"),   # z and dW2 in 256 x 256 tiles, ragged in both dimensions
     (2048, 1024, 8192, 2, "paper"),   # a and ds split 8 ways along K, z in 256 x 256 tiles
+    (64, 64, 33024, 2, "ones"),       # a vocabulary past 32768: the looping cross-entropy kernel
 ])
 def test_medusa1_loss_and_gradients_match_oracle(N, d, V, K, lam_kind):
     print(f"medusa1 N={N} d={d} V={V} K={K} lambda={lam_kind}", flush=True)

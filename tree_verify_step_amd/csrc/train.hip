@@ -499,6 +499,71 @@ __global__ __launch_bounds__(256) void medusa1_ce_kernel(const float* __restrict
   }
 }
 
+// The same for rows of at most NT * J * 4 logits, each read once: thread
+// tid holds float4 pieces tid + j NT (j < J) in registers through the max,
+// the sum and the gradient passes (the looping form reads the row three
+// times).
+template <int NT, int J>
+__global__ __launch_bounds__(NT) void medusa1_ce_regs_kernel(const float* __restrict__ z,
+                                                             const int32_t* __restrict__ labels,
+                                                             int ldl, int k, float lambda, int V,
+                                                             float* __restrict__ loss_tk,
+                                                             u16* __restrict__ g) {
+  constexpr int NW = NT / 64;
+  __shared__ float rmax[NW];
+  __shared__ double red[NW];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const float* zr = z + (size_t)t * V;
+  u16* gr = g + (size_t)t * V;
+  const int y = labels[(size_t)t * ldl + k];
+  const bool lab = y >= 0 && y < V;
+  const int V4 = V >> 2;
+  float4 v[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int i = tid + j * NT;
+    v[j] = i < V4 ? reinterpret_cast<const float4*>(zr)[i]
+                  : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < J; ++j) mx = fmaxf(mx, fmaxf(fmaxf(v[j].x, v[j].y), fmaxf(v[j].z, v[j].w)));
+  mx = warp_max(mx);
+  if (lane == 0) rmax[wave] = mx;
+  __syncthreads();
+  mx = rmax[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) mx = fmaxf(mx, rmax[w]);
+  double sum = 0.0;
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+    sum += (double)__expf(v[j].x - mx) + (double)__expf(v[j].y - mx) +
+           (double)__expf(v[j].z - mx) + (double)__expf(v[j].w - mx);
+  sum = warp_sum_d(sum);
+  if (lane == 0) red[wave] = sum;
+  __syncthreads();
+  double S = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) S += red[w];
+  const float lse = mx + (float)log(S);
+  if (tid == 0) loss_tk[(size_t)t * ldl + k] = lab ? lambda * (lse - zr[y]) : 0.f;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int i4 = tid + j * NT;
+    if (i4 >= V4) continue;
+    const float vv[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+    u16 o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p = __expf(vv[e] - lse);
+      o[e] = lab ? f32_to_bf16(lambda * (p - (i4 * 4 + e == y ? 1.f : 0.f))) : (u16)0;
+    }
+    *reinterpret_cast<uint2*>(gr + i4 * 4) = uint2{(uint32_t)o[0] | ((uint32_t)o[1] << 16),
+                                                   (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
+  }
+}
+
 // loss = sum of loss_tk [n] in a fixed order (one workgroup, fp64).
 __global__ __launch_bounds__(256) void medusa1_sum_kernel(const float* __restrict__ v, int n,
                                                           double* __restrict__ out) {
@@ -525,8 +590,12 @@ hipError_t launch_medusa1_dact(const float* ds, const float* a, u16* da, size_t 
 }
 hipError_t launch_medusa1_ce(const float* z, const int32_t* labels, int ldl, int k, float lambda,
                              int N, int V, float* loss_tk, u16* g, hipStream_t st) {
-  hipLaunchKernelGGL(medusa1_ce_kernel, dim3(N), dim3(256), 0, st, z, labels, ldl, k, lambda, V,
-                     loss_tk, g);
+  if (V / 4 <= 1024 * 8)
+    hipLaunchKernelGGL((medusa1_ce_regs_kernel<1024, 8>), dim3(N), dim3(1024), 0, st, z, labels, ldl,
+                       k, lambda, V, loss_tk, g);
+  else
+    hipLaunchKernelGGL(medusa1_ce_kernel, dim3(N), dim3(256), 0, st, z, labels, ldl, k, lambda, V,
+                       loss_tk, g);
   return hipGetLastError();
 }
 hipError_t launch_medusa1_sum(const float* v, int n, double* out, hipStream_t st) {
