@@ -66,6 +66,7 @@ __host__ __device__ __forceinline__ int qkv_feature(int p, int d, int hd) {
 // batches use for splits that do not exist.
 #define MV_CPOL_SYS 17              /* sc0 | sc1 */
 #define MV_BUF_DWORD3 0x00020000    /* raw (untyped) buffer resource */
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 #define MV_BUF_NONE 0x7ffffff0      /* an offset past any partial buffer */
 
 // A float moved between lanes of a 16-lane DPP row (VALU lane moves, no LDS
@@ -905,10 +906,12 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
 // -- are bound by LDS reads.  Here a workgroup of 8 waves owns 256 rows x
 // 32*NBH columns: wave (wm, wn) computes rows 64*wm .. +63 against column
 // blocks NBH*wn .. +NBH-1 of the tile (4 x NBH accumulators of 16 x 16), so
-// every fragment read from LDS feeds NBH or 4 MFMAs.  Both operands are staged
-// through LDS, WIDE_KS k-blocks a stage, double-buffered, from a register
-// prefetch WIDE_P stages deep (each thread issues 4 activation and up to 3
-// weight loads of 16 bytes a stage); one barrier a stage.  The epilogues work
+// every fragment read from LDS feeds NBH or 4 MFMAs.  Both operands go from
+// memory straight into LDS (buffer loads that write LDS, one 1 KiB fragment
+// piece per instruction), WIDE_KS k-blocks a stage, in three stage buffers
+// with two stages in flight; one barrier a stage.  (Staged through registers
+// instead, three stages deep, the kernel held 195-256 VGPRs and ran 2-8%
+// slower at the 13B and 33B shapes.)  The epilogues work
 // on the tile staged in LDS as fp32 (SwiGLU: the up accumulators parked
 // there), so that every global store is a whole 16-byte piece.
 // SwiGLU tiles take gate blocks NBH*nt .. +NBH-1 (waves wn = 0) and the same
@@ -922,7 +925,6 @@ __global__ __launch_bounds__(W * 64) void gemm_kernel(GemmArgs g) {
 // between register files in the loop) were slower.
 // ---------------------------------------------------------------------------
 constexpr int WIDE_KS = 2;       // k-blocks per stage
-constexpr int WIDE_P = 3;        // stages of loads in flight
 constexpr int WIDE_TR = 256;     // rows of a tile
 
 template <int NBH, int EPI>
@@ -933,10 +935,9 @@ struct WideShape {
   static constexpr int WP = NB * WIDE_KS;             // weight pieces a stage
   static constexpr int AL = AP / 8;                   // ... loaded per thread
   static constexpr int WL = (WP + 7) / 8;
-  static constexpr int WPS = WP % 8 == 0 ? WP : WP + 1;   // weight slots (+1: a sink for
-                                                      //   the loads past WP, no branch)
+  static constexpr int WPS = WP;                      // weight slots
   static constexpr int OPB = (AP + WPS) * 64;         // bf16x8 of one stage buffer
-  static constexpr int NBUF = 2;                      // stage buffers in LDS
+  static constexpr int NBUF = 3;                      // stage buffers in LDS
   static constexpr int LDF = TC + 4;                  // fp32 staging row (floats)
   static constexpr int FT = 16 * NBH;                 // SwiGLU: features of a tile
   static constexpr int LDH = FT + 8;                  // SwiGLU: bf16 staging row (u16)
@@ -985,34 +986,64 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g) {
     return min(blk, NBtot - 1);
   };
 
-  // stage st's loads: activation piece p = 8i + wave is (kl = p / 16, row
-  // block p % 16), weight piece p = 8i + wave is (kl = p / NB, block p % NB)
-  auto issue = [&](bf16x8 (&ra)[AL], bf16x8 (&rw)[WL], int st) {
-    const int kb0 = lo + st * WIDE_KS;
+  // Stage st's pieces go from memory straight into LDS buffer buf, one
+  // 1 KiB piece per instruction (the operands are stored in fragment order,
+  // so a piece is contiguous in both): activation piece p = 8i + wave is
+  // (kl = p / 16, row block p % 16), weight piece p = 8i + wave is
+  // (kl = p / NB, block p % NB); the waves past the last weight piece copy
+  // that piece again (the same bytes to the same place).  The copies are
+  // inline assembly, which the compiler's wait insertion does not see (it
+  // cannot tell the stage buffers apart and would hold every fragment read
+  // until all copies had landed); each step waits for its own stage by hand,
+  // and the only loads the compiler tracks (the norm factors) are used after
+  // the loop.
+  constexpr int DPW = AL + WL;                 // copies per wave and stage
+  auto piece_a = [&](int st, int i, uint32_t& off) {
+    const int pc = i * 8 + wave;
+    const int k = lo + st * WIDE_KS + pc / 16;
+    const int rbg = min(mt * 16 + pc % 16, MBtot - 1);
+    off = k < hi ? (uint32_t)((rbg * KB + k) * 64 + lane) * 16u : OOB;
+    return pc;
+  };
+  auto piece_w = [&](int st, int i, uint32_t& off, bool& second) {
+    const int pc = min(i * 8 + wave, WP - 1);
+    const int k = lo + st * WIDE_KS + pc / NB, j = pc % NB;
+    off = k < hi ? (uint32_t)((k * NBtot + wblk(j)) * 64 + lane) * 16u : OOB;
+    second = EPI == EPI_SWIGLU && j >= NBH;
+    return AP + pc;
+  };
+  const uint64_t ba = (uint64_t)g.A, bw = (uint64_t)g.W,
+                 bw2 = (uint64_t)(EPI == EPI_SWIGLU ? g.W2 : g.W);
+  const i32x4 qA = {(int)(uint32_t)ba, (int)(uint32_t)(ba >> 32), MBtot * KB * 1024, MV_BUF_DWORD3};
+  const i32x4 qW = {(int)(uint32_t)bw, (int)(uint32_t)(bw >> 32), KB * NBtot * 1024, MV_BUF_DWORD3};
+  const i32x4 qW2 = {(int)(uint32_t)bw2, (int)(uint32_t)(bw2 >> 32), KB * NBtot * 1024,
+                     MV_BUF_DWORD3};
+  auto lds_addr = [](const bf16x8* p) {
+    return (uint32_t)(size_t)(const __attribute__((address_space(3))) bf16x8*)p;
+  };
+  auto copy_asm = [&](int st, int buf) {
+    bf16x8* sb = smem + buf * OPB;
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
-      const int pc = i * 8 + wave;
-      const int k = kb0 + pc / 16;
-      const int rbg = min(mt * 16 + pc % 16, MBtot - 1);
-      const uint32_t off = k < hi ? (uint32_t)((rbg * KB + k) * 64 + lane) * 16u : OOB;
-      ra[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rA, off, 0, 0));
+      uint32_t off;
+      const int pc = piece_a(st, i, off);
+      const uint32_t la = __builtin_amdgcn_readfirstlane(lds_addr(sb + pc * 64));
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :: "s"(la), "v"(off), "s"(qA) : "memory", "m0");
     }
 #pragma unroll
     for (int i = 0; i < WL; ++i) {
-      const int pc = min(i * 8 + wave, WP - 1);
-      const int k = kb0 + pc / NB, j = pc % NB;
-      const uint32_t off = k < hi ? (uint32_t)((k * NBtot + wblk(j)) * 64 + lane) * 16u : OOB;
-      rw[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                             EPI == EPI_SWIGLU && j >= NBH ? rW2 : rW, off, 0, 0));
+      uint32_t off;
+      bool second;
+      const int pc = piece_w(st, i, off, second);
+      const uint32_t la = __builtin_amdgcn_readfirstlane(lds_addr(sb + pc * 64));
+      if (second)
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :: "s"(la), "v"(off), "s"(qW2) : "memory", "m0");
+      else
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :: "s"(la), "v"(off), "s"(qW) : "memory", "m0");
     }
-  };
-  // ... and their LDS stores
-  auto stash = [&](const bf16x8 (&ra)[AL], const bf16x8 (&rw)[WL], int buf) {
-    bf16x8* sb = smem + buf * OPB;
-#pragma unroll
-    for (int i = 0; i < AL; ++i) sb[(i * 8 + wave) * 64 + lane] = ra[i];
-#pragma unroll
-    for (int i = 0; i < WL; ++i) sb[(AP + min(i * 8 + wave, WPS - 1)) * 64 + lane] = rw[i];
   };
 
   f32x4 acc[4][NBH];
@@ -1036,8 +1067,8 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g) {
   };
 
   // norm factors: two threads a row, up to WIDE_SSQ f32x4 of partial sums
-  // each, requested before the weight prefetch so that their wait does not
-  // drain it (longer rows of partials: summed serially below)
+  // each, requested before the first copies and summed after the loop
+  // (longer rows of partials: summed serially there)
   constexpr int WIDE_SSQ = 8;
   const bool ss_fast = g.ss != nullptr && g.ss_tiles <= 2 * 4 * WIDE_SSQ;
   f32x4 ssv[WIDE_SSQ];
@@ -1053,13 +1084,28 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g) {
   }
   int nraw = 0;
   if (EPI == EPI_QKV && threadIdx.x < g.qkv.B) nraw = g.qkv.n_prefix[threadIdx.x];
-  // WIDE_P stages of loads in flight, 2 for 5-block waves (their
-  // accumulators leave registers for two register sets only)
-  constexpr int P = NBH == 5 ? 2 : WIDE_P;
-  bf16x8 ra0[AL], rw0[WL], ra1[AL], rw1[WL], ra2[P >= 3 ? AL : 1], rw2[P >= 3 ? WL : 1];
-  issue(ra0, rw0, 0);
-  issue(ra1, rw1, 1);
-  if constexpr (P >= 3) issue(ra2, rw2, 2);
+  // three LDS stage buffers, two stages copied ahead
+  copy_asm(0, 0);
+  copy_asm(1, 1);
+  // Step s: wait for this wave's copies of stage s (those of stage s + 1 may
+  // still fly) and for its LDS reads, barrier (stage s is readable and the
+  // buffer of stage s - 1 free), copy stage s + 2 into that buffer, then
+  // multiply stage s.  Copies past the range read zeros; the loop drains
+  // them before the epilogues reuse the LDS.
+  constexpr int GATE = (DPW & 15) | (7 << 4) | ((DPW >> 4) << 14);   // vmcnt(DPW) lgkmcnt(0)
+  for (int st = 0; st < nst; ++st) {
+    asm volatile("s_waitcnt %0\n\ts_barrier" :: "i"(GATE) : "memory");
+    copy_asm(st + 2, (st + 2) % 3);
+    const int buf = st % 3;
+    bf16x8 fa[4], fw[NBH];
+#pragma unroll
+    for (int kl = 0; kl < WIDE_KS; ++kl) {
+      read_frags(buf, kl, fa, fw);
+      mfma_kb(fa, fw);
+    }
+  }
+  // the norm factors (their loads went out before the copies and are long
+  // done), then the copies past the range drained and rs_s made visible
   if (ss_fast) {
     const int r = threadIdx.x >> 1, hf = threadIdx.x & 1;
     float sm = 0.f;
@@ -1084,41 +1130,7 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g) {
   }
   if (EPI == EPI_QKV && threadIdx.x < g.qkv.B)
     s_slot0[threadIdx.x] = min(max(nraw, 0), g.qkv.cap - g.qkv.T);
-  stash(ra0, rw0, 0);
-  issue(ra0, rw0, P);
-  __syncthreads();
-  // Two stage buffers in LDS.  Step s computes stage s from buffer s & 1
-  // (each k-block's fragments read just before its MFMAs), moves stage s + 1
-  // from its register set ((s + 1) % P) into the other buffer and refills
-  // the set with stage s + 1 + P.  The step count is padded to a multiple of
-  // P (stages past the range compute on zeros) and every step issues its
-  // loads (past the range: offsets past the buffers), so the loop has no
-  // branches and each stage waits only on its own loads.
-  const int nst_pad = (nst + P - 1) / P * P;
-#define MV_WIDE_STEP(S_, RA, RW)                                             \
-  {                                                                          \
-    bf16x8 fa[4], fw[NBH];                                                   \
-    _Pragma("unroll") for (int kl = 0; kl < WIDE_KS; ++kl) {                 \
-      read_frags((S_) & 1, kl, fa, fw);                                      \
-      mfma_kb(fa, fw);                                                       \
-    }                                                                        \
-    stash(RA, RW, ((S_) + 1) & 1);                                           \
-    issue(RA, RW, (S_) + 1 + P);                                             \
-    __syncthreads();                                                         \
-  }
-  if constexpr (P == 3) {
-    for (int s0 = 0; s0 < nst_pad; s0 += 3) {
-      MV_WIDE_STEP(s0, ra1, rw1)
-      MV_WIDE_STEP(s0 + 1, ra2, rw2)
-      MV_WIDE_STEP(s0 + 2, ra0, rw0)
-    }
-  } else {
-    for (int s0 = 0; s0 < nst_pad; s0 += 2) {
-      MV_WIDE_STEP(s0, ra1, rw1)
-      MV_WIDE_STEP(s0 + 1, ra0, rw0)
-    }
-  }
-#undef MV_WIDE_STEP
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   // ---- split-K: the last workgroup of the tile sums the splits in order
   if (g.splits > 1) {
