@@ -949,7 +949,7 @@ struct WideShape {
 template <int NBH, int EPI>
 __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g) {
   using S = WideShape<NBH, EPI>;
-  constexpr int NB = S::NB, TC = S::TC, AP = S::AP, WP = S::WP, WPS = S::WPS, AL = S::AL, WL = S::WL;
+  constexpr int NB = S::NB, TC = S::TC, AP = S::AP, WP = S::WP, AL = S::AL, WL = S::WL;
   constexpr int OPB = S::OPB, LDF = S::LDF;
   static_assert(AP % 8 == 0, "activation pieces divide over the waves");
   __shared__ bf16x8 smem[S::SMEM16];
@@ -969,15 +969,8 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g) {
   const int NT = EPI == EPI_SWIGLU ? (NBtot + NBH - 1) / NBH : (NBtot + NB - 1) / NB;
 
   // Operand loads are range-checked buffer loads: k-blocks past the split's
-  // range get an offset past the buffer and read zeros, so the LDS stores
-  // are plain copies (no selects on loaded registers, which the compiler
-  // would hoist to where they wait on the youngest loads).
-  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<u16*>(g.A), (short)0, MBtot * KB * 1024, MV_BUF_DWORD3);
-  const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<u16*>(g.W), (short)0, KB * NBtot * 1024, MV_BUF_DWORD3);
-  const __amdgpu_buffer_rsrc_t rW2 = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<u16*>(EPI == EPI_SWIGLU ? g.W2 : g.W), (short)0, KB * NBtot * 1024, MV_BUF_DWORD3);
+  // range get an offset past the buffer and read zeros, so the LDS copies
+  // need no selects or branches.
   constexpr uint32_t OOB = 0x80000000u;        // past every operand (each < 2 GiB)
   // the weight block of tile block j (clamped: blocks past the matrix load
   // valid memory and are never stored)
@@ -996,7 +989,8 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g) {
   // cannot tell the stage buffers apart and would hold every fragment read
   // until all copies had landed); each step waits for its own stage by hand,
   // and the only loads the compiler tracks (the norm factors) are used after
-  // the loop.
+  // the loop.  The LDS address goes in as an m0 operand, so the compiler
+  // itself sets m0 and knows its value is consumed there.
   constexpr int DPW = AL + WL;                 // copies per wave and stage
   auto piece_a = [&](int st, int i, uint32_t& off) {
     const int pc = i * 8 + wave;
@@ -1028,8 +1022,8 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g) {
       uint32_t off;
       const int pc = piece_a(st, i, off);
       const uint32_t la = __builtin_amdgcn_readfirstlane(lds_addr(sb + pc * 64));
-      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                   :: "s"(la), "v"(off), "s"(qA) : "memory", "m0");
+      asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                   :: "v"(off), "s"(qA), "{m0}"(la) : "memory");
     }
 #pragma unroll
     for (int i = 0; i < WL; ++i) {
@@ -1038,11 +1032,11 @@ __global__ __launch_bounds__(512) void gemm_wide_kernel(GemmArgs g) {
       const int pc = piece_w(st, i, off, second);
       const uint32_t la = __builtin_amdgcn_readfirstlane(lds_addr(sb + pc * 64));
       if (second)
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                     :: "s"(la), "v"(off), "s"(qW2) : "memory", "m0");
+        asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                     :: "v"(off), "s"(qW2), "{m0}"(la) : "memory");
       else
-        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                     :: "s"(la), "v"(off), "s"(qW) : "memory", "m0");
+        asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                     :: "v"(off), "s"(qW), "{m0}"(la) : "memory");
     }
   };
 
