@@ -186,24 +186,27 @@ def stages(layers: int) -> int:
     return 2 * layers + 1
 
 
-def _full_dims_session(wname, L, steps, cache_weights=True, dims=None):
-    """A step context at a workload's dims (or `dims`) with L decoder layers,
-    holding the state a prefill of the workload's prompt length leaves:
-    seeded bf16 prefix K/V, a post-norm hidden state of unit scale and a root
-    token (declared to the context with resume).  Returns the pieces both
-    sides need."""
+def _full_dims_session(wname, L, steps, cache_weights=True, dims=None, batch=1):
+    """A step context at a workload's dims (or `dims`) with L decoder layers
+    and the first `batch` sequences of the workload (each with its own tree
+    and prefix length), holding the state a prefill of the prompts leaves:
+    seeded bf16 prefix K/V, post-norm hidden states of unit scale and root
+    tokens (declared to the context with resume).  Returns the pieces both
+    sides need, per sequence (and, for one sequence, also unwrapped)."""
     w0 = configs.get(wname)
     b = dims or w0.dims
     D = configs.Dims(L=L, d=b.d, H=b.H, hd=b.hd, F=b.F, V=b.V, K=b.K)
     w = w0.with_(dims=D)
     Wt = synth.TorchDrawnWeights(w, cache=cache_weights)
     s = synth.tree_topk(w)
-    paths = synth.tree_paths(w, 0)
-    t = otree.compile_tree(paths)
-    trees = rt.DeviceTrees([paths], s)
-    assert trees.T == t.T
-    n0 = synth.prefix_lengths(w)[0]
-    cap = ((n0 + t.T + steps * (t.max_depth + 1) + 63) // 64) * 64
+    B = batch
+    paths = [synth.tree_paths(w, i) for i in range(B)]
+    ts = [otree.compile_tree(p) for p in paths]
+    trees = rt.DeviceTrees(paths, s)
+    assert all(trees.T == t.T for t in ts)
+    n0s = [int(x) for x in synth.prefix_lengths(w)[:B]]
+    depth = max(t.max_depth for t in ts)
+    cap = ((max(n0s) + trees.T + steps * (depth + 1) + 63) // 64) * 64
     dw = rt.DeviceWeights(D, Wt.get)
     reject = w.accept == "reject"
     mode = {"greedy": tv.ACCEPT_GREEDY, "typical": tv.ACCEPT_TYPICAL,
@@ -211,108 +214,120 @@ def _full_dims_session(wname, L, steps, cache_weights=True, dims=None):
     p = tv.AcceptParams(mode=mode,
                         root_mode=tv.ROOT_SAMPLE if w.root == "sample" else tv.ROOT_ARGMAX,
                         temperature=w.temperature, eps=w.eps, delta=w.delta)
-    u = synth.uniform_draws(w, steps + 1, t.T if reject else 0)
-    sess = rt.Session(D, 1, t.T, s, cap, dw, trees, p, u_draws=u, debug=True)
+    u = synth.uniform_draws(w, steps + 1, trees.T if reject else 0)[:, :B]
+    sess = rt.Session(D, B, trees.T, s, cap, dw, trees, p, u_draws=u, debug=True)
     rng = np.random.default_rng(77)
-    ocaches, kv = fill_prefix_kv(rng, D, 1, [n0], cap)
+    ocaches, kv = fill_prefix_kv(rng, D, B, n0s, cap)
     sess.kv.k.copy_(kv.k)
     sess.kv.v.copy_(kv.v)
     del kv
-    h = synth.round_to_bf16(rng.standard_normal(D.d).astype(np.float32)).astype(np.float64)
-    sess.h_last.copy_(torch.from_numpy(h.astype(np.float32)).to(torch.bfloat16).unsqueeze(0))
-    t0 = int(rng.integers(D.V))
-    sess.root_tok.fill_(t0)
-    sess.n_prefix.fill_(n0)
+    hs, t0s = [], []
+    for _ in range(B):
+        hs.append(synth.round_to_bf16(rng.standard_normal(D.d).astype(np.float32)).astype(np.float64))
+        t0s.append(int(rng.integers(D.V)))
+    sess.h_last.copy_(torch.from_numpy(np.stack(hs).astype(np.float32)).to(torch.bfloat16))
+    sess.root_tok.copy_(torch.tensor(t0s, dtype=torch.int32))
+    sess.n_prefix.copy_(torch.tensor(n0s, dtype=torch.int32))
     sess.u_index.fill_(1)              # a prefill consumes draw 0 for the first root
-    sess.resume([n0], 1)
+    sess.resume(n0s, 1)
     torch.cuda.synchronize()
-    return dict(w=w, D=D, Wt=Wt, s=s, t=t, sess=sess, okv=ocaches[0], h=h, t0=t0, n0=n0, u=u)
+    c = dict(w=w, D=D, Wt=Wt, s=s, ts=ts, sess=sess, okvs=ocaches, hs=hs, t0s=t0s, n0s=n0s, u=u, B=B)
+    if B == 1:
+        c.update(t=ts[0], okv=ocaches[0], h=hs[0], t0=t0s[0], n0=n0s[0])
+    return c
 
 
 def _teacher_forced_steps(c, steps, exact_head=True):
     """Run `steps` graph steps from the state of _full_dims_session and
-    compare each with the oracle, the oracle following the GPU's decisions.
-    Per-stage checks with identical inputs hold TOL: the head logits (from
-    the GPU's h_last) and the LM head (from the GPU's final residual rows).
-    The whole-forward drift of the tree logits, h_last and the K/V rows is
-    returned per step and held to the stage bound TOL * (2l + 1), for the
-    logits times max(1, their rms)."""
-    w, D, Wt, s, t, sess, okv = c["w"], c["D"], c["Wt"], c["s"], c["t"], c["sess"], c["okv"]
-    h, t0, n, u = c["h"], c["t0"], c["n0"], c["u"]
-    n0 = n
+    compare each with the oracle, sequence by sequence, the oracle following
+    the GPU's decisions.  Per-stage checks with identical inputs hold TOL:
+    the head logits (from the GPU's h_last) and the LM head (from the GPU's
+    final residual rows).  The whole-forward drift of the tree logits,
+    h_last and the K/V rows is returned per step and held to the stage bound
+    TOL * (2l + 1), for the logits times max(1, their rms)."""
+    w, D, Wt, s, sess, B = c["w"], c["D"], c["Wt"], c["s"], c["sess"], c["B"]
+    ts, okvs, u = c["ts"], c["okvs"], c["u"]
+    hs, t0s, ns = list(c["hs"]), list(c["t0s"]), list(c["n0s"])
+    n0s = list(ns)
     reject = w.accept == "reject"
+    T = sess.T
     drift = []
     for step in range(steps):
         sess.step(graph=True)
         torch.cuda.synchronize()
-        print(f"  step {step}: n={n}", flush=True)
-        hz = sess.head_logits[0].cpu().numpy()
-        want_z = oh.medusa_heads(Wt.get, h, t.max_depth)
-        assert np.abs(hz - want_z).max() <= TOL, (step, np.abs(hz - want_z).max())
-        top = sess.top_ids[0].cpu().numpy()
-        np.testing.assert_array_equal(top, oh.head_topk(hz, s))
-        tok = otree.fill_tokens(t, t0, top)
-        np.testing.assert_array_equal(sess.tree_tok[0].cpu().numpy(), tok)
-        gl = sess.logits[0].cpu().numpy().astype(np.float64)
-        # the LM-head stage on the GPU's own final residual rows
-        xg = sess.residual().cpu().numpy().astype(np.float64)
-        _, lm_want = om.final_head(Wt.get, xg)
-        lm_err = np.abs(gl - lm_want).max()
-        assert lm_err <= TOL, (step, lm_err)
-        # the whole forward against the oracle's own
-        hn, logits = om.tree_forward(Wt.get, D.L, D.H, t, tok, n, okv)
-        lerr = np.abs(gl - logits).max()
-        print(f"  step {step}: head logits err {np.abs(hz - want_z).max():.2e}, LM-head stage err "
-              f"{lm_err:.2e}, tree logits drift max {lerr:.4f} rms "
-              f"{np.sqrt(np.mean((gl - logits) ** 2)):.5f} (logits rms "
-              f"{np.sqrt(np.mean(logits ** 2)):.3f})", flush=True)
-        # the drift bound TOL per stage is for unit-scale values: bf16 rounding
-        # is relative, so the logits' bound scales with their rms (1.28 at
-        # the 7B width, 1.63 at 33B with N(0, 0.02) weights)
-        lscale = max(1.0, float(np.sqrt(np.mean(logits ** 2))))
-        assert lerr <= TOL * stages(D.L) * lscale, (step, lerr, lscale)
-        if w.accept == "typical":
-            res = oa.typical_accept(t, tok, gl, w.temperature, w.eps, w.delta)
-        elif reject:
-            res = oa.reject_accept(t, tok, gl, w.temperature, u[step + 1, 0])
-            m = res.margin
-            assert not np.any(np.abs(m[np.isfinite(m)]) <= 1e-9), "tie up to rounding"
-        else:
-            res = oa.greedy_accept(t, tok, gl)
-        L_acc = int(sess.accept_len[0])
-        assert L_acc == res.accept_len, step
-        np.testing.assert_array_equal(sess.path[0].cpu().numpy()[:L_acc + 1], res.path)
-        np.testing.assert_array_equal(sess.emitted[0].cpu().numpy()[:L_acc + 1], tok[res.path])
-        assert int(sess.best[0]) == res.best
-        if reject:
-            assert int(sess.root_tok[0]) == res.next_root
-        elif w.root == "sample":
-            want, margin = oa.sample_root(gl[res.best], w.temperature, u[step + 1, 0])
-            if margin > 1e-6:
-                assert int(sess.root_tok[0]) == want
-        else:
-            assert int(sess.root_tok[0]) == oa.argmax_lowest(gl[res.best])
-        t0 = int(sess.root_tok[0])
-        herr = np.abs(sess.h_last[0].float().cpu().numpy() - hn[res.best]).max()
-        assert herr <= TOL * stages(D.L), (step, herr)
-        h = sess.h_last[0].float().cpu().numpy().astype(np.float64)   # follow the GPU
-        od.compact_kv(okv, n, res.path)
-        n += len(res.path)
-        assert int(sess.n_prefix[0]) == n
-        kg = sess.kv.k_rows()[:, 0].float().cpu().numpy()
-        vg = sess.kv.v_rows()[:, 0].float().cpu().numpy()
-        kvd = []
-        for l in range(D.L):
-            np.testing.assert_array_equal(kg[l][:, :n0], okv.K[l][:, :n0])
-            np.testing.assert_array_equal(vg[l][:, :n0], okv.V[l][:, :n0])
-            # layer l's K/V rows come after l layers' stages plus their own rounding
-            kerr = np.abs(kg[l][:, :n] - okv.K[l][:, :n]).max()
-            verr = np.abs(vg[l][:, :n] - okv.V[l][:, :n]).max()
-            assert max(kerr, verr) <= TOL * stages(l), (step, l, kerr, verr)
-            kvd.append(max(kerr, verr))
-        drift.append(dict(logits=lerr, h_last=herr, kv_last_layer=kvd[-1]))
-        print(f"  step {step}: h_last drift {herr:.4f}, K/V drift of the last layer "
-              f"{kvd[-1]:.4f}", flush=True)
+        xg_all = sess.residual().cpu().numpy().astype(np.float64)
+        kg_all = sess.kv.k_rows().float().cpu().numpy()
+        vg_all = sess.kv.v_rows().float().cpu().numpy()
+        for b in range(B):
+            t, okv, h, t0, n, n0 = ts[b], okvs[b], hs[b], t0s[b], ns[b], n0s[b]
+            print(f"  step {step} seq {b}: n={n}", flush=True)
+            hz = sess.head_logits[b].cpu().numpy()[:t.max_depth]
+            want_z = oh.medusa_heads(Wt.get, h, t.max_depth)
+            assert np.abs(hz - want_z).max() <= TOL, (step, b, np.abs(hz - want_z).max())
+            top = sess.top_ids[b].cpu().numpy()[:t.max_depth]
+            np.testing.assert_array_equal(top, oh.head_topk(hz, s))
+            tok = otree.fill_tokens(t, t0, top)
+            np.testing.assert_array_equal(sess.tree_tok[b].cpu().numpy(), tok)
+            gl = sess.logits[b].cpu().numpy().astype(np.float64)
+            # the LM-head stage on the GPU's own final residual rows
+            xg = xg_all[b * T:(b + 1) * T]
+            _, lm_want = om.final_head(Wt.get, xg)
+            lm_err = np.abs(gl - lm_want).max()
+            assert lm_err <= TOL, (step, b, lm_err)
+            # the whole forward against the oracle's own
+            hn, logits = om.tree_forward(Wt.get, D.L, D.H, t, tok, n, okv)
+            lerr = np.abs(gl - logits).max()
+            print(f"  step {step} seq {b}: head logits err {np.abs(hz - want_z).max():.2e}, "
+                  f"LM-head stage err {lm_err:.2e}, tree logits drift max {lerr:.4f} rms "
+                  f"{np.sqrt(np.mean((gl - logits) ** 2)):.5f} (logits rms "
+                  f"{np.sqrt(np.mean(logits ** 2)):.3f})", flush=True)
+            # the drift bound TOL per stage is for unit-scale values: bf16
+            # rounding is relative, so the logits' bound scales with their rms
+            # (1.28 at the 7B width, 1.63 at 33B with N(0, 0.02) weights)
+            lscale = max(1.0, float(np.sqrt(np.mean(logits ** 2))))
+            assert lerr <= TOL * stages(D.L) * lscale, (step, b, lerr, lscale)
+            if w.accept == "typical":
+                res = oa.typical_accept(t, tok, gl, w.temperature, w.eps, w.delta)
+            elif reject:
+                res = oa.reject_accept(t, tok, gl, w.temperature, u[step + 1, b])
+                m = res.margin
+                assert not np.any(np.abs(m[np.isfinite(m)]) <= 1e-9), "tie up to rounding"
+            else:
+                res = oa.greedy_accept(t, tok, gl)
+            L_acc = int(sess.accept_len[b])
+            assert L_acc == res.accept_len, (step, b)
+            np.testing.assert_array_equal(sess.path[b].cpu().numpy()[:L_acc + 1], res.path)
+            np.testing.assert_array_equal(sess.emitted[b].cpu().numpy()[:L_acc + 1], tok[res.path])
+            assert int(sess.best[b]) == res.best
+            if reject:
+                assert int(sess.root_tok[b]) == res.next_root
+            elif w.root == "sample":
+                want, margin = oa.sample_root(gl[res.best], w.temperature, u[step + 1, b])
+                if margin > 1e-6:
+                    assert int(sess.root_tok[b]) == want
+            else:
+                assert int(sess.root_tok[b]) == oa.argmax_lowest(gl[res.best])
+            t0s[b] = int(sess.root_tok[b])
+            herr = np.abs(sess.h_last[b].float().cpu().numpy() - hn[res.best]).max()
+            assert herr <= TOL * stages(D.L), (step, b, herr)
+            hs[b] = sess.h_last[b].float().cpu().numpy().astype(np.float64)   # follow the GPU
+            od.compact_kv(okv, n, res.path)
+            n += len(res.path)
+            ns[b] = n
+            assert int(sess.n_prefix[b]) == n
+            kg, vg = kg_all[:, b], vg_all[:, b]
+            kvd = []
+            for l in range(D.L):
+                np.testing.assert_array_equal(kg[l][:, :n0], okv.K[l][:, :n0])
+                np.testing.assert_array_equal(vg[l][:, :n0], okv.V[l][:, :n0])
+                # layer l's K/V rows come after l layers' stages plus their own rounding
+                kerr = np.abs(kg[l][:, :n] - okv.K[l][:, :n]).max()
+                verr = np.abs(vg[l][:, :n] - okv.V[l][:, :n]).max()
+                assert max(kerr, verr) <= TOL * stages(l), (step, b, l, kerr, verr)
+                kvd.append(max(kerr, verr))
+            drift.append(dict(seq=b, logits=lerr, h_last=herr, kv_last_layer=kvd[-1]))
+            print(f"  step {step} seq {b}: h_last drift {herr:.4f}, K/V drift of the last layer "
+                  f"{kvd[-1]:.4f}", flush=True)
     assert int(sess.status[0]) == 0
     return drift
 
@@ -348,6 +363,23 @@ def test_full_dims_step_wide_tiles_at_33b_width():
                         K=configs.LLAMA13B_T256.dims.K)
     c = _full_dims_session(configs.LLAMA13B_T256.name, 1, 1, dims=dims)
     _teacher_forced_steps(c, 1)
+    c["sess"].close()
+
+
+@pytest.mark.timeout(900)
+def test_full_dims_step_batch_of_four_at_33b_dims():
+    """The 33B workload's batch: four sequences, each with its own 64-node
+    sparse tree and a prefix length in [1024, 2048], at the 33B dims (d =
+    6656, 52 x 128 heads, FFN 17920, V = 32000, K = 4 Medusa heads) with 1
+    decoder layer, two graph steps.  The batch-4 head GEMV, the per-sequence
+    tree fill, masks and prefix lengths, the 256-row wide-tile GEMMs, and
+    per-sequence acceptance and compaction, each sequence against the oracle
+    as above."""
+    print("full-dims step: 33B batch of four, L=1", flush=True)
+    w = configs.LLAMA33B_B4
+    c = _full_dims_session(w.name, 1, 2, batch=w.batch)
+    print(f"  prefix lengths {c['n0s']}", flush=True)
+    _teacher_forced_steps(c, 2)
     c["sess"].close()
 
 
