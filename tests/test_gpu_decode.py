@@ -367,6 +367,22 @@ def test_full_dims_step_wide_tiles_at_33b_width():
 
 
 @pytest.mark.timeout(900)
+@pytest.mark.parametrize("wname", [configs.LLAMA13B_T16.name, configs.LLAMA13B_T64.name,
+                                   configs.LLAMA13B_T256.name])
+def test_full_dims_step_13b_tree_sizes(wname):
+    """The 13B workloads' tree-size sweep at the 13B dims (d = 5120, 40 x 128
+    heads, FFN 13824, V = 32000, K = 5 Medusa heads, prefix 1024): the
+    16- and 64-node sparse trees of depth 5 and the 256-node Cartesian tree,
+    1 decoder layer, two graph steps, every kernel in the launch
+    configuration of the timed step at that tree size (16-, 64- and 256-row
+    GEMM tiles), against the oracle as above."""
+    print(f"full-dims step: {wname} with L=1", flush=True)
+    c = _full_dims_session(wname, 1, 2)
+    _teacher_forced_steps(c, 2)
+    c["sess"].close()
+
+
+@pytest.mark.timeout(900)
 def test_full_dims_step_batch_of_four_at_33b_dims():
     """The 33B workload's batch: four sequences, each with its own 64-node
     sparse tree and a prefix length in [1024, 2048], at the 33B dims (d =
