@@ -495,6 +495,60 @@ def test_full_dims_prefill_two_layers_matches_causal_decoding(prefill_rows, n):
     sess.close()
 
 
+@pytest.mark.timeout(900)
+def test_full_dims_prefill_batch_of_four_at_33b_dims():
+    """Prefill of four ragged prompts (300, 200, 40 and 513 tokens) as one
+    batch at the 33B dims (d = 6656, 52 x 128 heads, FFN 17920, 1 decoder
+    layer) in 256-row chunks: 1024-row GEMM launches in wide tiles, and
+    sequences whose prompts end in an earlier chunk than the others.  Every
+    sequence's K/V rows, h_last and first root against the oracle's plain
+    causal forward of its own prompt."""
+    w0 = configs.LLAMA33B_B4
+    D = configs.Dims(L=1, d=w0.dims.d, H=w0.dims.H, hd=w0.dims.hd, F=w0.dims.F,
+                     V=w0.dims.V, K=w0.dims.K)
+    w = w0.with_(dims=D)
+    lens = [300, 200, 40, 513]
+    B = len(lens)
+    print(f"full-dims prefill: 33B dims, batch of four prompts {lens}, L=1", flush=True)
+    Wt = synth.TorchDrawnWeights(w)
+    s = synth.tree_topk(w)
+    trees = rt.DeviceTrees([synth.tree_paths(w, b) for b in range(B)], s)
+    ids = [synth.random_tokens(4321 + b, n, D.V) for b, n in enumerate(lens)]
+    prefill_rows = 256
+    chunk = max(trees.T, prefill_rows)
+    cap = ((max(lens) + chunk + 63) // 64) * 64
+    dw = rt.DeviceWeights(D, Wt.get)
+    p = tv.AcceptParams(mode=tv.ACCEPT_GREEDY, root_mode=tv.ROOT_ARGMAX, temperature=0.0,
+                        eps=0.0, delta=0.0)
+    sess = rt.Session(D, B, trees.T, s, cap, dw, trees, p, debug=True, prefill_rows=prefill_rows)
+    sess.prefill(ids)
+    torch.cuda.synchronize()
+    bound = TOL * stages(D.L)
+    kg_all = sess.kv.k_rows().float().cpu().numpy()
+    vg_all = sess.kv.v_rows().float().cpu().numpy()
+    for b, n in enumerate(lens):
+        assert int(sess.n_prefix[b]) == n
+        okv = om.KVCache(D.L, D.H, D.hd, cap)
+        hn, logits = om.causal_forward(Wt.get, D.L, D.H, ids[b], 0, okv)
+        top2 = np.sort(logits[n - 1])[-2:]
+        if top2[1] - top2[0] > 2 * bound:
+            assert int(sess.root_tok[b]) == oa.argmax_lowest(logits[n - 1]), b
+        herr = np.abs(sess.h_last[b].float().cpu().numpy() - hn[n - 1]).max()
+        assert herr <= bound, (b, herr)
+        kvd = []
+        for l in range(D.L):
+            # the stage bound plus the cache's own bf16 rounding, up to half a
+            # unit in the last place (2^-9 |v|: K values reach 6-7 at this width)
+            for g, o in ((kg_all[l, b][:, :n], okv.K[l][:, :n]), (vg_all[l, b][:, :n], okv.V[l][:, :n])):
+                excess = np.abs(g - o) - (TOL * stages(l) + 2.0 ** -9 * np.abs(o))
+                assert excess.max() <= 0, (b, l, float(np.abs(g - o).max()), float(excess.max()))
+            kvd.append(max(np.abs(kg_all[l, b][:, :n] - okv.K[l][:, :n]).max(),
+                           np.abs(vg_all[l, b][:, :n] - okv.V[l][:, :n]).max()))
+        print(f"  sequence {b} ({n} tokens): h_last err {herr:.4f}, K/V err {max(kvd):.4f}, "
+              f"root {int(sess.root_tok[b])}", flush=True)
+    sess.close()
+
+
 @pytest.mark.parametrize("accept", ["typical", "reject"])
 def test_step_refuses_to_run_past_the_draws(accept):
     """Sampled roots and rejection sampling take one row of u_draws per step
