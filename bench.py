@@ -163,7 +163,7 @@ def attn_summary(dirs):
 
 
 MFMA_FILE = os.path.join(ROOT, "profiles", "gemm_mfma_llama7b_T64.md")
-GEMM_KINDS = (("QKV", "gemm_kernel<4, 4, 2, 3>"), ("O / down", "gemm_kernel<4, 4, 1, 1>"),
+GEMM_KINDS = (("QKV", "gemm_kernel<4, 4, 1, 3>"), ("O / down", "gemm_kernel<4, 4, 1, 1>"),
               ("gate/up", "gemm_kernel<4, 4, 2, 2>"), ("LM head", "gemm_kernel<4, 8, 1, 0>"))
 
 

@@ -88,9 +88,12 @@ static GemmCfg gemm_cfg(const mv_dims& D, int kind, int Mp) {
   GemmCfg c;
   c.MB = mvk::gemm_mb(Mp);
   switch (kind) {
-    case G_QKV: {   // 128- and 256-row tiles: one block per wave, RoPE partners across waves
+    case G_QKV: {   // one block per wave, RoPE partners in neighbouring waves: 8-wave tiles
+                    // at 128 and 256 rows; up to 64 rows 4-wave tiles of 64 columns, whose
+                    // count covers the chip without a K split (7B: 192 tiles)
       const bool split = c.MB >= 8 && (3 * D.d / 16 + 7) / 8 <= 256;
-      c.w = split ? 8 : 4; c.nbw = split ? 1 : 2; c.N = 3 * D.d; c.K = D.d; c.epi = mvk::EPI_QKV;
+      c.w = split ? 8 : 4; c.nbw = split || c.MB <= 4 ? 1 : 2; c.N = 3 * D.d; c.K = D.d;
+      c.epi = mvk::EPI_QKV;
       break;
     }
     case G_O: c.w = 4; c.nbw = 1; c.N = D.d; c.K = D.d; c.epi = mvk::EPI_ADD; break;

@@ -22,6 +22,8 @@
 //  * 128- and 256-row tiles give each wave one column block (gate/up: gate
 //    and up blocks in different waves; QKV: RoPE partners in neighbouring
 //    waves, exchanged through LDS), which leaves registers for an 8-deep ring.
+//    QKV tiles of up to 64 rows do the same with 4 waves (64 columns): their
+//    count covers the chip without splitting K, so no partials are exchanged.
 //  * K is split over `splits` workgroups when the column tiles alone cannot
 //    fill the chip.  Each split writes its partial tile with write-through
 //    (system-scope) stores, waits for them, and bumps the tile's arrival
@@ -1451,6 +1453,8 @@ static hipError_t launch_mb(const GemmArgs& g, dim3 grid, hipStream_t s) {
   } else if constexpr (NBW == 1) {
     if (g.epi == EPI_STORE) hipLaunchKernelGGL((gemm_kernel<MB, W, 1, EPI_STORE>), grid, blk, 0, s, g);
     else if (g.epi == EPI_ADD) hipLaunchKernelGGL((gemm_kernel<MB, W, 1, EPI_ADD>), grid, blk, 0, s, g);
+    else if (MB <= 4 && g.epi == EPI_QKV)        // 64-column QKV tiles, RoPE partners in wave pairs
+      hipLaunchKernelGGL((gemm_kernel<(MB <= 4 ? MB : 4), W, 1, EPI_QKV>), grid, blk, 0, s, g);
     else return hipErrorInvalidValue;
   } else {
     if (g.epi == EPI_SWIGLU) hipLaunchKernelGGL((gemm_kernel<MB, W, 2, EPI_SWIGLU>), grid, blk, 0, s, g);
