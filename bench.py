@@ -129,6 +129,60 @@ def pmc_summary(dirs, gate_up_name="gemm_kernel<4, 4, 2, 2>"):
     return out
 
 
+def gemm_traffic_summary(dirs):
+    """Per-kind HBM traffic of the headline step's 64-row GEMM launches from
+    rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes, scaled by what the same
+    counter reads for the calibration copy, against each launch's
+    algorithmic bytes.  O and down share one instantiation: in dispatch
+    order a launch of it after QKV is O, after gate/up down (back-to-back
+    timing launches, which follow neither, are left out)."""
+    import csv
+    import glob
+    import statistics
+    from workloads import configs
+    D, M = configs.HEADLINE.dims, 64
+    names = (("QKV", "gemm_kernel<4, 4, 1, 3>"), ("gate/up", "gemm_kernel<4, 4, 2, 2>"),
+             ("O / down", "gemm_kernel<4, 4, 1, 1>"), ("LM head", "gemm_kernel<4, 8, 1, 0>"))
+    algo = {"QKV": 2 * 3 * D.d * D.d + M * D.d * 2 + M * 3 * D.d * 2,
+            "O": 2 * D.d * D.d + M * D.d * (2 + 4 * 2 + 2),
+            "gate/up": gate_up_bytes(D, M),
+            "down": 2 * D.F * D.d + M * D.F * 2 + M * D.d * (4 * 2 + 2),
+            "LM head": 2 * D.V * D.d + M * D.V * 4}
+    per, copy = {}, {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            rows = sorted(csv.DictReader(open(f)), key=lambda r: int(r["Dispatch_Id"]))
+            prev = None
+            for r in rows:
+                name, ctr, v = r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
+                if "neg" in name:
+                    copy.setdefault(ctr, []).append(v)
+                    continue
+                kind = next((lab for lab, k in names if k in name), None)
+                if kind == "O / down":
+                    kind = "O" if prev == "QKV" else "down" if prev == "gate/up" else None
+                    prev = None
+                elif kind in ("QKV", "gate/up"):
+                    prev = kind
+                if kind:
+                    per.setdefault((kind, ctr), []).append(v)
+    lines = []
+    for kind in ("QKV", "O", "gate/up", "down", "LM head"):
+        tot, parts = 0.0, []
+        for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+            vals, cp = per.get((kind, ctr)), copy.get(ctr)
+            if not vals or not cp:
+                break
+            scale = (COPY_BYTES / 1024) / statistics.median(cp)
+            b = statistics.mean(vals) * 1024 * scale
+            tot += b
+            parts.append(f"{ctr} {statistics.mean(vals):.0f} KiB x{scale:.2f} over {len(vals)}")
+        else:
+            lines.append(f"{kind}: {'; '.join(parts)} -> {tot / 1e6:.2f} MB against "
+                         f"{algo[kind] / 1e6:.2f} MB algorithmic ({tot / algo[kind]:.3f}x)")
+    return lines
+
+
 ATTN_KINDS = (("per query block", "tree_attention_qb_kernel"), ("split keys", "tree_attention_kernel<"),
               ("split merge", "attention_merge_kernel"))
 
@@ -352,6 +406,9 @@ def main() -> int:
                     help="summarise rocprofv3 --pmc FETCH_SIZE/WRITE_SIZE output dirs and exit")
     ap.add_argument("--mfma-summary", nargs="+", metavar="DIR",
                     help="summarise rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 output dirs and exit")
+    ap.add_argument("--gemm-summary", nargs="+", metavar="DIR",
+                    help="summarise rocprofv3 --pmc FETCH_SIZE/WRITE_SIZE output dirs for every "
+                         "GEMM kind of the headline step and exit")
     ap.add_argument("--attn-summary", nargs="+", metavar="DIR",
                     help="summarise rocprofv3 --pmc FETCH_SIZE/WRITE_SIZE output dirs for the "
                          "tree-attention kernels of --workload and exit")
@@ -371,6 +428,11 @@ def main() -> int:
             print(f"traffic_bytes_per_launch = {int(round(tot))}")
             print(f"traffic_over_algorithmic = {tot / algo:.4f}")
             print(f"source_sha256 = {gemm_source_hash()}")
+        return 0
+    if args.gemm_summary:
+        for line in gemm_traffic_summary(args.gemm_summary):
+            print(line)
+        print(f"source_sha256 = {gemm_source_hash()}")
         return 0
     if args.attn_summary:
         from workloads import configs, synth
