@@ -193,6 +193,8 @@ def _layer_case(D, B, ns, paths_per_seq, topk, seed, gain_std=0.1):
 
 @pytest.mark.parametrize("name,B,ns", [
     ("tiny", 1, [32]),
+    ("tiny", 2, [32, 9]),      # 32 rows: 2-row-block tiles (QKV in 64-column tiles)
+    ("mid_t16", 2, [50, 7]),   # 32 rows, hd = 128: RoPE partners in neighbouring waves
     ("mid", 1, [77]),          # hd = 128: RoPE partners paired across 16-row blocks
     ("mid", 2, [64, 301]),     # 128 rows: split-K on the down projection
     ("mid", 4, [64, 301, 5, 1000]),   # 256 rows (batch 4): 16-row-block tiles
@@ -222,6 +224,7 @@ def test_decoder_layer_matches_oracle(name, B, ns):
     _flush(f"decoder_layer {name} B={B} ns={ns}")
     D = {"tiny": configs.TINY.dims, "tiny_b4": configs.TINY.dims,
          "mid": configs.Dims(L=1, d=256, H=2, hd=128, F=512, V=512, K=3),
+         "mid_t16": configs.Dims(L=1, d=256, H=2, hd=128, F=512, V=512, K=3),
          "mid_f480": configs.Dims(L=1, d=256, H=2, hd=128, F=480, V=512, K=3),
          "wide_f": configs.Dims(L=1, d=128, H=1, hd=128, F=16416, V=512, K=3),
          "wide_b4": configs.Dims(L=1, d=6144, H=48, hd=128, F=6144, V=512, K=3)}.get(name)
@@ -236,6 +239,8 @@ def test_decoder_layer_matches_oracle(name, B, ns):
         paths = [synth.tree_paths(wl, b) for b in range(B)]
     elif name == "wide_b4":
         paths = random_trees(rng, B, 255, 4, 6)
+    elif name == "mid_t16":
+        paths = random_trees(rng, B, 15, 3, 4)
     else:
         paths = random_trees(rng, B, 63, 4, 6)
     Wt, trees, ocaches, kv, x, cap = _layer_case(D, B, ns, paths, 10, 2024 + B)
